@@ -1,0 +1,241 @@
+"""CPU oracle for one SRU layer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never does, and this package never imports the product.
+
+Everything here is plain double-precision evaluation of the Simple Recurrent
+Unit as defined in "When Attention Meets Fast Recurrence: Training Language
+Models with Reduced Compute" (Lei), background section, Eqs. 1-5, with the
+readings listed in the C source header (highway scale alpha, initial state
+c0, bidirectional = two independent directions, backward by the chain rule,
+linear mode = the same recurrence with v = 0).  The arithmetic lives in
+``sru_oracle.c``; this module only marshals numpy arrays.
+
+Layouts (row-major): U [L, B, ndir, 3, d]; x [L, B, d]; v, b [ndir, 2, d];
+c0 [ndir, B, d]; h, c [L, B, ndir, d]; c_last [ndir, B, d].
+
+Pins (tests/test_oracle_pins.py): textbook matmul, saturated gates, the EMA
+closed form, brute-force unrolled recurrences at L <= 4, central finite
+differences for every gradient, the bidirectional time-flip invariant and
+channel/batch permutation equivariance.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle_sru.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_fp = ctypes.POINTER(ctypes.c_float)
+_ip = ctypes.POINTER(ctypes.c_int64)
+_i64 = ctypes.c_int64
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.sru_oracle_sigmoid.restype = ctypes.c_double
+    lib.sru_oracle_sigmoid.argtypes = [ctypes.c_double]
+    lib.sru_oracle_round_bf16.restype = ctypes.c_float
+    lib.sru_oracle_round_bf16.argtypes = [ctypes.c_float]
+    lib.sru_oracle_project.restype = None
+    lib.sru_oracle_project.argtypes = [_i64, _i64, _i64, _fp, ctypes.c_int, _fp,
+                                       _ip, _i64, _ip, _i64, _dp]
+    lib.sru_oracle_project_bwd_data.restype = None
+    lib.sru_oracle_project_bwd_data.argtypes = [_i64, _i64, _i64, _dp, _fp,
+                                                _ip, _i64, _dp]
+    d = ctypes.c_double
+    lib.sru_oracle_chain_forward.restype = None
+    lib.sru_oracle_chain_forward.argtypes = [_i64, ctypes.c_int, d, _dp, _dp, _dp, _dp,
+                                             d, d, d, d, d, _dp, _dp, _dp]
+    lib.sru_oracle_chain_backward.restype = None
+    lib.sru_oracle_chain_backward.argtypes = [_i64, ctypes.c_int, d, _dp, _dp, _dp, _dp,
+                                              d, d, d, d, d, _dp, _dp, d,
+                                              _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+    lib.sru_oracle_forward.restype = None
+    lib.sru_oracle_forward.argtypes = [_i64, _i64, _i64, ctypes.c_int, d,
+                                       _dp, _fp, _fp, _fp, _fp, _dp, _dp, _dp]
+    lib.sru_oracle_backward.restype = None
+    lib.sru_oracle_backward.argtypes = [_i64, _i64, _i64, ctypes.c_int, d,
+                                        _dp, _fp, _fp, _fp, _fp, _dp, _fp, _fp,
+                                        _dp, _dp, _dp, _dp, _dp]
+    lib.sru_oracle_num_threads.restype = ctypes.c_int
+    lib.sru_oracle_num_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _f32(a):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a, a.ctypes.data_as(_fp)
+
+
+def _f64(a):
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    return a, a.ctypes.data_as(_dp)
+
+
+def _i64arr(a):
+    a = np.ascontiguousarray(a, dtype=np.int64)
+    return a, a.ctypes.data_as(_ip)
+
+
+def _optf32(a):
+    if a is None:
+        return None, None
+    return _f32(a)
+
+
+def num_threads() -> int:
+    """Threads the oracle's whole-tensor drivers spread independent chains over."""
+    return int(_load().sru_oracle_num_threads())
+
+
+def sigmoid(z: float) -> float:
+    return float(_load().sru_oracle_sigmoid(float(z)))
+
+
+def round_bf16(a) -> np.ndarray:
+    """fp32 -> nearest bf16 (ties to even), returned widened to fp32."""
+    lib = _load()
+    flat = np.ascontiguousarray(a, dtype=np.float32).ravel()
+    out = np.empty_like(flat)
+    for i, v in enumerate(flat):
+        out[i] = lib.sru_oracle_round_bf16(float(v))
+    return out.reshape(np.shape(a))
+
+
+def project(A, W, round_a: bool, rows=None, cols=None) -> np.ndarray:
+    """Eq. 1 on selected rows x columns: out[i, k] = sum_q Atilde[rows[i], q] W[cols[k], q]."""
+    A, pa = _f32(A)
+    W, pw = _f32(W)
+    M, K = A.shape
+    N, K2 = W.shape
+    assert K == K2
+    rows = np.arange(M) if rows is None else np.asarray(rows)
+    cols = np.arange(N) if cols is None else np.asarray(cols)
+    rows, pr = _i64arr(rows)
+    cols, pc = _i64arr(cols)
+    out = np.empty((rows.size, cols.size), dtype=np.float64)
+    _load().sru_oracle_project(M, N, K, pa, int(bool(round_a)), pw, pr, rows.size,
+                               pc, cols.size, out.ctypes.data_as(_dp))
+    return out
+
+
+def project_bwd_data(G, W, rows=None) -> np.ndarray:
+    """out[i, q] = sum_n G[rows[i], n] W[n, q] (gradient of Eq. 1 w.r.t. its input)."""
+    G, pg = _f64(G)
+    W, pw = _f32(W)
+    M, N = G.shape
+    N2, K = W.shape
+    assert N == N2
+    rows = np.arange(M) if rows is None else np.asarray(rows)
+    rows, pr = _i64arr(rows)
+    out = np.empty((rows.size, K), dtype=np.float64)
+    _load().sru_oracle_project_bwd_data(M, N, K, pg, pw, pr, rows.size,
+                                        out.ctypes.data_as(_dp))
+    return out
+
+
+def chain_forward(uf, ur, ux, x, vf, vr, bf, br, c0, alpha, direction=0):
+    """One chain (Eqs. 2-5).  Returns (h[L], c[L], c_last)."""
+    uf, p1 = _f64(uf)
+    ur, p2 = _f64(ur)
+    ux, p3 = _f64(ux)
+    x, p4 = _f64(x)
+    L = uf.size
+    h = np.empty(L)
+    c = np.empty(L)
+    cl = ctypes.c_double()
+    _load().sru_oracle_chain_forward(L, int(direction), float(alpha), p1, p2, p3, p4,
+                                     float(vf), float(vr), float(bf), float(br), float(c0),
+                                     h.ctypes.data_as(_dp), c.ctypes.data_as(_dp),
+                                     ctypes.byref(cl))
+    return h, c, cl.value
+
+
+def chain_backward(uf, ur, ux, x, vf, vr, bf, br, c0, c, dh, dc_last, alpha, direction=0):
+    """Chain rule through one chain.  Returns a dict of per-step and scalar grads."""
+    uf, p1 = _f64(uf)
+    ur, p2 = _f64(ur)
+    ux, p3 = _f64(ux)
+    x, p4 = _f64(x)
+    c, pc = _f64(c)
+    dh, pd = _f64(dh)
+    L = uf.size
+    outs = {k: np.empty(L) for k in ("duf", "dur", "dux", "dx_hw")}
+    sc = {k: ctypes.c_double() for k in ("dvf", "dvr", "dbf", "dbr", "dc0")}
+    _load().sru_oracle_chain_backward(
+        L, int(direction), float(alpha), p1, p2, p3, p4,
+        float(vf), float(vr), float(bf), float(br), float(c0), pc, pd, float(dc_last),
+        *(outs[k].ctypes.data_as(_dp) for k in ("duf", "dur", "dux", "dx_hw")),
+        *(ctypes.byref(sc[k]) for k in ("dvf", "dvr", "dbf", "dbr", "dc0")))
+    res = dict(outs)
+    res.update({k: v.value for k, v in sc.items()})
+    return res
+
+
+def forward(U, x, v, b, c0, alpha):
+    """Whole-tensor forward.  U [L,B,ndir,3,d] -> h, c [L,B,ndir,d], c_last [ndir,B,d].
+
+    U may be fp32 values (given U) or the oracle's own double projection."""
+    U, pu = _f64(U)
+    L, B, ndir, three, d = U.shape
+    assert three == 3
+    x, px = _f32(x)
+    v, pv = _f32(v)
+    b, pb = _f32(b)
+    c0, pc0 = _optf32(c0)
+    h = np.empty((L, B, ndir, d))
+    c = np.empty((L, B, ndir, d))
+    cl = np.empty((ndir, B, d))
+    _load().sru_oracle_forward(L, B, d, ndir, float(alpha), pu, px, pv, pb, pc0,
+                               h.ctypes.data_as(_dp), c.ctypes.data_as(_dp),
+                               cl.ctypes.data_as(_dp))
+    return {"h": h, "c": c, "c_last": cl}
+
+
+def backward(U, x, v, b, c0, c, dh, dc_last, alpha):
+    """Whole-tensor backward given the oracle's own forward states ``c``."""
+    U, pu = _f64(U)
+    L, B, ndir, _, d = U.shape
+    x, px = _f32(x)
+    v, pv = _f32(v)
+    b, pb = _f32(b)
+    c0, pc0 = _optf32(c0)
+    c, pc = _f64(c)
+    dh, pdh = _f32(dh)
+    dc_last, pdcl = _optf32(dc_last)
+    dU = np.empty(U.shape)
+    dx = np.empty((L, B, d))
+    dv = np.empty((ndir, 2, d))
+    db = np.empty((ndir, 2, d))
+    dc0 = np.empty((ndir, B, d))
+    _load().sru_oracle_backward(L, B, d, ndir, float(alpha), pu, px, pv, pb, pc0, pc,
+                                pdh, pdcl, dU.ctypes.data_as(_dp), dx.ctypes.data_as(_dp),
+                                dv.ctypes.data_as(_dp), db.ctypes.data_as(_dp),
+                                dc0.ctypes.data_as(_dp))
+    return {"dU": dU, "dx_hw": dx, "dv": dv, "db": db, "dc0": dc0}
+
+
+def layer_U(X, W, round_x: bool, L, B, ndir, d):
+    """Eq. 1 for a whole layer: X [L,B,d], W [ndir*3d, d] -> U [L,B,ndir,3,d] (double)."""
+    U = project(np.asarray(X, np.float32).reshape(L * B, d), W, round_x)
+    return U.reshape(L, B, ndir, 3, d)
+
+
+def chain_inputs_from_projection(X, W, round_x, L, B, d, ndir, direction, b, j):
+    """The three U slots of chain (direction, b, j) computed by Eq. 1 from X and W."""
+    rows = np.arange(L) * B + b
+    cols = [(direction * 3 + g) * d + j for g in range(3)]
+    u = project(np.asarray(X, np.float32).reshape(L * B, d), W, round_x, rows=rows, cols=cols)
+    return u[:, 0], u[:, 1], u[:, 2]

@@ -1,0 +1,367 @@
+/*
+ * sru_oracle.c -- plain, slow, double-precision CPU oracle for one SRU layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link or
+ * call this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header, table or helper with the
+ * HIP library.
+ *
+ * What it computes, and where that is defined:
+ *
+ *   Lei, "When Attention Meets Fast Recurrence: Training Language Models with
+ *   Reduced Compute" (SRU++ paper), background section on the Simple Recurrent
+ *   Unit, unnumbered cell equations and Eqs. 1-5:
+ *     U^T = [W; W'; W''] X^T                          (Eq. 1, one projection)
+ *     f[t] = sigma(U[t,0] + v  * c[t-1] + b )         (Eq. 2)
+ *     r[t] = sigma(U[t,1] + v' * c[t-1] + b')         (Eq. 3)
+ *     c[t] = f[t] * c[t-1] + (1 - f[t]) * U[t,2]      (Eq. 4)
+ *     h[t] = r[t] * c[t] + (1 - r[t]) * x[t]          (Eq. 5)
+ *   Every channel of every sequence is an independent chain once U is known
+ *   (the remark after Eq. 5), so the oracle is written per chain.
+ *
+ * Readings taken where the pages are silent (each is listed in the design
+ * notes of the repository):
+ *   - the highway input is scaled by a scalar alpha: (1 - r) * alpha * x;
+ *     alpha = 1 gives Eq. 5 exactly;
+ *   - c[-1] = c0 is an input (0 when absent);
+ *   - a bidirectional layer is two independent directions; direction 1 walks
+ *     t = L-1 .. 0 and its c0 is the state before t = L-1;
+ *   - the backward pass is the chain rule applied to the equations above (the
+ *     pages print none);
+ *   - the linear mode ("Parallelizing Legendre Memory Unit Training",
+ *     abstract: linear recurrences can be trained in parallel) is the same
+ *     recurrence with v = v' = 0.  The oracle evaluates it sequentially; it
+ *     never chunks.
+ *
+ * All arithmetic is in double.  Inputs arrive as float (fp32, or bf16 values
+ * widened exactly to fp32) and are widened once.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Logistic sigmoid in double; the two branches avoid overflow of exp. */
+static double oracle_sigmoid(double z)
+{
+    if (z >= 0.0)
+        return 1.0 / (1.0 + exp(-z));
+    double e = exp(z);
+    return e / (1.0 + e);
+}
+
+double sru_oracle_sigmoid(double z) { return oracle_sigmoid(z); }
+
+/*
+ * Round an fp32 value to the nearest bfloat16 (ties to even) and return it
+ * widened back to fp32.  bfloat16 keeps the upper 16 bits of the fp32 pattern.
+ * NaN stays NaN (quietened); infinities and zeros pass through.
+ */
+float sru_oracle_round_bf16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    if ((u & 0x7f800000u) == 0x7f800000u) {          /* inf or nan */
+        if (u & 0x007fffffu)
+            u |= 0x00400000u;                          /* quiet nan */
+        u &= 0xffff0000u;
+    } else {
+        uint32_t lower = u & 0xffffu;
+        uint32_t upper = u >> 16;
+        if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+            upper += 1u;                               /* may carry into exponent */
+        u = upper << 16;
+    }
+    float y;
+    memcpy(&y, &u, sizeof y);
+    return y;
+}
+
+/*
+ * Projection (Eq. 1) for a cross product of selected rows and columns:
+ *   out[i][k] = sum_{q<K} Atilde[rows[i]][q] * W[cols[k]][q]
+ * A is [M, K] row-major, W is [N, K] row-major (row n = output feature n).
+ * Atilde = bf16-rounded A when round_a != 0, else A.  Sum in double, q in
+ * increasing order.
+ */
+void sru_oracle_project(int64_t M, int64_t N, int64_t K,
+                        const float *A, int round_a, const float *W,
+                        const int64_t *rows, int64_t n_rows,
+                        const int64_t *cols, int64_t n_cols,
+                        double *out)
+{
+    (void)M; (void)N;
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const float *a = A + rows[i] * K;
+        for (int64_t k = 0; k < n_cols; ++k) {
+            const float *w = W + cols[k] * K;
+            double s = 0.0;
+            for (int64_t q = 0; q < K; ++q) {
+                double av = round_a ? (double)sru_oracle_round_bf16(a[q]) : (double)a[q];
+                s += av * (double)w[q];
+            }
+            out[i * n_cols + k] = s;
+        }
+    }
+}
+
+/*
+ * Backward-data projection: out[i][q] = sum_n G[rows[i]][n] * W[n][q] for all
+ * q < K.  G is [M, N] row-major (the gradient of U), W is [N, K].  This is the
+ * transpose of Eq. 1's map applied to the gradient (chain rule).
+ */
+void sru_oracle_project_bwd_data(int64_t M, int64_t N, int64_t K,
+                                 const double *G, const float *W,
+                                 const int64_t *rows, int64_t n_rows,
+                                 double *out)
+{
+    (void)M;
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const double *g = G + rows[i] * N;
+        for (int64_t q = 0; q < K; ++q) {
+            double s = 0.0;
+            for (int64_t n = 0; n < N; ++n)
+                s += g[n] * (double)W[n * K + q];
+            out[i * K + q] = s;
+        }
+    }
+}
+
+/*
+ * One chain, forward.  All per-step arrays are indexed by the natural time
+ * index t = 0..L-1.  dir = 0 walks t = 0..L-1, dir = 1 walks t = L-1..0.
+ *   uf, ur, ux : the three slots of U for this channel (Eqs. 2, 3, 4)
+ *   x          : the layer input for this channel (highway term, Eq. 5)
+ * Outputs h[t], c[t] (the state after step t) and the final state.
+ */
+void sru_oracle_chain_forward(int64_t L, int dir, double alpha,
+                              const double *uf, const double *ur,
+                              const double *ux, const double *x,
+                              double vf, double vr, double bf, double br,
+                              double c0, double *h, double *c, double *c_last)
+{
+    double state = c0;
+    for (int64_t s = 0; s < L; ++s) {
+        int64_t t = dir ? (L - 1 - s) : s;
+        double prev = state;
+        double f = oracle_sigmoid(uf[t] + vf * prev + bf);          /* Eq. 2 */
+        double r = oracle_sigmoid(ur[t] + vr * prev + br);          /* Eq. 3 */
+        state = f * prev + (1.0 - f) * ux[t];                       /* Eq. 4 */
+        h[t] = r * state + (1.0 - r) * alpha * x[t];                /* Eq. 5 */
+        c[t] = state;
+    }
+    *c_last = state;
+}
+
+/*
+ * One chain, backward (chain rule through the forward above, in reverse
+ * order of the direction's walk).  c[] is the forward state sequence, dh[]
+ * the gradient of h, dc_last the gradient of the final state.  Outputs the
+ * gradients of uf, ur, ux, of x through the highway term only, the chain's
+ * contributions to dv, dv', db, db' and the gradient of c0.
+ */
+void sru_oracle_chain_backward(int64_t L, int dir, double alpha,
+                               const double *uf, const double *ur,
+                               const double *ux, const double *x,
+                               double vf, double vr, double bf, double br,
+                               double c0, const double *c, const double *dh,
+                               double dc_last,
+                               double *duf, double *dur, double *dux,
+                               double *dx_hw, double *dvf, double *dvr,
+                               double *dbf, double *dbr, double *dc0)
+{
+    double gc = dc_last;          /* dLoss/dc[t] arriving from later steps */
+    double svf = 0.0, svr = 0.0, sbf = 0.0, sbr = 0.0;
+    for (int64_t s = L - 1; s >= 0; --s) {
+        int64_t t = dir ? (L - 1 - s) : s;
+        double prev;
+        if (s == 0)
+            prev = c0;
+        else
+            prev = c[dir ? (t + 1) : (t - 1)];
+        double f = oracle_sigmoid(uf[t] + vf * prev + bf);
+        double r = oracle_sigmoid(ur[t] + vr * prev + br);
+        double ct = c[t];
+        /* h = r*c + (1-r)*alpha*x */
+        double dc = gc + dh[t] * r;
+        double dr = dh[t] * (ct - alpha * x[t]);
+        dx_hw[t] = dh[t] * (1.0 - r) * alpha;
+        /* c = f*prev + (1-f)*ux */
+        double df = dc * (prev - ux[t]);
+        dux[t] = dc * (1.0 - f);
+        /* through the sigmoids */
+        double dzf = df * f * (1.0 - f);
+        double dzr = dr * r * (1.0 - r);
+        duf[t] = dzf;
+        dur[t] = dzr;
+        svf += dzf * prev;
+        svr += dzr * prev;
+        sbf += dzf;
+        sbr += dzr;
+        /* prev reaches the loss through c (via f*prev), f and r */
+        gc = dc * f + dzf * vf + dzr * vr;
+    }
+    *dvf = svf; *dvr = svr; *dbf = sbf; *dbr = sbr;
+    *dc0 = gc;
+}
+
+/* ---------------------------------------------------------------------------
+ * Whole-tensor drivers.  Layouts (row-major, innermost last):
+ *   U      [L, B, ndir, 3, d]   slot 0 = f, 1 = r, 2 = candidate (double:
+ *                               given fp32/bf16 values widened, or the
+ *                               oracle's own projection)
+ *   x      [L, B, d]            shared by both directions
+ *   v, b   [ndir, 2, d]         row 0 = f gate, row 1 = r gate
+ *   c0     [ndir, B, d]         NULL means zeros
+ *   h, c   [L, B, ndir, d]
+ *   c_last [ndir, B, d]
+ *   dU     like U; dx_hw like x (sum over directions); dv, db like v;
+ *   dc0    like c0
+ * Chains are independent; OpenMP only spreads whole chains over threads and
+ * the reductions over the batch are done afterwards in a fixed order.
+ * ------------------------------------------------------------------------- */
+
+static void gather_chain(int64_t L, int64_t B, int64_t d, int ndir,
+                         int64_t dl, int64_t b, int64_t j,
+                         const double *U, const float *x,
+                         double *uf, double *ur, double *ux, double *xx)
+{
+    for (int64_t t = 0; t < L; ++t) {
+        int64_t base = ((t * B + b) * ndir + dl) * 3 * d;
+        uf[t] = U[base + 0 * d + j];
+        ur[t] = U[base + 1 * d + j];
+        ux[t] = U[base + 2 * d + j];
+        xx[t] = x[(t * B + b) * d + j];
+    }
+}
+
+void sru_oracle_forward(int64_t L, int64_t B, int64_t d, int ndir, double alpha,
+                        const double *U, const float *x, const float *v,
+                        const float *bias, const float *c0,
+                        double *h, double *c, double *c_last)
+{
+    int64_t chains = (int64_t)ndir * B * d;
+#pragma omp parallel
+    {
+        double *buf = (double *)malloc(sizeof(double) * 6 * (size_t)L);
+        double *uf = buf, *ur = buf + L, *ux = buf + 2 * L, *xx = buf + 3 * L;
+        double *hh = buf + 4 * L, *cc = buf + 5 * L;
+#pragma omp for schedule(static)
+        for (int64_t ch = 0; ch < chains; ++ch) {
+            int64_t dl = ch / (B * d), b = (ch / d) % B, j = ch % d;
+            gather_chain(L, B, d, ndir, dl, b, j, U, x, uf, ur, ux, xx);
+            double cl;
+            sru_oracle_chain_forward(L, (int)dl, alpha, uf, ur, ux, xx,
+                                     v[(dl * 2 + 0) * d + j], v[(dl * 2 + 1) * d + j],
+                                     bias[(dl * 2 + 0) * d + j], bias[(dl * 2 + 1) * d + j],
+                                     c0 ? (double)c0[(dl * B + b) * d + j] : 0.0,
+                                     hh, cc, &cl);
+            for (int64_t t = 0; t < L; ++t) {
+                int64_t o = ((t * B + b) * ndir + dl) * d + j;
+                h[o] = hh[t];
+                c[o] = cc[t];
+            }
+            c_last[(dl * B + b) * d + j] = cl;
+        }
+        free(buf);
+    }
+}
+
+/*
+ * c is the oracle's own forward state sequence [L, B, ndir, d] (double).
+ * dc_last may be NULL (zeros).  dv_part / db_part receive per-(dir, b)
+ * partials [ndir, B, 2, d] that are then summed over b in increasing b.
+ */
+void sru_oracle_backward(int64_t L, int64_t B, int64_t d, int ndir, double alpha,
+                         const double *U, const float *x, const float *v,
+                         const float *bias, const float *c0, const double *c,
+                         const float *dh, const float *dc_last,
+                         double *dU, double *dx_hw, double *dv, double *db,
+                         double *dc0)
+{
+    int64_t chains = (int64_t)ndir * B * d;
+    double *dv_part = (double *)calloc((size_t)chains * 2, sizeof(double));
+    double *db_part = (double *)calloc((size_t)chains * 2, sizeof(double));
+    double *dxd = (double *)calloc((size_t)chains * (size_t)L, sizeof(double));
+#pragma omp parallel
+    {
+        double *buf = (double *)malloc(sizeof(double) * 11 * (size_t)L);
+        double *uf = buf, *ur = buf + L, *ux = buf + 2 * L, *xx = buf + 3 * L;
+        double *cc = buf + 4 * L, *gh = buf + 5 * L;
+        double *duf = buf + 6 * L, *dur = buf + 7 * L, *dux = buf + 8 * L;
+        double *dxx = buf + 9 * L;
+#pragma omp for schedule(static)
+        for (int64_t ch = 0; ch < chains; ++ch) {
+            int64_t dl = ch / (B * d), b = (ch / d) % B, j = ch % d;
+            gather_chain(L, B, d, ndir, dl, b, j, U, x, uf, ur, ux, xx);
+            for (int64_t t = 0; t < L; ++t) {
+                int64_t o = ((t * B + b) * ndir + dl) * d + j;
+                cc[t] = c[o];
+                gh[t] = dh[o];
+            }
+            double dvf, dvr, dbf, dbr, g0;
+            sru_oracle_chain_backward(L, (int)dl, alpha, uf, ur, ux, xx,
+                                      v[(dl * 2 + 0) * d + j], v[(dl * 2 + 1) * d + j],
+                                      bias[(dl * 2 + 0) * d + j], bias[(dl * 2 + 1) * d + j],
+                                      c0 ? (double)c0[(dl * B + b) * d + j] : 0.0,
+                                      cc, gh,
+                                      dc_last ? (double)dc_last[(dl * B + b) * d + j] : 0.0,
+                                      duf, dur, dux, dxx, &dvf, &dvr, &dbf, &dbr, &g0);
+            for (int64_t t = 0; t < L; ++t) {
+                int64_t base = ((t * B + b) * ndir + dl) * 3 * d;
+                dU[base + 0 * d + j] = duf[t];
+                dU[base + 1 * d + j] = dur[t];
+                dU[base + 2 * d + j] = dux[t];
+                dxd[ch * L + t] = dxx[t];
+            }
+            dv_part[ch * 2 + 0] = dvf; dv_part[ch * 2 + 1] = dvr;
+            db_part[ch * 2 + 0] = dbf; db_part[ch * 2 + 1] = dbr;
+            dc0[(dl * B + b) * d + j] = g0;
+        }
+        free(buf);
+    }
+    /* highway gradient of x: sum over directions, direction 0 first */
+    for (int64_t t = 0; t < L; ++t)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t j = 0; j < d; ++j) {
+                double s = 0.0;
+                for (int64_t dl = 0; dl < ndir; ++dl)
+                    s += dxd[((dl * B + b) * d + j) * L + t];
+                dx_hw[(t * B + b) * d + j] = s;
+            }
+    /* parameter gradients: sum over the batch, b increasing */
+    for (int64_t dl = 0; dl < ndir; ++dl)
+        for (int g = 0; g < 2; ++g)
+            for (int64_t j = 0; j < d; ++j) {
+                double sv = 0.0, sb = 0.0;
+                for (int64_t b = 0; b < B; ++b) {
+                    int64_t ch = (dl * B + b) * d + j;
+                    sv += dv_part[ch * 2 + g];
+                    sb += db_part[ch * 2 + g];
+                }
+                dv[(dl * 2 + g) * d + j] = sv;
+                db[(dl * 2 + g) * d + j] = sb;
+            }
+    free(dv_part);
+    free(db_part);
+    free(dxd);
+}
+
+/* Number of threads the OpenMP runtime would use for the drivers above. */
+int sru_oracle_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp master
+        {
+#ifdef _OPENMP
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}
