@@ -1,0 +1,358 @@
+"""Benchmark of the SRU layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--no-extras] [--workload 2]
+
+One step = one pass of the whole hot path over one batch: projection GEMM
+(U = X~ W^T), forward recurrence, backward recurrence with the fused dv/db
+reduction, and the backward-data GEMM (dX = dU W + highway dx).  The headline
+workload is the bidirectional layer L=64, B=128, d=512 (fp32 activations,
+bf16 W).  Inputs are seeded synthetic draws (no dataset), resident in HBM
+before the timed region; several input/output sets rotate so consecutive steps
+do not reuse cached data.
+
+Printed: one JSON line.  ``value`` is the step's algorithmic HBM bytes (every
+tensor of every row counted once at its dtype) divided by the step time, in
+GB/s; per-row times (HIP events recorded on the stream the kernels run on),
+their roofline fractions, the dominant row's roofline object, the CPU oracle
+baseline on a bounded sample, and measurements of the other rows at the other
+workload sizes (given-U bf16 forward, the L=512 training step, the linear-mode
+chunked scan) are included.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
+METRIC = "SRU fwd+bwd recurrence GB/s and L·B·d steps/s; % HBM peak; GEMM % MFMA"
+KERNEL_SOURCES = ["gemm.hip", "recurrence.hip", "linear_scan.hip", "device_common.h"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=2, choices=[2, 4])
+    p.add_argument("--sets", type=int, default=3, help="rotating input/output sets")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="also run one torch copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "parallelizable_recurrent_units_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work of each row (every tensor counted once at its dtype)
+# ---------------------------------------------------------------------------
+def row_work(w):
+    L, B, d, nd = w.L, w.B, w.d, w.ndir
+    LB = L * B
+    xs = 2 if w.x_dtype == "bf16" else 4
+    us = 2 if w.u_dtype == "bf16" else 4
+    n3 = nd * 3 * d
+    rows = {}
+    if w.mode == "layer":
+        rows["a1_projection"] = dict(flops=2 * LB * n3 * d,
+                                     bytes=LB * d * xs + n3 * d * 2 + LB * n3 * 4)
+        rows["a5_projection_bwd_data"] = dict(flops=2 * LB * d * n3,
+                                              bytes=LB * n3 * 4 + n3 * d * 2 + 2 * LB * d * 4)
+    fwd = LB * n3 * us + LB * d * xs + LB * nd * d * 4 * (2 if w.backward else 1)
+    if w.linear:
+        rows["a6_linear_forward"] = dict(bytes=fwd)
+    else:
+        rows["a2_forward"] = dict(bytes=fwd)
+    if w.backward:
+        bwd = (LB * n3 * us + LB * d * xs + 2 * LB * nd * d * 4 + LB * n3 * 4 + LB * d * 4)
+        rows["a7_linear_backward" if w.linear else "a3_a4_backward"] = dict(bytes=bwd)
+    return rows
+
+
+def roofline_of(name, work, seconds):
+    if "flops" in work:
+        t_mfma = work["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+        t_hbm = work["bytes"] / (HBM_PEAK_GBS * 1e9)
+        if t_mfma >= t_hbm:
+            a = work["flops"] / seconds / 1e12
+            return dict(bound="mfma", achieved=a, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=a / MFMA_BF16_PEAK_TFLOPS)
+    a = work["bytes"] / seconds / 1e9
+    return dict(bound="hbm", achieved=a, peak=HBM_PEAK_GBS, unit="GB/s", frac=a / HBM_PEAK_GBS)
+
+
+# ---------------------------------------------------------------------------
+# device buffers for one training-step set
+# ---------------------------------------------------------------------------
+def device_set(w, seed):
+    import numpy as np
+    import torch
+    from parallelizable_recurrent_units_amd import SRU_WS_BACKWARD, SruShape, sru_workspace_size
+    from parallelizable_recurrent_units_amd.workloads import make_inputs
+    inp = make_inputs(w, seed=seed)
+    dev = {}
+    for k, v in inp.items():
+        if k.endswith("_bits"):
+            continue
+        if k + "_bits" in inp:
+            dev[k] = torch.from_numpy(inp[k + "_bits"].view(np.int16)).cuda().view(torch.bfloat16)
+        else:
+            dev[k] = torch.from_numpy(v).cuda()
+    L, B, d, nd = w.L, w.B, w.d, w.ndir
+    f32 = dict(device="cuda", dtype=torch.float32)
+    shape = SruShape(L, B, d, nd == 2, w.alpha)
+    dev.update(U=torch.empty((L, B, nd, 3, d), **f32), h=torch.empty((L, B, nd, d), **f32),
+               c_seq=torch.empty((L, B, nd, d), **f32), c_last=torch.empty((nd, B, d), **f32),
+               dU=torch.empty((L, B, nd, 3, d), **f32), dx=torch.empty((L, B, d), **f32),
+               dv=torch.empty((nd, 2, d), **f32), db=torch.empty((nd, 2, d), **f32),
+               dc0=torch.empty((nd, B, d), **f32),
+               ws=torch.empty(sru_workspace_size(shape, SRU_WS_BACKWARD), device="cuda",
+                              dtype=torch.uint8))
+    return shape, dev
+
+
+def training_step_rows(shape, t):
+    """The four row calls of one training step, each a C-ABI entry point."""
+    from parallelizable_recurrent_units_amd import (SRU_PROJ_BWD_DATA, SRU_PROJ_FWD, sru_backward,
+                                                    sru_forward, sru_project)
+    return [
+        ("a1_projection", lambda: sru_project(shape, SRU_PROJ_FWD, t["x"], t["W"], t["U"])),
+        ("a2_forward", lambda: sru_forward(shape, t["U"], t["x"], t["v"], t["b"], t["c0"], t["h"],
+                                           t["c_seq"], t["c_last"])),
+        ("a3_a4_backward", lambda: sru_backward(shape, t["U"], t["x"], t["v"], t["b"], t["c0"],
+                                                t["c_seq"], t["dh"], t["dc_last"], t["dU"],
+                                                t["dx"], t["dv"], t["db"], t["dc0"], t["ws"])),
+        ("a5_projection_bwd_data", lambda: sru_project(shape, SRU_PROJ_BWD_DATA, t["dU"], t["W"],
+                                                       t["dx"], True)),
+    ]
+
+
+def time_rows(row_sets, steps, warmup):
+    """Run ``steps`` passes (rotating sets), HIP events between the rows.
+
+    Returns (ms per step, {row: mean seconds})."""
+    import torch
+    nsets = len(row_sets)
+    for i in range(warmup):
+        for _, fn in row_sets[i % nsets]:
+            fn()
+    torch.cuda.synchronize()
+    names = [n for n, _ in row_sets[0]]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        ev = evs[i]
+        ev[0].record()
+        for k, (_, fn) in enumerate(row_sets[i % nsets]):
+            fn()
+            ev[k + 1].record()
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    per_row = {n: 0.0 for n in names}
+    for ev in evs:
+        for k, n in enumerate(names):
+            per_row[n] += ev[k].elapsed_time(ev[k + 1]) / 1e3 / steps
+    return total_ms / steps, per_row
+
+
+def extras(steps):
+    """Rows at the other workload sizes (each timed alone, inputs rotating)."""
+    import torch
+    from parallelizable_recurrent_units_amd import (SRU_BWD, SRU_FWD, SRU_WS_LINEAR_BWD,
+                                                    SRU_WS_LINEAR_FWD, SruShape, sru_forward,
+                                                    sru_linear_scan, sru_workspace_size)
+    from parallelizable_recurrent_units_amd.workloads import WORKLOADS
+    out = {}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    f32 = dict(device="cuda", dtype=torch.float32)
+    # given-U bf16 forward (L=1024, B=16, d=2048)
+    w = WORKLOADS[3]
+    s = SruShape(w.L, w.B, w.d, False, w.alpha)
+    sets = []
+    for _ in range(3):
+        U = torch.randn((w.L, w.B, 1, 3, w.d), generator=g, **f32).to(torch.bfloat16)
+        x = torch.randn((w.L, w.B, w.d), generator=g, **f32).to(torch.bfloat16)
+        v = (torch.rand((1, 2, w.d), generator=g, **f32) - 0.5) * 0.2
+        b = torch.zeros((1, 2, w.d), **f32)
+        h = torch.empty((w.L, w.B, 1, w.d), **f32)
+        cl = torch.empty((1, w.B, w.d), **f32)
+        sets.append([("a2_forward", (lambda U=U, x=x, v=v, b=b, h=h, cl=cl:
+                                     sru_forward(s, U, x, v, b, None, h, None, cl)))])
+    ms, rows = time_rows(sets, steps, 3)
+    work = row_work(w)
+    out[w.name] = {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
+    del sets
+    # L=512 training step
+    w = WORKLOADS[4]
+    row_sets = []
+    for i in range(3):
+        shape, t = device_set(w, 40 + i)
+        row_sets.append(training_step_rows(shape, t))
+    ms, rows = time_rows(row_sets, steps, 3)
+    work = row_work(w)
+    out[w.name] = {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
+    out[w.name]["ms_per_step"] = ms
+    del row_sets
+    torch.cuda.empty_cache()
+    # linear mode, chunk 256 (L=16384, B=4, d=4096)
+    w = WORKLOADS[5]
+    s = SruShape(w.L, w.B, w.d, False, w.alpha)
+    U = torch.randn((w.L, w.B, 1, 3, w.d), generator=g, **f32)
+    U[:, :, :, 0] += 2.0
+    x = torch.randn((w.L, w.B, w.d), generator=g, **f32)
+    dh = torch.randn((w.L, w.B, 1, w.d), generator=g, **f32)
+    b = torch.zeros((1, 2, w.d), **f32)
+    h = torch.empty((w.L, w.B, 1, w.d), **f32)
+    c_seq = torch.empty_like(h)
+    cl = torch.empty((1, w.B, w.d), **f32)
+    dU = torch.empty_like(U)
+    dx = torch.empty_like(x)
+    dbv = torch.empty((1, 2, w.d), **f32)
+    dc0 = torch.empty((1, w.B, w.d), **f32)
+    wsf = torch.empty(sru_workspace_size(s, SRU_WS_LINEAR_FWD, w.chunk), device="cuda",
+                      dtype=torch.uint8)
+    wsb = torch.empty(sru_workspace_size(s, SRU_WS_LINEAR_BWD, w.chunk), device="cuda",
+                      dtype=torch.uint8)
+    lin = [[("a6_linear_forward", lambda: sru_linear_scan(s, SRU_FWD, w.chunk, U, x, b, None, h=h,
+                                                          c_seq=c_seq, c_last=cl, workspace=wsf)),
+            ("a7_linear_backward", lambda: sru_linear_scan(s, SRU_BWD, w.chunk, U, x, b, None,
+                                                           c_seq=c_seq, dh=dh, dU=dU, dx=dx,
+                                                           db=dbv, dc0=dc0, workspace=wsb))]]
+    ms, rows = time_rows(lin, max(3, steps // 5), 2)
+    work = row_work(w)
+    out[w.name] = {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
+    return out
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The CPU oracle (as written) on a bounded sample: whole batch rows of the
+    same training step, until about ``budget_s`` seconds of work."""
+    import numpy as np
+    import oracle
+    from parallelizable_recurrent_units_amd.workloads import make_inputs
+    inp = make_inputs(w, seed=2)
+    L, B, d, nd = w.L, w.B, w.d, w.ndir
+    X2 = inp["x"].reshape(L * B, d)
+    t0 = time.perf_counter()
+    done = 0
+    for b in range(B):
+        rows = np.arange(L) * B + b
+        U = oracle.project(X2, inp["W"], True, rows=rows).reshape(L, 1, nd, 3, d)
+        sl = lambda a: np.ascontiguousarray(a[:, b:b + 1])
+        fo = oracle.forward(U, sl(inp["x"]), inp["v"], inp["b"], sl(inp["c0"]), w.alpha)
+        bo = oracle.backward(U, sl(inp["x"]), inp["v"], inp["b"], sl(inp["c0"]), fo["c"],
+                             sl(inp["dh"]), sl(inp["dc_last"]), w.alpha)
+        oracle.project_bwd_data(bo["dU"].reshape(L, -1), inp["W"])
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    secs = time.perf_counter() - t0
+    step_bytes = sum(r["bytes"] for r in row_work(w).values())
+    frac = done / B
+    return {"value": step_bytes * frac / secs / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{done} of {B} batch rows of the same training step (projection, forward, "
+                      f"backward, dX) in double precision, {secs:.1f} s; bytes scaled by {frac:.4f}"}
+
+
+def traffic_for(kernel_row, digest):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != digest:
+        return None
+    return rec.get("rows", {}).get(kernel_row)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path is not sharded in this build).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import parallelizable_recurrent_units_amd as sru
+    from parallelizable_recurrent_units_amd.workloads import WORKLOADS
+    sru.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = WORKLOADS[args.workload]
+    print(f"[bench] workload {w.name}: building {args.sets} input sets", file=sys.stderr, flush=True)
+    row_sets = []
+    for i in range(args.sets):
+        shape, t = device_set(w, seed=100 + i)
+        row_sets.append(training_step_rows(shape, t))
+    print("[bench] timing", file=sys.stderr, flush=True)
+    ms, rows = time_rows(row_sets, args.steps, args.warmup)
+    work = row_work(w)
+    per_row = {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
+    dominant = max(rows, key=lambda n: rows[n])
+    digest = source_digest()
+    roof = dict(roofline_of(dominant, work[dominant], rows[dominant]))
+    roof["kernel"] = dominant
+    roof["traffic"] = traffic_for(dominant, digest)
+    step_bytes = sum(r["bytes"] for r in work.values())
+    line = {
+        "metric": METRIC,
+        "value": step_bytes / (ms / 1e3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 recurrence, bf16 MFMA projection (fp32 accumulate)",
+        "data": "synthetic (seeded Gaussian/uniform draws of the workload's shapes)",
+        "config": {"workload": w.name, "L": w.L, "B": w.B, "d": w.d,
+                   "bidirectional": w.ndir == 2, "alpha": w.alpha,
+                   "x": w.x_dtype, "W": w.w_dtype, "parallelism": "single GPU"},
+        "elem_steps_per_s": w.elem_steps / (ms / 1e3),
+        "step_algorithmic_bytes": step_bytes,
+        "rows": per_row,
+        "roofline": roof,
+        "source_digest": digest,
+    }
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_probe_bytes"] = n * 4
+    if not args.no_extras:
+        print("[bench] other workloads", file=sys.stderr, flush=True)
+        line["other_workloads"] = extras(max(10, args.steps // 2))
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,187 @@
+/*
+ * sru.h -- C ABI of libsru, the MI355X (gfx950) implementation of one Simple
+ * Recurrent Unit layer's hot path.
+ *
+ * The layer is the one defined in Lei, "When Attention Meets Fast Recurrence:
+ * Training Language Models with Reduced Compute", background section on SRU,
+ * Eqs. 1-5:
+ *
+ *   U^T = [W; W'; W''] X^T                              (Eq. 1)
+ *   f[t] = sigma(U[t,0] + v  (.) c[t-1] + b )           (Eq. 2)
+ *   r[t] = sigma(U[t,1] + v' (.) c[t-1] + b')           (Eq. 3)
+ *   c[t] = f[t] (.) c[t-1] + (1 - f[t]) (.) U[t,2]      (Eq. 4)
+ *   h[t] = r[t] (.) c[t] + (1 - r[t]) (.) (alpha x[t])  (Eq. 5, alpha = 1 is
+ *                                                        the paper's form)
+ *
+ * plus the chain-rule backward of Eqs. 2-5 and a linear mode (v = v' = 0) in
+ * which the recurrence is an associative scan and is evaluated in time chunks,
+ * the parallel-training idea of "Parallelizing Legendre Memory Unit Training"
+ * (abstract).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is DEVICE memory owned by the caller.  The library
+ *   allocates nothing and keeps no state across calls except a thread-local
+ *   error string.
+ * - Tensors are dense, row-major, innermost dimension last, and every base
+ *   pointer must be 16-byte aligned.
+ * - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *   null stream).  Calls return after enqueueing and never synchronise; a
+ *   fault inside a kernel surfaces at the caller's next synchronisation.
+ * - Arguments are validated before anything is launched; on any error
+ *   nothing is written and the status says why (sru_last_error() has the
+ *   detail).  No exception or abort crosses the ABI.
+ * - Shapes: L (time), B (batch), d (hidden size) >= 1; ndir = 2 when
+ *   `bidirectional` is 1, else 1.  Direction 1 walks t = L-1 .. 0 and its c0
+ *   is the state before t = L-1.  x is shared by both directions.
+ *
+ * Layouts
+ *   X, x     [L, B, d]                 (the layer input; X viewed as [L*B, d])
+ *   W        [ndir*3*d, d]             row n = output feature n; per
+ *                                      direction the blocks are f | r | cand.
+ *   U, dU    [L, B, ndir, 3, d]        == the projection output [L*B, ndir*3*d]
+ *   v, b     [ndir, 2, d]              row 0 = forget gate, row 1 = reset gate
+ *   c0       [ndir, B, d]
+ *   h, c_seq [L, B, ndir, d]           c_seq[t] is the state after step t
+ *   c_last   [ndir, B, d]
+ *   dh       [L, B, ndir, d]
+ *   dx       [L, B, d]
+ *   dv, db   [ndir, 2, d]
+ *   dc0, dc_last [ndir, B, d]
+ */
+#ifndef SRU_H_
+#define SRU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SRU_OK = 0,
+    SRU_ERR_INVALID_ARG = 1,   /* bad shape, NULL required pointer, misalignment */
+    SRU_ERR_UNSUPPORTED = 2,   /* dtype combination not implemented              */
+    SRU_ERR_NO_DEVICE = 3,     /* no HIP device visible                          */
+    SRU_ERR_LAUNCH = 4,        /* a kernel launch failed                         */
+    SRU_ERR_WORKSPACE = 5      /* workspace NULL or smaller than required        */
+} sru_status;
+
+typedef enum { SRU_F32 = 0, SRU_BF16 = 1 } sru_dtype;
+typedef enum { SRU_FWD = 0, SRU_BWD = 1 } sru_pass;
+typedef enum {
+    SRU_PROJ_FWD = 0,       /* C (+)= A W^T : U = X~ W^T, A = X [L*B, d]          */
+    SRU_PROJ_BWD_DATA = 1   /* C (+)= A W   : dX = dU W, A = dU [L*B, ndir*3*d]   */
+} sru_proj_op;
+typedef enum {
+    SRU_WS_BACKWARD = 1,    /* sru_backward                      */
+    SRU_WS_LINEAR_FWD = 2,  /* sru_linear_scan(SRU_FWD, chunk)   */
+    SRU_WS_LINEAR_BWD = 3   /* sru_linear_scan(SRU_BWD, chunk)   */
+} sru_ws_op;
+
+typedef struct {
+    int64_t L, B, d;
+    int32_t bidirectional;   /* 0 or 1 */
+    float alpha;             /* highway scale; 1 reproduces Eq. 5 */
+} sru_shape;
+
+/*
+ * Projection, Eq. 1 (SRU++ paper, background section): all three gate
+ * matrices of both directions and all timesteps in one GEMM.
+ *   SRU_PROJ_FWD:      C[L*B, ndir*3d] (+)= A[L*B, d] . W^T
+ *   SRU_PROJ_BWD_DATA: C[L*B, d]       (+)= A[L*B, ndir*3d] . W
+ *     (the input gradient through Eq. 1; pass accumulate = 1 with C = the dx
+ *      returned by sru_backward to obtain the full input gradient).
+ * w_dt = SRU_BF16: bf16 MFMA with fp32 accumulation; A (fp32 or bf16) is
+ *   rounded to bf16 (nearest even) as it is loaded.
+ * w_dt = SRU_F32: fp32 arithmetic throughout (A widened if bf16).
+ * c_dt must be SRU_F32.  accumulate = 0 overwrites C, 1 adds to it.
+ */
+sru_status sru_project(const sru_shape *shape, sru_proj_op op,
+                       const void *A, sru_dtype a_dt,
+                       const void *W, sru_dtype w_dt,
+                       void *C, sru_dtype c_dt,
+                       int32_t accumulate, void *stream);
+
+/*
+ * Forward recurrence, Eqs. 2-5, for every (direction, batch, channel) chain.
+ *   U: u_dt in {F32, BF16}; x: x_dt in {F32, BF16}; v, b, c0: fp32.
+ *   c0 may be NULL (zero initial state).
+ *   h: fp32 (h_dt must be SRU_F32).
+ *   c_seq: fp32 or NULL (needed only when a backward pass follows).
+ *   c_last: fp32 or NULL.
+ * State and arithmetic are fp32.
+ */
+sru_status sru_forward(const sru_shape *shape,
+                       const void *U, sru_dtype u_dt,
+                       const void *x, sru_dtype x_dt,
+                       const float *v, const float *b, const float *c0,
+                       void *h, sru_dtype h_dt,
+                       float *c_seq, float *c_last,
+                       void *stream);
+
+/*
+ * Backward recurrence: the chain rule through Eqs. 2-5, walking each chain
+ * in the reverse of its direction's order (the pages give no backward; it
+ * is derived).  Needs the forward's c_seq.
+ *   dh: fp32 [L, B, ndir, d] (required); dc_last: fp32 or NULL (zero).
+ *   dU: fp32 [L, B, ndir, 3, d] (required, overwritten).
+ *   dx: fp32 [L, B, d] (required, overwritten): the highway part
+ *       alpha (1 - r) dh summed over directions.  The part through the
+ *       projection comes from sru_project(SRU_PROJ_BWD_DATA, accumulate = 1).
+ *   dv, db: fp32 [ndir, 2, d] or NULL (overwritten; summed over t and b in
+ *       a fixed order, so results are bit-reproducible run to run).
+ *   dc0: fp32 [ndir, B, d] or NULL.
+ *   workspace: at least sru_workspace_size(shape, SRU_WS_BACKWARD, 0) bytes
+ *       of device memory, 256-byte aligned; its contents are scratch.
+ */
+sru_status sru_backward(const sru_shape *shape,
+                        const void *U, sru_dtype u_dt,
+                        const void *x, sru_dtype x_dt,
+                        const float *v, const float *b, const float *c0,
+                        const float *c_seq, const float *dh, const float *dc_last,
+                        float *dU, float *dx, float *dv, float *db, float *dc0,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Linear mode (v = v' = 0): f and r depend on U only, so c[t] =
+ * a[t] c[t-1] + (1 - a[t]) U[t,2] is a first-order linear recurrence and is
+ * evaluated as a scan over time chunks of `chunk` steps (per chunk: local scan
+ * and its aggregate, then the carry between chunks, then the chunk's outputs).
+ * The result equals the sequential recurrence up to rounding for any chunk.
+ * ("Parallelizing Legendre Memory Unit Training", abstract: linear recurrent
+ * components can be trained in parallel and run as an RNN at inference.)
+ *   pass = SRU_FWD: reads U, x, b, c0 (nullable); writes h (fp32), c_seq
+ *     (nullable), c_last (nullable).  dh .. dc0 must be NULL or are ignored.
+ *   pass = SRU_BWD: reads U, x, b, c0 (nullable), c_seq (required), dh
+ *     (required), dc_last (nullable); writes dU (required), dx (required,
+ *     highway part summed over directions), db (nullable), dc0 (nullable).
+ *     h and c_last are ignored.
+ *   chunk >= 1.  workspace: sru_workspace_size(shape, SRU_WS_LINEAR_FWD or
+ *   SRU_WS_LINEAR_BWD, chunk) bytes, 256-byte aligned.
+ */
+sru_status sru_linear_scan(const sru_shape *shape, sru_pass pass, int32_t chunk,
+                           const void *U, sru_dtype u_dt,
+                           const void *x, sru_dtype x_dt,
+                           const float *b, const float *c0,
+                           void *h, sru_dtype h_dt, float *c_seq, float *c_last,
+                           const float *dh, const float *dc_last,
+                           float *dU, float *dx, float *db, float *dc0,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes needed by `op` for `shape` (and `chunk` for the linear
+ * mode); 0 on invalid arguments (sru_last_error() says why). */
+size_t sru_workspace_size(const sru_shape *shape, sru_ws_op op, int32_t chunk);
+
+/* Static text for a status code. */
+const char *sru_status_string(sru_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *sru_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SRU_H_ */

@@ -85,7 +85,7 @@ float sru_oracle_round_bf16(float x)
  *   out[i][k] = sum_{q<K} Atilde[rows[i]][q] * W[cols[k]][q]
  * A is [M, K] row-major, W is [N, K] row-major (row n = output feature n).
  * Atilde = bf16-rounded A when round_a != 0, else A.  Sum in double, q in
- * increasing order.
+ * increasing order.  Rows are independent and are spread over threads.
  */
 void sru_oracle_project(int64_t M, int64_t N, int64_t K,
                         const float *A, int round_a, const float *W,
@@ -94,17 +94,23 @@ void sru_oracle_project(int64_t M, int64_t N, int64_t K,
                         double *out)
 {
     (void)M; (void)N;
-    for (int64_t i = 0; i < n_rows; ++i) {
-        const float *a = A + rows[i] * K;
-        for (int64_t k = 0; k < n_cols; ++k) {
-            const float *w = W + cols[k] * K;
-            double s = 0.0;
-            for (int64_t q = 0; q < K; ++q) {
-                double av = round_a ? (double)sru_oracle_round_bf16(a[q]) : (double)a[q];
-                s += av * (double)w[q];
+#pragma omp parallel
+    {
+        double *arow = (double *)malloc(sizeof(double) * (size_t)K);
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < n_rows; ++i) {
+            const float *a = A + rows[i] * K;
+            for (int64_t q = 0; q < K; ++q)
+                arow[q] = round_a ? (double)sru_oracle_round_bf16(a[q]) : (double)a[q];
+            for (int64_t k = 0; k < n_cols; ++k) {
+                const float *w = W + cols[k] * K;
+                double s = 0.0;
+                for (int64_t q = 0; q < K; ++q)
+                    s += arow[q] * (double)w[q];
+                out[i * n_cols + k] = s;
             }
-            out[i * n_cols + k] = s;
         }
+        free(arow);
     }
 }
 
@@ -119,13 +125,17 @@ void sru_oracle_project_bwd_data(int64_t M, int64_t N, int64_t K,
                                  double *out)
 {
     (void)M;
+    /* for every q the terms are added in increasing n */
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n_rows; ++i) {
         const double *g = G + rows[i] * N;
-        for (int64_t q = 0; q < K; ++q) {
-            double s = 0.0;
-            for (int64_t n = 0; n < N; ++n)
-                s += g[n] * (double)W[n * K + q];
-            out[i * K + q] = s;
+        double *o = out + i * K;
+        for (int64_t q = 0; q < K; ++q)
+            o[q] = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const float *w = W + n * K;
+            for (int64_t q = 0; q < K; ++q)
+                o[q] += g[n] * (double)w[q];
         }
     }
 }

@@ -1,0 +1,16 @@
+"""One Simple Recurrent Unit layer's hot path on MI355X (gfx950).
+
+The computation is that of Lei, "When Attention Meets Fast Recurrence"
+(SRU background section, Eqs. 1-5): one projection GEMM followed by a fused
+elementwise recurrence, plus its backward pass and a linear (v = 0) mode
+evaluated as a time-chunked scan.  All of it runs in the HIP kernels of
+``libsru.so`` behind the C ABI in ``include/sru.h``; this package only binds
+that ABI (``_binding``), allocates outputs for convenience (``layer``) and
+draws seeded synthetic inputs (``workloads``).
+"""
+from ._binding import (  # noqa: F401
+    EXPORTED, LIB_PATH, SRU_BF16, SRU_BWD, SRU_ERR_INVALID_ARG, SRU_ERR_LAUNCH,
+    SRU_ERR_NO_DEVICE, SRU_ERR_UNSUPPORTED, SRU_ERR_WORKSPACE, SRU_F32, SRU_FWD, SRU_OK,
+    SRU_PROJ_BWD_DATA, SRU_PROJ_FWD, SRU_WS_BACKWARD, SRU_WS_LINEAR_BWD, SRU_WS_LINEAR_FWD,
+    SruError, SruShape, load_library, sru_backward, sru_forward, sru_linear_scan, sru_project,
+    sru_workspace_size)

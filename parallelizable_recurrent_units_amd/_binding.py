@@ -1,0 +1,171 @@
+"""ctypes binding of libsru (include/sru.h): argument marshalling only.
+
+Every function here has the name of the C entry point it calls and forwards
+torch tensors as raw device pointers plus the caller's current HIP stream.
+All arithmetic runs in the library's HIP kernels; there is no fallback: if
+libsru.so is missing, importing the functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsru.so")
+
+SRU_OK, SRU_ERR_INVALID_ARG, SRU_ERR_UNSUPPORTED = 0, 1, 2
+SRU_ERR_NO_DEVICE, SRU_ERR_LAUNCH, SRU_ERR_WORKSPACE = 3, 4, 5
+SRU_F32, SRU_BF16 = 0, 1
+SRU_FWD, SRU_BWD = 0, 1
+SRU_PROJ_FWD, SRU_PROJ_BWD_DATA = 0, 1
+SRU_WS_BACKWARD, SRU_WS_LINEAR_FWD, SRU_WS_LINEAR_BWD = 1, 2, 3
+
+# Every symbol include/sru.h declares.
+EXPORTED = ("sru_project", "sru_forward", "sru_backward", "sru_linear_scan",
+            "sru_workspace_size", "sru_status_string", "sru_last_error")
+
+
+class SruShape(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int64), ("B", ctypes.c_int64), ("d", ctypes.c_int64),
+                ("bidirectional", ctypes.c_int32), ("alpha", ctypes.c_float)]
+
+    def __init__(self, L, B, d, bidirectional=False, alpha=1.0):
+        super().__init__(int(L), int(B), int(d), int(bool(bidirectional)), float(alpha))
+
+    @property
+    def ndir(self) -> int:
+        return 2 if self.bidirectional else 1
+
+    def __repr__(self):
+        return (f"SruShape(L={self.L}, B={self.B}, d={self.d}, "
+                f"bidirectional={bool(self.bidirectional)}, alpha={self.alpha})")
+
+
+class SruError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name}: {detail}")
+        self.status = status
+
+
+_lib = None
+_vp = ctypes.c_void_p
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libsru.so once.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m parallelizable_recurrent_units_amd.build`")
+    lib = ctypes.CDLL(path)
+    sp = ctypes.POINTER(SruShape)
+    i32, sz = ctypes.c_int32, ctypes.c_size_t
+    lib.sru_project.restype = ctypes.c_int
+    lib.sru_project.argtypes = [sp, ctypes.c_int, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp,
+                                ctypes.c_int, i32, _vp]
+    lib.sru_forward.restype = ctypes.c_int
+    lib.sru_forward.argtypes = [sp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                ctypes.c_int, _vp, _vp, _vp]
+    lib.sru_backward.restype = ctypes.c_int
+    lib.sru_backward.argtypes = [sp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp]
+    lib.sru_linear_scan.restype = ctypes.c_int
+    lib.sru_linear_scan.argtypes = [sp, ctypes.c_int, i32, _vp, ctypes.c_int, _vp, ctypes.c_int,
+                                    _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _vp, _vp, _vp, sz, _vp]
+    lib.sru_workspace_size.restype = sz
+    lib.sru_workspace_size.argtypes = [sp, ctypes.c_int, i32]
+    lib.sru_status_string.restype = ctypes.c_char_p
+    lib.sru_status_string.argtypes = [ctypes.c_int]
+    lib.sru_last_error.restype = ctypes.c_char_p
+    lib.sru_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != SRU_OK:
+        lib = load_library()
+        raise SruError(status, lib.sru_status_string(status).decode(),
+                       lib.sru_last_error().decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return SRU_F32
+    if t.dtype == torch.bfloat16:
+        return SRU_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libsru must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libsru must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _shape(shape) -> SruShape:
+    return shape if isinstance(shape, SruShape) else SruShape(*shape)
+
+
+def sru_workspace_size(shape, op: int, chunk: int = 0) -> int:
+    s = _shape(shape)
+    n = load_library().sru_workspace_size(ctypes.byref(s), int(op), int(chunk))
+    if n == 0:
+        raise SruError(SRU_ERR_INVALID_ARG, "SRU_ERR_INVALID_ARG",
+                       load_library().sru_last_error().decode())
+    return int(n)
+
+
+def sru_project(shape, op: int, A, W, C, accumulate: bool = False, stream=None):
+    s = _shape(shape)
+    _check(load_library().sru_project(ctypes.byref(s), int(op), _ptr(A), _dtype_code(A),
+                                      _ptr(W), _dtype_code(W), _ptr(C), _dtype_code(C),
+                                      int(bool(accumulate)), _stream(stream)))
+
+
+def sru_forward(shape, U, x, v, b, c0, h, c_seq=None, c_last=None, stream=None):
+    s = _shape(shape)
+    _check(load_library().sru_forward(ctypes.byref(s), _ptr(U), _dtype_code(U), _ptr(x),
+                                      _dtype_code(x), _ptr(v), _ptr(b), _ptr(c0), _ptr(h),
+                                      _dtype_code(h), _ptr(c_seq), _ptr(c_last),
+                                      _stream(stream)))
+
+
+def sru_backward(shape, U, x, v, b, c0, c_seq, dh, dc_last, dU, dx, dv, db, dc0,
+                 workspace, stream=None):
+    s = _shape(shape)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().sru_backward(ctypes.byref(s), _ptr(U), _dtype_code(U), _ptr(x),
+                                       _dtype_code(x), _ptr(v), _ptr(b), _ptr(c0), _ptr(c_seq),
+                                       _ptr(dh), _ptr(dc_last), _ptr(dU), _ptr(dx), _ptr(dv),
+                                       _ptr(db), _ptr(dc0), _ptr(workspace), ws_bytes,
+                                       _stream(stream)))
+
+
+def sru_linear_scan(shape, pass_: int, chunk: int, U, x, b, c0, h=None, c_seq=None,
+                    c_last=None, dh=None, dc_last=None, dU=None, dx=None, db=None, dc0=None,
+                    workspace=None, stream=None):
+    s = _shape(shape)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    h_dt = _dtype_code(h) if h is not None else SRU_F32
+    _check(load_library().sru_linear_scan(
+        ctypes.byref(s), int(pass_), int(chunk), _ptr(U), _dtype_code(U), _ptr(x),
+        _dtype_code(x), _ptr(b), _ptr(c0), _ptr(h), h_dt, _ptr(c_seq), _ptr(c_last),
+        _ptr(dh), _ptr(dc_last), _ptr(dU), _ptr(dx), _ptr(db), _ptr(dc0), _ptr(workspace),
+        ws_bytes, _stream(stream)))

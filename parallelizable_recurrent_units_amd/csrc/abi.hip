@@ -1,0 +1,377 @@
+// abi.hip -- the C entry points declared in include/sru.h: argument
+// validation, dtype dispatch, workspace sizing and launches on the caller's
+// stream.  Nothing here allocates device memory or synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/sru.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+sru_status fail(sru_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+sru_status ok()
+{
+    g_last_error[0] = '\0';
+    return SRU_OK;
+}
+
+constexpr int64_t kMaxElems = (int64_t)1 << 56;   // far below int64 overflow
+constexpr int64_t kMaxBlocks = ((int64_t)1 << 31) - 1;
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out)
+{
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > kMaxElems / a) return false;
+    *out = a * b;
+    return true;
+}
+
+// Validates the shape; fills ndir and the element counts used below.
+struct Dims {
+    int ndir;
+    int64_t LB, chains, u_elems;
+};
+
+sru_status check_shape(const sru_shape *s, Dims *dm)
+{
+    if (!s) return fail(SRU_ERR_INVALID_ARG, "shape is NULL");
+    if (s->L < 1 || s->B < 1 || s->d < 1)
+        return fail(SRU_ERR_INVALID_ARG, "L, B, d must be >= 1 (got L=%lld B=%lld d=%lld)",
+                    (long long)s->L, (long long)s->B, (long long)s->d);
+    if (s->bidirectional != 0 && s->bidirectional != 1)
+        return fail(SRU_ERR_INVALID_ARG, "bidirectional must be 0 or 1 (got %d)",
+                    (int)s->bidirectional);
+    if (!isfinite(s->alpha)) return fail(SRU_ERR_INVALID_ARG, "alpha must be finite");
+    dm->ndir = s->bidirectional ? 2 : 1;
+    int64_t lbd, x3;
+    if (!mul_ok(s->L, s->B, &dm->LB) || !mul_ok(dm->LB, s->d, &lbd) ||
+        !mul_ok(lbd, 3 * dm->ndir, &dm->u_elems) || !mul_ok(s->B, s->d, &x3))
+        return fail(SRU_ERR_INVALID_ARG, "tensor sizes overflow");
+    dm->chains = x3 * dm->ndir;
+    // the widest grids: one thread per chain (256 per block) and one wave
+    // per 64 chains; both far below the grid limit for any legal size here.
+    if ((dm->chains + 63) / 64 > kMaxBlocks)
+        return fail(SRU_ERR_INVALID_ARG, "too many chains for one launch");
+    return SRU_OK;
+}
+
+bool valid_dtype(int d) { return d == SRU_F32 || d == SRU_BF16; }
+
+sru_status need_ptr(const void *p, const char *name)
+{
+    if (!p) return fail(SRU_ERR_INVALID_ARG, "%s must not be NULL", name);
+    if (((uintptr_t)p) & 15u)
+        return fail(SRU_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+    return SRU_OK;
+}
+
+sru_status opt_ptr(const void *p, const char *name)
+{
+    if (p && (((uintptr_t)p) & 15u))
+        return fail(SRU_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+    return SRU_OK;
+}
+
+#define SRU_TRY(expr)                       \
+    do {                                    \
+        sru_status st_ = (expr);            \
+        if (st_ != SRU_OK) return st_;      \
+    } while (0)
+
+sru_status need_device()
+{
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess || n < 1) {
+        (void)hipGetLastError();
+        return fail(SRU_ERR_NO_DEVICE, "no HIP device available (%s)",
+                    e != hipSuccess ? hipGetErrorString(e) : "device count is 0");
+    }
+    return SRU_OK;
+}
+
+sru_status launched(hipError_t e, const char *what)
+{
+    if (e != hipSuccess) return fail(SRU_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t backward_ws(const sru_shape *s, const Dims &dm)
+{
+    return round256((size_t)dm.ndir * (size_t)s->B * 4 * (size_t)s->d * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sru_status_string(sru_status st)
+{
+    switch (st) {
+    case SRU_OK: return "SRU_OK";
+    case SRU_ERR_INVALID_ARG: return "SRU_ERR_INVALID_ARG";
+    case SRU_ERR_UNSUPPORTED: return "SRU_ERR_UNSUPPORTED";
+    case SRU_ERR_NO_DEVICE: return "SRU_ERR_NO_DEVICE";
+    case SRU_ERR_LAUNCH: return "SRU_ERR_LAUNCH";
+    case SRU_ERR_WORKSPACE: return "SRU_ERR_WORKSPACE";
+    }
+    return "SRU_ERR_UNKNOWN";
+}
+
+const char *sru_last_error(void) { return g_last_error; }
+
+size_t sru_workspace_size(const sru_shape *shape, sru_ws_op op, int32_t chunk)
+{
+    Dims dm;
+    if (check_shape(shape, &dm) != SRU_OK) return 0;
+    switch (op) {
+    case SRU_WS_BACKWARD:
+        ok();
+        return backward_ws(shape, dm);
+    case SRU_WS_LINEAR_FWD:
+    case SRU_WS_LINEAR_BWD:
+        if (chunk < 1) {
+            fail(SRU_ERR_INVALID_ARG, "chunk must be >= 1 (got %d)", (int)chunk);
+            return 0;
+        }
+        ok();
+        return round256(sru::linear_workspace_bytes(shape->L, shape->B, shape->d, dm.ndir,
+                                                    chunk, op == SRU_WS_LINEAR_BWD));
+    }
+    fail(SRU_ERR_INVALID_ARG, "unknown workspace op %d", (int)op);
+    return 0;
+}
+
+sru_status sru_project(const sru_shape *shape, sru_proj_op op, const void *A, sru_dtype a_dt,
+                       const void *W, sru_dtype w_dt, void *C, sru_dtype c_dt,
+                       int32_t accumulate, void *stream)
+{
+    Dims dm;
+    SRU_TRY(check_shape(shape, &dm));
+    if (op != SRU_PROJ_FWD && op != SRU_PROJ_BWD_DATA)
+        return fail(SRU_ERR_INVALID_ARG, "unknown projection op %d", (int)op);
+    if (!valid_dtype(a_dt) || !valid_dtype(w_dt) || !valid_dtype(c_dt))
+        return fail(SRU_ERR_INVALID_ARG, "unknown dtype");
+    if (accumulate != 0 && accumulate != 1)
+        return fail(SRU_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+    SRU_TRY(need_ptr(A, "A"));
+    SRU_TRY(need_ptr(W, "W"));
+    SRU_TRY(need_ptr(C, "C"));
+    if (c_dt != SRU_F32) return fail(SRU_ERR_UNSUPPORTED, "C must be fp32");
+    // grid: x over row tiles (>= 64 rows each), y over column tiles (<= 65535)
+    if ((dm.LB + 63) / 64 > kMaxBlocks || (3 * dm.ndir * shape->d + 63) / 64 > 65535)
+        return fail(SRU_ERR_INVALID_ARG, "matrix too large for one projection launch");
+    SRU_TRY(need_device());
+    const int64_t n3 = 3 * dm.ndir * shape->d;
+    sru::GemmArgs g;
+    g.M = dm.LB;
+    g.A = A;
+    g.a_bf16 = a_dt == SRU_BF16;
+    g.Bm = W;
+    g.b_bf16 = w_dt == SRU_BF16;
+    g.C = (float *)C;
+    g.accumulate = accumulate != 0;
+    if (op == SRU_PROJ_FWD) {
+        g.N = n3;
+        g.K = shape->d;
+        g.b_kn = false;
+    } else {
+        g.N = shape->d;
+        g.K = n3;
+        g.b_kn = true;
+    }
+    return launched(sru::launch_gemm(g, (hipStream_t)stream), "projection");
+}
+
+sru_status sru_forward(const sru_shape *shape, const void *U, sru_dtype u_dt, const void *x,
+                       sru_dtype x_dt, const float *v, const float *b, const float *c0, void *h,
+                       sru_dtype h_dt, float *c_seq, float *c_last, void *stream)
+{
+    Dims dm;
+    SRU_TRY(check_shape(shape, &dm));
+    if (!valid_dtype(u_dt) || !valid_dtype(x_dt) || !valid_dtype(h_dt))
+        return fail(SRU_ERR_INVALID_ARG, "unknown dtype");
+    SRU_TRY(need_ptr(U, "U"));
+    SRU_TRY(need_ptr(x, "x"));
+    SRU_TRY(need_ptr(v, "v"));
+    SRU_TRY(need_ptr(b, "b"));
+    SRU_TRY(opt_ptr(c0, "c0"));
+    SRU_TRY(need_ptr(h, "h"));
+    SRU_TRY(opt_ptr(c_seq, "c_seq"));
+    SRU_TRY(opt_ptr(c_last, "c_last"));
+    if (h_dt != SRU_F32) return fail(SRU_ERR_UNSUPPORTED, "h must be fp32");
+    SRU_TRY(need_device());
+    sru::RecArgs a{};
+    a.L = shape->L;
+    a.B = shape->B;
+    a.d = shape->d;
+    a.ndir = dm.ndir;
+    a.alpha = shape->alpha;
+    a.U = U;
+    a.u_bf16 = u_dt == SRU_BF16;
+    a.x = x;
+    a.x_bf16 = x_dt == SRU_BF16;
+    a.v = v;
+    a.b = b;
+    a.c0 = c0;
+    a.h = (float *)h;
+    a.c_seq = c_seq;
+    a.c_last = c_last;
+    return launched(sru::launch_forward(a, (hipStream_t)stream), "forward recurrence");
+}
+
+sru_status sru_backward(const sru_shape *shape, const void *U, sru_dtype u_dt, const void *x,
+                        sru_dtype x_dt, const float *v, const float *b, const float *c0,
+                        const float *c_seq, const float *dh, const float *dc_last, float *dU,
+                        float *dx, float *dv, float *db, float *dc0, void *workspace,
+                        size_t workspace_bytes, void *stream)
+{
+    Dims dm;
+    SRU_TRY(check_shape(shape, &dm));
+    if (!valid_dtype(u_dt) || !valid_dtype(x_dt))
+        return fail(SRU_ERR_INVALID_ARG, "unknown dtype");
+    SRU_TRY(need_ptr(U, "U"));
+    SRU_TRY(need_ptr(x, "x"));
+    SRU_TRY(need_ptr(v, "v"));
+    SRU_TRY(need_ptr(b, "b"));
+    SRU_TRY(opt_ptr(c0, "c0"));
+    SRU_TRY(need_ptr(c_seq, "c_seq"));
+    SRU_TRY(need_ptr(dh, "dh"));
+    SRU_TRY(opt_ptr(dc_last, "dc_last"));
+    SRU_TRY(need_ptr(dU, "dU"));
+    SRU_TRY(need_ptr(dx, "dx"));
+    SRU_TRY(opt_ptr(dv, "dv"));
+    SRU_TRY(opt_ptr(db, "db"));
+    SRU_TRY(opt_ptr(dc0, "dc0"));
+    const size_t need = backward_ws(shape, dm);
+    if (!workspace || workspace_bytes < need)
+        return fail(SRU_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need,
+                    workspace_bytes, workspace ? "" : ", NULL");
+    SRU_TRY(opt_ptr(workspace, "workspace"));
+    SRU_TRY(need_device());
+    sru::RecArgs a{};
+    a.L = shape->L;
+    a.B = shape->B;
+    a.d = shape->d;
+    a.ndir = dm.ndir;
+    a.alpha = shape->alpha;
+    a.U = U;
+    a.u_bf16 = u_dt == SRU_BF16;
+    a.x = x;
+    a.x_bf16 = x_dt == SRU_BF16;
+    a.v = v;
+    a.b = b;
+    a.c0 = c0;
+    a.c_seq_in = c_seq;
+    a.dh = dh;
+    a.dc_last = dc_last;
+    a.dU = dU;
+    a.dx = dx;
+    a.dc0 = dc0;
+    a.partials = (float *)workspace;
+    hipStream_t s = (hipStream_t)stream;
+    // The highway gradient of x sums both directions: the last direction
+    // writes dx, the ones before it add to it (stream order serialises them).
+    for (int dir = dm.ndir - 1; dir >= 0; --dir) {
+        a.dir = dir;
+        a.dx_accumulate = dir != dm.ndir - 1;
+        hipError_t e = sru::launch_backward_dir(a, s);
+        if (e != hipSuccess) return launched(e, "backward recurrence");
+    }
+    if (dv || db) {
+        hipError_t e = sru::launch_param_reduce(a.partials, shape->B, shape->d, dm.ndir, dv, db, s);
+        if (e != hipSuccess) return launched(e, "parameter-gradient reduction");
+    }
+    return ok();
+}
+
+sru_status sru_linear_scan(const sru_shape *shape, sru_pass pass, int32_t chunk, const void *U,
+                           sru_dtype u_dt, const void *x, sru_dtype x_dt, const float *b,
+                           const float *c0, void *h, sru_dtype h_dt, float *c_seq, float *c_last,
+                           const float *dh, const float *dc_last, float *dU, float *dx, float *db,
+                           float *dc0, void *workspace, size_t workspace_bytes, void *stream)
+{
+    Dims dm;
+    SRU_TRY(check_shape(shape, &dm));
+    if (pass != SRU_FWD && pass != SRU_BWD)
+        return fail(SRU_ERR_INVALID_ARG, "unknown pass %d", (int)pass);
+    if (chunk < 1) return fail(SRU_ERR_INVALID_ARG, "chunk must be >= 1 (got %d)", (int)chunk);
+    if (!valid_dtype(u_dt) || !valid_dtype(x_dt))
+        return fail(SRU_ERR_INVALID_ARG, "unknown dtype");
+    SRU_TRY(need_ptr(U, "U"));
+    SRU_TRY(need_ptr(x, "x"));
+    SRU_TRY(need_ptr(b, "b"));
+    SRU_TRY(opt_ptr(c0, "c0"));
+    const int64_t nC = (shape->L + chunk - 1) / chunk;
+    int64_t lanes;
+    if (!mul_ok(nC, shape->B * shape->d, &lanes) || (lanes + 255) / 256 > kMaxBlocks)
+        return fail(SRU_ERR_INVALID_ARG, "too many (chain, chunk) pairs for one launch");
+    const bool bwd = pass == SRU_BWD;
+    if (!bwd) {
+        if (!valid_dtype(h_dt)) return fail(SRU_ERR_INVALID_ARG, "unknown dtype");
+        SRU_TRY(need_ptr(h, "h"));
+        SRU_TRY(opt_ptr(c_seq, "c_seq"));
+        SRU_TRY(opt_ptr(c_last, "c_last"));
+        if (h_dt != SRU_F32) return fail(SRU_ERR_UNSUPPORTED, "h must be fp32");
+    } else {
+        SRU_TRY(need_ptr(c_seq, "c_seq"));
+        SRU_TRY(need_ptr(dh, "dh"));
+        SRU_TRY(opt_ptr(dc_last, "dc_last"));
+        SRU_TRY(need_ptr(dU, "dU"));
+        SRU_TRY(need_ptr(dx, "dx"));
+        SRU_TRY(opt_ptr(db, "db"));
+        SRU_TRY(opt_ptr(dc0, "dc0"));
+    }
+    const size_t need = round256(sru::linear_workspace_bytes(shape->L, shape->B, shape->d,
+                                                             dm.ndir, chunk, bwd));
+    if (!workspace || workspace_bytes < need)
+        return fail(SRU_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need,
+                    workspace_bytes, workspace ? "" : ", NULL");
+    SRU_TRY(opt_ptr(workspace, "workspace"));
+    SRU_TRY(need_device());
+    sru::LinArgs a{};
+    a.L = shape->L;
+    a.B = shape->B;
+    a.d = shape->d;
+    a.ndir = dm.ndir;
+    a.alpha = shape->alpha;
+    a.chunk = chunk;
+    a.U = U;
+    a.u_bf16 = u_dt == SRU_BF16;
+    a.x = x;
+    a.x_bf16 = x_dt == SRU_BF16;
+    a.b = b;
+    a.c0 = c0;
+    a.ws = workspace;
+    if (!bwd) {
+        a.h = (float *)h;
+        a.c_seq = c_seq;
+        a.c_last = c_last;
+        return launched(sru::launch_linear_forward(a, (hipStream_t)stream), "linear scan forward");
+    }
+    a.c_seq = c_seq;
+    a.dh = dh;
+    a.dc_last = dc_last;
+    a.dU = dU;
+    a.dx = dx;
+    a.db = db;
+    a.dc0 = dc0;
+    return launched(sru::launch_linear_backward(a, (hipStream_t)stream), "linear scan backward");
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// internal.h -- launcher interfaces between the C-ABI layer and the kernels.
+// Host-side only types; nothing here is part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sru {
+
+// Arguments of the forward / backward recurrence launchers.  Element counts
+// and offsets are int64; layouts are those of include/sru.h.
+struct RecArgs {
+    int64_t L, B, d;
+    int ndir;
+    float alpha;
+    const void *U;
+    bool u_bf16;
+    const void *x;
+    bool x_bf16;
+    const float *v, *b, *c0;
+    // forward outputs
+    float *h, *c_seq, *c_last;
+    // backward
+    const float *c_seq_in, *dh, *dc_last;
+    float *dU, *dx, *dc0;
+    float *partials;     // [ndir, B, 4, d] per-chain sums over t
+    int dir;             // backward: the one direction this launch walks
+    bool dx_accumulate;  // backward: add to dx instead of overwriting
+};
+
+hipError_t launch_forward(const RecArgs &a, hipStream_t s);
+// One direction per call (a.dir); writes dU, dx (overwrite or accumulate),
+// dc0 and the per-chain parameter-gradient partials.
+hipError_t launch_backward_dir(const RecArgs &a, hipStream_t s);
+// dv, db [ndir, 2, d] = sum over b (increasing) of partials.
+hipError_t launch_param_reduce(const float *partials, int64_t B, int64_t d, int ndir,
+                               float *dv, float *db, hipStream_t s);
+
+struct LinArgs {
+    int64_t L, B, d;
+    int ndir;
+    float alpha;
+    int64_t chunk;
+    const void *U;
+    bool u_bf16;
+    const void *x;
+    bool x_bf16;
+    const float *b, *c0;
+    float *h, *c_seq, *c_last;
+    const float *dh, *dc_last;
+    float *dU, *dx, *db, *dc0;
+    void *ws;
+};
+
+size_t linear_workspace_bytes(int64_t L, int64_t B, int64_t d, int ndir, int64_t chunk,
+                              bool backward);
+hipError_t launch_linear_forward(const LinArgs &a, hipStream_t s);
+hipError_t launch_linear_backward(const LinArgs &a, hipStream_t s);
+
+// C[M, N] (+)= A[M, K] . op(B)
+//   b_kn = false: B stored [N, K] (C = A B^T)     -- projection forward
+//   b_kn = true : B stored [K, N] (C = A B)       -- projection backward-data
+struct GemmArgs {
+    int64_t M, N, K;
+    const void *A;
+    bool a_bf16;
+    const void *Bm;
+    bool b_bf16;
+    bool b_kn;
+    float *C;
+    bool accumulate;
+};
+
+hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
+
+}  // namespace sru

@@ -1,0 +1,86 @@
+"""Convenience wrappers: allocate outputs with torch, then call the C ABI.
+
+Each function is a single entry point (or a fixed sequence of them) of
+libsru; no arithmetic happens here.  Layouts are those of include/sru.h.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _binding as B
+
+
+def project(shape, X, W, U=None, accumulate=False, stream=None):
+    """Eq. 1: U[L*B, ndir*3d] (+)= X W^T (X rounded to bf16 when W is bf16)."""
+    s = B._shape(shape)
+    if U is None:
+        U = torch.empty((s.L, s.B, s.ndir, 3, s.d), device=X.device, dtype=torch.float32)
+    B.sru_project(s, B.SRU_PROJ_FWD, X, W, U, accumulate, stream)
+    return U
+
+
+def project_bwd_data(shape, dU, W, dX=None, accumulate=False, stream=None):
+    """dX[L*B, d] (+)= dU W (gradient through Eq. 1)."""
+    s = B._shape(shape)
+    if dX is None:
+        dX = torch.empty((s.L, s.B, s.d), device=dU.device, dtype=torch.float32)
+    B.sru_project(s, B.SRU_PROJ_BWD_DATA, dU, W, dX, accumulate, stream)
+    return dX
+
+
+def forward(shape, U, x, v, b, c0=None, keep_c_seq=False, stream=None):
+    s = B._shape(shape)
+    dev = U.device
+    h = torch.empty((s.L, s.B, s.ndir, s.d), device=dev, dtype=torch.float32)
+    c_seq = (torch.empty((s.L, s.B, s.ndir, s.d), device=dev, dtype=torch.float32)
+             if keep_c_seq else None)
+    c_last = torch.empty((s.ndir, s.B, s.d), device=dev, dtype=torch.float32)
+    B.sru_forward(s, U, x, v, b, c0, h, c_seq, c_last, stream)
+    return h, c_seq, c_last
+
+
+def workspace(shape, op, chunk=0, device="cuda"):
+    n = B.sru_workspace_size(shape, op, chunk)
+    return torch.empty(n, device=device, dtype=torch.uint8)
+
+
+def backward(shape, U, x, v, b, c0, c_seq, dh, dc_last=None, ws=None, stream=None):
+    s = B._shape(shape)
+    dev = U.device
+    dU = torch.empty((s.L, s.B, s.ndir, 3, s.d), device=dev, dtype=torch.float32)
+    dx = torch.empty((s.L, s.B, s.d), device=dev, dtype=torch.float32)
+    dv = torch.empty((s.ndir, 2, s.d), device=dev, dtype=torch.float32)
+    db = torch.empty((s.ndir, 2, s.d), device=dev, dtype=torch.float32)
+    dc0 = torch.empty((s.ndir, s.B, s.d), device=dev, dtype=torch.float32)
+    if ws is None:
+        ws = workspace(s, B.SRU_WS_BACKWARD, 0, dev)
+    B.sru_backward(s, U, x, v, b, c0, c_seq, dh, dc_last, dU, dx, dv, db, dc0, ws, stream)
+    return dU, dx, dv, db, dc0
+
+
+def linear_forward(shape, chunk, U, x, b, c0=None, keep_c_seq=True, ws=None, stream=None):
+    s = B._shape(shape)
+    dev = U.device
+    h = torch.empty((s.L, s.B, s.ndir, s.d), device=dev, dtype=torch.float32)
+    c_seq = (torch.empty((s.L, s.B, s.ndir, s.d), device=dev, dtype=torch.float32)
+             if keep_c_seq else None)
+    c_last = torch.empty((s.ndir, s.B, s.d), device=dev, dtype=torch.float32)
+    if ws is None:
+        ws = workspace(s, B.SRU_WS_LINEAR_FWD, chunk, dev)
+    B.sru_linear_scan(s, B.SRU_FWD, chunk, U, x, b, c0, h=h, c_seq=c_seq, c_last=c_last,
+                      workspace=ws, stream=stream)
+    return h, c_seq, c_last
+
+
+def linear_backward(shape, chunk, U, x, b, c0, c_seq, dh, dc_last=None, ws=None, stream=None):
+    s = B._shape(shape)
+    dev = U.device
+    dU = torch.empty((s.L, s.B, s.ndir, 3, s.d), device=dev, dtype=torch.float32)
+    dx = torch.empty((s.L, s.B, s.d), device=dev, dtype=torch.float32)
+    db = torch.empty((s.ndir, 2, s.d), device=dev, dtype=torch.float32)
+    dc0 = torch.empty((s.ndir, s.B, s.d), device=dev, dtype=torch.float32)
+    if ws is None:
+        ws = workspace(s, B.SRU_WS_LINEAR_BWD, chunk, dev)
+    B.sru_linear_scan(s, B.SRU_BWD, chunk, U, x, b, c0, c_seq=c_seq, dh=dh, dc_last=dc_last,
+                      dU=dU, dx=dx, db=db, dc0=dc0, workspace=ws, stream=stream)
+    return dU, dx, db, dc0

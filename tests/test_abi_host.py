@@ -1,0 +1,153 @@
+"""Host-side checks of the C ABI (CPU only; no kernel is ever launched here).
+
+* libsru.so loads and exports every function include/sru.h declares;
+* workspace sizes follow their stated formulas;
+* every validation path returns its status before touching a device;
+* a valid call on a machine without a GPU returns SRU_ERR_NO_DEVICE.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import parallelizable_recurrent_units_amd as sru
+from parallelizable_recurrent_units_amd import _binding as Bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(Bd.LIB_PATH):
+        from parallelizable_recurrent_units_amd import build
+        build.build()
+    return sru.load_library()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "sru.h")).read()
+    return sorted(set(re.findall(r"\b(sru_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert declared == sorted(Bd.EXPORTED)
+    for name in declared:
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings(lib):
+    for code, name in [(0, "SRU_OK"), (1, "SRU_ERR_INVALID_ARG"), (2, "SRU_ERR_UNSUPPORTED"),
+                       (3, "SRU_ERR_NO_DEVICE"), (4, "SRU_ERR_LAUNCH"), (5, "SRU_ERR_WORKSPACE")]:
+        assert lib.sru_status_string(code).decode() == name
+
+
+def round256(n):
+    return (n + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("L,B,d,bi", [(4, 2, 64, 0), (7, 3, 5, 1), (16384, 4, 4096, 0)])
+def test_workspace_sizes(lib, L, B, d, bi):
+    s = sru.SruShape(L, B, d, bi, 1.0)
+    nd = 2 if bi else 1
+    assert sru.sru_workspace_size(s, sru.SRU_WS_BACKWARD) == round256(nd * B * 4 * d * 4)
+    for chunk in (1, 7, 256):
+        nC = -(-L // chunk)
+        assert sru.sru_workspace_size(s, sru.SRU_WS_LINEAR_FWD, chunk) == round256(3 * nC * B * d * 4)
+        assert sru.sru_workspace_size(s, sru.SRU_WS_LINEAR_BWD, chunk) == round256(5 * nC * B * d * 4)
+    assert lib.sru_workspace_size(ctypes.byref(s), sru.SRU_WS_LINEAR_FWD, 0) == 0
+    assert b"chunk" in lib.sru_last_error()
+    assert lib.sru_workspace_size(ctypes.byref(s), 9, 1) == 0
+
+
+# Fake, 16-byte aligned "device" addresses: validation fails before any use.
+P = [0x10000 * (i + 1) for i in range(24)]
+
+
+def fwd(lib, s, **kw):
+    a = dict(U=P[0], u_dt=0, x=P[1], x_dt=0, v=P[2], b=P[3], c0=None, h=P[4], h_dt=0,
+             c_seq=None, c_last=None)
+    a.update(kw)
+    return lib.sru_forward(ctypes.byref(s) if s is not None else None, a["U"], a["u_dt"],
+                           a["x"], a["x_dt"], a["v"], a["b"], a["c0"], a["h"], a["h_dt"],
+                           a["c_seq"], a["c_last"], None)
+
+
+def bwd(lib, s, ws_bytes, **kw):
+    a = dict(U=P[0], x=P[1], v=P[2], b=P[3], c0=None, c_seq=P[5], dh=P[6], dc_last=None,
+             dU=P[7], dx=P[8], dv=None, db=None, dc0=None, ws=P[9])
+    a.update(kw)
+    return lib.sru_backward(ctypes.byref(s), a["U"], 0, a["x"], 0, a["v"], a["b"], a["c0"],
+                            a["c_seq"], a["dh"], a["dc_last"], a["dU"], a["dx"], a["dv"],
+                            a["db"], a["dc0"], a["ws"], ws_bytes, None)
+
+
+def lin(lib, s, pass_, chunk, ws_bytes, **kw):
+    a = dict(U=P[0], x=P[1], b=P[3], c0=None, h=P[4], h_dt=0, c_seq=P[5], c_last=None,
+             dh=P[6], dc_last=None, dU=P[7], dx=P[8], db=None, dc0=None, ws=P[9])
+    a.update(kw)
+    return lib.sru_linear_scan(ctypes.byref(s), pass_, chunk, a["U"], 0, a["x"], 0, a["b"],
+                               a["c0"], a["h"], a["h_dt"], a["c_seq"], a["c_last"], a["dh"],
+                               a["dc_last"], a["dU"], a["dx"], a["db"], a["dc0"], a["ws"],
+                               ws_bytes, None)
+
+
+def test_invalid_shapes(lib):
+    assert fwd(lib, None) == sru.SRU_ERR_INVALID_ARG
+    for L, B, d, bi, al in [(0, 1, 1, 0, 1.0), (1, 0, 1, 0, 1.0), (1, 1, 0, 0, 1.0),
+                            (1, 1, 1, 2, 1.0), (1, 1, 1, 0, float("inf")),
+                            (1, 1, 1, 0, float("nan")), (-3, 1, 1, 0, 1.0),
+                            (1 << 40, 1 << 20, 1 << 10, 0, 1.0)]:
+        s = Bd.SruShape.__new__(Bd.SruShape)
+        ctypes.Structure.__init__(s, L, B, d, bi, al)
+        assert fwd(lib, s) == sru.SRU_ERR_INVALID_ARG, (L, B, d, bi, al)
+
+
+def test_invalid_pointers_and_codes(lib):
+    s = sru.SruShape(8, 2, 64, 0, 1.0)
+    assert fwd(lib, s, U=None) == sru.SRU_ERR_INVALID_ARG
+    assert b"U" in lib.sru_last_error()
+    assert fwd(lib, s, h=None) == sru.SRU_ERR_INVALID_ARG
+    assert fwd(lib, s, x=P[1] + 4) == sru.SRU_ERR_INVALID_ARG       # misaligned
+    assert b"aligned" in lib.sru_last_error()
+    assert fwd(lib, s, c0=P[10] + 8) == sru.SRU_ERR_INVALID_ARG
+    assert fwd(lib, s, u_dt=7) == sru.SRU_ERR_INVALID_ARG
+    assert fwd(lib, s, h_dt=1) == sru.SRU_ERR_UNSUPPORTED
+    # projection
+    assert lib.sru_project(ctypes.byref(s), 5, P[0], 0, P[1], 1, P[2], 0, 0, None) == 1
+    assert lib.sru_project(ctypes.byref(s), 0, P[0], 0, P[1], 1, P[2], 1, 0, None) == 2
+    assert lib.sru_project(ctypes.byref(s), 0, P[0], 0, P[1], 1, P[2], 0, 3, None) == 1
+    assert lib.sru_project(ctypes.byref(s), 0, None, 0, P[1], 1, P[2], 0, 0, None) == 1
+
+
+def test_workspace_errors(lib):
+    s = sru.SruShape(8, 2, 64, 1, 1.0)
+    need = sru.sru_workspace_size(s, sru.SRU_WS_BACKWARD)
+    assert bwd(lib, s, need - 1) == sru.SRU_ERR_WORKSPACE
+    assert bwd(lib, s, need, ws=None) == sru.SRU_ERR_WORKSPACE
+    assert bwd(lib, s, need, c_seq=None) == sru.SRU_ERR_INVALID_ARG
+    assert bwd(lib, s, need, dU=None) == sru.SRU_ERR_INVALID_ARG
+    lneed = sru.sru_workspace_size(s, sru.SRU_WS_LINEAR_BWD, 4)
+    assert lin(lib, s, 1, 4, lneed - 256) == sru.SRU_ERR_WORKSPACE
+    assert lin(lib, s, 1, 0, lneed) == sru.SRU_ERR_INVALID_ARG
+    assert lin(lib, s, 2, 4, lneed) == sru.SRU_ERR_INVALID_ARG
+    assert lin(lib, s, 1, 4, lneed, dh=None) == sru.SRU_ERR_INVALID_ARG
+    assert lin(lib, s, 0, 4, lneed, h=None) == sru.SRU_ERR_INVALID_ARG
+    assert lin(lib, s, 0, 4, lneed, h_dt=1) == sru.SRU_ERR_UNSUPPORTED
+
+
+def test_binding_raises_sru_error(lib):
+    s = sru.SruShape(8, 2, 64, 0, 1.0)
+    with pytest.raises(sru.SruError) as ei:
+        sru.sru_workspace_size(s, 42)
+    assert ei.value.status == sru.SRU_ERR_INVALID_ARG
+
+
+def test_no_device_status_without_gpu(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible; this check is for GPU-less hosts")
+    s = sru.SruShape(8, 2, 64, 0, 1.0)
+    assert fwd(lib, s) == sru.SRU_ERR_NO_DEVICE
+    assert b"no HIP device" in lib.sru_last_error()

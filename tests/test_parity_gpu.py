@@ -1,0 +1,245 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Tolerances (normwise relative error, max|gpu - oracle| / max|oracle|, per
+output tensor):
+  * 1e-5 for everything computed from fp32 (or exactly-widened bf16) inputs
+    by the fp32 recurrence, and for the fp32 projection;
+  * 2e-2 for anything downstream of a bf16-input projection when compared
+    with the oracle evaluated on the UNROUNDED fp32 input (the bar for
+    bf16-input projections);
+  * 1e-4 for the same outputs compared with the oracle evaluated on the
+    bf16-rounded input the kernel actually multiplies: the only difference
+    left is the GEMM's fp32 accumulation (K <= 3072 terms, unit roundoff
+    2^-24: K u = 1.8e-4 worst case, ~sqrt(K) u = 3e-6 typical);
+  * 1e-2 for dX = dU W against the unrounded oracle at the tight stage: the
+    backward-data GEMM rounds dU to bf16 (relative 2^-9 = 2e-3 per element).
+Inputs are drawn by the seeded generators in
+parallelizable_recurrent_units_amd/workloads.py; no oracle input or expected
+value comes from the GPU.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from parallelizable_recurrent_units_amd import (SRU_PROJ_BWD_DATA, SRU_PROJ_FWD, SruShape,
+                                                layer, sru_project, workloads)
+from tests.gpu_util import check, dev_inputs, host
+
+pytestmark = pytest.mark.gpu
+
+TIGHT = 1e-5
+BF16_BAR = 2e-2
+GEMM_ACC = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU parity tests need a GPU"
+    yield
+    torch.cuda.synchronize()
+
+
+def run_fwd_bwd(shape, t, keep=True, with_bwd=True):
+    h, c_seq, c_last = layer.forward(shape, t["U"], t["x"], t["v"], t["b"], t.get("c0"),
+                                     keep_c_seq=keep)
+    out = {"h": h, "c_seq": c_seq, "c_last": c_last}
+    if with_bwd:
+        dU, dx, dv, db, dc0 = layer.backward(shape, t["U"], t["x"], t["v"], t["b"], t.get("c0"),
+                                             c_seq, t["dh"], t.get("dc_last"))
+        out.update(dU=dU, dx=dx, dv=dv, db=db, dc0=dc0)
+    return out
+
+
+def oracle_fwd_bwd(inp, alpha, with_bwd=True, U=None):
+    U = inp["U"] if U is None else U
+    fo = oracle.forward(U, inp["x"], inp["v"], inp["b"], inp.get("c0"), alpha)
+    if not with_bwd:
+        return fo, None
+    bo = oracle.backward(U, inp["x"], inp["v"], inp["b"], inp.get("c0"), fo["c"], inp["dh"],
+                         inp.get("dc_last"), alpha)
+    return fo, bo
+
+
+# ---------------------------------------------------------------------------
+# recurrence on a given U (fp32), small shapes: fast and generic paths, odd L,
+# both directions, c0, dc_last, b, alpha all non-trivial
+# ---------------------------------------------------------------------------
+CASES_F32 = [
+    # L, B, d, ndir
+    (1, 1, 1, 1),
+    (5, 3, 7, 2),
+    (2, 2, 64, 2),
+    (33, 2, 64, 1),
+    (17, 3, 128, 2),
+    (40, 1, 192, 1),
+    (64, 2, 200, 2),
+    (100, 2, 64, 1),
+]
+
+
+@pytest.mark.parametrize("L,B,d,nd", CASES_F32)
+def test_recurrence_fp32_given_u(L, B, d, nd):
+    w = workloads.custom(L, B, d, ndir=nd, alpha=1.7, mode="given_u", c0="normal0.1")
+    inp = workloads.make_inputs(w, seed=1000 + L + d, dc_last=True, v_scale=0.5, b_scale=0.3)
+    shape = SruShape(L, B, d, nd == 2, w.alpha)
+    print(f"case L={L} B={B} d={d} ndir={nd}", flush=True)
+    g = run_fwd_bwd(shape, dev_inputs(inp))
+    fo, bo = oracle_fwd_bwd(inp, w.alpha)
+    for k in ("h", "c_last"):
+        check(k, host(g[k]), fo[k], TIGHT)
+    check("c_seq", host(g["c_seq"]), fo["c"], TIGHT)
+    check("dU", host(g["dU"]), bo["dU"], TIGHT)
+    check("dx", host(g["dx"]), bo["dx_hw"], TIGHT)
+    for k in ("dv", "db", "dc0"):
+        check(k, host(g[k]), bo[k], TIGHT)
+
+
+@pytest.mark.parametrize("L,B,d,nd,xdt", [(37, 2, 128, 1, "bf16"), (8, 3, 64, 2, "bf16"),
+                                          (9, 2, 70, 1, "bf16"), (12, 2, 64, 1, "f32")])
+def test_recurrence_bf16_u(L, B, d, nd, xdt):
+    """bf16 U (and x): the fast two-steps-per-packet path and the generic one."""
+    w = workloads.custom(L, B, d, ndir=nd, alpha=1.3, mode="given_u", u_dtype="bf16",
+                         x_dtype=xdt, c0="normal0.1")
+    inp = workloads.make_inputs(w, seed=2000 + L, dc_last=True, v_scale=0.4, b_scale=0.2)
+    shape = SruShape(L, B, d, nd == 2, w.alpha)
+    print(f"case L={L} B={B} d={d} ndir={nd} x={xdt}", flush=True)
+    g = run_fwd_bwd(shape, dev_inputs(inp))
+    fo, bo = oracle_fwd_bwd(inp, w.alpha)
+    check("h", host(g["h"]), fo["h"], TIGHT)
+    check("c_seq", host(g["c_seq"]), fo["c"], TIGHT)
+    check("c_last", host(g["c_last"]), fo["c_last"], TIGHT)
+    check("dU", host(g["dU"]), bo["dU"], TIGHT)
+    check("dx", host(g["dx"]), bo["dx_hw"], TIGHT)
+    check("dv", host(g["dv"]), bo["dv"], TIGHT)
+
+
+def test_forward_without_state_outputs():
+    """c_seq and c_last may be NULL (inference): h is unchanged."""
+    import torch
+    w = workloads.custom(21, 2, 128, ndir=2, alpha=1.0, mode="given_u", backward=False,
+                         c0="zero")
+    inp = workloads.make_inputs(w, seed=5)
+    t = dev_inputs(inp)
+    shape = SruShape(w.L, w.B, w.d, True, 1.0)
+    h = torch.empty((w.L, w.B, 2, w.d), device="cuda")
+    from parallelizable_recurrent_units_amd import sru_forward
+    sru_forward(shape, t["U"], t["x"], t["v"], t["b"], None, h, None, None)
+    fo, _ = oracle_fwd_bwd(inp, 1.0, with_bwd=False)
+    check("h", host(h), fo["h"], TIGHT)
+
+
+def test_backward_is_deterministic():
+    w = workloads.custom(50, 8, 128, ndir=2, alpha=1.0, mode="given_u")
+    inp = workloads.make_inputs(w, seed=6)
+    t = dev_inputs(inp)
+    shape = SruShape(w.L, w.B, w.d, True, 1.0)
+    a = run_fwd_bwd(shape, t)
+    b = run_fwd_bwd(shape, t)
+    for k in ("h", "dU", "dx", "dv", "db", "dc0"):
+        assert np.array_equal(host(a[k]), host(b[k])), k
+
+
+# ---------------------------------------------------------------------------
+# projection GEMM
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("L,B,d,nd", [(3, 5, 64, 1), (7, 19, 100, 2), (2, 3, 37, 1),
+                                      (64, 4, 256, 2), (1, 1, 8, 1)])
+def test_projection_bf16(L, B, d, nd):
+    import torch
+    rng = np.random.default_rng(3000 + d)
+    X = rng.standard_normal((L, B, d)).astype(np.float32)
+    W_bits, W = workloads.to_bf16(rng.uniform(-0.1, 0.1, (nd * 3 * d, d)).astype(np.float32))
+    Xd = torch.from_numpy(X).cuda()
+    Wd = torch.from_numpy(W_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    shape = SruShape(L, B, d, nd == 2, 1.0)
+    print(f"case M={L*B} N={nd*3*d} K={d}", flush=True)
+    U = layer.project(shape, Xd, Wd)
+    X2 = X.reshape(L * B, d)
+    check("U vs rounded-X oracle", host(U).reshape(L * B, -1), oracle.project(X2, W, True),
+          GEMM_ACC)
+    check("U vs fp32-X oracle", host(U).reshape(L * B, -1), oracle.project(X2, W, False),
+          BF16_BAR)
+    # bf16 X in HBM takes the same path without the cast
+    Xb_bits, Xb = workloads.to_bf16(X)
+    Ub = layer.project(shape, torch.from_numpy(Xb_bits.view(np.int16)).cuda().view(torch.bfloat16),
+                       Wd)
+    check("U (bf16 X)", host(Ub).reshape(L * B, -1), oracle.project(Xb.reshape(L * B, d), W, False),
+          GEMM_ACC)
+    # backward-data with accumulation: dX = C0 + dU W
+    G = rng.standard_normal((L, B, nd, 3, d)).astype(np.float32)
+    C0 = rng.standard_normal((L, B, d)).astype(np.float32)
+    dX = torch.from_numpy(C0.copy()).cuda()
+    layer.project_bwd_data(shape, torch.from_numpy(G).cuda(), Wd, dX, accumulate=True)
+    G2 = G.reshape(L * B, -1).astype(np.float64)
+    ref = oracle.project_bwd_data(G2, W) + C0.reshape(L * B, d)
+    check("dX vs exact", host(dX).reshape(L * B, d), ref, 1e-2)
+    Gr = oracle.round_bf16(G).reshape(L * B, -1)
+    ref_r = oracle.project_bwd_data(Gr, W) + C0.reshape(L * B, d)
+    check("dX vs bf16(dU) oracle", host(dX).reshape(L * B, d), ref_r, GEMM_ACC)
+
+
+def test_projection_fp32_config1():
+    """Workload 1 (fp32 throughout): projection + forward at the 1e-5 bar."""
+    w = workloads.WORKLOADS[1]
+    inp = workloads.make_inputs(w, seed=1)
+    t = dev_inputs(inp)
+    shape = SruShape(w.L, w.B, w.d, False, w.alpha)
+    U = layer.project(shape, t["x"], t["W"])
+    h, _, c_last = layer.forward(shape, U, t["x"], t["v"], t["b"], t["c0"])
+    Uo = oracle.layer_U(inp["x"], inp["W"], False, w.L, w.B, w.ndir, w.d)
+    fo = oracle.forward(Uo, inp["x"], inp["v"], inp["b"], inp["c0"], w.alpha)
+    check("U", host(U), Uo, TIGHT)
+    check("h", host(h), fo["h"], TIGHT)
+    check("c_last", host(c_last), fo["c_last"], TIGHT)
+
+
+# ---------------------------------------------------------------------------
+# linear mode (v = 0): chunked scan == sequential oracle for every chunk size
+# ---------------------------------------------------------------------------
+def linear_case(L, B, d, nd, chunk, seed, uf_shift=2.0):
+    w = workloads.custom(L, B, d, ndir=nd, alpha=0.8, mode="given_u", linear=True,
+                         uf_shift=uf_shift, c0="normal0.1")
+    inp = workloads.make_inputs(w, seed=seed, dc_last=True, b_scale=0.3)
+    t = dev_inputs(inp)
+    shape = SruShape(L, B, d, nd == 2, w.alpha)
+    print(f"case L={L} B={B} d={d} ndir={nd} chunk={chunk} uf_shift={uf_shift}", flush=True)
+    h, c_seq, c_last = layer.linear_forward(shape, chunk, t["U"], t["x"], t["b"], t["c0"])
+    dU, dx, db, dc0 = layer.linear_backward(shape, chunk, t["U"], t["x"], t["b"], t["c0"], c_seq,
+                                            t["dh"], t["dc_last"])
+    fo, bo = oracle_fwd_bwd(inp, w.alpha)
+    check("h", host(h), fo["h"], TIGHT)
+    check("c_seq", host(c_seq), fo["c"], TIGHT)
+    check("c_last", host(c_last), fo["c_last"], TIGHT)
+    check("dU", host(dU), bo["dU"], TIGHT)
+    check("dx", host(dx), bo["dx_hw"], TIGHT)
+    check("db", host(db), bo["db"], TIGHT)
+    check("dc0", host(dc0), bo["dc0"], TIGHT)
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 64, 256, 300, 1000])
+def test_linear_scan_chunk_sizes(chunk):
+    linear_case(300, 2, 64, 1, chunk, seed=4000 + chunk)
+
+
+def test_linear_scan_bidirectional_ragged():
+    linear_case(50, 2, 33, 2, 8, seed=4100)
+
+
+def test_linear_scan_carry_stress():
+    """U_f ~ N(8, 1): the product of forget gates over a chunk of 256 stays
+    near 0.9, so the carries between chunks dominate the result."""
+    linear_case(1024, 2, 64, 1, 256, seed=4200, uf_shift=8.0)
+
+
+def test_linear_matches_nonlinear_kernel_at_v0():
+    """The linear scan and the sequential kernel agree when v = 0."""
+    w = workloads.custom(96, 2, 128, ndir=1, alpha=1.0, mode="given_u", linear=True,
+                         uf_shift=2.0, c0="normal0.1")
+    inp = workloads.make_inputs(w, seed=4300)
+    t = dev_inputs(inp)
+    shape = SruShape(w.L, w.B, w.d, False, 1.0)
+    h1, c1, _ = layer.linear_forward(shape, 16, t["U"], t["x"], t["b"], t["c0"])
+    h2, c2, _ = layer.forward(shape, t["U"], t["x"], t["v"], t["b"], t["c0"], keep_c_seq=True)
+    check("h", host(h1), host(h2), TIGHT)
+    check("c", host(c1), host(c2), TIGHT)

@@ -1,0 +1,195 @@
+"""GPU parity at the five specified workload sizes, in the launch configuration
+the benchmark times.
+
+* workload 1 (fp32, L=32 B=4 d=64): every output element (test_parity_gpu).
+* workload 2 (bidirectional, L=64 B=128 d=512): every output element of the
+  whole training step (projection, forward, backward, dv/db, dX).
+* workload 3 (given bf16 U, L=1024 B=16 d=2048): 48 sampled chains.
+* workload 4 (training step, L=512 B=32 d=1024): every chain of 3 sampled
+  batch rows, plus size-independent properties for dv and db.
+* workload 5 (linear mode, L=16384 B=4 d=4096, chunk 256): 24 sampled chains,
+  plus size-independent properties for db.
+Tolerances are explained in test_parity_gpu.py.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from parallelizable_recurrent_units_amd import SruShape, layer, workloads
+from tests.gpu_util import check, dev_inputs, host
+
+pytestmark = pytest.mark.gpu
+
+TIGHT = 1e-5
+BF16_BAR = 2e-2
+GEMM_ACC = 1e-4
+
+
+def _sum_bound_check(name, gpu, terms_sum, terms_abs_sum, n_terms):
+    """|gpu - exact| <= n u sum|terms| (fp32 summation of n terms, u = 2^-24)."""
+    bound = n_terms * 2.0 ** -24 * terms_abs_sum + 1e-30
+    err = np.abs(gpu - terms_sum)
+    worst = float(np.max(err / bound))
+    print(f"  {name}: max err / (n u sum|terms|) = {worst:.3f}", flush=True)
+    assert worst <= 1.0, name
+
+
+def training_step(w, t):
+    shape = SruShape(w.L, w.B, w.d, w.ndir == 2, w.alpha)
+    U = layer.project(shape, t["x"], t["W"])
+    h, c_seq, c_last = layer.forward(shape, U, t["x"], t["v"], t["b"], t["c0"], keep_c_seq=True)
+    dU, dx, dv, db, dc0 = layer.backward(shape, U, t["x"], t["v"], t["b"], t["c0"], c_seq,
+                                         t["dh"], t["dc_last"])
+    layer.project_bwd_data(shape, dU, t["W"], dx, accumulate=True)
+    return dict(U=U, h=h, c_seq=c_seq, c_last=c_last, dU=dU, dX=dx, dv=dv, db=db, dc0=dc0)
+
+
+def oracle_rows(w, inp, bs, round_x):
+    """Oracle for every chain of batch rows ``bs`` (projection included)."""
+    L, B, d, nd = w.L, w.B, w.d, w.ndir
+    X2 = inp["x"].reshape(L * B, d)
+    res = []
+    for b in bs:
+        rows = np.arange(L) * B + b
+        U = oracle.project(X2, inp["W"], round_x, rows=rows).reshape(L, 1, nd, 3, d)
+        sl = lambda a: np.ascontiguousarray(a[:, b:b + 1])
+        fo = oracle.forward(U, sl(inp["x"]), inp["v"], inp["b"], sl(inp["c0"]), w.alpha)
+        bo = oracle.backward(U, sl(inp["x"]), inp["v"], inp["b"], sl(inp["c0"]), fo["c"],
+                             sl(inp["dh"]), sl(inp["dc_last"]), w.alpha)
+        dX = oracle.project_bwd_data(bo["dU"].reshape(L, -1), inp["W"]) + bo["dx_hw"][:, 0]
+        res.append(dict(U=U[:, 0], h=fo["h"][:, 0], c_last=fo["c_last"][:, 0],
+                        dU=bo["dU"][:, 0], dc0=bo["dc0"][:, 0], dX=dX))
+    return res
+
+
+def test_workload2_full():
+    import torch
+    w = workloads.WORKLOADS[2]
+    inp = workloads.make_inputs(w, seed=2)
+    print(f"workload {w.name}", flush=True)
+    g = training_step(w, dev_inputs(inp))
+    torch.cuda.synchronize()
+    L, B, d, nd = w.L, w.B, w.d, w.ndir
+    for round_x, tol, tag in ((True, GEMM_ACC, "bf16-X oracle"), (False, BF16_BAR, "fp32-X oracle")):
+        Uo = oracle.layer_U(inp["x"], inp["W"], round_x, L, B, nd, d)
+        fo = oracle.forward(Uo, inp["x"], inp["v"], inp["b"], inp["c0"], w.alpha)
+        bo = oracle.backward(Uo, inp["x"], inp["v"], inp["b"], inp["c0"], fo["c"], inp["dh"],
+                             inp["dc_last"], w.alpha)
+        dXo = oracle.project_bwd_data(bo["dU"].reshape(L * B, -1), inp["W"]).reshape(L, B, d)
+        dXo += bo["dx_hw"]
+        print(f" vs {tag}", flush=True)
+        check("U", host(g["U"]), Uo, tol)
+        check("h", host(g["h"]), fo["h"], tol)
+        check("c_seq", host(g["c_seq"]), fo["c"], tol)
+        check("c_last", host(g["c_last"]), fo["c_last"], tol)
+        check("dU", host(g["dU"]), bo["dU"], tol)
+        check("dv", host(g["dv"]), bo["dv"], tol)
+        check("db", host(g["db"]), bo["db"], tol)
+        check("dc0", host(g["dc0"]), bo["dc0"], tol)
+        check("dX", host(g["dX"]), dXo, max(tol, 1e-2))
+
+
+def test_workload3_sampled_chains():
+    import torch
+    w = workloads.WORKLOADS[3]
+    inp = workloads.make_inputs(w, seed=3)
+    print(f"workload {w.name}", flush=True)
+    t = dev_inputs(inp)
+    shape = SruShape(w.L, w.B, w.d, False, w.alpha)
+    h, _, c_last = layer.forward(shape, t["U"], t["x"], t["v"], t["b"], t["c0"])
+    rng = np.random.default_rng(33)
+    chains = [(0, 0), (w.B - 1, w.d - 1), (0, w.d - 1), (w.B - 1, 0)]
+    chains += [(int(b), int(j)) for b, j in zip(rng.integers(0, w.B, 44), rng.integers(0, w.d, 44))]
+    bi = torch.tensor([b for b, _ in chains], device="cuda")
+    ji = torch.tensor([j for _, j in chains], device="cuda")
+    hg = host(h[:, bi, 0, ji])            # [L, n]
+    cg = host(c_last[0, bi, ji])
+    ho = np.empty_like(hg)
+    co = np.empty_like(cg)
+    U, x = inp["U"], inp["x"]
+    for n, (b, j) in enumerate(chains):
+        hh, _, cl = oracle.chain_forward(U[:, b, 0, 0, j], U[:, b, 0, 1, j], U[:, b, 0, 2, j],
+                                         x[:, b, j], inp["v"][0, 0, j], inp["v"][0, 1, j],
+                                         inp["b"][0, 0, j], inp["b"][0, 1, j], 0.0, w.alpha)
+        ho[:, n] = hh
+        co[n] = cl
+    check("h (48 chains)", hg, ho, TIGHT)
+    check("c_last (48 chains)", cg, co, TIGHT)
+
+
+def test_workload4_sampled_rows_and_properties():
+    import torch
+    w = workloads.WORKLOADS[4]
+    inp = workloads.make_inputs(w, seed=4)
+    print(f"workload {w.name}", flush=True)
+    g = training_step(w, dev_inputs(inp))
+    torch.cuda.synchronize()
+    bs = [0, w.B - 1, 13]
+    for round_x, tol, tag in ((True, GEMM_ACC, "bf16-X oracle"), (False, BF16_BAR, "fp32-X oracle")):
+        print(f" vs {tag}, batch rows {bs}", flush=True)
+        for b, o in zip(bs, oracle_rows(w, inp, bs, round_x)):
+            check(f"U[b={b}]", host(g["U"][:, b]), o["U"], tol)
+            check(f"h[b={b}]", host(g["h"][:, b]), o["h"], tol)
+            check(f"c_last[b={b}]", host(g["c_last"][:, b]), o["c_last"], tol)
+            check(f"dU[b={b}]", host(g["dU"][:, b]), o["dU"], tol)
+            check(f"dc0[b={b}]", host(g["dc0"][:, b]), o["dc0"], tol)
+            check(f"dX[b={b}]", host(g["dX"][:, b]), o["dX"], max(tol, 1e-2))
+    # dv, db: exact sums of the per-step terms the kernel produced
+    dU = g["dU"].double()
+    c_seq = g["c_seq"].double()
+    c_prev = torch.cat([torch.from_numpy(inp["c0"]).cuda().double()[None, :, :, :].permute(
+        0, 2, 1, 3), c_seq[:-1]], dim=0)           # [L, B, 1, d]
+    n = w.L * w.B
+    for gate, name in ((0, "f"), (1, "r")):
+        dz = dU[:, :, 0, gate, :]
+        _sum_bound_check(f"db_{name}", host(g["db"][0, gate]), host(dz.sum((0, 1))),
+                         host(dz.abs().sum((0, 1))), n)
+        terms = dz * c_prev[:, :, 0, :]
+        _sum_bound_check(f"dv_{name}", host(g["dv"][0, gate]), host(terms.sum((0, 1))),
+                         host(terms.abs().sum((0, 1))), n)
+
+
+def test_workload5_linear_sampled_chains():
+    import torch
+    w = workloads.WORKLOADS[5]
+    print(f"workload {w.name} (generating inputs)", flush=True)
+    inp = workloads.make_inputs(w, seed=5)
+    t = dev_inputs(inp)
+    shape = SruShape(w.L, w.B, w.d, False, w.alpha)
+    h, c_seq, c_last = layer.linear_forward(shape, w.chunk, t["U"], t["x"], t["b"], t["c0"])
+    dU, dx, db, dc0 = layer.linear_backward(shape, w.chunk, t["U"], t["x"], t["b"], t["c0"],
+                                            c_seq, t["dh"], t["dc_last"])
+    torch.cuda.synchronize()
+    print(" GPU done", flush=True)
+    rng = np.random.default_rng(55)
+    chains = [(0, 0), (w.B - 1, w.d - 1)]
+    chains += [(int(b), int(j)) for b, j in zip(rng.integers(0, w.B, 22), rng.integers(0, w.d, 22))]
+    U, x, dh = inp["U"], inp["x"], inp["dh"]
+    errs = {}
+    out = {k: [] for k in ("h", "c", "cl", "dU", "dx", "dc0")}
+    ref = {k: [] for k in out}
+    for b, j in chains:
+        uf, ur, ux = U[:, b, 0, 0, j], U[:, b, 0, 1, j], U[:, b, 0, 2, j]
+        bf, br = inp["b"][0, 0, j], inp["b"][0, 1, j]
+        hh, cc, cl = oracle.chain_forward(uf, ur, ux, x[:, b, j], 0.0, 0.0, bf, br, 0.0, w.alpha)
+        gb = oracle.chain_backward(uf, ur, ux, x[:, b, j], 0.0, 0.0, bf, br, 0.0, cc,
+                                   dh[:, b, 0, j], 0.0, w.alpha)
+        ref["h"].append(hh)
+        ref["c"].append(cc)
+        ref["cl"].append([cl])
+        ref["dU"].append(np.stack([gb["duf"], gb["dur"], gb["dux"]]))
+        ref["dx"].append(gb["dx_hw"])
+        ref["dc0"].append([gb["dc0"]])
+        out["h"].append(host(h[:, b, 0, j]))
+        out["c"].append(host(c_seq[:, b, 0, j]))
+        out["cl"].append(host(c_last[0, b, j:j + 1]))
+        out["dU"].append(host(dU[:, b, 0, :, j]).T)
+        out["dx"].append(host(dx[:, b, j]))
+        out["dc0"].append(host(dc0[0, b, j:j + 1]))
+    for k in out:
+        check(f"{k} (24 chains)", np.array(out[k]), np.array(ref[k]), TIGHT, errs)
+    n = w.L * w.B
+    for gate, name in ((0, "f"), (1, "r")):
+        dz = dU[:, :, 0, gate, :].double()
+        _sum_bound_check(f"db_{name}", host(db[0, gate]), host(dz.sum((0, 1))),
+                         host(dz.abs().sum((0, 1))), n)
