@@ -18,203 +18,405 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128, BN = 128, BK = 32;
-constexpr int LDK = BK + 8;   // padded LDS row (bf16 elements): 80 bytes
-constexpr int NT = 256;       // 4 waves, 2 x 2, each 64 x 64
+// Block tile BM x BN x BK with 4 waves in a 2 x 2 grid, each wave a
+// (BM/2) x (BN/2) tile of 32 x 32 MFMA blocks.
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int LDK = BK + 8;    // padded LDS row (bf16): 144 bytes, keeps the
+                               // 16-byte operand reads of 8 rows on distinct banks
+constexpr int NT = 256;
+constexpr int WM = BM / 2, WN = BN / 2;
+constexpr int TI = WM / 32, TJ = WN / 32;
+constexpr int EPI_LD = WN + 4; // fp32 epilogue staging row (per wave)
 
-struct alignas(16) Bf16x8 { bf16_bits v[8]; };
-
-// ---- A tile loader: BM x BK, into registers then LDS ----------------------
-template <typename TA, bool VEC>
+// ---- A tile (BM x BK) -> registers -> LDS (bf16) --------------------------
+// FAST (K % BK == 0): every thread's element offsets inside the k-tile window
+// are loop invariant 32-bit values (rows past M are clamped to M - 1: they
+// load valid memory whose results the epilogue never writes), and the
+// window's base pointer is uniform.  Otherwise every element is bounds
+// checked.
+template <typename TA, bool FAST>
 struct ALoader {
-    // fp32: 4 float4 per thread; bf16: 2 x (8 bf16) per thread
-    static constexpr int N = sizeof(TA) == 4 ? 4 : 2;
-    uint4 reg[N];
-    __device__ void load(const TA *A, int64_t M, int64_t K, int64_t m0, int64_t k0, int tid)
+    static constexpr int V = 16 / sizeof(TA);            // elements per 16 bytes
+    static constexpr int PER_ROW = BK / V;
+    static constexpr int N = BM * PER_ROW / NT;          // 16-byte loads per thread
+    struct Offsets {
+        uint32_t v[N];                                   // byte offsets (FAST)
+    };
+    u32x4 reg[N];
+    const Offsets *off = nullptr;                        // shared by both stages
+    __device__ __forceinline__ static void init(Offsets &o, int64_t M, int64_t K, int64_t m0,
+                                                int tid)
     {
-        constexpr int V = 16 / sizeof(TA);          // elements per 16 bytes
-        constexpr int PER_ROW = BK / V;
+        if (FAST) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int idx = tid + i * NT;
+                int64_t row = idx / PER_ROW;
+                if (m0 + row > M - 1) row = M - 1 - m0;
+                o.v[i] = (uint32_t)((row * K + (idx % PER_ROW) * V) * (int64_t)sizeof(TA));
+            }
+        }
+    }
+    __device__ __forceinline__ void load(const TA *A, int64_t M, int64_t K, int64_t m0,
+                                         int64_t k0, int tid)
+    {
+        if (FAST) {
+            const char *base = (const char *)(A + m0 * K + k0);   // uniform
+#pragma unroll
+            for (int i = 0; i < N; ++i) reg[i] = *(const u32x4 *)(base + off->v[i]);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int idx = tid + i * NT;
             const int row = idx / PER_ROW, cv = idx % PER_ROW;
             const int64_t m = m0 + row, k = k0 + cv * V;
-            if (VEC) {
-                if (m < M && k < K)
-                    reg[i] = *(const uint4 *)(A + m * K + k);
-                else
-                    reg[i] = make_uint4(0, 0, 0, 0);
-            } else {
-                TA tmp[V];
+            u32x4 v = {0u, 0u, 0u, 0u};
 #pragma unroll
-                for (int e = 0; e < V; ++e)
-                    tmp[e] = (m < M && k + e < K) ? A[m * K + k + e] : TA(0);
-                reg[i] = *(const uint4 *)tmp;
+            for (int e = 0; e < V; ++e) {
+                const TA a = (m < M && k + e < K) ? A[m * K + k + e] : TA(0);
+                if constexpr (sizeof(TA) == 4)
+                    v[e] = __builtin_bit_cast(uint32_t, a);
+                else
+                    v[e / 2] |= uint32_t(a) << (16 * (e % 2));
             }
+            reg[i] = v;
         }
     }
-    __device__ void store(bf16_bits *As, int tid) const
+    __device__ __forceinline__ void store(bf16_bits *As, int tid) const
     {
-        constexpr int V = 16 / sizeof(TA);
-        constexpr int PER_ROW = BK / V;
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int idx = tid + i * NT;
             const int row = idx / PER_ROW, cv = idx % PER_ROW;
             bf16_bits *dst = As + row * LDK + cv * V;
-            if (sizeof(TA) == 4) {
-                const float4 f = *(const float4 *)&reg[i];
-                uint2 packed;
-                packed.x = uint32_t(f32_to_bf16(f.x)) | (uint32_t(f32_to_bf16(f.y)) << 16);
-                packed.y = uint32_t(f32_to_bf16(f.z)) | (uint32_t(f32_to_bf16(f.w)) << 16);
-                *(uint2 *)dst = packed;
+            if constexpr (sizeof(TA) == 4) {   // round fp32 -> bf16 (nearest even) here
+                const u32x4 u = reg[i];
+                u32x2 packed;
+                packed.x = uint32_t(f32_to_bf16(__uint_as_float(u.x))) |
+                           (uint32_t(f32_to_bf16(__uint_as_float(u.y))) << 16);
+                packed.y = uint32_t(f32_to_bf16(__uint_as_float(u.z))) |
+                           (uint32_t(f32_to_bf16(__uint_as_float(u.w))) << 16);
+                *(u32x2 *)dst = packed;
             } else {
-                *(uint4 *)dst = reg[i];
+                *(u32x4 *)dst = reg[i];
             }
         }
     }
 };
 
-// ---- B tile loader: produces Bs[n][k] (BN x BK) ---------------------------
-template <bool KN, bool VEC>
-struct BLoader {
-    uint4 reg[2];
-    __device__ void load(const bf16_bits *Bm, int64_t N, int64_t K, int64_t n0, int64_t k0,
-                         int tid)
+// ---- B tile -> LDS as Bs[n][k] (BN x BK) ----------------------------------
+// KN = false: B is [N, K] (k contiguous), copied row by row.
+// KN = true : B is [K, N] (n contiguous).  Each thread gathers 16 k-values of
+//             two adjacent columns with 4-byte loads (a wave reads 256
+//             contiguous bytes of one k-row per load) and writes them as four
+//             16-byte LDS rows, so the tile is transposed without 2-byte LDS
+//             stores.
+template <bool KN, bool FAST>
+struct BLoader;
+
+template <bool FAST>
+struct BLoader<false, FAST> {
+    static constexpr int PER_ROW = BK / 8;
+    static constexpr int N = BN * PER_ROW / NT;
+    struct Offsets {
+        uint32_t v[N];
+    };
+    u32x4 reg[N];
+    const Offsets *off = nullptr;
+    __device__ __forceinline__ static void init(Offsets &o, int64_t N_, int64_t K, int64_t n0,
+                                                int tid)
     {
+        if (FAST) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = tid + i * NT;
-            if (!KN) {  // B[n][k], 4 x 8 bf16 per row of BK
-                const int row = idx / 4, cv = idx % 4;
-                const int64_t n = n0 + row, k = k0 + cv * 8;
-                if (VEC) {
-                    reg[i] = (n < N && k < K) ? *(const uint4 *)(Bm + n * K + k)
-                                              : make_uint4(0, 0, 0, 0);
-                } else {
-                    bf16_bits tmp[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        tmp[e] = (n < N && k + e < K) ? Bm[n * K + k + e] : bf16_bits(0);
-                    reg[i] = *(const uint4 *)tmp;
-                }
-            } else {    // B[k][n], BK rows of BN: 16 x 8 bf16 per row
-                const int kr = idx / 16, cv = idx % 16;
-                const int64_t k = k0 + kr, n = n0 + cv * 8;
-                if (VEC) {
-                    reg[i] = (k < K && n < N) ? *(const uint4 *)(Bm + k * N + n)
-                                              : make_uint4(0, 0, 0, 0);
-                } else {
-                    bf16_bits tmp[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        tmp[e] = (k < K && n + e < N) ? Bm[k * N + n + e] : bf16_bits(0);
-                    reg[i] = *(const uint4 *)tmp;
-                }
+            for (int i = 0; i < N; ++i) {
+                const int idx = tid + i * NT;
+                int64_t row = idx / PER_ROW;
+                if (n0 + row > N_ - 1) row = N_ - 1 - n0;
+                o.v[i] = (uint32_t)((row * K + (idx % PER_ROW) * 8) * 2);
             }
         }
     }
-    __device__ void store(bf16_bits *Bs, int tid) const
+    __device__ __forceinline__ void load(const bf16_bits *Bm, int64_t N_, int64_t K, int64_t n0,
+                                         int64_t k0, int tid)
+    {
+        if (FAST) {
+            const char *base = (const char *)(Bm + n0 * K + k0);
+#pragma unroll
+            for (int i = 0; i < N; ++i) reg[i] = *(const u32x4 *)(base + off->v[i]);
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = tid + i * NT;
+            const int row = idx / PER_ROW, cv = idx % PER_ROW;
+            const int64_t n = n0 + row, k = k0 + cv * 8;
+            u32x4 v = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t h = (n < N_ && k + e < K) ? Bm[n * K + k + e] : 0u;
+                v[e / 2] |= h << (16 * (e % 2));
+            }
+            reg[i] = v;
+        }
+    }
+    __device__ __forceinline__ void store(bf16_bits *Bs, int tid) const
     {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < N; ++i) {
             const int idx = tid + i * NT;
-            if (!KN) {
-                const int row = idx / 4, cv = idx % 4;
-                *(uint4 *)(Bs + row * LDK + cv * 8) = reg[i];
-            } else {
-                const int kr = idx / 16, cv = idx % 16;
-                const bf16_bits *v = (const bf16_bits *)&reg[i];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) Bs[(cv * 8 + e) * LDK + kr] = v[e];
-            }
+            const int row = idx / PER_ROW, cv = idx % PER_ROW;
+            *(u32x4 *)(Bs + row * LDK + cv * 8) = reg[i];
         }
     }
 };
+
+template <bool FAST>
+struct BLoader<true, FAST> {
+    // BN/2 column pairs x (NT / (BN/2)) k-groups of KG rows
+    static constexpr int NP = BN / 2;
+    static constexpr int KQ = NT / NP;
+    static constexpr int KG = BK / KQ;                   // 16
+    struct Offsets {
+        uint32_t v;                                      // byte offset
+    };
+    uint32_t reg[KG];
+    const Offsets *off = nullptr;
+    __device__ __forceinline__ static void init(Offsets &o, int64_t N_, int64_t K, int64_t n0,
+                                                int tid)
+    {
+        if (FAST) {   // N even: the pair (n, n+1) is one aligned dword
+            int64_t c = 2 * (tid % NP);
+            if (n0 + c > N_ - 2) c = N_ - 2 - n0;
+            o.v = (uint32_t)(((tid / NP) * KG * N_ + c) * 2);
+        }
+    }
+    __device__ __forceinline__ void load(const bf16_bits *Bm, int64_t N_, int64_t K, int64_t n0,
+                                         int64_t k0, int tid)
+    {
+        if (FAST) {
+#pragma unroll
+            for (int e = 0; e < KG; ++e) {
+                const char *base = (const char *)(Bm + (k0 + e) * N_ + n0);   // uniform
+                reg[e] = *(const uint32_t *)(base + off->v);
+            }
+            return;
+        }
+        const int np = tid % NP, kq = tid / NP;
+        const int64_t n = n0 + 2 * np;
+#pragma unroll
+        for (int e = 0; e < KG; ++e) {
+            const int64_t k = k0 + kq * KG + e;
+            const uint32_t lo = (k < K && n < N_) ? Bm[k * N_ + n] : 0u;
+            const uint32_t hi = (k < K && n + 1 < N_) ? Bm[k * N_ + n + 1] : 0u;
+            reg[e] = lo | (hi << 16);
+        }
+    }
+    __device__ __forceinline__ void store(bf16_bits *Bs, int tid) const
+    {
+        const int np = tid % NP, kq = tid / NP;
+        // column n takes the low halves, column n + 1 the high halves
+        auto lo2 = [](uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); };
+        auto hi2 = [](uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); };
+#pragma unroll
+        for (int h = 0; h < KG / 8; ++h) {
+            const uint32_t *r = reg + h * 8;
+            const u32x4 lo = {lo2(r[0], r[1]), lo2(r[2], r[3]), lo2(r[4], r[5]), lo2(r[6], r[7])};
+            const u32x4 hi = {hi2(r[0], r[1]), hi2(r[2], r[3]), hi2(r[4], r[5]), hi2(r[6], r[7])};
+            *(u32x4 *)(Bs + (2 * np) * LDK + kq * KG + h * 8) = lo;
+            *(u32x4 *)(Bs + (2 * np + 1) * LDK + kq * KG + h * 8) = hi;
+        }
+    }
+};
+
+// Tile order: the hardware hands consecutive workgroups to the 8 XCDs in
+// turn, each XCD with its own L2.  Workgroup `bid` is given logical tile
+// (bid % 8) * (T / 8) + bid / 8, so every XCD works through one contiguous
+// range of tiles; within the logical order, groups of 8 row tiles sweep the
+// column tiles so neighbouring tiles share A rows and B columns in that L2.
+__device__ __forceinline__ void tile_of(int64_t bid, int64_t TM, int64_t TN, int64_t *tm,
+                                        int64_t *tn)
+{
+    const int64_t T = TM * TN;
+    const int64_t T8 = T / 8;
+    int64_t lt = bid;
+    if (bid < 8 * T8) lt = (bid % 8) * T8 + bid / 8;
+    constexpr int64_t GM = 8;
+    const int64_t group = lt / (GM * TN);
+    const int64_t first = group * GM;
+    const int64_t gsz = (TM - first) < GM ? (TM - first) : GM;
+    const int64_t in = lt % (GM * TN);
+    *tm = first + in % gsz;
+    *tn = in / gsz;
+}
 
 // C[M, N] (+)= A[M, K] . B  with B given as [N, K] (KN = false) or [K, N].
-template <typename TA, bool KN, bool AVEC, bool BVEC>
-__global__ __launch_bounds__(NT) void gemm_bf16_mfma(int64_t M, int64_t N, int64_t K,
-                                                     const TA *__restrict__ A,
-                                                     const bf16_bits *__restrict__ Bm,
-                                                     float *__restrict__ C, bool accumulate)
+#ifndef SRU_GEMM_MIN_BLOCKS
+#define SRU_GEMM_MIN_BLOCKS 2
+#endif
+#ifndef SRU_GEMM_STAGES
+#define SRU_GEMM_STAGES 1   // register stages; 1 measured fastest at 2 blocks/CU
+#endif
+
+template <typename TA, bool KN, bool FAST>
+__global__ __launch_bounds__(NT, SRU_GEMM_MIN_BLOCKS) void gemm_bf16_mfma(int64_t M, int64_t N, int64_t K,
+                                                        const TA *__restrict__ A,
+                                                        const bf16_bits *__restrict__ Bm,
+                                                        float *__restrict__ C, bool accumulate)
 {
-    __shared__ __attribute__((aligned(16))) bf16_bits As[2][BM * LDK];
-    __shared__ __attribute__((aligned(16))) bf16_bits Bs[2][BN * LDK];
+    // two stages of A and B tiles; reused as fp32 staging by the epilogue
+    constexpr int STAGE = (BM + BN) * LDK;               // bf16 elements
+    __shared__ __attribute__((aligned(16))) bf16_bits smem[2 * STAGE];
+    static_assert(2 * STAGE * 2 >= 4 * WM * EPI_LD * 4, "epilogue staging must fit");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.x * BM;
-    const int64_t n0 = (int64_t)blockIdx.y * BN;
+    const int64_t TM = (M + BM - 1) / BM, TN = (N + BN - 1) / BN;
+    int64_t tm, tn;
+    tile_of(blockIdx.x, TM, TN, &tm, &tn);
+    const int64_t m0 = tm * BM, n0 = tn * BN;
 
-    ALoader<TA, AVEC> la;
-    BLoader<KN, BVEC> lb;
-    f32x16 acc[2][2];
+    bf16_bits *As0 = smem, *Bs0 = smem + BM * LDK;
+    bf16_bits *As1 = smem + STAGE, *Bs1 = smem + STAGE + BM * LDK;
+
+    typedef ALoader<TA, FAST> AL;
+    typedef BLoader<KN, FAST> BL;
+    typename AL::Offsets aoff;
+    typename BL::Offsets boff;
+    AL::init(aoff, M, K, m0, tid);
+    BL::init(boff, N, K, n0, tid);
+    AL la0, la1;
+    BL lb0, lb1;
+    la0.off = la1.off = &aoff;
+    lb0.off = lb1.off = &boff;
+    f32x16 acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int64_t KT = (K + BK - 1) / BK;
-    la.load(A, M, K, m0, 0, tid);
-    lb.load(Bm, N, K, n0, 0, tid);
-    la.store(As[0], tid);
-    lb.store(Bs[0], tid);
-    __syncthreads();
-
     const int r32 = lane & 31;
     const int kg = (lane >> 5) * 8;
-    for (int64_t kt = 0; kt < KT; ++kt) {
-        const int buf = (int)(kt & 1);
-        if (kt + 1 < KT) {
-            la.load(A, M, K, m0, (kt + 1) * BK, tid);
-            lb.load(Bm, N, K, n0, (kt + 1) * BK, tid);
-        }
+    auto compute = [&](const bf16_bits *As, const bf16_bits *Bs) {
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8 af[2], bfr[2];
+            bf16x8 af[TI], bfr[TJ];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                af[i] = *(const bf16x8 *)(As[buf] + (wm * 64 + i * 32 + r32) * LDK + ks * 16 + kg);
+            for (int i = 0; i < TI; ++i)
+                af[i] = *(const bf16x8 *)(As + (wm * WM + i * 32 + r32) * LDK + ks * 16 + kg);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bfr[j] = *(const bf16x8 *)(Bs[buf] + (wn * 64 + j * 32 + r32) * LDK + ks * 16 + kg);
+            for (int j = 0; j < TJ; ++j)
+                bfr[j] = *(const bf16x8 *)(Bs + (wn * WN + j * 32 + r32) * LDK + ks * 16 + kg);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < TI; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < TJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j],
                                                                         0, 0, 0);
         }
-        if (kt + 1 < KT) {
-            la.store(As[buf ^ 1], tid);
-            lb.store(Bs[buf ^ 1], tid);
-        }
-        __syncthreads();
-    }
+    };
 
-    // 32x32 accumulator layout: lane holds column (lane & 31) and rows
-    // 8*(r/4) + 4*(lane/32) + (r%4), r = 0..15.
+    // Software pipeline: k-tile kt is in LDS stage kt % 2 while the loads of
+    // k-tile kt + 1 (or, with two register stages, kt + 1 and kt + 2) are in
+    // flight, and two blocks per CU interleave.  The body has no conditional
+    // loads or stores (prefetch indices are clamped to the last k-tile; the
+    // surplus loads re-read it), which keeps the compiler's wait counts
+    // exact: a stage waits only for its own loads.
+    const int64_t KT = (K + BK - 1) / BK;
+    auto kc = [&](int64_t kt) { return (kt < KT ? kt : KT - 1) * BK; };
+    la0.load(A, M, K, m0, 0, tid);
+    lb0.load(Bm, N, K, n0, 0, tid);
+    la0.store(As0, tid);
+    lb0.store(Bs0, tid);
+#if SRU_GEMM_STAGES == 2
+    la1.load(A, M, K, m0, kc(1), tid);
+    lb1.load(Bm, N, K, n0, kc(1), tid);
+    __syncthreads();
+    for (int64_t kt = 0;; kt += 2) {
+        la0.load(A, M, K, m0, kc(kt + 2), tid);
+        lb0.load(Bm, N, K, n0, kc(kt + 2), tid);
+        compute(As0, Bs0);
+        la1.store(As1, tid);
+        lb1.store(Bs1, tid);
+        __syncthreads();
+        if (kt + 1 >= KT) break;
+        la1.load(A, M, K, m0, kc(kt + 3), tid);
+        lb1.load(Bm, N, K, n0, kc(kt + 3), tid);
+        compute(As1, Bs1);
+        la0.store(As0, tid);
+        lb0.store(Bs0, tid);
+        __syncthreads();
+        if (kt + 2 >= KT) break;
+    }
+#else
+    __syncthreads();
+    for (int64_t kt = 0;; kt += 2) {
+        la0.load(A, M, K, m0, kc(kt + 1), tid);
+        lb0.load(Bm, N, K, n0, kc(kt + 1), tid);
+        compute(As0, Bs0);
+        la0.store(As1, tid);
+        lb0.store(Bs1, tid);
+        __syncthreads();
+        if (kt + 1 >= KT) break;
+        la0.load(A, M, K, m0, kc(kt + 2), tid);
+        lb0.load(Bm, N, K, n0, kc(kt + 2), tid);
+        compute(As1, Bs1);
+        la0.store(As0, tid);
+        lb0.store(Bs0, tid);
+        __syncthreads();
+        if (kt + 2 >= KT) break;
+    }
+    (void)la1;
+    (void)lb1;
+#endif
+
+    // Epilogue: each wave stages its WM x WN fp32 tile in LDS (rows of the
+    // 32x32 accumulator layout: column lane & 31, rows 8*(r/4) + 4*(lane/32)
+    // + r%4) and writes it back as 16-byte row segments.
+    float *stage = (float *)smem + wave * (WM * EPI_LD);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t col = n0 + wn * 64 + j * 32 + r32;
-            if (col >= N) continue;
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-                if (row < M) {
-                    float *p = C + row * N + col;
-                    *p = accumulate ? *p + acc[i][j][r] : acc[i][j][r];
-                }
+                const int row = i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+                stage[row * EPI_LD + j * 32 + r32] = acc[i][j][r];
             }
+    // (LDS operations of one wave complete in order: no barrier needed here)
+    constexpr int C4 = WN / 4;            // float4 per staged row
+    const int64_t mw = m0 + wm * WM, nw = n0 + wn * WN;
+#pragma unroll 4
+    for (int it = 0; it < WM * C4 / 64; ++it) {
+        const int idx = it * 64 + lane;
+        const int row = idx / C4, c4 = idx % C4;
+        const int64_t m = mw + row, n = nw + c4 * 4;
+        if (m >= M) continue;
+        const float4 v = *(const float4 *)(stage + row * EPI_LD + c4 * 4);
+        float *p = C + m * N + n;
+        if (FAST) {   // N % 4 == 0
+            if (n < N) {
+                float4 o = v;
+                if (accumulate) {
+                    const float4 c = *(const float4 *)p;
+                    o.x += c.x; o.y += c.y; o.z += c.z; o.w += c.w;
+                }
+                *(float4 *)p = o;
+            }
+        } else {
+            const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (n + e < N) p[e] = accumulate ? p[e] + vv[e] : vv[e];
         }
+    }
 }
 
 // ---- fp32 path ------------------------------------------------------------
@@ -280,25 +482,23 @@ __global__ __launch_bounds__(256) void gemm_f32(int64_t M, int64_t N, int64_t K,
     }
 }
 
-template <typename TA, bool KN, bool AVEC, bool BVEC>
+template <typename TA, bool KN>
 hipError_t mfma_launch(const GemmArgs &g, hipStream_t s)
 {
-    dim3 grid((unsigned)((g.M + BM - 1) / BM), (unsigned)((g.N + BN - 1) / BN));
-    hipLaunchKernelGGL((gemm_bf16_mfma<TA, KN, AVEC, BVEC>), grid, dim3(NT), 0, s, g.M, g.N, g.K,
-                       (const TA *)g.A, (const bf16_bits *)g.Bm, g.C, g.accumulate);
+    const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+    // fast variant: whole k-tiles, 16-byte rows everywhere, 4-aligned C rows,
+    // and (for B as [K, N]) dword column pairs
+    const bool fast = (g.K % BK == 0) && (g.N % 4 == 0) && (g.K * BM < (int64_t(1) << 31)) &&
+                      (!KN || g.N * BK < (int64_t(1) << 31));
+    if (fast)
+        hipLaunchKernelGGL((gemm_bf16_mfma<TA, KN, true>), dim3((unsigned)tiles), dim3(NT), 0, s,
+                           g.M, g.N, g.K, (const TA *)g.A, (const bf16_bits *)g.Bm, g.C,
+                           g.accumulate);
+    else
+        hipLaunchKernelGGL((gemm_bf16_mfma<TA, KN, false>), dim3((unsigned)tiles), dim3(NT), 0, s,
+                           g.M, g.N, g.K, (const TA *)g.A, (const bf16_bits *)g.Bm, g.C,
+                           g.accumulate);
     return hipGetLastError();
-}
-
-template <typename TA, bool KN>
-hipError_t mfma_dispatch_vec(const GemmArgs &g, hipStream_t s)
-{
-    const int64_t va = 16 / sizeof(TA);
-    const bool avec = (g.K % va) == 0;
-    const bool bvec = KN ? (g.N % 8 == 0) : (g.K % 8 == 0);
-    if (avec && bvec) return mfma_launch<TA, KN, true, true>(g, s);
-    if (avec) return mfma_launch<TA, KN, true, false>(g, s);
-    if (bvec) return mfma_launch<TA, KN, false, true>(g, s);
-    return mfma_launch<TA, KN, false, false>(g, s);
 }
 
 template <typename TA, bool KN>
@@ -316,10 +516,8 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t s)
 {
     if (g.b_bf16) {
         if (g.a_bf16)
-            return g.b_kn ? mfma_dispatch_vec<bf16_bits, true>(g, s)
-                          : mfma_dispatch_vec<bf16_bits, false>(g, s);
-        return g.b_kn ? mfma_dispatch_vec<float, true>(g, s)
-                      : mfma_dispatch_vec<float, false>(g, s);
+            return g.b_kn ? mfma_launch<bf16_bits, true>(g, s) : mfma_launch<bf16_bits, false>(g, s);
+        return g.b_kn ? mfma_launch<float, true>(g, s) : mfma_launch<float, false>(g, s);
     }
     if (g.a_bf16)
         return g.b_kn ? f32_launch<bf16_bits, true>(g, s) : f32_launch<bf16_bits, false>(g, s);

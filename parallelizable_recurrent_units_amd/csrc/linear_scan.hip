@@ -201,18 +201,40 @@ __global__ __launch_bounds__(256) void lin_bwd_apply(LinGeom g, const TU *__rest
     dbpart[(k * 2 + 1) * g.chains + ch] = sbr;
 }
 
-// db[dl, g, j] = sum over b (increasing), then chunks (increasing).
+// db[dl, g, j] = sum over (b, chunk) of the per-(chain, chunk) partials.  A
+// block of 256 threads owns 64 consecutive j of one gate: wave w sums the
+// (b, chunk) pairs of index w mod 4 (pair index = b * nC + chunk), with loads
+// in flight, and the four wave sums are added in wave order; the order depends
+// only on the shape, so results are identical run to run.
 __global__ __launch_bounds__(256) void lin_db_reduce(LinGeom g, const float *__restrict__ part,
                                                      float *db)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= 2 * g.d) return;
-    const int64_t j = i % g.d;
-    const int gg = (int)(i / g.d);
+    __shared__ float red[4][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t jblocks = (g.d + 63) / 64;
+    const int gg = (int)(blockIdx.x / jblocks);
+    const int64_t j = (blockIdx.x % jblocks) * 64 + lane;
+    const int64_t pairs = g.B * g.nC;
     float s = 0.0f;
-    for (int64_t bb = 0; bb < g.B; ++bb)
-        for (int64_t k = 0; k < g.nC; ++k) s += part[(k * 2 + gg) * g.chains + bb * g.d + j];
-    db[(g.dl * 2 + gg) * g.d + j] = s;
+    if (j < g.d) {
+        auto at = [&](int64_t q) {
+            const int64_t bb = q / g.nC, k = q % g.nC;
+            return part[(k * 2 + gg) * g.chains + bb * g.d + j];
+        };
+        int64_t q = wv;
+        for (; q + 12 < pairs; q += 16) {
+            const float a0 = at(q), a1 = at(q + 4), a2 = at(q + 8), a3 = at(q + 12);
+            s += a0;
+            s += a1;
+            s += a2;
+            s += a3;
+        }
+        for (; q < pairs; q += 4) s += at(q);
+    }
+    red[wv][lane] = s;
+    __syncthreads();
+    if (wv == 0 && j < g.d)
+        db[(g.dl * 2 + gg) * g.d + j] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
 }
 
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
@@ -255,8 +277,8 @@ hipError_t lin_backward_t(const LinArgs &a, hipStream_t s)
                            s, g, (const TU *)a.U, (const TX *)a.x, a.b, a.alpha, a.c0, a.c_seq,
                            a.dh, gin, a.dU, a.dx, dl != a.ndir - 1, a.dc0, dbp);
         if (a.db)
-            hipLaunchKernelGGL(lin_db_reduce, dim3(blocks_for(2 * a.d)), dim3(256), 0, s, g, dbp,
-                               a.db);
+            hipLaunchKernelGGL(lin_db_reduce, dim3((unsigned)(2 * ((a.d + 63) / 64))), dim3(256), 0,
+                               s, g, dbp, a.db);
     }
     return hipGetLastError();
 }

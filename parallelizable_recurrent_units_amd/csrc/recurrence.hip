@@ -75,12 +75,24 @@ __global__ __launch_bounds__(256) void fwd_generic(RecArgs a)
 // Fast forward: one wavefront per 64 channels, packet loads + register ring.
 // BF16 = U and x both bf16 (a packet then carries two timesteps), else both
 // fp32.  Requires d % 64 == 0 and 16-byte aligned tensors.
+//
+// The sequence is walked in groups of G packets.  Per group the wave writes
+// G packets to LDS, refills those ring slots with the packets R ahead, reads
+// back every lane's own values, runs the G*SPP recurrence steps, and writes
+// h and c as 16-byte stores: one LDS round trip per group instead of per
+// step.  The loop body has no conditional memory operations (prefetch
+// indices are clamped), so the compiler's wait counts stay exact; the last
+// L mod (G*SPP) steps run in a short tail with direct loads.
 // ---------------------------------------------------------------------------
-template <bool BF16, int R>
+template <bool BF16, int R, int G>
 __global__ __launch_bounds__(kWave) void fwd_fast(RecArgs a)
 {
-    __shared__ uint4 in_slot[kWave];     // one packet, 1 KB
-    __shared__ float out_slot[4 * kWave];  // h, c for two timesteps, 1 KB
+    static_assert(R % G == 0, "ring holds whole groups");
+    constexpr int SPP = BF16 ? 2 : 1;                // timesteps per packet
+    constexpr int S = G * SPP;                       // timesteps per group
+    static_assert(S % 2 == 0, "outputs leave two timesteps per store");
+    __shared__ uint4 in_slot[G * kWave];             // G packets
+    __shared__ float out_slot[S * 2 * kWave];        // h, c of S timesteps
 
     const int lane = threadIdx.x;
     const int64_t gpr = a.d / kWave;                 // wave groups per row
@@ -91,20 +103,16 @@ __global__ __launch_bounds__(kWave) void fwd_fast(RecArgs a)
     const int64_t j0 = (rem % gpr) * kWave;
     const int64_t j = j0 + lane;
     const int64_t L = a.L;
-
-    // time index of direction-step s
     auto tix = [&](int64_t s) -> int64_t { return dl ? (L - 1 - s) : s; };
 
     // ---- input packet addressing (per lane) ----
-    constexpr int SPP = BF16 ? 2 : 1;                // timesteps per packet
     constexpr int ESZ = BF16 ? 2 : 4;                // element bytes
     const int e_in = BF16 ? (lane >> 5) : 0;         // timestep within packet
     const int q_in = BF16 ? ((lane >> 3) & 3) : (lane >> 4);  // 0 Uf 1 Ur 2 Ux 3 x
     const int sub_in = BF16 ? (lane & 7) : (lane & 15);
     const int64_t cpl = 16 / ESZ;                    // channels per lane
     const char *in_base;
-    int64_t in_row;   // element offset of this lane's data at time t = 0
-    int64_t in_tstride;  // element stride per time index
+    int64_t in_row, in_tstride;
     if (q_in < 3) {
         in_base = (const char *)a.U;
         in_row = (bb * a.ndir + dl) * 3 * a.d + q_in * a.d + j0 + cpl * sub_in;
@@ -114,15 +122,13 @@ __global__ __launch_bounds__(kWave) void fwd_fast(RecArgs a)
         in_row = bb * a.d + j0 + cpl * sub_in;
         in_tstride = a.B * a.d;
     }
-    const int64_t NP = (L + SPP - 1) / SPP;          // packets
     auto load_packet = [&](int64_t p) -> uint4 {
         int64_t s = p * SPP + e_in;
         s = s < L ? s : L - 1;                       // clamp: stays in bounds
-        const int64_t off = (in_row + tix(s) * in_tstride) * ESZ;
-        return *(const uint4 *)(in_base + off);
+        return *(const uint4 *)(in_base + (in_row + tix(s) * in_tstride) * ESZ);
     };
 
-    // ---- output addressing (per lane), two timesteps per flush ----
+    // ---- output addressing (per lane): lane = (step parity, h|c, 4 channels)
     const int e_out = lane >> 5;
     const int q_out = (lane >> 4) & 1;               // 0 h, 1 c
     const int sub_out = lane & 15;
@@ -136,61 +142,91 @@ __global__ __launch_bounds__(kWave) void fwd_fast(RecArgs a)
     const float alpha = a.alpha;
     float c = a.c0 ? a.c0[(dl * a.B + bb) * a.d + j] : 0.0f;
 
-    uint4 ring[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) ring[i] = load_packet(i);
-
-    const float *inf = (const float *)in_slot;
-    const bf16_bits *inh = (const bf16_bits *)in_slot;
-
-    auto step = [&](int e, int64_t s) {
-        float uf, ur, ux, xv;
-        if (BF16) {
-            uf = bf16_to_f32(inh[e * 256 + 0 * 64 + lane]);
-            ur = bf16_to_f32(inh[e * 256 + 1 * 64 + lane]);
-            ux = bf16_to_f32(inh[e * 256 + 2 * 64 + lane]);
-            xv = bf16_to_f32(inh[e * 256 + 3 * 64 + lane]);
-        } else {
-            uf = inf[0 * 64 + lane];
-            ur = inf[1 * 64 + lane];
-            ux = inf[2 * 64 + lane];
-            xv = inf[3 * 64 + lane];
-        }
+    auto cell = [&](float uf, float ur, float ux, float xv, float &h) {
         const Gate f = gate(fmaf(vf, c, uf + bf));
         const Gate r = gate(fmaf(vr, c, ur + br));
         c = fmaf(f.g, c, f.gc * ux);
         const float ax = alpha * xv;
-        const int pe = (int)(s & 1);
-        out_slot[pe * 128 + lane] = fmaf(r.g, c, r.gc * ax);
-        out_slot[pe * 128 + 64 + lane] = c;
-    };
-    auto flush = [&](int64_t s_even) {
-        // timesteps s_even and s_even + 1 (the latter only if < L)
-        const float4 val = ((const float4 *)out_slot)[lane];
-        const int64_t s = s_even + e_out;
-        if (out_on && s < L) {
-            *(float4 *)(out_base + out_row + tix(s) * out_tstride) = val;
-        }
+        h = fmaf(r.g, c, r.gc * ax);
     };
 
-    for (int64_t p0 = 0; p0 < NP; p0 += R) {
+    const int64_t groups = L / S;                    // full groups
+    if (groups > 0) {
+        uint4 ring[R];
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const int64_t p = p0 + i;
-            if (p < NP) {
-                in_slot[lane] = ring[i];
-                ring[i] = load_packet(p + R);
-                if (BF16) {
-                    const int64_t s = 2 * p;
-                    step(0, s);
-                    if (s + 1 < L) step(1, s + 1);
-                    flush(s);
-                } else {
-                    step(0, p);
-                    if ((p & 1) || p == L - 1) flush(p & ~(int64_t)1);
+        for (int i = 0; i < R; ++i) ring[i] = load_packet(i);
+        const float *inf = (const float *)in_slot;
+        const bf16_bits *inh = (const bf16_bits *)in_slot;
+        int64_t gi = 0;
+        for (;;) {
+#pragma unroll
+            for (int rg = 0; rg < R / G; ++rg) {
+                const int64_t p0 = (gi + rg) * G;    // first packet of this group
+#pragma unroll
+                for (int i = 0; i < G; ++i) in_slot[i * kWave + lane] = ring[rg * G + i];
+#pragma unroll
+                for (int i = 0; i < G; ++i) ring[rg * G + i] = load_packet(p0 + R + i);
+                float uf[S], ur[S], ux[S], xv[S];
+#pragma unroll
+                for (int st = 0; st < S; ++st) {
+                    if (BF16) {
+                        const bf16_bits *hp = inh + (st / 2) * 512 + (st % 2) * 256 + lane;
+                        uf[st] = bf16_to_f32(hp[0]);
+                        ur[st] = bf16_to_f32(hp[64]);
+                        ux[st] = bf16_to_f32(hp[128]);
+                        xv[st] = bf16_to_f32(hp[192]);
+                    } else {
+                        const float *fp = inf + st * 256 + lane;
+                        uf[st] = fp[0];
+                        ur[st] = fp[64];
+                        ux[st] = fp[128];
+                        xv[st] = fp[192];
+                    }
                 }
+#pragma unroll
+                for (int st = 0; st < S; ++st) {
+                    float h;
+                    cell(uf[st], ur[st], ux[st], xv[st], h);
+                    out_slot[st * 128 + lane] = h;
+                    out_slot[st * 128 + 64 + lane] = c;
+                }
+                if (out_on) {
+#pragma unroll
+                    for (int m = 0; m < S / 2; ++m) {
+                        const float4 val = ((const float4 *)out_slot)[m * 64 + lane];
+                        const int64_t st = p0 * SPP + 2 * m + e_out;
+                        *(float4 *)(out_base + out_row + tix(st) * out_tstride) = val;
+                    }
+                }
+                if (gi + rg + 1 >= groups) goto tail;
             }
+            gi += R / G;
         }
+    }
+tail:
+    // remaining L mod S timesteps: direct per-lane loads
+    for (int64_t st = groups * S; st < L; ++st) {
+        const int64_t t = tix(st);
+        const int64_t ub = ((t * a.B + bb) * a.ndir + dl) * 3 * a.d + j;
+        float uf, ur, ux, xv;
+        if (BF16) {
+            const bf16_bits *U = (const bf16_bits *)a.U;
+            uf = bf16_to_f32(U[ub]);
+            ur = bf16_to_f32(U[ub + a.d]);
+            ux = bf16_to_f32(U[ub + 2 * a.d]);
+            xv = bf16_to_f32(((const bf16_bits *)a.x)[(t * a.B + bb) * a.d + j]);
+        } else {
+            const float *U = (const float *)a.U;
+            uf = U[ub];
+            ur = U[ub + a.d];
+            ux = U[ub + 2 * a.d];
+            xv = ((const float *)a.x)[(t * a.B + bb) * a.d + j];
+        }
+        float h;
+        cell(uf, ur, ux, xv, h);
+        const int64_t o = ((t * a.B + bb) * a.ndir + dl) * a.d + j;
+        a.h[o] = h;
+        if (a.c_seq) a.c_seq[o] = c;
     }
     if (a.c_last) a.c_last[(dl * a.B + bb) * a.d + j] = c;
 }
@@ -259,18 +295,23 @@ __global__ __launch_bounds__(256) void bwd_generic(RecArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Fast backward (fp32 U and x, d % 64 == 0): one wavefront per 64 channels.
-// Per timestep two input packets:
+// Fast backward (fp32 U and x, d % 64 == 0): one wavefront per 64 channels,
+// walking its direction's steps in reverse.  Per timestep two input packets:
 //   A: lanes 0-15 U_f, 16-31 U_r, 32-47 U_cand, 48-63 x          (time t)
-//   B: lanes 0-15 c[t_prev], 16-31 dh[t], 32-47 dx[t] (accumulate), 48-63 idle
+//   B: lanes 0-15 c[t_prev], 16-31 dh[t], 32-47 dx[t] (read when
+//      accumulating; otherwise these lanes and lanes 48-63 re-read dh)
 // and one output packet: lanes 0-15 dU_f, 16-31 dU_r, 32-47 dU_cand, 48-63 dx.
+// Steps are processed in groups of G with one LDS round trip per group, a
+// branch-free main loop over whole groups and a direct-load tail, as in the
+// forward kernel.
 // ---------------------------------------------------------------------------
-template <int R>
+template <int R, int G>
 __global__ __launch_bounds__(kWave) void bwd_fast(RecArgs a)
 {
-    __shared__ uint4 slot_a[kWave];
-    __shared__ uint4 slot_b[kWave];
-    __shared__ float out_slot[4 * kWave];
+    static_assert(R % G == 0, "ring holds whole groups");
+    __shared__ uint4 slot_a[G * kWave];
+    __shared__ uint4 slot_b[G * kWave];
+    __shared__ float out_slot[G * 4 * kWave];
 
     const int lane = threadIdx.x;
     const int dl = a.dir;
@@ -284,6 +325,7 @@ __global__ __launch_bounds__(kWave) void bwd_fast(RecArgs a)
 
     const int q = lane >> 4;
     const int sub = lane & 15;
+    const bool dxacc = a.dx_accumulate;
     // packet A
     const char *pa_base;
     int64_t pa_row, pa_ts;
@@ -297,35 +339,33 @@ __global__ __launch_bounds__(kWave) void bwd_fast(RecArgs a)
         pa_ts = a.B * a.d;
     }
     // packet B
+    const int64_t hrow = (bb * a.ndir + dl) * a.d + j0 + 4 * sub;
+    const int64_t hts = a.B * a.ndir * a.d;
     const char *pb_base;
     int64_t pb_row, pb_ts, pb_soff;
-    const bool dxacc = a.dx_accumulate;
-    if (q == 0) {          // c at the previous direction-step
+    if (q == 0) {                       // c at the previous direction-step
         pb_base = (const char *)a.c_seq_in;
-        pb_row = (bb * a.ndir + dl) * a.d + j0 + 4 * sub;
-        pb_ts = a.B * a.ndir * a.d;
+        pb_row = hrow;
+        pb_ts = hts;
         pb_soff = -1;
-    } else if (q == 1) {   // dh
-        pb_base = (const char *)a.dh;
-        pb_row = (bb * a.ndir + dl) * a.d + j0 + 4 * sub;
-        pb_ts = a.B * a.ndir * a.d;
-        pb_soff = 0;
-    } else {               // dx (read only when accumulating; lanes 48-63 reuse it)
+    } else if (q == 2 && dxacc) {       // dx to accumulate into
         pb_base = (const char *)a.dx;
         pb_row = bb * a.d + j0 + 4 * sub;
         pb_ts = a.B * a.d;
         pb_soff = 0;
+    } else {                            // dh (lanes 48-63, and 32-47 unless accumulating)
+        pb_base = (const char *)a.dh;
+        pb_row = hrow;
+        pb_ts = hts;
+        pb_soff = 0;
     }
     auto clampL = [&](int64_t s) -> int64_t { return s < 0 ? 0 : (s >= L ? L - 1 : s); };
-    // direction-step s is processed at iteration k = L-1-s
+    // direction-step s is processed at reverse iteration k = L-1-s
     auto load_a = [&](int64_t k) -> uint4 {
-        const int64_t s = clampL(L - 1 - k);
-        return *(const uint4 *)(pa_base + (pa_row + tix(s) * pa_ts) * 4);
+        return *(const uint4 *)(pa_base + (pa_row + tix(clampL(L - 1 - k)) * pa_ts) * 4);
     };
     auto load_b = [&](int64_t k) -> uint4 {
-        const int64_t s = clampL(L - 1 - k + pb_soff);
-        if (q >= 2 && !dxacc) return make_uint4(0, 0, 0, 0);
-        return *(const uint4 *)(pb_base + (pb_row + tix(s) * pb_ts) * 4);
+        return *(const uint4 *)(pb_base + (pb_row + tix(clampL(L - 1 - k + pb_soff)) * pb_ts) * 4);
     };
 
     // output packet
@@ -342,53 +382,99 @@ __global__ __launch_bounds__(kWave) void bwd_fast(RecArgs a)
     float c = a.c_seq_in[((tix(L - 1) * a.B + bb) * a.ndir + dl) * a.d + j];
     float svf = 0.f, svr = 0.f, sbf = 0.f, sbr = 0.f;
 
-    uint4 ring_a[R], ring_b[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-        ring_a[i] = load_a(i);
-        ring_b[i] = load_b(i);
-    }
-    const float *fa = (const float *)slot_a;
-    const float *fb = (const float *)slot_b;
+    // one reverse step; returns dU_f, dU_r, dU_cand, dx (highway part)
+    auto cell = [&](float uf, float ur, float ux, float xv, float cp, float dhv, float &o0,
+                    float &o1, float &o2, float &o3) {
+        const Gate f = gate(fmaf(vf, cp, uf + bf));
+        const Gate r = gate(fmaf(vr, cp, ur + br));
+        const float dc = fmaf(dhv, r.g, gc);
+        const float dr = dhv * fmaf(-alpha, xv, c);
+        o3 = dhv * r.gc * alpha;
+        o2 = dc * f.gc;
+        const float df = dc * (cp - ux);
+        o0 = df * (f.g * f.gc);
+        o1 = dr * (r.g * r.gc);
+        svf = fmaf(o0, cp, svf);
+        svr = fmaf(o1, cp, svr);
+        sbf += o0;
+        sbr += o1;
+        gc = fmaf(dc, f.g, fmaf(o0, vf, o1 * vr));
+        c = cp;
+    };
 
-    for (int64_t k0 = 0; k0 < L; k0 += R) {
+    const int64_t groups = L / G;
+    if (groups > 0) {
+        uint4 ring_a[R], ring_b[R];
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-            const int64_t k = k0 + i;
-            if (k < L) {
-                const int64_t s = L - 1 - k;
-                slot_a[lane] = ring_a[i];
-                slot_b[lane] = ring_b[i];
-                ring_a[i] = load_a(k + R);
-                ring_b[i] = load_b(k + R);
-                const float uf = fa[lane], ur = fa[64 + lane], ux = fa[128 + lane];
-                const float xv = fa[192 + lane];
-                const float cp = s > 0 ? fb[lane] : c0;
-                const float dhv = fb[64 + lane];
-                const Gate f = gate(fmaf(vf, cp, uf + bf));
-                const Gate r = gate(fmaf(vr, cp, ur + br));
-                const float dc = fmaf(dhv, r.g, gc);
-                const float dr = dhv * fmaf(-alpha, xv, c);
-                float dxh = dhv * r.gc * alpha;
-                if (dxacc) dxh += fb[128 + lane];
-                const float dux = dc * f.gc;
-                const float df = dc * (cp - ux);
-                const float dzf = df * (f.g * f.gc);
-                const float dzr = dr * (r.g * r.gc);
-                svf = fmaf(dzf, cp, svf);
-                svr = fmaf(dzr, cp, svr);
-                sbf += dzf;
-                sbr += dzr;
-                gc = fmaf(dc, f.g, fmaf(dzf, vf, dzr * vr));
-                c = cp;
-                out_slot[lane] = dzf;
-                out_slot[64 + lane] = dzr;
-                out_slot[128 + lane] = dux;
-                out_slot[192 + lane] = dxh;
-                const float4 val = ((const float4 *)out_slot)[lane];
-                *(float4 *)(po_base + po_row + tix(s) * po_ts) = val;
-            }
+            ring_a[i] = load_a(i);
+            ring_b[i] = load_b(i);
         }
+        const float *fa = (const float *)slot_a;
+        const float *fb = (const float *)slot_b;
+        int64_t gi = 0;
+        for (;;) {
+#pragma unroll
+            for (int rg = 0; rg < R / G; ++rg) {
+                const int64_t k0 = (gi + rg) * G;
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    slot_a[i * kWave + lane] = ring_a[rg * G + i];
+                    slot_b[i * kWave + lane] = ring_b[rg * G + i];
+                }
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    ring_a[rg * G + i] = load_a(k0 + R + i);
+                    ring_b[rg * G + i] = load_b(k0 + R + i);
+                }
+                float uf[G], ur[G], ux[G], xv[G], cp[G], dhv[G], dxi[G];
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    uf[i] = fa[i * 256 + lane];
+                    ur[i] = fa[i * 256 + 64 + lane];
+                    ux[i] = fa[i * 256 + 128 + lane];
+                    xv[i] = fa[i * 256 + 192 + lane];
+                    cp[i] = fb[i * 256 + lane];
+                    dhv[i] = fb[i * 256 + 64 + lane];
+                    dxi[i] = fb[i * 256 + 128 + lane];
+                }
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    const int64_t s = L - 1 - (k0 + i);
+                    float o0, o1, o2, o3;
+                    cell(uf[i], ur[i], ux[i], xv[i], s > 0 ? cp[i] : c0, dhv[i], o0, o1, o2, o3);
+                    out_slot[i * 256 + lane] = o0;
+                    out_slot[i * 256 + 64 + lane] = o1;
+                    out_slot[i * 256 + 128 + lane] = o2;
+                    out_slot[i * 256 + 192 + lane] = dxacc ? o3 + dxi[i] : o3;
+                }
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    const float4 val = ((const float4 *)out_slot)[i * 64 + lane];
+                    const int64_t s = L - 1 - (k0 + i);
+                    *(float4 *)(po_base + po_row + tix(s) * po_ts) = val;
+                }
+                if (gi + rg + 1 >= groups) goto tail;
+            }
+            gi += R / G;
+        }
+    }
+tail:
+    for (int64_t k = groups * G; k < L; ++k) {
+        const int64_t s = L - 1 - k;
+        const int64_t t = tix(s);
+        const int64_t ub = ((t * a.B + bb) * a.ndir + dl) * 3 * a.d + j;
+        const float *U = (const float *)a.U;
+        const int64_t xi = (t * a.B + bb) * a.d + j;
+        const float cpv =
+            s > 0 ? a.c_seq_in[((tix(s - 1) * a.B + bb) * a.ndir + dl) * a.d + j] : c0;
+        float o0, o1, o2, o3;
+        cell(U[ub], U[ub + a.d], U[ub + 2 * a.d], ((const float *)a.x)[xi], cpv,
+             a.dh[((t * a.B + bb) * a.ndir + dl) * a.d + j], o0, o1, o2, o3);
+        a.dU[ub] = o0;
+        a.dU[ub + a.d] = o1;
+        a.dU[ub + 2 * a.d] = o2;
+        a.dx[xi] = dxacc ? o3 + a.dx[xi] : o3;
     }
     if (a.dc0) a.dc0[(dl * a.B + bb) * a.d + j] = gc;
     float *pp = a.partials + ((int64_t)(dl * a.B + bb) * 4) * a.d + j;
@@ -399,22 +485,43 @@ __global__ __launch_bounds__(kWave) void bwd_fast(RecArgs a)
 }
 
 // dv[dl, g, j] = sum_b partials[dl, b, g, j]; db[dl, g, j] likewise with rows
-// 2, 3.  b increases, so the result does not depend on the launch shape.
+// 2, 3.  A block of 256 threads owns 64 consecutive j of one (dl, g): its four
+// waves sum the b of residue 0..3 (mod 4) with many loads in flight, then the
+// four partial sums are added in wave order.  The summation order depends only
+// on B, so results are identical run to run.
 __global__ __launch_bounds__(256) void param_reduce(const float *__restrict__ part, int64_t B,
                                                      int64_t d, int ndir, float *dv, float *db)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (int64_t)ndir * 4 * d;
-    if (i >= total) return;
-    const int64_t j = i % d;
-    const int g = (int)((i / d) % 4);
-    const int dl = (int)(i / (4 * d));
+    __shared__ float red[4][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t jblocks = (d + 63) / 64;
+    const int64_t row = blockIdx.x / jblocks;           // dl * 4 + g
+    const int64_t j = (blockIdx.x % jblocks) * 64 + lane;
+    const int g = (int)(row % 4), dl = (int)(row / 4);
     float s = 0.0f;
-    for (int64_t bb = 0; bb < B; ++bb) s += part[((dl * B + bb) * 4 + g) * d + j];
-    if (g < 2) {
-        if (dv) dv[(dl * 2 + g) * d + j] = s;
-    } else {
-        if (db) db[(dl * 2 + (g - 2)) * d + j] = s;
+    if (j < d) {
+        const float *p = part + ((int64_t)dl * B * 4 + g) * d + j;
+        const int64_t stride = 4 * d;                   // next b
+        int64_t bb = wv;
+        for (; bb + 12 < B; bb += 16) {
+            const float a0 = p[bb * stride], a1 = p[(bb + 4) * stride];
+            const float a2 = p[(bb + 8) * stride], a3 = p[(bb + 12) * stride];
+            s += a0;
+            s += a1;
+            s += a2;
+            s += a3;
+        }
+        for (; bb < B; bb += 4) s += p[bb * stride];
+    }
+    red[wv][lane] = s;
+    __syncthreads();
+    if (wv == 0 && j < d) {
+        const float t = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+        if (g < 2) {
+            if (dv) dv[(dl * 2 + g) * d + j] = t;
+        } else {
+            if (db) db[(dl * 2 + (g - 2)) * d + j] = t;
+        }
     }
 }
 
@@ -438,9 +545,24 @@ hipError_t bwd_generic_launch(const RecArgs &a, hipStream_t s)
 
 }  // namespace
 
-constexpr int kFwdRingF32 = 16;
-constexpr int kFwdRingBF16 = 16;
-constexpr int kBwdRing = 12;
+#ifndef SRU_FWD_RING_F32
+#define SRU_FWD_RING_F32 32
+#endif
+#ifndef SRU_FWD_GROUP_F32
+#define SRU_FWD_GROUP_F32 8
+#endif
+#ifndef SRU_FWD_RING_BF16
+#define SRU_FWD_RING_BF16 16
+#endif
+#ifndef SRU_FWD_GROUP_BF16
+#define SRU_FWD_GROUP_BF16 4
+#endif
+#ifndef SRU_BWD_RING
+#define SRU_BWD_RING 16
+#endif
+#ifndef SRU_BWD_GROUP
+#define SRU_BWD_GROUP 4
+#endif
 
 hipError_t launch_forward(const RecArgs &a, hipStream_t s)
 {
@@ -448,11 +570,11 @@ hipError_t launch_forward(const RecArgs &a, hipStream_t s)
     if (fast) {
         const int64_t waves = (int64_t)a.ndir * a.B * (a.d / kWave);
         if (a.u_bf16)
-            hipLaunchKernelGGL((fwd_fast<true, kFwdRingBF16>), dim3((unsigned)waves),
-                               dim3(kWave), 0, s, a);
+            hipLaunchKernelGGL((fwd_fast<true, SRU_FWD_RING_BF16, SRU_FWD_GROUP_BF16>),
+                               dim3((unsigned)waves), dim3(kWave), 0, s, a);
         else
-            hipLaunchKernelGGL((fwd_fast<false, kFwdRingF32>), dim3((unsigned)waves),
-                               dim3(kWave), 0, s, a);
+            hipLaunchKernelGGL((fwd_fast<false, SRU_FWD_RING_F32, SRU_FWD_GROUP_F32>),
+                               dim3((unsigned)waves), dim3(kWave), 0, s, a);
         return hipGetLastError();
     }
     if (a.u_bf16) {
@@ -468,7 +590,8 @@ hipError_t launch_backward_dir(const RecArgs &a, hipStream_t s)
     const bool fast = (a.d % kWave == 0) && !a.u_bf16 && !a.x_bf16;
     if (fast) {
         const int64_t waves = a.B * (a.d / kWave);
-        hipLaunchKernelGGL((bwd_fast<kBwdRing>), dim3((unsigned)waves), dim3(kWave), 0, s, a);
+        hipLaunchKernelGGL((bwd_fast<SRU_BWD_RING, SRU_BWD_GROUP>), dim3((unsigned)waves),
+                           dim3(kWave), 0, s, a);
         return hipGetLastError();
     }
     if (a.u_bf16) {
@@ -482,8 +605,7 @@ hipError_t launch_backward_dir(const RecArgs &a, hipStream_t s)
 hipError_t launch_param_reduce(const float *partials, int64_t B, int64_t d, int ndir,
                                float *dv, float *db, hipStream_t s)
 {
-    const int64_t total = (int64_t)ndir * 4 * d;
-    const int64_t blocks = (total + 255) / 256;
+    const int64_t blocks = (int64_t)ndir * 4 * ((d + 63) / 64);
     hipLaunchKernelGGL(param_reduce, dim3((unsigned)blocks), dim3(256), 0, s, partials, B, d,
                        ndir, dv, db);
     return hipGetLastError();

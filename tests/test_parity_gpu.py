@@ -75,6 +75,8 @@ CASES_F32 = [
     (40, 1, 192, 1),
     (64, 2, 200, 2),
     (100, 2, 64, 1),
+    (300, 1, 128, 2),
+    (131, 2, 64, 1),
 ]
 
 
@@ -96,7 +98,8 @@ def test_recurrence_fp32_given_u(L, B, d, nd):
 
 
 @pytest.mark.parametrize("L,B,d,nd,xdt", [(37, 2, 128, 1, "bf16"), (8, 3, 64, 2, "bf16"),
-                                          (9, 2, 70, 1, "bf16"), (12, 2, 64, 1, "f32")])
+                                          (9, 2, 70, 1, "bf16"), (12, 2, 64, 1, "f32"),
+                                          (257, 1, 64, 2, "bf16")])
 def test_recurrence_bf16_u(L, B, d, nd, xdt):
     """bf16 U (and x): the fast two-steps-per-packet path and the generic one."""
     w = workloads.custom(L, B, d, ndir=nd, alpha=1.3, mode="given_u", u_dtype="bf16",
