@@ -5,7 +5,8 @@
 
 One step = one pass of the whole hot path over one batch: projection GEMM
 (U = X~ W^T), forward recurrence, backward recurrence with the fused dv/db
-reduction, and the backward-data GEMM (dX = dU W + highway dx).  The headline
+reduction, and the backward-data GEMM (W transposed once, then
+dX = dU W + highway dx).  The headline
 workload is the bidirectional layer L=64, B=128, d=512 (fp32 activations,
 bf16 W).  Inputs are seeded synthetic draws (no dataset), resident in HBM
 before the timed region; several input/output sets rotate so consecutive steps
@@ -121,6 +122,7 @@ def device_set(w, seed):
                dU=torch.empty((L, B, nd, 3, d), **f32), dx=torch.empty((L, B, d), **f32),
                dv=torch.empty((nd, 2, d), **f32), db=torch.empty((nd, 2, d), **f32),
                dc0=torch.empty((nd, B, d), **f32),
+               Wt=torch.empty((d, nd * 3 * d), device="cuda", dtype=dev["W"].dtype),
                ws=torch.empty(sru_workspace_size(shape, SRU_WS_BACKWARD), device="cuda",
                               dtype=torch.uint8))
     return shape, dev
@@ -128,8 +130,14 @@ def device_set(w, seed):
 
 def training_step_rows(shape, t):
     """The four row calls of one training step, each a C-ABI entry point."""
-    from parallelizable_recurrent_units_amd import (SRU_PROJ_BWD_DATA, SRU_PROJ_FWD, sru_backward,
-                                                    sru_forward, sru_project)
+    from parallelizable_recurrent_units_amd import (SRU_PROJ_BWD_DATA_WT, SRU_PROJ_FWD,
+                                                    sru_backward, sru_forward, sru_project,
+                                                    sru_transpose_weight)
+
+    def bwd_data():
+        sru_transpose_weight(shape, t["W"], t["Wt"])
+        sru_project(shape, SRU_PROJ_BWD_DATA_WT, t["dU"], t["Wt"], t["dx"], True)
+
     return [
         ("a1_projection", lambda: sru_project(shape, SRU_PROJ_FWD, t["x"], t["W"], t["U"])),
         ("a2_forward", lambda: sru_forward(shape, t["U"], t["x"], t["v"], t["b"], t["c0"], t["h"],
@@ -137,8 +145,7 @@ def training_step_rows(shape, t):
         ("a3_a4_backward", lambda: sru_backward(shape, t["U"], t["x"], t["v"], t["b"], t["c0"],
                                                 t["c_seq"], t["dh"], t["dc_last"], t["dU"],
                                                 t["dx"], t["dv"], t["db"], t["dc0"], t["ws"])),
-        ("a5_projection_bwd_data", lambda: sru_project(shape, SRU_PROJ_BWD_DATA, t["dU"], t["W"],
-                                                       t["dx"], True)),
+        ("a5_projection_bwd_data", bwd_data),
     ]
 
 

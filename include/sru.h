@@ -71,8 +71,9 @@ typedef enum {
 typedef enum { SRU_F32 = 0, SRU_BF16 = 1 } sru_dtype;
 typedef enum { SRU_FWD = 0, SRU_BWD = 1 } sru_pass;
 typedef enum {
-    SRU_PROJ_FWD = 0,       /* C (+)= A W^T : U = X~ W^T, A = X [L*B, d]          */
-    SRU_PROJ_BWD_DATA = 1   /* C (+)= A W   : dX = dU W, A = dU [L*B, ndir*3*d]   */
+    SRU_PROJ_FWD = 0,        /* C (+)= A W^T  : U = X~ W^T, A = X [L*B, d]           */
+    SRU_PROJ_BWD_DATA = 1,   /* C (+)= A W    : dX = dU W, A = dU [L*B, ndir*3*d]    */
+    SRU_PROJ_BWD_DATA_WT = 2 /* C (+)= A Wt^T : as BWD_DATA, with W passed transposed */
 } sru_proj_op;
 typedef enum {
     SRU_WS_BACKWARD = 1,    /* sru_backward                      */
@@ -93,6 +94,9 @@ typedef struct {
  *   SRU_PROJ_BWD_DATA: C[L*B, d]       (+)= A[L*B, ndir*3d] . W
  *     (the input gradient through Eq. 1; pass accumulate = 1 with C = the dx
  *      returned by sru_backward to obtain the full input gradient).
+ *   SRU_PROJ_BWD_DATA_WT: the same product with W supplied as its transpose
+ *     Wt [d, ndir*3d] (from sru_transpose_weight); both operands are then
+ *     contiguous along the reduction and the faster kernel path is used.
  * w_dt = SRU_BF16: bf16 MFMA with fp32 accumulation; A (fp32 or bf16) is
  *   rounded to bf16 (nearest even) as it is loaded.
  * w_dt = SRU_F32: fp32 arithmetic throughout (A widened if bf16).
@@ -169,6 +173,15 @@ sru_status sru_linear_scan(const sru_shape *shape, sru_pass pass, int32_t chunk,
                            const float *dh, const float *dc_last,
                            float *dU, float *dx, float *db, float *dc0,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Wt[d, ndir*3d] = W[ndir*3d, d]^T, for SRU_PROJ_BWD_DATA_WT (the weights
+ * of Eq. 1 laid out with the reduction index of the backward-data product
+ * contiguous).  w_dt gives the element type of both (bf16 or fp32).  W and
+ * Wt must not overlap.
+ */
+sru_status sru_transpose_weight(const sru_shape *shape, const void *W, sru_dtype w_dt,
+                                void *Wt, void *stream);
 
 /* Workspace bytes needed by `op` for `shape` (and `chunk` for the linear
  * mode); 0 on invalid arguments (sru_last_error() says why). */

@@ -18,12 +18,12 @@ SRU_OK, SRU_ERR_INVALID_ARG, SRU_ERR_UNSUPPORTED = 0, 1, 2
 SRU_ERR_NO_DEVICE, SRU_ERR_LAUNCH, SRU_ERR_WORKSPACE = 3, 4, 5
 SRU_F32, SRU_BF16 = 0, 1
 SRU_FWD, SRU_BWD = 0, 1
-SRU_PROJ_FWD, SRU_PROJ_BWD_DATA = 0, 1
+SRU_PROJ_FWD, SRU_PROJ_BWD_DATA, SRU_PROJ_BWD_DATA_WT = 0, 1, 2
 SRU_WS_BACKWARD, SRU_WS_LINEAR_FWD, SRU_WS_LINEAR_BWD = 1, 2, 3
 
 # Every symbol include/sru.h declares.
 EXPORTED = ("sru_project", "sru_forward", "sru_backward", "sru_linear_scan",
-            "sru_workspace_size", "sru_status_string", "sru_last_error")
+            "sru_transpose_weight", "sru_workspace_size", "sru_status_string", "sru_last_error")
 
 
 class SruShape(ctypes.Structure):
@@ -76,6 +76,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sru_linear_scan.argtypes = [sp, ctypes.c_int, i32, _vp, ctypes.c_int, _vp, ctypes.c_int,
                                     _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _vp, sz, _vp]
+    lib.sru_transpose_weight.restype = ctypes.c_int
+    lib.sru_transpose_weight.argtypes = [sp, _vp, ctypes.c_int, _vp, _vp]
     lib.sru_workspace_size.restype = sz
     lib.sru_workspace_size.argtypes = [sp, ctypes.c_int, i32]
     lib.sru_status_string.restype = ctypes.c_char_p
@@ -137,6 +139,12 @@ def sru_project(shape, op: int, A, W, C, accumulate: bool = False, stream=None):
     _check(load_library().sru_project(ctypes.byref(s), int(op), _ptr(A), _dtype_code(A),
                                       _ptr(W), _dtype_code(W), _ptr(C), _dtype_code(C),
                                       int(bool(accumulate)), _stream(stream)))
+
+
+def sru_transpose_weight(shape, W, Wt, stream=None):
+    s = _shape(shape)
+    _check(load_library().sru_transpose_weight(ctypes.byref(s), _ptr(W), _dtype_code(W), _ptr(Wt),
+                                               _stream(stream)))
 
 
 def sru_forward(shape, U, x, v, b, c0, h, c_seq=None, c_last=None, stream=None):

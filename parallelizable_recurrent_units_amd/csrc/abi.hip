@@ -163,7 +163,7 @@ sru_status sru_project(const sru_shape *shape, sru_proj_op op, const void *A, sr
 {
     Dims dm;
     SRU_TRY(check_shape(shape, &dm));
-    if (op != SRU_PROJ_FWD && op != SRU_PROJ_BWD_DATA)
+    if (op != SRU_PROJ_FWD && op != SRU_PROJ_BWD_DATA && op != SRU_PROJ_BWD_DATA_WT)
         return fail(SRU_ERR_INVALID_ARG, "unknown projection op %d", (int)op);
     if (!valid_dtype(a_dt) || !valid_dtype(w_dt) || !valid_dtype(c_dt))
         return fail(SRU_ERR_INVALID_ARG, "unknown dtype");
@@ -193,9 +193,28 @@ sru_status sru_project(const sru_shape *shape, sru_proj_op op, const void *A, sr
     } else {
         g.N = shape->d;
         g.K = n3;
-        g.b_kn = true;
+        g.b_kn = op == SRU_PROJ_BWD_DATA;   // the _WT form passes W as [N, K]
     }
     return launched(sru::launch_gemm(g, (hipStream_t)stream), "projection");
+}
+
+sru_status sru_transpose_weight(const sru_shape *shape, const void *W, sru_dtype w_dt, void *Wt,
+                                void *stream)
+{
+    Dims dm;
+    SRU_TRY(check_shape(shape, &dm));
+    if (!valid_dtype(w_dt)) return fail(SRU_ERR_INVALID_ARG, "unknown dtype");
+    SRU_TRY(need_ptr(W, "W"));
+    SRU_TRY(need_ptr(Wt, "Wt"));
+    const int64_t rows = 3 * dm.ndir * shape->d, cols = shape->d;
+    const size_t bytes = (size_t)rows * (size_t)cols * (w_dt == SRU_BF16 ? 2 : 4);
+    const uintptr_t a = (uintptr_t)W, b = (uintptr_t)Wt;
+    if (a < b + bytes && b < a + bytes) return fail(SRU_ERR_INVALID_ARG, "W and Wt overlap");
+    if ((cols + 63) / 64 > 65535 * 1024LL || (rows + 63) / 64 > 65535)
+        return fail(SRU_ERR_INVALID_ARG, "matrix too large for one transpose launch");
+    SRU_TRY(need_device());
+    return launched(sru::launch_transpose(rows, cols, W, Wt, w_dt == SRU_BF16, (hipStream_t)stream),
+                    "weight transpose");
 }
 
 sru_status sru_forward(const sru_shape *shape, const void *U, sru_dtype u_dt, const void *x,

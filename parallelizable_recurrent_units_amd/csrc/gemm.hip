@@ -5,11 +5,20 @@
 // bf16 path: v_mfma_f32_32x32x16_bf16 (gfx950) with fp32 accumulation.  The
 // A operand may arrive as fp32; it is rounded to bf16 (nearest even) while
 // it is staged into LDS, so no separate conversion pass touches HBM.
-// W is bf16 in HBM and is used either as [N, K] (forward: C = A W^T, both
-// operands K-contiguous) or as [K, N] (backward-data: C = A W, W is
-// transposed while it is staged into LDS).
+// B (the weights) is bf16 and is used either as [N, K] (C = A B^T, both
+// operands K-contiguous: the forward projection, and the backward-data
+// product when W has been transposed once by sru_transpose_weight) or as
+// [K, N] (C = A B, transposed while it is staged into LDS).
+//
+// Block tiles: 4 waves in a 2 x 2 grid, each wave a (BM/2) x (BN/2) tile of
+// 32 x 32 MFMA blocks.  LDS bytes read per MFMA fall as the wave tile grows
+// (1 KB at 64 x 64, 512 B at 128 x 128), so large problems use 256 x 256
+// blocks (one per CU, accumulators in AGPRs) and small ones 128 x 128 blocks
+// (two per CU) to keep every CU busy.
 //
 // fp32 path (W in fp32): LDS-tiled FMA kernel, fp32 products and sums.
+#include <stdlib.h>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -21,32 +30,42 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Block tile BM x BN x BK with 4 waves in a 2 x 2 grid, each wave a
-// (BM/2) x (BN/2) tile of 32 x 32 MFMA blocks.
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDK = BK + 8;    // padded LDS row (bf16): 144 bytes, keeps the
-                               // 16-byte operand reads of 8 rows on distinct banks
-constexpr int NT = 256;
-constexpr int WM = BM / 2, WN = BN / 2;
-constexpr int TI = WM / 32, TJ = WN / 32;
-constexpr int EPI_LD = WN + 4; // fp32 epilogue staging row (per wave)
+constexpr int NT = 256;   // threads per block: 4 waves
+
+template <int BM_, int BN_, int BK_, int STAGES_, int MINB_>
+struct TileCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_;
+    static constexpr int STAGES = STAGES_;   // register stages of prefetched k-tiles
+    static constexpr int MINB = MINB_;       // blocks per CU the registers are sized for
+    static constexpr int LDK = BK + 8;       // padded LDS row (bf16): 80 or 144 bytes
+                                             // keeps 16-byte reads of 8 rows on distinct banks
+    static constexpr int WM = BM / 2, WN = BN / 2;
+    static constexpr int TI = WM / 32, TJ = WN / 32;
+    static constexpr int EPI_LD = WN + 4;    // fp32 epilogue staging row
+    static constexpr int LDS_BYTES = 2 * (BM + BN) * LDK * 2;
+    static_assert(LDS_BYTES >= 4 * 32 * EPI_LD * 4, "epilogue staging must fit in LDS");
+};
+
+typedef TileCfg<128, 128, 64, 1, 2> CfgSmall;
+typedef TileCfg<256, 128, 64, 1, 1> CfgMid;
+typedef TileCfg<256, 256, 64, 1, 1> CfgBig;
 
 // ---- A tile (BM x BK) -> registers -> LDS (bf16) --------------------------
 // FAST (K % BK == 0): every thread's element offsets inside the k-tile window
-// are loop invariant 32-bit values (rows past M are clamped to M - 1: they
-// load valid memory whose results the epilogue never writes), and the
+// are loop invariant 32-bit byte offsets (rows past M are clamped to M - 1:
+// they load valid memory whose results the epilogue never writes), and the
 // window's base pointer is uniform.  Otherwise every element is bounds
 // checked.
-template <typename TA, bool FAST>
+template <class Cfg, typename TA, bool FAST>
 struct ALoader {
     static constexpr int V = 16 / sizeof(TA);            // elements per 16 bytes
-    static constexpr int PER_ROW = BK / V;
-    static constexpr int N = BM * PER_ROW / NT;          // 16-byte loads per thread
+    static constexpr int PER_ROW = Cfg::BK / V;
+    static constexpr int N = Cfg::BM * PER_ROW / NT;     // 16-byte loads per thread
     struct Offsets {
-        uint32_t v[N];                                   // byte offsets (FAST)
+        uint32_t v[N];
     };
     u32x4 reg[N];
-    const Offsets *off = nullptr;                        // shared by both stages
+    const Offsets *off = nullptr;                        // shared by the stages
     __device__ __forceinline__ static void init(Offsets &o, int64_t M, int64_t K, int64_t m0,
                                                 int tid)
     {
@@ -92,7 +111,7 @@ struct ALoader {
         for (int i = 0; i < N; ++i) {
             const int idx = tid + i * NT;
             const int row = idx / PER_ROW, cv = idx % PER_ROW;
-            bf16_bits *dst = As + row * LDK + cv * V;
+            bf16_bits *dst = As + row * Cfg::LDK + cv * V;
             if constexpr (sizeof(TA) == 4) {   // round fp32 -> bf16 (nearest even) here
                 const u32x4 u = reg[i];
                 u32x2 packed;
@@ -110,18 +129,18 @@ struct ALoader {
 
 // ---- B tile -> LDS as Bs[n][k] (BN x BK) ----------------------------------
 // KN = false: B is [N, K] (k contiguous), copied row by row.
-// KN = true : B is [K, N] (n contiguous).  Each thread gathers 16 k-values of
+// KN = true : B is [K, N] (n contiguous).  Each thread gathers KG k-values of
 //             two adjacent columns with 4-byte loads (a wave reads 256
-//             contiguous bytes of one k-row per load) and writes them as four
+//             contiguous bytes of one k-row per load) and writes them as
 //             16-byte LDS rows, so the tile is transposed without 2-byte LDS
 //             stores.
-template <bool KN, bool FAST>
+template <class Cfg, bool KN, bool FAST>
 struct BLoader;
 
-template <bool FAST>
-struct BLoader<false, FAST> {
-    static constexpr int PER_ROW = BK / 8;
-    static constexpr int N = BN * PER_ROW / NT;
+template <class Cfg, bool FAST>
+struct BLoader<Cfg, false, FAST> {
+    static constexpr int PER_ROW = Cfg::BK / 8;
+    static constexpr int N = Cfg::BN * PER_ROW / NT;
     struct Offsets {
         uint32_t v[N];
     };
@@ -169,17 +188,17 @@ struct BLoader<false, FAST> {
         for (int i = 0; i < N; ++i) {
             const int idx = tid + i * NT;
             const int row = idx / PER_ROW, cv = idx % PER_ROW;
-            *(u32x4 *)(Bs + row * LDK + cv * 8) = reg[i];
+            *(u32x4 *)(Bs + row * Cfg::LDK + cv * 8) = reg[i];
         }
     }
 };
 
-template <bool FAST>
-struct BLoader<true, FAST> {
-    // BN/2 column pairs x (NT / (BN/2)) k-groups of KG rows
-    static constexpr int NP = BN / 2;
-    static constexpr int KQ = NT / NP;
-    static constexpr int KG = BK / KQ;                   // 16
+template <class Cfg, bool FAST>
+struct BLoader<Cfg, true, FAST> {
+    static constexpr int NP = Cfg::BN / 2;               // column pairs
+    static constexpr int KQ = NT / NP;                   // k-groups
+    static constexpr int KG = Cfg::BK / KQ;              // k-rows per thread
+    static_assert(KG % 8 == 0, "whole 16-byte LDS rows");
     struct Offsets {
         uint32_t v;                                      // byte offset
     };
@@ -226,8 +245,8 @@ struct BLoader<true, FAST> {
             const uint32_t *r = reg + h * 8;
             const u32x4 lo = {lo2(r[0], r[1]), lo2(r[2], r[3]), lo2(r[4], r[5]), lo2(r[6], r[7])};
             const u32x4 hi = {hi2(r[0], r[1]), hi2(r[2], r[3]), hi2(r[4], r[5]), hi2(r[6], r[7])};
-            *(u32x4 *)(Bs + (2 * np) * LDK + kq * KG + h * 8) = lo;
-            *(u32x4 *)(Bs + (2 * np + 1) * LDK + kq * KG + h * 8) = hi;
+            *(u32x4 *)(Bs + (2 * np) * Cfg::LDK + kq * KG + h * 8) = lo;
+            *(u32x4 *)(Bs + (2 * np + 1) * Cfg::LDK + kq * KG + h * 8) = hi;
         }
     }
 };
@@ -237,14 +256,13 @@ struct BLoader<true, FAST> {
 // (bid % 8) * (T / 8) + bid / 8, so every XCD works through one contiguous
 // range of tiles; within the logical order, groups of 8 row tiles sweep the
 // column tiles so neighbouring tiles share A rows and B columns in that L2.
-__device__ __forceinline__ void tile_of(int64_t bid, int64_t TM, int64_t TN, int64_t *tm,
-                                        int64_t *tn)
+__device__ __forceinline__ void tile_of(int64_t bid, int64_t TM, int64_t TN, int64_t GM,
+                                        int64_t *tm, int64_t *tn)
 {
     const int64_t T = TM * TN;
     const int64_t T8 = T / 8;
     int64_t lt = bid;
     if (bid < 8 * T8) lt = (bid % 8) * T8 + bid / 8;
-    constexpr int64_t GM = 8;
     const int64_t group = lt / (GM * TN);
     const int64_t first = group * GM;
     const int64_t gsz = (TM - first) < GM ? (TM - first) : GM;
@@ -254,23 +272,17 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t TM, int64_t TN, int
 }
 
 // C[M, N] (+)= A[M, K] . B  with B given as [N, K] (KN = false) or [K, N].
-#ifndef SRU_GEMM_MIN_BLOCKS
-#define SRU_GEMM_MIN_BLOCKS 2
-#endif
-#ifndef SRU_GEMM_STAGES
-#define SRU_GEMM_STAGES 1   // register stages; 1 measured fastest at 2 blocks/CU
-#endif
-
-template <typename TA, bool KN, bool FAST>
-__global__ __launch_bounds__(NT, SRU_GEMM_MIN_BLOCKS) void gemm_bf16_mfma(int64_t M, int64_t N, int64_t K,
-                                                        const TA *__restrict__ A,
-                                                        const bf16_bits *__restrict__ Bm,
-                                                        float *__restrict__ C, bool accumulate)
+template <class Cfg, typename TA, bool KN, bool FAST>
+__global__ __launch_bounds__(NT, Cfg::MINB) void gemm_bf16_mfma(int64_t M, int64_t N, int64_t K,
+                                                               const TA *__restrict__ A,
+                                                               const bf16_bits *__restrict__ Bm,
+                                                               float *__restrict__ C,
+                                                               bool accumulate, int gm)
 {
-    // two stages of A and B tiles; reused as fp32 staging by the epilogue
-    constexpr int STAGE = (BM + BN) * LDK;               // bf16 elements
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, LDK = Cfg::LDK;
+    constexpr int WM = Cfg::WM, WN = Cfg::WN, TI = Cfg::TI, TJ = Cfg::TJ;
+    constexpr int STAGE = (BM + BN) * LDK;               // bf16 elements per LDS stage
     __shared__ __attribute__((aligned(16))) bf16_bits smem[2 * STAGE];
-    static_assert(2 * STAGE * 2 >= 4 * WM * EPI_LD * 4, "epilogue staging must fit");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -278,14 +290,14 @@ __global__ __launch_bounds__(NT, SRU_GEMM_MIN_BLOCKS) void gemm_bf16_mfma(int64_
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t TM = (M + BM - 1) / BM, TN = (N + BN - 1) / BN;
     int64_t tm, tn;
-    tile_of(blockIdx.x, TM, TN, &tm, &tn);
+    tile_of(blockIdx.x, TM, TN, gm, &tm, &tn);
     const int64_t m0 = tm * BM, n0 = tn * BN;
 
     bf16_bits *As0 = smem, *Bs0 = smem + BM * LDK;
     bf16_bits *As1 = smem + STAGE, *Bs1 = smem + STAGE + BM * LDK;
 
-    typedef ALoader<TA, FAST> AL;
-    typedef BLoader<KN, FAST> BL;
+    typedef ALoader<Cfg, TA, FAST> AL;
+    typedef BLoader<Cfg, KN, FAST> BL;
     typename AL::Offsets aoff;
     typename BL::Offsets boff;
     AL::init(aoff, M, K, m0, tid);
@@ -294,6 +306,7 @@ __global__ __launch_bounds__(NT, SRU_GEMM_MIN_BLOCKS) void gemm_bf16_mfma(int64_
     BL lb0, lb1;
     la0.off = la1.off = &aoff;
     lb0.off = lb1.off = &boff;
+
     f32x16 acc[TI][TJ];
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -305,7 +318,7 @@ __global__ __launch_bounds__(NT, SRU_GEMM_MIN_BLOCKS) void gemm_bf16_mfma(int64_
     const int r32 = lane & 31;
     const int kg = (lane >> 5) * 8;
     auto compute = [&](const bf16_bits *As, const bf16_bits *Bs) {
-#pragma unroll
+#pragma unroll 2   // full unrolling hoists every fragment read and spills
         for (int ks = 0; ks < BK / 16; ++ks) {
             bf16x8 af[TI], bfr[TJ];
 #pragma unroll
@@ -324,8 +337,7 @@ __global__ __launch_bounds__(NT, SRU_GEMM_MIN_BLOCKS) void gemm_bf16_mfma(int64_
     };
 
     // Software pipeline: k-tile kt is in LDS stage kt % 2 while the loads of
-    // k-tile kt + 1 (or, with two register stages, kt + 1 and kt + 2) are in
-    // flight, and two blocks per CU interleave.  The body has no conditional
+    // the next STAGES k-tiles are in flight.  The body has no conditional
     // loads or stores (prefetch indices are clamped to the last k-tile; the
     // surplus loads re-read it), which keeps the compiler's wait counts
     // exact: a stage waits only for its own loads.
@@ -335,87 +347,131 @@ __global__ __launch_bounds__(NT, SRU_GEMM_MIN_BLOCKS) void gemm_bf16_mfma(int64_
     lb0.load(Bm, N, K, n0, 0, tid);
     la0.store(As0, tid);
     lb0.store(Bs0, tid);
-#if SRU_GEMM_STAGES == 2
-    la1.load(A, M, K, m0, kc(1), tid);
-    lb1.load(Bm, N, K, n0, kc(1), tid);
-    __syncthreads();
-    for (int64_t kt = 0;; kt += 2) {
-        la0.load(A, M, K, m0, kc(kt + 2), tid);
-        lb0.load(Bm, N, K, n0, kc(kt + 2), tid);
-        compute(As0, Bs0);
-        la1.store(As1, tid);
-        lb1.store(Bs1, tid);
+    if constexpr (Cfg::STAGES == 2) {
+        la1.load(A, M, K, m0, kc(1), tid);
+        lb1.load(Bm, N, K, n0, kc(1), tid);
         __syncthreads();
-        if (kt + 1 >= KT) break;
-        la1.load(A, M, K, m0, kc(kt + 3), tid);
-        lb1.load(Bm, N, K, n0, kc(kt + 3), tid);
-        compute(As1, Bs1);
-        la0.store(As0, tid);
-        lb0.store(Bs0, tid);
+        for (int64_t kt = 0;; kt += 2) {
+            la0.load(A, M, K, m0, kc(kt + 2), tid);
+            lb0.load(Bm, N, K, n0, kc(kt + 2), tid);
+            compute(As0, Bs0);
+            la1.store(As1, tid);
+            lb1.store(Bs1, tid);
+            __syncthreads();
+            if (kt + 1 >= KT) break;
+            la1.load(A, M, K, m0, kc(kt + 3), tid);
+            lb1.load(Bm, N, K, n0, kc(kt + 3), tid);
+            compute(As1, Bs1);
+            la0.store(As0, tid);
+            lb0.store(Bs0, tid);
+            __syncthreads();
+            if (kt + 2 >= KT) break;
+        }
+    } else {
         __syncthreads();
-        if (kt + 2 >= KT) break;
+        for (int64_t kt = 0;; kt += 2) {
+            la0.load(A, M, K, m0, kc(kt + 1), tid);
+            lb0.load(Bm, N, K, n0, kc(kt + 1), tid);
+            compute(As0, Bs0);
+            la0.store(As1, tid);
+            lb0.store(Bs1, tid);
+            __syncthreads();
+            if (kt + 1 >= KT) break;
+            la0.load(A, M, K, m0, kc(kt + 2), tid);
+            lb0.load(Bm, N, K, n0, kc(kt + 2), tid);
+            compute(As1, Bs1);
+            la0.store(As0, tid);
+            lb0.store(Bs0, tid);
+            __syncthreads();
+            if (kt + 2 >= KT) break;
+        }
     }
-#else
-    __syncthreads();
-    for (int64_t kt = 0;; kt += 2) {
-        la0.load(A, M, K, m0, kc(kt + 1), tid);
-        lb0.load(Bm, N, K, n0, kc(kt + 1), tid);
-        compute(As0, Bs0);
-        la0.store(As1, tid);
-        lb0.store(Bs1, tid);
-        __syncthreads();
-        if (kt + 1 >= KT) break;
-        la0.load(A, M, K, m0, kc(kt + 2), tid);
-        lb0.load(Bm, N, K, n0, kc(kt + 2), tid);
-        compute(As1, Bs1);
-        la0.store(As0, tid);
-        lb0.store(Bs0, tid);
-        __syncthreads();
-        if (kt + 2 >= KT) break;
-    }
-    (void)la1;
-    (void)lb1;
-#endif
 
-    // Epilogue: each wave stages its WM x WN fp32 tile in LDS (rows of the
-    // 32x32 accumulator layout: column lane & 31, rows 8*(r/4) + 4*(lane/32)
-    // + r%4) and writes it back as 16-byte row segments.
-    float *stage = (float *)smem + wave * (WM * EPI_LD);
+    // Epilogue, one 32-row band of the wave tile at a time: stage it in LDS
+    // (the 32x32 accumulator layout holds column lane & 31 and rows
+    // 8*(r/4) + 4*(lane/32) + r%4) and write it back as 16-byte row segments.
+    // Each wave uses its own staging area; LDS operations of one wave complete
+    // in order, so no barrier is needed between bands.
+    constexpr int EPI_LD = Cfg::EPI_LD;
+    float *stage = (float *)smem + wave * (32 * EPI_LD);
+    constexpr int C4 = WN / 4;                           // float4 per staged row
+    const int64_t nw = n0 + wn * WN;
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+    for (int i = 0; i < TI; ++i) {
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+                const int row = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
                 stage[row * EPI_LD + j * 32 + r32] = acc[i][j][r];
             }
-    // (LDS operations of one wave complete in order: no barrier needed here)
-    constexpr int C4 = WN / 4;            // float4 per staged row
-    const int64_t mw = m0 + wm * WM, nw = n0 + wn * WN;
+        const int64_t mw = m0 + wm * WM + i * 32;
 #pragma unroll 4
-    for (int it = 0; it < WM * C4 / 64; ++it) {
-        const int idx = it * 64 + lane;
-        const int row = idx / C4, c4 = idx % C4;
-        const int64_t m = mw + row, n = nw + c4 * 4;
-        if (m >= M) continue;
-        const float4 v = *(const float4 *)(stage + row * EPI_LD + c4 * 4);
-        float *p = C + m * N + n;
-        if (FAST) {   // N % 4 == 0
-            if (n < N) {
-                float4 o = v;
-                if (accumulate) {
-                    const float4 c = *(const float4 *)p;
-                    o.x += c.x; o.y += c.y; o.z += c.z; o.w += c.w;
+        for (int it = 0; it < 32 * C4 / 64; ++it) {
+            const int idx = it * 64 + lane;
+            const int row = idx / C4, c4 = idx % C4;
+            const int64_t m = mw + row, n = nw + c4 * 4;
+            if (m >= M) continue;
+            const float4 v = *(const float4 *)(stage + row * EPI_LD + c4 * 4);
+            float *p = C + m * N + n;
+            if (FAST) {   // N % 4 == 0
+                if (n < N) {
+                    float4 o = v;
+                    if (accumulate) {
+                        const float4 c = *(const float4 *)p;
+                        o.x += c.x; o.y += c.y; o.z += c.z; o.w += c.w;
+                    }
+                    *(float4 *)p = o;
                 }
-                *(float4 *)p = o;
-            }
-        } else {
-            const float vv[4] = {v.x, v.y, v.z, v.w};
+            } else {
+                const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (n + e < N) p[e] = accumulate ? p[e] + vv[e] : vv[e];
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) p[e] = accumulate ? p[e] + vv[e] : vv[e];
+            }
         }
+    }
+}
+
+// dst[c][r] = src[r][c] for a rows x cols matrix of 2-byte elements, through
+// padded 64 x 64 LDS tiles (coalesced reads and writes).
+__global__ __launch_bounds__(256) void transpose16(int64_t rows, int64_t cols,
+                                                   const uint16_t *__restrict__ src,
+                                                   uint16_t *__restrict__ dst)
+{
+    __shared__ uint16_t t[64][66];
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int64_t r = r0 + ty * 16 + k, c = c0 + tx;
+        if (r < rows && c < cols) t[ty * 16 + k][tx] = src[r * cols + c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int64_t c = c0 + ty * 16 + k, r = r0 + tx;
+        if (r < rows && c < cols) dst[c * rows + r] = t[tx][ty * 16 + k];
+    }
+}
+
+__global__ __launch_bounds__(256) void transpose32(int64_t rows, int64_t cols,
+                                                   const float *__restrict__ src,
+                                                   float *__restrict__ dst)
+{
+    __shared__ float t[64][65];
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int64_t r = r0 + ty * 16 + k, c = c0 + tx;
+        if (r < rows && c < cols) t[ty * 16 + k][tx] = src[r * cols + c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int64_t c = c0 + ty * 16 + k, r = r0 + tx;
+        if (r < rows && c < cols) dst[c * rows + r] = t[tx][ty * 16 + k];
     }
 }
 
@@ -482,23 +538,44 @@ __global__ __launch_bounds__(256) void gemm_f32(int64_t M, int64_t N, int64_t K,
     }
 }
 
+template <class Cfg, typename TA, bool KN>
+hipError_t mfma_launch_cfg(const GemmArgs &g, hipStream_t s)
+{
+    const int64_t tiles = ((g.M + Cfg::BM - 1) / Cfg::BM) * ((g.N + Cfg::BN - 1) / Cfg::BN);
+    // fast variant: whole k-tiles, 4-aligned C rows, byte offsets inside a
+    // tile window below 2^32, and (for B as [K, N]) dword column pairs
+    const bool fast = (g.K % Cfg::BK == 0) && (g.N % 4 == 0) &&
+                      (g.K * Cfg::BM * 4 < (int64_t(1) << 32)) &&
+                      (!KN || (g.N % 2 == 0 && g.N * Cfg::BK * 2 < (int64_t(1) << 32)));
+    int gm = 8;
+    if (const char *e = getenv("SRU_GEMM_GM")) gm = atoi(e);   // tuning override
+    if (fast)
+        hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, TA, KN, true>), dim3((unsigned)tiles), dim3(NT), 0,
+                           s, g.M, g.N, g.K, (const TA *)g.A, (const bf16_bits *)g.Bm, g.C,
+                           g.accumulate, gm);
+    else
+        hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, TA, KN, false>), dim3((unsigned)tiles), dim3(NT), 0,
+                           s, g.M, g.N, g.K, (const TA *)g.A, (const bf16_bits *)g.Bm, g.C,
+                           g.accumulate, gm);
+    return hipGetLastError();
+}
+
+int64_t tiles_of(const GemmArgs &g, int bm, int bn)
+{
+    return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
+}
+
 template <typename TA, bool KN>
 hipError_t mfma_launch(const GemmArgs &g, hipStream_t s)
 {
-    const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-    // fast variant: whole k-tiles, 16-byte rows everywhere, 4-aligned C rows,
-    // and (for B as [K, N]) dword column pairs
-    const bool fast = (g.K % BK == 0) && (g.N % 4 == 0) && (g.K * BM < (int64_t(1) << 31)) &&
-                      (!KN || g.N * BK < (int64_t(1) << 31));
-    if (fast)
-        hipLaunchKernelGGL((gemm_bf16_mfma<TA, KN, true>), dim3((unsigned)tiles), dim3(NT), 0, s,
-                           g.M, g.N, g.K, (const TA *)g.A, (const bf16_bits *)g.Bm, g.C,
-                           g.accumulate);
-    else
-        hipLaunchKernelGGL((gemm_bf16_mfma<TA, KN, false>), dim3((unsigned)tiles), dim3(NT), 0, s,
-                           g.M, g.N, g.K, (const TA *)g.A, (const bf16_bits *)g.Bm, g.C,
-                           g.accumulate);
-    return hipGetLastError();
+    // The largest block tile that still gives every CU (256) a tile, so the
+    // wave tiles are as large as the grid allows.
+    int cfg = 0;
+    if (const char *e = getenv("SRU_GEMM_TILE")) cfg = atoi(e);   // tuning override
+    if (cfg == 0) cfg = tiles_of(g, 256, 256) >= 512 ? 3 : 1;
+    if (cfg == 3) return mfma_launch_cfg<CfgBig, TA, KN>(g, s);
+    if (cfg == 2) return mfma_launch_cfg<CfgMid, TA, KN>(g, s);
+    return mfma_launch_cfg<CfgSmall, TA, KN>(g, s);
 }
 
 template <typename TA, bool KN>
@@ -511,6 +588,19 @@ hipError_t f32_launch(const GemmArgs &g, hipStream_t s)
 }
 
 }  // namespace
+
+hipError_t launch_transpose(int64_t rows, int64_t cols, const void *src, void *dst, bool two_byte,
+                            hipStream_t s)
+{
+    dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+    if (two_byte)
+        hipLaunchKernelGGL(transpose16, grid, dim3(256), 0, s, rows, cols, (const uint16_t *)src,
+                           (uint16_t *)dst);
+    else
+        hipLaunchKernelGGL(transpose32, grid, dim3(256), 0, s, rows, cols, (const float *)src,
+                           (float *)dst);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s)
 {

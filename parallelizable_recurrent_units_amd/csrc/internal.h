@@ -73,5 +73,8 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
+// dst[cols, rows] = src[rows, cols]^T (2-byte or 4-byte elements).
+hipError_t launch_transpose(int64_t rows, int64_t cols, const void *src, void *dst, bool two_byte,
+                            hipStream_t s);
 
 }  // namespace sru

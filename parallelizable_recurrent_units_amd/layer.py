@@ -19,12 +19,27 @@ def project(shape, X, W, U=None, accumulate=False, stream=None):
     return U
 
 
-def project_bwd_data(shape, dU, W, dX=None, accumulate=False, stream=None):
-    """dX[L*B, d] (+)= dU W (gradient through Eq. 1)."""
+def transpose_weight(shape, W, Wt=None, stream=None):
+    """Wt = W^T ([d, ndir*3d]) for the transposed backward-data product."""
+    s = B._shape(shape)
+    if Wt is None:
+        Wt = torch.empty((s.d, s.ndir * 3 * s.d), device=W.device, dtype=W.dtype)
+    B.sru_transpose_weight(s, W, Wt, stream)
+    return Wt
+
+
+def project_bwd_data(shape, dU, W, dX=None, accumulate=False, Wt=None, stream=None):
+    """dX[L*B, d] (+)= dU W (gradient through Eq. 1).
+
+    With ``Wt`` (= W^T from transpose_weight) the K-contiguous kernel path is
+    used; otherwise W is transposed while it is staged into LDS."""
     s = B._shape(shape)
     if dX is None:
         dX = torch.empty((s.L, s.B, s.d), device=dU.device, dtype=torch.float32)
-    B.sru_project(s, B.SRU_PROJ_BWD_DATA, dU, W, dX, accumulate, stream)
+    if Wt is not None:
+        B.sru_project(s, B.SRU_PROJ_BWD_DATA_WT, dU, Wt, dX, accumulate, stream)
+    else:
+        B.sru_project(s, B.SRU_PROJ_BWD_DATA, dU, W, dX, accumulate, stream)
     return dX
 
 

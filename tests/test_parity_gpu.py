@@ -180,6 +180,12 @@ def test_projection_bf16(L, B, d, nd):
     Gr = oracle.round_bf16(G).reshape(L * B, -1)
     ref_r = oracle.project_bwd_data(Gr, W) + C0.reshape(L * B, d)
     check("dX vs bf16(dU) oracle", host(dX).reshape(L * B, d), ref_r, GEMM_ACC)
+    # the same product through the transposed weights (K-contiguous path)
+    Wt = layer.transpose_weight(shape, Wd)
+    assert np.array_equal(host(Wt), W.T.astype(np.float64))
+    dX2 = torch.from_numpy(C0.copy()).cuda()
+    layer.project_bwd_data(shape, torch.from_numpy(G).cuda(), Wd, dX2, accumulate=True, Wt=Wt)
+    check("dX (transposed W) vs bf16(dU) oracle", host(dX2).reshape(L * B, d), ref_r, GEMM_ACC)
 
 
 def test_projection_fp32_config1():
