@@ -5,8 +5,8 @@
 
 One step = one pass of the whole hot path over one batch: projection GEMM
 (U = X~ W^T), forward recurrence, backward recurrence with the fused dv/db
-reduction, and the backward-data GEMM (W transposed once, then
-dX = dU W + highway dx).  The headline
+reduction (which also writes dU rounded to bf16), and the backward-data GEMM
+(W transposed once, then dX = bf16(dU) W + highway dx).  The headline
 workload is the bidirectional layer L=64, B=128, d=512 (fp32 activations,
 bf16 W).  Inputs are seeded synthetic draws (no dataset), resident in HBM
 before the timed region; several input/output sets rotate so consecutive steps
@@ -120,6 +120,7 @@ def device_set(w, seed):
     dev.update(U=torch.empty((L, B, nd, 3, d), **f32), h=torch.empty((L, B, nd, d), **f32),
                c_seq=torch.empty((L, B, nd, d), **f32), c_last=torch.empty((nd, B, d), **f32),
                dU=torch.empty((L, B, nd, 3, d), **f32), dx=torch.empty((L, B, d), **f32),
+               dU_lp=torch.empty((L, B, nd, 3, d), device="cuda", dtype=torch.bfloat16),
                dv=torch.empty((nd, 2, d), **f32), db=torch.empty((nd, 2, d), **f32),
                dc0=torch.empty((nd, B, d), **f32),
                Wt=torch.empty((d, nd * 3 * d), device="cuda", dtype=dev["W"].dtype),
@@ -136,7 +137,7 @@ def training_step_rows(shape, t):
 
     def bwd_data():
         sru_transpose_weight(shape, t["W"], t["Wt"])
-        sru_project(shape, SRU_PROJ_BWD_DATA_WT, t["dU"], t["Wt"], t["dx"], True)
+        sru_project(shape, SRU_PROJ_BWD_DATA_WT, t["dU_lp"], t["Wt"], t["dx"], True)
 
     return [
         ("a1_projection", lambda: sru_project(shape, SRU_PROJ_FWD, t["x"], t["W"], t["U"])),
@@ -144,7 +145,8 @@ def training_step_rows(shape, t):
                                            t["c_seq"], t["c_last"])),
         ("a3_a4_backward", lambda: sru_backward(shape, t["U"], t["x"], t["v"], t["b"], t["c0"],
                                                 t["c_seq"], t["dh"], t["dc_last"], t["dU"],
-                                                t["dx"], t["dv"], t["db"], t["dc0"], t["ws"])),
+                                                t["dx"], t["dv"], t["db"], t["dc0"], t["ws"],
+                                                t["dU_lp"])),
         ("a5_projection_bwd_data", bwd_data),
     ]
 

@@ -131,6 +131,10 @@ sru_status sru_forward(const sru_shape *shape,
  * is derived).  Needs the forward's c_seq.
  *   dh: fp32 [L, B, ndir, d] (required); dc_last: fp32 or NULL (zero).
  *   dU: fp32 [L, B, ndir, 3, d] (required, overwritten).
+ *   dU_lp: bf16 [L, B, ndir, 3, d] or NULL: a copy of dU rounded to bf16
+ *       (nearest even), i.e. exactly the operand the bf16 backward-data
+ *       projection multiplies; passing it as A there halves that GEMM's
+ *       operand bytes.
  *   dx: fp32 [L, B, d] (required, overwritten): the highway part
  *       alpha (1 - r) dh summed over directions.  The part through the
  *       projection comes from sru_project(SRU_PROJ_BWD_DATA, accumulate = 1).
@@ -145,7 +149,7 @@ sru_status sru_backward(const sru_shape *shape,
                         const void *x, sru_dtype x_dt,
                         const float *v, const float *b, const float *c0,
                         const float *c_seq, const float *dh, const float *dc_last,
-                        float *dU, float *dx, float *dv, float *db, float *dc0,
+                        float *dU, void *dU_lp, float *dx, float *dv, float *db, float *dc0,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*

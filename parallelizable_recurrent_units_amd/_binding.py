@@ -71,7 +71,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                 ctypes.c_int, _vp, _vp, _vp]
     lib.sru_backward.restype = ctypes.c_int
     lib.sru_backward.argtypes = [sp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
-                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp]
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp]
     lib.sru_linear_scan.restype = ctypes.c_int
     lib.sru_linear_scan.argtypes = [sp, ctypes.c_int, i32, _vp, ctypes.c_int, _vp, ctypes.c_int,
                                     _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -156,13 +156,15 @@ def sru_forward(shape, U, x, v, b, c0, h, c_seq=None, c_last=None, stream=None):
 
 
 def sru_backward(shape, U, x, v, b, c0, c_seq, dh, dc_last, dU, dx, dv, db, dc0,
-                 workspace, stream=None):
+                 workspace, dU_lp=None, stream=None):
     s = _shape(shape)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if dU_lp is not None and _dtype_code(dU_lp) != SRU_BF16:
+        raise TypeError("dU_lp must be bfloat16")
     _check(load_library().sru_backward(ctypes.byref(s), _ptr(U), _dtype_code(U), _ptr(x),
                                        _dtype_code(x), _ptr(v), _ptr(b), _ptr(c0), _ptr(c_seq),
-                                       _ptr(dh), _ptr(dc_last), _ptr(dU), _ptr(dx), _ptr(dv),
-                                       _ptr(db), _ptr(dc0), _ptr(workspace), ws_bytes,
+                                       _ptr(dh), _ptr(dc_last), _ptr(dU), _ptr(dU_lp), _ptr(dx),
+                                       _ptr(dv), _ptr(db), _ptr(dc0), _ptr(workspace), ws_bytes,
                                        _stream(stream)))
 
 

@@ -257,7 +257,7 @@ sru_status sru_forward(const sru_shape *shape, const void *U, sru_dtype u_dt, co
 sru_status sru_backward(const sru_shape *shape, const void *U, sru_dtype u_dt, const void *x,
                         sru_dtype x_dt, const float *v, const float *b, const float *c0,
                         const float *c_seq, const float *dh, const float *dc_last, float *dU,
-                        float *dx, float *dv, float *db, float *dc0, void *workspace,
+                        void *dU_lp, float *dx, float *dv, float *db, float *dc0, void *workspace,
                         size_t workspace_bytes, void *stream)
 {
     Dims dm;
@@ -273,6 +273,7 @@ sru_status sru_backward(const sru_shape *shape, const void *U, sru_dtype u_dt, c
     SRU_TRY(need_ptr(dh, "dh"));
     SRU_TRY(opt_ptr(dc_last, "dc_last"));
     SRU_TRY(need_ptr(dU, "dU"));
+    SRU_TRY(opt_ptr(dU_lp, "dU_lp"));
     SRU_TRY(need_ptr(dx, "dx"));
     SRU_TRY(opt_ptr(dv, "dv"));
     SRU_TRY(opt_ptr(db, "db"));
@@ -300,6 +301,7 @@ sru_status sru_backward(const sru_shape *shape, const void *U, sru_dtype u_dt, c
     a.dh = dh;
     a.dc_last = dc_last;
     a.dU = dU;
+    a.dU_lp = (sru::bf16_bits_t *)dU_lp;
     a.dx = dx;
     a.dc0 = dc0;
     a.partials = (float *)workspace;

@@ -21,6 +21,16 @@ __device__ __forceinline__ bf16_bits f32_to_bf16(float f)
     return __builtin_bit_cast(bf16_bits, b);
 }
 
+// Two fp32 values -> two bf16 (nearest even) in one dword, low half first
+// (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 template <typename T> __device__ __forceinline__ float load_as_f32(const T *p);
 template <> __device__ __forceinline__ float load_as_f32<float>(const float *p) { return *p; }
 template <> __device__ __forceinline__ float load_as_f32<bf16_bits>(const bf16_bits *p)
@@ -33,18 +43,24 @@ template <> __device__ __forceinline__ float load_as_f32<bf16_bits>(const bf16_b
 // base-2 exponential and reciprocal (v_exp_f32, v_rcp_f32).  The complement
 // is never formed as 1 - g: with g close to 1 (e.g. forget gates at
 // sigma(8) = 0.9997) the subtraction would keep only ~11 significant bits.
-// e^-z is capped at 2^64 so that e^-z * g stays finite (g = 2^-64, gc = 1
-// for very negative z); NaN passes through.
+//
+// gate_scaled takes y = -z log2(e) (callers fold -log2(e) into their
+// parameters once).  y is capped at 64 so that 2^y g stays finite: for very
+// negative z, g = 2^-64 and gc = 1.  A NaN pre-activation takes the cap too
+// (the gate saturates closed) instead of propagating.
 struct Gate {
     float g, gc;
 };
 
-__device__ __forceinline__ Gate gate(float z)
+constexpr float kNegLog2e = -1.4426950408889634f;
+
+__device__ __forceinline__ Gate gate_scaled(float y)
 {
-    float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
-    e = e > 0x1p64f ? 0x1p64f : e;
+    const float e = __builtin_amdgcn_exp2f(fminf(y, 64.0f));
     const float g = __builtin_amdgcn_rcpf(1.0f + e);
     return {g, e * g};
 }
+
+__device__ __forceinline__ Gate gate(float z) { return gate_scaled(z * kNegLog2e); }
 
 }  // namespace sru

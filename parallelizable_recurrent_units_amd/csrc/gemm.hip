@@ -115,10 +115,8 @@ struct ALoader {
             if constexpr (sizeof(TA) == 4) {   // round fp32 -> bf16 (nearest even) here
                 const u32x4 u = reg[i];
                 u32x2 packed;
-                packed.x = uint32_t(f32_to_bf16(__uint_as_float(u.x))) |
-                           (uint32_t(f32_to_bf16(__uint_as_float(u.y))) << 16);
-                packed.y = uint32_t(f32_to_bf16(__uint_as_float(u.z))) |
-                           (uint32_t(f32_to_bf16(__uint_as_float(u.w))) << 16);
+                packed.x = pack_bf16x2(__uint_as_float(u.x), __uint_as_float(u.y));
+                packed.y = pack_bf16x2(__uint_as_float(u.z), __uint_as_float(u.w));
                 *(u32x2 *)dst = packed;
             } else {
                 *(u32x4 *)dst = reg[i];

@@ -8,6 +8,8 @@
 
 namespace sru {
 
+typedef uint16_t bf16_bits_t;
+
 // Arguments of the forward / backward recurrence launchers.  Element counts
 // and offsets are int64; layouts are those of include/sru.h.
 struct RecArgs {
@@ -24,6 +26,7 @@ struct RecArgs {
     // backward
     const float *c_seq_in, *dh, *dc_last;
     float *dU, *dx, *dc0;
+    bf16_bits_t *dU_lp;  // optional bf16 copy of dU (nearest even)
     float *partials;     // [ndir, B, 4, d] per-chain sums over t
     int dir;             // backward: the one direction this launch walks
     bool dx_accumulate;  // backward: add to dx instead of overwriting

@@ -74,7 +74,9 @@ __global__ __launch_bounds__(256) void fwd_generic(RecArgs a)
 // ---------------------------------------------------------------------------
 // Fast forward: one wavefront per 64 channels, packet loads + register ring.
 // BF16 = U and x both bf16 (a packet then carries two timesteps), else both
-// fp32.  Requires d % 64 == 0 and 16-byte aligned tensors.
+// fp32.  Requires d % 64 == 0, 16-byte aligned tensors, every tensor below
+// 2 GiB and time strides below 16 MiB (the host checks; addresses are then
+// a loop-invariant per-lane pointer plus a 24-bit x 24-bit product).
 //
 // The sequence is walked in groups of G packets.  Per group the wave writes
 // G packets to LDS, refills those ring slots with the packets R ahead, reads
@@ -82,7 +84,10 @@ __global__ __launch_bounds__(256) void fwd_generic(RecArgs a)
 // h and c as 16-byte stores: one LDS round trip per group instead of per
 // step.  The loop body has no conditional memory operations (prefetch
 // indices are clamped), so the compiler's wait counts stay exact; the last
-// L mod (G*SPP) steps run in a short tail with direct loads.
+// L mod (G*SPP) steps run in a short tail with direct loads.  With at most
+// one wave per SIMD on long sequences, the instruction count per step bounds
+// the kernel, so the gate constants are pre-scaled by -log2(e) (each gate is
+// fma, fma, min, exp, add, rcp, mul).
 // ---------------------------------------------------------------------------
 template <bool BF16, int R, int G>
 __global__ __launch_bounds__(kWave) void fwd_fast(RecArgs a)
@@ -105,49 +110,56 @@ __global__ __launch_bounds__(kWave) void fwd_fast(RecArgs a)
     const int64_t L = a.L;
     auto tix = [&](int64_t s) -> int64_t { return dl ? (L - 1 - s) : s; };
 
-    // ---- input packet addressing (per lane) ----
+    // ---- input packets: lane = (timestep in packet, stream, channels) ----
     constexpr int ESZ = BF16 ? 2 : 4;                // element bytes
-    const int e_in = BF16 ? (lane >> 5) : 0;         // timestep within packet
+    const int e_in = BF16 ? (lane >> 5) : 0;
     const int q_in = BF16 ? ((lane >> 3) & 3) : (lane >> 4);  // 0 Uf 1 Ur 2 Ux 3 x
     const int sub_in = BF16 ? (lane & 7) : (lane & 15);
     const int64_t cpl = 16 / ESZ;                    // channels per lane
-    const char *in_base;
-    int64_t in_row, in_tstride;
+    const char *in_ptr;
+    uint32_t in_stride;                              // bytes per time index
     if (q_in < 3) {
-        in_base = (const char *)a.U;
-        in_row = (bb * a.ndir + dl) * 3 * a.d + q_in * a.d + j0 + cpl * sub_in;
-        in_tstride = a.B * a.ndir * 3 * a.d;
+        in_ptr = (const char *)a.U +
+                 ((bb * a.ndir + dl) * 3 * a.d + q_in * a.d + j0 + cpl * sub_in) * ESZ;
+        in_stride = (uint32_t)(a.B * a.ndir * 3 * a.d * ESZ);
     } else {
-        in_base = (const char *)a.x;
-        in_row = bb * a.d + j0 + cpl * sub_in;
-        in_tstride = a.B * a.d;
+        in_ptr = (const char *)a.x + (bb * a.d + j0 + cpl * sub_in) * ESZ;
+        in_stride = (uint32_t)(a.B * a.d * ESZ);
     }
+    // packet p holds direction-steps p*SPP .. p*SPP + SPP - 1; this lane's
+    // time index is tin(p) + e_in (direction 0) or tin(p) + 1 - e_in
+    // (direction 1), tin uniform
+    if (BF16) in_ptr += (int64_t)(dl ? 1 - e_in : e_in) * in_stride;
+    const int64_t Pmax = L / SPP - 1;                // last packet fully inside
     auto load_packet = [&](int64_t p) -> uint4 {
-        int64_t s = p * SPP + e_in;
-        s = s < L ? s : L - 1;                       // clamp: stays in bounds
-        return *(const uint4 *)(in_base + (in_row + tix(s) * in_tstride) * ESZ);
+        p = p < Pmax ? p : Pmax;                     // clamp: stays in bounds
+        const uint32_t t = (uint32_t)(dl ? (L - SPP - p * SPP) : p * SPP);
+        return *(const uint4 *)(in_ptr + __umul24(t, in_stride));
     };
 
-    // ---- output addressing (per lane): lane = (step parity, h|c, 4 channels)
+    // ---- outputs: lane = (step parity, h|c, 4 channels), 2 steps per store
     const int e_out = lane >> 5;
     const int q_out = (lane >> 4) & 1;               // 0 h, 1 c
     const int sub_out = lane & 15;
-    float *out_base = q_out ? a.c_seq : a.h;
-    const int64_t out_row = (bb * a.ndir + dl) * a.d + j0 + 4 * sub_out;
-    const int64_t out_tstride = a.B * a.ndir * a.d;
-    const bool out_on = (out_base != nullptr);
+    float *out_t = q_out ? a.c_seq : a.h;
+    const bool out_on = (out_t != nullptr);
+    const uint32_t out_stride = (uint32_t)(a.B * a.ndir * a.d * 4);
+    char *out_ptr = out_on ? (char *)(out_t + (bb * a.ndir + dl) * a.d + j0 + 4 * sub_out) +
+                                 (int64_t)(dl ? 1 - e_out : e_out) * out_stride
+                           : nullptr;
 
-    const float vf = a.v[(dl * 2 + 0) * a.d + j], vr = a.v[(dl * 2 + 1) * a.d + j];
-    const float bf = a.b[(dl * 2 + 0) * a.d + j], br = a.b[(dl * 2 + 1) * a.d + j];
+    const float vfs = a.v[(dl * 2 + 0) * a.d + j] * kNegLog2e;
+    const float vrs = a.v[(dl * 2 + 1) * a.d + j] * kNegLog2e;
+    const float bfs = a.b[(dl * 2 + 0) * a.d + j] * kNegLog2e;
+    const float brs = a.b[(dl * 2 + 1) * a.d + j] * kNegLog2e;
     const float alpha = a.alpha;
     float c = a.c0 ? a.c0[(dl * a.B + bb) * a.d + j] : 0.0f;
 
     auto cell = [&](float uf, float ur, float ux, float xv, float &h) {
-        const Gate f = gate(fmaf(vf, c, uf + bf));
-        const Gate r = gate(fmaf(vr, c, ur + br));
+        const Gate f = gate_scaled(fmaf(vfs, c, fmaf(uf, kNegLog2e, bfs)));
+        const Gate r = gate_scaled(fmaf(vrs, c, fmaf(ur, kNegLog2e, brs)));
         c = fmaf(f.g, c, f.gc * ux);
-        const float ax = alpha * xv;
-        h = fmaf(r.g, c, r.gc * ax);
+        h = fmaf(r.g, c, r.gc * (alpha * xv));
     };
 
     const int64_t groups = L / S;                    // full groups
@@ -194,8 +206,9 @@ __global__ __launch_bounds__(kWave) void fwd_fast(RecArgs a)
 #pragma unroll
                     for (int m = 0; m < S / 2; ++m) {
                         const float4 val = ((const float4 *)out_slot)[m * 64 + lane];
-                        const int64_t st = p0 * SPP + 2 * m + e_out;
-                        *(float4 *)(out_base + out_row + tix(st) * out_tstride) = val;
+                        const int64_t st0 = p0 * SPP + 2 * m;       // even step of the pair
+                        const uint32_t t = (uint32_t)(dl ? (L - 2 - st0) : st0);
+                        *(float4 *)(out_ptr + __umul24(t, out_stride)) = val;
                     }
                 }
                 if (gi + rg + 1 >= groups) goto tail;
@@ -283,6 +296,11 @@ __global__ __launch_bounds__(256) void bwd_generic(RecArgs a)
         a.dU[ub] = dzf;
         a.dU[ub + a.d] = dzr;
         a.dU[ub + 2 * a.d] = dux;
+        if (a.dU_lp) {
+            a.dU_lp[ub] = f32_to_bf16(dzf);
+            a.dU_lp[ub + a.d] = f32_to_bf16(dzr);
+            a.dU_lp[ub + 2 * a.d] = f32_to_bf16(dux);
+        }
         a.dx[xi] = dxh;
         c = cp;
     }
@@ -295,15 +313,16 @@ __global__ __launch_bounds__(256) void bwd_generic(RecArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Fast backward (fp32 U and x, d % 64 == 0): one wavefront per 64 channels,
-// walking its direction's steps in reverse.  Per timestep two input packets:
+// Fast backward (fp32 U and x, d % 64 == 0, same size limits as the fast
+// forward): one wavefront per 64 channels, walking its direction's steps in
+// reverse.  Per timestep two input packets:
 //   A: lanes 0-15 U_f, 16-31 U_r, 32-47 U_cand, 48-63 x          (time t)
 //   B: lanes 0-15 c[t_prev], 16-31 dh[t], 32-47 dx[t] (read when
 //      accumulating; otherwise these lanes and lanes 48-63 re-read dh)
-// and one output packet: lanes 0-15 dU_f, 16-31 dU_r, 32-47 dU_cand, 48-63 dx.
-// Steps are processed in groups of G with one LDS round trip per group, a
-// branch-free main loop over whole groups and a direct-load tail, as in the
-// forward kernel.
+// and one output packet: lanes 0-15 dU_f, 16-31 dU_r, 32-47 dU_cand, 48-63 dx
+// (plus, optionally, the three dU rows rounded to bf16).  Steps are processed
+// in groups of G with one LDS round trip per group, a branch-free main loop
+// over whole groups and a direct-load tail, as in the forward kernel.
 // ---------------------------------------------------------------------------
 template <int R, int G>
 __global__ __launch_bounds__(kWave) void bwd_fast(RecArgs a)
@@ -326,56 +345,51 @@ __global__ __launch_bounds__(kWave) void bwd_fast(RecArgs a)
     const int q = lane >> 4;
     const int sub = lane & 15;
     const bool dxacc = a.dx_accumulate;
+    const uint32_t u_stride = (uint32_t)(a.B * a.ndir * 3 * a.d * 4);
+    const uint32_t x_stride = (uint32_t)(a.B * a.d * 4);
+    const uint32_t h_stride = (uint32_t)(a.B * a.ndir * a.d * 4);
+    const int64_t u_row = (bb * a.ndir + dl) * 3 * a.d + q * a.d + j0 + 4 * sub;
+    const int64_t x_row = bb * a.d + j0 + 4 * sub;
+    const int64_t h_row = (bb * a.ndir + dl) * a.d + j0 + 4 * sub;
     // packet A
-    const char *pa_base;
-    int64_t pa_row, pa_ts;
-    if (q < 3) {
-        pa_base = (const char *)a.U;
-        pa_row = (bb * a.ndir + dl) * 3 * a.d + q * a.d + j0 + 4 * sub;
-        pa_ts = a.B * a.ndir * 3 * a.d;
-    } else {
-        pa_base = (const char *)a.x;
-        pa_row = bb * a.d + j0 + 4 * sub;
-        pa_ts = a.B * a.d;
-    }
+    const char *pa_ptr = q < 3 ? (const char *)a.U + u_row * 4 : (const char *)a.x + x_row * 4;
+    const uint32_t pa_stride = q < 3 ? u_stride : x_stride;
     // packet B
-    const int64_t hrow = (bb * a.ndir + dl) * a.d + j0 + 4 * sub;
-    const int64_t hts = a.B * a.ndir * a.d;
-    const char *pb_base;
-    int64_t pb_row, pb_ts, pb_soff;
-    if (q == 0) {                       // c at the previous direction-step
-        pb_base = (const char *)a.c_seq_in;
-        pb_row = hrow;
-        pb_ts = hts;
-        pb_soff = -1;
-    } else if (q == 2 && dxacc) {       // dx to accumulate into
-        pb_base = (const char *)a.dx;
-        pb_row = bb * a.d + j0 + 4 * sub;
-        pb_ts = a.B * a.d;
-        pb_soff = 0;
-    } else {                            // dh (lanes 48-63, and 32-47 unless accumulating)
-        pb_base = (const char *)a.dh;
-        pb_row = hrow;
-        pb_ts = hts;
-        pb_soff = 0;
-    }
-    auto clampL = [&](int64_t s) -> int64_t { return s < 0 ? 0 : (s >= L ? L - 1 : s); };
-    // direction-step s is processed at reverse iteration k = L-1-s
+    const bool b_is_dx = (q == 2 && dxacc);
+    const char *pb_ptr = q == 0   ? (const char *)a.c_seq_in + h_row * 4
+                         : b_is_dx ? (const char *)a.dx + x_row * 4
+                                   : (const char *)a.dh + h_row * 4;
+    const uint32_t pb_stride = b_is_dx ? x_stride : h_stride;
+    const bool pb_prev = (q == 0);                   // c at the previous direction-step
+    // output packet
+    char *po_ptr = q < 3 ? (char *)a.dU + u_row * 4 : (char *)a.dx + x_row * 4;
+    const uint32_t po_stride = pa_stride;
+    const bool lp_on = a.dU_lp != nullptr && q < 3;
+    char *lp_ptr = lp_on ? (char *)a.dU_lp + u_row * 2 : nullptr;
+    const uint32_t lp_stride = u_stride / 2;
+
+    // time index of reverse iteration k (direction-step L-1-k), clamped
+    auto t_of = [&](int64_t k) -> uint32_t {
+        const int64_t kk = k < L ? k : L - 1;
+        return (uint32_t)(dl ? kk : L - 1 - kk);
+    };
+    auto tprev_of = [&](int64_t k) -> uint32_t {    // direction-step L-2-k, clamped
+        const int64_t kk = k < L - 1 ? k : L - 2;
+        if (kk < 0) return 0u;                       // L == 1: never used
+        return (uint32_t)(dl ? kk + 1 : L - 2 - kk);
+    };
     auto load_a = [&](int64_t k) -> uint4 {
-        return *(const uint4 *)(pa_base + (pa_row + tix(clampL(L - 1 - k)) * pa_ts) * 4);
+        return *(const uint4 *)(pa_ptr + __umul24(t_of(k), pa_stride));
     };
     auto load_b = [&](int64_t k) -> uint4 {
-        return *(const uint4 *)(pb_base + (pb_row + tix(clampL(L - 1 - k + pb_soff)) * pb_ts) * 4);
+        const uint32_t t = pb_prev ? tprev_of(k) : t_of(k);
+        return *(const uint4 *)(pb_ptr + __umul24(t, pb_stride));
     };
 
-    // output packet
-    float *po_base = q < 3 ? a.dU : a.dx;
-    const int64_t po_row = q < 3 ? ((bb * a.ndir + dl) * 3 * a.d + q * a.d + j0 + 4 * sub)
-                                 : (bb * a.d + j0 + 4 * sub);
-    const int64_t po_ts = q < 3 ? a.B * a.ndir * 3 * a.d : a.B * a.d;
-
     const float vf = a.v[(dl * 2 + 0) * a.d + j], vr = a.v[(dl * 2 + 1) * a.d + j];
-    const float bf = a.b[(dl * 2 + 0) * a.d + j], br = a.b[(dl * 2 + 1) * a.d + j];
+    const float vfs = vf * kNegLog2e, vrs = vr * kNegLog2e;
+    const float bfs = a.b[(dl * 2 + 0) * a.d + j] * kNegLog2e;
+    const float brs = a.b[(dl * 2 + 1) * a.d + j] * kNegLog2e;
     const float c0 = a.c0 ? a.c0[(dl * a.B + bb) * a.d + j] : 0.0f;
     const float alpha = a.alpha;
     float gc = a.dc_last ? a.dc_last[(dl * a.B + bb) * a.d + j] : 0.0f;
@@ -385,8 +399,8 @@ __global__ __launch_bounds__(kWave) void bwd_fast(RecArgs a)
     // one reverse step; returns dU_f, dU_r, dU_cand, dx (highway part)
     auto cell = [&](float uf, float ur, float ux, float xv, float cp, float dhv, float &o0,
                     float &o1, float &o2, float &o3) {
-        const Gate f = gate(fmaf(vf, cp, uf + bf));
-        const Gate r = gate(fmaf(vr, cp, ur + br));
+        const Gate f = gate_scaled(fmaf(vfs, cp, fmaf(uf, kNegLog2e, bfs)));
+        const Gate r = gate_scaled(fmaf(vrs, cp, fmaf(ur, kNegLog2e, brs)));
         const float dc = fmaf(dhv, r.g, gc);
         const float dr = dhv * fmaf(-alpha, xv, c);
         o3 = dhv * r.gc * alpha;
@@ -451,8 +465,14 @@ __global__ __launch_bounds__(kWave) void bwd_fast(RecArgs a)
 #pragma unroll
                 for (int i = 0; i < G; ++i) {
                     const float4 val = ((const float4 *)out_slot)[i * 64 + lane];
-                    const int64_t s = L - 1 - (k0 + i);
-                    *(float4 *)(po_base + po_row + tix(s) * po_ts) = val;
+                    const uint32_t t = t_of(k0 + i);
+                    *(float4 *)(po_ptr + __umul24(t, po_stride)) = val;
+                    if (lp_on) {     // lanes of the three dU rows also write bf16
+                        uint2 pk;
+                        pk.x = pack_bf16x2(val.x, val.y);
+                        pk.y = pack_bf16x2(val.z, val.w);
+                        *(uint2 *)(lp_ptr + __umul24(t, lp_stride)) = pk;
+                    }
                 }
                 if (gi + rg + 1 >= groups) goto tail;
             }
@@ -474,6 +494,11 @@ tail:
         a.dU[ub] = o0;
         a.dU[ub + a.d] = o1;
         a.dU[ub + 2 * a.d] = o2;
+        if (a.dU_lp) {
+            a.dU_lp[ub] = f32_to_bf16(o0);
+            a.dU_lp[ub + a.d] = f32_to_bf16(o1);
+            a.dU_lp[ub + 2 * a.d] = f32_to_bf16(o2);
+        }
         a.dx[xi] = dxacc ? o3 + a.dx[xi] : o3;
     }
     if (a.dc0) a.dc0[(dl * a.B + bb) * a.d + j] = gc;
@@ -546,27 +571,37 @@ hipError_t bwd_generic_launch(const RecArgs &a, hipStream_t s)
 }  // namespace
 
 #ifndef SRU_FWD_RING_F32
-#define SRU_FWD_RING_F32 32
+#define SRU_FWD_RING_F32 16
 #endif
 #ifndef SRU_FWD_GROUP_F32
 #define SRU_FWD_GROUP_F32 8
 #endif
 #ifndef SRU_FWD_RING_BF16
-#define SRU_FWD_RING_BF16 16
+#define SRU_FWD_RING_BF16 32
 #endif
 #ifndef SRU_FWD_GROUP_BF16
-#define SRU_FWD_GROUP_BF16 4
+#define SRU_FWD_GROUP_BF16 8
 #endif
 #ifndef SRU_BWD_RING
-#define SRU_BWD_RING 16
+#define SRU_BWD_RING 8
 #endif
 #ifndef SRU_BWD_GROUP
 #define SRU_BWD_GROUP 4
 #endif
 
+// The fast kernels address with 32-bit byte offsets built from 24-bit
+// products: every tensor below 2 GiB and every time stride below 16 MiB.
+static bool fast_sizes_ok(const RecArgs &a)
+{
+    const int64_t esz = a.u_bf16 ? 2 : 4;
+    const int64_t u_bytes = a.L * a.B * a.ndir * 3 * a.d * 4;   // fp32 bound covers bf16
+    const int64_t ustride = a.B * a.ndir * 3 * a.d * esz;
+    return u_bytes < (int64_t(1) << 31) && ustride < (int64_t(1) << 24) && a.L < (int64_t(1) << 24);
+}
+
 hipError_t launch_forward(const RecArgs &a, hipStream_t s)
 {
-    const bool fast = (a.d % kWave == 0) && (a.u_bf16 == a.x_bf16);
+    const bool fast = (a.d % kWave == 0) && (a.u_bf16 == a.x_bf16) && fast_sizes_ok(a);
     if (fast) {
         const int64_t waves = (int64_t)a.ndir * a.B * (a.d / kWave);
         if (a.u_bf16)
@@ -587,7 +622,7 @@ hipError_t launch_forward(const RecArgs &a, hipStream_t s)
 
 hipError_t launch_backward_dir(const RecArgs &a, hipStream_t s)
 {
-    const bool fast = (a.d % kWave == 0) && !a.u_bf16 && !a.x_bf16;
+    const bool fast = (a.d % kWave == 0) && !a.u_bf16 && !a.x_bf16 && fast_sizes_ok(a);
     if (fast) {
         const int64_t waves = a.B * (a.d / kWave);
         hipLaunchKernelGGL((bwd_fast<SRU_BWD_RING, SRU_BWD_GROUP>), dim3((unsigned)waves),

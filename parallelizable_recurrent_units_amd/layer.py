@@ -59,17 +59,22 @@ def workspace(shape, op, chunk=0, device="cuda"):
     return torch.empty(n, device=device, dtype=torch.uint8)
 
 
-def backward(shape, U, x, v, b, c0, c_seq, dh, dc_last=None, ws=None, stream=None):
+def backward(shape, U, x, v, b, c0, c_seq, dh, dc_last=None, ws=None, bf16_copy=False,
+             stream=None):
+    """Returns (dU, dx, dv, db, dc0), plus dU rounded to bf16 when bf16_copy."""
     s = B._shape(shape)
     dev = U.device
     dU = torch.empty((s.L, s.B, s.ndir, 3, s.d), device=dev, dtype=torch.float32)
+    dU_lp = torch.empty_like(dU, dtype=torch.bfloat16) if bf16_copy else None
     dx = torch.empty((s.L, s.B, s.d), device=dev, dtype=torch.float32)
     dv = torch.empty((s.ndir, 2, s.d), device=dev, dtype=torch.float32)
     db = torch.empty((s.ndir, 2, s.d), device=dev, dtype=torch.float32)
     dc0 = torch.empty((s.ndir, s.B, s.d), device=dev, dtype=torch.float32)
     if ws is None:
         ws = workspace(s, B.SRU_WS_BACKWARD, 0, dev)
-    B.sru_backward(s, U, x, v, b, c0, c_seq, dh, dc_last, dU, dx, dv, db, dc0, ws, stream)
+    B.sru_backward(s, U, x, v, b, c0, c_seq, dh, dc_last, dU, dx, dv, db, dc0, ws, dU_lp, stream)
+    if bf16_copy:
+        return dU, dx, dv, db, dc0, dU_lp
     return dU, dx, dv, db, dc0
 
 

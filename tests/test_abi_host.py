@@ -76,11 +76,11 @@ def fwd(lib, s, **kw):
 
 def bwd(lib, s, ws_bytes, **kw):
     a = dict(U=P[0], x=P[1], v=P[2], b=P[3], c0=None, c_seq=P[5], dh=P[6], dc_last=None,
-             dU=P[7], dx=P[8], dv=None, db=None, dc0=None, ws=P[9])
+             dU=P[7], dU_lp=None, dx=P[8], dv=None, db=None, dc0=None, ws=P[9])
     a.update(kw)
     return lib.sru_backward(ctypes.byref(s), a["U"], 0, a["x"], 0, a["v"], a["b"], a["c0"],
-                            a["c_seq"], a["dh"], a["dc_last"], a["dU"], a["dx"], a["dv"],
-                            a["db"], a["dc0"], a["ws"], ws_bytes, None)
+                            a["c_seq"], a["dh"], a["dc_last"], a["dU"], a["dU_lp"], a["dx"],
+                            a["dv"], a["db"], a["dc0"], a["ws"], ws_bytes, None)
 
 
 def lin(lib, s, pass_, chunk, ws_bytes, **kw):
@@ -128,6 +128,7 @@ def test_workspace_errors(lib):
     assert bwd(lib, s, need, ws=None) == sru.SRU_ERR_WORKSPACE
     assert bwd(lib, s, need, c_seq=None) == sru.SRU_ERR_INVALID_ARG
     assert bwd(lib, s, need, dU=None) == sru.SRU_ERR_INVALID_ARG
+    assert bwd(lib, s, need, dU_lp=P[11] + 2) == sru.SRU_ERR_INVALID_ARG
     lneed = sru.sru_workspace_size(s, sru.SRU_WS_LINEAR_BWD, 4)
     assert lin(lib, s, 1, 4, lneed - 256) == sru.SRU_ERR_WORKSPACE
     assert lin(lib, s, 1, 0, lneed) == sru.SRU_ERR_INVALID_ARG

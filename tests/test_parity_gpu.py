@@ -132,6 +132,26 @@ def test_forward_without_state_outputs():
     check("h", host(h), fo["h"], TIGHT)
 
 
+@pytest.mark.parametrize("L,B,d,nd", [(33, 2, 64, 1), (17, 3, 128, 2), (5, 3, 7, 2)])
+def test_backward_bf16_copy_of_dU(L, B, d, nd):
+    """The optional bf16 dU equals dU rounded to nearest even, bit for bit."""
+    import torch
+    w = workloads.custom(L, B, d, ndir=nd, alpha=1.1, mode="given_u", c0="normal0.1")
+    inp = workloads.make_inputs(w, seed=7000 + L, dc_last=True, v_scale=0.5, b_scale=0.3)
+    t = dev_inputs(inp)
+    shape = SruShape(L, B, d, nd == 2, w.alpha)
+    h, c_seq, _ = layer.forward(shape, t["U"], t["x"], t["v"], t["b"], t["c0"], keep_c_seq=True)
+    out = layer.backward(shape, t["U"], t["x"], t["v"], t["b"], t["c0"], c_seq, t["dh"],
+                         t["dc_last"], bf16_copy=True)
+    dU, dU_lp = out[0], out[5]
+    ref = dU.to(torch.bfloat16)
+    assert torch.equal(dU_lp.view(torch.int16), ref.view(torch.int16))
+    plain = layer.backward(shape, t["U"], t["x"], t["v"], t["b"], t["c0"], c_seq, t["dh"],
+                           t["dc_last"])
+    for a, b in zip(out[:5], plain):
+        assert torch.equal(a, b)
+
+
 def test_backward_is_deterministic():
     w = workloads.custom(50, 8, 128, ndir=2, alpha=1.0, mode="given_u")
     inp = workloads.make_inputs(w, seed=6)

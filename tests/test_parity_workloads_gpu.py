@@ -38,10 +38,10 @@ def training_step(w, t):
     shape = SruShape(w.L, w.B, w.d, w.ndir == 2, w.alpha)
     U = layer.project(shape, t["x"], t["W"])
     h, c_seq, c_last = layer.forward(shape, U, t["x"], t["v"], t["b"], t["c0"], keep_c_seq=True)
-    dU, dx, dv, db, dc0 = layer.backward(shape, U, t["x"], t["v"], t["b"], t["c0"], c_seq,
-                                         t["dh"], t["dc_last"])
+    dU, dx, dv, db, dc0, dU_lp = layer.backward(shape, U, t["x"], t["v"], t["b"], t["c0"], c_seq,
+                                                t["dh"], t["dc_last"], bf16_copy=True)
     Wt = layer.transpose_weight(shape, t["W"])
-    layer.project_bwd_data(shape, dU, t["W"], dx, accumulate=True, Wt=Wt)
+    layer.project_bwd_data(shape, dU_lp, t["W"], dx, accumulate=True, Wt=Wt)
     return dict(U=U, h=h, c_seq=c_seq, c_last=c_last, dU=dU, dX=dx, dv=dv, db=db, dc0=dc0)
 
 
