@@ -210,7 +210,8 @@ __global__ __launch_bounds__(256) void lin_db_reduce(LinGeom g, const float *__r
                                                      float *db)
 {
     __shared__ float red[4][64];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int64_t jblocks = (g.d + 63) / 64;
     const int gg = (int)(blockIdx.x / jblocks);
     const int64_t j = (blockIdx.x % jblocks) * 64 + lane;
@@ -237,11 +238,398 @@ __global__ __launch_bounds__(256) void lin_db_reduce(LinGeom g, const float *__r
         db[(g.dl * 2 + gg) * g.d + j] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
 }
 
+// ---------------------------------------------------------------------------
+// Single-pass chunked scan (chunk = W * SEG steps, d % 64 == 0).
+//
+// A workgroup of W waves owns 64 consecutive chains and one chunk; wave w
+// holds steps [w*SEG, (w+1)*SEG) of the chunk in registers, so every input
+// element is read from HBM once:
+//   1. each lane folds its SEG steps into the segment map (A, E);
+//   2. wave 0 folds the W segment maps into the chunk map, obtains the
+//      chunk's incoming state from the previous chunk of the same chains
+//      (published in the workspace with a ready flag), publishes its own
+//      outgoing state, and hands every segment its incoming state via LDS;
+//   3. each lane replays its steps from that state and writes h and c.
+// Chunks take dynamic tickets in chain-major order (ticket = chunk * tiles
+// + tile), so a chunk only ever waits for a chunk that started before it:
+// progress is guaranteed.  The wait is bounded; if the bound is ever hit the
+// kernel stops waiting and raises the error word of the workspace.
+// ---------------------------------------------------------------------------
+struct Lookback {
+    float *carry;        // [nC, chains]  outgoing state of each chunk
+    uint32_t *flags;     // [nC, tiles]   1 when that chunk's carry is published
+    uint32_t *ticket;    // dynamic chunk ticket
+    uint32_t *err;       // set if a wait ran out
+};
+
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+__device__ __forceinline__ void publish(Lookback lb, int64_t idx, float v, int64_t flag_idx,
+                                        int lane)
+{
+    __hip_atomic_store(lb.carry + idx, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (lane == 0)
+        __hip_atomic_store(lb.flags + flag_idx, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float consume(Lookback lb, int64_t idx, int64_t flag_idx, int lane)
+{
+    if (lane == 0) {
+        uint32_t spins = 0;
+        while (__hip_atomic_load(lb.flags + flag_idx, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins > kSpinLimit) {
+                __hip_atomic_store(lb.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return __hip_atomic_load(lb.carry + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int64_t take_ticket(Lookback lb, uint32_t *s_ticket)
+{
+    if (threadIdx.x == 0) *s_ticket = atomicAdd(lb.ticket, 1u);
+    __syncthreads();
+    // the same value in every lane: keep it (and every index derived from
+    // it) in scalar registers
+    return (int64_t)__builtin_amdgcn_readfirstlane(*s_ticket);
+}
+
+template <typename TU, typename TX, int W, int SEG>
+__global__ __launch_bounds__(W * 64) void lin_fwd_fused(LinGeom g, const TU *__restrict__ U,
+                                                         const TX *__restrict__ X,
+                                                         const float *__restrict__ bias,
+                                                         float alpha, const float *__restrict__ c0,
+                                                         float *h, float *c_seq, float *c_last,
+                                                         Lookback lb)
+{
+    __shared__ float sA[W][64], sE[W][64], sC[W][64];
+    __shared__ uint32_t s_ticket;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int64_t tiles = g.chains / 64;
+    const int64_t tk = take_ticket(lb, &s_ticket);
+    const int64_t k = tk / tiles, tile = tk % tiles;
+    // a tile is 64 consecutive channels of one batch row (d % 64 == 0): all
+    // addressing is uniform except the lane, so loads take a scalar base
+    const int64_t ch0 = tile * 64, ch = ch0 + lane;
+    const int64_t j0 = ch0 % g.d, bb = ch0 / g.d, j = j0 + lane;
+    const float bfs = bias[(g.dl * 2 + 0) * g.d + j] * kNegLog2e;
+    const float brs = bias[(g.dl * 2 + 1) * g.d + j] * kNegLog2e;
+    const int64_t s_lo = k * g.chunk + wv * SEG;
+    const int64_t ustride = g.B * g.ndir * 3 * g.d, xstride = g.B * g.d;
+    const TU *ub0 = U + (bb * g.ndir + g.dl) * 3 * g.d + j0;     // uniform
+    const TX *xb0 = X + bb * g.d + j0;                          // uniform
+    const uint32_t ulane = (uint32_t)lane;                      // the only per-lane offset
+
+    // phase 1: load the segment, fold it into (A, E)
+    float ga[SEG], gb[SEG], ur[SEG], xv[SEG];
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+        const int64_t s = s_lo + i < g.L ? s_lo + i : g.L - 1;   // clamp: in bounds
+        const int64_t t = lin_t(g, s);
+        const TU *up = ub0 + t * ustride;                           // uniform
+        ga[i] = load_as_f32(up + ulane);
+        gb[i] = load_as_f32(up + 2 * g.d + ulane);
+        ur[i] = load_as_f32(up + g.d + ulane);
+        xv[i] = load_as_f32(xb0 + t * xstride + ulane);
+    }
+    float A = 1.0f, E = 0.0f;
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+        if (s_lo + i < g.L) {
+            const Gate a = gate_scaled(fmaf(ga[i], kNegLog2e, bfs));
+            ga[i] = a.g;
+            gb[i] = a.gc * gb[i];          // beta = (1 - a) u_cand
+            E = fmaf(a.g, E, gb[i]);
+            A *= a.g;
+        } else {
+            ga[i] = 1.0f;                  // identity map past the end
+            gb[i] = 0.0f;
+        }
+    }
+    sA[wv][lane] = A;
+    sE[wv][lane] = E;
+    __syncthreads();
+
+    // phase 2 (wave 0): chunk map, carry in, carry out, segment carries
+    if (wv == 0) {
+        float Ac = 1.0f, Ec = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            Ec = fmaf(sA[w][lane], Ec, sE[w][lane]);
+            Ac *= sA[w][lane];
+        }
+        float cin;
+        if (k == 0)
+            cin = c0 ? c0[g.dl * g.chains + ch] : 0.0f;
+        else
+            cin = consume(lb, (k - 1) * g.chains + ch, (k - 1) * tiles + tile, lane);
+        if (k + 1 < g.nC) publish(lb, k * g.chains + ch, fmaf(Ac, cin, Ec), k * tiles + tile, lane);
+        float cc = cin;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            sC[w][lane] = cc;
+            cc = fmaf(sA[w][lane], cc, sE[w][lane]);
+        }
+    }
+    __syncthreads();
+
+    // phase 3: replay the segment, write h and c
+    float c = sC[wv][lane];
+    const int64_t ostride = g.B * g.ndir * g.d;
+    float *hb0 = h + (bb * g.ndir + g.dl) * g.d + j0;                    // uniform
+    float *cb0 = c_seq ? c_seq + (bb * g.ndir + g.dl) * g.d + j0 : nullptr;
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+        const int64_t s = s_lo + i;
+        if (s < g.L) {
+            c = fmaf(ga[i], c, gb[i]);
+            const Gate r = gate_scaled(fmaf(ur[i], kNegLog2e, brs));
+            const int64_t t = lin_t(g, s);
+            float *ho = hb0 + t * ostride;                          // uniform
+            ho[ulane] = fmaf(r.g, c, r.gc * (alpha * xv[i]));
+            if (cb0) (cb0 + t * ostride)[ulane] = c;
+            if (s == g.L - 1 && c_last) c_last[g.dl * g.chains + ch] = c;
+        }
+    }
+}
+
+// Backward: the adjoint of the state runs from the last step to the first,
+//   gc[t-1] = a[t] (gc[t] + r[t] dh[t]),
+// so chunks are chained from the last one down (ticket chunk = nC - 1 -
+// ticket / tiles) and each segment's map is g -> A g + G over its steps in
+// reverse.  Phase 3 recomputes the gates from the register-held U values and
+// writes dU, dx and the per-chunk partial sums of dU_f, dU_r (for db).
+template <typename TU, typename TX, int W, int SEG>
+__global__ __launch_bounds__(W * 64) void lin_bwd_fused(
+    LinGeom g, const TU *__restrict__ U, const TX *__restrict__ X, const float *__restrict__ bias,
+    float alpha, const float *__restrict__ c0, const float *__restrict__ c_seq,
+    const float *__restrict__ dh, const float *__restrict__ dc_last, float *dU, float *dx,
+    bool dx_acc, float *dc0, float *dbpart, Lookback lb)
+{
+    __shared__ float sA[W][64], sG[W][64], sC[W][64];
+    __shared__ float sbf_w[W][64], sbr_w[W][64];
+    __shared__ uint32_t s_ticket;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int64_t tiles = g.chains / 64;
+    const int64_t tk = take_ticket(lb, &s_ticket);
+    const int64_t k = g.nC - 1 - tk / tiles, tile = tk % tiles;
+    const int64_t ch0 = tile * 64, ch = ch0 + lane;     // see the forward kernel
+    const int64_t j0 = ch0 % g.d, bb = ch0 / g.d, j = j0 + lane;
+    const float bfs = bias[(g.dl * 2 + 0) * g.d + j] * kNegLog2e;
+    const float brs = bias[(g.dl * 2 + 1) * g.d + j] * kNegLog2e;
+    const int64_t s_lo = k * g.chunk + wv * SEG;
+    const int64_t ustride = g.B * g.ndir * 3 * g.d, xstride = g.B * g.d;
+    const int64_t hstride = g.B * g.ndir * g.d;
+    const TU *ul = U + (bb * g.ndir + g.dl) * 3 * g.d + j0;          // uniform bases
+    const TX *xl = X + bb * g.d + j0;
+    const float *dhl = dh + (bb * g.ndir + g.dl) * g.d + j0;
+    const float *csl = c_seq + (bb * g.ndir + g.dl) * g.d + j0;
+    const uint32_t ulane = (uint32_t)lane;                      // the only per-lane offset
+    auto clampL = [&](int64_t s) { return s < g.L ? s : g.L - 1; };
+
+    // phase 1: gates and dh of the segment, folded in reverse into (A, G)
+    float uf[SEG], ur[SEG], dv[SEG];
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+        const int64_t t = lin_t(g, clampL(s_lo + i));
+        const TU *up = ul + t * ustride;                            // uniform
+        uf[i] = load_as_f32(up + ulane);
+        ur[i] = load_as_f32(up + g.d + ulane);
+        dv[i] = (dhl + t * hstride)[ulane];
+    }
+    float A = 1.0f, G = 0.0f;
+#pragma unroll
+    for (int i = SEG - 1; i >= 0; --i) {
+        if (s_lo + i < g.L) {
+            const Gate a = gate_scaled(fmaf(uf[i], kNegLog2e, bfs));
+            const Gate r = gate_scaled(fmaf(ur[i], kNegLog2e, brs));
+            G = a.g * fmaf(r.g, dv[i], G);
+            A *= a.g;
+        }
+    }
+    sA[wv][lane] = A;
+    sG[wv][lane] = G;
+    __syncthreads();
+
+    if (wv == 0) {
+        float Ac = 1.0f, Gc = 0.0f;
+#pragma unroll
+        for (int w = W - 1; w >= 0; --w) {
+            Gc = fmaf(sA[w][lane], Gc, sG[w][lane]);
+            Ac *= sA[w][lane];
+        }
+        float gin;
+        if (k == g.nC - 1)
+            gin = dc_last ? dc_last[g.dl * g.chains + ch] : 0.0f;
+        else
+            gin = consume(lb, (k + 1) * g.chains + ch, (k + 1) * tiles + tile, lane);
+        if (k > 0) publish(lb, k * g.chains + ch, fmaf(Ac, gin, Gc), k * tiles + tile, lane);
+        float gg = gin;
+#pragma unroll
+        for (int w = W - 1; w >= 0; --w) {
+            sC[w][lane] = gg;
+            gg = fmaf(sA[w][lane], gg, sG[w][lane]);
+        }
+    }
+    __syncthreads();
+
+    // phase 3: local gradients, last step of the segment first
+    float ux[SEG], xv[SEG], cv[SEG];
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+        const int64_t t = lin_t(g, clampL(s_lo + i));
+        ux[i] = load_as_f32(ul + t * ustride + 2 * g.d + ulane);
+        xv[i] = load_as_f32(xl + t * xstride + ulane);
+        cv[i] = (csl + t * hstride)[ulane];
+    }
+    float cprev0;   // state before the segment's first step
+    if (s_lo == 0)
+        cprev0 = c0 ? c0[g.dl * g.chains + ch] : 0.0f;
+    else
+        cprev0 = (csl + lin_t(g, clampL(s_lo - 1)) * hstride)[ulane];
+    float gc = sC[wv][lane];
+    float sbf = 0.0f, sbr = 0.0f;
+    float *dul = dU + (bb * g.ndir + g.dl) * 3 * g.d + j0;              // uniform bases
+    float *dxl = dx + bb * g.d + j0;
+#pragma unroll
+    for (int i = SEG - 1; i >= 0; --i) {
+        const int64_t s = s_lo + i;
+        if (s < g.L) {
+            const Gate a = gate_scaled(fmaf(uf[i], kNegLog2e, bfs));
+            const Gate r = gate_scaled(fmaf(ur[i], kNegLog2e, brs));
+            const float cp = i > 0 ? cv[i - 1] : cprev0;
+            const float D = fmaf(r.g, dv[i], gc);
+            const float dr = dv[i] * fmaf(-alpha, xv[i], cv[i]);
+            const int64_t t = lin_t(g, s);
+            float dxh = dv[i] * r.gc * alpha;
+            float *xo = dxl + t * xstride;                          // uniform
+            float *uo = dul + t * ustride;
+            if (dx_acc) dxh += xo[ulane];
+            const float dzf = D * (cp - ux[i]) * (a.g * a.gc);
+            const float dzr = dr * (r.g * r.gc);
+            uo[ulane] = dzf;
+            (uo + g.d)[ulane] = dzr;
+            (uo + 2 * g.d)[ulane] = D * a.gc;
+            xo[ulane] = dxh;
+            sbf += dzf;
+            sbr += dzr;
+            gc = a.g * D;
+        }
+    }
+    if (k == 0 && wv == 0 && dc0) dc0[g.dl * g.chains + ch] = gc;
+    // per-(chunk, chain) partial sums of dz_f and dz_r, waves added in order
+    sbf_w[wv][lane] = sbf;
+    sbr_w[wv][lane] = sbr;
+    __syncthreads();
+    if (wv == 0) {
+        float f = 0.0f, r = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            f += sbf_w[w][lane];
+            r += sbr_w[w][lane];
+        }
+        dbpart[(k * 2 + 0) * g.chains + ch] = f;
+        dbpart[(k * 2 + 1) * g.chains + ch] = r;
+    }
+}
+
+// Clears the look-back flags, ticket and error word before a fused launch
+// (a plain kernel, so the sequence can also be captured in a graph).
+__global__ __launch_bounds__(256) void lin_clear(uint32_t *p, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+constexpr int kFusedChunk = 256;
+constexpr int kFwdW = 16, kFwdSeg = 16;   // 16 waves x 16 steps
+constexpr int kBwdW = 16, kBwdSeg = 16;   // 16 waves x 16 steps
+static_assert(kFwdW * kFwdSeg == kFusedChunk && kBwdW * kBwdSeg == kFusedChunk, "chunk split");
+
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+// Workspace layout of the fused kernels (floats / words):
+//   carry [nC * chains] | backward: db partials [2 * nC * chains] |
+//   control words: ticket, error, pad to 64 | flags [nC * tiles]
+struct FusedWs {
+    Lookback lb;
+    float *dbpart;
+    uint32_t *ctrl;
+    int64_t ctrl_words;
+};
+
+FusedWs fused_ws(const LinArgs &a, bool backward)
+{
+    const int64_t nC = (a.L + a.chunk - 1) / a.chunk;
+    const int64_t chains = a.B * a.d;
+    float *ws = (float *)a.ws;
+    FusedWs f;
+    f.lb.carry = ws;
+    f.dbpart = ws + nC * chains;
+    f.ctrl = (uint32_t *)(ws + (backward ? 3 : 1) * nC * chains);
+    f.lb.ticket = f.ctrl;
+    f.lb.err = f.ctrl + 1;
+    f.lb.flags = f.ctrl + 64;
+    f.ctrl_words = 64 + nC * (chains / 64);
+    return f;
+}
+
+bool use_fused(const LinArgs &a)
+{
+    const int64_t chains = a.B * a.d;
+    return a.chunk == kFusedChunk && a.d % 64 == 0 && (chains / 64) * ((a.L + a.chunk - 1) / a.chunk) <
+                                                          (int64_t(1) << 31);
+}
+
+template <typename TU, typename TX>
+hipError_t lin_forward_fused(const LinArgs &a, hipStream_t s)
+{
+    const int64_t nC = (a.L + a.chunk - 1) / a.chunk;
+    const int64_t chains = a.B * a.d;
+    const FusedWs f = fused_ws(a, false);
+    for (int dl = 0; dl < a.ndir; ++dl) {
+        LinGeom g{a.L, a.B, a.d, a.chunk, nC, chains, a.ndir, dl};
+        hipLaunchKernelGGL(lin_clear, dim3(blocks_for(f.ctrl_words)), dim3(256), 0, s, f.ctrl,
+                           f.ctrl_words);
+        hipLaunchKernelGGL((lin_fwd_fused<TU, TX, kFwdW, kFwdSeg>), dim3((unsigned)(nC * (chains / 64))),
+                           dim3(kFwdW * 64), 0, s, g, (const TU *)a.U, (const TX *)a.x, a.b, a.alpha,
+                           a.c0, a.h, a.c_seq, a.c_last, f.lb);
+    }
+    return hipGetLastError();
+}
+
+template <typename TU, typename TX>
+hipError_t lin_backward_fused(const LinArgs &a, hipStream_t s)
+{
+    const int64_t nC = (a.L + a.chunk - 1) / a.chunk;
+    const int64_t chains = a.B * a.d;
+    const FusedWs f = fused_ws(a, true);
+    for (int dl = a.ndir - 1; dl >= 0; --dl) {
+        LinGeom g{a.L, a.B, a.d, a.chunk, nC, chains, a.ndir, dl};
+        hipLaunchKernelGGL(lin_clear, dim3(blocks_for(f.ctrl_words)), dim3(256), 0, s, f.ctrl,
+                           f.ctrl_words);
+        hipLaunchKernelGGL((lin_bwd_fused<TU, TX, kBwdW, kBwdSeg>), dim3((unsigned)(nC * (chains / 64))),
+                           dim3(kBwdW * 64), 0, s, g, (const TU *)a.U, (const TX *)a.x, a.b, a.alpha,
+                           a.c0, a.c_seq, a.dh, a.dc_last, a.dU, a.dx, dl != a.ndir - 1, a.dc0,
+                           f.dbpart, f.lb);
+        if (a.db)
+            hipLaunchKernelGGL(lin_db_reduce, dim3((unsigned)(2 * ((a.d + 63) / 64))), dim3(256), 0,
+                               s, g, f.dbpart, a.db);
+    }
+    return hipGetLastError();
+}
 
 template <typename TU, typename TX>
 hipError_t lin_forward_t(const LinArgs &a, hipStream_t s)
 {
+    if (use_fused(a)) return lin_forward_fused<TU, TX>(a, s);
     const int64_t nC = (a.L + a.chunk - 1) / a.chunk;
     const int64_t chains = a.B * a.d;
     float *ws = (float *)a.ws;
@@ -262,6 +650,7 @@ hipError_t lin_forward_t(const LinArgs &a, hipStream_t s)
 template <typename TU, typename TX>
 hipError_t lin_backward_t(const LinArgs &a, hipStream_t s)
 {
+    if (use_fused(a)) return lin_backward_fused<TU, TX>(a, s);
     const int64_t nC = (a.L + a.chunk - 1) / a.chunk;
     const int64_t chains = a.B * a.d;
     float *ws = (float *)a.ws;
@@ -291,7 +680,9 @@ size_t linear_workspace_bytes(int64_t L, int64_t B, int64_t d, int ndir, int64_t
     (void)ndir;  // directions are processed one after another and reuse it
     const int64_t nC = (L + chunk - 1) / chunk;
     const int64_t per = nC * B * d;
-    const int64_t floats = backward ? 5 * per : 3 * per;
+    // three-phase: 3 (fwd) or 5 (bwd) per-chunk arrays; fused: carry (+ db
+    // partials) + 64 control words + one flag per 64 chains and chunk
+    const int64_t floats = (backward ? 5 * per : 3 * per) + 64;
     return (size_t)floats * sizeof(float);
 }
 

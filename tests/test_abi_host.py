@@ -54,8 +54,8 @@ def test_workspace_sizes(lib, L, B, d, bi):
     assert sru.sru_workspace_size(s, sru.SRU_WS_BACKWARD) == round256(nd * B * 4 * d * 4)
     for chunk in (1, 7, 256):
         nC = -(-L // chunk)
-        assert sru.sru_workspace_size(s, sru.SRU_WS_LINEAR_FWD, chunk) == round256(3 * nC * B * d * 4)
-        assert sru.sru_workspace_size(s, sru.SRU_WS_LINEAR_BWD, chunk) == round256(5 * nC * B * d * 4)
+        assert sru.sru_workspace_size(s, sru.SRU_WS_LINEAR_FWD, chunk) == round256((3 * nC * B * d + 64) * 4)
+        assert sru.sru_workspace_size(s, sru.SRU_WS_LINEAR_BWD, chunk) == round256((5 * nC * B * d + 64) * 4)
     assert lib.sru_workspace_size(ctypes.byref(s), sru.SRU_WS_LINEAR_FWD, 0) == 0
     assert b"chunk" in lib.sru_last_error()
     assert lib.sru_workspace_size(ctypes.byref(s), 9, 1) == 0

@@ -226,9 +226,9 @@ def test_projection_fp32_config1():
 # ---------------------------------------------------------------------------
 # linear mode (v = 0): chunked scan == sequential oracle for every chunk size
 # ---------------------------------------------------------------------------
-def linear_case(L, B, d, nd, chunk, seed, uf_shift=2.0):
+def linear_case(L, B, d, nd, chunk, seed, uf_shift=2.0, dt="f32"):
     w = workloads.custom(L, B, d, ndir=nd, alpha=0.8, mode="given_u", linear=True,
-                         uf_shift=uf_shift, c0="normal0.1")
+                         uf_shift=uf_shift, c0="normal0.1", u_dtype=dt, x_dtype=dt)
     inp = workloads.make_inputs(w, seed=seed, dc_last=True, b_scale=0.3)
     t = dev_inputs(inp)
     shape = SruShape(L, B, d, nd == 2, w.alpha)
@@ -253,6 +253,14 @@ def test_linear_scan_chunk_sizes(chunk):
 
 def test_linear_scan_bidirectional_ragged():
     linear_case(50, 2, 33, 2, 8, seed=4100)
+
+
+@pytest.mark.parametrize("L,B,d,nd,dt", [(700, 2, 64, 2, "f32"), (1000, 1, 128, 1, "f32"),
+                                         (520, 1, 128, 1, "bf16"), (256, 1, 64, 1, "f32"),
+                                         (3, 2, 64, 1, "f32")])
+def test_linear_scan_single_pass_chunk256(L, B, d, nd, dt):
+    """chunk 256 with d % 64 == 0 takes the single-pass look-back kernels."""
+    linear_case(L, B, d, nd, 256, seed=4500 + L, dt=dt)
 
 
 def test_linear_scan_carry_stress():
