@@ -168,6 +168,13 @@ sru_status sru_backward(const sru_shape *shape,
  *     h and c_last are ignored.
  *   chunk >= 1.  workspace: sru_workspace_size(shape, SRU_WS_LINEAR_FWD or
  *   SRU_WS_LINEAR_BWD, chunk) bytes, 256-byte aligned.
+ * With chunk == 256 and d % 64 == 0 the three steps run as one kernel per
+ * direction: each chunk takes its incoming state from the preceding chunk
+ * through the workspace (a bounded wait).  Should a wait ever run out, the
+ * kernel stops waiting and sets the 32-bit word at byte offset
+ * 8 * ceil(L / 256) * B * d + 4 of the workspace to a nonzero value; the
+ * outputs of that call are then invalid.  The word is cleared at the start
+ * of every such call and may be read after it completes.
  */
 sru_status sru_linear_scan(const sru_shape *shape, sru_pass pass, int32_t chunk,
                            const void *U, sru_dtype u_dt,

@@ -242,52 +242,53 @@ __global__ __launch_bounds__(256) void lin_db_reduce(LinGeom g, const float *__r
 // Single-pass chunked scan (chunk = W * SEG steps, d % 64 == 0).
 //
 // A workgroup of W waves owns 64 consecutive chains and one chunk; wave w
-// holds steps [w*SEG, (w+1)*SEG) of the chunk in registers, so every input
-// element is read from HBM once:
+// holds steps [w*SEG, (w+1)*SEG) of the chunk, so every input element is
+// read from HBM once:
 //   1. each lane folds its SEG steps into the segment map (A, E);
 //   2. wave 0 folds the W segment maps into the chunk map, obtains the
-//      chunk's incoming state from the previous chunk of the same chains
-//      (published in the workspace with a ready flag), publishes its own
-//      outgoing state, and hands every segment its incoming state via LDS;
+//      chunk's incoming state from the previous chunk of the same chains,
+//      publishes its own outgoing state, and hands every segment its
+//      incoming state via LDS;
 //   3. each lane replays its steps from that state and writes h and c.
-// Chunks take dynamic tickets in chain-major order (ticket = chunk * tiles
-// + tile), so a chunk only ever waits for a chunk that started before it:
-// progress is guaranteed.  The wait is bounded; if the bound is ever hit the
-// kernel stops waiting and raises the error word of the workspace.
+// A published state is one 64-bit word per (chunk, chain): the float's bits
+// in the low half and a ready mark in the high half, written and read with
+// single relaxed device-scope atomics.  Value and mark travel together, so
+// no fence (and none of the L2 write-back / invalidate a device-scope fence
+// costs) is needed.  Chunks take dynamic tickets in chain-major order
+// (ticket = chunk * tiles + tile), so a chunk only ever waits for a chunk
+// that started before it: progress is guaranteed.  The wait is bounded; if
+// the bound is ever hit the kernel stops waiting and raises the error word
+// of the workspace.
 // ---------------------------------------------------------------------------
 struct Lookback {
-    float *carry;        // [nC, chains]  outgoing state of each chunk
-    uint32_t *flags;     // [nC, tiles]   1 when that chunk's carry is published
+    uint64_t *carry;     // [nC, chains]  published outgoing state of each chunk
     uint32_t *ticket;    // dynamic chunk ticket
     uint32_t *err;       // set if a wait ran out
 };
 
 constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr uint64_t kReady = uint64_t(1) << 32;
 
-__device__ __forceinline__ void publish(Lookback lb, int64_t idx, float v, int64_t flag_idx,
-                                        int lane)
+__device__ __forceinline__ void publish(Lookback lb, int64_t idx, float v)
 {
-    __hip_atomic_store(lb.carry + idx, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    if (lane == 0)
-        __hip_atomic_store(lb.flags + flag_idx, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(lb.carry + idx, kReady | __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ float consume(Lookback lb, int64_t idx, int64_t flag_idx, int lane)
+__device__ __forceinline__ float consume(Lookback lb, int64_t idx, int lane)
 {
-    if (lane == 0) {
-        uint32_t spins = 0;
-        while (__hip_atomic_load(lb.flags + flag_idx, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-            __builtin_amdgcn_s_sleep(2);
-            if (++spins > kSpinLimit) {
+    uint64_t w = __hip_atomic_load(lb.carry + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t spins = 0;
+    while (!__all((w & kReady) != 0)) {
+        if (++spins > kSpinLimit) {
+            if (lane == 0)
                 __hip_atomic_store(lb.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
+            break;
         }
+        __builtin_amdgcn_s_sleep(2);
+        w = __hip_atomic_load(lb.carry + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    return __hip_atomic_load(lb.carry + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __uint_as_float((uint32_t)w);
 }
 
 __device__ __forceinline__ int64_t take_ticket(Lookback lb, uint32_t *s_ticket)
@@ -299,14 +300,51 @@ __device__ __forceinline__ int64_t take_ticket(Lookback lb, uint32_t *s_ticket)
     return (int64_t)__builtin_amdgcn_readfirstlane(*s_ticket);
 }
 
-template <typename TU, typename TX, int W, int SEG>
-__global__ __launch_bounds__(W * 64) void lin_fwd_fused(LinGeom g, const TU *__restrict__ U,
-                                                         const TX *__restrict__ X,
-                                                         const float *__restrict__ bias,
-                                                         float alpha, const float *__restrict__ c0,
-                                                         float *h, float *c_seq, float *c_last,
-                                                         Lookback lb)
+// Rows of one wave's segment.  Step i of the segment (i = 0..SEG-1, in the
+// direction's own order) lives at time t0 + row(i); steps past the end of
+// the sequence are clamped onto the segment's last valid step, so every
+// load stays in bounds.  t0 is the segment's lowest time index, so every
+// row offset is a small non-negative number: with one uniform 64-bit base
+// per stream, an access costs a 32-bit offset instead of 64-bit address
+// arithmetic per step.
+struct SegRows {
+    int64_t t0;   // lowest time index the segment touches
+    int nv1;      // index of the segment's last valid step (-1: none)
+    bool rev;     // reverse direction: time decreases along the segment
+
+    __device__ SegRows(const LinGeom &g, int64_t s_lo, int seg)
+    {
+        const int64_t left = g.L - 1 - s_lo;
+        nv1 = (int)(left < 0 ? -1 : (left < seg - 1 ? left : seg - 1));
+        rev = g.dl != 0;
+        t0 = rev ? g.L - 1 - (s_lo + (nv1 < 0 ? 0 : nv1)) : s_lo;
+    }
+    __device__ __forceinline__ uint32_t row(int i) const
+    {
+        const int r = i < nv1 ? i : nv1;
+        return (uint32_t)(rev ? nv1 - r : r);
+    }
+};
+
+template <typename T> __device__ __forceinline__ float ld_off(const char *base, uint32_t off)
 {
+    return load_as_f32((const T *)(base + off));
+}
+__device__ __forceinline__ void st_off(char *base, uint32_t off, float v)
+{
+    *(float *)(base + off) = v;
+}
+__device__ __forceinline__ float ldf_off(const char *base, uint32_t off)
+{
+    return *(const float *)(base + off);
+}
+
+template <typename TU, typename TX, int W, int SEG, int PB, int WPE>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(WPE))) void lin_fwd_fused(
+    LinGeom g, const TU *__restrict__ U, const TX *__restrict__ X, const float *__restrict__ bias,
+    float alpha, const float *__restrict__ c0, float *h, float *c_seq, float *c_last, Lookback lb)
+{
+    static_assert(SEG % PB == 0, "phase-3 batches must tile the segment");
     __shared__ float sA[W][64], sE[W][64], sC[W][64];
     __shared__ uint32_t s_ticket;
     const int lane = threadIdx.x & 63;
@@ -314,42 +352,44 @@ __global__ __launch_bounds__(W * 64) void lin_fwd_fused(LinGeom g, const TU *__r
     const int64_t tiles = g.chains / 64;
     const int64_t tk = take_ticket(lb, &s_ticket);
     const int64_t k = tk / tiles, tile = tk % tiles;
-    // a tile is 64 consecutive channels of one batch row (d % 64 == 0): all
-    // addressing is uniform except the lane, so loads take a scalar base
+    // a tile is 64 consecutive channels of one batch row (d % 64 == 0)
     const int64_t ch0 = tile * 64, ch = ch0 + lane;
     const int64_t j0 = ch0 % g.d, bb = ch0 / g.d, j = j0 + lane;
     const float bfs = bias[(g.dl * 2 + 0) * g.d + j] * kNegLog2e;
     const float brs = bias[(g.dl * 2 + 1) * g.d + j] * kNegLog2e;
     const int64_t s_lo = k * g.chunk + wv * SEG;
+    const SegRows sr(g, s_lo, SEG);
+    // uniform bases at row t0; per-lane part: lane * element size
     const int64_t ustride = g.B * g.ndir * 3 * g.d, xstride = g.B * g.d;
-    const TU *ub0 = U + (bb * g.ndir + g.dl) * 3 * g.d + j0;     // uniform
-    const TX *xb0 = X + bb * g.d + j0;                          // uniform
-    const uint32_t ulane = (uint32_t)lane;                      // the only per-lane offset
+    const int64_t ostride = g.B * g.ndir * g.d;
+    const char *ubase = (const char *)(U + sr.t0 * ustride + (bb * g.ndir + g.dl) * 3 * g.d + j0);
+    const char *xbase = (const char *)(X + sr.t0 * xstride + bb * g.d + j0);
+    const uint32_t urow = (uint32_t)(ustride * sizeof(TU)), xrow = (uint32_t)(xstride * sizeof(TX));
+    const uint32_t orow = (uint32_t)(ostride * sizeof(float));
+    const uint32_t ulane = (uint32_t)lane * sizeof(TU), xlane = (uint32_t)lane * sizeof(TX);
+    const uint32_t olane = (uint32_t)lane * sizeof(float);
+    const uint32_t ud = (uint32_t)(g.d * sizeof(TU));   // stream-to-stream distance in a row
 
-    // phase 1: load the segment, fold it into (A, E)
-    float ga[SEG], gb[SEG], ur[SEG], xv[SEG];
-#pragma unroll
-    for (int i = 0; i < SEG; ++i) {
-        const int64_t s = s_lo + i < g.L ? s_lo + i : g.L - 1;   // clamp: in bounds
-        const int64_t t = lin_t(g, s);
-        const TU *up = ub0 + t * ustride;                           // uniform
-        ga[i] = load_as_f32(up + ulane);
-        gb[i] = load_as_f32(up + 2 * g.d + ulane);
-        ur[i] = load_as_f32(up + g.d + ulane);
-        xv[i] = load_as_f32(xb0 + t * xstride + ulane);
-    }
+    // phase 1: load the forget-gate and candidate streams of the segment and
+    // fold them into (A, E); the map (a, beta) of each step stays in registers
+    float ga[SEG], gb[SEG];
     float A = 1.0f, E = 0.0f;
+    if (sr.nv1 >= 0) {
 #pragma unroll
-    for (int i = 0; i < SEG; ++i) {
-        if (s_lo + i < g.L) {
-            const Gate a = gate_scaled(fmaf(ga[i], kNegLog2e, bfs));
-            ga[i] = a.g;
-            gb[i] = a.gc * gb[i];          // beta = (1 - a) u_cand
-            E = fmaf(a.g, E, gb[i]);
-            A *= a.g;
-        } else {
-            ga[i] = 1.0f;                  // identity map past the end
-            gb[i] = 0.0f;
+        for (int i = 0; i < SEG; ++i) {
+            const uint32_t o = sr.row(i) * urow + ulane;
+            ga[i] = ld_off<TU>(ubase, o);
+            gb[i] = ld_off<TU>(ubase, o + 2 * ud);
+        }
+#pragma unroll
+        for (int i = 0; i < SEG; ++i) {
+            if (i <= sr.nv1) {
+                const Gate a = gate_scaled(fmaf(ga[i], kNegLog2e, bfs));
+                ga[i] = a.g;
+                gb[i] = a.gc * gb[i];          // beta = (1 - a) u_cand
+                E = fmaf(a.g, E, gb[i]);
+                A *= a.g;
+            }
         }
     }
     sA[wv][lane] = A;
@@ -368,8 +408,8 @@ __global__ __launch_bounds__(W * 64) void lin_fwd_fused(LinGeom g, const TU *__r
         if (k == 0)
             cin = c0 ? c0[g.dl * g.chains + ch] : 0.0f;
         else
-            cin = consume(lb, (k - 1) * g.chains + ch, (k - 1) * tiles + tile, lane);
-        if (k + 1 < g.nC) publish(lb, k * g.chains + ch, fmaf(Ac, cin, Ec), k * tiles + tile, lane);
+            cin = consume(lb, (k - 1) * g.chains + ch, lane);
+        if (k + 1 < g.nC) publish(lb, k * g.chains + ch, fmaf(Ac, cin, Ec));
         float cc = cin;
 #pragma unroll
         for (int w = 0; w < W; ++w) {
@@ -378,25 +418,35 @@ __global__ __launch_bounds__(W * 64) void lin_fwd_fused(LinGeom g, const TU *__r
         }
     }
     __syncthreads();
+    if (sr.nv1 < 0) return;   // the whole segment lies past the end
 
-    // phase 3: replay the segment, write h and c
+    // phase 3: replay the segment PB steps at a time; the reset-gate and x
+    // streams are loaded only now, next to the stores of h and c
     float c = sC[wv][lane];
-    const int64_t ostride = g.B * g.ndir * g.d;
-    float *hb0 = h + (bb * g.ndir + g.dl) * g.d + j0;                    // uniform
-    float *cb0 = c_seq ? c_seq + (bb * g.ndir + g.dl) * g.d + j0 : nullptr;
+    char *hbase = (char *)(h + sr.t0 * ostride + (bb * g.ndir + g.dl) * g.d + j0);
+    char *cbase = c_seq ? (char *)(c_seq + sr.t0 * ostride + (bb * g.ndir + g.dl) * g.d + j0)
+                        : nullptr;
 #pragma unroll
-    for (int i = 0; i < SEG; ++i) {
-        const int64_t s = s_lo + i;
-        if (s < g.L) {
-            c = fmaf(ga[i], c, gb[i]);
-            const Gate r = gate_scaled(fmaf(ur[i], kNegLog2e, brs));
-            const int64_t t = lin_t(g, s);
-            float *ho = hb0 + t * ostride;                          // uniform
-            ho[ulane] = fmaf(r.g, c, r.gc * (alpha * xv[i]));
-            if (cb0) (cb0 + t * ostride)[ulane] = c;
-            if (s == g.L - 1 && c_last) c_last[g.dl * g.chains + ch] = c;
+    for (int i0 = 0; i0 < SEG; i0 += PB) {
+        float ur[PB], xv[PB];
+#pragma unroll
+        for (int i = 0; i < PB; ++i) {
+            const uint32_t r = sr.row(i0 + i);
+            ur[i] = ld_off<TU>(ubase, r * urow + ulane + ud);
+            xv[i] = ld_off<TX>(xbase, r * xrow + xlane);
+        }
+#pragma unroll
+        for (int i = 0; i < PB; ++i) {
+            if (i0 + i <= sr.nv1) {
+                c = fmaf(ga[i0 + i], c, gb[i0 + i]);
+                const Gate rg = gate_scaled(fmaf(ur[i], kNegLog2e, brs));
+                const uint32_t o = sr.row(i0 + i) * orow + olane;
+                st_off(hbase, o, fmaf(rg.g, c, rg.gc * (alpha * xv[i])));
+                if (cbase) st_off(cbase, o, c);
+            }
         }
     }
+    if (c_last && s_lo + sr.nv1 == g.L - 1) c_last[g.dl * g.chains + ch] = c;
 }
 
 // Backward: the adjoint of the state runs from the last step to the first,
@@ -405,13 +455,14 @@ __global__ __launch_bounds__(W * 64) void lin_fwd_fused(LinGeom g, const TU *__r
 // ticket / tiles) and each segment's map is g -> A g + G over its steps in
 // reverse.  Phase 3 recomputes the gates from the register-held U values and
 // writes dU, dx and the per-chunk partial sums of dU_f, dU_r (for db).
-template <typename TU, typename TX, int W, int SEG>
-__global__ __launch_bounds__(W * 64) void lin_bwd_fused(
+template <typename TU, typename TX, int W, int SEG, int PB, int WPE>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(WPE))) void lin_bwd_fused(
     LinGeom g, const TU *__restrict__ U, const TX *__restrict__ X, const float *__restrict__ bias,
     float alpha, const float *__restrict__ c0, const float *__restrict__ c_seq,
     const float *__restrict__ dh, const float *__restrict__ dc_last, float *dU, float *dx,
     bool dx_acc, float *dc0, float *dbpart, Lookback lb)
 {
+    static_assert(SEG % PB == 0, "phase-3 batches must tile the segment");
     __shared__ float sA[W][64], sG[W][64], sC[W][64];
     __shared__ float sbf_w[W][64], sbr_w[W][64];
     __shared__ uint32_t s_ticket;
@@ -425,33 +476,41 @@ __global__ __launch_bounds__(W * 64) void lin_bwd_fused(
     const float bfs = bias[(g.dl * 2 + 0) * g.d + j] * kNegLog2e;
     const float brs = bias[(g.dl * 2 + 1) * g.d + j] * kNegLog2e;
     const int64_t s_lo = k * g.chunk + wv * SEG;
+    const SegRows sr(g, s_lo, SEG);
     const int64_t ustride = g.B * g.ndir * 3 * g.d, xstride = g.B * g.d;
     const int64_t hstride = g.B * g.ndir * g.d;
-    const TU *ul = U + (bb * g.ndir + g.dl) * 3 * g.d + j0;          // uniform bases
-    const TX *xl = X + bb * g.d + j0;
-    const float *dhl = dh + (bb * g.ndir + g.dl) * g.d + j0;
-    const float *csl = c_seq + (bb * g.ndir + g.dl) * g.d + j0;
-    const uint32_t ulane = (uint32_t)lane;                      // the only per-lane offset
-    auto clampL = [&](int64_t s) { return s < g.L ? s : g.L - 1; };
+    const int64_t uoff = (bb * g.ndir + g.dl) * 3 * g.d + j0, xoff = bb * g.d + j0;
+    const int64_t hoff = (bb * g.ndir + g.dl) * g.d + j0;
+    const char *ubase = (const char *)(U + sr.t0 * ustride + uoff);       // uniform bases
+    const char *xbase = (const char *)(X + sr.t0 * xstride + xoff);
+    const char *dhbase = (const char *)(dh + sr.t0 * hstride + hoff);
+    const char *csbase = (const char *)(c_seq + sr.t0 * hstride + hoff);
+    const uint32_t urow = (uint32_t)(ustride * sizeof(TU)), xrow = (uint32_t)(xstride * sizeof(TX));
+    const uint32_t hrow = (uint32_t)(hstride * sizeof(float));
+    const uint32_t frow = (uint32_t)(ustride * sizeof(float)), fxrow = (uint32_t)(xstride * sizeof(float));
+    const uint32_t ulane = (uint32_t)lane * sizeof(TU), xlane = (uint32_t)lane * sizeof(TX);
+    const uint32_t flane = (uint32_t)lane * sizeof(float);
+    const uint32_t ud = (uint32_t)(g.d * sizeof(TU)), fd = (uint32_t)(g.d * sizeof(float));
 
     // phase 1: gates and dh of the segment, folded in reverse into (A, G)
     float uf[SEG], ur[SEG], dv[SEG];
-#pragma unroll
-    for (int i = 0; i < SEG; ++i) {
-        const int64_t t = lin_t(g, clampL(s_lo + i));
-        const TU *up = ul + t * ustride;                            // uniform
-        uf[i] = load_as_f32(up + ulane);
-        ur[i] = load_as_f32(up + g.d + ulane);
-        dv[i] = (dhl + t * hstride)[ulane];
-    }
     float A = 1.0f, G = 0.0f;
+    if (sr.nv1 >= 0) {
 #pragma unroll
-    for (int i = SEG - 1; i >= 0; --i) {
-        if (s_lo + i < g.L) {
-            const Gate a = gate_scaled(fmaf(uf[i], kNegLog2e, bfs));
-            const Gate r = gate_scaled(fmaf(ur[i], kNegLog2e, brs));
-            G = a.g * fmaf(r.g, dv[i], G);
-            A *= a.g;
+        for (int i = 0; i < SEG; ++i) {
+            const uint32_t r = sr.row(i);
+            uf[i] = ld_off<TU>(ubase, r * urow + ulane);
+            ur[i] = ld_off<TU>(ubase, r * urow + ulane + ud);
+            dv[i] = ldf_off(dhbase, r * hrow + flane);
+        }
+#pragma unroll
+        for (int i = SEG - 1; i >= 0; --i) {
+            if (i <= sr.nv1) {
+                const Gate a = gate_scaled(fmaf(uf[i], kNegLog2e, bfs));
+                const Gate r = gate_scaled(fmaf(ur[i], kNegLog2e, brs));
+                G = a.g * fmaf(r.g, dv[i], G);
+                A *= a.g;
+            }
         }
     }
     sA[wv][lane] = A;
@@ -469,8 +528,8 @@ __global__ __launch_bounds__(W * 64) void lin_bwd_fused(
         if (k == g.nC - 1)
             gin = dc_last ? dc_last[g.dl * g.chains + ch] : 0.0f;
         else
-            gin = consume(lb, (k + 1) * g.chains + ch, (k + 1) * tiles + tile, lane);
-        if (k > 0) publish(lb, k * g.chains + ch, fmaf(Ac, gin, Gc), k * tiles + tile, lane);
+            gin = consume(lb, (k + 1) * g.chains + ch, lane);
+        if (k > 0) publish(lb, k * g.chains + ch, fmaf(Ac, gin, Gc));
         float gg = gin;
 #pragma unroll
         for (int w = W - 1; w >= 0; --w) {
@@ -480,47 +539,54 @@ __global__ __launch_bounds__(W * 64) void lin_bwd_fused(
     }
     __syncthreads();
 
-    // phase 3: local gradients, last step of the segment first
-    float ux[SEG], xv[SEG], cv[SEG];
-#pragma unroll
-    for (int i = 0; i < SEG; ++i) {
-        const int64_t t = lin_t(g, clampL(s_lo + i));
-        ux[i] = load_as_f32(ul + t * ustride + 2 * g.d + ulane);
-        xv[i] = load_as_f32(xl + t * xstride + ulane);
-        cv[i] = (csl + t * hstride)[ulane];
-    }
-    float cprev0;   // state before the segment's first step
-    if (s_lo == 0)
-        cprev0 = c0 ? c0[g.dl * g.chains + ch] : 0.0f;
-    else
-        cprev0 = (csl + lin_t(g, clampL(s_lo - 1)) * hstride)[ulane];
+    // phase 3: local gradients, last step of the segment first, PB steps at
+    // a time; the candidate, x and state streams are loaded only now.  Each
+    // batch also needs the state one step before it: the previous batch's
+    // last row, or for the first batch the state entering the segment.
     float gc = sC[wv][lane];
     float sbf = 0.0f, sbr = 0.0f;
-    float *dul = dU + (bb * g.ndir + g.dl) * 3 * g.d + j0;              // uniform bases
-    float *dxl = dx + bb * g.d + j0;
+    if (sr.nv1 >= 0) {
+        float c_enter;   // state before the segment's first step
+        if (s_lo == 0)
+            c_enter = c0 ? c0[g.dl * g.chains + ch] : 0.0f;
+        else
+            c_enter = c_seq[lin_t(g, s_lo - 1) * hstride + hoff + lane];
+        char *dubase = (char *)(dU + sr.t0 * ustride + uoff);
+        char *dxbase = (char *)(dx + sr.t0 * xstride + xoff);
 #pragma unroll
-    for (int i = SEG - 1; i >= 0; --i) {
-        const int64_t s = s_lo + i;
-        if (s < g.L) {
-            const Gate a = gate_scaled(fmaf(uf[i], kNegLog2e, bfs));
-            const Gate r = gate_scaled(fmaf(ur[i], kNegLog2e, brs));
-            const float cp = i > 0 ? cv[i - 1] : cprev0;
-            const float D = fmaf(r.g, dv[i], gc);
-            const float dr = dv[i] * fmaf(-alpha, xv[i], cv[i]);
-            const int64_t t = lin_t(g, s);
-            float dxh = dv[i] * r.gc * alpha;
-            float *xo = dxl + t * xstride;                          // uniform
-            float *uo = dul + t * ustride;
-            if (dx_acc) dxh += xo[ulane];
-            const float dzf = D * (cp - ux[i]) * (a.g * a.gc);
-            const float dzr = dr * (r.g * r.gc);
-            uo[ulane] = dzf;
-            (uo + g.d)[ulane] = dzr;
-            (uo + 2 * g.d)[ulane] = D * a.gc;
-            xo[ulane] = dxh;
-            sbf += dzf;
-            sbr += dzr;
-            gc = a.g * D;
+        for (int i0 = SEG - PB; i0 >= 0; i0 -= PB) {
+            float ux[PB], xv[PB], cv[PB + 1];   // cv[i + 1] = c at step i0 + i
+#pragma unroll
+            for (int i = 0; i < PB; ++i) {
+                const uint32_t r = sr.row(i0 + i);
+                ux[i] = ld_off<TU>(ubase, r * urow + ulane + 2 * ud);
+                xv[i] = ld_off<TX>(xbase, r * xrow + xlane);
+                cv[i + 1] = ldf_off(csbase, r * hrow + flane);
+            }
+            cv[0] = i0 == 0 ? c_enter : ldf_off(csbase, sr.row(i0 - 1) * hrow + flane);
+#pragma unroll
+            for (int i = PB - 1; i >= 0; --i) {
+                if (i0 + i <= sr.nv1) {
+                    const Gate a = gate_scaled(fmaf(uf[i0 + i], kNegLog2e, bfs));
+                    const Gate r = gate_scaled(fmaf(ur[i0 + i], kNegLog2e, brs));
+                    const float dvi = dv[i0 + i];
+                    const float D = fmaf(r.g, dvi, gc);
+                    const float dr = dvi * fmaf(-alpha, xv[i], cv[i + 1]);
+                    const uint32_t row = sr.row(i0 + i);
+                    const uint32_t xo = row * fxrow + flane, uo = row * frow + flane;
+                    float dxh = dvi * r.gc * alpha;
+                    if (dx_acc) dxh += ldf_off(dxbase, xo);
+                    const float dzf = D * (cv[i] - ux[i]) * (a.g * a.gc);
+                    const float dzr = dr * (r.g * r.gc);
+                    st_off(dubase, uo, dzf);
+                    st_off(dubase, uo + fd, dzr);
+                    st_off(dubase, uo + 2 * fd, D * a.gc);
+                    st_off(dxbase, xo, dxh);
+                    sbf += dzf;
+                    sbr += dzr;
+                    gc = a.g * D;
+                }
+            }
         }
     }
     if (k == 0 && wv == 0 && dc0) dc0[g.dl * g.chains + ch] = gc;
@@ -549,20 +615,42 @@ __global__ __launch_bounds__(256) void lin_clear(uint32_t *p, int64_t n)
 }
 
 constexpr int kFusedChunk = 256;
-constexpr int kFwdW = 16, kFwdSeg = 16;   // 16 waves x 16 steps
-constexpr int kBwdW = 16, kBwdSeg = 16;   // 16 waves x 16 steps
+#ifndef SRU_LIN_FWD_W
+#define SRU_LIN_FWD_W 16
+#endif
+#ifndef SRU_LIN_FWD_PB
+#define SRU_LIN_FWD_PB 16
+#endif
+#ifndef SRU_LIN_FWD_WPE
+#define SRU_LIN_FWD_WPE 4
+#endif
+#ifndef SRU_LIN_BWD_WPE
+#define SRU_LIN_BWD_WPE 4
+#endif
+#ifndef SRU_LIN_BWD_W
+#define SRU_LIN_BWD_W 16
+#endif
+#ifndef SRU_LIN_BWD_PB
+#define SRU_LIN_BWD_PB 16
+#endif
+constexpr int kFwdW = SRU_LIN_FWD_W, kFwdSeg = kFusedChunk / kFwdW, kFwdPB = SRU_LIN_FWD_PB,
+              kFwdWpe = SRU_LIN_FWD_WPE;
+constexpr int kBwdW = SRU_LIN_BWD_W, kBwdSeg = kFusedChunk / kBwdW, kBwdPB = SRU_LIN_BWD_PB,
+              kBwdWpe = SRU_LIN_BWD_WPE;
 static_assert(kFwdW * kFwdSeg == kFusedChunk && kBwdW * kBwdSeg == kFusedChunk, "chunk split");
 
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
-// Workspace layout of the fused kernels (floats / words):
-//   carry [nC * chains] | backward: db partials [2 * nC * chains] |
-//   control words: ticket, error, pad to 64 | flags [nC * tiles]
+// Workspace layout of the single-pass kernels (in floats):
+//   published states [nC * chains] 64-bit words (2 floats each) |
+//   ticket, error, pad to 64 | backward only: db partials [2 * nC * chains]
+// The states and the control words are cleared before each launch.
 struct FusedWs {
     Lookback lb;
     float *dbpart;
     uint32_t *ctrl;
-    int64_t ctrl_words;
+    uint32_t *clear;       // start of the region cleared before each launch
+    int64_t clear_words;
 };
 
 FusedWs fused_ws(const LinArgs &a, bool backward)
@@ -571,21 +659,24 @@ FusedWs fused_ws(const LinArgs &a, bool backward)
     const int64_t chains = a.B * a.d;
     float *ws = (float *)a.ws;
     FusedWs f;
-    f.lb.carry = ws;
-    f.dbpart = ws + nC * chains;
-    f.ctrl = (uint32_t *)(ws + (backward ? 3 : 1) * nC * chains);
+    f.lb.carry = (uint64_t *)ws;
+    f.ctrl = (uint32_t *)(ws + 2 * nC * chains);
+    f.dbpart = backward ? ws + 2 * nC * chains + 64 : nullptr;
     f.lb.ticket = f.ctrl;
     f.lb.err = f.ctrl + 1;
-    f.lb.flags = f.ctrl + 64;
-    f.ctrl_words = 64 + nC * (chains / 64);
+    f.clear = (uint32_t *)ws;
+    f.clear_words = 2 * nC * chains + 64;
     return f;
 }
 
 bool use_fused(const LinArgs &a)
 {
     const int64_t chains = a.B * a.d;
-    return a.chunk == kFusedChunk && a.d % 64 == 0 && (chains / 64) * ((a.L + a.chunk - 1) / a.chunk) <
-                                                          (int64_t(1) << 31);
+    const int64_t seg = kFwdSeg > kBwdSeg ? kFwdSeg : kBwdSeg;
+    // the kernels address a segment with 32-bit byte offsets from one base
+    const int64_t seg_bytes = (seg + 1) * a.B * a.ndir * 3 * a.d * (int64_t)sizeof(float);
+    return a.chunk == kFusedChunk && a.d % 64 == 0 && seg_bytes < (int64_t(1) << 31) &&
+           (chains / 64) * ((a.L + a.chunk - 1) / a.chunk) < (int64_t(1) << 31);
 }
 
 template <typename TU, typename TX>
@@ -596,9 +687,9 @@ hipError_t lin_forward_fused(const LinArgs &a, hipStream_t s)
     const FusedWs f = fused_ws(a, false);
     for (int dl = 0; dl < a.ndir; ++dl) {
         LinGeom g{a.L, a.B, a.d, a.chunk, nC, chains, a.ndir, dl};
-        hipLaunchKernelGGL(lin_clear, dim3(blocks_for(f.ctrl_words)), dim3(256), 0, s, f.ctrl,
-                           f.ctrl_words);
-        hipLaunchKernelGGL((lin_fwd_fused<TU, TX, kFwdW, kFwdSeg>), dim3((unsigned)(nC * (chains / 64))),
+        hipLaunchKernelGGL(lin_clear, dim3(blocks_for(f.clear_words)), dim3(256), 0, s, f.clear,
+                           f.clear_words);
+        hipLaunchKernelGGL((lin_fwd_fused<TU, TX, kFwdW, kFwdSeg, kFwdPB, kFwdWpe>), dim3((unsigned)(nC * (chains / 64))),
                            dim3(kFwdW * 64), 0, s, g, (const TU *)a.U, (const TX *)a.x, a.b, a.alpha,
                            a.c0, a.h, a.c_seq, a.c_last, f.lb);
     }
@@ -613,9 +704,9 @@ hipError_t lin_backward_fused(const LinArgs &a, hipStream_t s)
     const FusedWs f = fused_ws(a, true);
     for (int dl = a.ndir - 1; dl >= 0; --dl) {
         LinGeom g{a.L, a.B, a.d, a.chunk, nC, chains, a.ndir, dl};
-        hipLaunchKernelGGL(lin_clear, dim3(blocks_for(f.ctrl_words)), dim3(256), 0, s, f.ctrl,
-                           f.ctrl_words);
-        hipLaunchKernelGGL((lin_bwd_fused<TU, TX, kBwdW, kBwdSeg>), dim3((unsigned)(nC * (chains / 64))),
+        hipLaunchKernelGGL(lin_clear, dim3(blocks_for(f.clear_words)), dim3(256), 0, s, f.clear,
+                           f.clear_words);
+        hipLaunchKernelGGL((lin_bwd_fused<TU, TX, kBwdW, kBwdSeg, kBwdPB, kBwdWpe>), dim3((unsigned)(nC * (chains / 64))),
                            dim3(kBwdW * 64), 0, s, g, (const TU *)a.U, (const TX *)a.x, a.b, a.alpha,
                            a.c0, a.c_seq, a.dh, a.dc_last, a.dU, a.dx, dl != a.ndir - 1, a.dc0,
                            f.dbpart, f.lb);
@@ -680,8 +771,8 @@ size_t linear_workspace_bytes(int64_t L, int64_t B, int64_t d, int ndir, int64_t
     (void)ndir;  // directions are processed one after another and reuse it
     const int64_t nC = (L + chunk - 1) / chunk;
     const int64_t per = nC * B * d;
-    // three-phase: 3 (fwd) or 5 (bwd) per-chunk arrays; fused: carry (+ db
-    // partials) + 64 control words + one flag per 64 chains and chunk
+    // three-phase: 3 (fwd) or 5 (bwd) per-chunk arrays; single pass: 64-bit
+    // published states (+ db partials) and 64 control words
     const int64_t floats = (backward ? 5 * per : 3 * per) + 64;
     return (size_t)floats * sizeof(float);
 }
