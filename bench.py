@@ -42,12 +42,16 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=2, choices=[2, 4])
-    p.add_argument("--sets", type=int, default=3, help="rotating input/output sets")
+    p.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5],
+                   help="2, 4: training step; 3: given-U forward; 5: linear mode fwd+bwd")
+    p.add_argument("--sets", type=int, default=4, help="rotating input/output sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run one torch copy of this many MiB (counter calibration)")
+    p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU work: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
+                        "then WRITE_SIZE, each with --copy-probe-mib) into profiles/traffic.json")
     return p.parse_args()
 
 
@@ -72,8 +76,9 @@ def row_work(w):
     if w.mode == "layer":
         rows["a1_projection"] = dict(flops=2 * LB * n3 * d,
                                      bytes=LB * d * xs + n3 * d * 2 + LB * n3 * 4)
+        # bf16(dU) x bf16 W, plus the highway dx read and dX written
         rows["a5_projection_bwd_data"] = dict(flops=2 * LB * d * n3,
-                                              bytes=LB * n3 * 4 + n3 * d * 2 + 2 * LB * d * 4)
+                                              bytes=LB * n3 * 2 + n3 * d * 2 + 2 * LB * d * 4)
     fwd = LB * n3 * us + LB * d * xs + LB * nd * d * 4 * (2 if w.backward else 1)
     if w.linear:
         rows["a6_linear_forward"] = dict(bytes=fwd)
@@ -183,49 +188,37 @@ def time_rows(row_sets, steps, warmup):
     return total_ms / steps, per_row
 
 
-def extras(steps):
-    """Rows at the other workload sizes (each timed alone, inputs rotating)."""
+def row_sets_for(w, nsets, seed0):
+    """Rotating sets of the rows of workload ``w`` (each set: list of (row, fn))."""
     import torch
     from parallelizable_recurrent_units_amd import (SRU_BWD, SRU_FWD, SRU_WS_LINEAR_BWD,
                                                     SRU_WS_LINEAR_FWD, SruShape, sru_forward,
                                                     sru_linear_scan, sru_workspace_size)
-    from parallelizable_recurrent_units_amd.workloads import WORKLOADS
-    out = {}
-    g = torch.Generator(device="cuda")
-    g.manual_seed(3)
     f32 = dict(device="cuda", dtype=torch.float32)
-    # given-U bf16 forward (L=1024, B=16, d=2048)
-    w = WORKLOADS[3]
-    s = SruShape(w.L, w.B, w.d, False, w.alpha)
-    sets = []
-    for _ in range(3):
-        U = torch.randn((w.L, w.B, 1, 3, w.d), generator=g, **f32).to(torch.bfloat16)
-        x = torch.randn((w.L, w.B, w.d), generator=g, **f32).to(torch.bfloat16)
-        v = (torch.rand((1, 2, w.d), generator=g, **f32) - 0.5) * 0.2
-        b = torch.zeros((1, 2, w.d), **f32)
-        h = torch.empty((w.L, w.B, 1, w.d), **f32)
-        cl = torch.empty((1, w.B, w.d), **f32)
-        sets.append([("a2_forward", (lambda U=U, x=x, v=v, b=b, h=h, cl=cl:
-                                     sru_forward(s, U, x, v, b, None, h, None, cl)))])
-    ms, rows = time_rows(sets, steps, 3)
-    work = row_work(w)
-    out[w.name] = {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
-    del sets
-    # L=512 training step
-    w = WORKLOADS[4]
-    row_sets = []
-    for i in range(3):
-        shape, t = device_set(w, 40 + i)
-        row_sets.append(training_step_rows(shape, t))
-    ms, rows = time_rows(row_sets, steps, 3)
-    work = row_work(w)
-    out[w.name] = {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
-    out[w.name]["ms_per_step"] = ms
-    del row_sets
-    torch.cuda.empty_cache()
-    # linear mode, chunk 256 (L=16384, B=4, d=4096)
-    w = WORKLOADS[5]
-    s = SruShape(w.L, w.B, w.d, False, w.alpha)
+    if w.mode == "layer":
+        out = []
+        for i in range(nsets):
+            shape, t = device_set(w, seed0 + i)
+            out.append(training_step_rows(shape, t))
+        return out
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed0)
+    s = SruShape(w.L, w.B, w.d, w.ndir == 2, w.alpha)
+    if not w.linear:
+        # given U (bf16), forward only: U ~ N(0,1), x ~ N(0,1), v ~ U(-0.1, 0.1), b = 0
+        out = []
+        for _ in range(nsets):
+            U = torch.randn((w.L, w.B, 1, 3, w.d), generator=g, **f32).to(torch.bfloat16)
+            x = torch.randn((w.L, w.B, w.d), generator=g, **f32).to(torch.bfloat16)
+            v = (torch.rand((1, 2, w.d), generator=g, **f32) - 0.5) * 0.2
+            b = torch.zeros((1, 2, w.d), **f32)
+            h = torch.empty((w.L, w.B, 1, w.d), **f32)
+            cl = torch.empty((1, w.B, w.d), **f32)
+            out.append([("a2_forward", (lambda U=U, x=x, v=v, b=b, h=h, cl=cl:
+                                        sru_forward(s, U, x, v, b, None, h, None, cl)))])
+        return out
+    # linear mode, chunk 256: U_f ~ N(2,1), U_r, U_x, x, dh ~ N(0,1), b = 0, c0 = 0.
+    # One set: a single call's working set (>= 6 GB) is far beyond every cache.
     U = torch.randn((w.L, w.B, 1, 3, w.d), generator=g, **f32)
     U[:, :, :, 0] += 2.0
     x = torch.randn((w.L, w.B, w.d), generator=g, **f32)
@@ -242,20 +235,44 @@ def extras(steps):
                       dtype=torch.uint8)
     wsb = torch.empty(sru_workspace_size(s, SRU_WS_LINEAR_BWD, w.chunk), device="cuda",
                       dtype=torch.uint8)
-    lin = [[("a6_linear_forward", lambda: sru_linear_scan(s, SRU_FWD, w.chunk, U, x, b, None, h=h,
-                                                          c_seq=c_seq, c_last=cl, workspace=wsf)),
-            ("a7_linear_backward", lambda: sru_linear_scan(s, SRU_BWD, w.chunk, U, x, b, None,
-                                                           c_seq=c_seq, dh=dh, dU=dU, dx=dx,
-                                                           db=dbv, dc0=dc0, workspace=wsb))]]
-    ms, rows = time_rows(lin, max(3, steps // 5), 2)
+    return [[("a6_linear_forward", lambda: sru_linear_scan(s, SRU_FWD, w.chunk, U, x, b, None, h=h,
+                                                           c_seq=c_seq, c_last=cl, workspace=wsf)),
+             ("a7_linear_backward", lambda: sru_linear_scan(s, SRU_BWD, w.chunk, U, x, b, None,
+                                                            c_seq=c_seq, dh=dh, dU=dU, dx=dx,
+                                                            db=dbv, dc0=dc0, workspace=wsb))]]
+
+
+def measure(w, nsets, steps, warmup, seed0):
+    """(ms per step, {row: measurement}) for workload ``w``."""
+    import torch
+    sets = row_sets_for(w, nsets, seed0)
+    ms, rows = time_rows(sets, steps, warmup)
     work = row_work(w)
-    out[w.name] = {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
+    per_row = {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
+    del sets
+    torch.cuda.empty_cache()
+    return ms, per_row
+
+
+def extras(main_id, steps):
+    """Rows at the other workload sizes, each workload timed on its own."""
+    from parallelizable_recurrent_units_amd.workloads import WORKLOADS
+    out = {}
+    for wid in (2, 3, 4, 5):
+        if wid == main_id:
+            continue
+        w = WORKLOADS[wid]
+        linear = w.linear
+        ms, per_row = measure(w, 1 if linear else 4, max(3, steps // 5) if linear else steps,
+                              2 if linear else 3, 40 + 10 * wid)
+        out[w.name] = dict(per_row, ms_per_step=ms)
     return out
 
 
-def cpu_baseline(w, budget_s=20.0):
-    """The CPU oracle (as written) on a bounded sample: whole batch rows of the
-    same training step, until about ``budget_s`` seconds of work."""
+def cpu_baseline(w, budget_s=10.0):
+    """The CPU oracle (as written) on a bounded sample of the same training
+    step: batch rows in order, repeating the whole batch if it finishes early,
+    until about ``budget_s`` seconds of work."""
     import numpy as np
     import oracle
     from parallelizable_recurrent_units_amd.workloads import make_inputs
@@ -264,7 +281,8 @@ def cpu_baseline(w, budget_s=20.0):
     X2 = inp["x"].reshape(L * B, d)
     t0 = time.perf_counter()
     done = 0
-    for b in range(B):
+    while True:
+        b = done % B
         rows = np.arange(L) * B + b
         U = oracle.project(X2, inp["W"], True, rows=rows).reshape(L, 1, nd, 3, d)
         sl = lambda a: np.ascontiguousarray(a[:, b:b + 1])
@@ -280,8 +298,86 @@ def cpu_baseline(w, budget_s=20.0):
     frac = done / B
     return {"value": step_bytes * frac / secs / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{done} of {B} batch rows of the same training step (projection, forward, "
-                      f"backward, dX) in double precision, {secs:.1f} s; bytes scaled by {frac:.4f}"}
+            "elem_steps_per_s": w.elem_steps * frac / secs,
+            "sample": f"{done} batch rows ({frac:.2f} passes over the {B} rows) of the same "
+                      f"training step (projection, forward, backward, dX) in double precision, "
+                      f"{secs:.1f} s; algorithmic bytes scaled by {frac:.4f}"}
+
+
+# kernel launches of one call of each row (what its event-timed span covers)
+ROW_LAUNCHES = {
+    "a1_projection": ["gemm_bf16_mfma (A fp32 X, rounded to bf16 while staged)"],
+    "a2_forward": ["fwd_fast (both directions in one grid)"],
+    "a3_a4_backward": ["bwd_fast (direction 1)", "bwd_fast (direction 0, accumulates dx)",
+                       "param_reduce (dv, db)"],
+    "a5_projection_bwd_data": ["transpose16 (W -> W^T)", "gemm_bf16_mfma (A = bf16 dU copy)"],
+    "a6_linear_forward": ["lin_clear", "lin_fwd_fused"],
+    "a7_linear_backward": ["lin_clear", "lin_bwd_fused", "lin_db_reduce"],
+}
+
+# kernels of each training-step row (rocprofv3 kernel names), and the one
+# kernel that runs exactly once per call of the row
+ROW_KERNELS = {
+    "a1_projection": ([r"gemm_bf16_mfma<.*>, float, "], r"gemm_bf16_mfma<.*>, float, "),
+    "a2_forward": ([r"fwd_fast<"], r"fwd_fast<"),
+    "a3_a4_backward": ([r"bwd_fast<", r"param_reduce"], r"param_reduce"),
+    "a5_projection_bwd_data": ([r"transpose16", r"gemm_bf16_mfma<.*>, unsigned short, "],
+                               r"transpose16"),
+}
+
+
+def _per_dispatch(run_dir, counter):
+    """{dispatch id: (kernel name, counter summed over its hardware instances)}
+    from the rocpd database(s) a rocprofv3 --pmc run wrote under ``run_dir``."""
+    import glob
+    import sqlite3
+    files = glob.glob(os.path.join(run_dir, "**", "*.db"), recursive=True)
+    if not files:
+        raise SystemExit(f"no rocpd database under {run_dir}")
+    per = {}
+    for f in files:
+        db = sqlite3.connect(f)
+        q = "select dispatch_id, name, counter_value from pmc_events where counter_name = ?"
+        for did, name, v in db.execute(q, (counter,)):
+            key = (f, did)
+            n, acc = per.get(key, (name, 0.0))
+            per[key] = (n, acc + float(v))
+        db.close()
+    return per
+
+
+def write_traffic(fetch_dir, write_dir, copy_bytes):
+    """profiles/traffic.json: HBM bytes per call of each row.  FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) are each scaled by the factor that makes the
+    calibration copy (the largest torch copy kernel of the run, which moves
+    ``copy_bytes`` in and out) read and write exactly its size."""
+    import re
+    rows = {}
+    factors = {}
+    for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = _per_dispatch(run_dir, counter)
+        copies = [v for n, v in per.values() if "copyBuffer" in n]
+        if not copies:
+            raise SystemExit(f"{counter}: no calibration copy kernel under {run_dir}")
+        factors[counter] = copy_bytes / (max(copies) * 1024.0)
+        for row, (pats, anchor) in ROW_KERNELS.items():
+            calls = sum(1 for n, _ in per.values() if re.search(anchor, n))
+            if not calls:
+                continue
+            kib = sum(v for n, v in per.values() if any(re.search(q, n) for q in pats))
+            r = rows.setdefault(row, {"calls": calls})
+            r[counter.lower() + "_bytes"] = kib * 1024.0 * factors[counter] / calls
+    for r in rows.values():
+        if "fetch_size_bytes" in r and "write_size_bytes" in r:
+            r["bytes"] = r["fetch_size_bytes"] + r["write_size_bytes"]
+    rec = {"source_digest": source_digest(), "copy_probe_bytes": copy_bytes,
+           "calibration_factors": factors,
+           "rows": {k: v["bytes"] for k, v in rows.items() if "bytes" in v},
+           "detail": rows}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def traffic_for(kernel_row, digest):
@@ -299,6 +395,11 @@ def traffic_for(kernel_row, digest):
 
 def main():
     args = parse()
+    if args.write_traffic:
+        if not args.copy_probe_mib:
+            raise SystemExit("--write-traffic needs the --copy-probe-mib the runs used")
+        write_traffic(*args.write_traffic, copy_bytes=args.copy_probe_mib * (1 << 20))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the hot path is not sharded in this build).", file=sys.stderr)
@@ -309,19 +410,20 @@ def main():
     sru.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = WORKLOADS[args.workload]
-    print(f"[bench] workload {w.name}: building {args.sets} input sets", file=sys.stderr, flush=True)
-    row_sets = []
-    for i in range(args.sets):
-        shape, t = device_set(w, seed=100 + i)
-        row_sets.append(training_step_rows(shape, t))
+    nsets = 1 if w.linear else args.sets
+    print(f"[bench] workload {w.name}: building {nsets} input sets", file=sys.stderr, flush=True)
+    row_sets = row_sets_for(w, nsets, 100)
     print("[bench] timing", file=sys.stderr, flush=True)
     ms, rows = time_rows(row_sets, args.steps, args.warmup)
+    del row_sets
+    torch.cuda.empty_cache()
     work = row_work(w)
     per_row = {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
     dominant = max(rows, key=lambda n: rows[n])
     digest = source_digest()
     roof = dict(roofline_of(dominant, work[dominant], rows[dominant]))
     roof["kernel"] = dominant
+    roof["launches_per_call"] = ROW_LAUNCHES.get(dominant)
     roof["traffic"] = traffic_for(dominant, digest)
     step_bytes = sum(r["bytes"] for r in work.values())
     line = {
@@ -335,7 +437,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 recurrence, bf16 MFMA projection (fp32 accumulate)",
+        "dtype": "f32",
+        "dtype_note": "recurrences in fp32; projection GEMMs take bf16 operands on MFMA with "
+                      "fp32 accumulation",
         "data": "synthetic (seeded Gaussian/uniform draws of the workload's shapes)",
         "config": {"workload": w.name, "L": w.L, "B": w.B, "d": w.d,
                    "bidirectional": w.ndir == 2, "alpha": w.alpha,
@@ -356,8 +460,8 @@ def main():
         line["copy_probe_bytes"] = n * 4
     if not args.no_extras:
         print("[bench] other workloads", file=sys.stderr, flush=True)
-        line["other_workloads"] = extras(max(10, args.steps // 2))
-    if not args.no_cpu_baseline:
+        line["other_workloads"] = extras(args.workload, max(10, args.steps // 2))
+    if not args.no_cpu_baseline and w.mode == "layer":
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
