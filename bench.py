@@ -34,7 +34,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
 METRIC = "SRU fwd+bwd recurrence GB/s and L·B·d steps/s; % HBM peak; GEMM % MFMA"
-KERNEL_SOURCES = ["gemm.hip", "recurrence.hip", "linear_scan.hip", "device_common.h"]
+KERNEL_SOURCES = ["gemm.hip", "recurrence.hip", "backward_scan.hip", "linear_scan.hip",
+                  "device_common.h", "scan_common.h"]
 
 
 def parse():
@@ -308,11 +309,11 @@ def cpu_baseline(w, budget_s=10.0):
 ROW_LAUNCHES = {
     "a1_projection": ["gemm_bf16_mfma (A fp32 X, rounded to bf16 while staged)"],
     "a2_forward": ["fwd_fast (both directions in one grid)"],
-    "a3_a4_backward": ["bwd_fast (direction 1)", "bwd_fast (direction 0, accumulates dx)",
-                       "param_reduce (dv, db)"],
+    "a3_a4_backward": ["scan_clear", "bwd_scan (direction 1)", "scan_clear",
+                       "bwd_scan (direction 0, accumulates dx)", "param_reduce (dv, db)"],
     "a5_projection_bwd_data": ["transpose16 (W -> W^T)", "gemm_bf16_mfma (A = bf16 dU copy)"],
-    "a6_linear_forward": ["lin_clear", "lin_fwd_fused"],
-    "a7_linear_backward": ["lin_clear", "lin_bwd_fused", "lin_db_reduce"],
+    "a6_linear_forward": ["scan_clear", "lin_fwd_fused"],
+    "a7_linear_backward": ["scan_clear", "lin_bwd_fused", "lin_db_reduce"],
 }
 
 # kernels of each training-step row (rocprofv3 kernel names), and the one
@@ -320,7 +321,8 @@ ROW_LAUNCHES = {
 ROW_KERNELS = {
     "a1_projection": ([r"gemm_bf16_mfma<.*>, float, "], r"gemm_bf16_mfma<.*>, float, "),
     "a2_forward": ([r"fwd_fast<"], r"fwd_fast<"),
-    "a3_a4_backward": ([r"bwd_fast<", r"param_reduce"], r"param_reduce"),
+    "a3_a4_backward": ([r"bwd_scan<", r"bwd_fast<", r"scan_clear", r"param_reduce"],
+                       r"param_reduce"),
     "a5_projection_bwd_data": ([r"transpose16", r"gemm_bf16_mfma<.*>, unsigned short, "],
                                r"transpose16"),
 }

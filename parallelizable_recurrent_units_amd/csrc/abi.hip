@@ -111,9 +111,11 @@ sru_status launched(hipError_t e, const char *what)
 
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// The chunked-scan layout bounds the one-lane-per-chain layout
+// ([ndir, B, 4, d] partials) of the generic kernels.
 size_t backward_ws(const sru_shape *s, const Dims &dm)
 {
-    return round256((size_t)dm.ndir * (size_t)s->B * 4 * (size_t)s->d * sizeof(float));
+    return round256(sru::backward_scan_workspace_bytes(s->L, s->B, s->d, dm.ndir));
 }
 
 }  // namespace
@@ -306,6 +308,8 @@ sru_status sru_backward(const sru_shape *shape, const void *U, sru_dtype u_dt, c
     a.dc0 = dc0;
     a.partials = (float *)workspace;
     hipStream_t s = (hipStream_t)stream;
+    if (sru::backward_scan_ok(a.L, a.B, a.d, a.ndir, !a.u_bf16 && !a.x_bf16))
+        return launched(sru::launch_backward_scan(a, workspace, dv, db, s), "backward scan");
     // The highway gradient of x sums both directions: the last direction
     // writes dx, the ones before it add to it (stream order serialises them).
     for (int dir = dm.ndir - 1; dir >= 0; --dir) {

@@ -36,6 +36,13 @@ hipError_t launch_forward(const RecArgs &a, hipStream_t s);
 // One direction per call (a.dir); writes dU, dx (overwrite or accumulate),
 // dc0 and the per-chain parameter-gradient partials.
 hipError_t launch_backward_dir(const RecArgs &a, hipStream_t s);
+// The backward as a chunked scan of the adjoint (d % 64 == 0, sizes within
+// 32-bit segment offsets; with fp32 U and x only for longer sequences): both
+// directions, dv/db included.  ws holds
+// backward_scan_workspace_bytes(L, B, d, ndir) bytes.
+bool backward_scan_ok(int64_t L, int64_t B, int64_t d, int ndir, bool fp32_inputs);
+size_t backward_scan_workspace_bytes(int64_t L, int64_t B, int64_t d, int ndir);
+hipError_t launch_backward_scan(const RecArgs &a, void *ws, float *dv, float *db, hipStream_t s);
 // dv, db [ndir, 2, d] = sum over b (increasing) of partials.
 hipError_t launch_param_reduce(const float *partials, int64_t B, int64_t d, int ndir,
                                float *dv, float *db, hipStream_t s);

@@ -24,6 +24,7 @@
 // even though each chain alone is sequential.
 #include "device_common.h"
 #include "internal.h"
+#include "scan_common.h"
 
 namespace sru {
 namespace {
@@ -250,95 +251,9 @@ __global__ __launch_bounds__(256) void lin_db_reduce(LinGeom g, const float *__r
 //      publishes its own outgoing state, and hands every segment its
 //      incoming state via LDS;
 //   3. each lane replays its steps from that state and writes h and c.
-// A published state is one 64-bit word per (chunk, chain): the float's bits
-// in the low half and a ready mark in the high half, written and read with
-// single relaxed device-scope atomics.  Value and mark travel together, so
-// no fence (and none of the L2 write-back / invalidate a device-scope fence
-// costs) is needed.  Chunks take dynamic tickets in chain-major order
-// (ticket = chunk * tiles + tile), so a chunk only ever waits for a chunk
-// that started before it: progress is guaranteed.  The wait is bounded; if
-// the bound is ever hit the kernel stops waiting and raises the error word
-// of the workspace.
+// Chunks exchange states through the look-back of scan_common.h; tickets
+// are handed out chain-major (ticket = chunk * tiles + tile).
 // ---------------------------------------------------------------------------
-struct Lookback {
-    uint64_t *carry;     // [nC, chains]  published outgoing state of each chunk
-    uint32_t *ticket;    // dynamic chunk ticket
-    uint32_t *err;       // set if a wait ran out
-};
-
-constexpr uint32_t kSpinLimit = 1u << 22;
-constexpr uint64_t kReady = uint64_t(1) << 32;
-
-__device__ __forceinline__ void publish(Lookback lb, int64_t idx, float v)
-{
-    __hip_atomic_store(lb.carry + idx, kReady | __float_as_uint(v), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float consume(Lookback lb, int64_t idx, int lane)
-{
-    uint64_t w = __hip_atomic_load(lb.carry + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t spins = 0;
-    while (!__all((w & kReady) != 0)) {
-        if (++spins > kSpinLimit) {
-            if (lane == 0)
-                __hip_atomic_store(lb.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-        w = __hip_atomic_load(lb.carry + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    return __uint_as_float((uint32_t)w);
-}
-
-__device__ __forceinline__ int64_t take_ticket(Lookback lb, uint32_t *s_ticket)
-{
-    if (threadIdx.x == 0) *s_ticket = atomicAdd(lb.ticket, 1u);
-    __syncthreads();
-    // the same value in every lane: keep it (and every index derived from
-    // it) in scalar registers
-    return (int64_t)__builtin_amdgcn_readfirstlane(*s_ticket);
-}
-
-// Rows of one wave's segment.  Step i of the segment (i = 0..SEG-1, in the
-// direction's own order) lives at time t0 + row(i); steps past the end of
-// the sequence are clamped onto the segment's last valid step, so every
-// load stays in bounds.  t0 is the segment's lowest time index, so every
-// row offset is a small non-negative number: with one uniform 64-bit base
-// per stream, an access costs a 32-bit offset instead of 64-bit address
-// arithmetic per step.
-struct SegRows {
-    int64_t t0;   // lowest time index the segment touches
-    int nv1;      // index of the segment's last valid step (-1: none)
-    bool rev;     // reverse direction: time decreases along the segment
-
-    __device__ SegRows(const LinGeom &g, int64_t s_lo, int seg)
-    {
-        const int64_t left = g.L - 1 - s_lo;
-        nv1 = (int)(left < 0 ? -1 : (left < seg - 1 ? left : seg - 1));
-        rev = g.dl != 0;
-        t0 = rev ? g.L - 1 - (s_lo + (nv1 < 0 ? 0 : nv1)) : s_lo;
-    }
-    __device__ __forceinline__ uint32_t row(int i) const
-    {
-        const int r = i < nv1 ? i : nv1;
-        return (uint32_t)(rev ? nv1 - r : r);
-    }
-};
-
-template <typename T> __device__ __forceinline__ float ld_off(const char *base, uint32_t off)
-{
-    return load_as_f32((const T *)(base + off));
-}
-__device__ __forceinline__ void st_off(char *base, uint32_t off, float v)
-{
-    *(float *)(base + off) = v;
-}
-__device__ __forceinline__ float ldf_off(const char *base, uint32_t off)
-{
-    return *(const float *)(base + off);
-}
-
 template <typename TU, typename TX, int W, int SEG, int PB, int WPE>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(WPE))) void lin_fwd_fused(
     LinGeom g, const TU *__restrict__ U, const TX *__restrict__ X, const float *__restrict__ bias,
@@ -358,7 +273,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(WPE))) v
     const float bfs = bias[(g.dl * 2 + 0) * g.d + j] * kNegLog2e;
     const float brs = bias[(g.dl * 2 + 1) * g.d + j] * kNegLog2e;
     const int64_t s_lo = k * g.chunk + wv * SEG;
-    const SegRows sr(g, s_lo, SEG);
+    const SegRows sr(g.L, g.dl != 0, s_lo, SEG);
     // uniform bases at row t0; per-lane part: lane * element size
     const int64_t ustride = g.B * g.ndir * 3 * g.d, xstride = g.B * g.d;
     const int64_t ostride = g.B * g.ndir * g.d;
@@ -476,7 +391,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(WPE))) v
     const float bfs = bias[(g.dl * 2 + 0) * g.d + j] * kNegLog2e;
     const float brs = bias[(g.dl * 2 + 1) * g.d + j] * kNegLog2e;
     const int64_t s_lo = k * g.chunk + wv * SEG;
-    const SegRows sr(g, s_lo, SEG);
+    const SegRows sr(g.L, g.dl != 0, s_lo, SEG);
     const int64_t ustride = g.B * g.ndir * 3 * g.d, xstride = g.B * g.d;
     const int64_t hstride = g.B * g.ndir * g.d;
     const int64_t uoff = (bb * g.ndir + g.dl) * 3 * g.d + j0, xoff = bb * g.d + j0;
@@ -606,13 +521,6 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(WPE))) v
     }
 }
 
-// Clears the look-back flags, ticket and error word before a fused launch
-// (a plain kernel, so the sequence can also be captured in a graph).
-__global__ __launch_bounds__(256) void lin_clear(uint32_t *p, int64_t n)
-{
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0u;
-}
 
 constexpr int kFusedChunk = 256;
 #ifndef SRU_LIN_FWD_W
@@ -687,7 +595,7 @@ hipError_t lin_forward_fused(const LinArgs &a, hipStream_t s)
     const FusedWs f = fused_ws(a, false);
     for (int dl = 0; dl < a.ndir; ++dl) {
         LinGeom g{a.L, a.B, a.d, a.chunk, nC, chains, a.ndir, dl};
-        hipLaunchKernelGGL(lin_clear, dim3(blocks_for(f.clear_words)), dim3(256), 0, s, f.clear,
+        hipLaunchKernelGGL(scan_clear, dim3(blocks_for(f.clear_words)), dim3(256), 0, s, f.clear,
                            f.clear_words);
         hipLaunchKernelGGL((lin_fwd_fused<TU, TX, kFwdW, kFwdSeg, kFwdPB, kFwdWpe>), dim3((unsigned)(nC * (chains / 64))),
                            dim3(kFwdW * 64), 0, s, g, (const TU *)a.U, (const TX *)a.x, a.b, a.alpha,
@@ -704,7 +612,7 @@ hipError_t lin_backward_fused(const LinArgs &a, hipStream_t s)
     const FusedWs f = fused_ws(a, true);
     for (int dl = a.ndir - 1; dl >= 0; --dl) {
         LinGeom g{a.L, a.B, a.d, a.chunk, nC, chains, a.ndir, dl};
-        hipLaunchKernelGGL(lin_clear, dim3(blocks_for(f.clear_words)), dim3(256), 0, s, f.clear,
+        hipLaunchKernelGGL(scan_clear, dim3(blocks_for(f.clear_words)), dim3(256), 0, s, f.clear,
                            f.clear_words);
         hipLaunchKernelGGL((lin_bwd_fused<TU, TX, kBwdW, kBwdSeg, kBwdPB, kBwdWpe>), dim3((unsigned)(nC * (chains / 64))),
                            dim3(kBwdW * 64), 0, s, g, (const TU *)a.U, (const TX *)a.x, a.b, a.alpha,

@@ -51,7 +51,9 @@ def round256(n):
 def test_workspace_sizes(lib, L, B, d, bi):
     s = sru.SruShape(L, B, d, bi, 1.0)
     nd = 2 if bi else 1
-    assert sru.sru_workspace_size(s, sru.SRU_WS_BACKWARD) == round256(nd * B * 4 * d * 4)
+    nC64 = -(-L // 64)    # chunk count of the shortest backward chunk
+    assert sru.sru_workspace_size(s, sru.SRU_WS_BACKWARD) == round256(
+        (2 * nC64 * B * d + 64 + nd * nC64 * B * 4 * d) * 4)
     for chunk in (1, 7, 256):
         nC = -(-L // chunk)
         assert sru.sru_workspace_size(s, sru.SRU_WS_LINEAR_FWD, chunk) == round256((3 * nC * B * d + 64) * 4)

@@ -77,6 +77,11 @@ CASES_F32 = [
     (100, 2, 64, 1),
     (300, 1, 128, 2),
     (131, 2, 64, 1),
+    # the chunked backward scan (fp32 from 129 steps): chunks of 64 with a
+    # ragged last chunk, many chunks, both directions
+    (129, 2, 64, 2),
+    (640, 1, 64, 1),
+    (1000, 2, 128, 2),
 ]
 
 
@@ -99,7 +104,8 @@ def test_recurrence_fp32_given_u(L, B, d, nd):
 
 @pytest.mark.parametrize("L,B,d,nd,xdt", [(37, 2, 128, 1, "bf16"), (8, 3, 64, 2, "bf16"),
                                           (9, 2, 70, 1, "bf16"), (12, 2, 64, 1, "f32"),
-                                          (257, 1, 64, 2, "bf16")])
+                                          (257, 1, 64, 2, "bf16"), (65, 1, 64, 1, "bf16"),
+                                          (130, 2, 128, 2, "f32")])
 def test_recurrence_bf16_u(L, B, d, nd, xdt):
     """bf16 U (and x): the fast two-steps-per-packet path and the generic one."""
     w = workloads.custom(L, B, d, ndir=nd, alpha=1.3, mode="given_u", u_dtype="bf16",
@@ -132,7 +138,8 @@ def test_forward_without_state_outputs():
     check("h", host(h), fo["h"], TIGHT)
 
 
-@pytest.mark.parametrize("L,B,d,nd", [(33, 2, 64, 1), (17, 3, 128, 2), (5, 3, 7, 2)])
+@pytest.mark.parametrize("L,B,d,nd", [(33, 2, 64, 1), (17, 3, 128, 2), (5, 3, 7, 2),
+                                      (200, 2, 64, 2), (150, 1, 128, 1)])
 def test_backward_bf16_copy_of_dU(L, B, d, nd):
     """The optional bf16 dU equals dU rounded to nearest even, bit for bit."""
     import torch
@@ -152,8 +159,9 @@ def test_backward_bf16_copy_of_dU(L, B, d, nd):
         assert torch.equal(a, b)
 
 
-def test_backward_is_deterministic():
-    w = workloads.custom(50, 8, 128, ndir=2, alpha=1.0, mode="given_u")
+@pytest.mark.parametrize("L", [50, 300])
+def test_backward_is_deterministic(L):
+    w = workloads.custom(L, 8, 128, ndir=2, alpha=1.0, mode="given_u")
     inp = workloads.make_inputs(w, seed=6)
     t = dev_inputs(inp)
     shape = SruShape(w.L, w.B, w.d, True, 1.0)
