@@ -307,10 +307,11 @@ def cpu_baseline(w, budget_s=10.0):
 
 # kernel launches of one call of each row (what its event-timed span covers)
 ROW_LAUNCHES = {
-    "a1_projection": ["gemm_bf16_mfma (A fp32 X, rounded to bf16 while staged)"],
+    "a1_projection": ["gemm_bf16_mfma (A = fp32 X, rounded to bf16 while staged)"],
     "a2_forward": ["fwd_fast (both directions in one grid)"],
-    "a3_a4_backward": ["scan_clear", "bwd_scan (direction 1)", "scan_clear",
-                       "bwd_scan (direction 0, accumulates dx)", "param_reduce (dv, db)"],
+    "a3_a4_backward": ["per direction, last one first (the first adds to dx): bwd_fast "
+                       "(fp32 inputs, up to 128 steps) or scan_clear + bwd_scan",
+                       "param_reduce (dv, db)"],
     "a5_projection_bwd_data": ["transpose16 (W -> W^T)", "gemm_bf16_mfma (A = bf16 dU copy)"],
     "a6_linear_forward": ["scan_clear", "lin_fwd_fused"],
     "a7_linear_backward": ["scan_clear", "lin_bwd_fused", "lin_db_reduce"],

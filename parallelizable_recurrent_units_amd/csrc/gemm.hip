@@ -10,15 +10,13 @@
 // product when W has been transposed once by sru_transpose_weight) or as
 // [K, N] (C = A B, transposed while it is staged into LDS).
 //
-// Block tiles: 4 waves in a 2 x 2 grid, each wave a (BM/2) x (BN/2) tile of
-// 32 x 32 MFMA blocks.  LDS bytes read per MFMA fall as the wave tile grows
-// (1 KB at 64 x 64, 512 B at 128 x 128), so large problems use 256 x 256
-// blocks (one per CU, accumulators in AGPRs) and small ones 128 x 128 blocks
-// (two per CU) to keep every CU busy.
+// Block tiles: a grid of waves, each wave a tile of 32 x 32 MFMA blocks; the
+// k-tile is staged global -> registers -> LDS (double-buffered in LDS) while
+// the previous one is multiplied.  Large problems use 256 x 256 blocks of 8
+// waves (one block per CU, two waves per SIMD), small ones 128 x 128 blocks
+// of 4 waves (two blocks per CU) to keep every CU busy.
 //
 // fp32 path (W in fp32): LDS-tiled FMA kernel, fp32 products and sums.
-#include <stdlib.h>
-
 #include "device_common.h"
 #include "internal.h"
 
@@ -30,25 +28,39 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int NT = 256;   // threads per block: 4 waves
 
-template <int BM_, int BN_, int BK_, int STAGES_, int MINB_>
+#ifndef SRU_GEMM_DB
+#define SRU_GEMM_DB 1
+#endif
+#ifndef SRU_GEMM_HINTS
+#define SRU_GEMM_HINTS 1
+#endif
+
+template <int BM_, int BN_, int BK_, int STAGES_, int MINB_, int WGM_ = 2, int WGN_ = 2,
+          bool DB_ = true>
 struct TileCfg {
+    static constexpr bool DB = DB_ && SRU_GEMM_DB;   // two fragment buffers per wave
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int STAGES = STAGES_;   // register stages of prefetched k-tiles
     static constexpr int MINB = MINB_;       // blocks per CU the registers are sized for
+    static constexpr int WGM = WGM_, WGN = WGN_;   // wave grid of the block
+    static constexpr int NT = 64 * WGM * WGN;      // threads per block
     static constexpr int LDK = BK + 8;       // padded LDS row (bf16): 80 or 144 bytes
                                              // keeps 16-byte reads of 8 rows on distinct banks
-    static constexpr int WM = BM / 2, WN = BN / 2;
+    static constexpr int WM = BM / WGM, WN = BN / WGN;
     static constexpr int TI = WM / 32, TJ = WN / 32;
     static constexpr int EPI_LD = WN + 4;    // fp32 epilogue staging row
     static constexpr int LDS_BYTES = 2 * (BM + BN) * LDK * 2;
-    static_assert(LDS_BYTES >= 4 * 32 * EPI_LD * 4, "epilogue staging must fit in LDS");
+    static_assert(LDS_BYTES >= WGM * WGN * 32 * EPI_LD * 4, "epilogue staging must fit in LDS");
 };
 
+// 128 x 128 blocks of 4 waves (two blocks per CU) for grids too small to
+// fill the chip with larger tiles; 256 x 256 blocks of 8 waves (two waves per
+// SIMD, 128 x 64 each) otherwise.  With 8 waves a k-tile costs each thread
+// only a few staging registers, and the second wave of every SIMD issues its
+// MFMAs while the first waits on LDS or on its loads.
 typedef TileCfg<128, 128, 64, 1, 2> CfgSmall;
-typedef TileCfg<256, 128, 64, 1, 1> CfgMid;
-typedef TileCfg<256, 256, 64, 1, 1> CfgBig;
+typedef TileCfg<256, 256, 64, 1, 1, 2, 4, false> CfgBig8;
 
 // ---- A tile (BM x BK) -> registers -> LDS (bf16) --------------------------
 // FAST (K % BK == 0): every thread's element offsets inside the k-tile window
@@ -60,7 +72,7 @@ template <class Cfg, typename TA, bool FAST>
 struct ALoader {
     static constexpr int V = 16 / sizeof(TA);            // elements per 16 bytes
     static constexpr int PER_ROW = Cfg::BK / V;
-    static constexpr int N = Cfg::BM * PER_ROW / NT;     // 16-byte loads per thread
+    static constexpr int N = Cfg::BM * PER_ROW / Cfg::NT;     // 16-byte loads per thread
     struct Offsets {
         uint32_t v[N];
     };
@@ -72,7 +84,7 @@ struct ALoader {
         if (FAST) {
 #pragma unroll
             for (int i = 0; i < N; ++i) {
-                const int idx = tid + i * NT;
+                const int idx = tid + i * Cfg::NT;
                 int64_t row = idx / PER_ROW;
                 if (m0 + row > M - 1) row = M - 1 - m0;
                 o.v[i] = (uint32_t)((row * K + (idx % PER_ROW) * V) * (int64_t)sizeof(TA));
@@ -90,7 +102,7 @@ struct ALoader {
         }
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int idx = tid + i * NT;
+            const int idx = tid + i * Cfg::NT;
             const int row = idx / PER_ROW, cv = idx % PER_ROW;
             const int64_t m = m0 + row, k = k0 + cv * V;
             u32x4 v = {0u, 0u, 0u, 0u};
@@ -109,7 +121,7 @@ struct ALoader {
     {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int idx = tid + i * NT;
+            const int idx = tid + i * Cfg::NT;
             const int row = idx / PER_ROW, cv = idx % PER_ROW;
             bf16_bits *dst = As + row * Cfg::LDK + cv * V;
             if constexpr (sizeof(TA) == 4) {   // round fp32 -> bf16 (nearest even) here
@@ -138,7 +150,7 @@ struct BLoader;
 template <class Cfg, bool FAST>
 struct BLoader<Cfg, false, FAST> {
     static constexpr int PER_ROW = Cfg::BK / 8;
-    static constexpr int N = Cfg::BN * PER_ROW / NT;
+    static constexpr int N = Cfg::BN * PER_ROW / Cfg::NT;
     struct Offsets {
         uint32_t v[N];
     };
@@ -150,7 +162,7 @@ struct BLoader<Cfg, false, FAST> {
         if (FAST) {
 #pragma unroll
             for (int i = 0; i < N; ++i) {
-                const int idx = tid + i * NT;
+                const int idx = tid + i * Cfg::NT;
                 int64_t row = idx / PER_ROW;
                 if (n0 + row > N_ - 1) row = N_ - 1 - n0;
                 o.v[i] = (uint32_t)((row * K + (idx % PER_ROW) * 8) * 2);
@@ -168,7 +180,7 @@ struct BLoader<Cfg, false, FAST> {
         }
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int idx = tid + i * NT;
+            const int idx = tid + i * Cfg::NT;
             const int row = idx / PER_ROW, cv = idx % PER_ROW;
             const int64_t n = n0 + row, k = k0 + cv * 8;
             u32x4 v = {0u, 0u, 0u, 0u};
@@ -184,7 +196,7 @@ struct BLoader<Cfg, false, FAST> {
     {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int idx = tid + i * NT;
+            const int idx = tid + i * Cfg::NT;
             const int row = idx / PER_ROW, cv = idx % PER_ROW;
             *(u32x4 *)(Bs + row * Cfg::LDK + cv * 8) = reg[i];
         }
@@ -194,7 +206,7 @@ struct BLoader<Cfg, false, FAST> {
 template <class Cfg, bool FAST>
 struct BLoader<Cfg, true, FAST> {
     static constexpr int NP = Cfg::BN / 2;               // column pairs
-    static constexpr int KQ = NT / NP;                   // k-groups
+    static constexpr int KQ = Cfg::NT / NP;                   // k-groups
     static constexpr int KG = Cfg::BK / KQ;              // k-rows per thread
     static_assert(KG % 8 == 0, "whole 16-byte LDS rows");
     struct Offsets {
@@ -271,7 +283,7 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t TM, int64_t TN, int
 
 // C[M, N] (+)= A[M, K] . B  with B given as [N, K] (KN = false) or [K, N].
 template <class Cfg, typename TA, bool KN, bool FAST>
-__global__ __launch_bounds__(NT, Cfg::MINB) void gemm_bf16_mfma(int64_t M, int64_t N, int64_t K,
+__global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(int64_t M, int64_t N, int64_t K,
                                                                const TA *__restrict__ A,
                                                                const bf16_bits *__restrict__ Bm,
                                                                float *__restrict__ C,
@@ -285,7 +297,7 @@ __global__ __launch_bounds__(NT, Cfg::MINB) void gemm_bf16_mfma(int64_t M, int64
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
     const int64_t TM = (M + BM - 1) / BM, TN = (N + BN - 1) / BN;
     int64_t tm, tn;
     tile_of(blockIdx.x, TM, TN, gm, &tm, &tn);
@@ -315,9 +327,10 @@ __global__ __launch_bounds__(NT, Cfg::MINB) void gemm_bf16_mfma(int64_t M, int64
 
     const int r32 = lane & 31;
     const int kg = (lane >> 5) * 8;
-    auto compute = [&](const bf16_bits *As, const bf16_bits *Bs) {
+    // MFMAs of k16 steps [ks0, ks1) of the tile in LDS
+    auto compute_steps = [&](const bf16_bits *As, const bf16_bits *Bs, int ks0, int ks1) {
 #pragma unroll 2   // full unrolling hoists every fragment read and spills
-        for (int ks = 0; ks < BK / 16; ++ks) {
+        for (int ks = ks0; ks < ks1; ++ks) {
             bf16x8 af[TI], bfr[TJ];
 #pragma unroll
             for (int i = 0; i < TI; ++i)
@@ -333,6 +346,52 @@ __global__ __launch_bounds__(NT, Cfg::MINB) void gemm_bf16_mfma(int64_t M, int64
                                                                         0, 0, 0);
         }
     };
+    auto compute = [&](const bf16_bits *As, const bf16_bits *Bs) {
+        compute_steps(As, Bs, 0, BK / 16);
+    };
+    // The whole k-tile with the fragments of step ks + 1 read while the
+    // MFMAs of step ks run (two fragment buffers), and `tail` (the LDS writes
+    // of the next k-tile) issued among the MFMAs of the last step.  The
+    // scheduling hints keep the compiler from bunching the reads: one
+    // fragment read after every few MFMAs.
+    auto compute_db = [&](const bf16_bits *As, const bf16_bits *Bs, auto &&tail) {
+        constexpr int KS = BK / 16;
+        constexpr int NF = TI + TJ;                     // fragment reads per step
+        constexpr int MF = TI * TJ;                     // MFMAs per step
+        bf16x8 af[2][TI], bfr[2][TJ];
+        auto rd = [&](int buf, int ks) {
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+                af[buf][i] = *(const bf16x8 *)(As + (wm * WM + i * 32 + r32) * LDK + ks * 16 + kg);
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+                bfr[buf][j] = *(const bf16x8 *)(Bs + (wn * WN + j * 32 + r32) * LDK + ks * 16 + kg);
+        };
+        rd(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int cur = ks & 1;
+            if (ks + 1 < KS) rd(cur ^ 1, ks + 1);
+            if (ks + 1 == KS) tail();
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+#if SRU_GEMM_HINTS
+            if (ks + 1 < KS) {
+#pragma unroll
+                for (int t = 0; t < NF; ++t) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, MF / NF > 0 ? MF / NF : 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+#endif
+            // no code moves across steps: at most two fragment sets are live
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
 
     // Software pipeline: k-tile kt is in LDS stage kt % 2 while the loads of
     // the next STAGES k-tiles are in flight.  The body has no conditional
@@ -346,27 +405,68 @@ __global__ __launch_bounds__(NT, Cfg::MINB) void gemm_bf16_mfma(int64_t M, int64
     la0.store(As0, tid);
     lb0.store(Bs0, tid);
     if constexpr (Cfg::STAGES == 2) {
+        // Two register stages: the loads of tile kt + 2 are issued before the
+        // MFMAs of tile kt and land during them; tile kt + 1 (loaded one
+        // iteration earlier) is converted and written to the other LDS stage
+        // half way through those MFMAs, so the writes overlap matrix work.
+        // The other stage was last read before the previous barrier.
         la1.load(A, M, K, m0, kc(1), tid);
         lb1.load(Bm, N, K, n0, kc(1), tid);
         __syncthreads();
         for (int64_t kt = 0;; kt += 2) {
             la0.load(A, M, K, m0, kc(kt + 2), tid);
             lb0.load(Bm, N, K, n0, kc(kt + 2), tid);
-            compute(As0, Bs0);
-            la1.store(As1, tid);
-            lb1.store(Bs1, tid);
+            if constexpr (Cfg::DB) {
+                compute_db(As0, Bs0, [&] {
+                    la1.store(As1, tid);
+                    lb1.store(Bs1, tid);
+                });
+            } else {
+                compute(As0, Bs0);
+                la1.store(As1, tid);
+                lb1.store(Bs1, tid);
+            }
             __syncthreads();
             if (kt + 1 >= KT) break;
             la1.load(A, M, K, m0, kc(kt + 3), tid);
             lb1.load(Bm, N, K, n0, kc(kt + 3), tid);
-            compute(As1, Bs1);
-            la0.store(As0, tid);
-            lb0.store(Bs0, tid);
+            if constexpr (Cfg::DB) {
+                compute_db(As1, Bs1, [&] {
+                    la0.store(As0, tid);
+                    lb0.store(Bs0, tid);
+                });
+            } else {
+                compute(As1, Bs1);
+                la0.store(As0, tid);
+                lb0.store(Bs0, tid);
+            }
             __syncthreads();
             if (kt + 2 >= KT) break;
         }
     } else {
         __syncthreads();
+        // 256 x 256 wave tiles hold no second fragment set: plain steps there
+        constexpr bool kDB = Cfg::DB && !(TI * TJ >= 16);
+        if constexpr (kDB) {
+        for (int64_t kt = 0;; kt += 2) {
+            la0.load(A, M, K, m0, kc(kt + 1), tid);
+            lb0.load(Bm, N, K, n0, kc(kt + 1), tid);
+            compute_db(As0, Bs0, [&] {
+                la0.store(As1, tid);
+                lb0.store(Bs1, tid);
+            });
+            __syncthreads();
+            if (kt + 1 >= KT) break;
+            la0.load(A, M, K, m0, kc(kt + 2), tid);
+            lb0.load(Bm, N, K, n0, kc(kt + 2), tid);
+            compute_db(As1, Bs1, [&] {
+                la0.store(As0, tid);
+                lb0.store(Bs0, tid);
+            });
+            __syncthreads();
+            if (kt + 2 >= KT) break;
+        }
+        } else {
         for (int64_t kt = 0;; kt += 2) {
             la0.load(A, M, K, m0, kc(kt + 1), tid);
             lb0.load(Bm, N, K, n0, kc(kt + 1), tid);
@@ -382,6 +482,7 @@ __global__ __launch_bounds__(NT, Cfg::MINB) void gemm_bf16_mfma(int64_t M, int64
             lb0.store(Bs0, tid);
             __syncthreads();
             if (kt + 2 >= KT) break;
+        }
         }
     }
 
@@ -545,16 +646,19 @@ hipError_t mfma_launch_cfg(const GemmArgs &g, hipStream_t s)
     const bool fast = (g.K % Cfg::BK == 0) && (g.N % 4 == 0) &&
                       (g.K * Cfg::BM * 4 < (int64_t(1) << 32)) &&
                       (!KN || (g.N % 2 == 0 && g.N * Cfg::BK * 2 < (int64_t(1) << 32)));
-    int gm = 8;
-    if (const char *e = getenv("SRU_GEMM_GM")) gm = atoi(e);   // tuning override
-    if (fast)
-        hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, TA, KN, true>), dim3((unsigned)tiles), dim3(NT), 0,
+    const int gm = 8;   // row tiles per group of the tile order
+    if (fast) {
+        hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, TA, KN, true>), dim3((unsigned)tiles), dim3(Cfg::NT), 0,
                            s, g.M, g.N, g.K, (const TA *)g.A, (const bf16_bits *)g.Bm, g.C,
                            g.accumulate, gm);
-    else
-        hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, TA, KN, false>), dim3((unsigned)tiles), dim3(NT), 0,
-                           s, g.M, g.N, g.K, (const TA *)g.A, (const bf16_bits *)g.Bm, g.C,
+    } else {
+        // bounds-checked loads: one register stage, 128 x 128 tiles
+        const int64_t t1 = ((g.M + CfgSmall::BM - 1) / CfgSmall::BM) *
+                           ((g.N + CfgSmall::BN - 1) / CfgSmall::BN);
+        hipLaunchKernelGGL((gemm_bf16_mfma<CfgSmall, TA, KN, false>), dim3((unsigned)t1), dim3(CfgSmall::NT),
+                           0, s, g.M, g.N, g.K, (const TA *)g.A, (const bf16_bits *)g.Bm, g.C,
                            g.accumulate, gm);
+    }
     return hipGetLastError();
 }
 
@@ -566,13 +670,8 @@ int64_t tiles_of(const GemmArgs &g, int bm, int bn)
 template <typename TA, bool KN>
 hipError_t mfma_launch(const GemmArgs &g, hipStream_t s)
 {
-    // The largest block tile that still gives every CU (256) a tile, so the
-    // wave tiles are as large as the grid allows.
-    int cfg = 0;
-    if (const char *e = getenv("SRU_GEMM_TILE")) cfg = atoi(e);   // tuning override
-    if (cfg == 0) cfg = tiles_of(g, 256, 256) >= 512 ? 3 : 1;
-    if (cfg == 3) return mfma_launch_cfg<CfgBig, TA, KN>(g, s);
-    if (cfg == 2) return mfma_launch_cfg<CfgMid, TA, KN>(g, s);
+    // large tiles once they give every CU (256) at least one
+    if (tiles_of(g, 256, 256) >= 256) return mfma_launch_cfg<CfgBig8, TA, KN>(g, s);
     return mfma_launch_cfg<CfgSmall, TA, KN>(g, s);
 }
 
