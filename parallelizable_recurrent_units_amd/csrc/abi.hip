@@ -310,6 +310,12 @@ sru_status sru_backward(const sru_shape *shape, const void *U, sru_dtype u_dt, c
     hipStream_t s = (hipStream_t)stream;
     if (sru::backward_scan_ok(a.L, a.B, a.d, a.ndir, !a.u_bf16 && !a.x_bf16))
         return launched(sru::launch_backward_scan(a, workspace, dv, db, s), "backward scan");
+    if (sru::backward_bidi_ok(a)) {
+        hipError_t e = sru::launch_backward_bidi(a, s);
+        if (e == hipSuccess && (dv || db))
+            e = sru::launch_param_reduce(a.partials, shape->B, shape->d, dm.ndir, dv, db, s);
+        return launched(e, "backward recurrence");
+    }
     // The highway gradient of x sums both directions: the last direction
     // writes dx, the ones before it add to it (stream order serialises them).
     for (int dir = dm.ndir - 1; dir >= 0; --dir) {

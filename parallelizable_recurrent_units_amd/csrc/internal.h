@@ -36,6 +36,10 @@ hipError_t launch_forward(const RecArgs &a, hipStream_t s);
 // One direction per call (a.dir); writes dU, dx (overwrite or accumulate),
 // dc0 and the per-chain parameter-gradient partials.
 hipError_t launch_backward_dir(const RecArgs &a, hipStream_t s);
+// Both directions in one launch (ndir == 2, short fp32 sequences): writes dU,
+// dx (overwritten), dc0 and the partials.
+bool backward_bidi_ok(const RecArgs &a);
+hipError_t launch_backward_bidi(const RecArgs &a, hipStream_t s);
 // The backward as a chunked scan of the adjoint (d % 64 == 0, sizes within
 // 32-bit segment offsets; with fp32 U and x only for longer sequences): both
 // directions, dv/db included.  ws holds

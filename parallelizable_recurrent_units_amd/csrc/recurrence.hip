@@ -324,16 +324,31 @@ __global__ __launch_bounds__(256) void bwd_generic(RecArgs a)
 // in groups of G with one LDS round trip per group, a branch-free main loop
 // over whole groups and a direct-load tail, as in the forward kernel.
 // ---------------------------------------------------------------------------
-template <int R, int G>
-__global__ __launch_bounds__(kWave) void bwd_fast(RecArgs a)
+//
+// BIDI: both directions of one (batch row, 64 channels) in one workgroup of
+// two waves (wave w walks direction w).  Each wave keeps its highway dx
+// contributions of all L steps in LDS instead of writing them; at the end
+// the workgroup writes dx = (direction 0) + (direction 1) once, so the two
+// directions need no ordering between launches and dx is never re-read.
+// (fp32 addition of two terms is commutative, so the sum equals the one the
+// one-direction-per-launch path produces.)  LDS: 2 * L * 64 floats, passed
+// as dynamic shared memory.
+template <int R, int G, bool BIDI>
+__global__ __launch_bounds__(BIDI ? 2 * kWave : kWave) void bwd_fast(RecArgs a)
 {
     static_assert(R % G == 0, "ring holds whole groups");
-    __shared__ uint4 slot_a[G * kWave];
-    __shared__ uint4 slot_b[G * kWave];
-    __shared__ float out_slot[G * 4 * kWave];
+    constexpr int NW = BIDI ? 2 : 1;
+    __shared__ uint4 slot_a_all[NW][G * kWave];
+    __shared__ uint4 slot_b_all[NW][G * kWave];
+    __shared__ float out_slot_all[NW][G * 4 * kWave];
+    extern __shared__ float dxbuf[];                 // BIDI: [2][L][64]
 
-    const int lane = threadIdx.x;
-    const int dl = a.dir;
+    const int wv = BIDI ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+    const int lane = threadIdx.x & 63;
+    uint4 *slot_a = slot_a_all[wv];
+    uint4 *slot_b = slot_b_all[wv];
+    float *out_slot = out_slot_all[wv];
+    const int dl = BIDI ? wv : a.dir;
     const int64_t gpr = a.d / kWave;
     const int64_t w = blockIdx.x;
     const int64_t bb = w / gpr;
@@ -344,7 +359,8 @@ __global__ __launch_bounds__(kWave) void bwd_fast(RecArgs a)
 
     const int q = lane >> 4;
     const int sub = lane & 15;
-    const bool dxacc = a.dx_accumulate;
+    const bool dxacc = !BIDI && a.dx_accumulate;
+    float *dxw = BIDI ? dxbuf + (int64_t)wv * a.L * kWave : nullptr;   // this wave's dx rows
     const uint32_t u_stride = (uint32_t)(a.B * a.ndir * 3 * a.d * 4);
     const uint32_t x_stride = (uint32_t)(a.B * a.d * 4);
     const uint32_t h_stride = (uint32_t)(a.B * a.ndir * a.d * 4);
@@ -466,7 +482,10 @@ __global__ __launch_bounds__(kWave) void bwd_fast(RecArgs a)
                 for (int i = 0; i < G; ++i) {
                     const float4 val = ((const float4 *)out_slot)[i * 64 + lane];
                     const uint32_t t = t_of(k0 + i);
-                    *(float4 *)(po_ptr + __umul24(t, po_stride)) = val;
+                    if (BIDI && q == 3)   // the dx lanes: into this wave's LDS rows
+                        *(float4 *)(dxw + t * kWave + 4 * sub) = val;
+                    else
+                        *(float4 *)(po_ptr + __umul24(t, po_stride)) = val;
                     if (lp_on) {     // lanes of the three dU rows also write bf16
                         uint2 pk;
                         pk.x = pack_bf16x2(val.x, val.y);
@@ -499,7 +518,10 @@ tail:
             a.dU_lp[ub + a.d] = f32_to_bf16(o1);
             a.dU_lp[ub + 2 * a.d] = f32_to_bf16(o2);
         }
-        a.dx[xi] = dxacc ? o3 + a.dx[xi] : o3;
+        if (BIDI)
+            dxw[t * kWave + lane] = o3;
+        else
+            a.dx[xi] = dxacc ? o3 + a.dx[xi] : o3;
     }
     if (a.dc0) a.dc0[(dl * a.B + bb) * a.d + j] = gc;
     float *pp = a.partials + ((int64_t)(dl * a.B + bb) * 4) * a.d + j;
@@ -507,6 +529,23 @@ tail:
     pp[1 * a.d] = svr;
     pp[2 * a.d] = sbf;
     pp[3 * a.d] = sbr;
+    if constexpr (BIDI) {
+        // dx[t, bb, j0 .. j0 + 63] = direction 0 + direction 1, 16-byte stores
+        __syncthreads();
+        const float *d0 = dxbuf, *d1 = dxbuf + L * kWave;
+        for (int64_t idx = threadIdx.x; idx < L * 16; idx += 2 * kWave) {
+            const int64_t t = idx >> 4;
+            const int c = (int)(idx & 15) * 4;
+            const float4 u = *(const float4 *)(d0 + t * kWave + c);
+            const float4 v = *(const float4 *)(d1 + t * kWave + c);
+            float4 o;
+            o.x = u.x + v.x;
+            o.y = u.y + v.y;
+            o.z = u.z + v.z;
+            o.w = u.w + v.w;
+            *(float4 *)(a.dx + (t * a.B + bb) * a.d + j0 + c) = o;
+        }
+    }
 }
 
 // dv[dl, g, j] = sum_b partials[dl, b, g, j]; db[dl, g, j] likewise with rows
@@ -589,6 +628,10 @@ hipError_t bwd_generic_launch(const RecArgs &a, hipStream_t s)
 #define SRU_BWD_GROUP 4
 #endif
 
+// Longest sequence whose dx rows of both directions (2 * L * 256 bytes) the
+// two-direction backward keeps in LDS.
+constexpr int64_t kBidiMaxL = 64;
+
 // The fast kernels address with 32-bit byte offsets built from 24-bit
 // products: every tensor below 2 GiB and every time stride below 16 MiB.
 static bool fast_sizes_ok(const RecArgs &a)
@@ -620,12 +663,27 @@ hipError_t launch_forward(const RecArgs &a, hipStream_t s)
                     : fwd_generic_launch<float, float>(a, s);
 }
 
+bool backward_bidi_ok(const RecArgs &a)
+{
+    return a.ndir == 2 && a.L <= kBidiMaxL && (a.d % kWave == 0) && !a.u_bf16 && !a.x_bf16 &&
+           fast_sizes_ok(a);
+}
+
+hipError_t launch_backward_bidi(const RecArgs &a, hipStream_t s)
+{
+    const int64_t blocks = a.B * (a.d / kWave);
+    const size_t lds = (size_t)2 * a.L * kWave * sizeof(float);
+    hipLaunchKernelGGL((bwd_fast<SRU_BWD_RING, SRU_BWD_GROUP, true>), dim3((unsigned)blocks),
+                       dim3(2 * kWave), lds, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_backward_dir(const RecArgs &a, hipStream_t s)
 {
     const bool fast = (a.d % kWave == 0) && !a.u_bf16 && !a.x_bf16 && fast_sizes_ok(a);
     if (fast) {
         const int64_t waves = a.B * (a.d / kWave);
-        hipLaunchKernelGGL((bwd_fast<SRU_BWD_RING, SRU_BWD_GROUP>), dim3((unsigned)waves),
+        hipLaunchKernelGGL((bwd_fast<SRU_BWD_RING, SRU_BWD_GROUP, false>), dim3((unsigned)waves),
                            dim3(kWave), 0, s, a);
         return hipGetLastError();
     }
