@@ -532,25 +532,59 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(int64_t M, 
     }
 }
 
-// dst[c][r] = src[r][c] for a rows x cols matrix of 2-byte elements, through
-// padded 64 x 64 LDS tiles (coalesced reads and writes).
+// dst[c][r] = src[r][c] for a rows x cols matrix of 2-byte elements, one
+// 64 x 64 tile per block.  VEC (rows % 8 == 0 and cols % 8 == 0): every
+// global access moves 16 bytes (8 elements of a row in, 8 of a column out)
+// and the tile is turned in LDS; otherwise element by element.  The LDS row
+// of 66 elements (33 dwords) spreads the column gathers over the banks.
+template <bool VEC>
 __global__ __launch_bounds__(256) void transpose16(int64_t rows, int64_t cols,
                                                    const uint16_t *__restrict__ src,
                                                    uint16_t *__restrict__ dst)
 {
     __shared__ uint16_t t[64][66];
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
     const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+    if constexpr (VEC) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int64_t r = r0 + ty * 16 + k, c = c0 + tx;
-        if (r < rows && c < cols) t[ty * 16 + k][tx] = src[r * cols + c];
-    }
-    __syncthreads();
+        for (int h = 0; h < 2; ++h) {
+            const int id = tid + 256 * h, row = id >> 3, cc = (id & 7) * 8;
+            const int64_t r = r0 + row, c = c0 + cc;
+            if (r < rows && c < cols) {   // whole 8-element chunks: cols % 8 == 0
+                const uint4 v = *(const uint4 *)(src + r * cols + c);
+                uint32_t *tp = (uint32_t *)&t[row][cc];
+                tp[0] = v.x;
+                tp[1] = v.y;
+                tp[2] = v.z;
+                tp[3] = v.w;
+            }
+        }
+        __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int64_t c = c0 + ty * 16 + k, r = r0 + tx;
-        if (r < rows && c < cols) dst[c * rows + r] = t[tx][ty * 16 + k];
+        for (int h = 0; h < 2; ++h) {
+            const int id = tid + 256 * h, oc = id >> 3, rr = (id & 7) * 8;
+            const int64_t c = c0 + oc, r = r0 + rr;
+            if (c < cols && r < rows) {   // rows % 8 == 0
+                uint32_t w[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    w[k] = uint32_t(t[rr + 2 * k][oc]) | (uint32_t(t[rr + 2 * k + 1][oc]) << 16);
+                *(uint4 *)(dst + c * rows + r) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    } else {
+        const int tx = tid & 63, ty = tid >> 6;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int64_t r = r0 + ty * 16 + k, c = c0 + tx;
+            if (r < rows && c < cols) t[ty * 16 + k][tx] = src[r * cols + c];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int64_t c = c0 + ty * 16 + k, r = r0 + tx;
+            if (r < rows && c < cols) dst[c * rows + r] = t[tx][ty * 16 + k];
+        }
     }
 }
 
@@ -690,9 +724,12 @@ hipError_t launch_transpose(int64_t rows, int64_t cols, const void *src, void *d
                             hipStream_t s)
 {
     dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
-    if (two_byte)
-        hipLaunchKernelGGL(transpose16, grid, dim3(256), 0, s, rows, cols, (const uint16_t *)src,
-                           (uint16_t *)dst);
+    if (two_byte && rows % 8 == 0 && cols % 8 == 0)
+        hipLaunchKernelGGL((transpose16<true>), grid, dim3(256), 0, s, rows, cols,
+                           (const uint16_t *)src, (uint16_t *)dst);
+    else if (two_byte)
+        hipLaunchKernelGGL((transpose16<false>), grid, dim3(256), 0, s, rows, cols,
+                           (const uint16_t *)src, (uint16_t *)dst);
     else
         hipLaunchKernelGGL(transpose32, grid, dim3(256), 0, s, rows, cols, (const float *)src,
                            (float *)dst);

@@ -174,6 +174,22 @@ def test_backward_is_deterministic(L):
 # ---------------------------------------------------------------------------
 # projection GEMM
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("d,nd,dt", [(64, 1, "bf16"), (100, 2, "bf16"), (512, 2, "bf16"),
+                                     (8, 1, "bf16"), (1000, 1, "bf16"), (36, 2, "bf16"),
+                                     (100, 1, "f32")])
+def test_transpose_weight_exact(d, nd, dt):
+    """W^T bit for bit: 16-byte path (partial tiles included) and element path."""
+    import torch
+    g = torch.Generator().manual_seed(d * 10 + nd)
+    W = torch.randn(nd * 3 * d, d, generator=g)
+    W = (W.to(torch.bfloat16) if dt == "bf16" else W).cuda()
+    shape = SruShape(1, 1, d, nd == 2, 1.0)
+    Wt = layer.transpose_weight(shape, W)
+    ref = W.t().contiguous()
+    view = torch.int16 if dt == "bf16" else torch.int32
+    assert torch.equal(Wt.view(view).cpu(), ref.view(view).cpu())
+
+
 @pytest.mark.parametrize("L,B,d,nd", [(3, 5, 64, 1), (7, 19, 100, 2), (2, 3, 37, 1),
                                       (64, 4, 256, 2), (1, 1, 8, 1)])
 def test_projection_bf16(L, B, d, nd):
