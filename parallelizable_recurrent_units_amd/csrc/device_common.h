@@ -63,4 +63,16 @@ __device__ __forceinline__ Gate gate_scaled(float y)
 
 __device__ __forceinline__ Gate gate(float z) { return gate_scaled(z * kNegLog2e); }
 
+// The gate's blend g p + (1 - g) q for y = -z log2(e), evaluated as
+// g (p + e q) with e = 2^y and g = 1 / (1 + e): the complement is carried by
+// e (never 1 - g), and the fma runs beside 1 + e and the reciprocal, so a
+// recurrence through p waits on exp, add, rcp and one multiply.  The cap on
+// y is that of gate_scaled; e q stays finite for |q| < 2^64.
+__device__ __forceinline__ float gate_blend(float y, float p, float q)
+{
+    const float e = __builtin_amdgcn_exp2f(fminf(y, 64.0f));
+    const float g = __builtin_amdgcn_rcpf(1.0f + e);
+    return g * fmaf(e, q, p);
+}
+
 }  // namespace sru

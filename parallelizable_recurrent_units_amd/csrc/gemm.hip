@@ -62,6 +62,7 @@ struct TileCfg {
 typedef TileCfg<128, 128, 64, 1, 2> CfgSmall;
 typedef TileCfg<256, 256, 64, 1, 1, 2, 4, false> CfgBig8;
 
+
 // ---- A tile (BM x BK) -> registers -> LDS (bf16) --------------------------
 // FAST (K % BK == 0): every thread's element offsets inside the k-tile window
 // are loop invariant 32-bit byte offsets (rows past M are clamped to M - 1:

@@ -60,12 +60,11 @@ __global__ __launch_bounds__(256) void fwd_generic(RecArgs a)
         const float uf = load_as_f32(U + ub), ur = load_as_f32(U + ub + a.d);
         const float ux = load_as_f32(U + ub + 2 * a.d);
         const float xv = load_as_f32(X + (t * a.B + bb) * a.d + j);
-        const Gate f = gate(fmaf(vf, c, uf + bf));
-        const Gate r = gate(fmaf(vr, c, ur + br));
-        c = fmaf(f.g, c, f.gc * ux);
-        const float ax = a.alpha * xv;
+        const float yf = fmaf(vf, c, uf + bf) * kNegLog2e;
+        const float yr = fmaf(vr, c, ur + br) * kNegLog2e;
+        c = gate_blend(yf, c, ux);
         const int64_t o = ((t * a.B + bb) * a.ndir + dl) * a.d + j;
-        a.h[o] = fmaf(r.g, c, r.gc * ax);
+        a.h[o] = gate_blend(yr, c, a.alpha * xv);
         if (a.c_seq) a.c_seq[o] = c;
     }
     if (a.c_last) a.c_last[(dl * a.B + bb) * a.d + j] = c;
@@ -156,10 +155,10 @@ __global__ __launch_bounds__(kWave) void fwd_fast(RecArgs a)
     float c = a.c0 ? a.c0[(dl * a.B + bb) * a.d + j] : 0.0f;
 
     auto cell = [&](float uf, float ur, float ux, float xv, float &h) {
-        const Gate f = gate_scaled(fmaf(vfs, c, fmaf(uf, kNegLog2e, bfs)));
-        const Gate r = gate_scaled(fmaf(vrs, c, fmaf(ur, kNegLog2e, brs)));
-        c = fmaf(f.g, c, f.gc * ux);
-        h = fmaf(r.g, c, r.gc * (alpha * xv));
+        const float yf = fmaf(vfs, c, fmaf(uf, kNegLog2e, bfs));
+        const float yr = fmaf(vrs, c, fmaf(ur, kNegLog2e, brs));
+        c = gate_blend(yf, c, ux);                   // f c + (1 - f) U_cand
+        h = gate_blend(yr, c, alpha * xv);           // r c + (1 - r) alpha x
     };
 
     const int64_t groups = L / S;                    // full groups
