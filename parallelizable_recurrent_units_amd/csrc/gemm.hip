@@ -17,6 +17,9 @@
 // of 4 waves (two blocks per CU) to keep every CU busy.
 //
 // fp32 path (W in fp32): LDS-tiled FMA kernel, fp32 products and sums.
+#include <type_traits>
+#include <utility>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -61,6 +64,11 @@ struct TileCfg {
 // MFMAs while the first waits on LDS or on its loads.
 typedef TileCfg<128, 128, 64, 1, 2> CfgSmall;
 typedef TileCfg<256, 256, 64, 1, 1, 2, 4, false> CfgBig8;
+// Four register stages for bf16 A on small grids: with a long K and one
+// block per CU the loads must be requested four k-tiles ahead to cover a
+// round trip to HBM (the operand then comes from HBM, e.g. the bf16 dU the
+// backward has just written).  fp32 A has no registers for that depth.
+typedef TileCfg<128, 128, 64, 4, 2, 2, 2, false> CfgSmallDeep;
 
 
 // ---- A tile (BM x BK) -> registers -> LDS (bf16) --------------------------
@@ -262,6 +270,18 @@ struct BLoader<Cfg, true, FAST> {
     }
 };
 
+// f(integral_constant<0>) ... f(integral_constant<UNR - 1>) in order, until
+// one returns true (then true).
+template <int U, int UNR, class F> __device__ __forceinline__ bool unroll_until(F &&f)
+{
+    if constexpr (U == UNR) {
+        return false;
+    } else {
+        if (f(std::integral_constant<int, U>{})) return true;
+        return unroll_until<U + 1, UNR>(f);
+    }
+}
+
 // Tile order: the hardware hands consecutive workgroups to the 8 XCDs in
 // turn, each XCD with its own L2.  Workgroup `bid` is given logical tile
 // (bid % 8) * (T / 8) + bid / 8, so every XCD works through one contiguous
@@ -401,6 +421,52 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(int64_t M, 
     // exact: a stage waits only for its own loads.
     const int64_t KT = (K + BK - 1) / BK;
     auto kc = [&](int64_t kt) { return (kt < KT ? kt : KT - 1) * BK; };
+    if constexpr (Cfg::STAGES >= 3) {
+        // A ring of NS register stages: tile kt + NS is requested while tile
+        // kt is multiplied, and tile kt + 1 is written to the other LDS stage
+        // during the last MFMAs of tile kt, NS - 1 tiles after its loads were
+        // issued.  Long-K problems with one block per CU need this depth to
+        // cover a round trip to HBM.
+        constexpr int NS = Cfg::STAGES;
+        constexpr int UNR = NS % 2 == 0 ? NS : 2 * NS;   // stage and LDS parity repeat
+        AL la[NS];
+        BL lb[NS];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            la[i].off = &aoff;
+            lb[i].off = &boff;
+        }
+        bf16_bits *Asl[2] = {As0, As1}, *Bsl[2] = {Bs0, Bs1};
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            la[i].load(A, M, K, m0, kc(i), tid);
+            lb[i].load(Bm, N, K, n0, kc(i), tid);
+        }
+        la[0].store(As0, tid);
+        lb[0].store(Bs0, tid);
+        __syncthreads();
+        auto body = [&](int64_t kt, auto u_) -> bool {
+            constexpr int u = decltype(u_)::value;
+            constexpr int rs = u % NS, rn = (u + 1) % NS, ls = u % 2, ln = (u + 1) % 2;
+            la[rs].load(A, M, K, m0, kc(kt + NS), tid);
+            lb[rs].load(Bm, N, K, n0, kc(kt + NS), tid);
+            if constexpr (Cfg::DB) {
+                compute_db(Asl[ls], Bsl[ls], [&] {
+                    la[rn].store(Asl[ln], tid);
+                    lb[rn].store(Bsl[ln], tid);
+                });
+            } else {
+                compute(Asl[ls], Bsl[ls]);
+                la[rn].store(Asl[ln], tid);
+                lb[rn].store(Bsl[ln], tid);
+            }
+            __syncthreads();
+            return kt + 1 >= KT;
+        };
+        for (int64_t kt = 0;; kt += UNR)
+            if (unroll_until<0, UNR>([&](auto u_) { return body(kt + decltype(u_)::value, u_); }))
+                break;
+    } else {
     la0.load(A, M, K, m0, 0, tid);
     lb0.load(Bm, N, K, n0, 0, tid);
     la0.store(As0, tid);
@@ -485,6 +551,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(int64_t M, 
             if (kt + 2 >= KT) break;
         }
         }
+    }
+
     }
 
     // Epilogue, one 32-row band of the wave tile at a time: stage it in LDS
@@ -707,6 +775,7 @@ hipError_t mfma_launch(const GemmArgs &g, hipStream_t s)
 {
     // large tiles once they give every CU (256) at least one
     if (tiles_of(g, 256, 256) >= 256) return mfma_launch_cfg<CfgBig8, TA, KN>(g, s);
+    if constexpr (sizeof(TA) == 2 && !KN) return mfma_launch_cfg<CfgSmallDeep, TA, KN>(g, s);
     return mfma_launch_cfg<CfgSmall, TA, KN>(g, s);
 }
 
