@@ -333,10 +333,10 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(int64_t M, 
     typename BL::Offsets boff;
     AL::init(aoff, M, K, m0, tid);
     BL::init(boff, N, K, n0, tid);
-    AL la0, la1;
-    BL lb0, lb1;
-    la0.off = la1.off = &aoff;
-    lb0.off = lb1.off = &boff;
+    AL la0;
+    BL lb0;
+    la0.off = &aoff;
+    lb0.off = &boff;
 
     f32x16 acc[TI][TJ];
 #pragma unroll
@@ -415,7 +415,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(int64_t M, 
     };
 
     // Software pipeline: k-tile kt is in LDS stage kt % 2 while the loads of
-    // the next STAGES k-tiles are in flight.  The body has no conditional
+    // the next STAGES k-tiles are in flight (one register stage, or a ring of
+    // three or more).  The body has no conditional
     // loads or stores (prefetch indices are clamped to the last k-tile; the
     // surplus loads re-read it), which keeps the compiler's wait counts
     // exact: a stage waits only for its own loads.
@@ -471,46 +472,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(int64_t M, 
     lb0.load(Bm, N, K, n0, 0, tid);
     la0.store(As0, tid);
     lb0.store(Bs0, tid);
-    if constexpr (Cfg::STAGES == 2) {
-        // Two register stages: the loads of tile kt + 2 are issued before the
-        // MFMAs of tile kt and land during them; tile kt + 1 (loaded one
-        // iteration earlier) is converted and written to the other LDS stage
-        // half way through those MFMAs, so the writes overlap matrix work.
-        // The other stage was last read before the previous barrier.
-        la1.load(A, M, K, m0, kc(1), tid);
-        lb1.load(Bm, N, K, n0, kc(1), tid);
-        __syncthreads();
-        for (int64_t kt = 0;; kt += 2) {
-            la0.load(A, M, K, m0, kc(kt + 2), tid);
-            lb0.load(Bm, N, K, n0, kc(kt + 2), tid);
-            if constexpr (Cfg::DB) {
-                compute_db(As0, Bs0, [&] {
-                    la1.store(As1, tid);
-                    lb1.store(Bs1, tid);
-                });
-            } else {
-                compute(As0, Bs0);
-                la1.store(As1, tid);
-                lb1.store(Bs1, tid);
-            }
-            __syncthreads();
-            if (kt + 1 >= KT) break;
-            la1.load(A, M, K, m0, kc(kt + 3), tid);
-            lb1.load(Bm, N, K, n0, kc(kt + 3), tid);
-            if constexpr (Cfg::DB) {
-                compute_db(As1, Bs1, [&] {
-                    la0.store(As0, tid);
-                    lb0.store(Bs0, tid);
-                });
-            } else {
-                compute(As1, Bs1);
-                la0.store(As0, tid);
-                lb0.store(Bs0, tid);
-            }
-            __syncthreads();
-            if (kt + 2 >= KT) break;
-        }
-    } else {
+    static_assert(Cfg::STAGES == 1, "one register stage here; three or more above");
+    {
         __syncthreads();
         // 256 x 256 wave tiles hold no second fragment set: plain steps there
         constexpr bool kDB = Cfg::DB && !(TI * TJ >= 16);
