@@ -244,6 +244,207 @@ tail:
 }
 
 // ---------------------------------------------------------------------------
+// Two-wave forward (d % 64 == 0, same size limits as fwd_fast): a workgroup of
+// two waves per (direction, batch row, 64 channels).  Wave 0 carries the
+// state: it reads the U_f and U_cand rows and computes c (Eqs. 2 and 4),
+// writing c_seq and c_last.  Wave 1 reads the U_r and x rows and computes h
+// (Eqs. 3 and 5) one group of steps behind, taking c[t-1] and c[t] from an
+// LDS ring the state wave fills.  Each wave issues about half the
+// instructions of a step, so grids with fewer waves than SIMDs (long
+// sequences over few chains, where one wave per 64 chains is limited by its
+// own instruction issue) run twice as many waves at half the work each.
+// Per wave, one 16-byte-per-lane load fetches its two streams for SPP steps
+// (fp32 2, bf16 4): lanes 0-31 stream 0, lanes 32-63 stream 1.  Both waves
+// walk the same loop (one barrier per group) and keep their packets in one
+// register ring with the same slot sequence: at iteration g wave r works on
+// group g - r.
+// ---------------------------------------------------------------------------
+template <bool BF16, int R, int G>
+__global__ __launch_bounds__(2 * kWave) void fwd_split(RecArgs a)
+{
+    static_assert(R % G == 0, "ring holds whole groups");
+    constexpr int ESZ = BF16 ? 2 : 4;
+    constexpr int SPP = BF16 ? 4 : 2;                // steps per packet
+    constexpr int S = G * SPP;                       // steps per group
+    constexpr int NRG = R / G;                       // groups in the ring
+    static_assert(S % 4 == 0, "outputs leave four steps per store");
+    constexpr int LPS = 32 / SPP;                    // lanes per (stream, step)
+    constexpr int CPL = 16 / ESZ;                    // channels per lane
+    __shared__ uint4 slot_all[2][G * kWave];
+    __shared__ float ostage_all[2][S * kWave];
+    __shared__ float cring[2][S * kWave];
+
+    const int role = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    uint4 *slot = slot_all[role];
+    float *ostage = ostage_all[role];
+    const int64_t gpr = a.d / kWave;
+    const int64_t w = blockIdx.x;
+    const int dl = (int)(w / (a.B * gpr));
+    const int64_t rem = w % (a.B * gpr);
+    const int64_t bb = rem / gpr;
+    const int64_t j0 = (rem % gpr) * kWave;
+    const int64_t j = j0 + lane;
+    const int64_t L = a.L;
+    auto tix = [&](int64_t s) -> int64_t { return dl ? (L - 1 - s) : s; };
+
+    // ---- input packets: lane = (stream, step in packet, channels) ---------
+    const int q_in = lane >> 5;                      // 0: U_f | U_r, 1: U_cand | x
+    const int e_in = (lane & 31) / LPS;
+    const int sub_in = lane % LPS;
+    const char *in_ptr;
+    uint32_t in_stride;
+    const int64_t ch_off = j0 + (int64_t)CPL * sub_in;
+    if (role == 0 || q_in == 0) {                    // a U row: f / cand or r
+        const int gate = role == 0 ? 2 * q_in : 1;
+        in_ptr = (const char *)a.U + ((bb * a.ndir + dl) * 3 * a.d + gate * a.d + ch_off) * ESZ;
+        in_stride = (uint32_t)(a.B * a.ndir * 3 * a.d * ESZ);
+    } else {                                         // the x row
+        in_ptr = (const char *)a.x + (bb * a.d + ch_off) * ESZ;
+        in_stride = (uint32_t)(a.B * a.d * ESZ);
+    }
+    // packet p holds direction-steps p*SPP .. p*SPP + SPP - 1; this lane's
+    // time index is tin(p) + e_in (direction 0) or tin(p) + SPP-1 - e_in
+    if (dl) in_ptr += (int64_t)(SPP - 1 - e_in) * in_stride;
+    else in_ptr += (int64_t)e_in * in_stride;
+    const int64_t Pmax = L / SPP - 1;                // last packet fully inside
+    auto load_packet = [&](int64_t p) -> uint4 {
+        p = p < 0 ? 0 : (p < Pmax ? p : Pmax);       // clamp: stays in bounds
+        const uint32_t t = (uint32_t)(dl ? (L - SPP - p * SPP) : p * SPP);
+        return *(const uint4 *)(in_ptr + __umul24(t, in_stride));
+    };
+
+    // ---- outputs (c_seq for wave 0, h for wave 1): four steps per store ----
+    const int e_out = lane >> 4;                     // step in the quad
+    const int sub_out = lane & 15;                   // 4 channels
+    float *out_t = role == 0 ? a.c_seq : a.h;
+    const bool out_on = (out_t != nullptr);
+    const uint32_t out_stride = (uint32_t)(a.B * a.ndir * a.d * 4);
+    char *out_ptr = out_on ? (char *)(out_t + (bb * a.ndir + dl) * a.d + j0 + 4 * sub_out)
+                           : nullptr;
+
+    const float vs = a.v[(dl * 2 + role) * a.d + j] * kNegLog2e;   // v_f | v_r
+    const float bs = a.b[(dl * 2 + role) * a.d + j] * kNegLog2e;
+    const float alpha = a.alpha;
+    const float c0 = a.c0 ? a.c0[(dl * a.B + bb) * a.d + j] : 0.0f;
+    float c = c0;                                    // wave 0: the state
+    float cprev = c0;                                // wave 1: c[t-1]
+
+    auto store_outputs = [&](int64_t st0) {          // S staged steps from st0
+        if (!out_on) return;
+#pragma unroll
+        for (int m = 0; m < S / 4; ++m) {
+            const float4 val = *(const float4 *)(ostage + (m * 4 + e_out) * kWave + 4 * sub_out);
+            const uint32_t t = (uint32_t)tix(st0 + m * 4 + e_out);
+            *(float4 *)(out_ptr + __umul24(t, out_stride)) = val;
+        }
+    };
+
+    const int64_t groups = L / S;
+    {
+        uint4 ring[R];
+        // slot sequence: group g - role sits in ring slot (g % NRG)
+#pragma unroll
+        for (int u = 0; u < NRG; ++u)
+#pragma unroll
+            for (int i = 0; i < G; ++i) ring[u * G + i] = load_packet((u - role) * G + i);
+        const float *inf = (const float *)slot;
+        const bf16_bits *inh = (const bf16_bits *)slot;
+        for (int64_t g0 = 0;; g0 += NRG) {
+            bool done = false;
+#pragma unroll
+            for (int u = 0; u < NRG; ++u) {
+                const int64_t g = g0 + u;
+                if (done) break;
+                const int64_t mine = g - role;       // the group this wave works on
+                const bool work = mine >= 0 && mine < groups;
+#pragma unroll
+                for (int i = 0; i < G; ++i) slot[i * kWave + lane] = ring[u * G + i];
+#pragma unroll
+                for (int i = 0; i < G; ++i) ring[u * G + i] = load_packet((mine + NRG) * G + i);
+                if (work) {
+                    float u0[S], u1[S];
+#pragma unroll
+                    for (int st = 0; st < S; ++st) {
+                        const int pk = st / SPP, e = st % SPP;
+                        if (BF16) {
+                            u0[st] = bf16_to_f32(inh[pk * 512 + e * 64 + lane]);
+                            u1[st] = bf16_to_f32(inh[pk * 512 + 256 + e * 64 + lane]);
+                        } else {
+                            u0[st] = inf[pk * 256 + e * 64 + lane];
+                            u1[st] = inf[pk * 256 + 128 + e * 64 + lane];
+                        }
+                    }
+                    float *cr = cring[mine & 1];
+                    if (role == 0) {
+#pragma unroll
+                        for (int st = 0; st < S; ++st) {
+                            c = gate_blend(fmaf(vs, c, fmaf(u0[st], kNegLog2e, bs)), c, u1[st]);
+                            cr[st * kWave + lane] = c;
+                            ostage[st * kWave + lane] = c;
+                        }
+                    } else {
+#pragma unroll
+                        for (int st = 0; st < S; ++st) {
+                            const float ct = cr[st * kWave + lane];
+                            ostage[st * kWave + lane] = gate_blend(
+                                fmaf(vs, cprev, fmaf(u0[st], kNegLog2e, bs)), ct, alpha * u1[st]);
+                            cprev = ct;
+                        }
+                    }
+                    store_outputs(mine * S);
+                }
+                __syncthreads();                     // hand the ring half over
+                done = g >= groups;                  // wave 1 has done the last group
+            }
+            if (done) break;
+        }
+    }
+    // remaining L mod S steps: direct per-lane loads, state wave first
+    const int64_t st_tail = groups * S;
+    float *cr = cring[0];
+    if (role == 0) {
+        for (int64_t st = st_tail; st < L; ++st) {
+            const int64_t t = tix(st);
+            const int64_t ub = ((t * a.B + bb) * a.ndir + dl) * 3 * a.d + j;
+            float uf, ux;
+            if (BF16) {
+                const bf16_bits *U = (const bf16_bits *)a.U;
+                uf = bf16_to_f32(U[ub]);
+                ux = bf16_to_f32(U[ub + 2 * a.d]);
+            } else {
+                const float *U = (const float *)a.U;
+                uf = U[ub];
+                ux = U[ub + 2 * a.d];
+            }
+            c = gate_blend(fmaf(vs, c, fmaf(uf, kNegLog2e, bs)), c, ux);
+            cr[(st - st_tail) * kWave + lane] = c;
+            if (a.c_seq) a.c_seq[((t * a.B + bb) * a.ndir + dl) * a.d + j] = c;
+        }
+        if (a.c_last) a.c_last[(dl * a.B + bb) * a.d + j] = c;
+    }
+    __syncthreads();
+    if (role == 1) {
+        for (int64_t st = st_tail; st < L; ++st) {
+            const int64_t t = tix(st);
+            const int64_t ub = ((t * a.B + bb) * a.ndir + dl) * 3 * a.d + j;
+            float ur, xv;
+            if (BF16) {
+                ur = bf16_to_f32(((const bf16_bits *)a.U)[ub + a.d]);
+                xv = bf16_to_f32(((const bf16_bits *)a.x)[(t * a.B + bb) * a.d + j]);
+            } else {
+                ur = ((const float *)a.U)[ub + a.d];
+                xv = ((const float *)a.x)[(t * a.B + bb) * a.d + j];
+            }
+            const float ct = cr[(st - st_tail) * kWave + lane];
+            a.h[((t * a.B + bb) * a.ndir + dl) * a.d + j] =
+                gate_blend(fmaf(vs, cprev, fmaf(ur, kNegLog2e, bs)), ct, alpha * xv);
+            cprev = ct;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Generic backward (one direction per launch): one thread per chain.
 // ---------------------------------------------------------------------------
 template <typename TU, typename TX>
@@ -620,6 +821,21 @@ hipError_t bwd_generic_launch(const RecArgs &a, hipStream_t s)
 #ifndef SRU_FWD_GROUP_BF16
 #define SRU_FWD_GROUP_BF16 8
 #endif
+#ifndef SRU_FWD_SPLIT
+#define SRU_FWD_SPLIT 1
+#endif
+#ifndef SRU_SPLIT_RING_F32
+#define SRU_SPLIT_RING_F32 8
+#endif
+#ifndef SRU_SPLIT_RING_BF16
+#define SRU_SPLIT_RING_BF16 16
+#endif
+#ifndef SRU_SPLIT_GROUP
+#define SRU_SPLIT_GROUP 4
+#endif
+// below this many 64-channel waves (the SIMD count) the forward splits each
+// block's work over two waves
+constexpr int64_t kSplitBelowWaves = 1024;
 #ifndef SRU_BWD_RING
 #define SRU_BWD_RING 8
 #endif
@@ -646,6 +862,15 @@ hipError_t launch_forward(const RecArgs &a, hipStream_t s)
     const bool fast = (a.d % kWave == 0) && (a.u_bf16 == a.x_bf16) && fast_sizes_ok(a);
     if (fast) {
         const int64_t waves = (int64_t)a.ndir * a.B * (a.d / kWave);
+        if (SRU_FWD_SPLIT && waves < kSplitBelowWaves) {   // fewer waves than SIMDs
+            if (a.u_bf16)
+                hipLaunchKernelGGL((fwd_split<true, SRU_SPLIT_RING_BF16, SRU_SPLIT_GROUP>),
+                                   dim3((unsigned)waves), dim3(2 * kWave), 0, s, a);
+            else
+                hipLaunchKernelGGL((fwd_split<false, SRU_SPLIT_RING_F32, SRU_SPLIT_GROUP>),
+                                   dim3((unsigned)waves), dim3(2 * kWave), 0, s, a);
+            return hipGetLastError();
+        }
         if (a.u_bf16)
             hipLaunchKernelGGL((fwd_fast<true, SRU_FWD_RING_BF16, SRU_FWD_GROUP_BF16>),
                                dim3((unsigned)waves), dim3(kWave), 0, s, a);

@@ -123,6 +123,26 @@ def test_recurrence_bf16_u(L, B, d, nd, xdt):
     check("dv", host(g["dv"]), bo["dv"], TIGHT)
 
 
+@pytest.mark.parametrize("L,B,d,nd,dt", [(9, 64, 1024, 1, "f32"), (21, 32, 1024, 2, "bf16"),
+                                         (3, 64, 1024, 1, "bf16"), (13, 1, 64, 2, "f32"),
+                                         (70, 3, 128, 1, "bf16"), (16, 2, 64, 1, "bf16")])
+def test_forward_both_kernels(L, B, d, nd, dt):
+    """Forward: one wave per 64 channels (1024+ waves) and the two-wave split
+    (fewer), ragged group tails and sequences shorter than a group."""
+    w = workloads.custom(L, B, d, ndir=nd, alpha=0.8, mode="given_u", u_dtype=dt, x_dtype=dt,
+                         c0="normal0.1", backward=False)
+    inp = workloads.make_inputs(w, seed=3000 + L + B, v_scale=0.5, b_scale=0.3)
+    shape = SruShape(L, B, d, nd == 2, w.alpha)
+    print(f"case L={L} B={B} d={d} ndir={nd} {dt}", flush=True)
+    t = dev_inputs(inp)
+    h, c_seq, c_last = layer.forward(shape, t["U"], t["x"], t["v"], t["b"], t["c0"],
+                                     keep_c_seq=True)
+    fo, _ = oracle_fwd_bwd(inp, w.alpha, with_bwd=False)
+    check("h", host(h), fo["h"], TIGHT)
+    check("c_seq", host(c_seq), fo["c"], TIGHT)
+    check("c_last", host(c_last), fo["c_last"], TIGHT)
+
+
 def test_forward_without_state_outputs():
     """c_seq and c_last may be NULL (inference): h is unchanged."""
     import torch
