@@ -383,6 +383,29 @@ def write_traffic(fetch_dir, write_dir, copy_bytes):
     print(json.dumps(rec, indent=1))
 
 
+def copy_ceiling(gib=2, reps=10):
+    """HBM bandwidth of a plain device copy (torch copy_, read + write), the
+    practical ceiling the recurrence rows are compared with (context only;
+    the roofline fractions use the published peak)."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    secs = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"GB/s": 2 * n * 4 / secs / 1e9, "kind": f"torch device copy of {gib} GiB (read + write)"}
+
+
 def traffic_for(kernel_row, digest):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel sources."""
@@ -461,9 +484,18 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         line["copy_probe_bytes"] = n * 4
+    ceil = copy_ceiling()
+    line["copy_ceiling"] = ceil
+    for r in per_row.values():
+        if r["unit"] == "GB/s":
+            r["frac_of_copy_ceiling"] = r["achieved"] / ceil["GB/s"]
     if not args.no_extras:
         print("[bench] other workloads", file=sys.stderr, flush=True)
         line["other_workloads"] = extras(args.workload, max(10, args.steps // 2))
+        for rows_w in line["other_workloads"].values():
+            for r in rows_w.values():
+                if isinstance(r, dict) and r.get("unit") == "GB/s":
+                    r["frac_of_copy_ceiling"] = r["achieved"] / ceil["GB/s"]
     if not args.no_cpu_baseline and w.mode == "layer":
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w)
