@@ -427,8 +427,9 @@ def main():
         write_traffic(*args.write_traffic, copy_bytes=args.copy_probe_mib * (1 << 20))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the hot path is not sharded in this build).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the "
+              "kernels run on one GPU's share of the work and are not sharded (how they "
+              "would shard is described in the design notes).", file=sys.stderr)
         sys.exit(2)
     import torch
     import parallelizable_recurrent_units_amd as sru
