@@ -485,6 +485,15 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         line["copy_probe_bytes"] = n * 4
+    # the metric's two parts: the recurrence (forward + backward rows) in GB/s
+    # and element-steps/s, and the projection GEMMs against their roofline
+    rec_rows = [n for n in per_row if n in ("a2_forward", "a3_a4_backward",
+                                            "a6_linear_forward", "a7_linear_backward")]
+    if rec_rows:
+        rb = sum(work[n]["bytes"] for n in rec_rows)
+        rt = sum(rows[n] for n in rec_rows)
+        line["recurrence_fwd_bwd"] = {"GB/s": rb / rt / 1e9, "frac_of_hbm_peak": rb / rt / 1e9 / HBM_PEAK_GBS,
+                                      "elem_steps_per_s": w.elem_steps / rt, "rows": rec_rows}
     ceil = copy_ceiling()
     line["copy_ceiling"] = ceil
     for r in per_row.values():
