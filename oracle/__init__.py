@@ -54,6 +54,8 @@ def _load():
     lib.sru_oracle_project_bwd_data.argtypes = [_i64, _i64, _i64, _dp, _fp,
                                                 _ip, _i64, _dp]
     d = ctypes.c_double
+    lib.sru_oracle_project_bwd_weight.restype = None
+    lib.sru_oracle_project_bwd_weight.argtypes = [_i64, _i64, _i64, _dp, _fp, ctypes.c_int, _dp]
     lib.sru_oracle_chain_forward.restype = None
     lib.sru_oracle_chain_forward.argtypes = [_i64, ctypes.c_int, d, _dp, _dp, _dp, _dp,
                                              d, d, d, d, d, _dp, _dp, _dp]
@@ -143,6 +145,19 @@ def project_bwd_data(G, W, rows=None) -> np.ndarray:
     out = np.empty((rows.size, K), dtype=np.float64)
     _load().sru_oracle_project_bwd_data(M, N, K, pg, pw, pr, rows.size,
                                         out.ctypes.data_as(_dp))
+    return out
+
+
+def project_bwd_weight(G, X, round_x: bool) -> np.ndarray:
+    """out[n, q] = sum_m G[m, n] Xtilde[m, q] (gradient of Eq. 1 w.r.t. its weights)."""
+    G, pg = _f64(G)
+    X, px = _f32(X)
+    M, N = G.shape
+    M2, K = X.shape
+    assert M == M2
+    out = np.empty((N, K), dtype=np.float64)
+    _load().sru_oracle_project_bwd_weight(M, N, K, pg, px, int(bool(round_x)),
+                                          out.ctypes.data_as(_dp))
     return out
 
 

@@ -18,6 +18,8 @@
  *     h[t] = r[t] * c[t] + (1 - r[t]) * x[t]          (Eq. 5)
  *   Every channel of every sequence is an independent chain once U is known
  *   (the remark after Eq. 5), so the oracle is written per chain.
+ *   The projection's two gradients (input and weights) are the chain rule
+ *   through Eq. 1.
  *
  * Readings taken where the pages are silent (each is listed in the design
  * notes of the repository):
@@ -136,6 +138,34 @@ void sru_oracle_project_bwd_data(int64_t M, int64_t N, int64_t K,
             const float *w = W + n * K;
             for (int64_t q = 0; q < K; ++q)
                 o[q] += g[n] * (double)w[q];
+        }
+    }
+}
+
+/*
+ * Weight-gradient projection: out[n][q] = sum_m G[m][n] * Xt[m][q], with
+ * Xt = bf16(X) when round_x (the operand the forward projection multiplies)
+ * and X otherwise.  G is [M, N] row-major (the gradient of U), X is [M, K],
+ * out is [N, K] (the layout of W).  This is the derivative of Eq. 1's
+ * product with respect to its weights (chain rule); the terms of every
+ * output are added in increasing m.
+ */
+void sru_oracle_project_bwd_weight(int64_t M, int64_t N, int64_t K,
+                                   const double *G, const float *X, int round_x,
+                                   double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        double *o = out + n * K;
+        for (int64_t q = 0; q < K; ++q)
+            o[q] = 0.0;
+        for (int64_t m = 0; m < M; ++m) {
+            const double g = G[m * N + n];
+            const float *x = X + m * K;
+            for (int64_t q = 0; q < K; ++q) {
+                const double xv = round_x ? (double)sru_oracle_round_bf16(x[q]) : (double)x[q];
+                o[q] += g * xv;
+            }
         }
     }
 }

@@ -92,6 +92,42 @@ def test_project_bwd_data_matches_numpy_matmul():
     assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
 
 
+@pytest.mark.parametrize("round_x", [False, True])
+def test_project_bwd_weight_matches_numpy_matmul(round_x):
+    import torch
+    rng = np.random.default_rng(8)
+    M, N, K = 41, 13, 9
+    G = rng.standard_normal((M, N))
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    Xt = torch.from_numpy(X).to(torch.bfloat16).to(torch.float32).numpy() if round_x else X
+    ref = G.T @ Xt.astype(np.float64)
+    got = oracle.project_bwd_weight(G, X, round_x)
+    assert got.shape == (N, K)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_project_bwd_weight_is_the_weight_derivative_of_the_projection():
+    """Independent pin: central differences of sum(U * G) with U = Xt W^T,
+    taken through the forward projection oracle.  U is linear in W and the
+    perturbed weights are exact in float32, so the difference quotient is the
+    derivative up to double rounding."""
+    rng = np.random.default_rng(9)
+    M, N, K = 11, 5, 4
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    W = (np.round(rng.standard_normal((N, K)) * 256) / 256).astype(np.float32)
+    G = rng.standard_normal((M, N))
+    dW = oracle.project_bwd_weight(G, X, True)
+    h = 2.0 ** -6
+    for n in range(N):
+        for q in range(K):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[n, q] += h
+            Wm[n, q] -= h
+            fd = (np.sum(oracle.project(X, Wp, True) * G) -
+                  np.sum(oracle.project(X, Wm, True) * G)) / (2 * h)
+            assert fd == pytest.approx(dW[n, q], rel=1e-11, abs=1e-11)
+
+
 def test_sigmoid_values():
     for z in (-800.0, -30.0, -1.5, 0.0, 0.25, 4.0, 40.0, 800.0):
         ref = 1.0 / (1.0 + math.exp(-z)) if z > -700 else 0.0
