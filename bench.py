@@ -18,7 +18,9 @@ GB/s; per-row times (HIP events recorded on the stream the kernels run on),
 their roofline fractions, the dominant row's roofline object, the CPU oracle
 baseline on a bounded sample, and measurements of the other rows at the other
 workload sizes (given-U bf16 forward, the L=512 training step, the linear-mode
-chunked scan) are included.
+chunked scan) are included.  ``beyond_step`` times, after the step and on its
+buffers, the projection's weight gradient dW = bf16(dU)^T X~, which is not
+part of the step.
 """
 import argparse
 import hashlib
@@ -91,6 +93,19 @@ def row_work(w):
     return rows
 
 
+def next_row_work(w):
+    """Rows timed beside the step, not part of it: the weight gradient of
+    the projection, dW = bf16(dU)^T X~ (dU's bf16 copy and X read once, dW
+    written once)."""
+    if w.mode != "layer":
+        return {}
+    L, B, d, nd = w.L, w.B, w.d, w.ndir
+    LB, n3 = L * B, nd * 3 * d
+    xs = 2 if w.x_dtype == "bf16" else 4
+    return {"f1_projection_bwd_weight": dict(flops=2 * LB * n3 * d,
+                                             bytes=LB * n3 * 2 + LB * d * xs + n3 * d * 4)}
+
+
 def roofline_of(name, work, seconds):
     if "flops" in work:
         t_mfma = work["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
@@ -109,7 +124,8 @@ def roofline_of(name, work, seconds):
 def device_set(w, seed):
     import numpy as np
     import torch
-    from parallelizable_recurrent_units_amd import SRU_WS_BACKWARD, SruShape, sru_workspace_size
+    from parallelizable_recurrent_units_amd import (SRU_WS_BACKWARD, SRU_WS_BWD_WEIGHT, SruShape,
+                                                    sru_workspace_size)
     from parallelizable_recurrent_units_amd.workloads import make_inputs
     inp = make_inputs(w, seed=seed)
     dev = {}
@@ -131,7 +147,10 @@ def device_set(w, seed):
                dc0=torch.empty((nd, B, d), **f32),
                Wt=torch.empty((d, nd * 3 * d), device="cuda", dtype=dev["W"].dtype),
                ws=torch.empty(sru_workspace_size(shape, SRU_WS_BACKWARD), device="cuda",
-                              dtype=torch.uint8))
+                              dtype=torch.uint8),
+               dW=torch.empty((nd * 3 * d, d), **f32))
+    nw = sru_workspace_size(shape, SRU_WS_BWD_WEIGHT)
+    dev["ws_w"] = torch.empty(nw, device="cuda", dtype=torch.uint8) if nw else None
     return shape, dev
 
 
@@ -155,6 +174,15 @@ def training_step_rows(shape, t):
                                                 t["dU_lp"])),
         ("a5_projection_bwd_data", bwd_data),
     ]
+
+
+def next_rows(shape, t):
+    """The rows beyond the step, run on a step's buffers (dU_lp as the step
+    left it)."""
+    from parallelizable_recurrent_units_amd import SRU_BF16, sru_project_bwd_weight
+    return [("f1_projection_bwd_weight",
+             lambda: sru_project_bwd_weight(shape, t["dU_lp"], t["x"], t["dW"], SRU_BF16, False,
+                                            t["ws_w"]))]
 
 
 def time_rows(row_sets, steps, warmup):
@@ -189,6 +217,12 @@ def time_rows(row_sets, steps, warmup):
     return total_ms / steps, per_row
 
 
+class RowSet(list):
+    """One set's step rows [(row, fn)], plus ``beyond``: rows timed after the
+    step on the same buffers."""
+    beyond = ()
+
+
 def row_sets_for(w, nsets, seed0):
     """Rotating sets of the rows of workload ``w`` (each set: list of (row, fn))."""
     import torch
@@ -200,7 +234,8 @@ def row_sets_for(w, nsets, seed0):
         out = []
         for i in range(nsets):
             shape, t = device_set(w, seed0 + i)
-            out.append(training_step_rows(shape, t))
+            out.append(RowSet(training_step_rows(shape, t)))
+            out[-1].beyond = next_rows(shape, t)
         return out
     g = torch.Generator(device="cuda")
     g.manual_seed(seed0)
@@ -250,9 +285,22 @@ def measure(w, nsets, steps, warmup, seed0):
     ms, rows = time_rows(sets, steps, warmup)
     work = row_work(w)
     per_row = {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
+    beyond = time_beyond(w, sets, steps, warmup)
+    if beyond:
+        per_row["beyond_step"] = beyond
     del sets
     torch.cuda.empty_cache()
     return ms, per_row
+
+
+def time_beyond(w, sets, steps, warmup):
+    """{row: measurement} of the rows beyond the step (after the step has run
+    on every set, so their inputs hold a step's results)."""
+    if not sets or not getattr(sets[0], "beyond", ()):
+        return {}
+    _, rows = time_rows([s.beyond for s in sets], steps, warmup)
+    work = next_row_work(w)
+    return {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
 
 
 def extras(main_id, steps):
@@ -315,17 +363,23 @@ ROW_LAUNCHES = {
     "a5_projection_bwd_data": ["transpose16 (W -> W^T)", "gemm_bf16_mfma (A = bf16 dU copy)"],
     "a6_linear_forward": ["scan_clear", "lin_fwd_fused"],
     "a7_linear_backward": ["scan_clear", "lin_bwd_fused", "lin_db_reduce"],
+    "f1_projection_bwd_weight": ["gemm_bf16_mfma (A = bf16 dU copy and B = fp32 X, both read "
+                                 "along L*B; the reduction split over blocks)",
+                                 "split_reduce (partial sums added in split order)"],
 }
 
 # kernels of each training-step row (rocprofv3 kernel names), and the one
 # kernel that runs exactly once per call of the row
 ROW_KERNELS = {
-    "a1_projection": ([r"gemm_bf16_mfma<.*>, float, "], r"gemm_bf16_mfma<.*>, float, "),
+    "a1_projection": ([r"gemm_bf16_mfma<.*>, float, false, "],
+                      r"gemm_bf16_mfma<.*>, float, false, "),
     "a2_forward": ([r"fwd_fast<"], r"fwd_fast<"),
     "a3_a4_backward": ([r"bwd_scan<", r"bwd_fast<", r"scan_clear", r"param_reduce"],
                        r"param_reduce"),
-    "a5_projection_bwd_data": ([r"transpose16", r"gemm_bf16_mfma<.*>, unsigned short, "],
+    "a5_projection_bwd_data": ([r"transpose16", r"gemm_bf16_mfma<.*>, unsigned short, false, "],
                                r"transpose16"),
+    "f1_projection_bwd_weight": ([r"gemm_bf16_mfma<.*>, unsigned short, true, ", r"split_reduce"],
+                                 r"gemm_bf16_mfma<.*>, unsigned short, true, "),
 }
 
 
@@ -442,6 +496,7 @@ def main():
     row_sets = row_sets_for(w, nsets, 100)
     print("[bench] timing", file=sys.stderr, flush=True)
     ms, rows = time_rows(row_sets, args.steps, args.warmup)
+    beyond = time_beyond(w, row_sets, args.steps, args.warmup)
     del row_sets
     torch.cuda.empty_cache()
     work = row_work(w)
@@ -474,6 +529,7 @@ def main():
         "elem_steps_per_s": w.elem_steps / (ms / 1e3),
         "step_algorithmic_bytes": step_bytes,
         "rows": per_row,
+        "beyond_step": beyond,
         "roofline": roof,
         "source_digest": digest,
     }

@@ -78,7 +78,8 @@ typedef enum {
 typedef enum {
     SRU_WS_BACKWARD = 1,    /* sru_backward                      */
     SRU_WS_LINEAR_FWD = 2,  /* sru_linear_scan(SRU_FWD, chunk)   */
-    SRU_WS_LINEAR_BWD = 3   /* sru_linear_scan(SRU_BWD, chunk)   */
+    SRU_WS_LINEAR_BWD = 3,  /* sru_linear_scan(SRU_BWD, chunk)   */
+    SRU_WS_BWD_WEIGHT = 4   /* sru_project_bwd_weight            */
 } sru_ws_op;
 
 typedef struct {
@@ -107,6 +108,29 @@ sru_status sru_project(const sru_shape *shape, sru_proj_op op,
                        const void *W, sru_dtype w_dt,
                        void *C, sru_dtype c_dt,
                        int32_t accumulate, void *stream);
+
+/*
+ * Weight gradient of the projection, Eq. 1 (SRU++ paper, background
+ * section): U = X~ W^T, so dW = dU^T X~, summed over all L*B rows:
+ *   dW[ndir*3d, d] (+)= dU[L*B, ndir*3d]^T . X[L*B, d]
+ *   (row n of dW is the weight row that produced column n of U; the same
+ *    row order as W in sru_project).
+ * dU: du_dt in {F32, BF16} (sru_backward's dU or its dU_lp copy); X: x_dt in
+ *   {F32, BF16}, the projection's input; dW: fp32, must not overlap dU or X.
+ * math_dt = SRU_BF16: bf16 MFMA with fp32 accumulation on operands rounded
+ *   to bf16 (nearest even) as they are loaded; the reduction over L*B may
+ *   be split across blocks, the partial sums then added in a fixed order
+ *   (bit-reproducible run to run).
+ * math_dt = SRU_F32: fp32 arithmetic throughout (bf16 inputs widened).
+ * accumulate = 0 overwrites dW, 1 adds to it.
+ * workspace: sru_workspace_size(shape, SRU_WS_BWD_WEIGHT, 0) bytes of device
+ *   memory, 256-byte aligned (may be NULL when that size is 0); scratch.
+ */
+sru_status sru_project_bwd_weight(const sru_shape *shape,
+                                  const void *dU, sru_dtype du_dt,
+                                  const void *X, sru_dtype x_dt,
+                                  float *dW, sru_dtype math_dt, int32_t accumulate,
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Forward recurrence, Eqs. 2-5, for every (direction, batch, channel) chain.

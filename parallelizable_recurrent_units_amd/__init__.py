@@ -11,6 +11,7 @@ draws seeded synthetic inputs (``workloads``).
 from ._binding import (  # noqa: F401
     EXPORTED, LIB_PATH, SRU_BF16, SRU_BWD, SRU_ERR_INVALID_ARG, SRU_ERR_LAUNCH,
     SRU_ERR_NO_DEVICE, SRU_ERR_UNSUPPORTED, SRU_ERR_WORKSPACE, SRU_F32, SRU_FWD, SRU_OK,
-    SRU_PROJ_BWD_DATA, SRU_PROJ_BWD_DATA_WT, SRU_PROJ_FWD, SRU_WS_BACKWARD, SRU_WS_LINEAR_BWD, SRU_WS_LINEAR_FWD,
+    SRU_PROJ_BWD_DATA, SRU_PROJ_BWD_DATA_WT, SRU_PROJ_FWD, SRU_WS_BACKWARD, SRU_WS_BWD_WEIGHT, SRU_WS_LINEAR_BWD,
+    SRU_WS_LINEAR_FWD,
     SruError, SruShape, load_library, sru_backward, sru_forward, sru_linear_scan, sru_project,
-    sru_transpose_weight, sru_workspace_size)
+    sru_project_bwd_weight, sru_transpose_weight, sru_workspace_size)

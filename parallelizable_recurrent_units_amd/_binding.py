@@ -19,11 +19,12 @@ SRU_ERR_NO_DEVICE, SRU_ERR_LAUNCH, SRU_ERR_WORKSPACE = 3, 4, 5
 SRU_F32, SRU_BF16 = 0, 1
 SRU_FWD, SRU_BWD = 0, 1
 SRU_PROJ_FWD, SRU_PROJ_BWD_DATA, SRU_PROJ_BWD_DATA_WT = 0, 1, 2
-SRU_WS_BACKWARD, SRU_WS_LINEAR_FWD, SRU_WS_LINEAR_BWD = 1, 2, 3
+SRU_WS_BACKWARD, SRU_WS_LINEAR_FWD, SRU_WS_LINEAR_BWD, SRU_WS_BWD_WEIGHT = 1, 2, 3, 4
 
 # Every symbol include/sru.h declares.
-EXPORTED = ("sru_project", "sru_forward", "sru_backward", "sru_linear_scan",
-            "sru_transpose_weight", "sru_workspace_size", "sru_status_string", "sru_last_error")
+EXPORTED = ("sru_project", "sru_project_bwd_weight", "sru_forward", "sru_backward",
+            "sru_linear_scan", "sru_transpose_weight", "sru_workspace_size", "sru_status_string",
+            "sru_last_error")
 
 
 class SruShape(ctypes.Structure):
@@ -66,6 +67,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sru_project.restype = ctypes.c_int
     lib.sru_project.argtypes = [sp, ctypes.c_int, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp,
                                 ctypes.c_int, i32, _vp]
+    lib.sru_project_bwd_weight.restype = ctypes.c_int
+    lib.sru_project_bwd_weight.argtypes = [sp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp,
+                                           ctypes.c_int, i32, _vp, sz, _vp]
     lib.sru_forward.restype = ctypes.c_int
     lib.sru_forward.argtypes = [sp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
                                 ctypes.c_int, _vp, _vp, _vp]
@@ -128,7 +132,7 @@ def _shape(shape) -> SruShape:
 def sru_workspace_size(shape, op: int, chunk: int = 0) -> int:
     s = _shape(shape)
     n = load_library().sru_workspace_size(ctypes.byref(s), int(op), int(chunk))
-    if n == 0:
+    if n == 0 and load_library().sru_last_error():
         raise SruError(SRU_ERR_INVALID_ARG, "SRU_ERR_INVALID_ARG",
                        load_library().sru_last_error().decode())
     return int(n)
@@ -139,6 +143,15 @@ def sru_project(shape, op: int, A, W, C, accumulate: bool = False, stream=None):
     _check(load_library().sru_project(ctypes.byref(s), int(op), _ptr(A), _dtype_code(A),
                                       _ptr(W), _dtype_code(W), _ptr(C), _dtype_code(C),
                                       int(bool(accumulate)), _stream(stream)))
+
+
+def sru_project_bwd_weight(shape, dU, X, dW, math_dtype: int = SRU_BF16, accumulate: bool = False,
+                           workspace=None, stream=None):
+    s = _shape(shape)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().sru_project_bwd_weight(
+        ctypes.byref(s), _ptr(dU), _dtype_code(dU), _ptr(X), _dtype_code(X), _ptr(dW),
+        int(math_dtype), int(bool(accumulate)), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def sru_transpose_weight(shape, W, Wt, stream=None):

@@ -154,6 +154,9 @@ size_t sru_workspace_size(const sru_shape *shape, sru_ws_op op, int32_t chunk)
         ok();
         return round256(sru::linear_workspace_bytes(shape->L, shape->B, shape->d, dm.ndir,
                                                     chunk, op == SRU_WS_LINEAR_BWD));
+    case SRU_WS_BWD_WEIGHT:
+        ok();
+        return round256(sru::wgrad_workspace_bytes(3 * dm.ndir * shape->d, shape->d, dm.LB));
     }
     fail(SRU_ERR_INVALID_ARG, "unknown workspace op %d", (int)op);
     return 0;
@@ -198,6 +201,60 @@ sru_status sru_project(const sru_shape *shape, sru_proj_op op, const void *A, sr
         g.b_kn = op == SRU_PROJ_BWD_DATA;   // the _WT form passes W as [N, K]
     }
     return launched(sru::launch_gemm(g, (hipStream_t)stream), "projection");
+}
+
+sru_status sru_project_bwd_weight(const sru_shape *shape, const void *dU, sru_dtype du_dt,
+                                  const void *X, sru_dtype x_dt, float *dW, sru_dtype math_dt,
+                                  int32_t accumulate, void *workspace, size_t workspace_bytes,
+                                  void *stream)
+{
+    Dims dm;
+    SRU_TRY(check_shape(shape, &dm));
+    if (!valid_dtype(du_dt) || !valid_dtype(x_dt) || !valid_dtype(math_dt))
+        return fail(SRU_ERR_INVALID_ARG, "unknown dtype");
+    if (accumulate != 0 && accumulate != 1)
+        return fail(SRU_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+    SRU_TRY(need_ptr(dU, "dU"));
+    SRU_TRY(need_ptr(X, "X"));
+    SRU_TRY(need_ptr(dW, "dW"));
+    const int64_t n3 = 3 * dm.ndir * shape->d;
+    int64_t wel;
+    if (!mul_ok(n3, shape->d, &wel) || (wel + 255) / 256 > kMaxBlocks)
+        return fail(SRU_ERR_INVALID_ARG, "weight gradient too large for one launch");
+    // fp32 grid: y over column tiles of 64 (<= 65535)
+    if ((shape->d + 63) / 64 > 65535 || (n3 + 63) / 64 > kMaxBlocks)
+        return fail(SRU_ERR_INVALID_ARG, "weight gradient too large for one launch");
+    {   // dW written while dU and X are read
+        const size_t wb = (size_t)wel * 4;
+        const size_t ub = (size_t)dm.u_elems * (du_dt == SRU_BF16 ? 2 : 4);
+        const size_t xb = (size_t)dm.LB * (size_t)shape->d * (x_dt == SRU_BF16 ? 2 : 4);
+        const uintptr_t w = (uintptr_t)dW, u = (uintptr_t)dU, x = (uintptr_t)X;
+        if ((w < u + ub && u < w + wb) || (w < x + xb && x < w + wb))
+            return fail(SRU_ERR_INVALID_ARG, "dW overlaps dU or X");
+    }
+    const bool f32_math = math_dt == SRU_F32;
+    const size_t need =
+        f32_math ? 0 : round256(sru::wgrad_workspace_bytes(n3, shape->d, dm.LB));
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(SRU_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need,
+                        workspace_bytes, workspace ? "" : ", NULL");
+        SRU_TRY(opt_ptr(workspace, "workspace"));
+    }
+    SRU_TRY(need_device());
+    sru::GemmArgs g;
+    g.M = n3;
+    g.N = shape->d;
+    g.K = dm.LB;
+    g.A = dU;
+    g.a_bf16 = du_dt == SRU_BF16;
+    g.Bm = X;
+    g.b_bf16 = x_dt == SRU_BF16;
+    g.b_kn = true;
+    g.C = dW;
+    g.accumulate = accumulate != 0;
+    return launched(sru::launch_gemm_wgrad(g, f32_math, (float *)workspace, (hipStream_t)stream),
+                    "weight gradient");
 }
 
 sru_status sru_transpose_weight(const sru_shape *shape, const void *W, sru_dtype w_dt, void *Wt,

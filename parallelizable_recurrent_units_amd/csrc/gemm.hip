@@ -146,18 +146,9 @@ struct ALoader {
     }
 };
 
-// ---- B tile -> LDS as Bs[n][k] (BN x BK) ----------------------------------
-// KN = false: B is [N, K] (k contiguous), copied row by row.
-// KN = true : B is [K, N] (n contiguous).  Each thread gathers KG k-values of
-//             two adjacent columns with 4-byte loads (a wave reads 256
-//             contiguous bytes of one k-row per load) and writes them as
-//             16-byte LDS rows, so the tile is transposed without 2-byte LDS
-//             stores.
-template <class Cfg, bool KN, bool FAST>
-struct BLoader;
-
+// ---- B tile given as [N, K] (k contiguous) -> LDS as Bs[n][k], row by row --
 template <class Cfg, bool FAST>
-struct BLoader<Cfg, false, FAST> {
+struct BLoaderNK {
     static constexpr int PER_ROW = Cfg::BK / 8;
     static constexpr int N = Cfg::BN * PER_ROW / Cfg::NT;
     struct Offsets {
@@ -212,60 +203,83 @@ struct BLoader<Cfg, false, FAST> {
     }
 };
 
-template <class Cfg, bool FAST>
-struct BLoader<Cfg, true, FAST> {
-    static constexpr int NP = Cfg::BN / 2;               // column pairs
-    static constexpr int KQ = Cfg::NT / NP;                   // k-groups
+// ---- K-major operand -> LDS as S[r][k] (ROWS x BK) ------------------------
+// The operand is stored [K, ld] (its ROWS tile rows contiguous along ld): B
+// given as [K, N], or A given as [K, M].  Each thread gathers KG k-values of
+// two adjacent rows (one 4-byte load of a bf16 pair, or one 8-byte load of an
+// fp32 pair, per k; a wave reads whole contiguous row segments) and writes
+// them as 16-byte LDS rows (fp32 rounded to bf16, nearest even, here), so
+// the tile is transposed without 2-byte LDS stores.
+template <class Cfg, int ROWS, typename T, bool FAST>
+struct KLoader {
+    static constexpr int NP = ROWS / 2;                  // row pairs
+    static constexpr int KQ = Cfg::NT / NP;              // k-groups
     static constexpr int KG = Cfg::BK / KQ;              // k-rows per thread
-    static_assert(KG % 8 == 0, "whole 16-byte LDS rows");
+    static_assert(KG % 8 == 0 && KQ * NP == Cfg::NT, "whole 16-byte LDS rows");
+    typedef typename std::conditional<sizeof(T) == 2, uint32_t, u32x2>::type Reg;
     struct Offsets {
         uint32_t v;                                      // byte offset
     };
-    uint32_t reg[KG];
+    Reg reg[KG];
     const Offsets *off = nullptr;
-    __device__ __forceinline__ static void init(Offsets &o, int64_t N_, int64_t K, int64_t n0,
+    __device__ __forceinline__ static void init(Offsets &o, int64_t ld, int64_t K, int64_t r0,
                                                 int tid)
     {
-        if (FAST) {   // N even: the pair (n, n+1) is one aligned dword
+        if (FAST) {   // ld even: the pair (r, r+1) is one aligned load
             int64_t c = 2 * (tid % NP);
-            if (n0 + c > N_ - 2) c = N_ - 2 - n0;
-            o.v = (uint32_t)(((tid / NP) * KG * N_ + c) * 2);
+            if (r0 + c > ld - 2) c = ld - 2 - r0;        // rows past the end: any valid pair
+            o.v = (uint32_t)(((tid / NP) * KG * ld + c) * (int64_t)sizeof(T));
         }
     }
-    __device__ __forceinline__ void load(const bf16_bits *Bm, int64_t N_, int64_t K, int64_t n0,
+    __device__ __forceinline__ void load(const T *P, int64_t ld, int64_t K, int64_t r0,
                                          int64_t k0, int tid)
     {
         if (FAST) {
 #pragma unroll
             for (int e = 0; e < KG; ++e) {
-                const char *base = (const char *)(Bm + (k0 + e) * N_ + n0);   // uniform
-                reg[e] = *(const uint32_t *)(base + off->v);
+                const char *base = (const char *)(P + (k0 + e) * ld + r0);   // uniform
+                reg[e] = *(const Reg *)(base + off->v);
             }
             return;
         }
         const int np = tid % NP, kq = tid / NP;
-        const int64_t n = n0 + 2 * np;
+        const int64_t r = r0 + 2 * np;
 #pragma unroll
         for (int e = 0; e < KG; ++e) {
             const int64_t k = k0 + kq * KG + e;
-            const uint32_t lo = (k < K && n < N_) ? Bm[k * N_ + n] : 0u;
-            const uint32_t hi = (k < K && n + 1 < N_) ? Bm[k * N_ + n + 1] : 0u;
-            reg[e] = lo | (hi << 16);
+            const T lo = (k < K && r < ld) ? P[k * ld + r] : T(0);
+            const T hi = (k < K && r + 1 < ld) ? P[k * ld + r + 1] : T(0);
+            if constexpr (sizeof(T) == 2) {
+                reg[e] = uint32_t(lo) | (uint32_t(hi) << 16);
+            } else {
+                reg[e].x = __builtin_bit_cast(uint32_t, lo);
+                reg[e].y = __builtin_bit_cast(uint32_t, hi);
+            }
         }
     }
-    __device__ __forceinline__ void store(bf16_bits *Bs, int tid) const
+    __device__ __forceinline__ void store(bf16_bits *S, int tid) const
     {
         const int np = tid % NP, kq = tid / NP;
-        // column n takes the low halves, column n + 1 the high halves
-        auto lo2 = [](uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); };
-        auto hi2 = [](uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); };
+        // row r takes the low halves (first elements), row r + 1 the high ones
 #pragma unroll
         for (int h = 0; h < KG / 8; ++h) {
-            const uint32_t *r = reg + h * 8;
-            const u32x4 lo = {lo2(r[0], r[1]), lo2(r[2], r[3]), lo2(r[4], r[5]), lo2(r[6], r[7])};
-            const u32x4 hi = {hi2(r[0], r[1]), hi2(r[2], r[3]), hi2(r[4], r[5]), hi2(r[6], r[7])};
-            *(u32x4 *)(Bs + (2 * np) * Cfg::LDK + kq * KG + h * 8) = lo;
-            *(u32x4 *)(Bs + (2 * np + 1) * Cfg::LDK + kq * KG + h * 8) = hi;
+            const Reg *g = reg + h * 8;
+            u32x4 lo, hi;
+            if constexpr (sizeof(T) == 2) {
+                auto lo2 = [](uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); };
+                auto hi2 = [](uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); };
+                lo = u32x4{lo2(g[0], g[1]), lo2(g[2], g[3]), lo2(g[4], g[5]), lo2(g[6], g[7])};
+                hi = u32x4{hi2(g[0], g[1]), hi2(g[2], g[3]), hi2(g[4], g[5]), hi2(g[6], g[7])};
+            } else {
+                auto f = [](uint32_t u) { return __uint_as_float(u); };
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    lo[v] = pack_bf16x2(f(g[2 * v].x), f(g[2 * v + 1].x));
+                    hi[v] = pack_bf16x2(f(g[2 * v].y), f(g[2 * v + 1].y));
+                }
+            }
+            *(u32x4 *)(S + (2 * np) * Cfg::LDK + kq * KG + h * 8) = lo;
+            *(u32x4 *)(S + (2 * np + 1) * Cfg::LDK + kq * KG + h * 8) = hi;
         }
     }
 };
@@ -303,12 +317,15 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t TM, int64_t TN, int
 }
 
 // C[M, N] (+)= A[M, K] . B  with B given as [N, K] (KN = false) or [K, N].
-template <class Cfg, typename TA, bool KN, bool FAST>
-__global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(int64_t M, int64_t N, int64_t K,
-                                                               const TA *__restrict__ A,
-                                                               const bf16_bits *__restrict__ Bm,
-                                                               float *__restrict__ C,
-                                                               bool accumulate, int gm)
+// C[M, N] (+)= A . B, where A is given as [M, K] (AKM = false) or [K, M]
+// (AKM = true, i.e. C = A^T B) and B as [N, K] (KN = false, C = A B^T) or
+// [K, N].  With splits > 1 (K-major operands only) block s of a tile covers
+// k in [s * ksplit, (s + 1) * ksplit) and writes its partial product to
+// C + s * M * N, to be summed in order by split_reduce.
+template <class Cfg, typename TA, bool AKM, typename TB, bool KN, bool FAST>
+__global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(
+    int64_t M, int64_t N, int64_t K, const TA *__restrict__ A, const TB *__restrict__ Bm,
+    float *__restrict__ C, bool accumulate, int gm, int64_t ksplit)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, LDK = Cfg::LDK;
     constexpr int WM = Cfg::WM, WN = Cfg::WN, TI = Cfg::TI, TJ = Cfg::TJ;
@@ -320,15 +337,25 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(int64_t M, 
     const int wave = tid >> 6;
     const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
     const int64_t TM = (M + BM - 1) / BM, TN = (N + BN - 1) / BN;
+    const int64_t split = (int64_t)blockIdx.x / (TM * TN);
+    if (split > 0 || ksplit < K) {   // this block's k-range (K-major operands)
+        const int64_t kb = split * ksplit;
+        A += kb * M;
+        Bm += kb * N;
+        K = (K - kb) < ksplit ? (K - kb) : ksplit;
+        C += split * M * N;
+    }
     int64_t tm, tn;
-    tile_of(blockIdx.x, TM, TN, gm, &tm, &tn);
+    tile_of((int64_t)blockIdx.x % (TM * TN), TM, TN, gm, &tm, &tn);
     const int64_t m0 = tm * BM, n0 = tn * BN;
 
     bf16_bits *As0 = smem, *Bs0 = smem + BM * LDK;
     bf16_bits *As1 = smem + STAGE, *Bs1 = smem + STAGE + BM * LDK;
 
-    typedef ALoader<Cfg, TA, FAST> AL;
-    typedef BLoader<Cfg, KN, FAST> BL;
+    typedef typename std::conditional<AKM, KLoader<Cfg, BM, TA, FAST>, ALoader<Cfg, TA, FAST>>::type
+        AL;
+    typedef typename std::conditional<KN, KLoader<Cfg, BN, TB, FAST>, BLoaderNK<Cfg, FAST>>::type BL;
+    static_assert(KN || sizeof(TB) == 2, "B given as [N, K] is bf16");
     typename AL::Offsets aoff;
     typename BL::Offsets boff;
     AL::init(aoff, M, K, m0, tid);
@@ -643,10 +670,11 @@ __global__ __launch_bounds__(256) void transpose32(int64_t rows, int64_t cols,
 // ---- fp32 path ------------------------------------------------------------
 constexpr int FT = 64, FK = 16;
 
-template <typename TA, bool KN>
+// A as [M, K] or, with AKM, [K, M]; B as [N, K] or, with KN, [K, N].
+template <typename TA, bool AKM, typename TB, bool KN>
 __global__ __launch_bounds__(256) void gemm_f32(int64_t M, int64_t N, int64_t K,
                                                 const TA *__restrict__ A,
-                                                const float *__restrict__ Bm,
+                                                const TB *__restrict__ Bm,
                                                 float *__restrict__ C, bool accumulate)
 {
     __shared__ float As[FK][FT + 4];
@@ -659,19 +687,23 @@ __global__ __launch_bounds__(256) void gemm_f32(int64_t M, int64_t N, int64_t K,
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int idx = tid + i * 256;      // 0 .. 1023 = FT x FK
-            {   // A[m][k] -> As[k][m]
+            if (!AKM) {  // A[m][k] -> As[k][m]
                 const int r = idx / FK, kk = idx % FK;
                 const int64_t m = m0 + r, k = k0 + kk;
                 As[kk][r] = (m < M && k < K) ? load_as_f32(A + m * K + k) : 0.0f;
+            } else {     // A[k][m] -> As[k][m]
+                const int kk = idx / FT, r = idx % FT;
+                const int64_t m = m0 + r, k = k0 + kk;
+                As[kk][r] = (m < M && k < K) ? load_as_f32(A + k * M + m) : 0.0f;
             }
             if (!KN) {  // B[n][k] -> Bs[k][n]
                 const int r = idx / FK, kk = idx % FK;
                 const int64_t n = n0 + r, k = k0 + kk;
-                Bs[kk][r] = (n < N && k < K) ? Bm[n * K + k] : 0.0f;
+                Bs[kk][r] = (n < N && k < K) ? load_as_f32(Bm + n * K + k) : 0.0f;
             } else {    // B[k][n] -> Bs[k][n]
                 const int kk = idx / FT, r = idx % FT;
                 const int64_t n = n0 + r, k = k0 + kk;
-                Bs[kk][r] = (n < N && k < K) ? Bm[k * N + n] : 0.0f;
+                Bs[kk][r] = (n < N && k < K) ? load_as_f32(Bm + k * N + n) : 0.0f;
             }
         }
         __syncthreads();
@@ -703,27 +735,36 @@ __global__ __launch_bounds__(256) void gemm_f32(int64_t M, int64_t N, int64_t K,
     }
 }
 
-template <class Cfg, typename TA, bool KN>
-hipError_t mfma_launch_cfg(const GemmArgs &g, hipStream_t s)
+// splits > 1: partial products to ws ([splits, M, N]), k-range per split
+// ksplit (a multiple of the k-tile); otherwise straight into C.
+template <class Cfg, typename TA, bool AKM, typename TB, bool KN>
+hipError_t mfma_launch_cfg(const GemmArgs &g, hipStream_t s, int64_t splits = 1,
+                           int64_t ksplit = 0, float *ws = nullptr)
 {
     const int64_t tiles = ((g.M + Cfg::BM - 1) / Cfg::BM) * ((g.N + Cfg::BN - 1) / Cfg::BN);
     // fast variant: whole k-tiles, 4-aligned C rows, byte offsets inside a
-    // tile window below 2^32, and (for B as [K, N]) dword column pairs
+    // tile window below 2^32, and (for K-major operands) aligned row pairs
     const bool fast = (g.K % Cfg::BK == 0) && (g.N % 4 == 0) &&
-                      (g.K * Cfg::BM * 4 < (int64_t(1) << 32)) &&
-                      (!KN || (g.N % 2 == 0 && g.N * Cfg::BK * 2 < (int64_t(1) << 32)));
+                      (AKM || g.K * Cfg::BM * 4 < (int64_t(1) << 32)) &&
+                      (!AKM || (g.M % 2 == 0 &&
+                                g.M * Cfg::BK * (int64_t)sizeof(TA) < (int64_t(1) << 32))) &&
+                      (!KN || (g.N % 2 == 0 &&
+                               g.N * Cfg::BK * (int64_t)sizeof(TB) < (int64_t(1) << 32)));
     const int gm = 8;   // row tiles per group of the tile order
+    if (splits <= 1) ksplit = g.K;
+    float *C = splits > 1 ? ws : g.C;
+    const bool acc = splits > 1 ? false : g.accumulate;
     if (fast) {
-        hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, TA, KN, true>), dim3((unsigned)tiles), dim3(Cfg::NT), 0,
-                           s, g.M, g.N, g.K, (const TA *)g.A, (const bf16_bits *)g.Bm, g.C,
-                           g.accumulate, gm);
+        hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, TA, AKM, TB, KN, true>),
+                           dim3((unsigned)(tiles * splits)), dim3(Cfg::NT), 0, s, g.M, g.N, g.K,
+                           (const TA *)g.A, (const TB *)g.Bm, C, acc, gm, ksplit);
     } else {
         // bounds-checked loads: one register stage, 128 x 128 tiles
         const int64_t t1 = ((g.M + CfgSmall::BM - 1) / CfgSmall::BM) *
                            ((g.N + CfgSmall::BN - 1) / CfgSmall::BN);
-        hipLaunchKernelGGL((gemm_bf16_mfma<CfgSmall, TA, KN, false>), dim3((unsigned)t1), dim3(CfgSmall::NT),
-                           0, s, g.M, g.N, g.K, (const TA *)g.A, (const bf16_bits *)g.Bm, g.C,
-                           g.accumulate, gm);
+        hipLaunchKernelGGL((gemm_bf16_mfma<CfgSmall, TA, AKM, TB, KN, false>),
+                           dim3((unsigned)(t1 * splits)), dim3(CfgSmall::NT), 0, s, g.M, g.N, g.K,
+                           (const TA *)g.A, (const TB *)g.Bm, C, acc, gm, ksplit);
     }
     return hipGetLastError();
 }
@@ -737,17 +778,78 @@ template <typename TA, bool KN>
 hipError_t mfma_launch(const GemmArgs &g, hipStream_t s)
 {
     // large tiles once they give every CU (256) at least one
-    if (tiles_of(g, 256, 256) >= 256) return mfma_launch_cfg<CfgBig8, TA, KN>(g, s);
-    if constexpr (sizeof(TA) == 2 && !KN) return mfma_launch_cfg<CfgSmallDeep, TA, KN>(g, s);
-    return mfma_launch_cfg<CfgSmall, TA, KN>(g, s);
+    if (tiles_of(g, 256, 256) >= 256)
+        return mfma_launch_cfg<CfgBig8, TA, false, bf16_bits, KN>(g, s);
+    if constexpr (sizeof(TA) == 2 && !KN)
+        return mfma_launch_cfg<CfgSmallDeep, TA, false, bf16_bits, KN>(g, s);
+    return mfma_launch_cfg<CfgSmall, TA, false, bf16_bits, KN>(g, s);
 }
 
-template <typename TA, bool KN>
+// C = P[0] + P[1] + ... + P[splits - 1] (+ C first when accumulating), the
+// partial products added in split order: the result does not depend on
+// scheduling.
+__global__ __launch_bounds__(256) void split_reduce(const float *__restrict__ P, int64_t n,
+                                                    int64_t splits, float *__restrict__ C,
+                                                    bool accumulate)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float sum = P[i];
+    for (int64_t s = 1; s < splits; ++s) sum += P[s * n + i];
+    C[i] = accumulate ? C[i] + sum : sum;
+}
+
+// Split of the reduction over L*B for the weight gradient.  A block of the
+// 128 x 128 configuration takes one of 512 slots (2 per CU); a launch of n
+// blocks runs in ceil(n / 512) rounds, each as long as one block's k-tiles.
+// The partial sums cost a write and a read of M x N floats per split; at
+// the measured rates (one k-tile round ~1.6 us, ~5 TB/s) that is M*N/1e6
+// k-tile rounds per split.  Pick the split count with the least total
+// (ties: fewer splits), at least 8 k-tiles per split.
+constexpr int64_t kWgradSlots = 512, kWgradMinKt = 8, kWgradMaxSplits = 64;
+
+int64_t wgrad_splits(int64_t M, int64_t N, int64_t K)
+{
+    const int64_t tiles = ((M + CfgSmall::BM - 1) / CfgSmall::BM) *
+                          ((N + CfgSmall::BN - 1) / CfgSmall::BN);
+    const int64_t kt = K / CfgSmall::BK;
+    if (K % CfgSmall::BK != 0 || kt < 2 * kWgradMinKt) return 1;
+    const double reduce = (double)M * (double)N * 1e-6;
+    int64_t best = 1;
+    double best_cost = (double)((tiles + kWgradSlots - 1) / kWgradSlots) * (double)kt;
+    for (int64_t sp = 2; sp <= kt / kWgradMinKt && sp <= kWgradMaxSplits; ++sp) {
+        const double rounds = (double)((tiles * sp + kWgradSlots - 1) / kWgradSlots);
+        const double cost = rounds * (double)((kt + sp - 1) / sp) + reduce * (double)sp;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = sp;
+        }
+    }
+    return best;
+}
+
+template <typename TA, typename TB>
+hipError_t wgrad_launch(const GemmArgs &g, float *ws, hipStream_t s)
+{
+    const int64_t sp = wgrad_splits(g.M, g.N, g.K);
+    if (sp <= 1) return mfma_launch_cfg<CfgSmall, TA, true, TB, true>(g, s);
+    const int64_t kt = g.K / CfgSmall::BK;
+    const int64_t ksplit = ((kt + sp - 1) / sp) * CfgSmall::BK;
+    const int64_t used = (g.K + ksplit - 1) / ksplit;      // splits with work
+    hipError_t e = mfma_launch_cfg<CfgSmall, TA, true, TB, true>(g, s, used, ksplit, ws);
+    if (e != hipSuccess) return e;
+    const int64_t n = g.M * g.N;
+    hipLaunchKernelGGL(split_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ws, n,
+                       used, g.C, g.accumulate);
+    return hipGetLastError();
+}
+
+template <typename TA, bool AKM, typename TB, bool KN>
 hipError_t f32_launch(const GemmArgs &g, hipStream_t s)
 {
     dim3 grid((unsigned)((g.M + FT - 1) / FT), (unsigned)((g.N + FT - 1) / FT));
-    hipLaunchKernelGGL((gemm_f32<TA, KN>), grid, dim3(256), 0, s, g.M, g.N, g.K,
-                       (const TA *)g.A, (const float *)g.Bm, g.C, g.accumulate);
+    hipLaunchKernelGGL((gemm_f32<TA, AKM, TB, KN>), grid, dim3(256), 0, s, g.M, g.N, g.K,
+                       (const TA *)g.A, (const TB *)g.Bm, g.C, g.accumulate);
     return hipGetLastError();
 }
 
@@ -769,6 +871,27 @@ hipError_t launch_transpose(int64_t rows, int64_t cols, const void *src, void *d
     return hipGetLastError();
 }
 
+size_t wgrad_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    const int64_t sp = wgrad_splits(M, N, K);
+    return sp <= 1 ? 0 : (size_t)(sp * M * N) * sizeof(float);
+}
+
+hipError_t launch_gemm_wgrad(const GemmArgs &g, bool f32_math, float *ws, hipStream_t s)
+{
+    if (f32_math) {
+        if (g.a_bf16)
+            return g.b_bf16 ? f32_launch<bf16_bits, true, bf16_bits, true>(g, s)
+                            : f32_launch<bf16_bits, true, float, true>(g, s);
+        return g.b_bf16 ? f32_launch<float, true, bf16_bits, true>(g, s)
+                        : f32_launch<float, true, float, true>(g, s);
+    }
+    if (g.a_bf16)
+        return g.b_bf16 ? wgrad_launch<bf16_bits, bf16_bits>(g, ws, s)
+                        : wgrad_launch<bf16_bits, float>(g, ws, s);
+    return g.b_bf16 ? wgrad_launch<float, bf16_bits>(g, ws, s) : wgrad_launch<float, float>(g, ws, s);
+}
+
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s)
 {
     if (g.b_bf16) {
@@ -777,8 +900,10 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t s)
         return g.b_kn ? mfma_launch<float, true>(g, s) : mfma_launch<float, false>(g, s);
     }
     if (g.a_bf16)
-        return g.b_kn ? f32_launch<bf16_bits, true>(g, s) : f32_launch<bf16_bits, false>(g, s);
-    return g.b_kn ? f32_launch<float, true>(g, s) : f32_launch<float, false>(g, s);
+        return g.b_kn ? f32_launch<bf16_bits, false, float, true>(g, s)
+                      : f32_launch<bf16_bits, false, float, false>(g, s);
+    return g.b_kn ? f32_launch<float, false, float, true>(g, s)
+                  : f32_launch<float, false, float, false>(g, s);
 }
 
 }  // namespace sru

@@ -87,6 +87,13 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
+// C[M, N] (+)= A^T B with A given as [K, M] and B as [K, N] (each bf16 or
+// fp32): the weight gradient dW = dU^T Xt.  f32_math: fp32 FMA throughout;
+// otherwise bf16 MFMA on operands rounded to bf16 while staged, with the
+// reduction over K split across blocks when the output alone would not
+// fill the chip (ws then holds the partial products).
+size_t wgrad_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_wgrad(const GemmArgs &g, bool f32_math, float *ws, hipStream_t s);
 // dst[cols, rows] = src[rows, cols]^T (2-byte or 4-byte elements).
 hipError_t launch_transpose(int64_t rows, int64_t cols, const void *src, void *dst, bool two_byte,
                             hipStream_t s);

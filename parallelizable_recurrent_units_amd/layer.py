@@ -43,6 +43,22 @@ def project_bwd_data(shape, dU, W, dX=None, accumulate=False, Wt=None, stream=No
     return dX
 
 
+def project_bwd_weight(shape, dU, X, dW=None, accumulate=False, f32_math=False, ws=None,
+                       stream=None):
+    """dW[ndir*3d, d] (+)= dU^T X (weight gradient through Eq. 1).
+
+    bf16 MFMA on operands rounded to bf16 unless ``f32_math``."""
+    s = B._shape(shape)
+    if dW is None:
+        dW = torch.empty((s.ndir * 3 * s.d, s.d), device=dU.device, dtype=torch.float32)
+    if ws is None and not f32_math:
+        n = B.sru_workspace_size(s, B.SRU_WS_BWD_WEIGHT, 0)
+        ws = torch.empty(n, device=dU.device, dtype=torch.uint8) if n else None
+    B.sru_project_bwd_weight(s, dU, X, dW, B.SRU_F32 if f32_math else B.SRU_BF16, accumulate,
+                             ws, stream)
+    return dW
+
+
 def forward(shape, U, x, v, b, c0=None, keep_c_seq=False, stream=None):
     s = B._shape(shape)
     dev = U.device

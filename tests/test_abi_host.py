@@ -47,7 +47,8 @@ def round256(n):
     return (n + 255) // 256 * 256
 
 
-@pytest.mark.parametrize("L,B,d,bi", [(4, 2, 64, 0), (7, 3, 5, 1), (16384, 4, 4096, 0)])
+@pytest.mark.parametrize("L,B,d,bi", [(4, 2, 64, 0), (7, 3, 5, 1), (16384, 4, 4096, 0),
+                                      (64, 128, 512, 1), (128, 16, 128, 0)])
 def test_workspace_sizes(lib, L, B, d, bi):
     s = sru.SruShape(L, B, d, bi, 1.0)
     nd = 2 if bi else 1
@@ -58,6 +59,19 @@ def test_workspace_sizes(lib, L, B, d, bi):
         nC = -(-L // chunk)
         assert sru.sru_workspace_size(s, sru.SRU_WS_LINEAR_FWD, chunk) == round256((3 * nC * B * d + 64) * 4)
         assert sru.sru_workspace_size(s, sru.SRU_WS_LINEAR_BWD, chunk) == round256((5 * nC * B * d + 64) * 4)
+    # weight gradient: partial products [splits, ndir*3d, d] when the
+    # reduction over L*B is split (128 x 128 output tiles, 64-deep k-tiles,
+    # 512 block slots, >= 8 k-tiles per split, cost in k-tile rounds)
+    M, N, K = 3 * nd * d, d, L * B
+    tiles, kt = -(-M // 128) * -(-N // 128), K // 64
+    sp, best = 1, -(-tiles // 512) * kt
+    if K % 64 == 0 and kt >= 16:
+        for n in range(2, min(kt // 8, 64) + 1):
+            cost = -(-tiles * n // 512) * -(-kt // n) + M * N * 1e-6 * n
+            if cost < best:
+                sp, best = n, cost
+    assert sru.sru_workspace_size(s, sru.SRU_WS_BWD_WEIGHT) == (0 if sp == 1 else
+                                                                round256(sp * M * N * 4))
     assert lib.sru_workspace_size(ctypes.byref(s), sru.SRU_WS_LINEAR_FWD, 0) == 0
     assert b"chunk" in lib.sru_last_error()
     assert lib.sru_workspace_size(ctypes.byref(s), 9, 1) == 0
@@ -138,6 +152,43 @@ def test_workspace_errors(lib):
     assert lin(lib, s, 1, 4, lneed, dh=None) == sru.SRU_ERR_INVALID_ARG
     assert lin(lib, s, 0, 4, lneed, h=None) == sru.SRU_ERR_INVALID_ARG
     assert lin(lib, s, 0, 4, lneed, h_dt=1) == sru.SRU_ERR_UNSUPPORTED
+
+
+# Fake addresses far enough apart for the overlap check of dW.
+Q = [(i + 1) << 32 for i in range(4)]
+
+
+def wgrad(lib, s, ws_bytes, **kw):
+    a = dict(dU=Q[0], du_dt=1, X=Q[1], x_dt=0, dW=Q[2], math=1, acc=0, ws=Q[3])
+    a.update(kw)
+    return lib.sru_project_bwd_weight(ctypes.byref(s), a["dU"], a["du_dt"], a["X"], a["x_dt"],
+                                      a["dW"], a["math"], a["acc"], a["ws"], ws_bytes, None)
+
+
+def test_bwd_weight_validation(lib):
+    s = sru.SruShape(128, 16, 128, 0, 1.0)
+    need = sru.sru_workspace_size(s, sru.SRU_WS_BWD_WEIGHT)
+    assert need > 0
+    assert wgrad(lib, s, need, dU=None) == sru.SRU_ERR_INVALID_ARG
+    assert wgrad(lib, s, need, X=Q[1] + 2) == sru.SRU_ERR_INVALID_ARG
+    assert wgrad(lib, s, need, du_dt=3) == sru.SRU_ERR_INVALID_ARG
+    assert wgrad(lib, s, need, math=2) == sru.SRU_ERR_INVALID_ARG
+    assert wgrad(lib, s, need, acc=2) == sru.SRU_ERR_INVALID_ARG
+    assert wgrad(lib, s, need - 1) == sru.SRU_ERR_WORKSPACE
+    assert wgrad(lib, s, need, ws=None) == sru.SRU_ERR_WORKSPACE
+    assert wgrad(lib, s, need, ws=Q[3] + 8) == sru.SRU_ERR_INVALID_ARG
+    # dW [384, 128] fp32 starting inside dU, or ending inside X
+    assert wgrad(lib, s, need, dW=Q[0] + 1024) == sru.SRU_ERR_INVALID_ARG
+    assert b"overlap" in lib.sru_last_error()
+    assert wgrad(lib, s, need, dW=Q[1] - 4096) == sru.SRU_ERR_INVALID_ARG
+    assert b"overlap" in lib.sru_last_error()
+    # fp32 arithmetic needs no workspace
+    if __import__("torch").cuda.device_count() == 0:
+        assert wgrad(lib, s, 0, math=0, ws=None) == sru.SRU_ERR_NO_DEVICE
+    # no split: no workspace at all
+    s1 = sru.SruShape(3, 5, 64, 0, 1.0)
+    assert sru.sru_workspace_size(s1, sru.SRU_WS_BWD_WEIGHT) == 0
+    assert lib.sru_last_error() == b""
 
 
 def test_binding_raises_sru_error(lib):

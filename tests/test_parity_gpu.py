@@ -12,7 +12,11 @@ output tensor):
     left is the GEMM's fp32 accumulation (K <= 3072 terms, unit roundoff
     2^-24: K u = 1.8e-4 worst case, ~sqrt(K) u = 3e-6 typical);
   * 1e-2 for dX = dU W against the unrounded oracle at the tight stage: the
-    backward-data GEMM rounds dU to bf16 (relative 2^-9 = 2e-3 per element).
+    backward-data GEMM rounds dU to bf16 (relative 2^-9 = 2e-3 per element);
+    the same for the weight gradient dW = dU^T X at the workload sizes.
+  * the weight gradient reduces over K = L*B terms (<= 2048 in the small
+    cases here): 1e-4 against the oracle on the same bf16 operands (K u =
+    1.2e-4 worst case, sqrt(K) u = 3e-6 typical), 1e-5 with fp32 arithmetic.
 Inputs are drawn by the seeded generators in
 parallelizable_recurrent_units_amd/workloads.py; no oracle input or expected
 value comes from the GPU.
@@ -250,6 +254,66 @@ def test_projection_bf16(L, B, d, nd):
     dX2 = torch.from_numpy(C0.copy()).cuda()
     layer.project_bwd_data(shape, torch.from_numpy(G).cuda(), Wd, dX2, accumulate=True, Wt=Wt)
     check("dX (transposed W) vs bf16(dU) oracle", host(dX2).reshape(L * B, d), ref_r, GEMM_ACC)
+
+
+# weight gradient dW = dU^T X: (L, B, d, nd) spanning no split (K = L*B not a
+# multiple of the 64-deep k-tile, or too short), split reductions on the fast
+# path, and a split on the bounds-checked path (d = 37: rows of dW not
+# 4-aligned).
+WGRAD_CASES = [(3, 5, 64, 1), (7, 19, 100, 2), (2, 3, 37, 1), (1, 1, 8, 1), (64, 4, 256, 2),
+               (128, 16, 128, 1), (64, 32, 128, 2), (256, 8, 64, 2), (32, 64, 100, 1),
+               (64, 32, 37, 2), (16, 64, 512, 1)]
+
+
+@pytest.mark.parametrize("L,B,d,nd", WGRAD_CASES)
+def test_projection_bwd_weight(L, B, d, nd):
+    import torch
+    from parallelizable_recurrent_units_amd import SRU_WS_BWD_WEIGHT, sru_workspace_size
+    rng = np.random.default_rng(5000 + 7 * d + L)
+    M = L * B
+    X = rng.standard_normal((L, B, d)).astype(np.float32)
+    G = rng.standard_normal((L, B, nd, 3, d)).astype(np.float32)
+    C0 = rng.standard_normal((nd * 3 * d, d)).astype(np.float32)
+    shape = SruShape(L, B, d, nd == 2, 1.0)
+    print(f"case K={M} M={nd*3*d} N={d} ws={sru_workspace_size(shape, SRU_WS_BWD_WEIGHT)}",
+          flush=True)
+    X2, G2 = X.reshape(M, d), G.reshape(M, -1).astype(np.float64)
+    Gb_bits, Gb = workloads.to_bf16(G)
+    Xb_bits, Xb = workloads.to_bf16(X)
+    Gd, Xd = torch.from_numpy(G).cuda(), torch.from_numpy(X).cuda()
+    Gbd = torch.from_numpy(Gb_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    Xbd = torch.from_numpy(Xb_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    exact = oracle.project_bwd_weight(G2, X2, False)
+    rounded = oracle.project_bwd_weight(Gb.reshape(M, -1), X2, True)
+    # bf16 MFMA, every operand dtype: the kernel multiplies bf16(dU) and bf16(X)
+    for gd, xd, tag in ((Gd, Xd, "f32 dU, f32 X"), (Gbd, Xd, "bf16 dU, f32 X"),
+                        (Gd, Xbd, "f32 dU, bf16 X"), (Gbd, Xbd, "bf16 dU, bf16 X")):
+        dW = layer.project_bwd_weight(shape, gd, xd)
+        check(f"dW ({tag}) vs bf16-operand oracle", host(dW), rounded, GEMM_ACC)
+        check(f"dW ({tag}) vs exact oracle", host(dW), exact, BF16_BAR)
+    # accumulate onto an existing gradient
+    dW = torch.from_numpy(C0.copy()).cuda()
+    layer.project_bwd_weight(shape, Gbd, Xd, dW, accumulate=True)
+    check("dW (+=) vs bf16-operand oracle", host(dW), rounded + C0, GEMM_ACC)
+    # fp32 arithmetic
+    dW = layer.project_bwd_weight(shape, Gd, Xd, f32_math=True)
+    check("dW (fp32 math) vs exact oracle", host(dW), exact, TIGHT)
+    dW = torch.from_numpy(C0.copy()).cuda()
+    layer.project_bwd_weight(shape, Gbd, Xbd, dW, accumulate=True, f32_math=True)
+    check("dW (fp32 math, bf16 inputs, +=)", host(dW),
+          oracle.project_bwd_weight(Gb.reshape(M, -1), Xb.reshape(M, d), False) + C0, TIGHT)
+
+
+def test_projection_bwd_weight_is_deterministic():
+    """The split reduction adds its partial sums in a fixed order."""
+    import torch
+    shape = SruShape(128, 16, 128, True, 1.0)
+    g = torch.Generator().manual_seed(77)
+    dU = torch.randn(128 * 16, 6 * 128, generator=g).cuda()
+    X = torch.randn(128 * 16, 128, generator=g).cuda()
+    a = layer.project_bwd_weight(shape, dU, X)
+    b = layer.project_bwd_weight(shape, dU, X)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
 def test_projection_fp32_config1():

@@ -3,10 +3,12 @@ the benchmark times.
 
 * workload 1 (fp32, L=32 B=4 d=64): every output element (test_parity_gpu).
 * workload 2 (bidirectional, L=64 B=128 d=512): every output element of the
-  whole training step (projection, forward, backward, dv/db, dX).
+  whole training step (projection, forward, backward, dv/db, dX), and 52
+  sampled rows of the weight gradient dW.
 * workload 3 (given bf16 U, L=1024 B=16 d=2048): 48 sampled chains.
 * workload 4 (training step, L=512 B=32 d=1024): every chain of 3 sampled
-  batch rows, plus size-independent properties for dv and db.
+  batch rows, plus size-independent properties for dv and db, and sampled
+  rows of dW (each needs the oracle's dU of every batch row for its column).
 * workload 5 (linear mode, L=16384 B=4 d=4096, chunk 256): 24 sampled chains,
   plus size-independent properties for db.
 Tolerances are explained in test_parity_gpu.py.
@@ -42,7 +44,44 @@ def training_step(w, t):
                                                 t["dh"], t["dc_last"], bf16_copy=True)
     Wt = layer.transpose_weight(shape, t["W"])
     layer.project_bwd_data(shape, dU_lp, t["W"], dx, accumulate=True, Wt=Wt)
-    return dict(U=U, h=h, c_seq=c_seq, c_last=c_last, dU=dU, dX=dx, dv=dv, db=db, dc0=dc0)
+    dW = layer.project_bwd_weight(shape, dU_lp, t["x"])
+    return dict(U=U, h=h, c_seq=c_seq, c_last=c_last, dU=dU, dX=dx, dv=dv, db=db, dc0=dc0,
+                dW=dW)
+
+
+def dw_rows(w, seed, n_random):
+    """Rows of dW to sample: the first and last of every gate block, plus random ones."""
+    n3 = w.ndir * 3 * w.d
+    rng = np.random.default_rng(seed)
+    edges = [k * w.d for k in range(w.ndir * 3)] + [k * w.d - 1 for k in range(1, w.ndir * 3 + 1)]
+    return np.unique(np.concatenate([edges, rng.integers(0, n3, n_random)]))
+
+
+def oracle_dU_columns(w, inp, cols, round_x):
+    """The oracle's dU [L*B, len(cols)] at columns ``cols`` (index (dir, gate, j)
+    of the [ndir, 3, d] slot), every (t, b): one chain per (dir, j, b)."""
+    L, B, d, nd = w.L, w.B, w.d, w.ndir
+    G = np.empty((L, B, cols.size))
+    chains = {}
+    for k, n in enumerate(cols):
+        dr, rem = divmod(int(n), 3 * d)
+        gate, j = divmod(rem, d)
+        chains.setdefault((dr, j), []).append((k, gate))
+    for (dr, j), ks in chains.items():
+        v, bias = inp["v"][dr, :, j], inp["b"][dr, :, j]
+        for b in range(B):
+            uf, ur, ux = oracle.chain_inputs_from_projection(inp["x"], inp["W"], round_x, L, B, d,
+                                                             nd, dr, b, j)
+            x = inp["x"][:, b, j]
+            c0 = inp["c0"][dr, b, j]
+            _, c, _ = oracle.chain_forward(uf, ur, ux, x, v[0], v[1], bias[0], bias[1], c0,
+                                           w.alpha, direction=dr)
+            gb = oracle.chain_backward(uf, ur, ux, x, v[0], v[1], bias[0], bias[1], c0, c,
+                                       inp["dh"][:, b, dr, j], inp["dc_last"][dr, b, j], w.alpha,
+                                       direction=dr)
+            for k, gate in ks:
+                G[:, b, k] = gb[("duf", "dur", "dux")[gate]]
+    return G.reshape(L * B, cols.size)
 
 
 def oracle_rows(w, inp, bs, round_x):
@@ -88,6 +127,10 @@ def test_workload2_full():
         check("db", host(g["db"]), bo["db"], tol)
         check("dc0", host(g["dc0"]), bo["dc0"], tol)
         check("dX", host(g["dX"]), dXo, max(tol, 1e-2))
+        rows = dw_rows(w, 22, 40)
+        Gs = np.ascontiguousarray(bo["dU"].reshape(L * B, -1)[:, rows])
+        dWo = oracle.project_bwd_weight(Gs, inp["x"].reshape(L * B, d), round_x)
+        check(f"dW ({rows.size} sampled rows)", host(g["dW"])[rows], dWo, max(tol, 1e-2))
 
 
 def test_workload3_sampled_chains():
@@ -135,6 +178,14 @@ def test_workload4_sampled_rows_and_properties():
             check(f"dU[b={b}]", host(g["dU"][:, b]), o["dU"], tol)
             check(f"dc0[b={b}]", host(g["dc0"][:, b]), o["dc0"], tol)
             check(f"dX[b={b}]", host(g["dX"][:, b]), o["dX"], max(tol, 1e-2))
+    # dW sums over every (t, b): its sampled rows need the oracle's dU of every
+    # batch row for those columns only, i.e. one chain per (b, row) pair
+    rows = dw_rows(w, 44, 10)
+    X2 = inp["x"].reshape(w.L * w.B, w.d)
+    for round_x, tol in ((True, 1e-2), (False, BF16_BAR)):
+        Gs = oracle_dU_columns(w, inp, rows, round_x)
+        check(f"dW ({rows.size} sampled rows, round_x={round_x})", host(g["dW"])[rows],
+              oracle.project_bwd_weight(Gs, X2, round_x), tol)
     # dv, db: exact sums of the per-step terms the kernel produced
     dU = g["dU"].double()
     c_seq = g["c_seq"].double()
