@@ -15,10 +15,16 @@ linear mode = the same recurrence with v = 0).  The arithmetic lives in
 Layouts (row-major): U [L, B, ndir, 3, d]; x [L, B, d]; v, b [ndir, 2, d];
 c0 [ndir, B, d]; h, c [L, B, ndir, d]; c_last [ndir, B, d].
 
+The factorised projection of the same paper (Fig. 2(b): U = Wo (Wq X), inner
+dimension d' < d) and its gradients are compositions of a plain double
+matrix product (``matmul``).
+
 Pins (tests/test_oracle_pins.py): textbook matmul, saturated gates, the EMA
 closed form, brute-force unrolled recurrences at L <= 4, central finite
-differences for every gradient, the bidirectional time-flip invariant and
-channel/batch permutation equivariance.
+differences for every gradient, the bidirectional time-flip invariant,
+channel/batch permutation equivariance, and for the factorised projection
+associativity (one projection with the product weight), hand-computed bf16
+rounding of X and Q, and central differences.
 """
 import ctypes
 import os
@@ -70,6 +76,11 @@ def _load():
     lib.sru_oracle_backward.argtypes = [_i64, _i64, _i64, ctypes.c_int, d,
                                         _dp, _fp, _fp, _fp, _fp, _dp, _fp, _fp,
                                         _dp, _dp, _dp, _dp, _dp]
+    lib.sru_oracle_round_bf16_n.restype = None
+    lib.sru_oracle_round_bf16_n.argtypes = [_i64, _fp, _fp]
+    lib.sru_oracle_matmul.restype = None
+    lib.sru_oracle_matmul.argtypes = [_i64, _i64, _i64, _dp, ctypes.c_int, _dp, ctypes.c_int,
+                                      _dp]
     lib.sru_oracle_num_threads.restype = ctypes.c_int
     lib.sru_oracle_num_threads.argtypes = []
     _lib = lib
@@ -107,13 +118,54 @@ def sigmoid(z: float) -> float:
 
 
 def round_bf16(a) -> np.ndarray:
-    """fp32 -> nearest bf16 (ties to even), returned widened to fp32."""
-    lib = _load()
-    flat = np.ascontiguousarray(a, dtype=np.float32).ravel()
+    """fp32 -> nearest bf16 (ties to even), returned widened to fp32.  Wider
+    values are taken to fp32 first, as a kernel's fp32 register holds them."""
+    flat, pin = _f32(np.asarray(a).ravel())
     out = np.empty_like(flat)
-    for i, v in enumerate(flat):
-        out[i] = lib.sru_oracle_round_bf16(float(v))
+    _load().sru_oracle_round_bf16_n(flat.size, pin, out.ctypes.data_as(_fp))
     return out.reshape(np.shape(a))
+
+
+def matmul(A, B, a_km: bool = False, b_nk: bool = False) -> np.ndarray:
+    """C = A B in double: A [M, K] (or [K, M] with a_km), B [K, N] (or [N, K]
+    with b_nk)."""
+    A, pa = _f64(A)
+    B, pb = _f64(B)
+    M, K = (A.shape[1], A.shape[0]) if a_km else A.shape
+    N, K2 = B.shape if b_nk else (B.shape[1], B.shape[0])
+    assert K == K2, (A.shape, B.shape, a_km, b_nk)
+    C = np.empty((M, N), dtype=np.float64)
+    _load().sru_oracle_matmul(M, N, K, pa, int(bool(a_km)), pb, int(bool(b_nk)),
+                              C.ctypes.data_as(_dp))
+    return C
+
+
+def _maybe_bf16(a, on):
+    return round_bf16(a).astype(np.float64) if on else np.asarray(a, np.float64)
+
+
+def factored_project(X, Wq, Wo, round_ops: bool):
+    """The factorised projection of the SRU++ paper (Fig. 2(b); the same map is
+    its attention layer's output projection with alpha = 0): Q = Xt Wq^T,
+    U = Qt Wo^T, with X [M, d], Wq [d', d], Wo [ndir*3d, d'].  round_ops:
+    X and Q enter their products rounded to bf16 (nearest even), as the bf16
+    kernels multiply them; the weights are used as given."""
+    Q = matmul(_maybe_bf16(X, round_ops), Wq, b_nk=True)
+    U = matmul(_maybe_bf16(Q, round_ops), Wo, b_nk=True)
+    return {"Q": Q, "U": U}
+
+
+def factored_project_backward(X, Q, Wq, Wo, dU, round_ops: bool):
+    """Gradients of factored_project given dU (chain rule through both
+    products): dQ = dUt Wo, dX = dQt Wq, dWo = dUt^T Qt, dWq = dQt^T Xt, where
+    t marks bf16 rounding of the activation-side operands when round_ops."""
+    dUt = _maybe_bf16(dU, round_ops)
+    dQ = matmul(dUt, Wo)
+    dQt = _maybe_bf16(dQ, round_ops)
+    return {"dQ": dQ,
+            "dX": matmul(dQt, Wq),
+            "dWo": matmul(dUt, _maybe_bf16(Q, round_ops), a_km=True),
+            "dWq": matmul(dQt, _maybe_bf16(X, round_ops), a_km=True)}
 
 
 def project(A, W, round_a: bool, rows=None, cols=None) -> np.ndarray:

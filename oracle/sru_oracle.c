@@ -20,6 +20,9 @@
  *   (the remark after Eq. 5), so the oracle is written per chain.
  *   The projection's two gradients (input and weights) are the chain rule
  *   through Eq. 1.
+ *   The factorised projection (same paper, Fig. 2(b)): U = W_o (W_q X) with a
+ *   small inner dimension d'; it and its gradients are plain products
+ *   (sru_oracle_matmul).
  *
  * Readings taken where the pages are silent (each is listed in the design
  * notes of the repository):
@@ -80,6 +83,38 @@ float sru_oracle_round_bf16(float x)
     float y;
     memcpy(&y, &u, sizeof y);
     return y;
+}
+
+/* sru_oracle_round_bf16 applied to n values. */
+void sru_oracle_round_bf16_n(int64_t n, const float *in, float *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = sru_oracle_round_bf16(in[i]);
+}
+
+/*
+ * Plain matrix product in double: C[m][n] = sum_{k<K} A(m, k) B(k, n), the
+ * terms added in increasing k, with
+ *   A(m, k) = A[m*K + k] (A stored [M, K]) or, when a_km, A[k*M + m] ([K, M]);
+ *   B(k, n) = B[n*K + k] (B stored [N, K]) when b_nk, else B[k*N + n] ([K, N]).
+ * The factorised projection of the SRU++ paper (Fig. 2(b): U = W_o (W_q X),
+ * a small inner dimension d') and its gradients are products of this form.
+ */
+void sru_oracle_matmul(int64_t M, int64_t N, int64_t K, const double *A, int a_km,
+                       const double *B, int b_nk, double *C)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double a = a_km ? A[k * M + m] : A[m * K + k];
+                const double b = b_nk ? B[n * K + k] : B[k * N + n];
+                s += a * b;
+            }
+            C[m * N + n] = s;
+        }
+    }
 }
 
 /*

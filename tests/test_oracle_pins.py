@@ -128,6 +128,81 @@ def test_project_bwd_weight_is_the_weight_derivative_of_the_projection():
             assert fd == pytest.approx(dW[n, q], rel=1e-11, abs=1e-11)
 
 
+@pytest.mark.parametrize("a_km,b_nk", [(False, False), (True, False), (False, True),
+                                       (True, True)])
+def test_matmul_matches_numpy(a_km, b_nk):
+    rng = np.random.default_rng(21)
+    M, N, K = 7, 5, 9
+    A = rng.standard_normal((M, K))
+    B = rng.standard_normal((K, N))
+    got = oracle.matmul(A.T.copy() if a_km else A, B.T.copy() if b_nk else B, a_km, b_nk)
+    np.testing.assert_allclose(got, A @ B, rtol=1e-13, atol=1e-13)
+
+
+def test_factored_projection_is_one_projection_with_the_product_weight():
+    """Closed form (associativity): Wo (Wq X^T) = (Wo Wq) X^T, so without
+    rounding the factorised map equals Eq. 1's projection with the weight
+    Wo Wq, evaluated here by the Eq. 1 oracle in one product."""
+    rng = np.random.default_rng(22)
+    M, d, dp, n3 = 13, 8, 3, 24
+    # dyadic values with few bits: every product and sum below is exact in
+    # double, and Wo Wq is exact in float32 as the Eq. 1 oracle takes it
+    X = (rng.integers(-8, 8, (M, d)) / 4).astype(np.float32)
+    Wq = rng.integers(-4, 4, (dp, d)) / 8
+    Wo = rng.integers(-4, 4, (n3, dp)) / 8
+    f = oracle.factored_project(X, Wq, Wo, False)
+    Wcomb = (Wo @ Wq).astype(np.float32)
+    assert np.array_equal(Wcomb.astype(np.float64), Wo @ Wq)
+    assert np.array_equal(f["U"], oracle.project(X, Wcomb, False))
+    assert np.array_equal(f["Q"], oracle.project(X, Wq.astype(np.float32), False))
+
+
+def test_factored_projection_rounds_x_and_q():
+    """Hand-computed: with Wq = Wo = [[1]] the map is U = bf16(bf16(x)).
+    x = 1 + 2^-9 lies below half an ulp of bf16 at 1 (2^-8) and rounds to 1;
+    x = 1 + 3 * 2^-9 lies above it and rounds to 1 + 2^-7."""
+    one = np.ones((1, 1))
+    for x, want in ((1 + 2 ** -9, 1.0), (1 + 3 * 2 ** -9, 1 + 2 ** -7)):
+        X = np.array([[x]], np.float32)
+        assert oracle.factored_project(X, one, one, True)["U"][0, 0] == want
+        assert oracle.factored_project(X, one, one, False)["U"][0, 0] == np.float32(x)
+    # Q rounded between the products: x = 1, Wq = [[1 + 2^-9]] gives Q = 1 + 2^-9,
+    # which enters the second product as 1
+    f = oracle.factored_project(np.ones((1, 1), np.float32), np.array([[1 + 2 ** -9]]), one, True)
+    assert f["Q"][0, 0] == 1 + 2 ** -9 and f["U"][0, 0] == 1.0
+
+
+def test_factored_projection_backward_finite_differences():
+    """Central differences of s = sum(G * U(X, Wq, Wo)) for every entry of X,
+    Wq and Wo (no rounding).  U is bilinear in (Wq, Wo) and linear in X, so
+    the central quotient is exact up to double rounding."""
+    rng = np.random.default_rng(23)
+    M, d, dp, n3 = 5, 4, 2, 6
+    X = rng.standard_normal((M, d)).astype(np.float32).astype(np.float64)
+    Wq = rng.standard_normal((dp, d))
+    Wo = rng.standard_normal((n3, dp))
+    G = rng.standard_normal((M, n3))
+    f = oracle.factored_project(X.astype(np.float32), Wq, Wo, False)
+    g = oracle.factored_project_backward(X.astype(np.float32), f["Q"], Wq, Wo, G, False)
+
+    def s_of(X_, Wq_, Wo_):
+        # the map written out directly, so the pin does not go through the oracle
+        return float(np.sum(G * ((X_ @ Wq_.T) @ Wo_.T)))
+
+    h = 2.0 ** -10
+    for name, arr in (("dX", X), ("dWq", Wq), ("dWo", Wo)):
+        for idx in np.ndindex(arr.shape):
+            p, m = arr.copy(), arr.copy()
+            p[idx] += h
+            m[idx] -= h
+            args_p = [p if a is arr else a for a in (X, Wq, Wo)]
+            args_m = [m if a is arr else a for a in (X, Wq, Wo)]
+            fd = (s_of(*args_p) - s_of(*args_m)) / (2 * h)
+            assert fd == pytest.approx(g[name][idx], rel=1e-9, abs=1e-9), (name, idx)
+    # dQ is the gradient with respect to the intermediate Q
+    np.testing.assert_allclose(g["dQ"], G @ Wo, rtol=1e-12, atol=1e-12)
+
+
 def test_sigmoid_values():
     for z in (-800.0, -30.0, -1.5, 0.0, 0.25, 4.0, 40.0, 800.0):
         ref = 1.0 / (1.0 + math.exp(-z)) if z > -700 else 0.0
