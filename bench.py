@@ -19,8 +19,9 @@ their roofline fractions, the dominant row's roofline object, the CPU oracle
 baseline on a bounded sample, and measurements of the other rows at the other
 workload sizes (given-U bf16 forward, the L=512 training step, the linear-mode
 chunked scan) are included.  ``beyond_step`` times, after the step and on its
-buffers, the projection's weight gradient dW = bf16(dU)^T X~, which is not
-part of the step.
+buffers, rows that are not part of the step: the projection's weight gradient
+dW = bf16(dU)^T X~, and the factorised projection U = Wo (Wq X~) with d' = d/4
+(SRU++ paper, Fig. 2(b)), forward and backward.
 """
 import argparse
 import hashlib
@@ -50,6 +51,9 @@ def parse():
     p.add_argument("--sets", type=int, default=4, help="rotating input/output sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true")
+    p.add_argument("--no-beyond", action="store_true",
+                   help="skip the rows timed beyond the step (counter runs use this, so "
+                        "that every dispatch of a kernel belongs to a step row)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run one torch copy of this many MiB (counter calibration)")
     p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -102,8 +106,25 @@ def next_row_work(w):
     L, B, d, nd = w.L, w.B, w.d, w.ndir
     LB, n3 = L * B, nd * 3 * d
     xs = 2 if w.x_dtype == "bf16" else 4
+    di = factored_inner(w)
+    fwd_flops = 2 * LB * d * di + 2 * LB * di * n3
+    fwd_bytes = (LB * d * xs + di * d * 2 + LB * di * 4          # Q = X Wq^T
+                 + LB * di * 4 + n3 * di * 2 + LB * n3 * 4)     # U = Q Wo^T
+    bwd_flops = 4 * LB * n3 * di + 4 * LB * di * d
+    bwd_bytes = (LB * n3 * 2 + n3 * di * 2 + LB * di * 4         # dQ = bf16(dU) Wo
+                 + LB * di * 4 + di * d * 2 + 2 * LB * d * 4    # dX += dQ Wq
+                 + LB * di * 4 + LB * d * xs + di * d * 4       # dWq = dQ^T X
+                 + LB * n3 * 2 + LB * di * 4 + n3 * di * 4)     # dWo = bf16(dU)^T Q
     return {"f1_projection_bwd_weight": dict(flops=2 * LB * n3 * d,
-                                             bytes=LB * n3 * 2 + LB * d * xs + n3 * d * 4)}
+                                             bytes=LB * n3 * 2 + LB * d * xs + n3 * d * 4),
+            "f3_factored_forward": dict(flops=fwd_flops, bytes=fwd_bytes),
+            "f3_factored_backward": dict(flops=bwd_flops, bytes=bwd_bytes)}
+
+
+def factored_inner(w):
+    """Inner dimension of the factorised projection: d / 4, the proportion of
+    the SRU++ paper's Fig. 2 (d = 2048, d' = 512)."""
+    return max(1, w.d // 4)
 
 
 def roofline_of(name, work, seconds):
@@ -124,7 +145,8 @@ def roofline_of(name, work, seconds):
 def device_set(w, seed):
     import numpy as np
     import torch
-    from parallelizable_recurrent_units_amd import (SRU_WS_BACKWARD, SRU_WS_BWD_WEIGHT, SruShape,
+    from parallelizable_recurrent_units_amd import (SRU_WS_BACKWARD, SRU_WS_BWD_WEIGHT,
+                                                    SRU_WS_FACTORED_WEIGHT, SruShape,
                                                     sru_workspace_size)
     from parallelizable_recurrent_units_amd.workloads import make_inputs
     inp = make_inputs(w, seed=seed)
@@ -151,6 +173,16 @@ def device_set(w, seed):
                dW=torch.empty((nd * 3 * d, d), **f32))
     nw = sru_workspace_size(shape, SRU_WS_BWD_WEIGHT)
     dev["ws_w"] = torch.empty(nw, device="cuda", dtype=torch.uint8) if nw else None
+    # factorised projection (timed beyond the step): weights ~ U(-0.05, 0.05) in bf16
+    di = factored_inner(w)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    dev["Wq"] = ((torch.rand((di, d), generator=g, **f32) - 0.5) * 0.1).to(torch.bfloat16)
+    dev["Wo"] = ((torch.rand((nd * 3 * d, di), generator=g, **f32) - 0.5) * 0.1).to(torch.bfloat16)
+    dev.update(Q=torch.empty((L * B, di), **f32), dQ=torch.empty((L * B, di), **f32),
+               dWq=torch.empty((di, d), **f32), dWo=torch.empty((nd * 3 * d, di), **f32))
+    nf = sru_workspace_size(shape, SRU_WS_FACTORED_WEIGHT, di)
+    dev["ws_f"] = torch.empty(nf, device="cuda", dtype=torch.uint8) if nf else None
     return shape, dev
 
 
@@ -178,11 +210,32 @@ def training_step_rows(shape, t):
 
 def next_rows(shape, t):
     """The rows beyond the step, run on a step's buffers (dU_lp as the step
-    left it)."""
-    from parallelizable_recurrent_units_amd import SRU_BF16, sru_project_bwd_weight
+    left it): the weight gradient, and the factorised projection's forward
+    (writing U) and backward (adding to dx)."""
+    from parallelizable_recurrent_units_amd import (SRU_BF16, SRU_FACT_BWD_Q, SRU_FACT_BWD_X,
+                                                    SRU_FACT_Q, SRU_FACT_U, SRU_FACT_WGRAD_O,
+                                                    SRU_FACT_WGRAD_Q, sru_project_bwd_weight,
+                                                    sru_project_factored,
+                                                    sru_project_factored_bwd_weight)
+    di = t["Q"].shape[1]
+
+    def fact_fwd():
+        sru_project_factored(shape, di, SRU_FACT_Q, t["x"], t["Wq"], t["Q"])
+        sru_project_factored(shape, di, SRU_FACT_U, t["Q"], t["Wo"], t["U"])
+
+    def fact_bwd():
+        sru_project_factored(shape, di, SRU_FACT_BWD_Q, t["dU_lp"], t["Wo"], t["dQ"])
+        sru_project_factored(shape, di, SRU_FACT_BWD_X, t["dQ"], t["Wq"], t["dx"], True)
+        sru_project_factored_bwd_weight(shape, di, SRU_FACT_WGRAD_Q, t["dQ"], t["x"], t["dWq"],
+                                        SRU_BF16, False, t["ws_f"])
+        sru_project_factored_bwd_weight(shape, di, SRU_FACT_WGRAD_O, t["dU_lp"], t["Q"],
+                                        t["dWo"], SRU_BF16, False, t["ws_f"])
+
     return [("f1_projection_bwd_weight",
              lambda: sru_project_bwd_weight(shape, t["dU_lp"], t["x"], t["dW"], SRU_BF16, False,
-                                            t["ws_w"]))]
+                                            t["ws_w"])),
+            ("f3_factored_forward", fact_fwd),
+            ("f3_factored_backward", fact_bwd)]
 
 
 def time_rows(row_sets, steps, warmup):
@@ -366,6 +419,10 @@ ROW_LAUNCHES = {
     "f1_projection_bwd_weight": ["gemm_bf16_mfma (A = bf16 dU copy and B = fp32 X, both read "
                                  "along L*B; the reduction split over blocks)",
                                  "split_reduce (partial sums added in split order)"],
+    "f3_factored_forward": ["gemm_bf16_mfma (Q = X Wq^T)", "gemm_bf16_mfma (U = Q Wo^T)"],
+    "f3_factored_backward": ["gemm_bf16_mfma (dQ = bf16(dU) Wo)", "gemm_bf16_mfma (dx += dQ Wq)",
+                             "gemm_bf16_mfma + split_reduce (dWq = dQ^T X)",
+                             "gemm_bf16_mfma + split_reduce (dWo = bf16(dU)^T Q)"],
 }
 
 # kernels of each training-step row (rocprofv3 kernel names), and the one
@@ -496,7 +553,7 @@ def main():
     row_sets = row_sets_for(w, nsets, 100)
     print("[bench] timing", file=sys.stderr, flush=True)
     ms, rows = time_rows(row_sets, args.steps, args.warmup)
-    beyond = time_beyond(w, row_sets, args.steps, args.warmup)
+    beyond = {} if args.no_beyond else time_beyond(w, row_sets, args.steps, args.warmup)
     del row_sets
     torch.cuda.empty_cache()
     work = row_work(w)

@@ -79,8 +79,20 @@ typedef enum {
     SRU_WS_BACKWARD = 1,    /* sru_backward                      */
     SRU_WS_LINEAR_FWD = 2,  /* sru_linear_scan(SRU_FWD, chunk)   */
     SRU_WS_LINEAR_BWD = 3,  /* sru_linear_scan(SRU_BWD, chunk)   */
-    SRU_WS_BWD_WEIGHT = 4   /* sru_project_bwd_weight            */
+    SRU_WS_BWD_WEIGHT = 4,  /* sru_project_bwd_weight            */
+    SRU_WS_FACTORED_WEIGHT = 5  /* sru_project_factored_bwd_weight, either
+                                   gradient; `chunk` carries the inner dimension d' */
 } sru_ws_op;
+typedef enum {
+    SRU_FACT_Q = 0,      /* Q  [L*B, d']       (+)= X~  . Wq^T   Wq [d', d]        */
+    SRU_FACT_U = 1,      /* U  [L*B, ndir*3d]  (+)= Q~  . Wo^T   Wo [ndir*3d, d']  */
+    SRU_FACT_BWD_Q = 2,  /* dQ [L*B, d']       (+)= dU~ . Wo                       */
+    SRU_FACT_BWD_X = 3   /* dX [L*B, d]        (+)= dQ~ . Wq                       */
+} sru_fact_op;
+typedef enum {
+    SRU_FACT_WGRAD_Q = 0,   /* dWq [d', d]      (+)= dQ~^T . X~ */
+    SRU_FACT_WGRAD_O = 1    /* dWo [ndir*3d, d'] (+)= dU~^T . Q~ */
+} sru_fact_wgrad_op;
 
 typedef struct {
     int64_t L, B, d;
@@ -131,6 +143,42 @@ sru_status sru_project_bwd_weight(const sru_shape *shape,
                                   const void *X, sru_dtype x_dt,
                                   float *dW, sru_dtype math_dt, int32_t accumulate,
                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Factorised projection (SRU++ paper, Fig. 2(b), and the output projection of
+ * its attention layer with the attention weight alpha = 0):
+ *   Q = X~ Wq^T (inner dimension d_inner = d' < d), U = Q~ Wo^T,
+ * so Wo Wq takes the place of Eq. 1's W.  Each call is one product of the
+ * forward or of the input-side backward (layouts in sru_fact_op; Q and dQ are
+ * [L*B, d'] row-major, the other tensors as for sru_project).  The backward
+ * chain: dQ = dU Wo, then dX = dQ Wq (accumulate = 1 onto sru_backward's dx
+ * gives the full input gradient).
+ * w_dt = SRU_BF16: bf16 MFMA with fp32 accumulation; A (fp32 or bf16) is
+ *   rounded to bf16 (nearest even) as it is loaded ("~" above).
+ * w_dt = SRU_F32: fp32 arithmetic throughout (A widened if bf16).
+ * C is fp32 and must not overlap A or W.  accumulate = 0 overwrites C, 1
+ * adds to it.  d_inner >= 1.
+ */
+sru_status sru_project_factored(const sru_shape *shape, int64_t d_inner, sru_fact_op op,
+                                const void *A, sru_dtype a_dt,
+                                const void *W, sru_dtype w_dt,
+                                float *C, int32_t accumulate, void *stream);
+
+/*
+ * Weight gradients of the factorised projection (chain rule through both
+ * products): which = SRU_FACT_WGRAD_Q: dWq (+)= dQ^T X~, G = dQ [L*B, d'],
+ * Y = X [L*B, d]; SRU_FACT_WGRAD_O: dWo (+)= dU^T Q~, G = dU [L*B, ndir*3d],
+ * Y = Q [L*B, d'].  Arithmetic, accumulation, reproducibility and the
+ * workspace as for sru_project_bwd_weight; the workspace size is
+ * sru_workspace_size(shape, SRU_WS_FACTORED_WEIGHT, d_inner).
+ */
+sru_status sru_project_factored_bwd_weight(const sru_shape *shape, int64_t d_inner,
+                                           sru_fact_wgrad_op which,
+                                           const void *G, sru_dtype g_dt,
+                                           const void *Y, sru_dtype y_dt,
+                                           float *dW, sru_dtype math_dt, int32_t accumulate,
+                                           void *workspace, size_t workspace_bytes,
+                                           void *stream);
 
 /*
  * Forward recurrence, Eqs. 2-5, for every (direction, batch, channel) chain.
@@ -218,8 +266,10 @@ sru_status sru_linear_scan(const sru_shape *shape, sru_pass pass, int32_t chunk,
 sru_status sru_transpose_weight(const sru_shape *shape, const void *W, sru_dtype w_dt,
                                 void *Wt, void *stream);
 
-/* Workspace bytes needed by `op` for `shape` (and `chunk` for the linear
- * mode); 0 on invalid arguments (sru_last_error() says why). */
+/* Workspace bytes needed by `op` for `shape` (and `chunk`: the chunk length
+ * for the linear mode, the inner dimension d' for SRU_WS_FACTORED_WEIGHT);
+ * 0 either when none is needed or on invalid arguments (then
+ * sru_last_error() is not empty and says why). */
 size_t sru_workspace_size(const sru_shape *shape, sru_ws_op op, int32_t chunk);
 
 /* Static text for a status code. */

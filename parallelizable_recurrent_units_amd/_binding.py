@@ -20,11 +20,14 @@ SRU_F32, SRU_BF16 = 0, 1
 SRU_FWD, SRU_BWD = 0, 1
 SRU_PROJ_FWD, SRU_PROJ_BWD_DATA, SRU_PROJ_BWD_DATA_WT = 0, 1, 2
 SRU_WS_BACKWARD, SRU_WS_LINEAR_FWD, SRU_WS_LINEAR_BWD, SRU_WS_BWD_WEIGHT = 1, 2, 3, 4
+SRU_WS_FACTORED_WEIGHT = 5
+SRU_FACT_Q, SRU_FACT_U, SRU_FACT_BWD_Q, SRU_FACT_BWD_X = 0, 1, 2, 3
+SRU_FACT_WGRAD_Q, SRU_FACT_WGRAD_O = 0, 1
 
 # Every symbol include/sru.h declares.
-EXPORTED = ("sru_project", "sru_project_bwd_weight", "sru_forward", "sru_backward",
-            "sru_linear_scan", "sru_transpose_weight", "sru_workspace_size", "sru_status_string",
-            "sru_last_error")
+EXPORTED = ("sru_project", "sru_project_bwd_weight", "sru_project_factored",
+            "sru_project_factored_bwd_weight", "sru_forward", "sru_backward", "sru_linear_scan",
+            "sru_transpose_weight", "sru_workspace_size", "sru_status_string", "sru_last_error")
 
 
 class SruShape(ctypes.Structure):
@@ -70,6 +73,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sru_project_bwd_weight.restype = ctypes.c_int
     lib.sru_project_bwd_weight.argtypes = [sp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp,
                                            ctypes.c_int, i32, _vp, sz, _vp]
+    lib.sru_project_factored.restype = ctypes.c_int
+    lib.sru_project_factored.argtypes = [sp, ctypes.c_int64, ctypes.c_int, _vp, ctypes.c_int, _vp,
+                                         ctypes.c_int, _vp, i32, _vp]
+    lib.sru_project_factored_bwd_weight.restype = ctypes.c_int
+    lib.sru_project_factored_bwd_weight.argtypes = [sp, ctypes.c_int64, ctypes.c_int, _vp,
+                                                    ctypes.c_int, _vp, ctypes.c_int, _vp,
+                                                    ctypes.c_int, i32, _vp, sz, _vp]
     lib.sru_forward.restype = ctypes.c_int
     lib.sru_forward.argtypes = [sp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
                                 ctypes.c_int, _vp, _vp, _vp]
@@ -152,6 +162,29 @@ def sru_project_bwd_weight(shape, dU, X, dW, math_dtype: int = SRU_BF16, accumul
     _check(load_library().sru_project_bwd_weight(
         ctypes.byref(s), _ptr(dU), _dtype_code(dU), _ptr(X), _dtype_code(X), _ptr(dW),
         int(math_dtype), int(bool(accumulate)), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def sru_project_factored(shape, d_inner: int, op: int, A, W, C, accumulate: bool = False,
+                         stream=None):
+    s = _shape(shape)
+    if _dtype_code(C) != SRU_F32:
+        raise TypeError("C must be float32")
+    _check(load_library().sru_project_factored(
+        ctypes.byref(s), int(d_inner), int(op), _ptr(A), _dtype_code(A), _ptr(W), _dtype_code(W),
+        _ptr(C), int(bool(accumulate)), _stream(stream)))
+
+
+def sru_project_factored_bwd_weight(shape, d_inner: int, which: int, G, Y, dW,
+                                    math_dtype: int = SRU_BF16, accumulate: bool = False,
+                                    workspace=None, stream=None):
+    s = _shape(shape)
+    if _dtype_code(dW) != SRU_F32:
+        raise TypeError("dW must be float32")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().sru_project_factored_bwd_weight(
+        ctypes.byref(s), int(d_inner), int(which), _ptr(G), _dtype_code(G), _ptr(Y),
+        _dtype_code(Y), _ptr(dW), int(math_dtype), int(bool(accumulate)), _ptr(workspace),
+        ws_bytes, _stream(stream)))
 
 
 def sru_transpose_weight(shape, W, Wt, stream=None):

@@ -118,6 +118,81 @@ size_t backward_ws(const sru_shape *s, const Dims &dm)
     return round256(sru::backward_scan_workspace_bytes(s->L, s->B, s->d, dm.ndir));
 }
 
+// The projection-shaped products of the factorised projection and of the
+// weight gradients: C[M, N] (+)= op(A) op(B) in one of three layouts.
+enum class Layout {
+    NT,   // A [M, K], B [N, K]
+    NN,   // A [M, K], B [K, N]
+    TN    // A [K, M], B [K, N] (the weight gradients)
+};
+
+size_t elem_bytes(sru_dtype t) { return t == SRU_BF16 ? 2 : 4; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+size_t product_ws(Layout lay, int64_t M, int64_t N, int64_t K)
+{
+    return lay == Layout::TN ? round256(sru::wgrad_workspace_bytes(M, N, K)) : 0;
+}
+
+// Validates and launches one product.  bf16 math: MFMA on operands rounded
+// to bf16 as they are loaded (B must be bf16 unless the layout is TN); fp32
+// math: fp32 FMA on widened operands.  C is fp32 and must not overlap A or B.
+sru_status run_product(Layout lay, int64_t M, int64_t N, int64_t K, const void *A,
+                       sru_dtype a_dt, const char *a_name, const void *B, sru_dtype b_dt,
+                       const char *b_name, float *C, const char *c_name, sru_dtype math_dt,
+                       int32_t accumulate, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream, const char *what)
+{
+    if (!valid_dtype(a_dt) || !valid_dtype(b_dt) || !valid_dtype(math_dt))
+        return fail(SRU_ERR_INVALID_ARG, "unknown dtype");
+    if (accumulate != 0 && accumulate != 1)
+        return fail(SRU_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+    SRU_TRY(need_ptr(A, a_name));
+    SRU_TRY(need_ptr(B, b_name));
+    SRU_TRY(need_ptr(C, c_name));
+    const bool f32_math = math_dt == SRU_F32;
+    if (lay != Layout::TN && f32_math != (b_dt == SRU_F32))
+        return fail(SRU_ERR_UNSUPPORTED, "%s: the weight dtype selects the arithmetic", what);
+    int64_t ae, be, ce;
+    if (!mul_ok(M, K, &ae) || !mul_ok(N, K, &be) || !mul_ok(M, N, &ce))
+        return fail(SRU_ERR_INVALID_ARG, "%s: tensor sizes overflow", what);
+    // grids: fp32 kernel x over M / 64 (y over N / 64 <= 65535); MFMA kernels
+    // one dimension over (M / 128) x (N / 128) tiles; the split reduction
+    // over M x N / 256
+    if ((M + 63) / 64 > kMaxBlocks || (N + 63) / 64 > 65535 || (ce + 255) / 256 > kMaxBlocks)
+        return fail(SRU_ERR_INVALID_ARG, "%s: matrix too large for one launch", what);
+    if (overlaps(C, (size_t)ce * 4, A, (size_t)ae * elem_bytes(a_dt)) ||
+        overlaps(C, (size_t)ce * 4, B, (size_t)be * elem_bytes(b_dt)))
+        return fail(SRU_ERR_INVALID_ARG, "%s: %s overlaps %s or %s", what, c_name, a_name, b_name);
+    const size_t need = f32_math ? 0 : product_ws(lay, M, N, K);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(SRU_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need,
+                        workspace_bytes, workspace ? "" : ", NULL");
+        SRU_TRY(opt_ptr(workspace, "workspace"));
+    }
+    SRU_TRY(need_device());
+    sru::GemmArgs g;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.A = A;
+    g.a_bf16 = a_dt == SRU_BF16;
+    g.Bm = B;
+    g.b_bf16 = b_dt == SRU_BF16;
+    g.b_kn = lay != Layout::NT;
+    g.C = C;
+    g.accumulate = accumulate != 0;
+    if (lay == Layout::TN)
+        return launched(sru::launch_gemm_wgrad(g, f32_math, (float *)workspace, stream), what);
+    return launched(sru::launch_gemm(g, stream), what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -157,6 +232,17 @@ size_t sru_workspace_size(const sru_shape *shape, sru_ws_op op, int32_t chunk)
     case SRU_WS_BWD_WEIGHT:
         ok();
         return round256(sru::wgrad_workspace_bytes(3 * dm.ndir * shape->d, shape->d, dm.LB));
+    case SRU_WS_FACTORED_WEIGHT: {
+        const int64_t di = chunk;   // the inner dimension d'
+        if (di < 1) {
+            fail(SRU_ERR_INVALID_ARG, "the inner dimension must be >= 1 (got %d)", (int)chunk);
+            return 0;
+        }
+        const size_t a = product_ws(Layout::TN, di, shape->d, dm.LB);
+        const size_t b = product_ws(Layout::TN, 3 * dm.ndir * shape->d, di, dm.LB);
+        ok();
+        return a > b ? a : b;
+    }
     }
     fail(SRU_ERR_INVALID_ARG, "unknown workspace op %d", (int)op);
     return 0;
@@ -210,51 +296,62 @@ sru_status sru_project_bwd_weight(const sru_shape *shape, const void *dU, sru_dt
 {
     Dims dm;
     SRU_TRY(check_shape(shape, &dm));
-    if (!valid_dtype(du_dt) || !valid_dtype(x_dt) || !valid_dtype(math_dt))
-        return fail(SRU_ERR_INVALID_ARG, "unknown dtype");
-    if (accumulate != 0 && accumulate != 1)
-        return fail(SRU_ERR_INVALID_ARG, "accumulate must be 0 or 1");
-    SRU_TRY(need_ptr(dU, "dU"));
-    SRU_TRY(need_ptr(X, "X"));
-    SRU_TRY(need_ptr(dW, "dW"));
-    const int64_t n3 = 3 * dm.ndir * shape->d;
-    int64_t wel;
-    if (!mul_ok(n3, shape->d, &wel) || (wel + 255) / 256 > kMaxBlocks)
-        return fail(SRU_ERR_INVALID_ARG, "weight gradient too large for one launch");
-    // fp32 grid: y over column tiles of 64 (<= 65535)
-    if ((shape->d + 63) / 64 > 65535 || (n3 + 63) / 64 > kMaxBlocks)
-        return fail(SRU_ERR_INVALID_ARG, "weight gradient too large for one launch");
-    {   // dW written while dU and X are read
-        const size_t wb = (size_t)wel * 4;
-        const size_t ub = (size_t)dm.u_elems * (du_dt == SRU_BF16 ? 2 : 4);
-        const size_t xb = (size_t)dm.LB * (size_t)shape->d * (x_dt == SRU_BF16 ? 2 : 4);
-        const uintptr_t w = (uintptr_t)dW, u = (uintptr_t)dU, x = (uintptr_t)X;
-        if ((w < u + ub && u < w + wb) || (w < x + xb && x < w + wb))
-            return fail(SRU_ERR_INVALID_ARG, "dW overlaps dU or X");
+    return run_product(Layout::TN, 3 * dm.ndir * shape->d, shape->d, dm.LB, dU, du_dt, "dU", X,
+                       x_dt, "X", dW, "dW", math_dt, accumulate, workspace, workspace_bytes,
+                       (hipStream_t)stream, "weight gradient");
+}
+
+sru_status sru_project_factored(const sru_shape *shape, int64_t d_inner, sru_fact_op op,
+                                const void *A, sru_dtype a_dt, const void *W, sru_dtype w_dt,
+                                float *C, int32_t accumulate, void *stream)
+{
+    Dims dm;
+    SRU_TRY(check_shape(shape, &dm));
+    if (d_inner < 1)
+        return fail(SRU_ERR_INVALID_ARG, "the inner dimension must be >= 1 (got %lld)",
+                    (long long)d_inner);
+    const int64_t d = shape->d, n3 = 3 * dm.ndir * d, LB = dm.LB;
+    switch (op) {
+    case SRU_FACT_Q:
+        return run_product(Layout::NT, LB, d_inner, d, A, a_dt, "X", W, w_dt, "Wq", C, "Q", w_dt,
+                           accumulate, nullptr, 0, (hipStream_t)stream, "factored Q");
+    case SRU_FACT_U:
+        return run_product(Layout::NT, LB, n3, d_inner, A, a_dt, "Q", W, w_dt, "Wo", C, "U", w_dt,
+                           accumulate, nullptr, 0, (hipStream_t)stream, "factored U");
+    case SRU_FACT_BWD_Q:
+        return run_product(Layout::NN, LB, d_inner, n3, A, a_dt, "dU", W, w_dt, "Wo", C, "dQ",
+                           w_dt, accumulate, nullptr, 0, (hipStream_t)stream, "factored dQ");
+    case SRU_FACT_BWD_X:
+        return run_product(Layout::NN, LB, d, d_inner, A, a_dt, "dQ", W, w_dt, "Wq", C, "dX",
+                           w_dt, accumulate, nullptr, 0, (hipStream_t)stream, "factored dX");
     }
-    const bool f32_math = math_dt == SRU_F32;
-    const size_t need =
-        f32_math ? 0 : round256(sru::wgrad_workspace_bytes(n3, shape->d, dm.LB));
-    if (need > 0) {
-        if (!workspace || workspace_bytes < need)
-            return fail(SRU_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need,
-                        workspace_bytes, workspace ? "" : ", NULL");
-        SRU_TRY(opt_ptr(workspace, "workspace"));
+    return fail(SRU_ERR_INVALID_ARG, "unknown factored op %d", (int)op);
+}
+
+sru_status sru_project_factored_bwd_weight(const sru_shape *shape, int64_t d_inner,
+                                           sru_fact_wgrad_op which, const void *G,
+                                           sru_dtype g_dt, const void *Y, sru_dtype y_dt,
+                                           float *dW, sru_dtype math_dt, int32_t accumulate,
+                                           void *workspace, size_t workspace_bytes,
+                                           void *stream)
+{
+    Dims dm;
+    SRU_TRY(check_shape(shape, &dm));
+    if (d_inner < 1)
+        return fail(SRU_ERR_INVALID_ARG, "the inner dimension must be >= 1 (got %lld)",
+                    (long long)d_inner);
+    const int64_t d = shape->d, n3 = 3 * dm.ndir * d, LB = dm.LB;
+    switch (which) {
+    case SRU_FACT_WGRAD_Q:
+        return run_product(Layout::TN, d_inner, d, LB, G, g_dt, "dQ", Y, y_dt, "X", dW, "dWq",
+                           math_dt, accumulate, workspace, workspace_bytes, (hipStream_t)stream,
+                           "factored dWq");
+    case SRU_FACT_WGRAD_O:
+        return run_product(Layout::TN, n3, d_inner, LB, G, g_dt, "dU", Y, y_dt, "Q", dW, "dWo",
+                           math_dt, accumulate, workspace, workspace_bytes, (hipStream_t)stream,
+                           "factored dWo");
     }
-    SRU_TRY(need_device());
-    sru::GemmArgs g;
-    g.M = n3;
-    g.N = shape->d;
-    g.K = dm.LB;
-    g.A = dU;
-    g.a_bf16 = du_dt == SRU_BF16;
-    g.Bm = X;
-    g.b_bf16 = x_dt == SRU_BF16;
-    g.b_kn = true;
-    g.C = dW;
-    g.accumulate = accumulate != 0;
-    return launched(sru::launch_gemm_wgrad(g, f32_math, (float *)workspace, (hipStream_t)stream),
-                    "weight gradient");
+    return fail(SRU_ERR_INVALID_ARG, "unknown factored weight gradient %d", (int)which);
 }
 
 sru_status sru_transpose_weight(const sru_shape *shape, const void *W, sru_dtype w_dt, void *Wt,

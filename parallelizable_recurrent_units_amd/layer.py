@@ -59,6 +59,44 @@ def project_bwd_weight(shape, dU, X, dW=None, accumulate=False, f32_math=False, 
     return dW
 
 
+def project_factored(shape, d_inner, X, Wq, Wo, stream=None):
+    """Fig. 2(b) of the SRU++ paper: Q = X Wq^T, U = Q Wo^T (two calls).
+    Returns (Q [L*B, d'], U [L, B, ndir, 3, d])."""
+    s = B._shape(shape)
+    Q = torch.empty((s.L * s.B, d_inner), device=X.device, dtype=torch.float32)
+    U = torch.empty((s.L, s.B, s.ndir, 3, s.d), device=X.device, dtype=torch.float32)
+    B.sru_project_factored(s, d_inner, B.SRU_FACT_Q, X, Wq, Q, False, stream)
+    B.sru_project_factored(s, d_inner, B.SRU_FACT_U, Q, Wo, U, False, stream)
+    return Q, U
+
+
+def project_factored_backward(shape, d_inner, X, Q, Wq, Wo, dU, dX=None, accumulate=False,
+                              f32_math=None, ws=None, stream=None):
+    """Gradients of project_factored given dU: (dQ, dX, dWq, dWo).  dX is
+    added to when ``accumulate`` (e.g. onto sru_backward's highway dx)."""
+    s = B._shape(shape)
+    dev = dU.device
+    f32 = dict(device=dev, dtype=torch.float32)
+    if f32_math is None:
+        f32_math = Wq.dtype == torch.float32
+    dQ = torch.empty((s.L * s.B, d_inner), **f32)
+    if dX is None:
+        dX = torch.empty((s.L, s.B, s.d), **f32)
+    dWq = torch.empty((d_inner, s.d), **f32)
+    dWo = torch.empty((s.ndir * 3 * s.d, d_inner), **f32)
+    if ws is None and not f32_math:
+        n = B.sru_workspace_size(s, B.SRU_WS_FACTORED_WEIGHT, d_inner)
+        ws = torch.empty(n, device=dev, dtype=torch.uint8) if n else None
+    math = B.SRU_F32 if f32_math else B.SRU_BF16
+    B.sru_project_factored(s, d_inner, B.SRU_FACT_BWD_Q, dU, Wo, dQ, False, stream)
+    B.sru_project_factored(s, d_inner, B.SRU_FACT_BWD_X, dQ, Wq, dX, accumulate, stream)
+    B.sru_project_factored_bwd_weight(s, d_inner, B.SRU_FACT_WGRAD_Q, dQ, X, dWq, math, False,
+                                      ws, stream)
+    B.sru_project_factored_bwd_weight(s, d_inner, B.SRU_FACT_WGRAD_O, dU, Q, dWo, math, False,
+                                      ws, stream)
+    return dQ, dX, dWq, dWo
+
+
 def forward(shape, U, x, v, b, c0=None, keep_c_seq=False, stream=None):
     s = B._shape(shape)
     dev = U.device

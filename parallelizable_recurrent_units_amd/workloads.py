@@ -173,3 +173,27 @@ def custom(L, B, d, ndir=1, alpha=1.0, mode="given_u", x_dtype="f32", w_dtype=No
                     x_dtype=x_dtype, w_dtype=w_dtype, u_dtype=u_dtype, w_init=w_init,
                     c0=c0, backward=backward, linear=linear, chunk=chunk,
                     uf_shift=uf_shift)
+
+
+def factored_inputs(L, B, d, ndir, d_inner, seed, w_dtype="bf16"):
+    """Inputs of the factorised projection (SRU++ paper, Fig. 2(b); the paper
+    pairs d = 2048 with d' = 512, i.e. d' = d / 4).  Draw order: X, Wq, Wo,
+    then stand-ins for the tensors the rest of the layer would supply: Q (an
+    input of the U and weight products when tested on their own), dU and dQ.
+    X, Q, dU, dQ ~ N(0, 1); Wq ~ Xavier-U for d -> d', Wo ~ Xavier-U for
+    d' -> ndir*3d, rounded once to bf16 when ``w_dtype`` is "bf16".  Arrays
+    are 2-D: [L*B, features] for activations, [out, in] for weights."""
+    rng = np.random.default_rng(seed)
+    M, n3 = L * B, ndir * 3 * d
+    out = {"X": _std_normal(rng, (M, d))}
+    for name, fan_in, fan_out in (("Wq", d, d_inner), ("Wo", d_inner, n3)):
+        bound = math.sqrt(6.0 / (fan_in + fan_out))
+        W = rng.uniform(-bound, bound, size=(fan_out, fan_in)).astype(np.float32)
+        if w_dtype == "bf16":
+            out[name + "_bits"], out[name] = to_bf16(W)
+        else:
+            out[name] = W
+    out["Q"] = _std_normal(rng, (M, d_inner))
+    out["dU"] = _std_normal(rng, (M, n3))
+    out["dQ"] = _std_normal(rng, (M, d_inner))
+    return out

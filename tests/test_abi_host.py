@@ -191,6 +191,75 @@ def test_bwd_weight_validation(lib):
     assert lib.sru_last_error() == b""
 
 
+def wgrad_ws(M, N, K):
+    """Split-reduction workspace of one weight-gradient product (see above)."""
+    tiles, kt = -(-M // 128) * -(-N // 128), K // 64
+    sp, best = 1, -(-tiles // 512) * kt
+    if K % 64 == 0 and kt >= 16:
+        for n in range(2, min(kt // 8, 64) + 1):
+            cost = -(-tiles * n // 512) * -(-kt // n) + M * N * 1e-6 * n
+            if cost < best:
+                sp, best = n, cost
+    return 0 if sp == 1 else round256(sp * M * N * 4)
+
+
+@pytest.mark.parametrize("L,B,d,bi,di", [(128, 16, 128, 0, 32), (64, 128, 512, 1, 128),
+                                         (512, 32, 1024, 0, 256), (3, 5, 64, 0, 16)])
+def test_factored_workspace_size(lib, L, B, d, bi, di):
+    s = sru.SruShape(L, B, d, bi, 1.0)
+    n3 = 3 * (2 if bi else 1) * d
+    want = max(wgrad_ws(di, d, L * B), wgrad_ws(n3, di, L * B))
+    assert sru.sru_workspace_size(s, sru.SRU_WS_FACTORED_WEIGHT, di) == want
+    assert lib.sru_workspace_size(ctypes.byref(s), sru.SRU_WS_FACTORED_WEIGHT, 0) == 0
+    assert b"inner" in lib.sru_last_error()
+
+
+def fact(lib, s, di, op, **kw):
+    a = dict(A=Q[0], a_dt=0, W=Q[1], w_dt=1, C=Q[2], acc=0)
+    a.update(kw)
+    return lib.sru_project_factored(ctypes.byref(s), di, op, a["A"], a["a_dt"], a["W"],
+                                    a["w_dt"], a["C"], a["acc"], None)
+
+
+def fact_w(lib, s, di, which, ws_bytes, **kw):
+    a = dict(G=Q[0], g_dt=1, Y=Q[1], y_dt=0, dW=Q[2], math=1, acc=0, ws=Q[3])
+    a.update(kw)
+    return lib.sru_project_factored_bwd_weight(ctypes.byref(s), di, which, a["G"], a["g_dt"],
+                                               a["Y"], a["y_dt"], a["dW"], a["math"], a["acc"],
+                                               a["ws"], ws_bytes, None)
+
+
+def test_factored_validation(lib):
+    s = sru.SruShape(128, 16, 128, 0, 1.0)
+    import torch
+    gpu = torch.cuda.device_count() > 0
+    for op in range(4):
+        assert fact(lib, s, 0, op) == sru.SRU_ERR_INVALID_ARG
+        assert fact(lib, s, 32, op, A=None) == sru.SRU_ERR_INVALID_ARG
+        assert fact(lib, s, 32, op, C=Q[2] + 4) == sru.SRU_ERR_INVALID_ARG
+        assert fact(lib, s, 32, op, acc=5) == sru.SRU_ERR_INVALID_ARG
+        # C [L*B, >= 32] fp32 starting inside the weights
+        assert fact(lib, s, 32, op, C=Q[1] + 256) == sru.SRU_ERR_INVALID_ARG
+        assert b"overlaps" in lib.sru_last_error()
+        if not gpu:
+            assert fact(lib, s, 32, op) == sru.SRU_ERR_NO_DEVICE
+            assert fact(lib, s, 32, op, w_dt=0) == sru.SRU_ERR_NO_DEVICE   # fp32 arithmetic
+    assert fact(lib, s, 32, 4) == sru.SRU_ERR_INVALID_ARG
+    need = sru.sru_workspace_size(s, sru.SRU_WS_FACTORED_WEIGHT, 32)
+    assert need > 0
+    own = (wgrad_ws(32, 128, 2048), wgrad_ws(384, 32, 2048))   # dWq, dWo
+    assert need == max(own) and min(own) > 0
+    for which in range(2):
+        assert fact_w(lib, s, 32, which, own[which] - 1) == sru.SRU_ERR_WORKSPACE
+        assert fact_w(lib, s, 32, which, need, ws=None) == sru.SRU_ERR_WORKSPACE
+        assert fact_w(lib, s, 32, which, need, g_dt=4) == sru.SRU_ERR_INVALID_ARG
+        assert fact_w(lib, s, 0, which, need) == sru.SRU_ERR_INVALID_ARG
+        if not gpu:
+            assert fact_w(lib, s, 32, which, need) == sru.SRU_ERR_NO_DEVICE
+            assert fact_w(lib, s, 32, which, 0, math=0, ws=None) == sru.SRU_ERR_NO_DEVICE
+    assert fact_w(lib, s, 32, 2, need) == sru.SRU_ERR_INVALID_ARG
+
+
 def test_binding_raises_sru_error(lib):
     s = sru.SruShape(8, 2, 64, 0, 1.0)
     with pytest.raises(sru.SruError) as ei:

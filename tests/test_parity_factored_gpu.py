@@ -1,0 +1,187 @@
+"""GPU parity of the factorised projection (SRU++ paper, Fig. 2(b)):
+Q = X~ Wq^T, U = Q~ Wo^T and the four gradient products, through the C ABI,
+against the CPU oracle on the same seeded inputs.
+
+Tolerances (normwise, as in test_parity_gpu.py):
+  * each product on its own, against the oracle on the same bf16-rounded
+    operands: 1e-4 (fp32 accumulation order only); against unrounded
+    operands: 2e-2; with fp32 weights (fp32 arithmetic): 1e-5;
+  * the chained forward and backward against the oracle's chain with the same
+    rounding: 1e-3.  Q (or dQ) is rounded to bf16 between the two products on
+    both sides, but from fp32 values that differ by accumulation order, so a
+    few elements round to neighbouring bf16 values (2^-8 apart) and shift the
+    next product slightly; against the unrounded chain: 2e-2.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from parallelizable_recurrent_units_amd import (SRU_BF16, SRU_F32, SRU_FACT_BWD_Q,
+                                                SRU_FACT_BWD_X, SRU_FACT_Q, SRU_FACT_U,
+                                                SRU_FACT_WGRAD_O, SRU_FACT_WGRAD_Q,
+                                                SRU_WS_FACTORED_WEIGHT, SruShape, layer,
+                                                sru_project_factored,
+                                                sru_project_factored_bwd_weight,
+                                                sru_workspace_size, workloads)
+from tests.gpu_util import check, host
+
+pytestmark = pytest.mark.gpu
+
+TIGHT = 1e-5
+BF16_BAR = 2e-2
+GEMM_ACC = 1e-4
+CHAIN = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU parity tests need a GPU"
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(a, bits=None):
+    """numpy -> device; bf16 from its bit pattern when given."""
+    import torch
+    if bits is not None:
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(
+            torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def r(a):
+    return oracle.round_bf16(a).astype(np.float64)
+
+
+# (L, B, d, ndir, d'): ragged sizes, K = L*B from 1 to 2048 (split weight
+# products at 2048), the d' = d / 4 of the paper's figure
+CASES = [(3, 5, 64, 1, 16), (7, 19, 100, 2, 25), (2, 3, 37, 1, 9), (64, 4, 256, 2, 64),
+         (1, 1, 8, 1, 2), (32, 64, 128, 1, 32), (16, 128, 64, 2, 16)]
+
+
+@pytest.mark.parametrize("L,B,d,nd,di", CASES)
+def test_factored_products(L, B, d, nd, di):
+    import torch
+    inp = workloads.factored_inputs(L, B, d, nd, di, seed=600 + d + di)
+    shape = SruShape(L, B, d, nd == 2, 1.0)
+    M, n3 = L * B, nd * 3 * d
+    print(f"case M={M} d={d} d'={di} n3={n3}", flush=True)
+    X, Q, dU, dQ, Wq, Wo = (inp[k] for k in ("X", "Q", "dU", "dQ", "Wq", "Wo"))
+    Wq_d, Wo_d = dev(Wq, inp["Wq_bits"]), dev(Wo, inp["Wo_bits"])
+    f32 = dict(device="cuda", dtype=torch.float32)
+    # data products: (op, A, W (host), W (device), C shape, oracle on rounded / exact A)
+    prods = [
+        (SRU_FACT_Q, X, Wq, Wq_d, (M, di), lambda A: oracle.matmul(A, Wq, b_nk=True)),
+        (SRU_FACT_U, Q, Wo, Wo_d, (M, n3), lambda A: oracle.matmul(A, Wo, b_nk=True)),
+        (SRU_FACT_BWD_Q, dU, Wo, Wo_d, (M, di), lambda A: oracle.matmul(A, Wo)),
+        (SRU_FACT_BWD_X, dQ, Wq, Wq_d, (M, d), lambda A: oracle.matmul(A, Wq)),
+    ]
+    for op, A, W, Wd, cshape, ref in prods:
+        want_r, want = ref(r(A)), ref(A)
+        C = torch.empty(cshape, **f32)
+        sru_project_factored(shape, di, op, dev(A), Wd, C)
+        check(f"op {op} vs rounded-operand oracle", host(C), want_r, GEMM_ACC)
+        check(f"op {op} vs exact oracle", host(C), want, BF16_BAR)
+        Ab_bits, Ab = workloads.to_bf16(A)          # bf16 activations in HBM
+        sru_project_factored(shape, di, op, dev(Ab, Ab_bits), Wd, C)
+        check(f"op {op} (bf16 A)", host(C), ref(Ab), GEMM_ACC)
+        C0 = np.random.default_rng(op).standard_normal(cshape).astype(np.float32)
+        C = dev(C0.copy())
+        sru_project_factored(shape, di, op, dev(A), Wd, C, accumulate=True)
+        check(f"op {op} (+=)", host(C), want_r + C0, GEMM_ACC)
+        # fp32 weights: fp32 arithmetic
+        sru_project_factored(shape, di, op, dev(A), dev(W), C)
+        check(f"op {op} (fp32)", host(C), want, TIGHT)
+    # weight products
+    need = sru_workspace_size(shape, SRU_WS_FACTORED_WEIGHT, di)
+    ws = torch.empty(max(need, 256), device="cuda", dtype=torch.uint8)
+    for which, G, Y, wshape in ((SRU_FACT_WGRAD_Q, dQ, X, (di, d)),
+                                (SRU_FACT_WGRAD_O, dU, Q, (n3, di))):
+        dW = torch.empty(wshape, **f32)
+        sru_project_factored_bwd_weight(shape, di, which, dev(G), dev(Y), dW, SRU_BF16, False, ws)
+        check(f"wgrad {which} vs rounded-operand oracle", host(dW),
+              oracle.matmul(r(G), r(Y), a_km=True), GEMM_ACC)
+        check(f"wgrad {which} vs exact oracle", host(dW), oracle.matmul(G, Y, a_km=True),
+              BF16_BAR)
+        sru_project_factored_bwd_weight(shape, di, which, dev(G), dev(Y), dW, SRU_F32)
+        check(f"wgrad {which} (fp32)", host(dW), oracle.matmul(G, Y, a_km=True), TIGHT)
+
+
+@pytest.mark.parametrize("L,B,d,nd,di", [(7, 19, 100, 2, 25), (32, 64, 128, 1, 32),
+                                         (64, 4, 256, 2, 64)])
+def test_factored_chain(L, B, d, nd, di):
+    """layer.project_factored + project_factored_backward against the oracle's
+    factorised forward and backward (chained products)."""
+    inp = workloads.factored_inputs(L, B, d, nd, di, seed=700 + d)
+    shape = SruShape(L, B, d, nd == 2, 1.0)
+    M = L * B
+    X, dU, Wq, Wo = inp["X"], inp["dU"], inp["Wq"], inp["Wo"]
+    Xd, dUd = dev(X), dev(dU)
+    Wq_d, Wo_d = dev(Wq, inp["Wq_bits"]), dev(Wo, inp["Wo_bits"])
+    Q, U = layer.project_factored(shape, di, Xd, Wq_d, Wo_d)
+    dx0 = np.random.default_rng(1).standard_normal((L, B, d)).astype(np.float32)
+    dX = dev(dx0.copy())
+    dQ, dX, dWq, dWo = layer.project_factored_backward(shape, di, Xd, Q, Wq_d, Wo_d, dUd, dX,
+                                                       accumulate=True)
+    for round_ops, tol, tag in ((True, CHAIN, "rounded"), (False, BF16_BAR, "exact")):
+        fo = oracle.factored_project(X, Wq, Wo, round_ops)
+        bo = oracle.factored_project_backward(X, fo["Q"], Wq, Wo, dU, round_ops)
+        print(f" vs {tag} oracle", flush=True)
+        check("Q", host(Q), fo["Q"], GEMM_ACC if round_ops else BF16_BAR)
+        check("U", host(U).reshape(M, -1), fo["U"], tol)
+        check("dQ", host(dQ), bo["dQ"], GEMM_ACC if round_ops else BF16_BAR)
+        check("dX (+ highway dx)", host(dX).reshape(M, d), bo["dX"] + dx0.reshape(M, d), tol)
+        check("dWq", host(dWq), bo["dWq"], tol)
+        check("dWo", host(dWo), bo["dWo"], tol)
+
+
+def test_factored_alpha_zero_matches_single_projection():
+    """With fp32 weights the factorised map equals Eq. 1's projection with the
+    product weight Wo Wq (associativity), here run through sru_project."""
+    import torch
+    from parallelizable_recurrent_units_amd import SRU_PROJ_FWD, sru_project
+    L, B, d, nd, di = 16, 8, 64, 1, 16
+    inp = workloads.factored_inputs(L, B, d, nd, di, seed=801, w_dtype="f32")
+    shape = SruShape(L, B, d, False, 1.0)
+    X, Wq, Wo = dev(inp["X"]), dev(inp["Wq"]), dev(inp["Wo"])
+    _, U = layer.project_factored(shape, di, X, Wq, Wo)
+    Wc = (inp["Wo"].astype(np.float64) @ inp["Wq"].astype(np.float64)).astype(np.float32)
+    U1 = torch.empty_like(U)
+    sru_project(shape, SRU_PROJ_FWD, X, dev(Wc), U1)
+    check("factored vs single projection (fp32)", host(U), host(U1), TIGHT)
+
+
+def test_factored_workload_sampled():
+    """The paper's proportion d' = d / 4 at the L=512 B=32 d=1024 training
+    shape: sampled rows of every output against the oracle."""
+    import torch
+    L, B, d, nd, di = 512, 32, 1024, 1, 256
+    M, n3 = L * B, nd * 3 * d
+    inp = workloads.factored_inputs(L, B, d, nd, di, seed=900)
+    shape = SruShape(L, B, d, False, 1.0)
+    X, dU, Wq, Wo = inp["X"], inp["dU"], inp["Wq"], inp["Wo"]
+    Xd, dUd = dev(X), dev(dU)
+    Q, U = layer.project_factored(shape, di, Xd, dev(Wq, inp["Wq_bits"]),
+                                  dev(Wo, inp["Wo_bits"]))
+    dQ, dX, dWq, dWo = layer.project_factored_backward(shape, di, Xd, Q, dev(Wq, inp["Wq_bits"]),
+                                                       dev(Wo, inp["Wo_bits"]), dUd)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(901)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 30)]))
+    Xr, dUr = r(X), r(dU)
+    Qs = oracle.matmul(Xr[rows], Wq, b_nk=True)
+    check("Q (sampled rows)", host(Q)[rows], Qs, GEMM_ACC)
+    check("U (sampled rows)", host(U).reshape(M, -1)[rows], oracle.matmul(r(Qs), Wo, b_nk=True),
+          CHAIN)
+    dQs = oracle.matmul(dUr[rows], Wo)
+    check("dQ (sampled rows)", host(dQ)[rows], dQs, GEMM_ACC)
+    check("dX (sampled rows)", host(dX).reshape(M, d)[rows], oracle.matmul(r(dQs), Wq), CHAIN)
+    # dWq rows k: need column k of dQ over all M; dWo rows n: need all of Q
+    ks = np.unique(np.concatenate([[0, di - 1], rng.integers(0, di, 6)]))
+    dQ_cols = oracle.matmul(dUr, np.ascontiguousarray(Wo[:, ks]))
+    check("dWq (sampled rows)", host(dWq)[ks], oracle.matmul(r(dQ_cols), Xr, a_km=True), CHAIN)
+    ns = np.unique(np.concatenate([[0, n3 - 1], rng.integers(0, n3, 6)]))
+    Q_all = oracle.matmul(Xr, Wq, b_nk=True)
+    check("dWo (sampled rows)", host(dWo)[ns],
+          oracle.matmul(np.ascontiguousarray(dUr[:, ns]), r(Q_all), a_km=True), CHAIN)
