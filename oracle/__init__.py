@@ -24,7 +24,11 @@ closed form, brute-force unrolled recurrences at L <= 4, central finite
 differences for every gradient, the bidirectional time-flip invariant,
 channel/batch permutation equivariance, and for the factorised projection
 associativity (one projection with the product weight), hand-computed bf16
-rounding of X and Q, and central differences.
+rounding of X and Q, and central differences; for the SRU++ attention, the
+uniform-weight average, the single visible key, the two-key sigmoid form,
+saturation, convexity and key-permutation invariance, rounded weights, the
+layer-norm closed form, and the pages' alpha = 0 reduction to the factorised
+projection.
 """
 import ctypes
 import os
@@ -81,6 +85,11 @@ def _load():
     lib.sru_oracle_matmul.restype = None
     lib.sru_oracle_matmul.argtypes = [_i64, _i64, _i64, _dp, ctypes.c_int, _dp, ctypes.c_int,
                                       _dp]
+    lib.sru_oracle_attention.restype = None
+    lib.sru_oracle_attention.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, _dp, _dp, _dp,
+                                         ctypes.c_int, _dp]
+    lib.sru_oracle_layernorm.restype = None
+    lib.sru_oracle_layernorm.argtypes = [_i64, _i64, _dp, _dp, _dp, ctypes.c_double, _dp]
     lib.sru_oracle_num_threads.restype = ctypes.c_int
     lib.sru_oracle_num_threads.argtypes = []
     _lib = lib
@@ -306,3 +315,56 @@ def chain_inputs_from_projection(X, W, round_x, L, B, d, ndir, direction, b, j):
     cols = [(direction * 3 + g) * d + j for g in range(3)]
     u = project(np.asarray(X, np.float32).reshape(L * B, d), W, round_x, rows=rows, cols=cols)
     return u[:, 0], u[:, 1], u[:, 2]
+
+
+def attention(Q, K, V, mem_len: int, causal: bool, round_p: bool = False) -> np.ndarray:
+    """Single-head scaled dot-product attention of an SRU++ layer.  Q [L, B, d'];
+    K, V [mem_len + L, B, d'] (the previous segment's rows first).  Returns
+    A [L, B, d'] (see sru_oracle_attention)."""
+    Q, pq = _f64(Q)
+    K, pk = _f64(K)
+    V, pv = _f64(V)
+    L, B, dp = Q.shape
+    assert K.shape == (mem_len + L, B, dp) and V.shape == K.shape
+    A = np.empty_like(Q)
+    _load().sru_oracle_attention(L, B, dp, int(mem_len), int(bool(causal)), pq, pk, pv,
+                                 int(bool(round_p)), A.ctypes.data_as(_dp))
+    return A
+
+
+def layernorm(x, gamma, beta, eps: float) -> np.ndarray:
+    """Layer normalisation over the last dimension (biased variance)."""
+    x, px = _f64(x)
+    g, pg = _f64(gamma)
+    b, pb = _f64(beta)
+    w = x.shape[-1]
+    y = np.empty_like(x)
+    _load().sru_oracle_layernorm(x.size // w, w, px, pg, pb, float(eps), y.ctypes.data_as(_dp))
+    return y
+
+
+def attention_project(X, Wq, Wk, Wv, Wo, L, B, alpha, mem_len=0, Kmem=None, Vmem=None,
+                      causal=True, ln=None, round_ops=False):
+    """The U-producer of an SRU++ layer (SRU++ paper, section on SRU++):
+    Q = Xt Wq^T, K = Qt Wk^T, V = Qt Wv^T over this segment's L steps (the
+    previous segment's keys and values Kmem, Vmem [mem_len, B, d'] in front),
+    A = attention(Q, K, V), R = Q + alpha A, optionally R <- layernorm(R)
+    (ln = (gamma, beta, eps)), U = Rt Wo^T.  X is [L*B, d]; returns a dict
+    with Q, K, V (all rows, memory included), A, R, U as [L*B, .] or
+    [Lk, B, .] arrays.  round_ops rounds every product's activation operand to
+    bf16 and the attention weights p to bf16, as the bf16 GPU path does."""
+    dp = Wq.shape[0]
+    Q = matmul(_maybe_bf16(X, round_ops), Wq, b_nk=True)
+    Qt = _maybe_bf16(Q, round_ops)
+    Kc = matmul(Qt, Wk, b_nk=True).reshape(L, B, dp)
+    Vc = matmul(Qt, Wv, b_nk=True).reshape(L, B, dp)
+    if mem_len:
+        Kc = np.concatenate([np.asarray(Kmem, np.float64), Kc])
+        Vc = np.concatenate([np.asarray(Vmem, np.float64), Vc])
+    A = attention(_maybe_bf16(Q, round_ops).reshape(L, B, dp), _maybe_bf16(Kc, round_ops),
+                  _maybe_bf16(Vc, round_ops), mem_len, causal, round_p=round_ops)
+    R = Q + alpha * A.reshape(L * B, dp)
+    if ln is not None:
+        R = layernorm(R, ln[0], ln[1], ln[2])
+    U = matmul(_maybe_bf16(R, round_ops), Wo, b_nk=True)
+    return {"Q": Q, "K": Kc, "V": Vc, "A": A.reshape(L * B, dp), "R": R, "U": U}

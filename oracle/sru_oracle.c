@@ -23,6 +23,10 @@
  *   The factorised projection (same paper, Fig. 2(b)): U = W_o (W_q X) with a
  *   small inner dimension d'; it and its gradients are plain products
  *   (sru_oracle_matmul).
+ *   The SRU++ attention that produces U (same paper, section on SRU++):
+ *   Q = W_q X^T, K = W_k Q, V = W_v Q, A^T = softmax(Q^T K / sqrt(d')) V^T,
+ *   U^T = W_o (Q + alpha A), optionally with layer normalisation of
+ *   Q + alpha A (sru_oracle_attention, sru_oracle_layernorm, and products).
  *
  * Readings taken where the pages are silent (each is listed in the design
  * notes of the repository):
@@ -114,6 +118,93 @@ void sru_oracle_matmul(int64_t M, int64_t N, int64_t K, const double *A, int a_k
             }
             C[m * N + n] = s;
         }
+    }
+}
+
+/*
+ * The attention of an SRU++ layer (SRU++ paper, section on SRU++): single
+ * head, scaled dot product.  For every sequence b and query step t:
+ *   s_j = (Q[t] . K[j]) / sqrt(dp)  over the keys j the query may see,
+ *   p_j = exp(s_j - max s) / sum_i exp(s_i - max s),
+ *   A[t] = sum_j p_j V[j].
+ * Keys and values are [Lk, B, dp] with Lk = Lm + L: the first Lm rows are the
+ * previous segment's (context carried over, the paper's training setup) and
+ * row Lm + t belongs to step t of this segment.  Without `causal` every query
+ * sees all Lk keys; with it, query t sees keys j <= Lm + t.
+ * round_p != 0: p_j is rounded to bf16 after normalisation, the value the
+ * GPU path multiplies (the sum then uses the rounded weights).
+ * Q [L, B, dp]; A [L, B, dp].  Every (b, t) is independent.
+ */
+void sru_oracle_attention(int64_t L, int64_t B, int64_t dp, int64_t Lm, int causal,
+                          const double *Q, const double *K, const double *V, int round_p,
+                          double *A)
+{
+    const int64_t Lk = Lm + L;
+    const double scale = 1.0 / sqrt((double)dp);
+#pragma omp parallel
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)Lk);
+#pragma omp for schedule(static)
+        for (int64_t bt = 0; bt < L * B; ++bt) {
+            const int64_t t = bt / B, b = bt % B;
+            const double *q = Q + (t * B + b) * dp;
+            const int64_t nk = causal ? Lm + t + 1 : Lk;
+            double mx = -INFINITY;
+            for (int64_t j = 0; j < nk; ++j) {
+                const double *k = K + (j * B + b) * dp;
+                double s = 0.0;
+                for (int64_t e = 0; e < dp; ++e)
+                    s += q[e] * k[e];
+                p[j] = s * scale;
+                if (p[j] > mx)
+                    mx = p[j];
+            }
+            double l = 0.0;
+            for (int64_t j = 0; j < nk; ++j) {
+                p[j] = exp(p[j] - mx);
+                l += p[j];
+            }
+            for (int64_t j = 0; j < nk; ++j) {
+                p[j] /= l;
+                if (round_p)
+                    p[j] = (double)sru_oracle_round_bf16((float)p[j]);
+            }
+            double *a = A + (t * B + b) * dp;
+            for (int64_t e = 0; e < dp; ++e)
+                a[e] = 0.0;
+            for (int64_t j = 0; j < nk; ++j) {
+                const double *v = V + (j * B + b) * dp;
+                for (int64_t e = 0; e < dp; ++e)
+                    a[e] += p[j] * v[e];
+            }
+        }
+        free(p);
+    }
+}
+
+/*
+ * Layer normalisation over the last dimension (Ba et al.; the SRU++ paper
+ * applies it to Q + alpha A before the output projection): for each of the
+ * n rows of width w, y = gamma * (x - mean) / sqrt(var + eps) + beta with the
+ * biased variance (mean of squared deviations).
+ */
+void sru_oracle_layernorm(int64_t n, int64_t w, const double *x, const double *gamma,
+                          const double *beta, double eps, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        const double *r = x + i * w;
+        double mean = 0.0;
+        for (int64_t e = 0; e < w; ++e)
+            mean += r[e];
+        mean /= (double)w;
+        double var = 0.0;
+        for (int64_t e = 0; e < w; ++e)
+            var += (r[e] - mean) * (r[e] - mean);
+        var /= (double)w;
+        const double inv = 1.0 / sqrt(var + eps);
+        for (int64_t e = 0; e < w; ++e)
+            y[i * w + e] = gamma[e] * (r[e] - mean) * inv + beta[e];
     }
 }
 

@@ -505,3 +505,108 @@ def test_permutation_equivariance():
                         c0[:, pb][..., pj], 1.0)
     assert np.array_equal(o2["h"], o["h"][:, pb][..., pj])
     assert np.array_equal(o2["c_last"], o["c_last"][:, pb][..., pj])
+
+
+# --------------------------------------------------------------------------
+# SRU++ attention (the U-producer)
+# --------------------------------------------------------------------------
+
+def _attn_inputs(L, B, dp, Lm, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((L, B, dp)), rng.standard_normal((Lm + L, B, dp)),
+            rng.standard_normal((Lm + L, B, dp)))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_zero_keys_average_the_visible_values(causal):
+    """All scores equal -> uniform weights: A[t] is the mean of the values
+    the query may see (all Lm + L, or the first Lm + t + 1 when causal)."""
+    L, B, dp, Lm = 6, 3, 5, 2
+    Q, K, V = _attn_inputs(L, B, dp, Lm, 30)
+    A = oracle.attention(Q, np.zeros_like(K), V, Lm, causal)
+    for t in range(L):
+        n = Lm + t + 1 if causal else Lm + L
+        np.testing.assert_allclose(A[t], V[:n].mean(axis=0), rtol=1e-13, atol=1e-14)
+
+
+def test_attention_first_causal_query_copies_first_value():
+    L, B, dp = 4, 2, 3
+    Q, K, V = _attn_inputs(L, B, dp, 0, 31)
+    A = oracle.attention(Q, K, V, 0, True)
+    np.testing.assert_array_equal(A[0], V[0])
+
+
+def test_attention_two_keys_closed_form():
+    """One query, two keys: weights sigma(s0 - s1) and 1 - sigma(s0 - s1)."""
+    q = np.array([[[0.5, -1.0, 2.0, 0.25]]])
+    k = np.array([[[1.0, 0.0, 0.5, -2.0]], [[-0.5, 1.5, 0.0, 1.0]]])
+    v = np.array([[[2.0, -1.0, 0.0, 3.0]], [[-4.0, 0.5, 1.0, 1.0]]])
+    s0, s1 = (q[0, 0] @ k[0, 0]) / 2.0, (q[0, 0] @ k[1, 0]) / 2.0   # sqrt(4) = 2
+    w0 = 1.0 / (1.0 + math.exp(-(s0 - s1)))
+    want = w0 * v[0, 0] + (1.0 - w0) * v[1, 0]
+    got = oracle.attention(q, k, v, 1, False)          # key 0 is the memory row
+    np.testing.assert_allclose(got[0, 0], want, rtol=1e-14, atol=1e-15)
+    # causal: the current row (key 1) is the query's own step, so both are seen
+    np.testing.assert_allclose(oracle.attention(q, k, v, 1, True)[0, 0], want, rtol=1e-14)
+
+
+def test_attention_saturated_score_selects_one_value():
+    L, B, dp = 3, 1, 4
+    Q, K, V = _attn_inputs(L, B, dp, 0, 32)
+    K[1, 0] = 200.0 * Q[2, 0]                  # query 2 scores key 1 far above the rest
+    A = oracle.attention(Q, K, V, 0, False)
+    np.testing.assert_allclose(A[2, 0], V[1, 0], rtol=1e-12, atol=1e-12)
+
+
+def test_attention_convex_and_key_permutation_invariant():
+    L, B, dp, Lm = 5, 2, 6, 3
+    Q, K, V = _attn_inputs(L, B, dp, Lm, 33)
+    A = oracle.attention(Q, K, V, Lm, False)
+    assert np.all(A <= V.max(axis=0)[None] + 1e-12) and np.all(A >= V.min(axis=0)[None] - 1e-12)
+    perm = np.random.default_rng(34).permutation(Lm + L)
+    np.testing.assert_allclose(oracle.attention(Q, K[perm], V[perm], Lm, False), A,
+                               rtol=1e-12, atol=1e-13)
+    bperm = np.array([1, 0])
+    np.testing.assert_allclose(oracle.attention(Q[:, bperm], K[:, bperm], V[:, bperm], Lm, False),
+                               A[:, bperm], rtol=0, atol=0)
+
+
+def test_attention_rounded_weights_closed_form():
+    """Three visible keys with equal scores: each weight 1/3 becomes
+    bf16(1/3) = 0.333984375 before the sum."""
+    q = np.zeros((1, 1, 2))
+    k = np.zeros((3, 1, 2))
+    v = np.full((3, 1, 2), 1.5)
+    got = oracle.attention(q, k, v, 2, True, round_p=True)
+    assert got[0, 0, 0] == 3 * 0.333984375 * 1.5
+
+
+def test_layernorm_closed_form():
+    """[a, b] normalises to [-1, 1] * h / sqrt(h^2 + eps) with h = (b - a) / 2,
+    then scale and shift; with unit gain and zero shift every row has mean 0
+    and variance var / (var + eps)."""
+    eps = 1e-5
+    y = oracle.layernorm(np.array([[1.0, 4.0]]), np.array([2.0, 3.0]), np.array([0.5, -1.0]), eps)
+    h = 1.5
+    n = h / math.sqrt(h * h + eps)
+    np.testing.assert_allclose(y[0], [2.0 * -n + 0.5, 3.0 * n - 1.0], rtol=1e-15)
+    x = np.random.default_rng(35).standard_normal((4, 9)) * 3 + 1
+    z = oracle.layernorm(x, np.ones(9), np.zeros(9), eps)
+    np.testing.assert_allclose(z.mean(axis=1), 0.0, atol=1e-14)
+    v = x.var(axis=1)
+    np.testing.assert_allclose(z.var(axis=1), v / (v + eps), rtol=1e-13)
+
+
+def test_attention_project_alpha_zero_is_the_factorised_projection():
+    """The pages' own special case: with alpha = 0 (its initial value), the
+    attention drops out and U = Wo Wq X, the factorised projection."""
+    rng = np.random.default_rng(36)
+    L, B, d, dp = 4, 3, 8, 4
+    X = rng.standard_normal((L * B, d)).astype(np.float32)
+    Wq, Wk, Wv = (rng.standard_normal((dp, n)) for n in (d, dp, dp))
+    Wo = rng.standard_normal((3 * d, dp))
+    for round_ops in (False, True):
+        a = oracle.attention_project(X, Wq, Wk, Wv, Wo, L, B, 0.0, round_ops=round_ops)
+        f = oracle.factored_project(X, Wq, Wo, round_ops)
+        np.testing.assert_array_equal(a["U"], f["U"])
+        np.testing.assert_array_equal(a["Q"], f["Q"])
