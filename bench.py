@@ -21,7 +21,9 @@ workload sizes (given-U bf16 forward, the L=512 training step, the linear-mode
 chunked scan) are included.  ``beyond_step`` times, after the step and on its
 buffers, rows that are not part of the step: the projection's weight gradient
 dW = bf16(dU)^T X~, and the factorised projection U = Wo (Wq X~) with d' = d/4
-(SRU++ paper, Fig. 2(b)), forward and backward.
+(SRU++ paper, Fig. 2(b)), forward and backward; at the given-U workload, the
+SRU++ attention that would produce that U (causal, previous segment as
+context, layer norm).
 """
 import argparse
 import hashlib
@@ -102,7 +104,7 @@ def next_row_work(w):
     the projection, dW = bf16(dU)^T X~ (dU's bf16 copy and X read once, dW
     written once)."""
     if w.mode != "layer":
-        return {}
+        return attention_work(w) if not w.linear else {}
     L, B, d, nd = w.L, w.B, w.d, w.ndir
     LB, n3 = L * B, nd * 3 * d
     xs = 2 if w.x_dtype == "bf16" else 4
@@ -119,6 +121,24 @@ def next_row_work(w):
                                              bytes=LB * n3 * 2 + LB * d * xs + n3 * d * 4),
             "f3_factored_forward": dict(flops=fwd_flops, bytes=fwd_bytes),
             "f3_factored_backward": dict(flops=bwd_flops, bytes=bwd_bytes)}
+
+
+ATTN_CONTEXT = 1.0   # previous-segment context length, in units of L
+
+
+def attention_work(w):
+    """The SRU++ attention producing this workload's U: d' = d / 4, causal,
+    the previous segment (L steps) as context.  Flops count the visible
+    (query, key) pairs only; bytes count X, the weights, Q, the keys and
+    values (written once for this segment, read once for all Lm + L steps),
+    R and U, not the scores the kernels keep in a workspace."""
+    L, B, d, nd = w.L, w.B, w.d, w.ndir
+    dp, Lm, n3, LB = max(1, d // 4), int(ATTN_CONTEXT * L), nd * 3 * d, L * B
+    pairs = B * (L * Lm + L * (L + 1) // 2)
+    flops = (2 * LB * d * dp + 2 * LB * dp * 2 * dp + 4 * pairs * dp + 2 * LB * dp * n3)
+    byts = (LB * d * 4 + (dp * d + 2 * dp * dp + n3 * dp) * 2 + LB * dp * 4
+            + LB * 2 * dp * 2 + (Lm + L) * B * 2 * dp * 2 + LB * dp * 4 + LB * n3 * 4)
+    return {"f2_attention_forward": dict(flops=flops, bytes=byts)}
 
 
 def factored_inner(w):
@@ -270,6 +290,30 @@ def time_rows(row_sets, steps, warmup):
     return total_ms / steps, per_row
 
 
+def attention_rows(w, shape, g):
+    """The SRU++ attention that would produce this workload's U (one buffer
+    set): X ~ N(0, 1), bf16 weights ~ U(-0.05, 0.05), layer norm on, the
+    previous segment's keys and values ~ N(0, 1) in front."""
+    import torch
+    from parallelizable_recurrent_units_amd import (SruAttnCfg, sru_attention_forward,
+                                                    sru_attention_workspace_size)
+    L, B, d, nd = w.L, w.B, w.d, w.ndir
+    dp, Lm = max(1, d // 4), int(ATTN_CONTEXT * L)
+    f32 = dict(device="cuda", dtype=torch.float32)
+    wt = lambda r, c: ((torch.rand((r, c), generator=g, **f32) - 0.5) * 0.1).to(torch.bfloat16)
+    cfg = SruAttnCfg(dp, Lm, True, True, 1.0, 1e-5)
+    X = torch.randn((L * B, d), generator=g, **f32)
+    Wq, Wkv, Wo = wt(dp, d), wt(2 * dp, dp), wt(nd * 3 * d, dp)
+    gamma, beta = torch.ones(dp, **f32), torch.zeros(dp, **f32)
+    KV = torch.randn((Lm + L, B, 2 * dp), generator=g, **f32).to(torch.bfloat16)
+    Q, R = torch.empty((L * B, dp), **f32), torch.empty((L * B, dp), **f32)
+    U = torch.empty((L, B, nd, 3, d), **f32)
+    ws = torch.empty(sru_attention_workspace_size(shape, cfg), device="cuda", dtype=torch.uint8)
+    return [("f2_attention_forward",
+             lambda: sru_attention_forward(shape, cfg, X, Wq, Wkv, Wo, gamma, beta, Q, KV, R, U,
+                                           ws))]
+
+
 class RowSet(list):
     """One set's step rows [(row, fn)], plus ``beyond``: rows timed after the
     step on the same buffers."""
@@ -303,8 +347,9 @@ def row_sets_for(w, nsets, seed0):
             b = torch.zeros((1, 2, w.d), **f32)
             h = torch.empty((w.L, w.B, 1, w.d), **f32)
             cl = torch.empty((1, w.B, w.d), **f32)
-            out.append([("a2_forward", (lambda U=U, x=x, v=v, b=b, h=h, cl=cl:
-                                        sru_forward(s, U, x, v, b, None, h, None, cl)))])
+            out.append(RowSet([("a2_forward", (lambda U=U, x=x, v=v, b=b, h=h, cl=cl:
+                                               sru_forward(s, U, x, v, b, None, h, None, cl)))]))
+        out[0].beyond = attention_rows(w, s, g)
         return out
     # linear mode, chunk 256: U_f ~ N(2,1), U_r, U_x, x, dh ~ N(0,1), b = 0, c0 = 0.
     # One set: a single call's working set (>= 6 GB) is far beyond every cache.
@@ -349,9 +394,10 @@ def measure(w, nsets, steps, warmup, seed0):
 def time_beyond(w, sets, steps, warmup):
     """{row: measurement} of the rows beyond the step (after the step has run
     on every set, so their inputs hold a step's results)."""
-    if not sets or not getattr(sets[0], "beyond", ()):
+    beyond = [s.beyond for s in sets if getattr(s, "beyond", ())]
+    if not beyond:
         return {}
-    _, rows = time_rows([s.beyond for s in sets], steps, warmup)
+    _, rows = time_rows(beyond, steps, warmup)
     work = next_row_work(w)
     return {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
 
@@ -420,6 +466,11 @@ ROW_LAUNCHES = {
                                  "along L*B; the reduction split over blocks)",
                                  "split_reduce (partial sums added in split order)"],
     "f3_factored_forward": ["gemm_bf16_mfma (Q = X Wq^T)", "gemm_bf16_mfma (U = Q Wo^T)"],
+    "f2_attention_forward": ["gemm_bf16_mfma (Q = X Wq^T)", "gemm_bf16_mfma ([K|V] = Q Wkv^T, "
+                             "bf16 out)", "gemm_bf16_mfma (scores, one batch per sequence)",
+                             "attn_softmax", "gemm_bf16_mfma (weights x V, batched)",
+                             "attn_residual (R = layernorm(Q + alpha A))",
+                             "gemm_bf16_mfma (U = R Wo^T)"],
     "f3_factored_backward": ["gemm_bf16_mfma (dQ = bf16(dU) Wo)", "gemm_bf16_mfma (dx += dQ Wq)",
                              "gemm_bf16_mfma + split_reduce (dWq = dQ^T X)",
                              "gemm_bf16_mfma + split_reduce (dWo = bf16(dU)^T Q)"],

@@ -100,6 +100,19 @@ typedef struct {
     float alpha;             /* highway scale; 1 reproduces Eq. 5 */
 } sru_shape;
 
+/* Options of the SRU++ attention (sru_attention_forward). */
+typedef struct {
+    int64_t d_inner;         /* attention dimension d' >= 1                        */
+    int64_t mem_len;         /* Lm >= 0: the previous segment's steps in front of
+                                this segment's keys and values                      */
+    int32_t causal;          /* 1: step t sees the Lm context steps and steps <= t;
+                                0: every step sees all Lm + L                       */
+    int32_t layernorm;       /* 1: R = layernorm(Q + alpha A) with gamma, beta      */
+    float attn_alpha;        /* alpha of the residual Q + alpha A (learned scalar,
+                                initially 0 in the paper)                           */
+    float ln_eps;            /* layer-norm epsilon (> 0 when layernorm = 1)         */
+} sru_attn_cfg;
+
 /*
  * Projection, Eq. 1 (SRU++ paper, background section): all three gate
  * matrices of both directions and all timesteps in one GEMM.
@@ -179,6 +192,41 @@ sru_status sru_project_factored_bwd_weight(const sru_shape *shape, int64_t d_inn
                                            float *dW, sru_dtype math_dt, int32_t accumulate,
                                            void *workspace, size_t workspace_bytes,
                                            void *stream);
+
+/*
+ * The U-producer of an SRU++ layer (SRU++ paper, section on SRU++): single
+ * head scaled dot-product attention, then the output projection:
+ *   Q = X~ Wq^T                         Q  fp32 [L*B, d'] (written)
+ *   [K | V] = Q~ [Wk; Wv]^T             KV bf16 [Lm + L, B, 2d']: rows t < Lm
+ *                                       are read (the previous segment's keys
+ *                                       and values, context the paper's
+ *                                       training carries over); rows Lm + t
+ *                                       are written for this segment's steps
+ *   A_b = softmax(Q~_b K~_b^T / sqrt(d')) V~_b   per sequence b, with the
+ *                                       visibility of sru_attn_cfg.causal
+ *   R = Q + alpha A, or layernorm(Q + alpha A) (biased variance, gain gamma,
+ *       shift beta, both fp32 [d'])    R  fp32 [L*B, d'] (written)
+ *   U = R~ Wo^T                         U  fp32 [L, B, ndir, 3, d] (written)
+ * X [L*B, d] fp32 or bf16 (x_dt).  Wq [d', d], Wkv [2d', d'] (Wk's rows, then
+ * Wv's), Wo [ndir*3d, d']: bf16 only.  "~" marks operands rounded to bf16
+ * (nearest even) as the bf16 MFMA products load them; the attention weights
+ * are rounded to bf16 before they multiply V.  The softmax and the
+ * residual / normalisation are fp32.
+ * gamma, beta: required when cfg->layernorm, else ignored (may be NULL).
+ * workspace: sru_attention_workspace_size(shape, cfg) bytes, 256-byte
+ *   aligned: the scores [B, L, Lm + L] (fp32), the weights (bf16) and A.
+ * Outputs must not overlap each other or the inputs.
+ */
+sru_status sru_attention_forward(const sru_shape *shape, const sru_attn_cfg *cfg,
+                                 const void *X, sru_dtype x_dt,
+                                 const void *Wq, const void *Wkv, const void *Wo,
+                                 const float *gamma, const float *beta,
+                                 float *Q, void *KV, float *R, float *U,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of sru_attention_forward; 0 on invalid arguments
+ * (sru_last_error() says why). */
+size_t sru_attention_workspace_size(const sru_shape *shape, const sru_attn_cfg *cfg);
 
 /*
  * Forward recurrence, Eqs. 2-5, for every (direction, batch, channel) chain.

@@ -26,7 +26,8 @@ SRU_FACT_WGRAD_Q, SRU_FACT_WGRAD_O = 0, 1
 
 # Every symbol include/sru.h declares.
 EXPORTED = ("sru_project", "sru_project_bwd_weight", "sru_project_factored",
-            "sru_project_factored_bwd_weight", "sru_forward", "sru_backward", "sru_linear_scan",
+            "sru_project_factored_bwd_weight", "sru_attention_forward",
+            "sru_attention_workspace_size", "sru_forward", "sru_backward", "sru_linear_scan",
             "sru_transpose_weight", "sru_workspace_size", "sru_status_string", "sru_last_error")
 
 
@@ -44,6 +45,17 @@ class SruShape(ctypes.Structure):
     def __repr__(self):
         return (f"SruShape(L={self.L}, B={self.B}, d={self.d}, "
                 f"bidirectional={bool(self.bidirectional)}, alpha={self.alpha})")
+
+
+class SruAttnCfg(ctypes.Structure):
+    _fields_ = [("d_inner", ctypes.c_int64), ("mem_len", ctypes.c_int64),
+                ("causal", ctypes.c_int32), ("layernorm", ctypes.c_int32),
+                ("attn_alpha", ctypes.c_float), ("ln_eps", ctypes.c_float)]
+
+    def __init__(self, d_inner, mem_len=0, causal=True, layernorm=False, attn_alpha=0.0,
+                 ln_eps=1e-5):
+        super().__init__(int(d_inner), int(mem_len), int(bool(causal)), int(bool(layernorm)),
+                         float(attn_alpha), float(ln_eps))
 
 
 class SruError(RuntimeError):
@@ -80,6 +92,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sru_project_factored_bwd_weight.argtypes = [sp, ctypes.c_int64, ctypes.c_int, _vp,
                                                     ctypes.c_int, _vp, ctypes.c_int, _vp,
                                                     ctypes.c_int, i32, _vp, sz, _vp]
+    cp = ctypes.POINTER(SruAttnCfg)
+    lib.sru_attention_forward.restype = ctypes.c_int
+    lib.sru_attention_forward.argtypes = [sp, cp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
+                                          _vp, _vp, _vp, _vp, _vp, sz, _vp]
+    lib.sru_attention_workspace_size.restype = sz
+    lib.sru_attention_workspace_size.argtypes = [sp, cp]
     lib.sru_forward.restype = ctypes.c_int
     lib.sru_forward.argtypes = [sp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
                                 ctypes.c_int, _vp, _vp, _vp]
@@ -184,6 +202,31 @@ def sru_project_factored_bwd_weight(shape, d_inner: int, which: int, G, Y, dW,
     _check(load_library().sru_project_factored_bwd_weight(
         ctypes.byref(s), int(d_inner), int(which), _ptr(G), _dtype_code(G), _ptr(Y),
         _dtype_code(Y), _ptr(dW), int(math_dtype), int(bool(accumulate)), _ptr(workspace),
+        ws_bytes, _stream(stream)))
+
+
+def sru_attention_workspace_size(shape, cfg) -> int:
+    s = _shape(shape)
+    n = load_library().sru_attention_workspace_size(ctypes.byref(s), ctypes.byref(cfg))
+    if n == 0:
+        raise SruError(SRU_ERR_INVALID_ARG, "SRU_ERR_INVALID_ARG",
+                       load_library().sru_last_error().decode())
+    return int(n)
+
+
+def sru_attention_forward(shape, cfg, X, Wq, Wkv, Wo, gamma, beta, Q, KV, R, U, workspace,
+                          stream=None):
+    s = _shape(shape)
+    for name, t in (("Wq", Wq), ("Wkv", Wkv), ("Wo", Wo), ("KV", KV)):
+        if _dtype_code(t) != SRU_BF16:
+            raise TypeError(f"{name} must be bfloat16")
+    for name, t in (("Q", Q), ("R", R), ("U", U)):
+        if _dtype_code(t) != SRU_F32:
+            raise TypeError(f"{name} must be float32")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().sru_attention_forward(
+        ctypes.byref(s), ctypes.byref(cfg), _ptr(X), _dtype_code(X), _ptr(Wq), _ptr(Wkv),
+        _ptr(Wo), _ptr(gamma), _ptr(beta), _ptr(Q), _ptr(KV), _ptr(R), _ptr(U), _ptr(workspace),
         ws_bytes, _stream(stream)))
 
 

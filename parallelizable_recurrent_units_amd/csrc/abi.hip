@@ -354,6 +354,124 @@ sru_status sru_project_factored_bwd_weight(const sru_shape *shape, int64_t d_inn
     return fail(SRU_ERR_INVALID_ARG, "unknown factored weight gradient %d", (int)which);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validates the attention options and the sizes derived from them.
+sru_status check_attn(const sru_shape *shape, const sru_attn_cfg *cfg, Dims *dm)
+{
+    SRU_TRY(check_shape(shape, dm));
+    if (!cfg) return fail(SRU_ERR_INVALID_ARG, "cfg is NULL");
+    if (cfg->d_inner < 1)
+        return fail(SRU_ERR_INVALID_ARG, "d_inner must be >= 1 (got %lld)",
+                    (long long)cfg->d_inner);
+    if (cfg->mem_len < 0)
+        return fail(SRU_ERR_INVALID_ARG, "mem_len must be >= 0 (got %lld)",
+                    (long long)cfg->mem_len);
+    if (cfg->causal != 0 && cfg->causal != 1)
+        return fail(SRU_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (cfg->layernorm != 0 && cfg->layernorm != 1)
+        return fail(SRU_ERR_INVALID_ARG, "layernorm must be 0 or 1");
+    if (!isfinite(cfg->attn_alpha)) return fail(SRU_ERR_INVALID_ARG, "attn_alpha must be finite");
+    if (cfg->layernorm && !(cfg->ln_eps > 0.0f && isfinite(cfg->ln_eps)))
+        return fail(SRU_ERR_INVALID_ARG, "ln_eps must be finite and > 0");
+    const int64_t L = shape->L, B = shape->B, dp = cfg->d_inner;
+    int64_t lk, s1, s2, kv, q;
+    if (!mul_ok(cfg->mem_len + L, B, &lk) || !mul_ok(lk, 2 * dp, &kv) || !mul_ok(dm->LB, dp, &q) ||
+        !mul_ok(B * L, cfg->mem_len + L, &s1) || !mul_ok(s1, 4, &s2) ||
+        !mul_ok(dp, shape->d, &q) || !mul_ok(3 * dm->ndir * shape->d, dp, &q))
+        return fail(SRU_ERR_INVALID_ARG, "attention sizes overflow");
+    // grids: per-sequence products batch over blockIdx.y; one wave per row
+    if (B > 65535) return fail(SRU_ERR_INVALID_ARG, "B must be <= 65535 for the attention");
+    if ((s1 + 3) / 4 > kMaxBlocks || (dm->LB + 63) / 64 > kMaxBlocks ||
+        (3 * dm->ndir * shape->d + 63) / 64 > 65535 || (2 * dp + 63) / 64 > 65535 ||
+        (cfg->mem_len + L + 63) / 64 > 65535)
+        return fail(SRU_ERR_INVALID_ARG, "attention too large for one launch");
+    return SRU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sru_attention_workspace_size(const sru_shape *shape, const sru_attn_cfg *cfg)
+{
+    Dims dm;
+    if (check_attn(shape, cfg, &dm) != SRU_OK) return 0;
+    ok();
+    return round256(
+        sru::attention_workspace_bytes(shape->L, shape->B, cfg->d_inner, cfg->mem_len));
+}
+
+sru_status sru_attention_forward(const sru_shape *shape, const sru_attn_cfg *cfg, const void *X,
+                                 sru_dtype x_dt, const void *Wq, const void *Wkv, const void *Wo,
+                                 const float *gamma, const float *beta, float *Q, void *KV,
+                                 float *R, float *U, void *workspace, size_t workspace_bytes,
+                                 void *stream)
+{
+    Dims dm;
+    SRU_TRY(check_attn(shape, cfg, &dm));
+    if (!valid_dtype(x_dt)) return fail(SRU_ERR_INVALID_ARG, "unknown dtype");
+    SRU_TRY(need_ptr(X, "X"));
+    SRU_TRY(need_ptr(Wq, "Wq"));
+    SRU_TRY(need_ptr(Wkv, "Wkv"));
+    SRU_TRY(need_ptr(Wo, "Wo"));
+    SRU_TRY(need_ptr(Q, "Q"));
+    SRU_TRY(need_ptr(KV, "KV"));
+    SRU_TRY(need_ptr(R, "R"));
+    SRU_TRY(need_ptr(U, "U"));
+    if (cfg->layernorm) {
+        SRU_TRY(need_ptr(gamma, "gamma"));
+        SRU_TRY(need_ptr(beta, "beta"));
+    }
+    const int64_t L = shape->L, B = shape->B, d = shape->d, dp = cfg->d_inner;
+    const int64_t Lm = cfg->mem_len, n3 = 3 * dm.ndir * d;
+    {   // the written outputs against each other and every input
+        struct Span {
+            const void *p;
+            size_t n;
+            const char *name;
+        };
+        const Span out[] = {{Q, (size_t)(dm.LB * dp) * 4, "Q"},
+                            {KV, (size_t)((Lm + L) * B * 2 * dp) * 2, "KV"},
+                            {R, (size_t)(dm.LB * dp) * 4, "R"},
+                            {U, (size_t)(dm.LB * n3) * 4, "U"}};
+        const Span in[] = {{X, (size_t)(dm.LB * d) * (x_dt == SRU_BF16 ? 2 : 4), "X"},
+                           {Wq, (size_t)(dp * d) * 2, "Wq"},
+                           {Wkv, (size_t)(2 * dp * dp) * 2, "Wkv"},
+                           {Wo, (size_t)(n3 * dp) * 2, "Wo"},
+                           {gamma, cfg->layernorm ? (size_t)dp * 4 : 0, "gamma"},
+                           {beta, cfg->layernorm ? (size_t)dp * 4 : 0, "beta"}};
+        for (int i = 0; i < 4; ++i) {
+            for (int j = i + 1; j < 4; ++j)
+                if (overlaps(out[i].p, out[i].n, out[j].p, out[j].n))
+                    return fail(SRU_ERR_INVALID_ARG, "%s overlaps %s", out[i].name, out[j].name);
+            for (const Span &x : in)
+                if (x.p && x.n && overlaps(out[i].p, out[i].n, x.p, x.n))
+                    return fail(SRU_ERR_INVALID_ARG, "%s overlaps %s", out[i].name, x.name);
+        }
+    }
+    const size_t need = round256(sru::attention_workspace_bytes(L, B, dp, Lm));
+    if (!workspace || workspace_bytes < need)
+        return fail(SRU_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need,
+                    workspace_bytes, workspace ? "" : ", NULL");
+    if (((uintptr_t)workspace) & 255u)
+        return fail(SRU_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    SRU_TRY(need_device());
+    sru::AttnArgs a;
+    a.L = L, a.B = B, a.d = d, a.dp = dp, a.Lm = Lm, a.n3 = n3;
+    a.causal = cfg->causal, a.layernorm = cfg->layernorm;
+    a.alpha = cfg->attn_alpha, a.eps = cfg->ln_eps;
+    a.X = X, a.x_bf16 = x_dt == SRU_BF16;
+    a.Wq = (const sru::bf16_bits_t *)Wq;
+    a.Wkv = (const sru::bf16_bits_t *)Wkv;
+    a.Wo = (const sru::bf16_bits_t *)Wo;
+    a.gamma = gamma, a.beta = beta;
+    a.Q = Q, a.R = R, a.U = U, a.KV = KV, a.workspace = workspace;
+    return launched(sru::launch_attention_forward(a, (hipStream_t)stream), "attention");
+}
+
 sru_status sru_transpose_weight(const sru_shape *shape, const void *W, sru_dtype w_dt, void *Wt,
                                 void *stream)
 {

@@ -71,40 +71,43 @@ typedef TileCfg<256, 256, 64, 1, 1, 2, 4, false> CfgBig8;
 typedef TileCfg<128, 128, 64, 4, 2, 2, 2, false> CfgSmallDeep;
 
 
-// ---- A tile (BM x BK) -> registers -> LDS (bf16) --------------------------
-// FAST (K % BK == 0): every thread's element offsets inside the k-tile window
-// are loop invariant 32-bit byte offsets (rows past M are clamped to M - 1:
-// they load valid memory whose results the epilogue never writes), and the
-// window's base pointer is uniform.  Otherwise every element is bounds
-// checked.
-template <class Cfg, typename TA, bool FAST>
-struct ALoader {
-    static constexpr int V = 16 / sizeof(TA);            // elements per 16 bytes
+// ---- row-major operand tile (ROWS x BK) -> registers -> LDS (bf16) --------
+// The operand is stored with its tile rows along the reduction (A as [M, K],
+// or B as [N, K]), row stride ld elements.  FAST (whole k-tiles, 16-byte
+// aligned rows): every thread's element offsets inside the k-tile window are
+// loop invariant 32-bit byte offsets (rows past the end are clamped to the
+// last row: they load valid memory whose results the epilogue never writes),
+// and the window's base pointer is uniform.  Otherwise every element is
+// bounds checked.  fp32 elements are rounded to bf16 (nearest even) as they
+// are written to LDS.
+template <class Cfg, int ROWS, typename T, bool FAST>
+struct RowLoader {
+    static constexpr int V = 16 / sizeof(T);             // elements per 16 bytes
     static constexpr int PER_ROW = Cfg::BK / V;
-    static constexpr int N = Cfg::BM * PER_ROW / Cfg::NT;     // 16-byte loads per thread
+    static constexpr int N = ROWS * PER_ROW / Cfg::NT;   // 16-byte loads per thread
     struct Offsets {
         uint32_t v[N];
     };
     u32x4 reg[N];
     const Offsets *off = nullptr;                        // shared by the stages
-    __device__ __forceinline__ static void init(Offsets &o, int64_t M, int64_t K, int64_t m0,
-                                                int tid)
+    __device__ __forceinline__ static void init(Offsets &o, int64_t ld, int64_t rows,
+                                                int64_t r0, int tid)
     {
         if (FAST) {
 #pragma unroll
             for (int i = 0; i < N; ++i) {
                 const int idx = tid + i * Cfg::NT;
                 int64_t row = idx / PER_ROW;
-                if (m0 + row > M - 1) row = M - 1 - m0;
-                o.v[i] = (uint32_t)((row * K + (idx % PER_ROW) * V) * (int64_t)sizeof(TA));
+                if (r0 + row > rows - 1) row = rows - 1 - r0;
+                o.v[i] = (uint32_t)((row * ld + (idx % PER_ROW) * V) * (int64_t)sizeof(T));
             }
         }
     }
-    __device__ __forceinline__ void load(const TA *A, int64_t M, int64_t K, int64_t m0,
-                                         int64_t k0, int tid)
+    __device__ __forceinline__ void load(const T *P, int64_t ld, int64_t rows, int64_t K,
+                                         int64_t r0, int64_t k0, int tid)
     {
         if (FAST) {
-            const char *base = (const char *)(A + m0 * K + k0);   // uniform
+            const char *base = (const char *)(P + r0 * ld + k0);   // uniform
 #pragma unroll
             for (int i = 0; i < N; ++i) reg[i] = *(const u32x4 *)(base + off->v[i]);
             return;
@@ -113,12 +116,12 @@ struct ALoader {
         for (int i = 0; i < N; ++i) {
             const int idx = tid + i * Cfg::NT;
             const int row = idx / PER_ROW, cv = idx % PER_ROW;
-            const int64_t m = m0 + row, k = k0 + cv * V;
+            const int64_t r = r0 + row, k = k0 + cv * V;
             u32x4 v = {0u, 0u, 0u, 0u};
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                const TA a = (m < M && k + e < K) ? A[m * K + k + e] : TA(0);
-                if constexpr (sizeof(TA) == 4)
+                const T a = (r < rows && k + e < K) ? P[r * ld + k + e] : T(0);
+                if constexpr (sizeof(T) == 4)
                     v[e] = __builtin_bit_cast(uint32_t, a);
                 else
                     v[e / 2] |= uint32_t(a) << (16 * (e % 2));
@@ -126,14 +129,14 @@ struct ALoader {
             reg[i] = v;
         }
     }
-    __device__ __forceinline__ void store(bf16_bits *As, int tid) const
+    __device__ __forceinline__ void store(bf16_bits *S, int tid) const
     {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int idx = tid + i * Cfg::NT;
             const int row = idx / PER_ROW, cv = idx % PER_ROW;
-            bf16_bits *dst = As + row * Cfg::LDK + cv * V;
-            if constexpr (sizeof(TA) == 4) {   // round fp32 -> bf16 (nearest even) here
+            bf16_bits *dst = S + row * Cfg::LDK + cv * V;
+            if constexpr (sizeof(T) == 4) {   // round fp32 -> bf16 (nearest even) here
                 const u32x4 u = reg[i];
                 u32x2 packed;
                 packed.x = pack_bf16x2(__uint_as_float(u.x), __uint_as_float(u.y));
@@ -146,66 +149,9 @@ struct ALoader {
     }
 };
 
-// ---- B tile given as [N, K] (k contiguous) -> LDS as Bs[n][k], row by row --
-template <class Cfg, bool FAST>
-struct BLoaderNK {
-    static constexpr int PER_ROW = Cfg::BK / 8;
-    static constexpr int N = Cfg::BN * PER_ROW / Cfg::NT;
-    struct Offsets {
-        uint32_t v[N];
-    };
-    u32x4 reg[N];
-    const Offsets *off = nullptr;
-    __device__ __forceinline__ static void init(Offsets &o, int64_t N_, int64_t K, int64_t n0,
-                                                int tid)
-    {
-        if (FAST) {
-#pragma unroll
-            for (int i = 0; i < N; ++i) {
-                const int idx = tid + i * Cfg::NT;
-                int64_t row = idx / PER_ROW;
-                if (n0 + row > N_ - 1) row = N_ - 1 - n0;
-                o.v[i] = (uint32_t)((row * K + (idx % PER_ROW) * 8) * 2);
-            }
-        }
-    }
-    __device__ __forceinline__ void load(const bf16_bits *Bm, int64_t N_, int64_t K, int64_t n0,
-                                         int64_t k0, int tid)
-    {
-        if (FAST) {
-            const char *base = (const char *)(Bm + n0 * K + k0);
-#pragma unroll
-            for (int i = 0; i < N; ++i) reg[i] = *(const u32x4 *)(base + off->v[i]);
-            return;
-        }
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const int idx = tid + i * Cfg::NT;
-            const int row = idx / PER_ROW, cv = idx % PER_ROW;
-            const int64_t n = n0 + row, k = k0 + cv * 8;
-            u32x4 v = {0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t h = (n < N_ && k + e < K) ? Bm[n * K + k + e] : 0u;
-                v[e / 2] |= h << (16 * (e % 2));
-            }
-            reg[i] = v;
-        }
-    }
-    __device__ __forceinline__ void store(bf16_bits *Bs, int tid) const
-    {
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const int idx = tid + i * Cfg::NT;
-            const int row = idx / PER_ROW, cv = idx % PER_ROW;
-            *(u32x4 *)(Bs + row * Cfg::LDK + cv * 8) = reg[i];
-        }
-    }
-};
-
 // ---- K-major operand -> LDS as S[r][k] (ROWS x BK) ------------------------
-// The operand is stored [K, ld] (its ROWS tile rows contiguous along ld): B
-// given as [K, N], or A given as [K, M].  Each thread gathers KG k-values of
+// The operand is stored [K, rows] with row stride ld >= rows (its tile rows
+// contiguous): B given as [K, N], or A given as [K, M].  Each thread gathers KG k-values of
 // two adjacent rows (one 4-byte load of a bf16 pair, or one 8-byte load of an
 // fp32 pair, per k; a wave reads whole contiguous row segments) and writes
 // them as 16-byte LDS rows (fp32 rounded to bf16, nearest even, here), so
@@ -222,17 +168,17 @@ struct KLoader {
     };
     Reg reg[KG];
     const Offsets *off = nullptr;
-    __device__ __forceinline__ static void init(Offsets &o, int64_t ld, int64_t K, int64_t r0,
-                                                int tid)
+    __device__ __forceinline__ static void init(Offsets &o, int64_t ld, int64_t rows,
+                                                int64_t r0, int tid)
     {
-        if (FAST) {   // ld even: the pair (r, r+1) is one aligned load
+        if (FAST) {   // ld and rows even: the pair (r, r+1) is one aligned load
             int64_t c = 2 * (tid % NP);
-            if (r0 + c > ld - 2) c = ld - 2 - r0;        // rows past the end: any valid pair
+            if (r0 + c > rows - 2) c = rows - 2 - r0;    // rows past the end: any valid pair
             o.v = (uint32_t)(((tid / NP) * KG * ld + c) * (int64_t)sizeof(T));
         }
     }
-    __device__ __forceinline__ void load(const T *P, int64_t ld, int64_t K, int64_t r0,
-                                         int64_t k0, int tid)
+    __device__ __forceinline__ void load(const T *P, int64_t ld, int64_t rows, int64_t K,
+                                         int64_t r0, int64_t k0, int tid)
     {
         if (FAST) {
 #pragma unroll
@@ -247,8 +193,8 @@ struct KLoader {
 #pragma unroll
         for (int e = 0; e < KG; ++e) {
             const int64_t k = k0 + kq * KG + e;
-            const T lo = (k < K && r < ld) ? P[k * ld + r] : T(0);
-            const T hi = (k < K && r + 1 < ld) ? P[k * ld + r + 1] : T(0);
+            const T lo = (k < K && r < rows) ? P[k * ld + r] : T(0);
+            const T hi = (k < K && r + 1 < rows) ? P[k * ld + r + 1] : T(0);
             if constexpr (sizeof(T) == 2) {
                 reg[e] = uint32_t(lo) | (uint32_t(hi) << 16);
             } else {
@@ -316,50 +262,66 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t TM, int64_t TN, int
     *tn = in / gsz;
 }
 
-// C[M, N] (+)= A[M, K] . B  with B given as [N, K] (KN = false) or [K, N].
+// Shape, strides and options of one launch (passed by value).
+struct MM {
+    int64_t M, N, K;
+    int64_t lda, ldb, ldc;   // row strides (elements) of A, B and C as stored
+    int64_t sa, sb, sc;      // element offsets between the batches (blockIdx.y)
+    int64_t ksplit;          // k-range per split (>= K: no split)
+    int gm;                  // row tiles per group of the tile order
+    bool accumulate;
+};
+
 // C[M, N] (+)= A . B, where A is given as [M, K] (AKM = false) or [K, M]
 // (AKM = true, i.e. C = A^T B) and B as [N, K] (KN = false, C = A B^T) or
-// [K, N].  With splits > 1 (K-major operands only) block s of a tile covers
-// k in [s * ksplit, (s + 1) * ksplit) and writes its partial product to
-// C + s * M * N, to be summed in order by split_reduce.
-template <class Cfg, typename TA, bool AKM, typename TB, bool KN, bool FAST>
+// [K, N], each with its own row stride; blockIdx.y selects a batch (base
+// offsets sa, sb, sc).  With several splits block s of a tile covers k in
+// [s * ksplit, (s + 1) * ksplit) and writes its partial product to
+// C + s * M * ldc, to be summed in order by split_reduce.  C is fp32, or
+// bf16 (rounded to nearest even; no accumulation) when TC is bf16.
+template <class Cfg, typename TA, bool AKM, typename TB, bool KN, bool FAST, typename TC>
 __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(
-    int64_t M, int64_t N, int64_t K, const TA *__restrict__ A, const TB *__restrict__ Bm,
-    float *__restrict__ C, bool accumulate, int gm, int64_t ksplit)
+    MM p, const TA *__restrict__ A, const TB *__restrict__ Bm, TC *__restrict__ C)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, LDK = Cfg::LDK;
     constexpr int WM = Cfg::WM, WN = Cfg::WN, TI = Cfg::TI, TJ = Cfg::TJ;
     constexpr int STAGE = (BM + BN) * LDK;               // bf16 elements per LDS stage
     __shared__ __attribute__((aligned(16))) bf16_bits smem[2 * STAGE];
 
+    const int64_t M = p.M, N = p.N, lda = p.lda, ldb = p.ldb, ldc = p.ldc;
+    int64_t K = p.K;
+    const bool accumulate = p.accumulate;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
+    A += (int64_t)blockIdx.y * p.sa;
+    Bm += (int64_t)blockIdx.y * p.sb;
+    C += (int64_t)blockIdx.y * p.sc;
     const int64_t TM = (M + BM - 1) / BM, TN = (N + BN - 1) / BN;
     const int64_t split = (int64_t)blockIdx.x / (TM * TN);
-    if (split > 0 || ksplit < K) {   // this block's k-range (K-major operands)
-        const int64_t kb = split * ksplit;
-        A += kb * M;
-        Bm += kb * N;
-        K = (K - kb) < ksplit ? (K - kb) : ksplit;
-        C += split * M * N;
+    if (split > 0 || p.ksplit < K) {   // this block's k-range
+        const int64_t kb = split * p.ksplit;
+        A += AKM ? kb * lda : kb;
+        Bm += KN ? kb * ldb : kb;
+        K = (K - kb) < p.ksplit ? (K - kb) : p.ksplit;
+        C += split * M * ldc;
     }
     int64_t tm, tn;
-    tile_of((int64_t)blockIdx.x % (TM * TN), TM, TN, gm, &tm, &tn);
+    tile_of((int64_t)blockIdx.x % (TM * TN), TM, TN, p.gm, &tm, &tn);
     const int64_t m0 = tm * BM, n0 = tn * BN;
 
     bf16_bits *As0 = smem, *Bs0 = smem + BM * LDK;
     bf16_bits *As1 = smem + STAGE, *Bs1 = smem + STAGE + BM * LDK;
 
-    typedef typename std::conditional<AKM, KLoader<Cfg, BM, TA, FAST>, ALoader<Cfg, TA, FAST>>::type
-        AL;
-    typedef typename std::conditional<KN, KLoader<Cfg, BN, TB, FAST>, BLoaderNK<Cfg, FAST>>::type BL;
-    static_assert(KN || sizeof(TB) == 2, "B given as [N, K] is bf16");
+    typedef typename std::conditional<AKM, KLoader<Cfg, BM, TA, FAST>,
+                                      RowLoader<Cfg, BM, TA, FAST>>::type AL;
+    typedef typename std::conditional<KN, KLoader<Cfg, BN, TB, FAST>,
+                                      RowLoader<Cfg, BN, TB, FAST>>::type BL;
     typename AL::Offsets aoff;
     typename BL::Offsets boff;
-    AL::init(aoff, M, K, m0, tid);
-    BL::init(boff, N, K, n0, tid);
+    AL::init(aoff, lda, M, m0, tid);
+    BL::init(boff, ldb, N, n0, tid);
     AL la0;
     BL lb0;
     la0.off = &aoff;
@@ -467,8 +429,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(
         bf16_bits *Asl[2] = {As0, As1}, *Bsl[2] = {Bs0, Bs1};
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-            la[i].load(A, M, K, m0, kc(i), tid);
-            lb[i].load(Bm, N, K, n0, kc(i), tid);
+            la[i].load(A, lda, M, K, m0, kc(i), tid);
+            lb[i].load(Bm, ldb, N, K, n0, kc(i), tid);
         }
         la[0].store(As0, tid);
         lb[0].store(Bs0, tid);
@@ -476,8 +438,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(
         auto body = [&](int64_t kt, auto u_) -> bool {
             constexpr int u = decltype(u_)::value;
             constexpr int rs = u % NS, rn = (u + 1) % NS, ls = u % 2, ln = (u + 1) % 2;
-            la[rs].load(A, M, K, m0, kc(kt + NS), tid);
-            lb[rs].load(Bm, N, K, n0, kc(kt + NS), tid);
+            la[rs].load(A, lda, M, K, m0, kc(kt + NS), tid);
+            lb[rs].load(Bm, ldb, N, K, n0, kc(kt + NS), tid);
             if constexpr (Cfg::DB) {
                 compute_db(Asl[ls], Bsl[ls], [&] {
                     la[rn].store(Asl[ln], tid);
@@ -495,8 +457,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(
             if (unroll_until<0, UNR>([&](auto u_) { return body(kt + decltype(u_)::value, u_); }))
                 break;
     } else {
-    la0.load(A, M, K, m0, 0, tid);
-    lb0.load(Bm, N, K, n0, 0, tid);
+    la0.load(A, lda, M, K, m0, 0, tid);
+    lb0.load(Bm, ldb, N, K, n0, 0, tid);
     la0.store(As0, tid);
     lb0.store(Bs0, tid);
     static_assert(Cfg::STAGES == 1, "one register stage here; three or more above");
@@ -506,16 +468,16 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(
         constexpr bool kDB = Cfg::DB && !(TI * TJ >= 16);
         if constexpr (kDB) {
         for (int64_t kt = 0;; kt += 2) {
-            la0.load(A, M, K, m0, kc(kt + 1), tid);
-            lb0.load(Bm, N, K, n0, kc(kt + 1), tid);
+            la0.load(A, lda, M, K, m0, kc(kt + 1), tid);
+            lb0.load(Bm, ldb, N, K, n0, kc(kt + 1), tid);
             compute_db(As0, Bs0, [&] {
                 la0.store(As1, tid);
                 lb0.store(Bs1, tid);
             });
             __syncthreads();
             if (kt + 1 >= KT) break;
-            la0.load(A, M, K, m0, kc(kt + 2), tid);
-            lb0.load(Bm, N, K, n0, kc(kt + 2), tid);
+            la0.load(A, lda, M, K, m0, kc(kt + 2), tid);
+            lb0.load(Bm, ldb, N, K, n0, kc(kt + 2), tid);
             compute_db(As1, Bs1, [&] {
                 la0.store(As0, tid);
                 lb0.store(Bs0, tid);
@@ -525,15 +487,15 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(
         }
         } else {
         for (int64_t kt = 0;; kt += 2) {
-            la0.load(A, M, K, m0, kc(kt + 1), tid);
-            lb0.load(Bm, N, K, n0, kc(kt + 1), tid);
+            la0.load(A, lda, M, K, m0, kc(kt + 1), tid);
+            lb0.load(Bm, ldb, N, K, n0, kc(kt + 1), tid);
             compute(As0, Bs0);
             la0.store(As1, tid);
             lb0.store(Bs1, tid);
             __syncthreads();
             if (kt + 1 >= KT) break;
-            la0.load(A, M, K, m0, kc(kt + 2), tid);
-            lb0.load(Bm, N, K, n0, kc(kt + 2), tid);
+            la0.load(A, lda, M, K, m0, kc(kt + 2), tid);
+            lb0.load(Bm, ldb, N, K, n0, kc(kt + 2), tid);
             compute(As1, Bs1);
             la0.store(As0, tid);
             lb0.store(Bs0, tid);
@@ -571,21 +533,30 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(
             const int64_t m = mw + row, n = nw + c4 * 4;
             if (m >= M) continue;
             const float4 v = *(const float4 *)(stage + row * EPI_LD + c4 * 4);
-            float *p = C + m * N + n;
-            if (FAST) {   // N % 4 == 0
+            TC *q = C + m * ldc + n;
+            if constexpr (sizeof(TC) == 2) {
+                if (FAST) {
+                    if (n < N) *(u32x2 *)q = u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+                } else {
+                    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) q[e] = f32_to_bf16(vv[e]);
+                }
+            } else if (FAST) {   // N, ldc and the batch offset multiples of 4
                 if (n < N) {
                     float4 o = v;
                     if (accumulate) {
-                        const float4 c = *(const float4 *)p;
+                        const float4 c = *(const float4 *)q;
                         o.x += c.x; o.y += c.y; o.z += c.z; o.w += c.w;
                     }
-                    *(float4 *)p = o;
+                    *(float4 *)q = o;
                 }
             } else {
                 const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (n + e < N) p[e] = accumulate ? p[e] + vv[e] : vv[e];
+                    if (n + e < N) q[e] = accumulate ? q[e] + vv[e] : vv[e];
             }
         }
     }
@@ -670,15 +641,19 @@ __global__ __launch_bounds__(256) void transpose32(int64_t rows, int64_t cols,
 // ---- fp32 path ------------------------------------------------------------
 constexpr int FT = 64, FK = 16;
 
-// A as [M, K] or, with AKM, [K, M]; B as [N, K] or, with KN, [K, N].
+// A as [M, K] or, with AKM, [K, M]; B as [N, K] or, with KN, [K, N]; row
+// strides and batch offsets as in MM.
 template <typename TA, bool AKM, typename TB, bool KN>
-__global__ __launch_bounds__(256) void gemm_f32(int64_t M, int64_t N, int64_t K,
-                                                const TA *__restrict__ A,
+__global__ __launch_bounds__(256) void gemm_f32(MM p, const TA *__restrict__ A,
                                                 const TB *__restrict__ Bm,
-                                                float *__restrict__ C, bool accumulate)
+                                                float *__restrict__ C)
 {
     __shared__ float As[FK][FT + 4];
     __shared__ float Bs[FK][FT + 4];
+    const int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    A += (int64_t)blockIdx.z * p.sa;
+    Bm += (int64_t)blockIdx.z * p.sb;
+    C += (int64_t)blockIdx.z * p.sc;
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
     const int64_t m0 = (int64_t)blockIdx.x * FT, n0 = (int64_t)blockIdx.y * FT;
@@ -690,20 +665,20 @@ __global__ __launch_bounds__(256) void gemm_f32(int64_t M, int64_t N, int64_t K,
             if (!AKM) {  // A[m][k] -> As[k][m]
                 const int r = idx / FK, kk = idx % FK;
                 const int64_t m = m0 + r, k = k0 + kk;
-                As[kk][r] = (m < M && k < K) ? load_as_f32(A + m * K + k) : 0.0f;
+                As[kk][r] = (m < M && k < K) ? load_as_f32(A + m * lda + k) : 0.0f;
             } else {     // A[k][m] -> As[k][m]
                 const int kk = idx / FT, r = idx % FT;
                 const int64_t m = m0 + r, k = k0 + kk;
-                As[kk][r] = (m < M && k < K) ? load_as_f32(A + k * M + m) : 0.0f;
+                As[kk][r] = (m < M && k < K) ? load_as_f32(A + k * lda + m) : 0.0f;
             }
             if (!KN) {  // B[n][k] -> Bs[k][n]
                 const int r = idx / FK, kk = idx % FK;
                 const int64_t n = n0 + r, k = k0 + kk;
-                Bs[kk][r] = (n < N && k < K) ? load_as_f32(Bm + n * K + k) : 0.0f;
+                Bs[kk][r] = (n < N && k < K) ? load_as_f32(Bm + n * ldb + k) : 0.0f;
             } else {    // B[k][n] -> Bs[k][n]
                 const int kk = idx / FT, r = idx % FT;
                 const int64_t n = n0 + r, k = k0 + kk;
-                Bs[kk][r] = (n < N && k < K) ? load_as_f32(Bm + k * N + n) : 0.0f;
+                Bs[kk][r] = (n < N && k < K) ? load_as_f32(Bm + k * ldb + n) : 0.0f;
             }
         }
         __syncthreads();
@@ -729,60 +704,87 @@ __global__ __launch_bounds__(256) void gemm_f32(int64_t M, int64_t N, int64_t K,
         for (int j = 0; j < 4; ++j) {
             const int64_t n = n0 + tx * 4 + j;
             if (n >= N) continue;
-            float *p = C + m * N + n;
-            *p = accumulate ? *p + acc[i][j] : acc[i][j];
+            float *q = C + m * p.ldc + n;
+            *q = p.accumulate ? *q + acc[i][j] : acc[i][j];
         }
     }
 }
 
-// splits > 1: partial products to ws ([splits, M, N]), k-range per split
-// ksplit (a multiple of the k-tile); otherwise straight into C.
-template <class Cfg, typename TA, bool AKM, typename TB, bool KN>
+// splits > 1: partial products to ws ([splits, M, N], dense), k-range per
+// split ksplit (a multiple of the k-tile; one batch only); otherwise
+// straight into C.
+template <class Cfg, typename TA, bool AKM, typename TB, bool KN, typename TC = float>
 hipError_t mfma_launch_cfg(const GemmArgs &g, hipStream_t s, int64_t splits = 1,
                            int64_t ksplit = 0, float *ws = nullptr)
 {
-    const int64_t tiles = ((g.M + Cfg::BM - 1) / Cfg::BM) * ((g.N + Cfg::BN - 1) / Cfg::BN);
-    // fast variant: whole k-tiles, 4-aligned C rows, byte offsets inside a
-    // tile window below 2^32, and (for K-major operands) aligned row pairs
-    const bool fast = (g.K % Cfg::BK == 0) && (g.N % 4 == 0) &&
-                      (AKM || g.K * Cfg::BM * 4 < (int64_t(1) << 32)) &&
-                      (!AKM || (g.M % 2 == 0 &&
-                                g.M * Cfg::BK * (int64_t)sizeof(TA) < (int64_t(1) << 32))) &&
-                      (!KN || (g.N % 2 == 0 &&
-                               g.N * Cfg::BK * (int64_t)sizeof(TB) < (int64_t(1) << 32)));
-    const int gm = 8;   // row tiles per group of the tile order
-    if (splits <= 1) ksplit = g.K;
-    float *C = splits > 1 ? ws : g.C;
-    const bool acc = splits > 1 ? false : g.accumulate;
+    MM p;
+    p.M = g.M;
+    p.N = g.N;
+    p.K = g.K;
+    p.lda = g.lda ? g.lda : (AKM ? g.M : g.K);
+    p.ldb = g.ldb ? g.ldb : (KN ? g.N : g.K);
+    p.ldc = g.ldc ? g.ldc : g.N;
+    p.sa = g.sa;
+    p.sb = g.sb;
+    p.sc = g.sc;
+    p.gm = 8;
+    p.ksplit = splits > 1 ? ksplit : g.K;
+    p.accumulate = splits > 1 ? false : g.accumulate;
+    const int64_t batch = g.batch > 0 ? g.batch : 1;
+    TC *C = (TC *)g.C;
+    if (splits > 1) {
+        C = (TC *)ws;
+        p.ldc = g.N;
+        p.sc = 0;
+    }
+    // fast variant: whole k-tiles; 4-aligned C rows and batch offsets;
+    // row-major operands with 16-byte aligned rows and offsets and a k-tile
+    // window below 2^32 bytes; K-major operands with even strides, row
+    // counts and offsets (row pairs load aligned)
+    constexpr int64_t kWin = int64_t(1) << 32;
+    auto row_ok = [&](int64_t ld, int64_t off, int rows, int64_t es) {
+        const int64_t v = 16 / es;
+        return ld % v == 0 && off % v == 0 && ld * rows * es < kWin;
+    };
+    auto kmaj_ok = [&](int64_t ld, int64_t rows, int64_t off, int64_t es) {
+        return ld % 2 == 0 && rows % 2 == 0 && off % 2 == 0 && ld * Cfg::BK * es < kWin;
+    };
+    auto al16 = [](const void *q) { return ((uintptr_t)q & 15u) == 0; };
+    const bool fast =
+        al16(g.A) && al16(g.Bm) && al16(C) &&
+        g.K % Cfg::BK == 0 && g.N % 4 == 0 && p.ldc % 4 == 0 && p.sc % 4 == 0 &&
+        (AKM ? kmaj_ok(p.lda, g.M, p.sa, sizeof(TA)) : row_ok(p.lda, p.sa, Cfg::BM, sizeof(TA))) &&
+        (KN ? kmaj_ok(p.ldb, g.N, p.sb, sizeof(TB)) : row_ok(p.ldb, p.sb, Cfg::BN, sizeof(TB)));
     if (fast) {
-        hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, TA, AKM, TB, KN, true>),
-                           dim3((unsigned)(tiles * splits)), dim3(Cfg::NT), 0, s, g.M, g.N, g.K,
-                           (const TA *)g.A, (const TB *)g.Bm, C, acc, gm, ksplit);
+        const int64_t tiles = ((g.M + Cfg::BM - 1) / Cfg::BM) * ((g.N + Cfg::BN - 1) / Cfg::BN);
+        hipLaunchKernelGGL((gemm_bf16_mfma<Cfg, TA, AKM, TB, KN, true, TC>),
+                           dim3((unsigned)(tiles * splits), (unsigned)batch), dim3(Cfg::NT), 0, s,
+                           p, (const TA *)g.A, (const TB *)g.Bm, C);
     } else {
         // bounds-checked loads: one register stage, 128 x 128 tiles
         const int64_t t1 = ((g.M + CfgSmall::BM - 1) / CfgSmall::BM) *
                            ((g.N + CfgSmall::BN - 1) / CfgSmall::BN);
-        hipLaunchKernelGGL((gemm_bf16_mfma<CfgSmall, TA, AKM, TB, KN, false>),
-                           dim3((unsigned)(t1 * splits)), dim3(CfgSmall::NT), 0, s, g.M, g.N, g.K,
-                           (const TA *)g.A, (const TB *)g.Bm, C, acc, gm, ksplit);
+        hipLaunchKernelGGL((gemm_bf16_mfma<CfgSmall, TA, AKM, TB, KN, false, TC>),
+                           dim3((unsigned)(t1 * splits), (unsigned)batch), dim3(CfgSmall::NT), 0,
+                           s, p, (const TA *)g.A, (const TB *)g.Bm, C);
     }
     return hipGetLastError();
 }
 
 int64_t tiles_of(const GemmArgs &g, int bm, int bn)
 {
-    return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
+    return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn) * (g.batch > 0 ? g.batch : 1);
 }
 
-template <typename TA, bool KN>
+template <typename TA, bool KN, typename TC = float>
 hipError_t mfma_launch(const GemmArgs &g, hipStream_t s)
 {
     // large tiles once they give every CU (256) at least one
     if (tiles_of(g, 256, 256) >= 256)
-        return mfma_launch_cfg<CfgBig8, TA, false, bf16_bits, KN>(g, s);
+        return mfma_launch_cfg<CfgBig8, TA, false, bf16_bits, KN, TC>(g, s);
     if constexpr (sizeof(TA) == 2 && !KN)
-        return mfma_launch_cfg<CfgSmallDeep, TA, false, bf16_bits, KN>(g, s);
-    return mfma_launch_cfg<CfgSmall, TA, false, bf16_bits, KN>(g, s);
+        return mfma_launch_cfg<CfgSmallDeep, TA, false, bf16_bits, KN, TC>(g, s);
+    return mfma_launch_cfg<CfgSmall, TA, false, bf16_bits, KN, TC>(g, s);
 }
 
 // C = P[0] + P[1] + ... + P[splits - 1] (+ C first when accumulating), the
@@ -847,9 +849,23 @@ hipError_t wgrad_launch(const GemmArgs &g, float *ws, hipStream_t s)
 template <typename TA, bool AKM, typename TB, bool KN>
 hipError_t f32_launch(const GemmArgs &g, hipStream_t s)
 {
-    dim3 grid((unsigned)((g.M + FT - 1) / FT), (unsigned)((g.N + FT - 1) / FT));
-    hipLaunchKernelGGL((gemm_f32<TA, AKM, TB, KN>), grid, dim3(256), 0, s, g.M, g.N, g.K,
-                       (const TA *)g.A, (const TB *)g.Bm, g.C, g.accumulate);
+    MM p;
+    p.M = g.M;
+    p.N = g.N;
+    p.K = g.K;
+    p.lda = g.lda ? g.lda : (AKM ? g.M : g.K);
+    p.ldb = g.ldb ? g.ldb : (KN ? g.N : g.K);
+    p.ldc = g.ldc ? g.ldc : g.N;
+    p.sa = g.sa;
+    p.sb = g.sb;
+    p.sc = g.sc;
+    p.ksplit = g.K;
+    p.gm = 1;
+    p.accumulate = g.accumulate;
+    dim3 grid((unsigned)((g.M + FT - 1) / FT), (unsigned)((g.N + FT - 1) / FT),
+              (unsigned)(g.batch > 0 ? g.batch : 1));
+    hipLaunchKernelGGL((gemm_f32<TA, AKM, TB, KN>), grid, dim3(256), 0, s, p, (const TA *)g.A,
+                       (const TB *)g.Bm, g.C);
     return hipGetLastError();
 }
 
@@ -890,6 +906,12 @@ hipError_t launch_gemm_wgrad(const GemmArgs &g, bool f32_math, float *ws, hipStr
         return g.b_bf16 ? wgrad_launch<bf16_bits, bf16_bits>(g, ws, s)
                         : wgrad_launch<bf16_bits, float>(g, ws, s);
     return g.b_bf16 ? wgrad_launch<float, bf16_bits>(g, ws, s) : wgrad_launch<float, float>(g, ws, s);
+}
+
+hipError_t launch_gemm_bf16_out(const GemmArgs &g, hipStream_t s)
+{
+    if (!g.b_bf16 || g.b_kn || g.accumulate || g.a_bf16) return hipErrorInvalidValue;
+    return mfma_launch<float, false, bf16_bits>(g, s);
 }
 
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s)

@@ -75,6 +75,8 @@ hipError_t launch_linear_backward(const LinArgs &a, hipStream_t s);
 // C[M, N] (+)= A[M, K] . op(B)
 //   b_kn = false: B stored [N, K] (C = A B^T)     -- projection forward
 //   b_kn = true : B stored [K, N] (C = A B)       -- projection backward-data
+// Row strides lda, ldb, ldc (elements; 0 = dense) and `batch` independent
+// products whose operands start sa, sb, sc elements apart.
 struct GemmArgs {
     int64_t M, N, K;
     const void *A;
@@ -84,9 +86,15 @@ struct GemmArgs {
     bool b_kn;
     float *C;
     bool accumulate;
+    int64_t lda = 0, ldb = 0, ldc = 0;
+    int64_t batch = 1, sa = 0, sb = 0, sc = 0;
 };
 
+// bf16 B: bf16 MFMA (A rounded to bf16 as it is loaded); fp32 B: fp32 FMA.
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
+// As launch_gemm for fp32 A, bf16 B given as [N, K], no accumulation, with
+// C written as bf16 (rounded to nearest even); C points to bf16 storage.
+hipError_t launch_gemm_bf16_out(const GemmArgs &g, hipStream_t s);
 // C[M, N] (+)= A^T B with A given as [K, M] and B as [K, N] (each bf16 or
 // fp32): the weight gradient dW = dU^T Xt.  f32_math: fp32 FMA throughout;
 // otherwise bf16 MFMA on operands rounded to bf16 while staged, with the
@@ -94,6 +102,22 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
 // fill the chip (ws then holds the partial products).
 size_t wgrad_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_wgrad(const GemmArgs &g, bool f32_math, float *ws, hipStream_t s);
+// The SRU++ attention U-producer (attention.hip); layouts as in sru.h.
+struct AttnArgs {
+    int64_t L, B, d, dp, Lm, n3;   // n3 = ndir * 3 * d
+    int causal, layernorm;
+    float alpha, eps;
+    const void *X;
+    bool x_bf16;
+    const bf16_bits_t *Wq, *Wkv, *Wo;
+    const float *gamma, *beta;
+    float *Q, *R, *U;
+    void *KV;                      // bf16 [Lm + L, B, 2 dp]
+    void *workspace;               // attention_workspace_bytes
+};
+size_t attention_workspace_bytes(int64_t L, int64_t B, int64_t dp, int64_t Lm);
+hipError_t launch_attention_forward(const AttnArgs &a, hipStream_t s);
+
 // dst[cols, rows] = src[rows, cols]^T (2-byte or 4-byte elements).
 hipError_t launch_transpose(int64_t rows, int64_t cols, const void *src, void *dst, bool two_byte,
                             hipStream_t s);

@@ -197,3 +197,27 @@ def factored_inputs(L, B, d, ndir, d_inner, seed, w_dtype="bf16"):
     out["dU"] = _std_normal(rng, (M, n3))
     out["dQ"] = _std_normal(rng, (M, d_inner))
     return out
+
+
+def attention_inputs(L, B, d, ndir, d_inner, mem_len, seed):
+    """Inputs of the SRU++ attention U-producer (SRU++ paper, section on
+    SRU++; its models use d = 4 d').  Draw order: X ~ N(0, 1) [L*B, d]; Wq,
+    Wk, Wv, Wo ~ Xavier-U for d -> d', d' -> d', d' -> d', d' -> ndir*3d, each
+    rounded once to bf16 (Wk and Wv stacked as Wkv [2d', d']); the previous
+    segment's keys and values ~ N(0, 1) [mem_len, B, d'] in bf16; gamma ~
+    1 + U(-0.1, 0.1), beta ~ U(-0.1, 0.1) [d'] (fp32)."""
+    rng = np.random.default_rng(seed)
+    out = {"X": _std_normal(rng, (L * B, d))}
+    ws = []
+    for fan_in, fan_out in ((d, d_inner), (d_inner, d_inner), (d_inner, d_inner),
+                            (d_inner, ndir * 3 * d)):
+        bound = math.sqrt(6.0 / (fan_in + fan_out))
+        ws.append(rng.uniform(-bound, bound, size=(fan_out, fan_in)).astype(np.float32))
+    out["Wq_bits"], out["Wq"] = to_bf16(ws[0])
+    out["Wkv_bits"], out["Wkv"] = to_bf16(np.concatenate([ws[1], ws[2]]))
+    out["Wo_bits"], out["Wo"] = to_bf16(ws[3])
+    out["Kmem_bits"], out["Kmem"] = to_bf16(_std_normal(rng, (mem_len, B, d_inner)))
+    out["Vmem_bits"], out["Vmem"] = to_bf16(_std_normal(rng, (mem_len, B, d_inner)))
+    out["gamma"] = (1.0 + rng.uniform(-0.1, 0.1, size=d_inner)).astype(np.float32)
+    out["beta"] = rng.uniform(-0.1, 0.1, size=d_inner).astype(np.float32)
+    return out

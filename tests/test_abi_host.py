@@ -9,6 +9,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import parallelizable_recurrent_units_amd as sru
@@ -258,6 +259,52 @@ def test_factored_validation(lib):
             assert fact_w(lib, s, 32, which, need) == sru.SRU_ERR_NO_DEVICE
             assert fact_w(lib, s, 32, which, 0, math=0, ws=None) == sru.SRU_ERR_NO_DEVICE
     assert fact_w(lib, s, 32, 2, need) == sru.SRU_ERR_INVALID_ARG
+
+
+def attn(lib, s, cfg, ws_bytes, **kw):
+    a = dict(X=Q[0], x_dt=0, Wq=Q[1], Wkv=Q[1] + (1 << 30), Wo=Q[1] + (2 << 30), gamma=None,
+             beta=None, Qo=Q[2], KV=Q[2] + (1 << 30), R=Q[2] + (2 << 30), U=Q[2] + (3 << 30),
+             ws=Q[3])
+    a.update(kw)
+    return lib.sru_attention_forward(ctypes.byref(s), ctypes.byref(cfg) if cfg else None, a["X"],
+                                     a["x_dt"], a["Wq"], a["Wkv"], a["Wo"], a["gamma"], a["beta"],
+                                     a["Qo"], a["KV"], a["R"], a["U"], a["ws"], ws_bytes, None)
+
+
+def test_attention_workspace_and_validation(lib):
+    s = sru.SruShape(64, 4, 128, 0, 1.0)
+    cfg = sru.SruAttnCfg(32, mem_len=16, causal=True, layernorm=False, attn_alpha=0.5)
+    Lk = 16 + 64
+    want = (round256(4 * 64 * Lk * 4) + round256(4 * 64 * Lk * 2) + round256(64 * 4 * 32 * 4))
+    assert sru.sru_attention_workspace_size(s, cfg) == want
+    bad = [sru.SruAttnCfg(0), sru.SruAttnCfg(32, mem_len=-1), sru.SruAttnCfg(32, attn_alpha=np.nan),
+           sru.SruAttnCfg(32, layernorm=True, ln_eps=0.0)]
+    c2 = sru.SruAttnCfg(32)
+    c2.causal = 2
+    bad.append(c2)
+    for c in bad:
+        assert lib.sru_attention_workspace_size(ctypes.byref(s), ctypes.byref(c)) == 0
+        assert lib.sru_last_error() != b""
+        assert attn(lib, s, c, want) == sru.SRU_ERR_INVALID_ARG
+    assert attn(lib, s, None, want) == sru.SRU_ERR_INVALID_ARG
+    assert attn(lib, s, cfg, want, Wq=None) == sru.SRU_ERR_INVALID_ARG
+    assert attn(lib, s, cfg, want, KV=Q[2] + (1 << 30) + 8) == sru.SRU_ERR_INVALID_ARG
+    assert attn(lib, s, cfg, want, x_dt=5) == sru.SRU_ERR_INVALID_ARG
+    assert attn(lib, s, cfg, want - 1) == sru.SRU_ERR_WORKSPACE
+    assert attn(lib, s, cfg, want, ws=Q[3] + 16) == sru.SRU_ERR_INVALID_ARG   # 256-byte alignment
+    # outputs overlapping each other or an input
+    assert attn(lib, s, cfg, want, R=Q[2] + 64) == sru.SRU_ERR_INVALID_ARG
+    assert b"overlaps" in lib.sru_last_error()
+    assert attn(lib, s, cfg, want, U=Q[1] + 1024) == sru.SRU_ERR_INVALID_ARG
+    # layer norm needs gamma and beta
+    cln = sru.SruAttnCfg(32, layernorm=True)
+    nln = sru.sru_attention_workspace_size(s, cln)
+    assert attn(lib, s, cln, nln) == sru.SRU_ERR_INVALID_ARG
+    import torch
+    if torch.cuda.device_count() == 0:
+        assert attn(lib, s, cfg, want) == sru.SRU_ERR_NO_DEVICE
+        assert attn(lib, s, cln, nln, gamma=Q[3] + (1 << 30),
+                    beta=Q[3] + (1 << 30) + 4096) == sru.SRU_ERR_NO_DEVICE
 
 
 def test_binding_raises_sru_error(lib):
