@@ -368,3 +368,16 @@ def attention_project(X, Wq, Wk, Wv, Wo, L, B, alpha, mem_len=0, Kmem=None, Vmem
         R = layernorm(R, ln[0], ln[1], ln[2])
     U = matmul(_maybe_bf16(R, round_ops), Wo, b_nk=True)
     return {"Q": Q, "K": Kc, "V": Vc, "A": A.reshape(L * B, dp), "R": R, "U": U}
+
+
+def step(x, W, v, b, c_prev, alpha, round_x: bool):
+    """One step of a unidirectional layer (Eq. 1, then Eqs. 2-5 at L = 1):
+    x [B, d], W [3d, d], v, b [2, d], c_prev [B, d] or None (zero state).
+    Returns (h, c_next), each [B, d]."""
+    x = np.asarray(x, np.float32)
+    B, d = x.shape
+    U = project(x, W, round_x).reshape(1, B, 1, 3, d)
+    c0 = np.zeros((1, B, d), np.float32) if c_prev is None else np.asarray(c_prev).reshape(1, B, d)
+    fo = forward(U, x.reshape(1, B, d), np.asarray(v).reshape(1, 2, d),
+                 np.asarray(b).reshape(1, 2, d), c0, alpha)
+    return fo["h"][0, :, 0], fo["c_last"][0]

@@ -610,3 +610,43 @@ def test_attention_project_alpha_zero_is_the_factorised_projection():
         f = oracle.factored_project(X, Wq, Wo, round_ops)
         np.testing.assert_array_equal(a["U"], f["U"])
         np.testing.assert_array_equal(a["Q"], f["Q"])
+
+
+# --------------------------------------------------------------------------
+# decoding step
+# --------------------------------------------------------------------------
+
+def test_steps_reproduce_the_sequence_forward():
+    """Carrying c through L single steps gives the sequence forward (Eqs. 1-5
+    over all L at once) step for step.  The step takes its state as fp32 (as
+    stored between calls), so each step starts from the fp64 state rounded to
+    fp32: 1e-6 covers that rounding."""
+    rng = np.random.default_rng(40)
+    L, B, d, alpha = 6, 3, 8, 0.7
+    X = rng.standard_normal((L, B, d)).astype(np.float32)
+    W = rng.uniform(-0.3, 0.3, (3 * d, d)).astype(np.float32)
+    v = rng.uniform(-0.5, 0.5, (2, d)).astype(np.float32)
+    b = rng.uniform(-0.5, 0.5, (2, d)).astype(np.float32)
+    c0 = rng.standard_normal((B, d)).astype(np.float32)
+    U = oracle.project(X.reshape(L * B, d), W, False).reshape(L, B, 1, 3, d)
+    fo = oracle.forward(U, X, v.reshape(1, 2, d), b.reshape(1, 2, d), c0.reshape(1, B, d), alpha)
+    c = c0.astype(np.float64)
+    for t in range(L):
+        h, c = oracle.step(X[t], W, v, b, c.astype(np.float32), alpha, False)
+        np.testing.assert_allclose(h, fo["h"][t, :, 0], rtol=1e-6, atol=1e-6)
+        np.testing.assert_allclose(c, fo["c"][t, :, 0], rtol=1e-6, atol=1e-6)
+
+
+def test_step_closed_gate_copies_candidate():
+    """f = 0 and r = 1 (saturated through b): c_next = u_cand = x W_cand^T and
+    h = c_next, whatever the state."""
+    rng = np.random.default_rng(41)
+    B, d = 2, 4
+    x = rng.standard_normal((B, d)).astype(np.float32)
+    W = rng.uniform(-0.5, 0.5, (3 * d, d)).astype(np.float32)
+    v = np.zeros((2, d), np.float32)
+    b = np.stack([np.full(d, -1e4), np.full(d, 1e4)]).astype(np.float32)
+    h, c = oracle.step(x, W, v, b, rng.standard_normal((B, d)).astype(np.float32), 1.0, False)
+    ucand = x.astype(np.float64) @ W[2 * d:].astype(np.float64).T
+    np.testing.assert_allclose(c, ucand, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(h, ucand, rtol=1e-14, atol=1e-14)
