@@ -23,7 +23,8 @@ buffers, rows that are not part of the step: the projection's weight gradient
 dW = bf16(dU)^T X~, and the factorised projection U = Wo (Wq X~) with d' = d/4
 (SRU++ paper, Fig. 2(b)), forward and backward; at the given-U workload, the
 SRU++ attention that would produce that U (causal, previous segment as
-context, layer norm).
+context, layer norm); for unidirectional layers, 32 consecutive decoding
+steps (sru_step) at B = 1 and at the layer's B.
 """
 import argparse
 import hashlib
@@ -117,10 +118,20 @@ def next_row_work(w):
                  + LB * di * 4 + di * d * 2 + 2 * LB * d * 4    # dX += dQ Wq
                  + LB * di * 4 + LB * d * xs + di * d * 4       # dWq = dQ^T X
                  + LB * n3 * 2 + LB * di * 4 + n3 * di * 4)     # dWo = bf16(dU)^T Q
-    return {"f1_projection_bwd_weight": dict(flops=2 * LB * n3 * d,
+    rows = {"f1_projection_bwd_weight": dict(flops=2 * LB * n3 * d,
                                              bytes=LB * n3 * 2 + LB * d * xs + n3 * d * 4),
             "f3_factored_forward": dict(flops=fwd_flops, bytes=fwd_bytes),
             "f3_factored_backward": dict(flops=bwd_flops, bytes=bwd_bytes)}
+    if nd == 1:   # decoding steps (unidirectional layers only)
+        ws = 2 if w.w_dtype == "bf16" else 4
+        for bb in sorted({1, B}):
+            rows[f"f4_decode_step_B{bb}"] = dict(
+                flops=DECODE_STEPS * 2 * bb * 3 * d * d,
+                bytes=DECODE_STEPS * (3 * d * d * ws + 4 * d * 4 + bb * d * (xs + 3 * 4)))
+    return rows
+
+
+DECODE_STEPS = 32   # consecutive single-step calls per timed decode row
 
 
 ATTN_CONTEXT = 1.0   # previous-segment context length, in units of L
@@ -251,11 +262,42 @@ def next_rows(shape, t):
         sru_project_factored_bwd_weight(shape, di, SRU_FACT_WGRAD_O, t["dU_lp"], t["Q"],
                                         t["dWo"], SRU_BF16, False, t["ws_f"])
 
-    return [("f1_projection_bwd_weight",
+    rows = [("f1_projection_bwd_weight",
              lambda: sru_project_bwd_weight(shape, t["dU_lp"], t["x"], t["dW"], SRU_BF16, False,
                                             t["ws_w"])),
             ("f3_factored_forward", fact_fwd),
             ("f3_factored_backward", fact_bwd)]
+    if not shape.bidirectional:
+        rows += decode_rows(shape, t)
+    return rows
+
+
+def decode_rows(shape, t):
+    """DECODE_STEPS single-step calls (sru_step) with the state carried in
+    place, the inputs of step i being row i of the layer's x; at B = 1 and at
+    the layer's B.  The steps are captured once in a HIP graph and the row
+    replays it (a decoding loop issues its steps that way; launched one by
+    one from Python, the host's launch rate would be measured instead)."""
+    import torch
+    from parallelizable_recurrent_units_amd import SruShape, sru_step
+    out = []
+    for bb in sorted({1, shape.B}):
+        s1 = SruShape(1, bb, shape.d, False, shape.alpha)
+        xs = [t["x"][i, :bb] for i in range(DECODE_STEPS)]
+        h = torch.empty((bb, shape.d), device="cuda", dtype=torch.float32)
+        c = torch.zeros((bb, shape.d), device="cuda", dtype=torch.float32)
+
+        def steps(s1=s1, xs=xs, h=h, c=c):
+            for x in xs:
+                sru_step(s1, x, t["W"], t["v"], t["b"], c, h, c)
+
+        steps()                                   # once outside capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            steps()
+        out.append((f"f4_decode_step_B{bb}", graph.replay))
+    return out
 
 
 def time_rows(row_sets, steps, warmup):
@@ -399,7 +441,13 @@ def time_beyond(w, sets, steps, warmup):
         return {}
     _, rows = time_rows(beyond, steps, warmup)
     work = next_row_work(w)
-    return {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
+    out = {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
+    for n, r in out.items():
+        if n.startswith("f4_decode_step_B"):
+            bb = int(n[len("f4_decode_step_B"):])
+            r["us_per_step"] = r["us"] / DECODE_STEPS
+            r["tokens_per_s"] = bb * DECODE_STEPS / rows[n]
+    return out
 
 
 def extras(main_id, steps):
@@ -466,6 +514,8 @@ ROW_LAUNCHES = {
                                  "along L*B; the reduction split over blocks)",
                                  "split_reduce (partial sums added in split order)"],
     "f3_factored_forward": ["gemm_bf16_mfma (Q = X Wq^T)", "gemm_bf16_mfma (U = Q Wo^T)"],
+    "f4_decode_step_B1": [f"step_cell x {DECODE_STEPS} (one call per step, state in place, "
+                          "replayed from a HIP graph)"],
     "f2_attention_forward": ["gemm_bf16_mfma (Q = X Wq^T)", "gemm_bf16_mfma ([K|V] = Q Wkv^T, "
                              "bf16 out)", "gemm_bf16_mfma (scores, one batch per sequence)",
                              "attn_softmax", "gemm_bf16_mfma (weights x V, batched)",

@@ -229,6 +229,28 @@ sru_status sru_attention_forward(const sru_shape *shape, const sru_attn_cfg *cfg
 size_t sru_attention_workspace_size(const sru_shape *shape, const sru_attn_cfg *cfg);
 
 /*
+ * One step of a unidirectional layer for decoding: the recurrence run as an
+ * RNN at inference ("Parallelizing Legendre Memory Unit Training", abstract),
+ * i.e. Eq. 1 and Eqs. 2-5 for a single time step with the state carried
+ * between calls (SRU++ paper, background section):
+ *   u = x~ W^T for the step's B rows, then per channel
+ *   c_next = f c_prev + (1 - f) u_cand, h = r c_next + (1 - r) alpha x.
+ * shape->L must be 1 and shape->bidirectional 0 (a decoding step sees no
+ * future input).  x [B, d] fp32 or bf16; W [3d, d] fp32 or bf16 (the same
+ * weights as sru_project); v, b fp32 [2, d]; c_prev fp32 [B, d] or NULL
+ * (zero state); h, c_next fp32 [B, d].  With bf16 W, x is rounded to bf16
+ * (nearest even) for the product, as in sru_project; the highway term uses
+ * x.  The products are fp32 sums.  c_next may be the same buffer as c_prev
+ * (the state updated in place); no other output may overlap an input or the
+ * other output.
+ */
+sru_status sru_step(const sru_shape *shape,
+                    const void *x, sru_dtype x_dt,
+                    const void *W, sru_dtype w_dt,
+                    const float *v, const float *b, const float *c_prev,
+                    float *h, float *c_next, void *stream);
+
+/*
  * Forward recurrence, Eqs. 2-5, for every (direction, batch, channel) chain.
  *   U: u_dt in {F32, BF16}; x: x_dt in {F32, BF16}; v, b, c0: fp32.
  *   c0 may be NULL (zero initial state).

@@ -27,7 +27,7 @@ SRU_FACT_WGRAD_Q, SRU_FACT_WGRAD_O = 0, 1
 # Every symbol include/sru.h declares.
 EXPORTED = ("sru_project", "sru_project_bwd_weight", "sru_project_factored",
             "sru_project_factored_bwd_weight", "sru_attention_forward",
-            "sru_attention_workspace_size", "sru_forward", "sru_backward", "sru_linear_scan",
+            "sru_attention_workspace_size", "sru_step", "sru_forward", "sru_backward", "sru_linear_scan",
             "sru_transpose_weight", "sru_workspace_size", "sru_status_string", "sru_last_error")
 
 
@@ -98,6 +98,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                           _vp, _vp, _vp, _vp, _vp, sz, _vp]
     lib.sru_attention_workspace_size.restype = sz
     lib.sru_attention_workspace_size.argtypes = [sp, cp]
+    lib.sru_step.restype = ctypes.c_int
+    lib.sru_step.argtypes = [sp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
+                             _vp]
     lib.sru_forward.restype = ctypes.c_int
     lib.sru_forward.argtypes = [sp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
                                 ctypes.c_int, _vp, _vp, _vp]
@@ -228,6 +231,13 @@ def sru_attention_forward(shape, cfg, X, Wq, Wkv, Wo, gamma, beta, Q, KV, R, U, 
         ctypes.byref(s), ctypes.byref(cfg), _ptr(X), _dtype_code(X), _ptr(Wq), _ptr(Wkv),
         _ptr(Wo), _ptr(gamma), _ptr(beta), _ptr(Q), _ptr(KV), _ptr(R), _ptr(U), _ptr(workspace),
         ws_bytes, _stream(stream)))
+
+
+def sru_step(shape, x, W, v, b, c_prev, h, c_next, stream=None):
+    s = _shape(shape)
+    _check(load_library().sru_step(ctypes.byref(s), _ptr(x), _dtype_code(x), _ptr(W),
+                                   _dtype_code(W), _ptr(v), _ptr(b), _ptr(c_prev), _ptr(h),
+                                   _ptr(c_next), _stream(stream)))
 
 
 def sru_transpose_weight(shape, W, Wt, stream=None):

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsru.so")
 SOURCES = ["abi.hip", "recurrence.hip", "backward_scan.hip", "linear_scan.hip", "gemm.hip",
-           "attention.hip"]
+           "attention.hip", "step.hip"]
 
 ARCH = os.environ.get("SRU_OFFLOAD_ARCH", "gfx950")
 # Packed fp32 VALU ops are disabled for every kernel (hipcc emits them from

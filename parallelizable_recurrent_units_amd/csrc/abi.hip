@@ -472,6 +472,55 @@ sru_status sru_attention_forward(const sru_shape *shape, const sru_attn_cfg *cfg
     return launched(sru::launch_attention_forward(a, (hipStream_t)stream), "attention");
 }
 
+sru_status sru_step(const sru_shape *shape, const void *x, sru_dtype x_dt, const void *W,
+                    sru_dtype w_dt, const float *v, const float *b, const float *c_prev, float *h,
+                    float *c_next, void *stream)
+{
+    Dims dm;
+    SRU_TRY(check_shape(shape, &dm));
+    if (shape->L != 1) return fail(SRU_ERR_INVALID_ARG, "a step has L = 1 (got %lld)",
+                                   (long long)shape->L);
+    if (shape->bidirectional)
+        return fail(SRU_ERR_INVALID_ARG, "a decoding step is unidirectional");
+    if (!valid_dtype(x_dt) || !valid_dtype(w_dt)) return fail(SRU_ERR_INVALID_ARG, "unknown dtype");
+    SRU_TRY(need_ptr(x, "x"));
+    SRU_TRY(need_ptr(W, "W"));
+    SRU_TRY(need_ptr(v, "v"));
+    SRU_TRY(need_ptr(b, "b"));
+    SRU_TRY(opt_ptr(c_prev, "c_prev"));
+    SRU_TRY(need_ptr(h, "h"));
+    SRU_TRY(need_ptr(c_next, "c_next"));
+    const int64_t B = shape->B, d = shape->d;
+    int64_t w_el;
+    if (!mul_ok(3 * d, d, &w_el)) return fail(SRU_ERR_INVALID_ARG, "tensor sizes overflow");
+    if ((d + 3) / 4 > kMaxBlocks) return fail(SRU_ERR_INVALID_ARG, "d too large for one launch");
+    const size_t bd = (size_t)(B * d) * 4;
+    if (overlaps(h, bd, c_next, bd)) return fail(SRU_ERR_INVALID_ARG, "h overlaps c_next");
+    if (c_prev && c_prev != c_next && overlaps(c_prev, bd, c_next, bd))
+        return fail(SRU_ERR_INVALID_ARG, "c_next overlaps c_prev without being it");
+    {
+        const void *ins[] = {x, W, v, b, c_prev};
+        const size_t sz[] = {(size_t)(B * d) * (x_dt == SRU_BF16 ? 2 : 4),
+                             (size_t)w_el * (w_dt == SRU_BF16 ? 2 : 4), (size_t)(2 * d) * 4,
+                             (size_t)(2 * d) * 4, c_prev ? bd : 0};
+        for (int i = 0; i < 5; ++i) {
+            if (!ins[i] || !sz[i]) continue;
+            if (overlaps(h, bd, ins[i], sz[i]) ||
+                (i < 4 && overlaps(c_next, bd, ins[i], sz[i])))
+                return fail(SRU_ERR_INVALID_ARG, "an output overlaps an input");
+        }
+    }
+    SRU_TRY(need_device());
+    sru::StepArgs a;
+    a.B = B, a.d = d;
+    a.x = x, a.W = W;
+    a.x_bf16 = x_dt == SRU_BF16, a.w_bf16 = w_dt == SRU_BF16;
+    a.v = v, a.b = b, a.c_prev = c_prev;
+    a.h = h, a.c_next = c_next;
+    a.alpha = shape->alpha;
+    return launched(sru::launch_step(a, (hipStream_t)stream), "step");
+}
+
 sru_status sru_transpose_weight(const sru_shape *shape, const void *W, sru_dtype w_dt, void *Wt,
                                 void *stream)
 {

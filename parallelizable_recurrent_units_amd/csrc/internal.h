@@ -118,6 +118,18 @@ struct AttnArgs {
 size_t attention_workspace_bytes(int64_t L, int64_t B, int64_t dp, int64_t Lm);
 hipError_t launch_attention_forward(const AttnArgs &a, hipStream_t s);
 
+// One decoding step of a unidirectional layer (step.hip).
+struct StepArgs {
+    int64_t B, d;
+    const void *x, *W;             // x [B, d]; W [3d, d]
+    bool x_bf16, w_bf16;
+    const float *v, *b;            // [2, d]
+    const float *c_prev;           // [B, d] or null (zero state)
+    float *h, *c_next;             // [B, d]; c_next may be c_prev
+    float alpha;
+};
+hipError_t launch_step(const StepArgs &a, hipStream_t s);
+
 // dst[cols, rows] = src[rows, cols]^T (2-byte or 4-byte elements).
 hipError_t launch_transpose(int64_t rows, int64_t cols, const void *src, void *dst, bool two_byte,
                             hipStream_t s);

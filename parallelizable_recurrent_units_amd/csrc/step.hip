@@ -1,0 +1,187 @@
+// step.hip -- one decoding step of a unidirectional SRU layer: the "run as an
+// RNN at inference" side of the recurrence ("Parallelizing Legendre Memory
+// Unit Training", abstract; SRU++ paper, background section, Eqs. 1-5).  For
+// the B input rows of one time step, Eq. 1 gives the three gate inputs of
+// every channel, and Eqs. 2-5 advance the carried state c:
+//   u = x~ W^T, f = sigma(u_f + v c + b), r = sigma(u_r + v' c + b'),
+//   c' = f c + (1 - f) u_cand, h = r c' + (1 - r) alpha x.
+// x~ = bf16(x) (nearest even) when W is bf16, as in the projection; the
+// highway term uses x itself.
+//
+// One wave per channel j.  It keeps rows j, d + j and 2d + j of W (the three
+// gates of channel j) in registers, then for each batch row forms the three
+// dot products with x~ (per-lane partial sums over 8-element pieces, then a
+// wave reduction); the cell runs one batch row per lane.  W is read from
+// memory once per step; x (B x d) is read by every wave from the caches.
+#include "device_common.h"
+#include "internal.h"
+
+namespace sru {
+namespace {
+
+typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// 8 consecutive elements as fp32 (bf16 widened exactly).
+template <typename T> __device__ __forceinline__ void load8(const T *p, float (&o)[8]);
+template <> __device__ __forceinline__ void load8<float>(const float *p, float (&o)[8])
+{
+    const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
+    o[0] = a.x, o[1] = a.y, o[2] = a.z, o[3] = a.w;
+    o[4] = b.x, o[5] = b.y, o[6] = b.z, o[7] = b.w;
+}
+template <> __device__ __forceinline__ void load8<bf16_bits>(const bf16_bits *p, float (&o)[8])
+{
+    const u32x4s v = *(const u32x4s *)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __uint_as_float(v[i] << 16);
+        o[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ float round_bf16(float x) { return bf16_to_f32(f32_to_bf16(x)); }
+
+// Applies Eqs. 2-5 for (b, j) given the state c, the three gate inputs and
+// the highway input xv.
+__device__ __forceinline__ void cell(const StepArgs &a, int64_t b, int64_t j, float vf, float vr,
+                                     float bf, float br, float c, float uf, float ur, float ux,
+                                     float xv)
+{
+    const float yf = fmaf(vf, c, uf + bf) * kNegLog2e;
+    const float yr = fmaf(vr, c, ur + br) * kNegLog2e;
+    const float cn = gate_blend(yf, c, ux);              // f c + (1 - f) u_cand
+    a.h[b * a.d + j] = gate_blend(yr, cn, a.alpha * xv); // r c' + (1 - r) alpha x
+    a.c_next[b * a.d + j] = cn;
+}
+
+// VEC (d % 8 == 0): 8-element pieces; NC > 0: a W row of d <= 512 NC
+// elements stays in registers (NC pieces per lane); NC == 0: W is re-read
+// for every batch row.  Without VEC every element is loaded on its own.
+// Batch rows go in groups of 64: after the wave reduction of row b0 + i,
+// lane i keeps its three gate inputs, and the cell then runs for the whole
+// group at once, one batch row per lane (one round of state loads).
+template <typename TW, typename TX, bool VEC, int NC>
+__global__ __launch_bounds__(256) void step_cell(StepArgs a)
+{
+    const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (j >= a.d) return;
+    const int64_t d = a.d;
+    const TW *W = (const TW *)a.W;
+    const TX *X = (const TX *)a.x;
+    const bool rnd = sizeof(TW) == 2;                    // x~ = bf16(x) with bf16 W
+    const float vf = a.v[j], vr = a.v[d + j], bf = a.b[j], br = a.b[d + j];
+    float w[3][NC > 0 ? NC : 1][8];
+    if constexpr (VEC && NC > 0) {
+#pragma unroll
+        for (int g = 0; g < 3; ++g)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int64_t k = 512 * c + 8 * lane;
+                if (k < d)
+                    load8(W + (g * d + j) * d + k, w[g][c]);
+                else
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w[g][c][e] = 0.0f;
+            }
+    }
+    // the three dot products of batch row b, summed over the wave
+    auto dots = [&](int64_t b, float (&u)[3]) {
+        float s[3] = {0.0f, 0.0f, 0.0f};
+        if constexpr (VEC && NC > 0) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int64_t k = 512 * c + 8 * lane;
+                if (k >= d) continue;
+                float xv[8];
+                load8(X + b * d + k, xv);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float xt = rnd ? round_bf16(xv[e]) : xv[e];
+#pragma unroll
+                    for (int g = 0; g < 3; ++g) s[g] = fmaf(w[g][c][e], xt, s[g]);
+                }
+            }
+        } else if constexpr (VEC) {
+            for (int64_t k = 8 * lane; k < d; k += 512) {
+                float xv[8], wv[8];
+                load8(X + b * d + k, xv);
+#pragma unroll
+                for (int g = 0; g < 3; ++g) {
+                    load8(W + (g * d + j) * d + k, wv);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        s[g] = fmaf(wv[e], rnd ? round_bf16(xv[e]) : xv[e], s[g]);
+                }
+            }
+        } else {
+            for (int64_t k = lane; k < d; k += 64) {
+                const float xv = load_as_f32(X + b * d + k);
+                const float xt = rnd ? round_bf16(xv) : xv;
+#pragma unroll
+                for (int g = 0; g < 3; ++g)
+                    s[g] = fmaf(load_as_f32(W + (g * d + j) * d + k), xt, s[g]);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < 3; ++g) u[g] = wave_sum(s[g]);
+    };
+    for (int64_t b0 = 0; b0 < a.B; b0 += 64) {
+        const int nb = a.B - b0 < 64 ? (int)(a.B - b0) : 64;
+        // this lane's state and highway input, requested before the products
+        float cp = 0.0f, xh = 0.0f;
+        if (lane < nb) {
+            const int64_t b = b0 + lane;
+            if (a.c_prev) cp = a.c_prev[b * d + j];
+            xh = load_as_f32(X + b * d + j);
+        }
+        float mine[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll 2
+        for (int i = 0; i < nb; ++i) {
+            float u[3];
+            dots(b0 + i, u);
+            if (lane == i) {
+                mine[0] = u[0];
+                mine[1] = u[1];
+                mine[2] = u[2];
+            }
+        }
+        if (lane < nb) cell(a, b0 + lane, j, vf, vr, bf, br, cp, mine[0], mine[1], mine[2], xh);
+    }
+}
+
+template <typename TW, typename TX>
+hipError_t step_launch(const StepArgs &a, hipStream_t s)
+{
+    const dim3 grid((unsigned)((a.d + 3) / 4)), block(256);
+    const bool vec = a.d % 8 == 0;
+    if (vec && a.d <= 512)
+        hipLaunchKernelGGL((step_cell<TW, TX, true, 1>), grid, block, 0, s, a);
+    else if (vec && a.d <= 1024)
+        hipLaunchKernelGGL((step_cell<TW, TX, true, 2>), grid, block, 0, s, a);
+    else if (vec && a.d <= 2048)
+        hipLaunchKernelGGL((step_cell<TW, TX, true, 4>), grid, block, 0, s, a);
+    else if (vec)
+        hipLaunchKernelGGL((step_cell<TW, TX, true, 0>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((step_cell<TW, TX, false, 0>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_step(const StepArgs &a, hipStream_t s)
+{
+    if (a.w_bf16)
+        return a.x_bf16 ? step_launch<bf16_bits, bf16_bits>(a, s) : step_launch<bf16_bits, float>(a, s);
+    return a.x_bf16 ? step_launch<float, bf16_bits>(a, s) : step_launch<float, float>(a, s);
+}
+
+}  // namespace sru

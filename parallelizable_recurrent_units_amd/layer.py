@@ -117,6 +117,19 @@ def attention_forward(shape, cfg, X, Wq, Wkv, Wo, gamma=None, beta=None, KV=None
     return Q, KV, R, U
 
 
+def step(shape, x, W, v, b, c=None, h=None, stream=None):
+    """One decoding step: (h, c_next) for input rows x [B, d] from state c
+    [B, d] (zero when None).  Pass the same tensor as ``c`` each call to carry
+    the state in place; h is allocated unless given."""
+    s = B._shape(shape)
+    f32 = dict(device=x.device, dtype=torch.float32)
+    if h is None:
+        h = torch.empty((s.B, s.d), **f32)
+    c_next = c if c is not None else torch.empty((s.B, s.d), **f32)
+    B.sru_step(s, x, W, v, b, c, h, c_next, stream)
+    return h, c_next
+
+
 def forward(shape, U, x, v, b, c0=None, keep_c_seq=False, stream=None):
     s = B._shape(shape)
     dev = U.device

@@ -307,6 +307,32 @@ def test_attention_workspace_and_validation(lib):
                     beta=Q[3] + (1 << 30) + 4096) == sru.SRU_ERR_NO_DEVICE
 
 
+def stepc(lib, s, **kw):
+    a = dict(x=Q[0], x_dt=0, W=Q[1], w_dt=1, v=Q[2], b=Q[2] + 4096, c=None, h=Q[3],
+             cn=Q[3] + (1 << 30))
+    a.update(kw)
+    return lib.sru_step(ctypes.byref(s), a["x"], a["x_dt"], a["W"], a["w_dt"], a["v"], a["b"],
+                        a["c"], a["h"], a["cn"], None)
+
+
+def test_step_validation(lib):
+    s = sru.SruShape(1, 4, 256, 0, 1.0)
+    assert stepc(lib, sru.SruShape(2, 4, 256, 0, 1.0)) == sru.SRU_ERR_INVALID_ARG
+    assert stepc(lib, sru.SruShape(1, 4, 256, 1, 1.0)) == sru.SRU_ERR_INVALID_ARG
+    assert b"unidirectional" in lib.sru_last_error()
+    assert stepc(lib, s, W=None) == sru.SRU_ERR_INVALID_ARG
+    assert stepc(lib, s, w_dt=3) == sru.SRU_ERR_INVALID_ARG
+    assert stepc(lib, s, c=Q[3] + (2 << 30) + 4) == sru.SRU_ERR_INVALID_ARG   # misaligned
+    assert stepc(lib, s, h=Q[3], cn=Q[3] + 64) == sru.SRU_ERR_INVALID_ARG       # h and c_next
+    assert stepc(lib, s, c=Q[3] + (1 << 30) + 16) == sru.SRU_ERR_INVALID_ARG   # partial alias
+    assert stepc(lib, s, h=Q[1] + 64) == sru.SRU_ERR_INVALID_ARG               # h inside W
+    import torch
+    if torch.cuda.device_count() == 0:
+        assert stepc(lib, s) == sru.SRU_ERR_NO_DEVICE
+        # the state updated in place is allowed
+        assert stepc(lib, s, c=Q[3] + (1 << 30)) == sru.SRU_ERR_NO_DEVICE
+
+
 def test_binding_raises_sru_error(lib):
     s = sru.SruShape(8, 2, 64, 0, 1.0)
     with pytest.raises(sru.SruError) as ei:
