@@ -708,17 +708,19 @@ def main():
         rt = sum(rows[n] for n in rec_rows)
         line["recurrence_fwd_bwd"] = {"GB/s": rb / rt / 1e9, "frac_of_hbm_peak": rb / rt / 1e9 / HBM_PEAK_GBS,
                                       "elem_steps_per_s": w.elem_steps / rt, "rows": rec_rows}
-    ceil = copy_ceiling()
+    # counter runs (--copy-probe-mib) skip the ceiling: its 2 GiB copies would
+    # be taken for the calibration copy
+    ceil = None if args.copy_probe_mib else copy_ceiling()
     line["copy_ceiling"] = ceil
     for r in per_row.values():
-        if r["unit"] == "GB/s":
+        if ceil and r["unit"] == "GB/s":
             r["frac_of_copy_ceiling"] = r["achieved"] / ceil["GB/s"]
     if not args.no_extras:
         print("[bench] other workloads", file=sys.stderr, flush=True)
         line["other_workloads"] = extras(args.workload, max(10, args.steps // 2))
         for rows_w in line["other_workloads"].values():
             for r in rows_w.values():
-                if isinstance(r, dict) and r.get("unit") == "GB/s":
+                if ceil and isinstance(r, dict) and r.get("unit") == "GB/s":
                     r["frac_of_copy_ceiling"] = r["achieved"] / ceil["GB/s"]
     if not args.no_cpu_baseline and w.mode == "layer":
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
