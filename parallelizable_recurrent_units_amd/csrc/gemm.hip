@@ -562,6 +562,280 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(
     }
 }
 
+// ---- bf16 x bf16^T with operands copied straight into LDS ------------------
+// C[M, N] (+)= A[M, K] B[N, K]^T for bf16 A and B (16-byte aligned rows; K a
+// multiple of 64), fp32 C.  Each k-tile of A and B (rows of 64 bf16 = 128
+// bytes) travels from memory to LDS by global_load_lds_dwordx4: one instruction moves 64 lanes x 16 bytes
+// into 1 KB of LDS, so the operands take no registers on the way and no LDS
+// write instructions.  NS LDS stages form a ring: k-tile kt + NS - 1 is
+// requested while k-tile kt is multiplied, and a wave waits (vmcnt) only for
+// its own requests of k-tile kt before the barrier that publishes the stage.
+// Inside a row the sixteen-byte piece holding k-chunk c sits at position
+// c ^ (row % 8), so the fragment reads of eight consecutive rows hit eight
+// different bank groups.  (fp32 A is not taken: converted as its fragments
+// are read, by every wave that reads them, it is slower than the register-
+// staged kernel, which converts each element once.)
+template <int N_> __device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N_ >= 0 && N_ < 64, "vmcnt is 6 bits");
+    // vmcnt[3:0] | expcnt[6:4] = 7 | lgkmcnt[11:8] = 15 | vmcnt[5:4] at [15:14]
+    __builtin_amdgcn_s_waitcnt((N_ & 15) | (7 << 4) | (15 << 8) | ((N_ >> 4) << 14));
+}
+
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// 16 bytes per lane from gptr into LDS at lds_base + 16 * lane (lds_base is
+// wave-uniform; M0 carries it).  The instruction has no register result; the
+// caller accounts for its completion with wait_vmcnt.
+__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_base), "v"(gptr)
+                 : "memory");
+}
+
+template <int BM_, int BN_, int NS_, int WGM_, int WGN_, int MINB_>
+struct LdsCfg {
+    static constexpr int BM = BM_, BN = BN_, NS = NS_, WGM = WGM_, WGN = WGN_, MINB = MINB_;
+    static constexpr int NT = 64 * WGM * WGN, NW = NT / 64;
+    static constexpr int WM = BM / WGM, WN = BN / WGN, TI = WM / 32, TJ = WN / 32;
+    static constexpr int EPI_LD = WN + 4;
+};
+
+// Stage layout for an A of element type TA: BM rows of 64 A elements (128 or
+// 256 bytes), then BN rows of 64 bf16 of B (128 bytes); 1 KB requests.
+template <class Cfg, typename TA> struct LdsStage {
+    static constexpr int AROW = 64 * (int)sizeof(TA);   // bytes of one A row
+    static constexpr int APR = AROW / 16;                // 16-byte pieces per A row
+    static constexpr int A_BYTES = Cfg::BM * AROW;
+    static constexpr int BYTES = A_BYTES + Cfg::BN * 128;
+    static constexpr int QA = A_BYTES / 1024;            // requests for A
+    static constexpr int Q = BYTES / 1024;
+    static constexpr int IPW = Q / Cfg::NW;              // requests per wave per stage
+    static_assert(IPW * Cfg::NW == Q, "whole 1 KB requests per wave");
+    static_assert(Cfg::NW * 32 * Cfg::EPI_LD * 4 <= Cfg::NS * BYTES, "epilogue staging fits");
+};
+
+// 256 x 256 tiles, 8 waves, two stages: long reductions on grids that fill
+// the chip.  128 x 128 tiles, 8 waves, four stages (one block per CU): long
+// reductions on smaller grids, where an operand streamed from HBM needs
+// requests several k-tiles ahead.  128 x 128 tiles, 4 waves, two stages (two
+// blocks per CU): short reductions.
+typedef LdsCfg<256, 256, 2, 2, 4, 1> LdsBig;
+typedef LdsCfg<128, 128, 4, 2, 4, 1> LdsDeep;
+typedef LdsCfg<128, 128, 2, 2, 2, 2> LdsSmall;
+
+template <class Cfg, typename TA>
+__global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *__restrict__ A,
+                                                               const bf16_bits *__restrict__ B,
+                                                               float *__restrict__ C)
+{
+    typedef LdsStage<Cfg, TA> St;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, NS = Cfg::NS, IPW = St::IPW;
+    constexpr int WM = Cfg::WM, WN = Cfg::WN, TI = Cfg::TI, TJ = Cfg::TJ;
+    constexpr int SB = St::BYTES, AROW = St::AROW, APR = St::APR;
+    __shared__ __attribute__((aligned(16))) char smem[NS * SB];
+
+    const int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb, ldc = p.ldc;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
+    A += (int64_t)blockIdx.y * p.sa;
+    B += (int64_t)blockIdx.y * p.sb;
+    C += (int64_t)blockIdx.y * p.sc;
+    const int64_t TM = (M + BM - 1) / BM, TN = (N + BN - 1) / BN;
+    int64_t tm, tn;
+    tile_of((int64_t)blockIdx.x, TM, TN, p.gm, &tm, &tn);
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;    // low half of a flat LDS address
+
+    // this lane's source of each of the wave's requests, at k = 0.  Request q
+    // fills 1 KB of the stage: 1024 / AROW rows of A (q < QA) or 8 rows of B.
+    // Lane l takes piece l % (pieces per row) of row l / (pieces per row); in
+    // a row the piece at position s holds k-chunk s ^ (row % pieces per row).
+    // Rows past M or N repeat the last row (loaded, never stored).
+    const char *src[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int q = wave * IPW + i;
+        if (q < St::QA) {
+            const int row = q * (1024 / AROW) + lane / APR;
+            const int c = (lane % APR) ^ (row % APR);
+            const int64_t m = m0 + row < M ? m0 + row : M - 1;
+            src[i] = (const char *)(A + m * lda) + 16 * c;
+        } else {
+            const int row = (q - St::QA) * 8 + lane / 8;
+            const int c = (lane % 8) ^ (row % 8);
+            const int64_t n = n0 + row < N ? n0 + row : N - 1;
+            src[i] = (const char *)(B + n * ldb) + 16 * c;
+        }
+    }
+    const int64_t KT = K / 64;
+    // requests of k-tile kt into stage st; past the last k-tile the last one
+    // is requested again, so every iteration waits on the same count
+    auto issue = [&](int64_t kt, int st) {
+        const int64_t k0 = (kt < KT ? kt : KT - 1) * 64;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int q = wave * IPW + i;
+            const int64_t off = k0 * (q < St::QA ? (int64_t)sizeof(TA) : 2);
+            dma16(src[i] + off, __builtin_amdgcn_readfirstlane(lds0 + st * SB + q * 1024));
+        }
+    };
+
+    f32x16 acc[TI][TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int r32 = lane & 31, hi = lane >> 5;
+    // fragment of 8 k-values (16 ks + 8 hi ..) of A row `row` / B row `row`
+    static_assert(sizeof(TA) == 2, "bf16 A");
+    auto afrag = [&](int st, int row, int ks) -> bf16x8 {
+        const int c = 2 * ks + hi;
+        return *(const bf16x8 *)(smem + st * SB + row * AROW + ((c ^ (row % APR)) << 4));
+    };
+    auto bfrag = [&](int st, int row, int ks) -> bf16x8 {
+        const int c = 2 * ks + hi;
+        return *(const bf16x8 *)(smem + st * SB + St::A_BYTES + row * 128 + ((c ^ (row & 7)) << 4));
+    };
+
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st) issue(st, st);
+    for (int64_t kt = 0; kt < KT; ++kt) {
+        const int st = (int)(kt % NS);
+        wait_vmcnt<(NS - 2) * IPW>();                    // this wave's share of k-tile kt
+        wait_lgkm0();                                    // and its reads of the last stage
+        __builtin_amdgcn_s_barrier();
+        issue(kt + NS - 1, (int)((kt + NS - 1) % NS));   // into the stage read last time
+        bf16x8 a[2][TI], b[2][TJ];
+        auto rd = [&](int buf, int ks) {
+#pragma unroll
+            for (int i = 0; i < TI; ++i) a[buf][i] = afrag(st, wm * WM + i * 32 + r32, ks);
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) b[buf][j] = bfrag(st, wn * WN + j * 32 + r32, ks);
+        };
+        rd(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int cur = ks & 1;
+            if (ks < 3) rd(cur ^ 1, ks + 1);
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j],
+                                                                        acc[i][j], 0, 0, 0);
+            if (ks < 3) {   // one fragment read between groups of MFMAs
+                constexpr int NF = TI + TJ, MF = TI * TJ;
+#pragma unroll
+                for (int t = 0; t < NF; ++t) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, MF / NF > 0 ? MF / NF : 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    wait_vmcnt<0>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+
+    // epilogue through LDS, one 32-row band per wave at a time (the 32x32
+    // accumulator holds column lane & 31, rows 8 (r / 4) + 4 (lane / 32) + r % 4)
+    constexpr int EPI_LD = Cfg::EPI_LD, C4 = WN / 4;
+    float *stage = (float *)smem + wave * (32 * EPI_LD);
+    const int64_t nw = n0 + wn * WN;
+    const bool vec = N % 4 == 0 && ldc % 4 == 0 && p.sc % 4 == 0 && ((uintptr_t)C & 15u) == 0;
+    const bool accumulate = p.accumulate;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                stage[(8 * (r / 4) + 4 * hi + (r % 4)) * EPI_LD + j * 32 + r32] = acc[i][j][r];
+        const int64_t mw = m0 + wm * WM + i * 32;
+#pragma unroll 4
+        for (int it = 0; it < 32 * C4 / 64; ++it) {
+            const int idx = it * 64 + lane;
+            const int row = idx / C4, c4 = idx % C4;
+            const int64_t m = mw + row, n = nw + c4 * 4;
+            if (m >= M) continue;
+            const float4 v = *(const float4 *)(stage + row * EPI_LD + c4 * 4);
+            float *q = C + m * ldc + n;
+            if (vec) {
+                if (n < N) {
+                    float4 o = v;
+                    if (accumulate) {
+                        const float4 c = *(const float4 *)q;
+                        o.x += c.x; o.y += c.y; o.z += c.z; o.w += c.w;
+                    }
+                    *(float4 *)q = o;
+                }
+            } else {
+                const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) q[e] = accumulate ? q[e] + vv[e] : vv[e];
+            }
+        }
+    }
+}
+
+// The bf16 x bf16^T products that gemm_lds takes: whole 64-deep k-tiles,
+// 16-byte aligned operand rows and batch offsets.
+bool lds_path_ok(const GemmArgs &g)
+{
+    if (!g.a_bf16 || !g.b_bf16 || g.b_kn || g.K % 64 != 0 || g.K < 64) return false;
+    const int64_t lda = g.lda ? g.lda : g.K, ldb = g.ldb ? g.ldb : g.K;
+    auto al16 = [](const void *q) { return ((uintptr_t)q & 15u) == 0; };
+    return lda % 8 == 0 && ldb % 8 == 0 && g.sa % 8 == 0 && g.sb % 8 == 0 && al16(g.A) &&
+           al16(g.Bm);
+}
+
+template <class Cfg, typename TA>
+hipError_t lds_launch_cfg(const GemmArgs &g, hipStream_t s)
+{
+    MM p;
+    p.M = g.M;
+    p.N = g.N;
+    p.K = g.K;
+    p.lda = g.lda ? g.lda : g.K;
+    p.ldb = g.ldb ? g.ldb : g.K;
+    p.ldc = g.ldc ? g.ldc : g.N;
+    p.sa = g.sa;
+    p.sb = g.sb;
+    p.sc = g.sc;
+    p.ksplit = g.K;
+    p.gm = 8;
+    p.accumulate = g.accumulate;
+    const int64_t tiles = ((g.M + Cfg::BM - 1) / Cfg::BM) * ((g.N + Cfg::BN - 1) / Cfg::BN);
+    hipLaunchKernelGGL((gemm_lds<Cfg, TA>),
+                       dim3((unsigned)tiles, (unsigned)(g.batch > 0 ? g.batch : 1)),
+                       dim3(Cfg::NT), 0, s, p, (const TA *)g.A, (const bf16_bits *)g.Bm, g.C);
+    return hipGetLastError();
+}
+
+template <typename TA>
+hipError_t lds_launch_t(const GemmArgs &g, hipStream_t s)
+{
+    // the large tiles once they give every CU one and the reduction is long
+    // enough to amortise their prologue and epilogue; deep small tiles for
+    // other long reductions; two small blocks per CU for short ones
+    const int64_t big = ((g.M + 255) / 256) * ((g.N + 255) / 256) * (g.batch > 0 ? g.batch : 1);
+    if (g.K >= 1024) {
+        if (big >= 256) return lds_launch_cfg<LdsBig, TA>(g, s);
+        return lds_launch_cfg<LdsDeep, TA>(g, s);
+    }
+    return lds_launch_cfg<LdsSmall, TA>(g, s);
+}
+
+hipError_t lds_launch(const GemmArgs &g, hipStream_t s) { return lds_launch_t<bf16_bits>(g, s); }
+
 // dst[c][r] = src[r][c] for a rows x cols matrix of 2-byte elements, one
 // 64 x 64 tile per block.  VEC (rows % 8 == 0 and cols % 8 == 0): every
 // global access moves 16 bytes (8 elements of a row in, 8 of a column out)
@@ -917,6 +1191,7 @@ hipError_t launch_gemm_bf16_out(const GemmArgs &g, hipStream_t s)
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s)
 {
     if (g.b_bf16) {
+        if (lds_path_ok(g)) return lds_launch(g, s);
         if (g.a_bf16)
             return g.b_kn ? mfma_launch<bf16_bits, true>(g, s) : mfma_launch<bf16_bits, false>(g, s);
         return g.b_kn ? mfma_launch<float, true>(g, s) : mfma_launch<float, false>(g, s);

@@ -316,6 +316,42 @@ def test_projection_bwd_weight_is_deterministic():
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
+# bf16 dU times the transposed bf16 weights: the products whose operands go
+# straight to LDS (whole 64-deep k-tiles), at ragged M and N, one k-tile up to
+# long reductions, with accumulation; the last case takes the 256 x 256 tiles
+# (sampled rows, the last ragged tile included).
+@pytest.mark.parametrize("L,B,d,nd", [(3, 5, 64, 1), (7, 19, 128, 2), (64, 4, 256, 2),
+                                      (33, 3, 64, 1), (1, 1, 64, 1), (40, 50, 512, 2),
+                                      (100, 164, 1024, 1)])
+def test_bwd_data_bf16_dU_transposed_weight(L, B, d, nd):
+    import torch
+    rng = np.random.default_rng(6000 + d + L)
+    M = L * B
+    shape = SruShape(L, B, d, nd == 2, 1.0)
+    W_bits, W = workloads.to_bf16(rng.uniform(-0.1, 0.1, (nd * 3 * d, d)).astype(np.float32))
+    G_bits, G = workloads.to_bf16(rng.standard_normal((L, B, nd, 3, d)).astype(np.float32))
+    C0 = rng.standard_normal((L, B, d)).astype(np.float32)
+    Wd = torch.from_numpy(W_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    Gd = torch.from_numpy(G_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    Wt = layer.transpose_weight(shape, Wd)
+    dX = torch.from_numpy(C0.copy()).cuda()
+    print(f"case M={M} N={d} K={nd * 3 * d}", flush=True)
+    layer.project_bwd_data(shape, Gd, Wd, dX, accumulate=True, Wt=Wt)
+    G2 = G.reshape(M, -1)
+    if M * d * nd * 3 * d <= 1 << 31:
+        want = oracle.project_bwd_data(G2, W) + C0.reshape(M, d)
+        check("dX (bf16 dU, W^T)", host(dX).reshape(M, d), want, GEMM_ACC)
+    else:
+        rows = np.unique(np.concatenate([np.arange(M - 130, M), np.arange(0, 40),
+                                         rng.integers(0, M, 60)]))
+        want = oracle.project_bwd_data(G2, W, rows=rows) + C0.reshape(M, d)[rows]
+        check("dX (bf16 dU, W^T; sampled rows)", host(dX).reshape(M, d)[rows], want, GEMM_ACC)
+    # the same product without accumulation
+    dX1 = layer.project_bwd_data(shape, Gd, Wd, Wt=Wt)
+    check("dX == accumulated - C0", host(dX1).reshape(M, d), host(dX).reshape(M, d) - C0.reshape(M, d),
+          1e-6)
+
+
 def test_projection_fp32_config1():
     """Workload 1 (fp32 throughout): projection + forward at the 1e-5 bar."""
     w = workloads.WORKLOADS[1]
