@@ -218,7 +218,9 @@ def device_set(w, seed):
 
 
 def training_step_rows(shape, t):
-    """The four row calls of one training step, each a C-ABI entry point."""
+    """The four row calls of one training step (C-ABI entry points).  The
+    projection reads fp32 X and rounds it to bf16 as it stages it: at these
+    shapes that is faster than rounding X into a bf16 copy first."""
     from parallelizable_recurrent_units_amd import (SRU_PROJ_BWD_DATA_WT, SRU_PROJ_FWD,
                                                     sru_backward, sru_forward, sru_project,
                                                     sru_transpose_weight)
@@ -263,8 +265,8 @@ def next_rows(shape, t):
                                         t["dWo"], SRU_BF16, False, t["ws_f"])
 
     rows = [("f1_projection_bwd_weight",
-             lambda: sru_project_bwd_weight(shape, t["dU_lp"], t["x"], t["dW"], SRU_BF16, False,
-                                            t["ws_w"])),
+             lambda: sru_project_bwd_weight(shape, t["dU_lp"], t["x"], t["dW"], SRU_BF16,
+                                            False, t["ws_w"])),
             ("f3_factored_forward", fact_fwd),
             ("f3_factored_backward", fact_bwd)]
     if not shape.bidirectional:
@@ -507,7 +509,8 @@ ROW_LAUNCHES = {
     "a3_a4_backward": ["per direction, last one first (the first adds to dx): bwd_fast "
                        "(fp32 inputs, up to 128 steps) or scan_clear + bwd_scan",
                        "param_reduce (dv, db)"],
-    "a5_projection_bwd_data": ["transpose16 (W -> W^T)", "gemm_bf16_mfma (A = bf16 dU copy)"],
+    "a5_projection_bwd_data": ["transpose16 (W -> W^T)",
+                               "gemm_lds (bf16 dU copy x bf16 W, operands copied straight into LDS)"],
     "a6_linear_forward": ["scan_clear", "lin_fwd_fused"],
     "a7_linear_backward": ["scan_clear", "lin_bwd_fused", "lin_db_reduce"],
     "f1_projection_bwd_weight": ["gemm_bf16_mfma (A = bf16 dU copy and B = fp32 X, both read "
@@ -534,10 +537,8 @@ ROW_KERNELS = {
     "a2_forward": ([r"fwd_fast<"], r"fwd_fast<"),
     "a3_a4_backward": ([r"bwd_scan<", r"bwd_fast<", r"scan_clear", r"param_reduce"],
                        r"param_reduce"),
-    "a5_projection_bwd_data": ([r"transpose16", r"gemm_bf16_mfma<.*>, unsigned short, false, "],
+    "a5_projection_bwd_data": ([r"transpose16", r"gemm_lds<.*LdsCfg<128, 128, 4, 2, 4, 1>"],
                                r"transpose16"),
-    "f1_projection_bwd_weight": ([r"gemm_bf16_mfma<.*>, unsigned short, true, ", r"split_reduce"],
-                                 r"gemm_bf16_mfma<.*>, unsigned short, true, "),
 }
 
 

@@ -336,6 +336,16 @@ sru_status sru_linear_scan(const sru_shape *shape, sru_pass pass, int32_t chunk,
 sru_status sru_transpose_weight(const sru_shape *shape, const void *W, sru_dtype w_dt,
                                 void *Wt, void *stream);
 
+/*
+ * dst[i] = bf16(src[i]) for i < n, rounded to nearest even: the operand X~ of
+ * Eq. 1 (SRU++ paper, background section) as the bf16 projection multiplies
+ * it.  A caller that keeps X~ hands it to sru_project (half the bytes of fp32
+ * X, the same product) and to sru_project_bwd_weight (the same X~ the
+ * gradient needs).  src fp32, dst bf16, both 16-byte aligned, not
+ * overlapping; n >= 1.
+ */
+sru_status sru_round_bf16(int64_t n, const float *src, void *dst, void *stream);
+
 /* Workspace bytes needed by `op` for `shape` (and `chunk`: the chunk length
  * for the linear mode, the inner dimension d' for SRU_WS_FACTORED_WEIGHT);
  * 0 either when none is needed or on invalid arguments (then

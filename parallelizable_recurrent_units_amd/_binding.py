@@ -28,7 +28,8 @@ SRU_FACT_WGRAD_Q, SRU_FACT_WGRAD_O = 0, 1
 EXPORTED = ("sru_project", "sru_project_bwd_weight", "sru_project_factored",
             "sru_project_factored_bwd_weight", "sru_attention_forward",
             "sru_attention_workspace_size", "sru_step", "sru_forward", "sru_backward", "sru_linear_scan",
-            "sru_transpose_weight", "sru_workspace_size", "sru_status_string", "sru_last_error")
+            "sru_transpose_weight", "sru_round_bf16", "sru_workspace_size", "sru_status_string",
+            "sru_last_error")
 
 
 class SruShape(ctypes.Structure):
@@ -101,6 +102,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sru_step.restype = ctypes.c_int
     lib.sru_step.argtypes = [sp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
                              _vp]
+    lib.sru_round_bf16.restype = ctypes.c_int
+    lib.sru_round_bf16.argtypes = [ctypes.c_int64, _vp, _vp, _vp]
     lib.sru_forward.restype = ctypes.c_int
     lib.sru_forward.argtypes = [sp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
                                 ctypes.c_int, _vp, _vp, _vp]
@@ -238,6 +241,14 @@ def sru_step(shape, x, W, v, b, c_prev, h, c_next, stream=None):
     _check(load_library().sru_step(ctypes.byref(s), _ptr(x), _dtype_code(x), _ptr(W),
                                    _dtype_code(W), _ptr(v), _ptr(b), _ptr(c_prev), _ptr(h),
                                    _ptr(c_next), _stream(stream)))
+
+
+def sru_round_bf16(src, dst, stream=None):
+    if _dtype_code(src) != SRU_F32 or _dtype_code(dst) != SRU_BF16:
+        raise TypeError("src must be float32 and dst bfloat16")
+    if src.numel() != dst.numel():
+        raise ValueError("src and dst differ in size")
+    _check(load_library().sru_round_bf16(int(src.numel()), _ptr(src), _ptr(dst), _stream(stream)))
 
 
 def sru_transpose_weight(shape, W, Wt, stream=None):

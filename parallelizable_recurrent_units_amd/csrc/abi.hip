@@ -521,6 +521,17 @@ sru_status sru_step(const sru_shape *shape, const void *x, sru_dtype x_dt, const
     return launched(sru::launch_step(a, (hipStream_t)stream), "step");
 }
 
+sru_status sru_round_bf16(int64_t n, const float *src, void *dst, void *stream)
+{
+    if (n < 1 || n > kMaxElems) return fail(SRU_ERR_INVALID_ARG, "n must be in [1, 2^56]");
+    SRU_TRY(need_ptr(src, "src"));
+    SRU_TRY(need_ptr(dst, "dst"));
+    if (overlaps(src, (size_t)n * 4, dst, (size_t)n * 2))
+        return fail(SRU_ERR_INVALID_ARG, "src and dst overlap");
+    SRU_TRY(need_device());
+    return launched(sru::launch_round_bf16(n, src, dst, (hipStream_t)stream), "bf16 rounding");
+}
+
 sru_status sru_transpose_weight(const sru_shape *shape, const void *W, sru_dtype w_dt, void *Wt,
                                 void *stream)
 {

@@ -836,6 +836,21 @@ hipError_t lds_launch_t(const GemmArgs &g, hipStream_t s)
 
 hipError_t lds_launch(const GemmArgs &g, hipStream_t s) { return lds_launch_t<bf16_bits>(g, s); }
 
+// dst[i] = bf16(src[i]) (nearest even), four elements per lane and step.
+__global__ __launch_bounds__(256) void round_bf16_kernel(int64_t n, const float *__restrict__ src,
+                                                         bf16_bits *__restrict__ dst)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+    for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += stride) {
+        if (i + 4 <= n) {
+            const float4 v = *(const float4 *)(src + i);
+            *(u32x2 *)(dst + i) = u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+        } else {
+            for (int64_t e = i; e < n; ++e) dst[e] = f32_to_bf16(src[e]);
+        }
+    }
+}
+
 // dst[c][r] = src[r][c] for a rows x cols matrix of 2-byte elements, one
 // 64 x 64 tile per block.  VEC (rows % 8 == 0 and cols % 8 == 0): every
 // global access moves 16 bytes (8 elements of a row in, 8 of a column out)
@@ -1144,6 +1159,14 @@ hipError_t f32_launch(const GemmArgs &g, hipStream_t s)
 }
 
 }  // namespace
+
+hipError_t launch_round_bf16(int64_t n, const float *src, void *dst, hipStream_t s)
+{
+    const int64_t blocks = (n + 1023) / 1024;
+    hipLaunchKernelGGL(round_bf16_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)),
+                       dim3(256), 0, s, n, src, (bf16_bits *)dst);
+    return hipGetLastError();
+}
 
 hipError_t launch_transpose(int64_t rows, int64_t cols, const void *src, void *dst, bool two_byte,
                             hipStream_t s)

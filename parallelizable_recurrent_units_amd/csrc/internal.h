@@ -130,6 +130,8 @@ struct StepArgs {
 };
 hipError_t launch_step(const StepArgs &a, hipStream_t s);
 
+// dst[i] = bf16(src[i]), nearest even (dst: 2-byte elements).
+hipError_t launch_round_bf16(int64_t n, const float *src, void *dst, hipStream_t s);
 // dst[cols, rows] = src[rows, cols]^T (2-byte or 4-byte elements).
 hipError_t launch_transpose(int64_t rows, int64_t cols, const void *src, void *dst, bool two_byte,
                             hipStream_t s);

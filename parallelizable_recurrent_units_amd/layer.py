@@ -10,6 +10,14 @@ import torch
 from . import _binding as B
 
 
+def round_bf16(x, out=None, stream=None):
+    """bf16(x), nearest even (the operand X~ of the bf16 projection)."""
+    if out is None:
+        out = torch.empty(x.shape, device=x.device, dtype=torch.bfloat16)
+    B.sru_round_bf16(x, out, stream)
+    return out
+
+
 def project(shape, X, W, U=None, accumulate=False, stream=None):
     """Eq. 1: U[L*B, ndir*3d] (+)= X W^T (X rounded to bf16 when W is bf16)."""
     s = B._shape(shape)

@@ -28,7 +28,7 @@ def lib():
 
 def header_functions():
     text = open(os.path.join(ROOT, "include", "sru.h")).read()
-    return sorted(set(re.findall(r"\b(sru_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(sru_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -331,6 +331,16 @@ def test_step_validation(lib):
         assert stepc(lib, s) == sru.SRU_ERR_NO_DEVICE
         # the state updated in place is allowed
         assert stepc(lib, s, c=Q[3] + (1 << 30)) == sru.SRU_ERR_NO_DEVICE
+
+
+def test_round_bf16_validation(lib):
+    assert lib.sru_round_bf16(0, Q[0], Q[1], None) == sru.SRU_ERR_INVALID_ARG
+    assert lib.sru_round_bf16(16, None, Q[1], None) == sru.SRU_ERR_INVALID_ARG
+    assert lib.sru_round_bf16(16, Q[0], Q[0] + 32, None) == sru.SRU_ERR_INVALID_ARG   # overlap
+    assert lib.sru_round_bf16(16, Q[0], Q[1] + 2, None) == sru.SRU_ERR_INVALID_ARG    # misaligned
+    import torch
+    if torch.cuda.device_count() == 0:
+        assert lib.sru_round_bf16(16, Q[0], Q[1], None) == sru.SRU_ERR_NO_DEVICE
 
 
 def test_binding_raises_sru_error(lib):

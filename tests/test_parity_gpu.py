@@ -352,6 +352,26 @@ def test_bwd_data_bf16_dU_transposed_weight(L, B, d, nd):
           1e-6)
 
 
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 1000003])
+def test_round_bf16_exact(n):
+    """sru_round_bf16 bit for bit against the oracle's rounding (ties, both
+    parities of the kept bit, infinities, tiny and huge values, NaN)."""
+    import torch
+    rng = np.random.default_rng(n)
+    x = (rng.standard_normal(n) * 10.0 ** rng.integers(-30, 30, n)).astype(np.float32)
+    special = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), np.inf, -np.inf,
+                        3.3895314e38, 1e-40, 0.0, -0.0], np.float32)
+    x[:min(n, special.size)] = special[:min(n, special.size)]
+    got = layer.round_bf16(torch.from_numpy(x).cuda())
+    want = oracle.round_bf16(x)
+    g = got.float().cpu().numpy()
+    assert np.array_equal(g.view(np.uint32), want.view(np.uint32))
+    if n > 10:
+        x[7] = np.nan
+        g = layer.round_bf16(torch.from_numpy(x).cuda()).float().cpu().numpy()
+        assert np.isnan(g[7])
+
+
 def test_projection_fp32_config1():
     """Workload 1 (fp32 throughout): projection + forward at the 1e-5 bar."""
     w = workloads.WORKLOADS[1]

@@ -37,6 +37,8 @@ def _sum_bound_check(name, gpu, terms_sum, terms_abs_sum, n_terms):
 
 
 def training_step(w, t):
+    """The step as the benchmark runs it, plus the weight gradient (which the
+    benchmark times beside the step)."""
     shape = SruShape(w.L, w.B, w.d, w.ndir == 2, w.alpha)
     U = layer.project(shape, t["x"], t["W"])
     h, c_seq, c_last = layer.forward(shape, U, t["x"], t["v"], t["b"], t["c0"], keep_c_seq=True)
