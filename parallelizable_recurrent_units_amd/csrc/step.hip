@@ -13,6 +13,8 @@
 // dot products with x~ (per-lane partial sums over 8-element pieces, then a
 // wave reduction); the cell runs one batch row per lane.  W is read from
 // memory once per step; x (B x d) is read by every wave from the caches.
+// From 8 batch rows on, with bf16 W, step_mfma below forms the products on
+// the matrix cores instead.
 #include "device_common.h"
 #include "internal.h"
 
@@ -157,9 +159,105 @@ __global__ __launch_bounds__(256) void step_cell(StepArgs a)
     }
 }
 
+// Batches of rows with bf16 W (d % 32 == 0, d <= 2048): the products as
+// bf16 MFMAs.  A block owns 32 channels and 32 batch rows.  It rounds its x
+// rows to bf16 into LDS once (row pitch d + 8 keeps the fragment reads of
+// eight rows on different banks); wave w multiplies them by the 32 W rows of
+// gate w % 3 over half w / 3 of the reduction (v_mfma_f32_32x32x16_bf16, W
+// fragments loaded straight from memory); the two halves meet in LDS and the
+// block applies the cell to its 32 x 32 (batch row, channel) pairs.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+constexpr int kStepRows = 32, kStepWaves = 6;
+
+template <typename TX>
+__global__ __launch_bounds__(64 * kStepWaves) void step_mfma(StepArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int64_t d = a.d, P = d + 8;                    // LDS row pitch (bf16)
+    bf16_bits *xs = (bf16_bits *)smem;                   // [32][P]
+    float *red = (float *)(smem + kStepRows * P * 2);    // [2][3][32][33]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t ngroups = d / 32;
+    const int64_t j0 = (blockIdx.x % ngroups) * 32;
+    const int64_t b0 = (blockIdx.x / ngroups) * kStepRows;
+    const TX *X = (const TX *)a.x;
+    const bf16_bits *W = (const bf16_bits *)a.W;
+
+    // x~ rows b0 .. b0 + 31 (rows past B repeat the last one; never written)
+    for (int64_t i = tid; i < kStepRows * d / 4; i += 64 * kStepWaves) {
+        const int64_t r = (4 * i) / d, k = (4 * i) % d;
+        const int64_t b = b0 + r < a.B ? b0 + r : a.B - 1;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = load_as_f32(X + b * d + k + e);
+        *(uint2 *)(xs + r * P + k) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
+    __syncthreads();
+
+    const int g = wave % 3, kh = wave / 3;
+    const int64_t K2 = d / 2, kb = kh * K2;
+    const int r32 = lane & 31, hi = lane >> 5;
+    const bf16_bits *wrow = W + (g * d + j0 + r32) * d + kb + 8 * hi;
+    const bf16_bits *xrow = xs + r32 * P + kb + 8 * hi;
+    f32x16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    constexpr int U = 8;                                 // k-steps whose W loads are in flight
+    const int64_t steps = K2 / 16;
+    int64_t ks = 0;
+    for (; ks + U <= steps; ks += U) {
+        bf16x8_t wf[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) wf[u] = *(const bf16x8_t *)(wrow + 16 * (ks + u));
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bf16x8_t xf = *(const bf16x8_t *)(xrow + 16 * (ks + u));
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, wf[u], acc, 0, 0, 0);
+        }
+    }
+    for (; ks < steps; ++ks) {
+        const bf16x8_t wf = *(const bf16x8_t *)(wrow + 16 * ks);
+        const bf16x8_t xf = *(const bf16x8_t *)(xrow + 16 * ks);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, wf, acc, 0, 0, 0);
+    }
+    // acc holds row (batch) 8 (r / 4) + 4 hi + r % 4, column (channel) r32
+    float *rw = red + ((kh * 3 + g) * 32) * 33;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rw[(8 * (r / 4) + 4 * hi + (r % 4)) * 33 + r32] = acc[r];
+    __syncthreads();
+
+    for (int idx = tid; idx < kStepRows * 32; idx += 64 * kStepWaves) {
+        const int r = idx / 32, n = idx % 32;
+        const int64_t b = b0 + r, j = j0 + n;
+        if (b >= a.B) continue;
+        float u[3];
+#pragma unroll
+        for (int gg = 0; gg < 3; ++gg)
+            u[gg] = red[(gg * 32 + r) * 33 + n] + red[((3 + gg) * 32 + r) * 33 + n];
+        const float c = a.c_prev ? a.c_prev[b * d + j] : 0.0f;
+        cell(a, b, j, a.v[j], a.v[d + j], a.b[j], a.b[d + j], c, u[0], u[1], u[2],
+             load_as_f32(X + b * d + j));
+    }
+}
+
+size_t step_mfma_lds(int64_t d) { return (size_t)kStepRows * (d + 8) * 2 + 2 * 3 * 32 * 33 * 4; }
+
 template <typename TW, typename TX>
 hipError_t step_launch(const StepArgs &a, hipStream_t s)
 {
+    if constexpr (sizeof(TW) == 2) {
+        if (a.B >= 8 && a.d % 32 == 0 && a.d <= 2048) {
+            const int64_t blocks = (a.d / 32) * ((a.B + kStepRows - 1) / kStepRows);
+            static const hipError_t attr = hipFuncSetAttribute(
+                (const void *)step_mfma<TX>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                (int)step_mfma_lds(2048));
+            if (attr != hipSuccess) return attr;
+            hipLaunchKernelGGL((step_mfma<TX>), dim3((unsigned)blocks), dim3(64 * kStepWaves),
+                               step_mfma_lds(a.d), s, a);
+            return hipGetLastError();
+        }
+    }
     const dim3 grid((unsigned)((a.d + 3) / 4)), block(256);
     const bool vec = a.d % 8 == 0;
     if (vec && a.d <= 512)

@@ -54,8 +54,11 @@ def params(d, seed, w_dtype):
 
 
 # (B, d): every kernel variant: d <= 512, 1024, 2048 with the W rows in
-# registers, 4096 streamed, d not a multiple of 8 (element path), B up to 64
-CASES = [(1, 64), (3, 100), (4, 512), (2, 1024), (5, 2048), (1, 4096), (64, 256), (7, 37)]
+# registers, 4096 streamed, d not a multiple of 8 (element path), B up to 100
+CASES = [(1, 64), (3, 100), (4, 512), (2, 1024), (5, 2048), (1, 4096), (64, 256), (7, 37),
+         # bf16 W from 8 rows on, d % 32 == 0, d <= 2048: the MFMA kernel
+         # (whole and ragged 32-row batch groups, d from 96 to 2048)
+         (8, 96), (32, 1024), (33, 512), (16, 2048), (100, 128)]
 
 
 @pytest.mark.parametrize("B,d", CASES)
