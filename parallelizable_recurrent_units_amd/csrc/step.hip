@@ -163,100 +163,160 @@ __global__ __launch_bounds__(256) void step_cell(StepArgs a)
 // bf16 MFMAs.  A block owns 32 channels and 32 batch rows.  It rounds its x
 // rows to bf16 into LDS once (row pitch d + 8 keeps the fragment reads of
 // eight rows on different banks); wave w multiplies them by the 32 W rows of
-// gate w % 3 over half w / 3 of the reduction (v_mfma_f32_32x32x16_bf16, W
-// fragments loaded straight from memory); the two halves meet in LDS and the
-// block applies the cell to its 32 x 32 (batch row, channel) pairs.
+// gate w % 3 over part w / 3 of the KP parts of the reduction
+// (v_mfma_f32_32x32x16_bf16, W fragments loaded straight from memory, 16 at
+// a time, the first 16 requested together with the x rows); the parts meet
+// in LDS, over the x~ rows, and the block applies the cell to its 32 x 32
+// (batch row, channel) pairs, whose state and highway inputs it also loaded
+// before the products.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-constexpr int kStepRows = 32, kStepWaves = 6;
+constexpr int kStepRows = 32;
 
-template <typename TX>
-__global__ __launch_bounds__(64 * kStepWaves) void step_mfma(StepArgs a)
+// four consecutive x values rounded to bf16, as two packed pairs
+template <typename TX> __device__ __forceinline__ uint2 load4_bf16(const TX *p);
+template <> __device__ __forceinline__ uint2 load4_bf16<float>(const float *p)
 {
+    const float4 v = *(const float4 *)p;
+    return uint2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+}
+template <> __device__ __forceinline__ uint2 load4_bf16<bf16_bits>(const bf16_bits *p)
+{
+    return *(const uint2 *)p;                            // already bf16: x~ = x
+}
+
+template <typename TX, int KP>
+__global__ __launch_bounds__(192 * KP) void step_mfma(StepArgs a)
+{
+    constexpr int NT = 192 * KP;                         // 3 gates x KP parts, one wave each
+    constexpr int NP = (kStepRows * 32 + NT - 1) / NT;   // cell pairs per thread
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int64_t d = a.d, P = d + 8;                    // LDS row pitch (bf16)
+    const int d = (int)a.d, P = d + 8;                   // LDS row pitch (bf16)
     bf16_bits *xs = (bf16_bits *)smem;                   // [32][P]
-    float *red = (float *)(smem + kStepRows * P * 2);    // [2][3][32][33]
+    float *red = (float *)smem;                          // [KP][3][32][33], after the products
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t ngroups = d / 32;
-    const int64_t j0 = (blockIdx.x % ngroups) * 32;
-    const int64_t b0 = (blockIdx.x / ngroups) * kStepRows;
+    const int ngroups = d / 32;
+    const int j0 = (int)(blockIdx.x % ngroups) * 32;
+    const int64_t b0 = (int64_t)(blockIdx.x / ngroups) * kStepRows;
     const TX *X = (const TX *)a.x;
     const bf16_bits *W = (const bf16_bits *)a.W;
 
-    // x~ rows b0 .. b0 + 31 (rows past B repeat the last one; never written)
-    for (int64_t i = tid; i < kStepRows * d / 4; i += 64 * kStepWaves) {
-        const int64_t r = (4 * i) / d, k = (4 * i) % d;
-        const int64_t b = b0 + r < a.B ? b0 + r : a.B - 1;
-        float v[4];
+    // the first U W fragments of this wave (gate wave % 3, part wave / 3 of
+    // the reduction), the cell's per-pair inputs and the x rows are all
+    // requested before anything waits on them
+    const int g = wave % 3, kp = wave / 3;
+    const int part = d / KP, steps = part / 16;
+    const int r32 = lane & 31, hi = lane >> 5;
+    const bf16_bits *wrow = W + (int64_t)(g * d + j0 + r32) * d + kp * part + 8 * hi;
+    constexpr int U = 16;
+    bf16x8_t wf[U];
+    auto load_w = [&](int ks) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = load_as_f32(X + b * d + k + e);
-        *(uint2 *)(xs + r * P + k) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        for (int u = 0; u < U; ++u)
+            if (ks + u < steps) wf[u] = *(const bf16x8_t *)(wrow + 16 * (ks + u));
+    };
+    load_w(0);
+
+    float cp[NP], xv[NP], vf[NP], vr[NP], bf[NP], br[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int idx = tid + p * NT, r = idx / 32, j = j0 + idx % 32;
+        const int64_t b = b0 + r;
+        cp[p] = xv[p] = vf[p] = vr[p] = bf[p] = br[p] = 0.0f;
+        if (idx < kStepRows * 32 && b < a.B) {
+            cp[p] = a.c_prev ? a.c_prev[b * d + j] : 0.0f;
+            xv[p] = load_as_f32(X + b * d + j);
+            vf[p] = a.v[j], vr[p] = a.v[d + j], bf[p] = a.b[j], br[p] = a.b[d + j];
+        }
+    }
+
+    // x~ rows b0 .. b0 + 31 (rows past B repeat the last one; never written),
+    // SB 4-element pieces per thread in flight
+    const int q = d / 4, total = kStepRows * q;
+    constexpr int SB = 8;
+    for (int base = 0; base < total; base += SB * NT) {
+        uint2 v[SB];
+#pragma unroll
+        for (int s = 0; s < SB; ++s) {
+            const int i = base + s * NT + tid;
+            v[s] = uint2{0u, 0u};
+            if (i < total) {
+                const int r = i / q, k = 4 * (i - r * q);
+                const int64_t b = b0 + r < a.B ? b0 + r : a.B - 1;
+                v[s] = load4_bf16(X + b * d + k);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < SB; ++s) {
+            const int i = base + s * NT + tid;
+            if (i < total) {
+                const int r = i / q, k = 4 * (i - r * q);
+                *(uint2 *)(xs + r * P + k) = v[s];
+            }
+        }
     }
     __syncthreads();
 
-    const int g = wave % 3, kh = wave / 3;
-    const int64_t K2 = d / 2, kb = kh * K2;
-    const int r32 = lane & 31, hi = lane >> 5;
-    const bf16_bits *wrow = W + (g * d + j0 + r32) * d + kb + 8 * hi;
-    const bf16_bits *xrow = xs + r32 * P + kb + 8 * hi;
+    const bf16_bits *xrow = xs + r32 * P + kp * part + 8 * hi;
     f32x16_t acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    constexpr int U = 8;                                 // k-steps whose W loads are in flight
-    const int64_t steps = K2 / 16;
-    int64_t ks = 0;
-    for (; ks + U <= steps; ks += U) {
-        bf16x8_t wf[U];
+    for (int ks = 0;;) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) wf[u] = *(const bf16x8_t *)(wrow + 16 * (ks + u));
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const bf16x8_t xf = *(const bf16x8_t *)(xrow + 16 * (ks + u));
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, wf[u], acc, 0, 0, 0);
-        }
+        for (int u = 0; u < U; ++u)
+            if (ks + u < steps) {
+                const bf16x8_t xf = *(const bf16x8_t *)(xrow + 16 * (ks + u));
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, wf[u], acc, 0, 0, 0);
+            }
+        ks += U;
+        if (ks >= steps) break;
+        load_w(ks);
     }
-    for (; ks < steps; ++ks) {
-        const bf16x8_t wf = *(const bf16x8_t *)(wrow + 16 * ks);
-        const bf16x8_t xf = *(const bf16x8_t *)(xrow + 16 * ks);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, wf, acc, 0, 0, 0);
-    }
+    __syncthreads();                                     // x~ no longer read: red may overwrite it
     // acc holds row (batch) 8 (r / 4) + 4 hi + r % 4, column (channel) r32
-    float *rw = red + ((kh * 3 + g) * 32) * 33;
+    float *rw = red + ((kp * 3 + g) * 32) * 33;
 #pragma unroll
     for (int r = 0; r < 16; ++r) rw[(8 * (r / 4) + 4 * hi + (r % 4)) * 33 + r32] = acc[r];
     __syncthreads();
 
-    for (int idx = tid; idx < kStepRows * 32; idx += 64 * kStepWaves) {
-        const int r = idx / 32, n = idx % 32;
-        const int64_t b = b0 + r, j = j0 + n;
-        if (b >= a.B) continue;
-        float u[3];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int idx = tid + p * NT, r = idx / 32, n = idx % 32;
+        const int64_t b = b0 + r;
+        if (idx >= kStepRows * 32 || b >= a.B) continue;
+        float u[3] = {0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int gg = 0; gg < 3; ++gg)
-            u[gg] = red[(gg * 32 + r) * 33 + n] + red[((3 + gg) * 32 + r) * 33 + n];
-        const float c = a.c_prev ? a.c_prev[b * d + j] : 0.0f;
-        cell(a, b, j, a.v[j], a.v[d + j], a.b[j], a.b[d + j], c, u[0], u[1], u[2],
-             load_as_f32(X + b * d + j));
+#pragma unroll
+            for (int k = 0; k < KP; ++k) u[gg] += red[((k * 3 + gg) * 32 + r) * 33 + n];
+        cell(a, b, j0 + n, vf[p], vr[p], bf[p], br[p], cp[p], u[0], u[1], u[2], xv[p]);
     }
 }
 
-size_t step_mfma_lds(int64_t d) { return (size_t)kStepRows * (d + 8) * 2 + 2 * 3 * 32 * 33 * 4; }
+template <int KP> size_t step_mfma_lds(int64_t d)
+{
+    const size_t xs = (size_t)kStepRows * (d + 8) * 2, red = (size_t)KP * 3 * 32 * 33 * 4;
+    return xs > red ? xs : red;
+}
+
+template <typename TX, int KP> hipError_t step_mfma_launch(const StepArgs &a, hipStream_t s)
+{
+    static const hipError_t attr = hipFuncSetAttribute(
+        (const void *)step_mfma<TX, KP>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)step_mfma_lds<KP>(2048));
+    if (attr != hipSuccess) return attr;
+    const int64_t blocks = (a.d / 32) * ((a.B + kStepRows - 1) / kStepRows);
+    hipLaunchKernelGGL((step_mfma<TX, KP>), dim3((unsigned)blocks), dim3(192 * KP),
+                       step_mfma_lds<KP>(a.d), s, a);
+    return hipGetLastError();
+}
 
 template <typename TW, typename TX>
 hipError_t step_launch(const StepArgs &a, hipStream_t s)
 {
     if constexpr (sizeof(TW) == 2) {
-        if (a.B >= 8 && a.d % 32 == 0 && a.d <= 2048) {
-            const int64_t blocks = (a.d / 32) * ((a.B + kStepRows - 1) / kStepRows);
-            static const hipError_t attr = hipFuncSetAttribute(
-                (const void *)step_mfma<TX>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                (int)step_mfma_lds(2048));
-            if (attr != hipSuccess) return attr;
-            hipLaunchKernelGGL((step_mfma<TX>), dim3((unsigned)blocks), dim3(64 * kStepWaves),
-                               step_mfma_lds(a.d), s, a);
-            return hipGetLastError();
-        }
+        if (a.B >= 8 && a.d % 32 == 0 && a.d <= 2048)
+            return a.d % 64 == 0 ? step_mfma_launch<TX, 4>(a, s) : step_mfma_launch<TX, 2>(a, s);
     }
     const dim3 grid((unsigned)((a.d + 3) / 4)), block(256);
     const bool vec = a.d % 8 == 0;
