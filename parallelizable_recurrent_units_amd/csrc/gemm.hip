@@ -571,8 +571,10 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(
 // requested while k-tile kt is multiplied, and a wave waits (vmcnt) only for
 // its own requests of k-tile kt before the barrier that publishes the stage.
 // Inside a row the sixteen-byte piece holding k-chunk c sits at position
-// c ^ (row % 8), so the fragment reads of eight consecutive rows hit eight
-// different bank groups.  (fp32 A is not taken: converted as its fragments
+// c ^ ((row / 2) % 8): LDS serves a 16-byte-per-lane read 16 lanes (256
+// bytes, all 64 banks) at a time, and two 128-byte rows share one bank line,
+// so the fragment reads of sixteen consecutive rows then touch every bank
+// once.  (fp32 A is not taken: converted as its fragments
 // are read, by every wave that reads them, it is slower than the register-
 // staged kernel, which converts each element once.)
 template <int N_> __device__ __forceinline__ void wait_vmcnt()
@@ -583,6 +585,9 @@ template <int N_> __device__ __forceinline__ void wait_vmcnt()
 }
 
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// position key of a 128-byte LDS row (see above)
+__device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & 7; }
 
 // 16 bytes per lane from gptr into LDS at lds_base + 16 * lane (lds_base is
 // wave-uniform; M0 carries it).  The instruction has no register result; the
@@ -652,7 +657,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
     // this lane's source of each of the wave's requests, at k = 0.  Request q
     // fills 1 KB of the stage: 1024 / AROW rows of A (q < QA) or 8 rows of B.
     // Lane l takes piece l % (pieces per row) of row l / (pieces per row); in
-    // a row the piece at position s holds k-chunk s ^ (row % pieces per row).
+    // a row the piece at position s holds k-chunk s ^ lds_swz(row).
     // Rows past M or N repeat the last row (loaded, never stored).
     const char *src[IPW];
 #pragma unroll
@@ -660,12 +665,12 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
         const int q = wave * IPW + i;
         if (q < St::QA) {
             const int row = q * (1024 / AROW) + lane / APR;
-            const int c = (lane % APR) ^ (row % APR);
+            const int c = (lane % APR) ^ lds_swz(row);
             const int64_t m = m0 + row < M ? m0 + row : M - 1;
             src[i] = (const char *)(A + m * lda) + 16 * c;
         } else {
             const int row = (q - St::QA) * 8 + lane / 8;
-            const int c = (lane % 8) ^ (row % 8);
+            const int c = (lane % 8) ^ lds_swz(row);
             const int64_t n = n0 + row < N ? n0 + row : N - 1;
             src[i] = (const char *)(B + n * ldb) + 16 * c;
         }
@@ -696,11 +701,11 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
     static_assert(sizeof(TA) == 2, "bf16 A");
     auto afrag = [&](int st, int row, int ks) -> bf16x8 {
         const int c = 2 * ks + hi;
-        return *(const bf16x8 *)(smem + st * SB + row * AROW + ((c ^ (row % APR)) << 4));
+        return *(const bf16x8 *)(smem + st * SB + row * AROW + ((c ^ lds_swz(row)) << 4));
     };
     auto bfrag = [&](int st, int row, int ks) -> bf16x8 {
         const int c = 2 * ks + hi;
-        return *(const bf16x8 *)(smem + st * SB + St::A_BYTES + row * 128 + ((c ^ (row & 7)) << 4));
+        return *(const bf16x8 *)(smem + st * SB + St::A_BYTES + row * 128 + ((c ^ lds_swz(row)) << 4));
     };
 
 #pragma unroll
