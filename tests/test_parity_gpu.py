@@ -256,6 +256,33 @@ def test_projection_bf16(L, B, d, nd):
     check("dX (transposed W) vs bf16(dU) oracle", host(dX2).reshape(L * B, d), ref_r, GEMM_ACC)
 
 
+# bf16 X on grids of 256 x 256 tiles (operands straight into LDS): ragged M,
+# and ragged M and N (sampled rows, the last ragged row tile included, every
+# column).  X rounded by sru_round_bf16 and then multiplied gives U bit for
+# bit equal to fp32 X rounded while the tiles are staged by the other kernel
+# (same bf16 operands, same k order, same MFMA).
+@pytest.mark.parametrize("L,B,d", [(100, 80, 1024), (60, 100, 1088)])
+def test_projection_bf16_x_large(L, B, d):
+    import torch
+    rng = np.random.default_rng(3100 + d)
+    M = L * B
+    X = rng.standard_normal((L, B, d)).astype(np.float32)
+    W_bits, W = workloads.to_bf16(rng.uniform(-0.05, 0.05, (3 * d, d)).astype(np.float32))
+    Wd = torch.from_numpy(W_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    shape = SruShape(L, B, d, False, 1.0)
+    print(f"case M={M} N={3 * d} K={d}", flush=True)
+    Xd = torch.from_numpy(X).cuda()
+    Xb = layer.round_bf16(Xd)
+    U = layer.project(shape, Xb, Wd)
+    rows = np.unique(np.concatenate([np.arange(M - 120, M), np.arange(0, 16),
+                                     rng.integers(0, M, 40)]))
+    want = oracle.project(oracle.round_bf16(X.reshape(M, d)), W, False, rows=rows)
+    check("U (bf16 X; sampled rows)", host(U).reshape(M, -1)[rows], want, GEMM_ACC)
+    U32 = layer.project(shape, Xd, Wd)
+    torch.cuda.synchronize()
+    assert torch.equal(U.view(torch.int32), U32.view(torch.int32))
+
+
 # weight gradient dW = dU^T X: (L, B, d, nd) spanning no split (K = L*B not a
 # multiple of the 64-deep k-tile, or too short), split reductions on the fast
 # path, and a split on the bounds-checked path (d = 37: rows of dW not
@@ -318,11 +345,12 @@ def test_projection_bwd_weight_is_deterministic():
 
 # bf16 dU times the transposed bf16 weights: the products whose operands go
 # straight to LDS (whole 64-deep k-tiles), at ragged M and N, one k-tile up to
-# long reductions, with accumulation; the last case takes the 256 x 256 tiles
-# (sampled rows, the last ragged tile included).
+# long reductions, with accumulation; the last two cases take the 256 x 256
+# tiles, ragged in M and in both M and N (sampled rows, the last ragged tile
+# included).
 @pytest.mark.parametrize("L,B,d,nd", [(3, 5, 64, 1), (7, 19, 128, 2), (64, 4, 256, 2),
                                       (33, 3, 64, 1), (1, 1, 64, 1), (40, 50, 512, 2),
-                                      (100, 164, 1024, 1)])
+                                      (100, 164, 1024, 1), (100, 140, 1088, 1)])
 def test_bwd_data_bf16_dU_transposed_weight(L, B, d, nd):
     import torch
     rng = np.random.default_rng(6000 + d + L)
