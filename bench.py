@@ -142,13 +142,14 @@ def attention_work(w):
     the previous segment (L steps) as context.  Flops count the visible
     (query, key) pairs only; bytes count X, the weights, Q, the keys and
     values (written once for this segment, read once for all Lm + L steps),
-    R and U, not the scores the kernels keep in a workspace."""
+    R and U (bf16, the U the given-U recurrence takes), not the scores the
+    kernels keep in a workspace."""
     L, B, d, nd = w.L, w.B, w.d, w.ndir
     dp, Lm, n3, LB = max(1, d // 4), int(ATTN_CONTEXT * L), nd * 3 * d, L * B
     pairs = B * (L * Lm + L * (L + 1) // 2)
     flops = (2 * LB * d * dp + 2 * LB * dp * 2 * dp + 4 * pairs * dp + 2 * LB * dp * n3)
     byts = (LB * d * 4 + (dp * d + 2 * dp * dp + n3 * dp) * 2 + LB * dp * 4
-            + LB * 2 * dp * 2 + (Lm + L) * B * 2 * dp * 2 + LB * dp * 4 + LB * n3 * 4)
+            + LB * 2 * dp * 2 + (Lm + L) * B * 2 * dp * 2 + LB * dp * 4 + LB * n3 * 2)
     return {"f2_attention_forward": dict(flops=flops, bytes=byts)}
 
 
@@ -337,7 +338,8 @@ def time_rows(row_sets, steps, warmup):
 def attention_rows(w, shape, g):
     """The SRU++ attention that would produce this workload's U (one buffer
     set): X ~ N(0, 1), bf16 weights ~ U(-0.05, 0.05), layer norm on, the
-    previous segment's keys and values ~ N(0, 1) in front."""
+    previous segment's keys and values ~ N(0, 1) in front; U written in
+    bf16, as the given-U recurrence takes it."""
     import torch
     from parallelizable_recurrent_units_amd import (SruAttnCfg, sru_attention_forward,
                                                     sru_attention_workspace_size)
@@ -351,7 +353,7 @@ def attention_rows(w, shape, g):
     gamma, beta = torch.ones(dp, **f32), torch.zeros(dp, **f32)
     KV = torch.randn((Lm + L, B, 2 * dp), generator=g, **f32).to(torch.bfloat16)
     Q, R = torch.empty((L * B, dp), **f32), torch.empty((L * B, dp), **f32)
-    U = torch.empty((L, B, nd, 3, d), **f32)
+    U = torch.empty((L, B, nd, 3, d), device="cuda", dtype=torch.bfloat16)
     ws = torch.empty(sru_attention_workspace_size(shape, cfg), device="cuda", dtype=torch.uint8)
     return [("f2_attention_forward",
              lambda: sru_attention_forward(shape, cfg, X, Wq, Wkv, Wo, gamma, beta, Q, KV, R, U,

@@ -206,7 +206,10 @@ sru_status sru_project_factored_bwd_weight(const sru_shape *shape, int64_t d_inn
  *                                       visibility of sru_attn_cfg.causal
  *   R = Q + alpha A, or layernorm(Q + alpha A) (biased variance, gain gamma,
  *       shift beta, both fp32 [d'])    R  fp32 [L*B, d'] (written)
- *   U = R~ Wo^T                         U  fp32 [L, B, ndir, 3, d] (written)
+ *   U = R~ Wo^T                         U  [L, B, ndir, 3, d] (written), fp32,
+ *                                          or bf16 (u_dt; rounded to nearest
+ *                                          even from the fp32 sum) as the bf16
+ *                                          U that sru_forward takes
  * X [L*B, d] fp32 or bf16 (x_dt).  Wq [d', d], Wkv [2d', d'] (Wk's rows, then
  * Wv's), Wo [ndir*3d, d']: bf16 only.  "~" marks operands rounded to bf16
  * (nearest even) as the bf16 MFMA products load them; the attention weights
@@ -221,7 +224,7 @@ sru_status sru_attention_forward(const sru_shape *shape, const sru_attn_cfg *cfg
                                  const void *X, sru_dtype x_dt,
                                  const void *Wq, const void *Wkv, const void *Wo,
                                  const float *gamma, const float *beta,
-                                 float *Q, void *KV, float *R, float *U,
+                                 float *Q, void *KV, float *R, void *U, sru_dtype u_dt,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes of sru_attention_forward; 0 on invalid arguments

@@ -96,7 +96,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     cp = ctypes.POINTER(SruAttnCfg)
     lib.sru_attention_forward.restype = ctypes.c_int
     lib.sru_attention_forward.argtypes = [sp, cp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
-                                          _vp, _vp, _vp, _vp, _vp, sz, _vp]
+                                          _vp, _vp, _vp, _vp, ctypes.c_int, _vp, sz, _vp]
     lib.sru_attention_workspace_size.restype = sz
     lib.sru_attention_workspace_size.argtypes = [sp, cp]
     lib.sru_step.restype = ctypes.c_int
@@ -226,14 +226,14 @@ def sru_attention_forward(shape, cfg, X, Wq, Wkv, Wo, gamma, beta, Q, KV, R, U, 
     for name, t in (("Wq", Wq), ("Wkv", Wkv), ("Wo", Wo), ("KV", KV)):
         if _dtype_code(t) != SRU_BF16:
             raise TypeError(f"{name} must be bfloat16")
-    for name, t in (("Q", Q), ("R", R), ("U", U)):
+    for name, t in (("Q", Q), ("R", R)):
         if _dtype_code(t) != SRU_F32:
             raise TypeError(f"{name} must be float32")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().sru_attention_forward(
         ctypes.byref(s), ctypes.byref(cfg), _ptr(X), _dtype_code(X), _ptr(Wq), _ptr(Wkv),
-        _ptr(Wo), _ptr(gamma), _ptr(beta), _ptr(Q), _ptr(KV), _ptr(R), _ptr(U), _ptr(workspace),
-        ws_bytes, _stream(stream)))
+        _ptr(Wo), _ptr(gamma), _ptr(beta), _ptr(Q), _ptr(KV), _ptr(R), _ptr(U), _dtype_code(U),
+        _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def sru_step(shape, x, W, v, b, c_prev, h, c_next, stream=None):

@@ -407,12 +407,12 @@ size_t sru_attention_workspace_size(const sru_shape *shape, const sru_attn_cfg *
 sru_status sru_attention_forward(const sru_shape *shape, const sru_attn_cfg *cfg, const void *X,
                                  sru_dtype x_dt, const void *Wq, const void *Wkv, const void *Wo,
                                  const float *gamma, const float *beta, float *Q, void *KV,
-                                 float *R, float *U, void *workspace, size_t workspace_bytes,
-                                 void *stream)
+                                 float *R, void *U, sru_dtype u_dt, void *workspace,
+                                 size_t workspace_bytes, void *stream)
 {
     Dims dm;
     SRU_TRY(check_attn(shape, cfg, &dm));
-    if (!valid_dtype(x_dt)) return fail(SRU_ERR_INVALID_ARG, "unknown dtype");
+    if (!valid_dtype(x_dt) || !valid_dtype(u_dt)) return fail(SRU_ERR_INVALID_ARG, "unknown dtype");
     SRU_TRY(need_ptr(X, "X"));
     SRU_TRY(need_ptr(Wq, "Wq"));
     SRU_TRY(need_ptr(Wkv, "Wkv"));
@@ -436,7 +436,7 @@ sru_status sru_attention_forward(const sru_shape *shape, const sru_attn_cfg *cfg
         const Span out[] = {{Q, (size_t)(dm.LB * dp) * 4, "Q"},
                             {KV, (size_t)((Lm + L) * B * 2 * dp) * 2, "KV"},
                             {R, (size_t)(dm.LB * dp) * 4, "R"},
-                            {U, (size_t)(dm.LB * n3) * 4, "U"}};
+                            {U, (size_t)(dm.LB * n3) * (u_dt == SRU_BF16 ? 2 : 4), "U"}};
         const Span in[] = {{X, (size_t)(dm.LB * d) * (x_dt == SRU_BF16 ? 2 : 4), "X"},
                            {Wq, (size_t)(dp * d) * 2, "Wq"},
                            {Wkv, (size_t)(2 * dp * dp) * 2, "Wkv"},
@@ -468,7 +468,7 @@ sru_status sru_attention_forward(const sru_shape *shape, const sru_attn_cfg *cfg
     a.Wkv = (const sru::bf16_bits_t *)Wkv;
     a.Wo = (const sru::bf16_bits_t *)Wo;
     a.gamma = gamma, a.beta = beta;
-    a.Q = Q, a.R = R, a.U = U, a.KV = KV, a.workspace = workspace;
+    a.Q = Q, a.R = R, a.U = U, a.u_bf16 = u_dt == SRU_BF16, a.KV = KV, a.workspace = workspace;
     return launched(sru::launch_attention_forward(a, (hipStream_t)stream), "attention");
 }
 

@@ -253,13 +253,14 @@ hipError_t launch_attention_forward(const AttnArgs &a, hipStream_t s)
         if ((e = launch_gemm(g, s)) != hipSuccess) return e;
     }
     if ((e = launch_residual(a, O, s)) != hipSuccess) return e;
-    {   // U [L*B, ndir*3d] = R~ Wo^T
+    {   // U [L*B, ndir*3d] = R~ Wo^T, fp32 or rounded to bf16
         GemmArgs g;
         g.M = LB, g.N = a.n3, g.K = dp;
         g.A = a.R, g.a_bf16 = false;
         g.Bm = a.Wo, g.b_bf16 = true, g.b_kn = false;
-        g.C = a.U, g.accumulate = false;
-        if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+        g.C = (float *)a.U, g.accumulate = false;
+        if ((e = a.u_bf16 ? launch_gemm_bf16_out(g, s) : launch_gemm(g, s)) != hipSuccess)
+            return e;
     }
     return hipSuccess;
 }

@@ -111,7 +111,9 @@ struct AttnArgs {
     bool x_bf16;
     const bf16_bits_t *Wq, *Wkv, *Wo;
     const float *gamma, *beta;
-    float *Q, *R, *U;
+    float *Q, *R;
+    void *U;                       // fp32, or bf16 when u_bf16
+    bool u_bf16;
     void *KV;                      // bf16 [Lm + L, B, 2 dp]
     void *workspace;               // attention_workspace_bytes
 };

@@ -106,17 +106,18 @@ def project_factored_backward(shape, d_inner, X, Q, Wq, Wo, dU, dX=None, accumul
 
 
 def attention_forward(shape, cfg, X, Wq, Wkv, Wo, gamma=None, beta=None, KV=None, ws=None,
-                      stream=None):
+                      u_dtype=torch.float32, stream=None):
     """SRU++ attention U-producer.  ``KV`` (bf16 [mem_len + L, B, 2 d']) may
     carry the previous segment's keys and values in its first mem_len rows;
-    its remaining rows are written.  Returns (Q, KV, R, U)."""
+    its remaining rows are written.  U is float32 or bfloat16 (``u_dtype``).
+    Returns (Q, KV, R, U)."""
     s = B._shape(shape)
     dev = X.device
     dp, Lm = cfg.d_inner, cfg.mem_len
     f32 = dict(device=dev, dtype=torch.float32)
     Q = torch.empty((s.L * s.B, dp), **f32)
     R = torch.empty((s.L * s.B, dp), **f32)
-    U = torch.empty((s.L, s.B, s.ndir, 3, s.d), **f32)
+    U = torch.empty((s.L, s.B, s.ndir, 3, s.d), device=dev, dtype=u_dtype)
     if KV is None:
         KV = torch.empty((Lm + s.L, s.B, 2 * dp), device=dev, dtype=torch.bfloat16)
     if ws is None:

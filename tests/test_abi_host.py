@@ -264,11 +264,12 @@ def test_factored_validation(lib):
 def attn(lib, s, cfg, ws_bytes, **kw):
     a = dict(X=Q[0], x_dt=0, Wq=Q[1], Wkv=Q[1] + (1 << 30), Wo=Q[1] + (2 << 30), gamma=None,
              beta=None, Qo=Q[2], KV=Q[2] + (1 << 30), R=Q[2] + (2 << 30), U=Q[2] + (3 << 30),
-             ws=Q[3])
+             u_dt=0, ws=Q[3])
     a.update(kw)
     return lib.sru_attention_forward(ctypes.byref(s), ctypes.byref(cfg) if cfg else None, a["X"],
                                      a["x_dt"], a["Wq"], a["Wkv"], a["Wo"], a["gamma"], a["beta"],
-                                     a["Qo"], a["KV"], a["R"], a["U"], a["ws"], ws_bytes, None)
+                                     a["Qo"], a["KV"], a["R"], a["U"], a["u_dt"], a["ws"],
+                                     ws_bytes, None)
 
 
 def test_attention_workspace_and_validation(lib):
@@ -290,19 +291,26 @@ def test_attention_workspace_and_validation(lib):
     assert attn(lib, s, cfg, want, Wq=None) == sru.SRU_ERR_INVALID_ARG
     assert attn(lib, s, cfg, want, KV=Q[2] + (1 << 30) + 8) == sru.SRU_ERR_INVALID_ARG
     assert attn(lib, s, cfg, want, x_dt=5) == sru.SRU_ERR_INVALID_ARG
+    assert attn(lib, s, cfg, want, u_dt=5) == sru.SRU_ERR_INVALID_ARG
     assert attn(lib, s, cfg, want - 1) == sru.SRU_ERR_WORKSPACE
     assert attn(lib, s, cfg, want, ws=Q[3] + 16) == sru.SRU_ERR_INVALID_ARG   # 256-byte alignment
     # outputs overlapping each other or an input
     assert attn(lib, s, cfg, want, R=Q[2] + 64) == sru.SRU_ERR_INVALID_ARG
     assert b"overlaps" in lib.sru_last_error()
     assert attn(lib, s, cfg, want, U=Q[1] + 1024) == sru.SRU_ERR_INVALID_ARG
+    # U's extent follows its dtype: 64 * 4 * 384 elements of 4 or 2 bytes end
+    # before R only in bf16
+    nU = 64 * 4 * 384
+    assert attn(lib, s, cfg, want, U=Q[2] + (2 << 30) - 2 * nU) == sru.SRU_ERR_INVALID_ARG
     # layer norm needs gamma and beta
     cln = sru.SruAttnCfg(32, layernorm=True)
     nln = sru.sru_attention_workspace_size(s, cln)
     assert attn(lib, s, cln, nln) == sru.SRU_ERR_INVALID_ARG
     import torch
-    if torch.cuda.device_count() == 0:
+    if torch.cuda.device_count() == 0:   # the addresses here are not memory: no launches
         assert attn(lib, s, cfg, want) == sru.SRU_ERR_NO_DEVICE
+        assert attn(lib, s, cfg, want, U=Q[2] + (2 << 30) - 2 * nU,
+                    u_dt=sru.SRU_BF16) == sru.SRU_ERR_NO_DEVICE
         assert attn(lib, s, cln, nln, gamma=Q[3] + (1 << 30),
                     beta=Q[3] + (1 << 30) + 4096) == sru.SRU_ERR_NO_DEVICE
 

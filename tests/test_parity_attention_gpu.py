@@ -102,6 +102,33 @@ def test_attention_forward(L, B, d, nd, dp, Lm, causal, ln, alpha):
                 round_ops)
 
 
+def test_attention_bf16_u():
+    """U written in bf16 is the fp32 U of the same call rounded to nearest
+    even, bit for bit (same product, same accumulation; only the epilogue
+    rounds), and meets the oracle within the chain tolerance plus one
+    rounding of the output (2^-9 relative per element)."""
+    import torch
+    L, B, d, nd, dp, Lm = 96, 3, 128, 2, 32, 40
+    inp = workloads.attention_inputs(L, B, d, nd, dp, Lm, seed=1250)
+    shape = SruShape(L, B, d, nd == 2, 1.0)
+    cfg = SruAttnCfg(dp, Lm, True, True, 0.7, 1e-5)
+    mem = torch.cat([dev(inp["Kmem"], inp["Kmem_bits"]), dev(inp["Vmem"], inp["Vmem_bits"])], dim=2)
+    args = (shape, cfg, dev(inp["X"]), dev(inp["Wq"], inp["Wq_bits"]),
+            dev(inp["Wkv"], inp["Wkv_bits"]), dev(inp["Wo"], inp["Wo_bits"]))
+    ln = dict(gamma=dev(inp["gamma"]), beta=dev(inp["beta"]))
+    outs = []
+    for u_dtype in (torch.float32, torch.bfloat16):
+        KV = torch.empty((Lm + L, B, 2 * dp), device="cuda", dtype=torch.bfloat16)
+        KV[:Lm] = mem
+        outs.append(layer.attention_forward(*args, KV=KV, u_dtype=u_dtype, **ln))
+    torch.cuda.synchronize()
+    U32, Ub = outs[0][3], outs[1][3]
+    assert Ub.dtype == torch.bfloat16
+    assert torch.equal(Ub.view(torch.int16), U32.to(torch.bfloat16).view(torch.int16))
+    ref = reference(L, B, dp, Lm, True, True, 0.7, inp, True)
+    check("U (bf16)", host(Ub).reshape(L * B, -1), ref["U"], CHAIN + 2.0 ** -9)
+
+
 def test_attention_alpha_zero_is_the_factorised_projection():
     """alpha = 0: U equals the factorised projection's U bit for bit (the
     attention term is multiplied by zero; both run Q and U on the same
