@@ -1095,49 +1095,66 @@ __global__ __launch_bounds__(256) void split_reduce(const float *__restrict__ P,
     C[i] = accumulate ? C[i] + sum : sum;
 }
 
-// Split of the reduction over L*B for the weight gradient.  A block of the
-// 128 x 128 configuration takes one of 512 slots (2 per CU); a launch of n
-// blocks runs in ceil(n / 512) rounds, each as long as one block's k-tiles.
-// The partial sums cost a write and a read of M x N floats per split; at
-// the measured rates (one k-tile round ~1.6 us, ~5 TB/s) that is M*N/1e6
-// k-tile rounds per split.  Pick the split count with the least total
-// (ties: fewer splits), at least 8 k-tiles per split.
-constexpr int64_t kWgradSlots = 512, kWgradMinKt = 8, kWgradMaxSplits = 64;
+// Tiles and split of the reduction over L*B for the weight gradient.  A
+// block takes one of the resident slots (128 x 128 tiles: 512, two per CU;
+// 256 x 256 tiles: 256, one per CU), and a launch of n blocks runs in
+// ceil(n / slots) rounds, each as long as one block's k-tiles.  A k-tile
+// round moves the same operand bytes per CU in both configurations (~1.6 us
+// measured), so the large tiles cover four times the output per round.  The
+// partial sums cost a write and a read of M x N floats per split; at ~5 TB/s
+// that is M*N/1e6 k-tile rounds per split.  Pick the configuration and split
+// count with the least total (ties: the small tiles, fewer splits), at least
+// 8 k-tiles per split.
+constexpr int64_t kWgradMinKt = 8, kWgradMaxSplits = 64;
 
-int64_t wgrad_splits(int64_t M, int64_t N, int64_t K)
+struct WgradPlan {
+    bool big;          // 256 x 256 tiles
+    int64_t splits;    // 1: no partial sums
+};
+
+WgradPlan wgrad_plan(int64_t M, int64_t N, int64_t K)
 {
-    const int64_t tiles = ((M + CfgSmall::BM - 1) / CfgSmall::BM) *
-                          ((N + CfgSmall::BN - 1) / CfgSmall::BN);
-    const int64_t kt = K / CfgSmall::BK;
-    if (K % CfgSmall::BK != 0 || kt < 2 * kWgradMinKt) return 1;
+    const int64_t kt = K / 64;                           // both configurations: 64-deep k-tiles
+    if (K % 64 != 0 || kt < 2 * kWgradMinKt) return {false, 1};
     const double reduce = (double)M * (double)N * 1e-6;
-    int64_t best = 1;
-    double best_cost = (double)((tiles + kWgradSlots - 1) / kWgradSlots) * (double)kt;
-    for (int64_t sp = 2; sp <= kt / kWgradMinKt && sp <= kWgradMaxSplits; ++sp) {
-        const double rounds = (double)((tiles * sp + kWgradSlots - 1) / kWgradSlots);
-        const double cost = rounds * (double)((kt + sp - 1) / sp) + reduce * (double)sp;
-        if (cost < best_cost) {
-            best_cost = cost;
-            best = sp;
+    WgradPlan best{false, 1};
+    double best_cost = -1.0;
+    for (int big = 0; big < 2; ++big) {
+        const int64_t t = big ? 256 : 128, slots = big ? 256 : 512;
+        const int64_t tiles = ((M + t - 1) / t) * ((N + t - 1) / t);
+        for (int64_t sp = 1; sp <= kt / kWgradMinKt && sp <= kWgradMaxSplits; ++sp) {
+            const double rounds = (double)((tiles * sp + slots - 1) / slots);
+            const double cost = rounds * (double)((kt + sp - 1) / sp) + (sp > 1 ? reduce * sp : 0.0);
+            if (best_cost < 0.0 || cost < best_cost) {
+                best_cost = cost;
+                best = {big != 0, sp};
+            }
         }
     }
     return best;
 }
 
-template <typename TA, typename TB>
-hipError_t wgrad_launch(const GemmArgs &g, float *ws, hipStream_t s)
+template <class Cfg, typename TA, typename TB>
+hipError_t wgrad_launch_cfg(const GemmArgs &g, int64_t sp, float *ws, hipStream_t s)
 {
-    const int64_t sp = wgrad_splits(g.M, g.N, g.K);
-    if (sp <= 1) return mfma_launch_cfg<CfgSmall, TA, true, TB, true>(g, s);
-    const int64_t kt = g.K / CfgSmall::BK;
-    const int64_t ksplit = ((kt + sp - 1) / sp) * CfgSmall::BK;
+    if (sp <= 1) return mfma_launch_cfg<Cfg, TA, true, TB, true>(g, s);
+    const int64_t kt = g.K / Cfg::BK;
+    const int64_t ksplit = ((kt + sp - 1) / sp) * Cfg::BK;
     const int64_t used = (g.K + ksplit - 1) / ksplit;      // splits with work
-    hipError_t e = mfma_launch_cfg<CfgSmall, TA, true, TB, true>(g, s, used, ksplit, ws);
+    hipError_t e = mfma_launch_cfg<Cfg, TA, true, TB, true>(g, s, used, ksplit, ws);
     if (e != hipSuccess) return e;
     const int64_t n = g.M * g.N;
     hipLaunchKernelGGL(split_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ws, n,
                        used, g.C, g.accumulate);
     return hipGetLastError();
+}
+
+template <typename TA, typename TB>
+hipError_t wgrad_launch(const GemmArgs &g, float *ws, hipStream_t s)
+{
+    const WgradPlan pl = wgrad_plan(g.M, g.N, g.K);
+    return pl.big ? wgrad_launch_cfg<CfgBig8, TA, TB>(g, pl.splits, ws, s)
+                  : wgrad_launch_cfg<CfgSmall, TA, TB>(g, pl.splits, ws, s);
 }
 
 template <typename TA, bool AKM, typename TB, bool KN>
@@ -1191,7 +1208,7 @@ hipError_t launch_transpose(int64_t rows, int64_t cols, const void *src, void *d
 
 size_t wgrad_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
-    const int64_t sp = wgrad_splits(M, N, K);
+    const int64_t sp = wgrad_plan(M, N, K).splits;
     return sp <= 1 ? 0 : (size_t)(sp * M * N) * sizeof(float);
 }
 

@@ -60,19 +60,8 @@ def test_workspace_sizes(lib, L, B, d, bi):
         nC = -(-L // chunk)
         assert sru.sru_workspace_size(s, sru.SRU_WS_LINEAR_FWD, chunk) == round256((3 * nC * B * d + 64) * 4)
         assert sru.sru_workspace_size(s, sru.SRU_WS_LINEAR_BWD, chunk) == round256((5 * nC * B * d + 64) * 4)
-    # weight gradient: partial products [splits, ndir*3d, d] when the
-    # reduction over L*B is split (128 x 128 output tiles, 64-deep k-tiles,
-    # 512 block slots, >= 8 k-tiles per split, cost in k-tile rounds)
-    M, N, K = 3 * nd * d, d, L * B
-    tiles, kt = -(-M // 128) * -(-N // 128), K // 64
-    sp, best = 1, -(-tiles // 512) * kt
-    if K % 64 == 0 and kt >= 16:
-        for n in range(2, min(kt // 8, 64) + 1):
-            cost = -(-tiles * n // 512) * -(-kt // n) + M * N * 1e-6 * n
-            if cost < best:
-                sp, best = n, cost
-    assert sru.sru_workspace_size(s, sru.SRU_WS_BWD_WEIGHT) == (0 if sp == 1 else
-                                                                round256(sp * M * N * 4))
+    # weight gradient: the split-reduction workspace of [ndir*3d, d] = dU^T X
+    assert sru.sru_workspace_size(s, sru.SRU_WS_BWD_WEIGHT) == wgrad_ws(3 * nd * d, d, L * B)
     assert lib.sru_workspace_size(ctypes.byref(s), sru.SRU_WS_LINEAR_FWD, 0) == 0
     assert b"chunk" in lib.sru_last_error()
     assert lib.sru_workspace_size(ctypes.byref(s), 9, 1) == 0
@@ -193,14 +182,19 @@ def test_bwd_weight_validation(lib):
 
 
 def wgrad_ws(M, N, K):
-    """Split-reduction workspace of one weight-gradient product (see above)."""
-    tiles, kt = -(-M // 128) * -(-N // 128), K // 64
-    sp, best = 1, -(-tiles // 512) * kt
+    """Split-reduction workspace of one weight-gradient product: partial
+    products [splits, M, N] when the reduction over L*B is split (128 x 128
+    output tiles in 512 block slots or 256 x 256 in 256, 64-deep k-tiles,
+    >= 8 k-tiles per split, cost in k-tile rounds plus M*N/1e6 per split)."""
+    kt = K // 64
+    sp, best = 1, None
     if K % 64 == 0 and kt >= 16:
-        for n in range(2, min(kt // 8, 64) + 1):
-            cost = -(-tiles * n // 512) * -(-kt // n) + M * N * 1e-6 * n
-            if cost < best:
-                sp, best = n, cost
+        for t, slots in ((128, 512), (256, 256)):
+            tiles = -(-M // t) * -(-N // t)
+            for n in range(1, min(kt // 8, 64) + 1):
+                cost = -(-tiles * n // slots) * -(-kt // n) + (M * N * 1e-6 * n if n > 1 else 0)
+                if best is None or cost < best:
+                    sp, best = n, cost
     return 0 if sp == 1 else round256(sp * M * N * 4)
 
 

@@ -331,6 +331,37 @@ def test_projection_bwd_weight(L, B, d, nd):
           oracle.project_bwd_weight(Gb.reshape(M, -1), Xb.reshape(M, d), False) + C0, TIGHT)
 
 
+# 256 x 256 tiles: split 16 ways (ragged M = 1800 and N = 300, K = 8192), and
+# unsplit (M = 7800, N = 1300, K = 2048).  Sampled rows of dW (the first and
+# last ragged tiles included) against the oracle on the bf16 operands, with
+# and without accumulation; the split sums are deterministic.
+@pytest.mark.parametrize("L,B,d,nd", [(128, 64, 300, 2), (64, 32, 1300, 2)])
+def test_projection_bwd_weight_large_tiles(L, B, d, nd):
+    import torch
+    rng = np.random.default_rng(5500 + d)
+    M, n3 = L * B, nd * 3 * d
+    shape = SruShape(L, B, d, nd == 2, 1.0)
+    X = rng.standard_normal((L, B, d)).astype(np.float32)
+    Gb_bits, Gb = workloads.to_bf16(rng.standard_normal((L, B, nd, 3, d)).astype(np.float32))
+    Gbd = torch.from_numpy(Gb_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    Xd = torch.from_numpy(X).cuda()
+    print(f"case K={M} M={n3} N={d}", flush=True)
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(n3 - 40, n3),
+                                     rng.integers(0, n3, 24)]))
+    G2 = Gb.reshape(M, n3)
+    want = oracle.matmul(np.ascontiguousarray(G2[:, rows]), oracle.round_bf16(X.reshape(M, d)),
+                         a_km=True)
+    dW = layer.project_bwd_weight(shape, Gbd, Xd)
+    check("dW (bf16 dU, f32 X; sampled rows)", host(dW)[rows], want, GEMM_ACC)
+    C0 = rng.standard_normal((n3, d)).astype(np.float32)
+    dW2 = torch.from_numpy(C0.copy()).cuda()
+    layer.project_bwd_weight(shape, Gbd, Xd, dW2, accumulate=True)
+    check("dW (+=; sampled rows)", host(dW2)[rows], want + C0[rows], GEMM_ACC)
+    dW3 = layer.project_bwd_weight(shape, Gbd, Xd)
+    torch.cuda.synchronize()
+    assert torch.equal(dW.view(torch.int32), dW3.view(torch.int32))
+
+
 def test_projection_bwd_weight_is_deterministic():
     """The split reduction adds its partial sums in a fixed order."""
     import torch
