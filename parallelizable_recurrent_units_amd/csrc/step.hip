@@ -311,12 +311,158 @@ template <typename TX, int KP> hipError_t step_mfma_launch(const StepArgs &a, hi
     return hipGetLastError();
 }
 
+// The same with 16 channels x 16 batch rows per block
+// (v_mfma_f32_16x16x32_bf16): half the W rows and x rows per block, so four
+// times the blocks, for batches too small to occupy the chip with 32 x 32
+// blocks.  Operand lane l holds row l % 16 (a batch row of x~, a channel's W
+// row) and k-chunk l / 16 of the 32-deep step; the accumulator holds column
+// (channel) l % 16, rows (batch) 4 (l / 16) .. + 3.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kStep16 = 16;
+
+template <typename TX, int KP>
+__global__ __launch_bounds__(192 * KP) void step_mfma16(StepArgs a)
+{
+    constexpr int NT = 192 * KP;
+    constexpr int NP = (kStep16 * kStep16 + NT - 1) / NT;   // cell pairs per thread
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int d = (int)a.d, P = d + 8;                   // LDS row pitch (bf16)
+    bf16_bits *xs = (bf16_bits *)smem;                   // [16][P]
+    float *red = (float *)smem;                          // [KP][3][16][17], after the products
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ngroups = d / kStep16;
+    const int j0 = (int)(blockIdx.x % ngroups) * kStep16;
+    const int64_t b0 = (int64_t)(blockIdx.x / ngroups) * kStep16;
+    const TX *X = (const TX *)a.x;
+    const bf16_bits *W = (const bf16_bits *)a.W;
+
+    const int g = wave % 3, kp = wave / 3;
+    const int part = d / KP, steps = part / 32;
+    const int r16 = lane & 15, q4 = lane >> 4;
+    const bf16_bits *wrow = W + (int64_t)(g * d + j0 + r16) * d + kp * part + 8 * q4;
+    constexpr int U = 16;
+    bf16x8_t wf[U];
+    auto load_w = [&](int ks) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (ks + u < steps) wf[u] = *(const bf16x8_t *)(wrow + 32 * (ks + u));
+    };
+    load_w(0);
+
+    float cp[NP], xv[NP], vf[NP], vr[NP], bf[NP], br[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int idx = tid + p * NT, r = idx / kStep16, j = j0 + idx % kStep16;
+        const int64_t b = b0 + r;
+        cp[p] = xv[p] = vf[p] = vr[p] = bf[p] = br[p] = 0.0f;
+        if (idx < kStep16 * kStep16 && b < a.B) {
+            cp[p] = a.c_prev ? a.c_prev[b * d + j] : 0.0f;
+            xv[p] = load_as_f32(X + b * d + j);
+            vf[p] = a.v[j], vr[p] = a.v[d + j], bf[p] = a.b[j], br[p] = a.b[d + j];
+        }
+    }
+
+    // x~ rows b0 .. b0 + 15 (rows past B repeat the last one; never written)
+    const int q = d / 4, total = kStep16 * q;
+    constexpr int SB = 8;
+    for (int base = 0; base < total; base += SB * NT) {
+        uint2 v[SB];
+#pragma unroll
+        for (int s = 0; s < SB; ++s) {
+            const int i = base + s * NT + tid;
+            v[s] = uint2{0u, 0u};
+            if (i < total) {
+                const int r = i / q, k = 4 * (i - r * q);
+                const int64_t b = b0 + r < a.B ? b0 + r : a.B - 1;
+                v[s] = load4_bf16(X + b * d + k);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < SB; ++s) {
+            const int i = base + s * NT + tid;
+            if (i < total) {
+                const int r = i / q, k = 4 * (i - r * q);
+                *(uint2 *)(xs + r * P + k) = v[s];
+            }
+        }
+    }
+    __syncthreads();
+
+    const bf16_bits *xrow = xs + r16 * P + kp * part + 8 * q4;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int ks = 0;;) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (ks + u < steps) {
+                const bf16x8_t xf = *(const bf16x8_t *)(xrow + 32 * (ks + u));
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, wf[u], acc, 0, 0, 0);
+            }
+        ks += U;
+        if (ks >= steps) break;
+        load_w(ks);
+    }
+    __syncthreads();                                     // x~ no longer read: red may overwrite it
+    float *rw = red + ((kp * 3 + g) * kStep16) * 17;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rw[(4 * q4 + i) * 17 + r16] = acc[i];
+    __syncthreads();
+
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int idx = tid + p * NT, r = idx / kStep16, n = idx % kStep16;
+        const int64_t b = b0 + r;
+        if (idx >= kStep16 * kStep16 || b >= a.B) continue;
+        float u[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int gg = 0; gg < 3; ++gg)
+#pragma unroll
+            for (int k = 0; k < KP; ++k) u[gg] += red[((k * 3 + gg) * kStep16 + r) * 17 + n];
+        cell(a, b, j0 + n, vf[p], vr[p], bf[p], br[p], cp[p], u[0], u[1], u[2], xv[p]);
+    }
+}
+
+template <int KP> size_t step_mfma16_lds(int64_t d)
+{
+    const size_t xs = (size_t)kStep16 * (d + 8) * 2, red = (size_t)KP * 3 * kStep16 * 17 * 4;
+    return xs > red ? xs : red;
+}
+
+template <typename TX, int KP> hipError_t step_mfma16_launch(const StepArgs &a, hipStream_t s)
+{
+    static const hipError_t attr = hipFuncSetAttribute(
+        (const void *)step_mfma16<TX, KP>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)step_mfma16_lds<KP>(2048));
+    if (attr != hipSuccess) return attr;
+    const int64_t blocks = (a.d / kStep16) * ((a.B + kStep16 - 1) / kStep16);
+    hipLaunchKernelGGL((step_mfma16<TX, KP>), dim3((unsigned)blocks), dim3(192 * KP),
+                       step_mfma16_lds<KP>(a.d), s, a);
+    return hipGetLastError();
+}
+
+// A block's time goes with the bytes it streams (its W rows and its x rows),
+// and blocks beyond the 256 CUs run in further rounds: the smaller blocks
+// when they finish sooner by that measure.
+bool step_small_blocks(const StepArgs &a)
+{
+    const int64_t sx = a.x_bf16 ? 2 : 4;
+    auto est = [&](int64_t ch) {
+        const int64_t blocks = (a.d / ch) * ((a.B + ch - 1) / ch);
+        return (blocks + 255) / 256 * (3 * ch * a.d * 2 + ch * a.d * sx);
+    };
+    return est(kStep16) < est(kStepRows);
+}
+
 template <typename TW, typename TX>
 hipError_t step_launch(const StepArgs &a, hipStream_t s)
 {
     if constexpr (sizeof(TW) == 2) {
-        if (a.B >= 8 && a.d % 32 == 0 && a.d <= 2048)
+        if (a.B >= 8 && a.d % 32 == 0 && a.d <= 2048) {
+            if (step_small_blocks(a))
+                return a.d % 128 == 0  ? step_mfma16_launch<TX, 4>(a, s)
+                       : a.d % 64 == 0 ? step_mfma16_launch<TX, 2>(a, s)
+                                       : step_mfma16_launch<TX, 1>(a, s);
             return a.d % 64 == 0 ? step_mfma_launch<TX, 4>(a, s) : step_mfma_launch<TX, 2>(a, s);
+        }
     }
     const dim3 grid((unsigned)((a.d + 3) / 4)), block(256);
     const bool vec = a.d % 8 == 0;

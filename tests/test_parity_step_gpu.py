@@ -56,9 +56,12 @@ def params(d, seed, w_dtype):
 # (B, d): every kernel variant: d <= 512, 1024, 2048 with the W rows in
 # registers, 4096 streamed, d not a multiple of 8 (element path), B up to 100
 CASES = [(1, 64), (3, 100), (4, 512), (2, 1024), (5, 2048), (1, 4096), (64, 256), (7, 37),
-         # bf16 W from 8 rows on, d % 32 == 0, d <= 2048: the MFMA kernel
-         # (whole and ragged 32-row batch groups, d from 96 to 2048)
-         (8, 96), (32, 1024), (33, 512), (16, 2048), (100, 128)]
+         # bf16 W from 8 rows on, d % 32 == 0, d <= 2048: the MFMA kernels.
+         # 16 x 16 blocks (reduction in 1, 2 or 4 parts; whole and ragged
+         # 16-row batch groups, d from 96 to 2048), and 32 x 32 blocks on
+         # batches that fill the chip with them (4 and 2 parts, ragged)
+         (8, 96), (32, 1024), (33, 512), (16, 2048), (100, 128), (20, 320),
+         (512, 256), (700, 96)]
 
 
 @pytest.mark.parametrize("B,d", CASES)
@@ -90,11 +93,13 @@ def test_step(B, d, w_dtype):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("B", [3, 20])
 @pytest.mark.parametrize("w_dtype", ["bf16", "f32"])
-def test_steps_follow_the_sequence(w_dtype):
+def test_steps_follow_the_sequence(w_dtype, B):
     """40 steps, state updated in place, against the oracle's sequence forward
-    (U from the projection oracle on the same x, rounded as the kernel does)."""
-    L, B, d, alpha = 40, 3, 256, 1.0
+    (U from the projection oracle on the same x, rounded as the kernel does);
+    B = 20 with bf16 W takes the matrix-core kernel."""
+    L, d, alpha = 40, 256, 1.0
     W, Wd, v, b = params(d, 77, w_dtype)
     rng = np.random.default_rng(78)
     X = rng.standard_normal((L, B, d)).astype(np.float32)
