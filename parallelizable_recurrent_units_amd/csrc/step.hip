@@ -13,8 +13,8 @@
 // dot products with x~ (per-lane partial sums over 8-element pieces, then a
 // wave reduction); the cell runs one batch row per lane.  W is read from
 // memory once per step; x (B x d) is read by every wave from the caches.
-// From 8 batch rows on, with bf16 W, step_mfma below forms the products on
-// the matrix cores instead.
+// From 8 batch rows on, with bf16 W, step_mfma16 and step_mfma below form
+// the products on the matrix cores instead.
 #include "device_common.h"
 #include "internal.h"
 
