@@ -508,8 +508,9 @@ def cpu_baseline(w, budget_s=10.0):
 ROW_LAUNCHES = {
     "a1_projection": ["gemm_bf16_mfma (A = fp32 X, rounded to bf16 while staged)"],
     "a2_forward": ["fwd_fast (both directions in one grid)"],
-    "a3_a4_backward": ["per direction, last one first (the first adds to dx): bwd_fast "
-                       "(fp32 inputs, up to 128 steps) or scan_clear + bwd_scan",
+    "a3_a4_backward": ["bwd_fast (fp32 inputs, up to 128 steps; both directions in one "
+                       "launch when bidirectional and L <= 64, else one per direction, the "
+                       "last one first) or scan_clear + bwd_scan per direction",
                        "param_reduce (dv, db)"],
     "a5_projection_bwd_data": ["transpose16 (W -> W^T)",
                                "gemm_lds (bf16 dU copy x bf16 W, operands copied straight into LDS)"],
