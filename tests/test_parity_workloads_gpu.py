@@ -11,6 +11,8 @@ the benchmark times.
   rows of dW (each needs the oracle's dU of every batch row for its column).
 * workload 5 (linear mode, L=16384 B=4 d=4096, chunk 256): 24 sampled chains,
   plus size-independent properties for db.
+* beyond 2 GiB per tensor (L=4096 B=16 d=4096, fp32 U of 3.2 GB): the forward
+  and backward on their large-tensor paths, 6 sampled chains.
 Tolerances are explained in test_parity_gpu.py.
 """
 import numpy as np
@@ -247,3 +249,44 @@ def test_workload5_linear_sampled_chains():
         dz = dU[:, :, 0, gate, :].double()
         _sum_bound_check(f"db_{name}", host(db[0, gate]), host(dz.sum((0, 1))),
                          host(dz.abs().sum((0, 1))), n)
+
+
+def test_recurrence_beyond_2gib_sampled_chains():
+    """fp32 U of 3.2 GB (every fast-path tensor limit is 2 GiB): the forward
+    takes the generic kernel, the backward the segmented chunked scan.
+    Inputs are drawn on the device from a seeded generator; the sampled
+    chains' inputs are copied to the host for the oracle, which runs its own
+    forward for the states its backward needs."""
+    import torch
+    L, B, d, alpha = 4096, 16, 4096, 1.0
+    gen = torch.Generator(device="cuda").manual_seed(2024)
+    f32 = dict(device="cuda", dtype=torch.float32)
+    U = torch.randn((L, B, 1, 3, d), generator=gen, **f32)
+    x = torch.randn((L, B, d), generator=gen, **f32)
+    v = (torch.rand((1, 2, d), generator=gen, **f32) - 0.5) * 0.2
+    b = (torch.rand((1, 2, d), generator=gen, **f32) - 0.5) * 0.2
+    c0 = 0.1 * torch.randn((1, B, d), generator=gen, **f32)
+    dh = torch.randn((L, B, 1, d), generator=gen, **f32)
+    assert U.numel() * 4 > 2 ** 31
+    shape = SruShape(L, B, d, False, alpha)
+    print(f"L={L} B={B} d={d}: U {U.numel() * 4 / 2 ** 30:.2f} GiB", flush=True)
+    h, c_seq, c_last = layer.forward(shape, U, x, v, b, c0, keep_c_seq=True)
+    dU, dx, _, _, dc0 = layer.backward(shape, U, x, v, b, c0, c_seq, dh)
+    torch.cuda.synchronize()
+    chains = [(0, 0), (B - 1, d - 1), (5, 1234), (11, 3000), (2, 4095), (15, 64)]
+    vh, bh = host(v)[0], host(b)[0]
+    for bb, j in chains:
+        u = host(U[:, bb, 0, :, j])                      # [L, 3]
+        xs, dhs = host(x[:, bb, j]), host(dh[:, bb, 0, j])
+        cz = float(host(c0[0, bb, j]))
+        hh, cc, cl = oracle.chain_forward(u[:, 0], u[:, 1], u[:, 2], xs, vh[0, j], vh[1, j],
+                                          bh[0, j], bh[1, j], cz, alpha)
+        g = oracle.chain_backward(u[:, 0], u[:, 1], u[:, 2], xs, vh[0, j], vh[1, j], bh[0, j],
+                                  bh[1, j], cz, cc, dhs, 0.0, alpha)
+        tag = f"chain (b={bb}, j={j})"
+        check(f"h {tag}", host(h[:, bb, 0, j]), hh, TIGHT)
+        check(f"c_last {tag}", host(c_last[0, bb, j]), cl, TIGHT)
+        check(f"dU {tag}", host(dU[:, bb, 0, :, j]), np.stack([g["duf"], g["dur"], g["dux"]], 1),
+              TIGHT)
+        check(f"dx {tag}", host(dx[:, bb, j]), g["dx_hw"], TIGHT)
+        check(f"dc0 {tag}", host(dc0[0, bb, j]), g["dc0"], TIGHT)
