@@ -754,7 +754,7 @@ tail:
 // four partial sums are added in wave order.  The summation order depends only
 // on B, so results are identical run to run.
 __global__ __launch_bounds__(256) void param_reduce(const float *__restrict__ part, int64_t B,
-                                                     int64_t d, int ndir, float *dv, float *db)
+                                                     int64_t d, float *dv, float *db)
 {
     __shared__ float red[4][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -930,7 +930,7 @@ hipError_t launch_param_reduce(const float *partials, int64_t B, int64_t d, int 
 {
     const int64_t blocks = (int64_t)ndir * 4 * ((d + 63) / 64);
     hipLaunchKernelGGL(param_reduce, dim3((unsigned)blocks), dim3(256), 0, s, partials, B, d,
-                       ndir, dv, db);
+                       dv, db);
     return hipGetLastError();
 }
 

@@ -145,7 +145,6 @@ __global__ __launch_bounds__(256) void step_cell(StepArgs a)
             xh = load_as_f32(X + b * d + j);
         }
         float mine[3] = {0.0f, 0.0f, 0.0f};
-#pragma unroll 2
         for (int i = 0; i < nb; ++i) {
             float u[3];
             dots(b0 + i, u);
