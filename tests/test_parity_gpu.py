@@ -256,6 +256,31 @@ def test_projection_bf16(L, B, d, nd):
     check("dX (transposed W) vs bf16(dU) oracle", host(dX2).reshape(L * B, d), ref_r, GEMM_ACC)
 
 
+# fp32 X on 256 x 256 tile grids of the register-staged kernel (384 tiles, the
+# last round part-empty): ragged M, and ragged M and N; sampled rows (the last
+# ragged row tile included), every column.  bf16(X) multiplied on the LDS-copy
+# path gives the same bits.
+@pytest.mark.parametrize("L,B,d", [(90, 90, 1024), (90, 90, 960)])
+def test_projection_fp32_x_large_ragged(L, B, d):
+    import torch
+    rng = np.random.default_rng(3200 + d)
+    M = L * B
+    X = rng.standard_normal((L, B, d)).astype(np.float32)
+    W_bits, W = workloads.to_bf16(rng.uniform(-0.05, 0.05, (3 * d, d)).astype(np.float32))
+    Wd = torch.from_numpy(W_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    shape = SruShape(L, B, d, False, 1.0)
+    print(f"case M={M} N={3 * d} K={d}", flush=True)
+    Xd = torch.from_numpy(X).cuda()
+    U = layer.project(shape, Xd, Wd)
+    rows = np.unique(np.concatenate([np.arange(M - 140, M), np.arange(0, 16),
+                                     rng.integers(0, M, 40)]))
+    want = oracle.project(X.reshape(M, d)[rows], W, True)
+    check("U (fp32 X; sampled rows)", host(U).reshape(M, -1)[rows], want, GEMM_ACC)
+    Ub = layer.project(shape, layer.round_bf16(Xd), Wd)
+    torch.cuda.synchronize()
+    assert torch.equal(U.view(torch.int32), Ub.view(torch.int32))
+
+
 # bf16 X on grids of 256 x 256 tiles (operands straight into LDS): ragged M,
 # and ragged M and N (sampled rows, the last ragged row tile included, every
 # column).  X rounded by sru_round_bf16 and then multiplied gives U bit for
