@@ -749,14 +749,18 @@ tail:
 }
 
 // dv[dl, g, j] = sum_b partials[dl, b, g, j]; db[dl, g, j] likewise with rows
-// 2, 3.  A block of 256 threads owns 64 consecutive j of one (dl, g): its four
-// waves sum the b of residue 0..3 (mod 4) with many loads in flight, then the
-// four partial sums are added in wave order.  The summation order depends only
-// on B, so results are identical run to run.
-__global__ __launch_bounds__(256) void param_reduce(const float *__restrict__ part, int64_t B,
-                                                     int64_t d, float *dv, float *db)
+// 2, 3.  A block of 16 waves owns 64 consecutive j of one (dl, g): wave w sums
+// the b of residue w (mod 16), eight loads in flight at a time, then the 16
+// partial sums are added in wave order.  The summation order depends only on
+// B, so results are identical run to run.
+constexpr int kReduceWaves = 16;
+
+__global__ __launch_bounds__(64 * kReduceWaves) void param_reduce(const float *__restrict__ part,
+                                                                 int64_t B, int64_t d, float *dv,
+                                                                 float *db)
 {
-    __shared__ float red[4][64];
+    constexpr int NWv = kReduceWaves, U = 8;
+    __shared__ float red[NWv][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t jblocks = (d + 63) / 64;
     const int64_t row = blockIdx.x / jblocks;           // dl * 4 + g
@@ -767,20 +771,21 @@ __global__ __launch_bounds__(256) void param_reduce(const float *__restrict__ pa
         const float *p = part + ((int64_t)dl * B * 4 + g) * d + j;
         const int64_t stride = 4 * d;                   // next b
         int64_t bb = wv;
-        for (; bb + 12 < B; bb += 16) {
-            const float a0 = p[bb * stride], a1 = p[(bb + 4) * stride];
-            const float a2 = p[(bb + 8) * stride], a3 = p[(bb + 12) * stride];
-            s += a0;
-            s += a1;
-            s += a2;
-            s += a3;
+        for (; bb + (U - 1) * NWv < B; bb += U * NWv) {
+            float v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = p[(bb + u * NWv) * stride];
+#pragma unroll
+            for (int u = 0; u < U; ++u) s += v[u];
         }
-        for (; bb < B; bb += 4) s += p[bb * stride];
+        for (; bb < B; bb += NWv) s += p[bb * stride];
     }
     red[wv][lane] = s;
     __syncthreads();
     if (wv == 0 && j < d) {
-        const float t = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+        float t = red[0][lane];
+#pragma unroll
+        for (int w = 1; w < NWv; ++w) t += red[w][lane];
         if (g < 2) {
             if (dv) dv[(dl * 2 + g) * d + j] = t;
         } else {
@@ -929,8 +934,8 @@ hipError_t launch_param_reduce(const float *partials, int64_t B, int64_t d, int 
                                float *dv, float *db, hipStream_t s)
 {
     const int64_t blocks = (int64_t)ndir * 4 * ((d + 63) / 64);
-    hipLaunchKernelGGL(param_reduce, dim3((unsigned)blocks), dim3(256), 0, s, partials, B, d,
-                       dv, db);
+    hipLaunchKernelGGL(param_reduce, dim3((unsigned)blocks), dim3(64 * kReduceWaves), 0, s,
+                       partials, B, d, dv, db);
     return hipGetLastError();
 }
 
