@@ -243,7 +243,6 @@ constexpr int kLongW = SRU_BWDS_LONG_W, kLongSeg = SRU_BWDS_LONG_SEG;
 static_assert(kShortW * kShortSeg >= 64 && kLongW * kLongSeg >= 64, "chunks of >= 64 steps");
 constexpr int kMaxSeg = kShortSeg > kLongSeg ? kShortSeg : kLongSeg;
 
-inline unsigned blocks_of(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 inline bool is_short(int64_t L) { return L <= SRU_BWDS_SHORT_L; }
 inline int chunk_for(int64_t L) { return is_short(L) ? kShortW * kShortSeg : kLongW * kLongSeg; }
@@ -331,7 +330,7 @@ hipError_t launch_backward_scan(const RecArgs &r, void *ws, float *dv, float *db
         a.dl = dl;
         a.dx_acc = dl != r.ndir - 1;
         if (nC > 1)
-            hipLaunchKernelGGL(scan_clear, dim3(blocks_of(clear_words)), dim3(256), 0, s,
+            hipLaunchKernelGGL(scan_clear, dim3(scan_clear_blocks(clear_words)), dim3(256), 0, s,
                                (uint32_t *)wsf, clear_words);
         if (r.u_bf16)
             r.x_bf16 ? launch_typed<bf16_bits, bf16_bits>(a, grid, s)

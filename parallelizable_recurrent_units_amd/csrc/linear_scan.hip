@@ -595,7 +595,7 @@ hipError_t lin_forward_fused(const LinArgs &a, hipStream_t s)
     const FusedWs f = fused_ws(a, false);
     for (int dl = 0; dl < a.ndir; ++dl) {
         LinGeom g{a.L, a.B, a.d, a.chunk, nC, chains, a.ndir, dl};
-        hipLaunchKernelGGL(scan_clear, dim3(blocks_for(f.clear_words)), dim3(256), 0, s, f.clear,
+        hipLaunchKernelGGL(scan_clear, dim3(scan_clear_blocks(f.clear_words)), dim3(256), 0, s, f.clear,
                            f.clear_words);
         hipLaunchKernelGGL((lin_fwd_fused<TU, TX, kFwdW, kFwdSeg, kFwdPB, kFwdWpe>), dim3((unsigned)(nC * (chains / 64))),
                            dim3(kFwdW * 64), 0, s, g, (const TU *)a.U, (const TX *)a.x, a.b, a.alpha,
@@ -612,7 +612,7 @@ hipError_t lin_backward_fused(const LinArgs &a, hipStream_t s)
     const FusedWs f = fused_ws(a, true);
     for (int dl = a.ndir - 1; dl >= 0; --dl) {
         LinGeom g{a.L, a.B, a.d, a.chunk, nC, chains, a.ndir, dl};
-        hipLaunchKernelGGL(scan_clear, dim3(blocks_for(f.clear_words)), dim3(256), 0, s, f.clear,
+        hipLaunchKernelGGL(scan_clear, dim3(scan_clear_blocks(f.clear_words)), dim3(256), 0, s, f.clear,
                            f.clear_words);
         hipLaunchKernelGGL((lin_bwd_fused<TU, TX, kBwdW, kBwdSeg, kBwdPB, kBwdWpe>), dim3((unsigned)(nC * (chains / 64))),
                            dim3(kBwdW * 64), 0, s, g, (const TU *)a.U, (const TX *)a.x, a.b, a.alpha,

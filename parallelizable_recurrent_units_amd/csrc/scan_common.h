@@ -100,11 +100,18 @@ __device__ __forceinline__ float ldf_off(const char *base, uint32_t off)
 
 // Clears look-back states, ticket and error word before a launch (a plain
 // kernel, so the sequence can also be captured in a graph).
+// Zeroes n 32-bit words at p (16-byte aligned): one 16-byte store per thread,
+// the words of a last partial quad one by one.
 __global__ __launch_bounds__(256) void scan_clear(uint32_t *p, int64_t n)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0u;
+    const int64_t w = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+    if (w + 3 < n)
+        *(uint4 *)(p + w) = make_uint4(0u, 0u, 0u, 0u);
+    else
+        for (int64_t k = w; k < n; ++k) p[k] = 0u;
 }
+
+inline unsigned scan_clear_blocks(int64_t n) { return (unsigned)(((n + 3) / 4 + 255) / 256); }
 
 }  // namespace
 }  // namespace sru
