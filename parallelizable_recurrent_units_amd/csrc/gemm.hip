@@ -14,7 +14,15 @@
 // k-tile is staged global -> registers -> LDS (double-buffered in LDS) while
 // the previous one is multiplied.  Large problems use 256 x 256 blocks of 8
 // waves (one block per CU, two waves per SIMD), small ones 128 x 128 blocks
-// of 4 waves (two blocks per CU) to keep every CU busy.
+// of 4 waves (two blocks per CU) to keep every CU busy.  C is fp32, or bf16
+// for the products whose consumers take bf16.
+//
+// When both operands are bf16 and K-contiguous, gemm_lds copies the k-tiles
+// from memory straight into LDS (no registers, no LDS write instructions).
+//
+// The weight gradient dW = dU^T X~ reads both operands K-major (the
+// reduction index L*B is the slow one) and may split that reduction across
+// blocks; split_reduce then adds the partial products in a fixed order.
 //
 // fp32 path (W in fp32): LDS-tiled FMA kernel, fp32 products and sums.
 #include <type_traits>
