@@ -118,7 +118,7 @@ def _optf32(a):
 
 
 def num_threads() -> int:
-    """Threads the oracle's whole-tensor drivers spread independent chains over."""
+    """Threads the oracle's whole-tensor routines spread independent chains over."""
     return int(_load().sru_oracle_num_threads())
 
 

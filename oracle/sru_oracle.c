@@ -375,7 +375,7 @@ void sru_oracle_chain_backward(int64_t L, int dir, double alpha,
 }
 
 /* ---------------------------------------------------------------------------
- * Whole-tensor drivers.  Layouts (row-major, innermost last):
+ * Whole-tensor routines.  Layouts (row-major, innermost last):
  *   U      [L, B, ndir, 3, d]   slot 0 = f, 1 = r, 2 = candidate (double:
  *                               given fp32/bf16 values widened, or the
  *                               oracle's own projection)
@@ -516,7 +516,7 @@ void sru_oracle_backward(int64_t L, int64_t B, int64_t d, int ndir, double alpha
     free(dxd);
 }
 
-/* Number of threads the OpenMP runtime would use for the drivers above. */
+/* Number of threads the OpenMP runtime would use for the routines above. */
 int sru_oracle_num_threads(void)
 {
     int n = 1;

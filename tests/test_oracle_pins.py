@@ -37,7 +37,7 @@ def rand_problem(rng, L, B, d, nd, v_scale=0.5, b_scale=0.5):
     v = rng.uniform(-v_scale, v_scale, (nd, 2, d))
     b = rng.uniform(-b_scale, b_scale, (nd, 2, d))
     c0 = rng.standard_normal((nd, B, d))
-    # the drivers take x, v, b, c0 as float32: keep them exactly representable
+    # the whole-tensor routines take x, v, b, c0 as float32: keep them exactly representable
     v = v.astype(np.float32).astype(np.float64)
     b = b.astype(np.float32).astype(np.float64)
     c0 = c0.astype(np.float32).astype(np.float64)
@@ -337,8 +337,8 @@ def test_bruteforce_unrolled(L, direction):
     assert cl == pytest.approx(ks[L - 1], rel=1e-15, abs=1e-15)
 
 
-def test_tensor_driver_layout_matches_chain():
-    """The whole-tensor driver places chain (dir, b, j) where the layouts say."""
+def test_tensor_routine_layout_matches_chain():
+    """The whole-tensor routine places chain (dir, b, j) where the layouts say."""
     rng = np.random.default_rng(9)
     L, B, d, nd = 4, 3, 5, 2
     U, x, v, b, c0 = rand_problem(rng, L, B, d, nd)
@@ -389,7 +389,7 @@ def test_backward_finite_differences(linear):
         lm = _loss(args["U"], args["x"], args["v"], args["b"], args["c0"], dh, dcl, al)
         return (lp - lm) / (2 * eps)
 
-    # x, v, b, c0 go through float32 inside the drivers: perturb with a step
+    # x, v, b, c0 go through float32 inside the whole-tensor routines: perturb with a step
     # that float32 represents and compare at a matching tolerance.
     for idx in np.ndindex(U.shape):
         assert g["dU"][idx] == pytest.approx(fd(U, idx, name="U"), rel=1e-6, abs=1e-8)
@@ -403,7 +403,7 @@ def test_backward_finite_differences(linear):
 
 
 def _fd32(name, arr, idx, U, x, v, b, c0, dh, dcl, al):
-    """Central difference for an input the driver reads as float32."""
+    """Central difference for an input the whole-tensor routine reads as float32."""
     eps = 2.0 ** -10
     args = dict(U=U, x=x, v=v, b=b, c0=c0)
     plus = arr.copy(); plus[idx] += eps
