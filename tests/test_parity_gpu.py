@@ -106,6 +106,35 @@ def test_recurrence_fp32_given_u(L, B, d, nd):
         check(k, host(g[k]), bo[k], TIGHT)
 
 
+# saturated gates: |U_f|, |U_r| drawn in [20, 120] with random signs, so the
+# gates are exactly 0 or 1 in fp32 for most steps and e^(-z) exceeds the fp32
+# range for some (the kernels cap the exponent; reading s19).  Forward and
+# every backward kernel: streaming (L = 40), chunked scan (L = 300), generic
+# (d = 37).
+@pytest.mark.parametrize("L,B,d,nd", [(40, 3, 128, 2), (300, 2, 128, 1), (20, 2, 37, 2)])
+def test_recurrence_saturated_gates(L, B, d, nd):
+    w = workloads.custom(L, B, d, ndir=nd, alpha=1.3, mode="given_u", c0="normal0.1")
+    inp = workloads.make_inputs(w, seed=4000 + L + d, dc_last=True, v_scale=0.5, b_scale=0.3)
+    rng = np.random.default_rng(4100 + L)
+    for gate in (0, 1):
+        mag = rng.uniform(20.0, 120.0, inp["U"][:, :, :, gate].shape)
+        sign = np.where(rng.random(mag.shape) < 0.5, -1.0, 1.0)
+        inp["U"][:, :, :, gate] = (sign * mag).astype(np.float32)
+    shape = SruShape(L, B, d, nd == 2, w.alpha)
+    print(f"case L={L} B={B} d={d} ndir={nd} (saturated gates)", flush=True)
+    g = run_fwd_bwd(shape, dev_inputs(inp))
+    fo, bo = oracle_fwd_bwd(inp, w.alpha)
+    for k in ("h", "c_last"):
+        check(k, host(g[k]), fo[k], TIGHT)
+    check("c_seq", host(g["c_seq"]), fo["c"], TIGHT)
+    check("dU", host(g["dU"]), bo["dU"], TIGHT)
+    check("dx", host(g["dx"]), bo["dx_hw"], TIGHT)
+    for k in ("dv", "db", "dc0"):
+        check(k, host(g[k]), bo[k], TIGHT)
+    for k in ("h", "dU", "dx"):
+        assert np.isfinite(host(g[k])).all(), k
+
+
 @pytest.mark.parametrize("L,B,d,nd,xdt", [(37, 2, 128, 1, "bf16"), (8, 3, 64, 2, "bf16"),
                                           (9, 2, 70, 1, "bf16"), (12, 2, 64, 1, "f32"),
                                           (257, 1, 64, 2, "bf16"), (65, 1, 64, 1, "bf16"),
