@@ -66,6 +66,7 @@ __device__ __forceinline__ void cell(const StepArgs &a, int64_t b, int64_t j, fl
 // VEC (d % 8 == 0): 8-element pieces; NC > 0: a W row of d <= 512 NC
 // elements stays in registers (NC pieces per lane); NC == 0: W is re-read
 // for every batch row.  Without VEC every element is loaded on its own.
+// Batch row 0's x pieces are requested together with W.
 // Batch rows go in groups of 64: after the wave reduction of row b0 + i,
 // lane i keeps its three gate inputs, and the cell then runs for the whole
 // group at once, one batch row per lane (one round of state loads).
@@ -81,6 +82,7 @@ __global__ __launch_bounds__(256) void step_cell(StepArgs a)
     const bool rnd = sizeof(TW) == 2;                    // x~ = bf16(x) with bf16 W
     const float vf = a.v[j], vr = a.v[d + j], bf = a.b[j], br = a.b[d + j];
     float w[3][NC > 0 ? NC : 1][8];
+    float x0[NC > 0 ? NC : 1][8];                        // batch row 0, requested with W
     if constexpr (VEC && NC > 0) {
 #pragma unroll
         for (int g = 0; g < 3; ++g)
@@ -93,6 +95,15 @@ __global__ __launch_bounds__(256) void step_cell(StepArgs a)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) w[g][c][e] = 0.0f;
             }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int64_t k = 512 * c + 8 * lane;
+            if (k < d)
+                load8(X + k, x0[c]);
+            else
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x0[c][e] = 0.0f;
+        }
     }
     // the three dot products of batch row b, summed over the wave
     auto dots = [&](int64_t b, float (&u)[3]) {
@@ -103,7 +114,12 @@ __global__ __launch_bounds__(256) void step_cell(StepArgs a)
                 const int64_t k = 512 * c + 8 * lane;
                 if (k >= d) continue;
                 float xv[8];
-                load8(X + b * d + k, xv);
+                if (b == 0) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) xv[e] = x0[c][e];
+                } else {
+                    load8(X + b * d + k, xv);
+                }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float xt = rnd ? round_bf16(xv[e]) : xv[e];
