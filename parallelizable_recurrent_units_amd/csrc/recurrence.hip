@@ -340,8 +340,10 @@ __global__ __launch_bounds__(2 * kWave) void fwd_split(RecArgs a)
         }
     };
 
+    // The ring's packet clamp needs a whole packet inside the sequence, which
+    // a whole group guarantees; shorter sequences run in the tail alone.
     const int64_t groups = L / S;
-    {
+    if (groups > 0) {
         uint4 ring[R];
         // slot sequence: group g - role sits in ring slot (g % NRG)
 #pragma unroll

@@ -158,10 +158,13 @@ def test_recurrence_bf16_u(L, B, d, nd, xdt):
 
 @pytest.mark.parametrize("L,B,d,nd,dt", [(9, 64, 1024, 1, "f32"), (21, 32, 1024, 2, "bf16"),
                                          (3, 64, 1024, 1, "bf16"), (13, 1, 64, 2, "f32"),
-                                         (70, 3, 128, 1, "bf16"), (16, 2, 64, 1, "bf16")])
+                                         (70, 3, 128, 1, "bf16"), (16, 2, 64, 1, "bf16"),
+                                         (1, 2, 64, 2, "f32"), (1, 1, 64, 1, "bf16"),
+                                         (3, 2, 128, 2, "bf16"), (2, 1, 64, 2, "bf16")])
 def test_forward_both_kernels(L, B, d, nd, dt):
     """Forward: one wave per 64 channels (1024+ waves) and the two-wave split
-    (fewer), ragged group tails and sequences shorter than a group."""
+    (fewer), ragged group tails and sequences shorter than a group, down to
+    sequences shorter than one packet (fp32 packets hold 2 steps, bf16 4)."""
     w = workloads.custom(L, B, d, ndir=nd, alpha=0.8, mode="given_u", u_dtype=dt, x_dtype=dt,
                          c0="normal0.1", backward=False)
     inp = workloads.make_inputs(w, seed=3000 + L + B, v_scale=0.5, b_scale=0.3)
