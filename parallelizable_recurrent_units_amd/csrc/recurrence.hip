@@ -528,13 +528,15 @@ __global__ __launch_bounds__(256) void bwd_generic(RecArgs a)
 // ---------------------------------------------------------------------------
 //
 // BIDI: both directions of one (batch row, 64 channels) in one workgroup of
-// two waves (wave w walks direction w).  Each wave keeps its highway dx
-// contributions of all L steps in LDS instead of writing them; at the end
-// the workgroup writes dx = (direction 0) + (direction 1) once, so the two
+// two waves (wave w walks direction w).  The highway dx contributions of all
+// L steps go into one LDS row per step, started at -0.0, to which each wave
+// adds its term with an LDS float atomic (round to nearest even, denormals
+// kept); at the end the workgroup writes the rows to dx once, so the two
 // directions need no ordering between launches and dx is never re-read.
-// (fp32 addition of two terms is commutative, so the sum equals the one the
-// one-direction-per-launch path produces.)  LDS: 2 * L * 64 floats, passed
-// as dynamic shared memory.
+// -0.0 + a is a exactly, and fp32 addition of two terms is commutative, so
+// the row ends as (direction 0) + (direction 1) whichever wave adds first:
+// the sum the one-direction-per-launch path produces.  LDS: L * 64 floats,
+// passed as dynamic shared memory.
 template <int R, int G, bool BIDI>
 __global__ __launch_bounds__(BIDI ? 2 * kWave : kWave) void bwd_fast(RecArgs a)
 {
@@ -543,7 +545,7 @@ __global__ __launch_bounds__(BIDI ? 2 * kWave : kWave) void bwd_fast(RecArgs a)
     __shared__ uint4 slot_a_all[NW][G * kWave];
     __shared__ uint4 slot_b_all[NW][G * kWave];
     __shared__ float out_slot_all[NW][G * 4 * kWave];
-    extern __shared__ float dxbuf[];                 // BIDI: [2][L][64]
+    extern __shared__ float dxbuf[];                 // BIDI: [L][64]
 
     const int wv = BIDI ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
     const int lane = threadIdx.x & 63;
@@ -562,7 +564,6 @@ __global__ __launch_bounds__(BIDI ? 2 * kWave : kWave) void bwd_fast(RecArgs a)
     const int q = lane >> 4;
     const int sub = lane & 15;
     const bool dxacc = !BIDI && a.dx_accumulate;
-    float *dxw = BIDI ? dxbuf + (int64_t)wv * a.L * kWave : nullptr;   // this wave's dx rows
     const uint32_t u_stride = (uint32_t)(a.B * a.ndir * 3 * a.d * 4);
     const uint32_t x_stride = (uint32_t)(a.B * a.d * 4);
     const uint32_t h_stride = (uint32_t)(a.B * a.ndir * a.d * 4);
@@ -613,6 +614,16 @@ __global__ __launch_bounds__(BIDI ? 2 * kWave : kWave) void bwd_fast(RecArgs a)
     float gc = a.dc_last ? a.dc_last[(dl * a.B + bb) * a.d + j] : 0.0f;
     float c = a.c_seq_in[((tix(L - 1) * a.B + bb) * a.ndir + dl) * a.d + j];
     float svf = 0.f, svr = 0.f, sbf = 0.f, sbr = 0.f;
+    // adds one direction's highway dx term to row t of the shared rows
+    auto dx_add = [&](uint32_t t, float v) {
+        __hip_atomic_fetch_add(dxbuf + t * kWave + lane, v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    if constexpr (BIDI) {
+        for (int64_t idx = threadIdx.x; idx < L * 16; idx += 2 * kWave)
+            *(float4 *)(dxbuf + 4 * idx) = make_float4(-0.0f, -0.0f, -0.0f, -0.0f);
+        __syncthreads();
+    }
 
     // one reverse step; returns dU_f, dU_r, dU_cand, dx (highway part)
     auto cell = [&](float uf, float ur, float ux, float xv, float cp, float dhv, float &o0,
@@ -675,6 +686,7 @@ __global__ __launch_bounds__(BIDI ? 2 * kWave : kWave) void bwd_fast(RecArgs a)
                     const int64_t s = L - 1 - (k0 + i);
                     float o0, o1, o2, o3;
                     cell(uf[i], ur[i], ux[i], xv[i], s > 0 ? cp[i] : c0, dhv[i], o0, o1, o2, o3);
+                    if (BIDI) dx_add(t_of(k0 + i), o3);
                     out_slot[i * 256 + lane] = o0;
                     out_slot[i * 256 + 64 + lane] = o1;
                     out_slot[i * 256 + 128 + lane] = o2;
@@ -684,9 +696,7 @@ __global__ __launch_bounds__(BIDI ? 2 * kWave : kWave) void bwd_fast(RecArgs a)
                 for (int i = 0; i < G; ++i) {
                     const float4 val = ((const float4 *)out_slot)[i * 64 + lane];
                     const uint32_t t = t_of(k0 + i);
-                    if (BIDI && q == 3)   // the dx lanes: into this wave's LDS rows
-                        *(float4 *)(dxw + t * kWave + 4 * sub) = val;
-                    else
+                    if (!BIDI || q < 3)   // BIDI: dx went to the LDS rows
                         *(float4 *)(po_ptr + __umul24(t, po_stride)) = val;
                     if (lp_on) {     // lanes of the three dU rows also write bf16
                         uint2 pk;
@@ -721,7 +731,7 @@ tail:
             a.dU_lp[ub + 2 * a.d] = f32_to_bf16(o2);
         }
         if (BIDI)
-            dxw[t * kWave + lane] = o3;
+            dx_add((uint32_t)t, o3);
         else
             a.dx[xi] = dxacc ? o3 + a.dx[xi] : o3;
     }
@@ -734,18 +744,11 @@ tail:
     if constexpr (BIDI) {
         // dx[t, bb, j0 .. j0 + 63] = direction 0 + direction 1, 16-byte stores
         __syncthreads();
-        const float *d0 = dxbuf, *d1 = dxbuf + L * kWave;
         for (int64_t idx = threadIdx.x; idx < L * 16; idx += 2 * kWave) {
             const int64_t t = idx >> 4;
             const int c = (int)(idx & 15) * 4;
-            const float4 u = *(const float4 *)(d0 + t * kWave + c);
-            const float4 v = *(const float4 *)(d1 + t * kWave + c);
-            float4 o;
-            o.x = u.x + v.x;
-            o.y = u.y + v.y;
-            o.z = u.z + v.z;
-            o.w = u.w + v.w;
-            *(float4 *)(a.dx + (t * a.B + bb) * a.d + j0 + c) = o;
+            *(float4 *)(a.dx + (t * a.B + bb) * a.d + j0 + c) =
+                *(const float4 *)(dxbuf + t * kWave + c);
         }
     }
 }
@@ -856,8 +859,8 @@ constexpr int64_t kSplitBelowWaves = 1024;
 #define SRU_BWD_GROUP 4
 #endif
 
-// Longest sequence whose dx rows of both directions (2 * L * 256 bytes) the
-// two-direction backward keeps in LDS.
+// Longest sequence whose dx rows (L * 256 bytes) the two-direction backward
+// keeps in LDS.
 constexpr int64_t kBidiMaxL = 64;
 
 // The fast kernels address with 32-bit byte offsets built from 24-bit
@@ -909,7 +912,7 @@ bool backward_bidi_ok(const RecArgs &a)
 hipError_t launch_backward_bidi(const RecArgs &a, hipStream_t s)
 {
     const int64_t blocks = a.B * (a.d / kWave);
-    const size_t lds = (size_t)2 * a.L * kWave * sizeof(float);
+    const size_t lds = (size_t)a.L * kWave * sizeof(float);
     hipLaunchKernelGGL((bwd_fast<SRU_BWD_RING, SRU_BWD_GROUP, true>), dim3((unsigned)blocks),
                        dim3(2 * kWave), lds, s, a);
     return hipGetLastError();

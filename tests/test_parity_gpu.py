@@ -227,6 +227,49 @@ def test_backward_is_deterministic(L):
         assert np.array_equal(host(a[k]), host(b[k])), k
 
 
+@pytest.mark.parametrize("L", [1, 37, 64])
+@pytest.mark.parametrize("tiny_dh", [False, True])
+def test_two_direction_dx_is_the_sum_of_each_direction(L, tiny_dh):
+    """Up to 64 steps both directions run in one launch and add their highway
+    dx terms into shared rows.  dx must equal, bit for bit, the fp32 sum of
+    what each direction gives on its own (direction 1 as a one-direction
+    layer on time-reversed inputs), whichever direction adds first; with
+    tiny_dh half of dh is scaled by 2^-130, so many terms and sums are fp32
+    denormals, which must be kept."""
+    import torch
+    B, d, alpha = 4, 128, 1.3
+    w = workloads.custom(L, B, d, ndir=2, alpha=alpha, mode="given_u", c0="normal0.1")
+    inp = workloads.make_inputs(w, seed=7600 + L, dc_last=True, v_scale=0.5, b_scale=0.3)
+    if tiny_dh:
+        rng = np.random.default_rng(7700 + L)
+        inp["dh"] = np.where(rng.random(inp["dh"].shape) < 0.5,
+                             inp["dh"] * np.float32(2.0 ** -130), inp["dh"]).astype(np.float32)
+    t = dev_inputs(inp)
+    shape = SruShape(L, B, d, True, alpha)
+    _, c_seq, _ = layer.forward(shape, t["U"], t["x"], t["v"], t["b"], t["c0"], keep_c_seq=True)
+    both = layer.backward(shape, t["U"], t["x"], t["v"], t["b"], t["c0"], c_seq, t["dh"],
+                          t["dc_last"])
+    one = SruShape(L, B, d, False, alpha)
+    parts = []
+    for k in (0, 1):
+        def sel(a, time_axis=True):
+            a = a.narrow(2 if time_axis else 0, k, 1)
+            return (a.flip(0) if (k and time_axis) else a).contiguous()
+        x = t["x"].flip(0).contiguous() if k else t["x"]
+        out = layer.backward(one, sel(t["U"]), x, sel(t["v"], False), sel(t["b"], False),
+                             sel(t["c0"], False), sel(c_seq), sel(t["dh"]),
+                             sel(t["dc_last"], False))
+        dx = out[1].cpu().numpy()                   # fp32 as computed
+        parts.append(dx[::-1] if k else dx)
+    torch.cuda.synchronize()
+    want = parts[0] + parts[1]                      # numpy fp32: IEEE, denormals kept
+    got = both[1].cpu().numpy()
+    assert got.dtype == np.float32 and want.dtype == np.float32
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    if tiny_dh:
+        assert (np.abs(want[want != 0]) < np.finfo(np.float32).tiny).sum() > 100
+
+
 # ---------------------------------------------------------------------------
 # projection GEMM
 # ---------------------------------------------------------------------------
