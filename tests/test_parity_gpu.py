@@ -138,9 +138,11 @@ def test_recurrence_saturated_gates(L, B, d, nd):
 @pytest.mark.parametrize("L,B,d,nd,xdt", [(37, 2, 128, 1, "bf16"), (8, 3, 64, 2, "bf16"),
                                           (9, 2, 70, 1, "bf16"), (12, 2, 64, 1, "f32"),
                                           (257, 1, 64, 2, "bf16"), (65, 1, 64, 1, "bf16"),
-                                          (130, 2, 128, 2, "f32")])
+                                          (130, 2, 128, 2, "f32"), (1, 2, 64, 2, "bf16"),
+                                          (2, 1, 128, 2, "bf16"), (3, 2, 64, 1, "f32")])
 def test_recurrence_bf16_u(L, B, d, nd, xdt):
-    """bf16 U (and x): the fast two-steps-per-packet path and the generic one."""
+    """bf16 U (and x): the fast two-steps-per-packet path and the generic one;
+    the chunked backward scan down to one step."""
     w = workloads.custom(L, B, d, ndir=nd, alpha=1.3, mode="given_u", u_dtype="bf16",
                          x_dtype=xdt, c0="normal0.1")
     inp = workloads.make_inputs(w, seed=2000 + L, dc_last=True, v_scale=0.4, b_scale=0.2)
@@ -580,7 +582,7 @@ def test_linear_scan_bidirectional_ragged():
 
 @pytest.mark.parametrize("L,B,d,nd,dt", [(700, 2, 64, 2, "f32"), (1000, 1, 128, 1, "f32"),
                                          (520, 1, 128, 1, "bf16"), (256, 1, 64, 1, "f32"),
-                                         (3, 2, 64, 1, "f32")])
+                                         (3, 2, 64, 1, "f32"), (1, 1, 64, 2, "bf16")])
 def test_linear_scan_single_pass_chunk256(L, B, d, nd, dt):
     """chunk 256 with d % 64 == 0 takes the single-pass look-back kernels."""
     linear_case(L, B, d, nd, 256, seed=4500 + L, dt=dt)
