@@ -88,7 +88,13 @@ CASES = [(8, 3, 64, 1, 16, 0, True, False, 0.5),
          (64, 2, 256, 1, 64, 0, False, True, 0.3),
          (130, 2, 128, 1, 32, 0, True, False, 1.0),
          (300, 1, 64, 2, 16, 44, False, False, 2.0),
-         (1100, 1, 64, 1, 16, 1000, True, True, 1.0)]
+         (1100, 1, 64, 1, 16, 1000, True, True, 1.0),
+         # odd key counts (bf16 weight rows at odd element offsets): one query
+         # that sees one key (weight exactly 1), one query over 5 context
+         # steps, five queries over five keys without the mask
+         (1, 3, 64, 1, 16, 0, True, False, 0.5),
+         (1, 2, 64, 1, 16, 5, True, True, 1.0),
+         (5, 2, 64, 1, 16, 0, False, False, 1.0)]
 
 
 @pytest.mark.parametrize("L,B,d,nd,dp,Lm,causal,ln,alpha", CASES)
