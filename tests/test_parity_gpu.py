@@ -81,6 +81,11 @@ CASES_F32 = [
     (100, 2, 64, 1),
     (300, 1, 128, 2),
     (131, 2, 64, 1),
+    # two directions from 65 to 128 fp32 steps: one streaming launch per
+    # direction, the second adding its highway dx to the first's
+    (65, 3, 64, 2),
+    (100, 2, 128, 2),
+    (128, 1, 192, 2),
     # the chunked backward scan (fp32 from 129 steps): chunks of 64 with a
     # ragged last chunk, many chunks, both directions
     (129, 2, 64, 2),
