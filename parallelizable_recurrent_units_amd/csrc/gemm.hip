@@ -72,6 +72,13 @@ struct TileCfg {
 // MFMAs while the first waits on LDS or on its loads.
 typedef TileCfg<128, 128, 64, 1, 2> CfgSmall;
 typedef TileCfg<256, 256, 64, 1, 1, 2, 4, false> CfgBig8;
+// 256 x 192 blocks of 8 waves (4 x 2, 64 x 96 each): used where 256 x 256
+// tiles would leave the last round of blocks part-empty and these fill whole
+// rounds of the 256 CUs.
+typedef TileCfg<256, 192, 64, 1, 1, 4, 2, false> CfgWide8;
+#ifndef SRU_GEMM_WIDE
+#define SRU_GEMM_WIDE 1
+#endif
 // Four register stages for bf16 A on small grids: with a long K and one
 // block per CU the loads must be requested four k-tiles ahead to cover a
 // round trip to HBM (the operand then comes from HBM, e.g. the bf16 dU the
@@ -1082,7 +1089,12 @@ template <typename TA, bool KN, typename TC = float>
 hipError_t mfma_launch(const GemmArgs &g, hipStream_t s)
 {
     // large tiles once they give every CU (256) at least one
-    if (tiles_of(g, 256, 256) >= 256)
+    const int64_t big = tiles_of(g, 256, 256), wide = tiles_of(g, 256, 192);
+    if constexpr (!KN) {   // B as [N, K]
+        if (SRU_GEMM_WIDE && big >= 256 && big % 256 != 0 && wide % 256 == 0)
+            return mfma_launch_cfg<CfgWide8, TA, false, bf16_bits, KN, TC>(g, s);
+    }
+    if (big >= 256)
         return mfma_launch_cfg<CfgBig8, TA, false, bf16_bits, KN, TC>(g, s);
     if constexpr (sizeof(TA) == 2 && !KN)
         return mfma_launch_cfg<CfgSmallDeep, TA, false, bf16_bits, KN, TC>(g, s);

@@ -338,11 +338,12 @@ def test_projection_bf16(L, B, d, nd):
     check("dX (transposed W) vs bf16(dU) oracle", host(dX2).reshape(L * B, d), ref_r, GEMM_ACC)
 
 
-# fp32 X on 256 x 256 tile grids of the register-staged kernel (384 tiles, the
-# last round part-empty): ragged M, and ragged M and N; sampled rows (the last
-# ragged row tile included), every column.  bf16(X) multiplied on the LDS-copy
-# path gives the same bits.
-@pytest.mark.parametrize("L,B,d", [(90, 90, 1024), (90, 90, 960)])
+# fp32 X on the register-staged kernel's large tiles: 256 x 192 where 256 x 256
+# would leave the last round part-empty (d = 1024 at M = 8100, d = 512 at
+# M = 16200: 512 tiles for 384), 256 x 256 otherwise (d = 960); ragged M;
+# sampled rows (the last ragged row tile included), every column.  bf16(X)
+# multiplied on the LDS-copy path gives the same bits.
+@pytest.mark.parametrize("L,B,d", [(90, 90, 1024), (90, 90, 960), (90, 180, 512)])
 def test_projection_fp32_x_large_ragged(L, B, d):
     import torch
     rng = np.random.default_rng(3200 + d)
