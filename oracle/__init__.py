@@ -28,7 +28,10 @@ rounding of X and Q, and central differences; for the SRU++ attention, the
 uniform-weight average, the single visible key, the two-key sigmoid form,
 saturation, convexity and key-permutation invariance, rounded weights, the
 layer-norm closed form, and the pages' alpha = 0 reduction to the factorised
-projection.
+projection; for its composition (attention_project) at alpha != 0, the
+closed form with all keys zero (uniform weights: A is a mean of value rows,
+context rows first), the layer norm applied by hand before Wo, and the bf16
+rounding points worked out by hand on a one-key example.
 """
 import ctypes
 import os

@@ -4,6 +4,10 @@ Each case plants one mistake in a copy of oracle/sru_oracle.c (a flipped sign,
 a dropped term, a wrong parameter or index, the wrong rounding or
 normalisation), builds it on the CPU, points the oracle module at the mutant
 library and runs the pin suite (tests/test_oracle_pins.py) in a subprocess.
+The compositions written in Python (oracle/__init__.py: the SRU++ attention's
+residual, context order, rounding points and layer-norm placement) get the
+same treatment: a mutated copy of the module is loaded in place of the real
+one, over an unchanged build of the C library.
 At least one pin must fail for every mutant.  Nothing here touches the GPU
 or the HIP library.
 """
@@ -52,6 +56,37 @@ MUTANTS = [
      "var /= (double)w;", "var /= (double)(w > 1 ? w - 1 : 1);"),
 ]
 
+# (name, text in oracle/__init__.py, the planted mistake)
+PY_SRC = os.path.join(ROOT, "oracle", "__init__.py")
+PY_MUTANTS = [
+    ("attention residual with the wrong sign",
+     "R = Q + alpha * A.reshape(L * B, dp)", "R = Q - alpha * A.reshape(L * B, dp)"),
+    ("context rows after the segment's own rows",
+     "        Kc = np.concatenate([np.asarray(Kmem, np.float64), Kc])\n"
+     "        Vc = np.concatenate([np.asarray(Vmem, np.float64), Vc])",
+     "        Kc = np.concatenate([Kc, np.asarray(Kmem, np.float64)])\n"
+     "        Vc = np.concatenate([Vc, np.asarray(Vmem, np.float64)])"),
+    ("keys and values from the unrounded Q",
+     "Qt = _maybe_bf16(Q, round_ops)", "Qt = Q"),
+    ("values from the key weights",
+     "Vc = matmul(Qt, Wv, b_nk=True)", "Vc = matmul(Qt, Wk, b_nk=True)"),
+    ("layer norm after the output projection",
+     "    if ln is not None:\n"
+     "        R = layernorm(R, ln[0], ln[1], ln[2])\n"
+     "    U = matmul(_maybe_bf16(R, round_ops), Wo, b_nk=True)",
+     "    U = matmul(_maybe_bf16(R, round_ops), Wo, b_nk=True)\n"
+     "    if ln is not None:\n"
+     "        U = layernorm(U, np.resize(ln[0], U.shape[1]), np.resize(ln[1], U.shape[1]), ln[2])"),
+    ("layer norm of Q before the attention term is added",
+     "    R = Q + alpha * A.reshape(L * B, dp)\n"
+     "    if ln is not None:\n"
+     "        R = layernorm(R, ln[0], ln[1], ln[2])",
+     "    R = Q\n"
+     "    if ln is not None:\n"
+     "        R = layernorm(R, ln[0], ln[1], ln[2])\n"
+     "    R = R + alpha * A.reshape(L * B, dp)"),
+]
+
 RUNNER = """
 import sys
 sys.path.insert(0, {root!r})
@@ -63,8 +98,27 @@ sys.exit(pytest.main(["-q", "-x", "-p", "no:cacheprovider", {pins!r}]))
 """
 
 
-def run_pins(tmp_path, source):
-    """Build `source` as the oracle library and run the pin suite against it."""
+# As RUNNER, with the oracle module itself replaced by a copy loaded from a
+# scratch package directory before the pins import it.
+RUNNER_PY = """
+import importlib.util
+import sys
+sys.path.insert(0, {root!r})
+spec = importlib.util.spec_from_file_location("oracle", {init!r},
+                                              submodule_search_locations=[{pkg!r}])
+mod = importlib.util.module_from_spec(spec)
+sys.modules["oracle"] = mod
+spec.loader.exec_module(mod)
+mod._LIB_PATH = {lib!r}
+mod._lib = None
+import pytest
+sys.exit(pytest.main(["-q", "-x", "-p", "no:cacheprovider", {pins!r}]))
+"""
+
+
+def run_pins(tmp_path, source, py_source=None):
+    """Build `source` as the oracle library and run the pin suite against it
+    (with `py_source` as the oracle module, when given)."""
     if shutil.which("gcc") is None:
         pytest.skip("no C compiler")
     c = tmp_path / "sru_oracle_copy.c"
@@ -72,8 +126,16 @@ def run_pins(tmp_path, source):
     lib = tmp_path / "liboracle_copy.so"
     subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", str(c),
                     "-o", str(lib), "-lm"], check=True)
-    code = RUNNER.format(root=ROOT, lib=str(lib),
-                         pins=os.path.join(ROOT, "tests", "test_oracle_pins.py"))
+    pins = os.path.join(ROOT, "tests", "test_oracle_pins.py")
+    if py_source is None:
+        code = RUNNER.format(root=ROOT, lib=str(lib), pins=pins)
+    else:
+        pkg = tmp_path / "oracle_copy"
+        pkg.mkdir()
+        (pkg / "__init__.py").write_text(py_source)
+        shutil.copy(os.path.join(ROOT, "oracle", "build.py"), pkg / "build.py")
+        code = RUNNER_PY.format(root=ROOT, init=str(pkg / "__init__.py"), pkg=str(pkg),
+                                lib=str(lib), pins=pins)
     return subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True,
                           text=True, timeout=600, env=dict(os.environ, OMP_NUM_THREADS="4"))
 
@@ -90,5 +152,20 @@ def test_pins_catch_planted_mistake(tmp_path, name, old, new):
     assert src.count(old) == 1, f"mutation site not unique: {old}"
     r = run_pins(tmp_path, src.replace(old, new))
     # pytest's exit status 1 with a failed pin (not an import or collection error)
+    assert r.returncode == 1 and " failed" in r.stdout, (
+        f"no pin caught '{name}' (exit {r.returncode})\n" + r.stdout[-2000:] + r.stderr[-2000:])
+
+
+def test_unchanged_module_copy_passes_every_pin(tmp_path):
+    """Control for the Python mutants: an unchanged copy of the module."""
+    r = run_pins(tmp_path, open(SRC).read(), open(PY_SRC).read())
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+
+
+@pytest.mark.parametrize("name,old,new", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_pins_catch_planted_mistake_in_the_python_compositions(tmp_path, name, old, new):
+    src = open(PY_SRC).read()
+    assert src.count(old) == 1, f"mutation site not unique: {old}"
+    r = run_pins(tmp_path, open(SRC).read(), src.replace(old, new))
     assert r.returncode == 1 and " failed" in r.stdout, (
         f"no pin caught '{name}' (exit {r.returncode})\n" + r.stdout[-2000:] + r.stderr[-2000:])

@@ -612,6 +612,100 @@ def test_attention_project_alpha_zero_is_the_factorised_projection():
         np.testing.assert_array_equal(a["Q"], f["Q"])
 
 
+def _uniform_attention_case(seed, L, B, d, dp, Lm):
+    """Inputs whose keys are all zero (W_k = 0 and zero context keys), so
+    every score is 0 and each query's weights are uniform over the keys it
+    may see: the attention is then a plain mean of value rows."""
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((L * B, d)).astype(np.float32)
+    Wq = rng.standard_normal((dp, d))
+    Wk = np.zeros((dp, dp))
+    Wv = rng.standard_normal((dp, dp))
+    Wo = rng.standard_normal((3 * d, dp))
+    Kmem = np.zeros((Lm, B, dp))
+    Vmem = rng.standard_normal((Lm, B, dp))
+    return X, Wq, Wk, Wv, Wo, Kmem, Vmem
+
+
+def _uniform_attention_by_hand(X, Wq, Wv, Vmem, L, B, Lm, causal):
+    """Q = X Wq^T and V = Q Wv^T with numpy; A[t, b] = mean of the visible
+    value rows, the context rows first (the previous segment precedes this
+    one), so with a causal mask step t sees the Lm context rows and steps
+    0..t of its own segment."""
+    Q = X.astype(np.float64) @ Wq.T
+    V = (Q @ Wv.T).reshape(L, B, -1)
+    allv = np.concatenate([Vmem, V])
+    A = np.empty_like(V)
+    for t in range(L):
+        n = Lm + t + 1 if causal else Lm + L
+        A[t] = allv[:n].mean(axis=0)
+    return Q, V, A.reshape(L * B, -1)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_project_uniform_weights_closed_form(causal):
+    """SRU++ section: U = Wo (Q + alpha A) with K = Wk Q and V = Wv Q.  With
+    all keys zero, A is a mean of value rows, so the whole composition has a
+    closed form at alpha != 0: it fixes the sign of the residual, that V is
+    built from Q, and that the context rows come first (causal: a context
+    appended after the segment would let step 0 see steps 1.. instead)."""
+    L, B, d, dp, Lm, alpha = 3, 2, 6, 4, 2, 0.75
+    X, Wq, Wk, Wv, Wo, Kmem, Vmem = _uniform_attention_case(37, L, B, d, dp, Lm)
+    a = oracle.attention_project(X, Wq, Wk, Wv, Wo, L, B, alpha, mem_len=Lm, Kmem=Kmem,
+                                 Vmem=Vmem, causal=causal)
+    Q, V, A = _uniform_attention_by_hand(X, Wq, Wv, Vmem, L, B, Lm, causal)
+    R = Q + alpha * A
+    np.testing.assert_allclose(a["Q"], Q, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(a["V"][Lm:], V, rtol=1e-13, atol=1e-13)
+    np.testing.assert_array_equal(a["V"][:Lm], Vmem)
+    np.testing.assert_allclose(a["A"], A, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(a["R"], R, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(a["U"], R @ Wo.T, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_project_layernorm_before_the_output_projection():
+    """The layer-norm variant normalises the residual sum Q + alpha A over
+    its d' features (biased variance, gain, shift) and only then applies Wo
+    (SRU++ section).  Closed form as above; the normalisation by hand with
+    numpy's mean and variance."""
+    L, B, d, dp, Lm, alpha, eps = 3, 2, 6, 4, 2, -1.25, 1e-5
+    X, Wq, Wk, Wv, Wo, Kmem, Vmem = _uniform_attention_case(38, L, B, d, dp, Lm)
+    rng = np.random.default_rng(39)
+    gamma = rng.uniform(0.5, 1.5, dp)
+    beta = rng.uniform(-0.5, 0.5, dp)
+    a = oracle.attention_project(X, Wq, Wk, Wv, Wo, L, B, alpha, mem_len=Lm, Kmem=Kmem,
+                                 Vmem=Vmem, causal=True, ln=(gamma, beta, eps))
+    Q, _, A = _uniform_attention_by_hand(X, Wq, Wv, Vmem, L, B, Lm, True)
+    S = Q + alpha * A
+    mu = S.mean(axis=1, keepdims=True)
+    var = S.var(axis=1, keepdims=True)
+    R = (S - mu) / np.sqrt(var + eps) * gamma + beta
+    np.testing.assert_allclose(a["R"], R, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(a["U"], R @ Wo.T, rtol=1e-11, atol=1e-11)
+
+
+def test_attention_project_rounding_points_by_hand():
+    """The bf16 path: K and V are products of the rounded Q~, not of Q, and
+    the residual adds the unrounded Q.  One step, one key, d = 2, d' = 1:
+      Q  = 1 * 1 + 1 * 2^-9 = 1.001953125, Q~ = bf16(Q) = 1 (spacing 2^-7);
+      K  = Q~ * 0.5 = 0.5;  V = Q~ * 3 = 3 (3.005859375 from unrounded Q);
+      the single visible key has weight 1, so A = bf16(V) = 3;
+      R  = Q + 0.5 * A = 2.501953125, R~ = 2.5 (spacing 2^-6);
+      U  = R~ * Wo = 2.5 * [1, 2, -1, 0.5, 4, -2]."""
+    X = np.array([[1.0, 1.0]], np.float32)
+    Wq = np.array([[1.0, 2.0 ** -9]])
+    Wk = np.array([[0.5]])
+    Wv = np.array([[3.0]])
+    Wo = np.array([[1.0], [2.0], [-1.0], [0.5], [4.0], [-2.0]])
+    a = oracle.attention_project(X, Wq, Wk, Wv, Wo, 1, 1, 0.5, causal=True, round_ops=True)
+    assert a["Q"][0, 0] == 1.001953125
+    assert a["K"][0, 0, 0] == 0.5
+    assert a["V"][0, 0, 0] == 3.0
+    assert a["A"][0, 0] == 3.0
+    assert a["R"][0, 0] == 2.501953125
+    np.testing.assert_array_equal(a["U"][0], 2.5 * Wo[:, 0])
+
+
 # --------------------------------------------------------------------------
 # decoding step
 # --------------------------------------------------------------------------
