@@ -287,7 +287,12 @@ sru_status sru_forward(const sru_shape *shape,
  *       a fixed order, so results are bit-reproducible run to run).
  *   dc0: fp32 [ndir, B, d] or NULL.
  *   workspace: at least sru_workspace_size(shape, SRU_WS_BACKWARD, 0) bytes
- *       of device memory, 256-byte aligned; its contents are scratch.
+ *       of device memory, 256-byte aligned; scratch, except for its error
+ *       word (SRU_WS_ERROR_OFFSET below).
+ * For longer sequences the backward runs as a chunked scan of the state's
+ * adjoint, in which each chunk takes its incoming adjoint from the chunk
+ * after it through the workspace (a bounded wait); the error word reports a
+ * wait that ran out.
  */
 sru_status sru_backward(const sru_shape *shape,
                         const void *U, sru_dtype u_dt,
@@ -315,11 +320,8 @@ sru_status sru_backward(const sru_shape *shape,
  *   SRU_WS_LINEAR_BWD, chunk) bytes, 256-byte aligned.
  * With chunk == 256 and d % 64 == 0 the three steps run as one kernel per
  * direction: each chunk takes its incoming state from the preceding chunk
- * through the workspace (a bounded wait).  Should a wait ever run out, the
- * kernel stops waiting and sets the 32-bit word at byte offset
- * 8 * ceil(L / 256) * B * d + 4 of the workspace to a nonzero value; the
- * outputs of that call are then invalid.  The word is cleared at the start
- * of every such call and may be read after it completes.
+ * through the workspace (a bounded wait); the error word reports a wait that
+ * ran out (SRU_WS_ERROR_OFFSET below).
  */
 sru_status sru_linear_scan(const sru_shape *shape, sru_pass pass, int32_t chunk,
                            const void *U, sru_dtype u_dt,
@@ -348,6 +350,18 @@ sru_status sru_transpose_weight(const sru_shape *shape, const void *W, sru_dtype
  * overlapping; n >= 1.
  */
 sru_status sru_round_bf16(int64_t n, const float *src, void *dst, void *stream);
+
+/*
+ * The error word of sru_backward and sru_linear_scan: the 32-bit word at
+ * byte offset SRU_WS_ERROR_OFFSET of the workspace passed to the call (the
+ * first 256 bytes of those workspaces are a control block).  Every such call
+ * clears it before its first kernel runs; once the call's work has completed
+ * (after the caller synchronises with `stream`) it is 0, or nonzero if a
+ * bounded wait between chunks ran out, in which case that call's outputs are
+ * invalid.  The kernels stop waiting rather than hang, so the call still
+ * completes.  The word keeps its value until the next call on that workspace.
+ */
+#define SRU_WS_ERROR_OFFSET 0
 
 /* Workspace bytes needed by `op` for `shape` (and `chunk`: the chunk length
  * for the linear mode, the inner dimension d' for SRU_WS_FACTORED_WEIGHT);

@@ -17,4 +17,5 @@ from ._binding import (  # noqa: F401
     SRU_PROJ_BWD_DATA, SRU_PROJ_BWD_DATA_WT, SRU_PROJ_FWD, SRU_WS_BACKWARD, SRU_WS_BWD_WEIGHT, SRU_WS_LINEAR_BWD,
     SRU_WS_LINEAR_FWD,
     SruError, SruShape, load_library, sru_backward, sru_forward, sru_linear_scan, sru_project,
-    sru_project_bwd_weight, sru_transpose_weight, sru_workspace_size)
+    sru_project_bwd_weight, sru_transpose_weight, sru_workspace_size,
+    SRU_WS_ERROR_OFFSET, workspace_error_word, check_workspace)

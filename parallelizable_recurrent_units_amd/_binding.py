@@ -152,6 +152,14 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _need_f32(**tensors):
+    """The arguments libsru reads or writes only as fp32 (None is skipped)."""
+    import torch
+    for name, t in tensors.items():
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32 (got {t.dtype})")
+
+
 def _stream(stream) -> Optional[int]:
     import torch
     if stream is None:
@@ -182,6 +190,7 @@ def sru_project(shape, op: int, A, W, C, accumulate: bool = False, stream=None):
 def sru_project_bwd_weight(shape, dU, X, dW, math_dtype: int = SRU_BF16, accumulate: bool = False,
                            workspace=None, stream=None):
     s = _shape(shape)
+    _need_f32(dW=dW)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().sru_project_bwd_weight(
         ctypes.byref(s), _ptr(dU), _dtype_code(dU), _ptr(X), _dtype_code(X), _ptr(dW),
@@ -226,9 +235,7 @@ def sru_attention_forward(shape, cfg, X, Wq, Wkv, Wo, gamma, beta, Q, KV, R, U, 
     for name, t in (("Wq", Wq), ("Wkv", Wkv), ("Wo", Wo), ("KV", KV)):
         if _dtype_code(t) != SRU_BF16:
             raise TypeError(f"{name} must be bfloat16")
-    for name, t in (("Q", Q), ("R", R)):
-        if _dtype_code(t) != SRU_F32:
-            raise TypeError(f"{name} must be float32")
+    _need_f32(Q=Q, R=R, gamma=gamma, beta=beta)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().sru_attention_forward(
         ctypes.byref(s), ctypes.byref(cfg), _ptr(X), _dtype_code(X), _ptr(Wq), _ptr(Wkv),
@@ -238,6 +245,7 @@ def sru_attention_forward(shape, cfg, X, Wq, Wkv, Wo, gamma, beta, Q, KV, R, U, 
 
 def sru_step(shape, x, W, v, b, c_prev, h, c_next, stream=None):
     s = _shape(shape)
+    _need_f32(v=v, b=b, c_prev=c_prev, h=h, c_next=c_next)
     _check(load_library().sru_step(ctypes.byref(s), _ptr(x), _dtype_code(x), _ptr(W),
                                    _dtype_code(W), _ptr(v), _ptr(b), _ptr(c_prev), _ptr(h),
                                    _ptr(c_next), _stream(stream)))
@@ -259,6 +267,7 @@ def sru_transpose_weight(shape, W, Wt, stream=None):
 
 def sru_forward(shape, U, x, v, b, c0, h, c_seq=None, c_last=None, stream=None):
     s = _shape(shape)
+    _need_f32(v=v, b=b, c0=c0, c_seq=c_seq, c_last=c_last)
     _check(load_library().sru_forward(ctypes.byref(s), _ptr(U), _dtype_code(U), _ptr(x),
                                       _dtype_code(x), _ptr(v), _ptr(b), _ptr(c0), _ptr(h),
                                       _dtype_code(h), _ptr(c_seq), _ptr(c_last),
@@ -268,6 +277,8 @@ def sru_forward(shape, U, x, v, b, c0, h, c_seq=None, c_last=None, stream=None):
 def sru_backward(shape, U, x, v, b, c0, c_seq, dh, dc_last, dU, dx, dv, db, dc0,
                  workspace, dU_lp=None, stream=None):
     s = _shape(shape)
+    _need_f32(v=v, b=b, c0=c0, c_seq=c_seq, dh=dh, dc_last=dc_last, dU=dU, dx=dx, dv=dv, db=db,
+              dc0=dc0)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if dU_lp is not None and _dtype_code(dU_lp) != SRU_BF16:
         raise TypeError("dU_lp must be bfloat16")
@@ -282,6 +293,8 @@ def sru_linear_scan(shape, pass_: int, chunk: int, U, x, b, c0, h=None, c_seq=No
                     c_last=None, dh=None, dc_last=None, dU=None, dx=None, db=None, dc0=None,
                     workspace=None, stream=None):
     s = _shape(shape)
+    _need_f32(b=b, c0=c0, c_seq=c_seq, c_last=c_last, dh=dh, dc_last=dc_last, dU=dU, dx=dx,
+              db=db, dc0=dc0)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     h_dt = _dtype_code(h) if h is not None else SRU_F32
     _check(load_library().sru_linear_scan(
@@ -289,3 +302,27 @@ def sru_linear_scan(shape, pass_: int, chunk: int, U, x, b, c0, h=None, c_seq=No
         _dtype_code(x), _ptr(b), _ptr(c0), _ptr(h), h_dt, _ptr(c_seq), _ptr(c_last),
         _ptr(dh), _ptr(dc_last), _ptr(dU), _ptr(dx), _ptr(db), _ptr(dc0), _ptr(workspace),
         ws_bytes, _stream(stream)))
+
+
+# Byte offset of the error word in the workspaces of sru_backward and
+# sru_linear_scan (SRU_WS_ERROR_OFFSET in include/sru.h).
+SRU_WS_ERROR_OFFSET = 0
+
+
+def workspace_error_word(workspace) -> int:
+    """The 32-bit error word of a workspace last passed to sru_backward or
+    sru_linear_scan: 0, or nonzero when a bounded wait between chunks ran out
+    (that call's outputs are then invalid).  Reads 4 bytes from the device,
+    which waits for the work queued before it on the current stream."""
+    import torch
+    raw = workspace.view(torch.uint8)[SRU_WS_ERROR_OFFSET:SRU_WS_ERROR_OFFSET + 4]
+    return int(raw.cpu().view(torch.int32)[0])
+
+
+def check_workspace(workspace, what: str = "scan"):
+    """Raise if the workspace's error word is set (see workspace_error_word)."""
+    w = workspace_error_word(workspace)
+    if w != 0:
+        raise SruError(SRU_ERR_LAUNCH, "SRU_ERR_LAUNCH",
+                       f"{what}: a wait between chunks ran out (error word {w:#x}); "
+                       "the outputs of that call are invalid")

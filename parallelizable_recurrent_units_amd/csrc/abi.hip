@@ -134,6 +134,29 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
     return x < y + nb && y < x + na;
 }
 
+// A device buffer as the checks below see it: base, bytes, name.  A NULL
+// pointer or a zero size is skipped.
+struct Span {
+    const void *p;
+    size_t n;
+    const char *name;
+};
+
+// Fails when a written buffer overlaps another written buffer or any input.
+sru_status no_overlap(const Span *out, int nout, const Span *in, int nin)
+{
+    for (int i = 0; i < nout; ++i) {
+        if (!out[i].p || !out[i].n) continue;
+        for (int j = i + 1; j < nout; ++j)
+            if (out[j].p && out[j].n && overlaps(out[i].p, out[i].n, out[j].p, out[j].n))
+                return fail(SRU_ERR_INVALID_ARG, "%s overlaps %s", out[i].name, out[j].name);
+        for (int j = 0; j < nin; ++j)
+            if (in[j].p && in[j].n && overlaps(out[i].p, out[i].n, in[j].p, in[j].n))
+                return fail(SRU_ERR_INVALID_ARG, "%s overlaps %s", out[i].name, in[j].name);
+    }
+    return SRU_OK;
+}
+
 size_t product_ws(Layout lay, int64_t M, int64_t N, int64_t K)
 {
     return lay == Layout::TN ? round256(sru::wgrad_workspace_bytes(M, N, K)) : 0;
@@ -267,8 +290,16 @@ sru_status sru_project(const sru_shape *shape, sru_proj_op op, const void *A, sr
     // grid: x over row tiles (>= 64 rows each), y over column tiles (<= 65535)
     if ((dm.LB + 63) / 64 > kMaxBlocks || (3 * dm.ndir * shape->d + 63) / 64 > 65535)
         return fail(SRU_ERR_INVALID_ARG, "matrix too large for one projection launch");
-    SRU_TRY(need_device());
     const int64_t n3 = 3 * dm.ndir * shape->d;
+    {   // C [L*B, n3 or d] against A [L*B, d or n3] and W (n3 * d elements)
+        const size_t lbd = (size_t)(dm.LB * shape->d), lbn = (size_t)dm.u_elems;
+        const bool fwd = op == SRU_PROJ_FWD;
+        const Span out[] = {{C, (fwd ? lbn : lbd) * 4, "C"}};
+        const Span in[] = {{A, (fwd ? lbd : lbn) * elem_bytes(a_dt), "A"},
+                           {W, (size_t)(n3 * shape->d) * elem_bytes(w_dt), "W"}};
+        SRU_TRY(no_overlap(out, 1, in, 2));
+    }
+    SRU_TRY(need_device());
     sru::GemmArgs g;
     g.M = dm.LB;
     g.A = A;
@@ -428,11 +459,6 @@ sru_status sru_attention_forward(const sru_shape *shape, const sru_attn_cfg *cfg
     const int64_t L = shape->L, B = shape->B, d = shape->d, dp = cfg->d_inner;
     const int64_t Lm = cfg->mem_len, n3 = 3 * dm.ndir * d;
     {   // the written outputs against each other and every input
-        struct Span {
-            const void *p;
-            size_t n;
-            const char *name;
-        };
         const Span out[] = {{Q, (size_t)(dm.LB * dp) * 4, "Q"},
                             {KV, (size_t)((Lm + L) * B * 2 * dp) * 2, "KV"},
                             {R, (size_t)(dm.LB * dp) * 4, "R"},
@@ -443,14 +469,7 @@ sru_status sru_attention_forward(const sru_shape *shape, const sru_attn_cfg *cfg
                            {Wo, (size_t)(n3 * dp) * 2, "Wo"},
                            {gamma, cfg->layernorm ? (size_t)dp * 4 : 0, "gamma"},
                            {beta, cfg->layernorm ? (size_t)dp * 4 : 0, "beta"}};
-        for (int i = 0; i < 4; ++i) {
-            for (int j = i + 1; j < 4; ++j)
-                if (overlaps(out[i].p, out[i].n, out[j].p, out[j].n))
-                    return fail(SRU_ERR_INVALID_ARG, "%s overlaps %s", out[i].name, out[j].name);
-            for (const Span &x : in)
-                if (x.p && x.n && overlaps(out[i].p, out[i].n, x.p, x.n))
-                    return fail(SRU_ERR_INVALID_ARG, "%s overlaps %s", out[i].name, x.name);
-        }
+        SRU_TRY(no_overlap(out, 4, in, 6));
     }
     const size_t need = round256(sru::attention_workspace_bytes(L, B, dp, Lm));
     if (!workspace || workspace_bytes < need)
@@ -568,6 +587,15 @@ sru_status sru_forward(const sru_shape *shape, const void *U, sru_dtype u_dt, co
     SRU_TRY(opt_ptr(c_seq, "c_seq"));
     SRU_TRY(opt_ptr(c_last, "c_last"));
     if (h_dt != SRU_F32) return fail(SRU_ERR_UNSUPPORTED, "h must be fp32");
+    {
+        const size_t lbd = (size_t)(dm.LB * shape->d), hs = lbd * dm.ndir * 4;
+        const size_t cs = (size_t)dm.chains * 4, ps = (size_t)(dm.ndir * 2 * shape->d) * 4;
+        const Span out[] = {{h, hs, "h"}, {c_seq, hs, "c_seq"}, {c_last, cs, "c_last"}};
+        const Span in[] = {{U, (size_t)dm.u_elems * elem_bytes(u_dt), "U"},
+                           {x, lbd * elem_bytes(x_dt), "x"}, {v, ps, "v"}, {b, ps, "b"},
+                           {c0, cs, "c0"}};
+        SRU_TRY(no_overlap(out, 3, in, 5));
+    }
     SRU_TRY(need_device());
     sru::RecArgs a{};
     a.L = shape->L;
@@ -617,6 +645,18 @@ sru_status sru_backward(const sru_shape *shape, const void *U, sru_dtype u_dt, c
         return fail(SRU_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need,
                     workspace_bytes, workspace ? "" : ", NULL");
     SRU_TRY(opt_ptr(workspace, "workspace"));
+    {
+        const size_t lbd = (size_t)(dm.LB * shape->d), hs = lbd * dm.ndir * 4;
+        const size_t cs = (size_t)dm.chains * 4, ps = (size_t)(dm.ndir * 2 * shape->d) * 4;
+        const size_t ue = (size_t)dm.u_elems;
+        const Span out[] = {{dU, ue * 4, "dU"}, {dU_lp, ue * 2, "dU_lp"}, {dx, lbd * 4, "dx"},
+                            {dv, ps, "dv"}, {db, ps, "db"}, {dc0, cs, "dc0"},
+                            {workspace, need, "workspace"}};
+        const Span in[] = {{U, ue * elem_bytes(u_dt), "U"}, {x, lbd * elem_bytes(x_dt), "x"},
+                           {v, ps, "v"}, {b, ps, "b"}, {c0, cs, "c0"}, {c_seq, hs, "c_seq"},
+                           {dh, hs, "dh"}, {dc_last, cs, "dc_last"}};
+        SRU_TRY(no_overlap(out, 7, in, 8));
+    }
     SRU_TRY(need_device());
     sru::RecArgs a{};
     a.L = shape->L;
@@ -638,7 +678,10 @@ sru_status sru_backward(const sru_shape *shape, const void *U, sru_dtype u_dt, c
     a.dU_lp = (sru::bf16_bits_t *)dU_lp;
     a.dx = dx;
     a.dc0 = dc0;
-    a.partials = (float *)workspace;
+    // the per-chain kernels' partial sums follow the control block; they
+    // clear its error word themselves (they have no look-back)
+    a.partials = (float *)workspace + sru::kCtrlWords;
+    a.err_word = (uint32_t *)workspace + sru::kErrWord;
     hipStream_t s = (hipStream_t)stream;
     if (sru::backward_scan_ok(a.L, a.B, a.d, a.ndir, !a.u_bf16 && !a.x_bf16))
         return launched(sru::launch_backward_scan(a, workspace, dv, db, s), "backward scan");
@@ -706,6 +749,24 @@ sru_status sru_linear_scan(const sru_shape *shape, sru_pass pass, int32_t chunk,
         return fail(SRU_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need,
                     workspace_bytes, workspace ? "" : ", NULL");
     SRU_TRY(opt_ptr(workspace, "workspace"));
+    {
+        const size_t lbd = (size_t)(dm.LB * shape->d), hs = lbd * dm.ndir * 4;
+        const size_t cs = (size_t)dm.chains * 4, ps = (size_t)(dm.ndir * 2 * shape->d) * 4;
+        const size_t ue = (size_t)dm.u_elems;
+        const Span in_common[] = {{U, ue * elem_bytes(u_dt), "U"}, {x, lbd * elem_bytes(x_dt), "x"},
+                                  {b, ps, "b"}, {c0, cs, "c0"}};
+        if (!bwd) {
+            const Span out[] = {{h, hs, "h"}, {c_seq, hs, "c_seq"}, {c_last, cs, "c_last"},
+                                {workspace, need, "workspace"}};
+            SRU_TRY(no_overlap(out, 4, in_common, 4));
+        } else {
+            const Span out[] = {{dU, ue * 4, "dU"}, {dx, lbd * 4, "dx"}, {db, ps, "db"},
+                                {dc0, cs, "dc0"}, {workspace, need, "workspace"}};
+            const Span in[] = {in_common[0], in_common[1], in_common[2], in_common[3],
+                               {c_seq, hs, "c_seq"}, {dh, hs, "dh"}, {dc_last, cs, "dc_last"}};
+            SRU_TRY(no_overlap(out, 5, in, 7));
+        }
+    }
     SRU_TRY(need_device());
     sru::LinArgs a{};
     a.L = shape->L;

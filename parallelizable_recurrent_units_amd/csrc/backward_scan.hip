@@ -65,7 +65,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(WPE))) v
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int64_t tiles = a.chains / 64;
-    // one chunk: no look-back, so no ticket either
+    // one chunk: no look-back, so no ticket either, and no wait can run out
+    if (a.nC == 1 && blockIdx.x == 0 && threadIdx.x == 0) *a.lb.err = 0u;
     const int64_t tk = a.nC == 1 ? (int64_t)blockIdx.x : take_ticket(a.lb, &s_ticket);
     const int64_t k = a.nC - 1 - tk / tiles, tile = tk % tiles;       // last chunk first
     const int64_t ch0 = tile * 64, ch = ch0 + lane;
@@ -283,10 +284,10 @@ bool backward_scan_ok(int64_t L, int64_t B, int64_t d, int ndir, bool fp32_input
 
 size_t backward_scan_workspace_bytes(int64_t L, int64_t B, int64_t d, int ndir)
 {
-    // look-back states (64-bit) + 64 control words + partial sums; the
+    // the control block + look-back states (64-bit) + partial sums; the
     // shortest chunk (64 steps) bounds the chunk count
     const int64_t nC = (L + 63) / 64;
-    const int64_t floats = 2 * nC * B * d + 64 + (int64_t)ndir * nC * B * 4 * d;
+    const int64_t floats = kCtrlWords + 2 * nC * B * d + (int64_t)ndir * nC * B * 4 * d;
     return (size_t)floats * sizeof(float);
 }
 
@@ -317,21 +318,26 @@ hipError_t launch_backward_scan(const RecArgs &r, void *ws, float *dv, float *db
     a.dx = r.dx;
     a.dc0 = r.dc0;
     a.dU_lp = r.dU_lp;
-    a.lb.carry = (uint64_t *)wsf;
-    uint32_t *ctrl = (uint32_t *)(wsf + 2 * nC * chains);
-    a.lb.ticket = ctrl;
-    a.lb.err = ctrl + 1;
-    a.part = wsf + 2 * nC * chains + 64;
-    const int64_t clear_words = 2 * nC * chains + 64;
+    // control block (error word, ticket), then the published adjoints, then
+    // the partial sums
+    uint32_t *ctrl = (uint32_t *)wsf;
+    a.lb.err = ctrl + kErrWord;
+    a.lb.ticket = ctrl + kTicketWord;
+    a.lb.carry = (uint64_t *)(wsf + kCtrlWords);
+    a.part = wsf + kCtrlWords + 2 * nC * chains;
+    const int64_t clear_words = kCtrlWords + 2 * nC * chains;
     const unsigned grid = (unsigned)(nC * (chains / 64));
     // the highway dx sums both directions: the last direction writes it, the
     // one before adds to it (stream order serialises the launches)
     for (int dl = r.ndir - 1; dl >= 0; --dl) {
         a.dl = dl;
         a.dx_acc = dl != r.ndir - 1;
+        // the error word is cleared once per call (before the first
+        // direction), the ticket and the published adjoints before each
+        const int64_t from = dl == r.ndir - 1 ? 0 : kTicketWord;
         if (nC > 1)
-            hipLaunchKernelGGL(scan_clear, dim3(scan_clear_blocks(clear_words)), dim3(256), 0, s,
-                               (uint32_t *)wsf, clear_words);
+            hipLaunchKernelGGL(scan_clear, dim3(scan_clear_blocks(clear_words - from)), dim3(256),
+                               0, s, ctrl + from, clear_words - from);
         if (r.u_bf16)
             r.x_bf16 ? launch_typed<bf16_bits, bf16_bits>(a, grid, s)
                      : launch_typed<bf16_bits, float>(a, grid, s);

@@ -10,6 +10,14 @@ namespace sru {
 
 typedef uint16_t bf16_bits_t;
 
+// Every workspace of sru_backward and sru_linear_scan starts with a control
+// block of kCtrlWords 32-bit words (256 bytes): word kErrWord is the call's
+// error word (cleared by every call; nonzero after it only if a bounded
+// look-back wait between chunks ran out), word kTicketWord the chunk ticket
+// of the single-pass scans.  The kernels' own data follows at byte 256.
+constexpr int64_t kCtrlWords = 64;
+constexpr int64_t kErrWord = 0, kTicketWord = 4;
+
 // Arguments of the forward / backward recurrence launchers.  Element counts
 // and offsets are int64; layouts are those of include/sru.h.
 struct RecArgs {
@@ -28,6 +36,8 @@ struct RecArgs {
     float *dU, *dx, *dc0;
     bf16_bits_t *dU_lp;  // optional bf16 copy of dU (nearest even)
     float *partials;     // [ndir, B, 4, d] per-chain sums over t
+    uint32_t *err_word;  // the workspace's error word: zeroed by the kernels
+                         // that have no look-back (nothing else writes it)
     int dir;             // backward: the one direction this launch walks
     bool dx_accumulate;  // backward: add to dx instead of overwriting
 };

@@ -550,14 +550,15 @@ static_assert(kFwdW * kFwdSeg == kFusedChunk && kBwdW * kBwdSeg == kFusedChunk, 
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 // Workspace layout of the single-pass kernels (in floats):
+//   control block [kCtrlWords] (error word, ticket) |
 //   published states [nC * chains] 64-bit words (2 floats each) |
-//   ticket, error, pad to 64 | backward only: db partials [2 * nC * chains]
-// The states and the control words are cleared before each launch.
+//   backward only: db partials [2 * nC * chains]
+// The ticket and the states are cleared before each direction's launch, the
+// error word once per call (before the first direction).
 struct FusedWs {
     Lookback lb;
     float *dbpart;
-    uint32_t *ctrl;
-    uint32_t *clear;       // start of the region cleared before each launch
+    uint32_t *ctrl;        // the control block; the cleared region starts here
     int64_t clear_words;
 };
 
@@ -567,14 +568,22 @@ FusedWs fused_ws(const LinArgs &a, bool backward)
     const int64_t chains = a.B * a.d;
     float *ws = (float *)a.ws;
     FusedWs f;
-    f.lb.carry = (uint64_t *)ws;
-    f.ctrl = (uint32_t *)(ws + 2 * nC * chains);
-    f.dbpart = backward ? ws + 2 * nC * chains + 64 : nullptr;
-    f.lb.ticket = f.ctrl;
-    f.lb.err = f.ctrl + 1;
-    f.clear = (uint32_t *)ws;
-    f.clear_words = 2 * nC * chains + 64;
+    f.ctrl = (uint32_t *)ws;
+    f.lb.err = f.ctrl + kErrWord;
+    f.lb.ticket = f.ctrl + kTicketWord;
+    f.lb.carry = (uint64_t *)(ws + kCtrlWords);
+    f.dbpart = backward ? ws + kCtrlWords + 2 * nC * chains : nullptr;
+    f.clear_words = kCtrlWords + 2 * nC * chains;
     return f;
+}
+
+// Clears the control block and states before direction number `k` of a
+// call (k = 0 first): the error word only before the first.
+void fused_clear(const FusedWs &f, int k, hipStream_t s)
+{
+    const int64_t from = k == 0 ? 0 : kTicketWord;
+    hipLaunchKernelGGL(scan_clear, dim3(scan_clear_blocks(f.clear_words - from)), dim3(256), 0, s,
+                       f.ctrl + from, f.clear_words - from);
 }
 
 bool use_fused(const LinArgs &a)
@@ -595,8 +604,7 @@ hipError_t lin_forward_fused(const LinArgs &a, hipStream_t s)
     const FusedWs f = fused_ws(a, false);
     for (int dl = 0; dl < a.ndir; ++dl) {
         LinGeom g{a.L, a.B, a.d, a.chunk, nC, chains, a.ndir, dl};
-        hipLaunchKernelGGL(scan_clear, dim3(scan_clear_blocks(f.clear_words)), dim3(256), 0, s, f.clear,
-                           f.clear_words);
+        fused_clear(f, dl, s);
         hipLaunchKernelGGL((lin_fwd_fused<TU, TX, kFwdW, kFwdSeg, kFwdPB, kFwdWpe>), dim3((unsigned)(nC * (chains / 64))),
                            dim3(kFwdW * 64), 0, s, g, (const TU *)a.U, (const TX *)a.x, a.b, a.alpha,
                            a.c0, a.h, a.c_seq, a.c_last, f.lb);
@@ -612,8 +620,7 @@ hipError_t lin_backward_fused(const LinArgs &a, hipStream_t s)
     const FusedWs f = fused_ws(a, true);
     for (int dl = a.ndir - 1; dl >= 0; --dl) {
         LinGeom g{a.L, a.B, a.d, a.chunk, nC, chains, a.ndir, dl};
-        hipLaunchKernelGGL(scan_clear, dim3(scan_clear_blocks(f.clear_words)), dim3(256), 0, s, f.clear,
-                           f.clear_words);
+        fused_clear(f, a.ndir - 1 - dl, s);
         hipLaunchKernelGGL((lin_bwd_fused<TU, TX, kBwdW, kBwdSeg, kBwdPB, kBwdWpe>), dim3((unsigned)(nC * (chains / 64))),
                            dim3(kBwdW * 64), 0, s, g, (const TU *)a.U, (const TX *)a.x, a.b, a.alpha,
                            a.c0, a.c_seq, a.dh, a.dc_last, a.dU, a.dx, dl != a.ndir - 1, a.dc0,
@@ -631,8 +638,11 @@ hipError_t lin_forward_t(const LinArgs &a, hipStream_t s)
     if (use_fused(a)) return lin_forward_fused<TU, TX>(a, s);
     const int64_t nC = (a.L + a.chunk - 1) / a.chunk;
     const int64_t chains = a.B * a.d;
-    float *ws = (float *)a.ws;
+    float *ws = (float *)a.ws + kCtrlWords;
     float *A = ws, *E = ws + nC * chains, *cin = ws + 2 * nC * chains;
+    // no look-back on this path: the error word is only cleared
+    hipLaunchKernelGGL(scan_clear, dim3(1), dim3(256), 0, s, (uint32_t *)a.ws + kErrWord,
+                       (int64_t)1);
     for (int dl = 0; dl < a.ndir; ++dl) {
         LinGeom g{a.L, a.B, a.d, a.chunk, nC, chains, a.ndir, dl};
         hipLaunchKernelGGL(lin_fwd_aggregate<TU>, dim3(blocks_for(chains * nC)), dim3(256), 0, s,
@@ -652,9 +662,12 @@ hipError_t lin_backward_t(const LinArgs &a, hipStream_t s)
     if (use_fused(a)) return lin_backward_fused<TU, TX>(a, s);
     const int64_t nC = (a.L + a.chunk - 1) / a.chunk;
     const int64_t chains = a.B * a.d;
-    float *ws = (float *)a.ws;
+    float *ws = (float *)a.ws + kCtrlWords;
     float *A = ws, *G = ws + nC * chains, *gin = ws + 2 * nC * chains;
     float *dbp = ws + 3 * nC * chains;  // [nC, 2, chains]
+    // no look-back on this path: the error word is only cleared
+    hipLaunchKernelGGL(scan_clear, dim3(1), dim3(256), 0, s, (uint32_t *)a.ws + kErrWord,
+                       (int64_t)1);
     for (int dl = a.ndir - 1; dl >= 0; --dl) {
         LinGeom g{a.L, a.B, a.d, a.chunk, nC, chains, a.ndir, dl};
         hipLaunchKernelGGL(lin_bwd_aggregate<TU>, dim3(blocks_for(chains * nC)), dim3(256), 0, s,
@@ -679,9 +692,9 @@ size_t linear_workspace_bytes(int64_t L, int64_t B, int64_t d, int ndir, int64_t
     (void)ndir;  // directions are processed one after another and reuse it
     const int64_t nC = (L + chunk - 1) / chunk;
     const int64_t per = nC * B * d;
-    // three-phase: 3 (fwd) or 5 (bwd) per-chunk arrays; single pass: 64-bit
-    // published states (+ db partials) and 64 control words
-    const int64_t floats = (backward ? 5 * per : 3 * per) + 64;
+    // the control block, then three-phase: 3 (fwd) or 5 (bwd) per-chunk
+    // arrays; single pass: 64-bit published states (+ db partials)
+    const int64_t floats = kCtrlWords + (backward ? 5 * per : 3 * per);
     return (size_t)floats * sizeof(float);
 }
 

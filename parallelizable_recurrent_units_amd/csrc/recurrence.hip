@@ -454,6 +454,7 @@ __global__ __launch_bounds__(256) void bwd_generic(RecArgs a)
 {
     const int64_t chains = a.B * a.d;
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g == 0 && a.err_word) *a.err_word = 0u;   // no look-back here: no error
     if (g >= chains) return;
     const int dl = a.dir;
     const int64_t j = g % a.d;
@@ -549,6 +550,8 @@ __global__ __launch_bounds__(BIDI ? 2 * kWave : kWave) void bwd_fast(RecArgs a)
 
     const int wv = BIDI ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
     const int lane = threadIdx.x & 63;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && a.err_word)
+        *a.err_word = 0u;                            // no look-back here: no error
     uint4 *slot_a = slot_a_all[wv];
     uint4 *slot_b = slot_b_all[wv];
     float *out_slot = out_slot_all[wv];

@@ -155,6 +155,17 @@ def workspace(shape, op, chunk=0, device="cuda"):
     return torch.empty(n, device=device, dtype=torch.uint8)
 
 
+# When True, backward() and the linear scans read their workspace's error
+# word after the call (a synchronising 4-byte read, skipped while a graph is
+# being captured) and raise if a wait between chunks ran out.
+CHECK_SCAN_ERRORS = False
+
+
+def _checked(ws, what):
+    if CHECK_SCAN_ERRORS and not torch.cuda.is_current_stream_capturing():
+        B.check_workspace(ws, what)
+
+
 def backward(shape, U, x, v, b, c0, c_seq, dh, dc_last=None, ws=None, bf16_copy=False,
              stream=None):
     """Returns (dU, dx, dv, db, dc0), plus dU rounded to bf16 when bf16_copy."""
@@ -169,6 +180,7 @@ def backward(shape, U, x, v, b, c0, c_seq, dh, dc_last=None, ws=None, bf16_copy=
     if ws is None:
         ws = workspace(s, B.SRU_WS_BACKWARD, 0, dev)
     B.sru_backward(s, U, x, v, b, c0, c_seq, dh, dc_last, dU, dx, dv, db, dc0, ws, dU_lp, stream)
+    _checked(ws, "sru_backward")
     if bf16_copy:
         return dU, dx, dv, db, dc0, dU_lp
     return dU, dx, dv, db, dc0
@@ -185,6 +197,7 @@ def linear_forward(shape, chunk, U, x, b, c0=None, keep_c_seq=True, ws=None, str
         ws = workspace(s, B.SRU_WS_LINEAR_FWD, chunk, dev)
     B.sru_linear_scan(s, B.SRU_FWD, chunk, U, x, b, c0, h=h, c_seq=c_seq, c_last=c_last,
                       workspace=ws, stream=stream)
+    _checked(ws, "sru_linear_scan forward")
     return h, c_seq, c_last
 
 
@@ -199,4 +212,5 @@ def linear_backward(shape, chunk, U, x, b, c0, c_seq, dh, dc_last=None, ws=None,
         ws = workspace(s, B.SRU_WS_LINEAR_BWD, chunk, dev)
     B.sru_linear_scan(s, B.SRU_BWD, chunk, U, x, b, c0, c_seq=c_seq, dh=dh, dc_last=dc_last,
                       dU=dU, dx=dx, db=db, dc0=dc0, workspace=ws, stream=stream)
+    _checked(ws, "sru_linear_scan backward")
     return dU, dx, db, dc0

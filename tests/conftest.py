@@ -16,3 +16,18 @@ def pytest_configure(config):
 def oracle_mod():
     import oracle
     return oracle
+
+
+@pytest.fixture(autouse=True)
+def _read_scan_error_words(request):
+    """GPU tests: every backward and linear-scan call made through layer.py
+    reads its workspace's error word afterwards and fails if it is set."""
+    if request.node.get_closest_marker("gpu") is None:
+        yield
+        return
+    from parallelizable_recurrent_units_amd import layer
+    layer.CHECK_SCAN_ERRORS = True
+    try:
+        yield
+    finally:
+        layer.CHECK_SCAN_ERRORS = False

@@ -359,3 +359,52 @@ def test_no_device_status_without_gpu(lib):
     s = sru.SruShape(8, 2, 64, 0, 1.0)
     assert fwd(lib, s) == sru.SRU_ERR_NO_DEVICE
     assert b"no HIP device" in lib.sru_last_error()
+
+
+def test_outputs_overlapping_inputs_are_rejected(lib):
+    """An output that overlaps an input or another output is refused before
+    any launch (the kernels read and write them concurrently)."""
+    s = sru.SruShape(8, 2, 64, 1, 1.0)
+    # forward: h on top of U, c_seq on top of h, c_last inside x
+    assert fwd(lib, s, h=P[0]) == sru.SRU_ERR_INVALID_ARG
+    assert b"overlaps" in lib.sru_last_error()
+    assert fwd(lib, s, c_seq=P[4] + 16) == sru.SRU_ERR_INVALID_ARG
+    assert fwd(lib, s, c_last=P[1] + 64) == sru.SRU_ERR_INVALID_ARG
+    need = sru.sru_workspace_size(s, sru.SRU_WS_BACKWARD)
+    assert bwd(lib, s, need, dU=P[6]) == sru.SRU_ERR_INVALID_ARG        # dU on dh
+    assert bwd(lib, s, need, dx=P[7] + 256) == sru.SRU_ERR_INVALID_ARG  # dx inside dU
+    assert bwd(lib, s, need, ws=P[5]) == sru.SRU_ERR_INVALID_ARG        # workspace on c_seq
+    assert bwd(lib, s, need, dv=P[8], db=P[12]) == sru.SRU_ERR_INVALID_ARG   # dv inside dx
+    lneed = sru.sru_workspace_size(s, sru.SRU_WS_LINEAR_BWD, 4)
+    assert lin(lib, s, 1, 4, lneed, dx=P[6]) == sru.SRU_ERR_INVALID_ARG
+    assert lin(lib, s, 0, 4, lneed, h=P[1]) == sru.SRU_ERR_INVALID_ARG
+    # projection: C on top of A, and C inside W
+    assert lib.sru_project(ctypes.byref(s), 0, P[0], 0, P[1], 1, P[0], 0, 0, None) == 1
+    assert b"overlaps" in lib.sru_last_error()
+    assert lib.sru_project(ctypes.byref(s), 1, P[0], 0, P[1], 1, P[1] + 512, 0, 0, None) == 1
+    # disjoint buffers still reach the device check
+    assert lib.sru_project(ctypes.byref(s), 0, P[0], 0, P[1], 1, P[2], 0, 0, None) in (
+        sru.SRU_ERR_NO_DEVICE, sru.SRU_OK)
+
+
+def test_error_word_offset_matches_the_header():
+    """The binding reads the error word where include/sru.h says it is."""
+    text = open(os.path.join(ROOT, "include", "sru.h")).read()
+    m = re.search(r"#define\s+SRU_WS_ERROR_OFFSET\s+(\d+)", text)
+    assert m and int(m.group(1)) == Bd.SRU_WS_ERROR_OFFSET
+
+
+def test_error_word_reader_on_host_bytes():
+    """workspace_error_word / check_workspace read 4 bytes at the offset as a
+    little-endian int32 (exercised on a host tensor: no device needed)."""
+    import torch
+    ws = torch.zeros(1024, dtype=torch.uint8)
+    assert Bd.workspace_error_word(ws) == 0
+    Bd.check_workspace(ws)
+    ws[Bd.SRU_WS_ERROR_OFFSET] = 1
+    assert Bd.workspace_error_word(ws) == 1
+    with pytest.raises(Bd.SruError, match="ran out"):
+        Bd.check_workspace(ws, "test")
+    ws.zero_()
+    ws[Bd.SRU_WS_ERROR_OFFSET + 4] = 7          # the ticket word is not the error word
+    assert Bd.workspace_error_word(ws) == 0
