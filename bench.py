@@ -1,30 +1,36 @@
 """Benchmark of the SRU layer hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--no-extras] [--workload 2]
+                    [--no-extras] [--workload 4]
 
 One step = one pass of the whole hot path over one batch: projection GEMM
 (U = X~ W^T), forward recurrence, backward recurrence with the fused dv/db
 reduction (which also writes dU rounded to bf16), and the backward-data GEMM
 (W transposed once, then dX = bf16(dU) W + highway dx).  The headline
-workload is the bidirectional layer L=64, B=128, d=512 (fp32 activations,
-bf16 W).  Inputs are seeded synthetic draws (no dataset), resident in HBM
-before the timed region; several input/output sets rotate so consecutive steps
-do not reuse cached data.
+workload is the full layer training step L=512, B=32, d=1024 (fp32
+activations, bf16 W), the largest configuration that carries every part of
+the metric.  Inputs are seeded synthetic draws (no dataset), resident in HBM
+before the timed region; several input/output sets rotate so consecutive
+steps do not reuse cached data.
 
-Printed: one JSON line.  ``value`` is the step's algorithmic HBM bytes (every
-tensor of every row counted once at its dtype) divided by the step time, in
-GB/s; per-row times (HIP events recorded on the stream the kernels run on),
-their roofline fractions, the dominant row's roofline object, the CPU oracle
-baseline on a bounded sample, and measurements of the other rows at the other
-workload sizes (given-U bf16 forward, the L=512 training step, the linear-mode
-chunked scan) are included.  ``beyond_step`` times, after the step and on its
-buffers, rows that are not part of the step: the projection's weight gradient
-dW = bf16(dU)^T X~, and the factorised projection U = Wo (Wq X~) with d' = d/4
-(SRU++ paper, Fig. 2(b)), forward and backward; at the given-U workload, the
-SRU++ attention that would produce that U (causal, previous segment as
-context, layer norm); for unidirectional layers, 32 consecutive decoding
-steps (sru_step) at B = 1 and at the layer's B.
+Printed: one JSON line.  ``value`` is the metric's first part, the forward +
+backward recurrence's algorithmic HBM bytes (every tensor of the two rows
+counted once at its dtype) divided by the two rows' event-timed time, in
+GB/s; ``elem_steps_per_s`` is L*B*d*ndir over the same time; the projection
+GEMMs' fraction of the bf16 MFMA peak is ``gemm_frac_of_mfma_peak``.  Also:
+per-row times (HIP events recorded on the stream the kernels run on), their
+roofline fractions, the dominant row's roofline object, the CPU oracle
+baseline on a bounded sample (single-threaded and on every core), and
+measurements at the other workload sizes (the bidirectional L=64 step, the
+given-U bf16 forward, the linear-mode chunked scan).  ``beyond_step`` times,
+after the step and on its buffers, rows that are not part of the step: the
+projection's weight gradient dW = bf16(dU)^T X~, and the factorised
+projection U = Wo (Wq X~) with d' = d/4 (SRU++ paper, Fig. 2(b)), forward and
+backward; at the given-U workload, the SRU++ attention that would produce
+that U (causal, previous segment as context, layer norm); for
+unidirectional layers, 32 consecutive decoding steps (sru_step) at B = 1 and
+at the layer's B.  After every timed region the error word of each scan
+workspace is read; a set word aborts the run before anything is printed.
 """
 import argparse
 import hashlib
@@ -49,7 +55,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5],
+    p.add_argument("--workload", type=int, default=4, choices=[2, 3, 4, 5],
                    help="2, 4: training step; 3: given-U forward; 5: linear mode fwd+bwd")
     p.add_argument("--sets", type=int, default=4, help="rotating input/output sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -96,8 +102,14 @@ def row_work(w):
         rows["a2_forward"] = dict(bytes=fwd)
     if w.backward:
         bwd = (LB * n3 * us + LB * d * xs + 2 * LB * nd * d * 4 + LB * n3 * 4 + LB * d * 4)
+        if w.mode == "layer":
+            bwd += LB * n3 * 2       # the bf16 copy of dU the backward-data GEMM reads
         rows["a7_linear_backward" if w.linear else "a3_a4_backward"] = dict(bytes=bwd)
     return rows
+
+
+GEMM_ROWS = ("a1_projection", "a5_projection_bwd_data")
+RECURRENCE_ROWS = ("a2_forward", "a3_a4_backward", "a6_linear_forward", "a7_linear_backward")
 
 
 def next_row_work(w):
@@ -362,8 +374,19 @@ def attention_rows(w, shape, g):
 
 class RowSet(list):
     """One set's step rows [(row, fn)], plus ``beyond``: rows timed after the
-    step on the same buffers."""
+    step on the same buffers, and ``workspaces``: the scan workspaces whose
+    error words are read after timing."""
     beyond = ()
+    workspaces = ()
+
+
+def check_error_words(sets):
+    """Raise if any scan workspace of ``sets`` has its error word set (a
+    bounded wait between chunks ran out: that call's outputs are invalid)."""
+    from parallelizable_recurrent_units_amd import check_workspace
+    for rs in sets:
+        for name, ws in getattr(rs, "workspaces", ()):
+            check_workspace(ws, name)
 
 
 def row_sets_for(w, nsets, seed0):
@@ -379,6 +402,7 @@ def row_sets_for(w, nsets, seed0):
             shape, t = device_set(w, seed0 + i)
             out.append(RowSet(training_step_rows(shape, t)))
             out[-1].beyond = next_rows(shape, t)
+            out[-1].workspaces = [("sru_backward", t["ws"])]
         return out
     g = torch.Generator(device="cuda")
     g.manual_seed(seed0)
@@ -415,11 +439,14 @@ def row_sets_for(w, nsets, seed0):
                       dtype=torch.uint8)
     wsb = torch.empty(sru_workspace_size(s, SRU_WS_LINEAR_BWD, w.chunk), device="cuda",
                       dtype=torch.uint8)
-    return [[("a6_linear_forward", lambda: sru_linear_scan(s, SRU_FWD, w.chunk, U, x, b, None, h=h,
-                                                           c_seq=c_seq, c_last=cl, workspace=wsf)),
-             ("a7_linear_backward", lambda: sru_linear_scan(s, SRU_BWD, w.chunk, U, x, b, None,
-                                                            c_seq=c_seq, dh=dh, dU=dU, dx=dx,
-                                                            db=dbv, dc0=dc0, workspace=wsb))]]
+    rs = RowSet([("a6_linear_forward", lambda: sru_linear_scan(s, SRU_FWD, w.chunk, U, x, b, None,
+                                                               h=h, c_seq=c_seq, c_last=cl,
+                                                               workspace=wsf)),
+                 ("a7_linear_backward", lambda: sru_linear_scan(s, SRU_BWD, w.chunk, U, x, b, None,
+                                                                c_seq=c_seq, dh=dh, dU=dU, dx=dx,
+                                                                db=dbv, dc0=dc0, workspace=wsb))])
+    rs.workspaces = [("linear scan forward", wsf), ("linear scan backward", wsb)]
+    return [rs]
 
 
 def measure(w, nsets, steps, warmup, seed0):
@@ -427,6 +454,7 @@ def measure(w, nsets, steps, warmup, seed0):
     import torch
     sets = row_sets_for(w, nsets, seed0)
     ms, rows = time_rows(sets, steps, warmup)
+    check_error_words(sets)
     work = row_work(w)
     per_row = {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
     beyond = time_beyond(w, sets, steps, warmup)
@@ -454,7 +482,7 @@ def time_beyond(w, sets, steps, warmup):
     return out
 
 
-def extras(main_id, steps):
+def extras(main_id, steps, cpu_s=0.0):
     """Rows at the other workload sizes, each workload timed on its own."""
     from parallelizable_recurrent_units_amd.workloads import WORKLOADS
     out = {}
@@ -466,42 +494,90 @@ def extras(main_id, steps):
         ms, per_row = measure(w, 1 if linear else 4, max(3, steps // 5) if linear else steps,
                               2 if linear else 3, 40 + 10 * wid)
         out[w.name] = dict(per_row, ms_per_step=ms)
+        if cpu_s > 0:
+            print(f"[bench] CPU oracle baseline, {w.name}", file=sys.stderr, flush=True)
+            out[w.name]["cpu_baseline"] = cpu_baseline(w, cpu_s)
     return out
 
 
-def cpu_baseline(w, budget_s=10.0):
-    """The CPU oracle (as written) on a bounded sample of the same training
-    step: batch rows in order, repeating the whole batch if it finishes early,
-    until about ``budget_s`` seconds of work."""
+CPU_BLOCK = 512   # channels per CPU-sample unit of the given-U workloads
+
+
+def cpu_baseline_run(w, budget_s, threads):
+    """The CPU oracle (as written, double precision) on a bounded sample of
+    workload ``w``: units of one batch row (and, where U is given rather than
+    projected, CPU_BLOCK channels), drawn with the workload's distributions,
+    run through the same rows as the GPU step, repeated until about
+    ``budget_s`` seconds.  Each row is timed on its own, so the recurrence
+    rate (the metric's first part) and the whole step's are both reported,
+    scaled by the fraction of the workload the sample covered."""
+    import dataclasses
     import numpy as np
     import oracle
     from parallelizable_recurrent_units_amd.workloads import make_inputs
-    inp = make_inputs(w, seed=2)
-    L, B, d, nd = w.L, w.B, w.d, w.ndir
-    X2 = inp["x"].reshape(L * B, d)
-    t0 = time.perf_counter()
+    oracle.set_num_threads(threads)
+    dd = w.d if w.mode == "layer" else min(w.d, CPU_BLOCK)
+    unit = dataclasses.replace(w, B=1, d=dd)
+    inp = make_inputs(unit, seed=2)
+    L, nd = w.L, w.ndir
+    frac_unit = dd / (w.B * w.d)
+    times = {}
+
+    def timed(row, fn):
+        t0 = time.perf_counter()
+        r = fn()
+        times[row] = times.get(row, 0.0) + time.perf_counter() - t0
+        return r
+
+    t_start = time.perf_counter()
     done = 0
     while True:
-        b = done % B
-        rows = np.arange(L) * B + b
-        U = oracle.project(X2, inp["W"], True, rows=rows).reshape(L, 1, nd, 3, d)
-        sl = lambda a: np.ascontiguousarray(a[:, b:b + 1])
-        fo = oracle.forward(U, sl(inp["x"]), inp["v"], inp["b"], sl(inp["c0"]), w.alpha)
-        bo = oracle.backward(U, sl(inp["x"]), inp["v"], inp["b"], sl(inp["c0"]), fo["c"],
-                             sl(inp["dh"]), sl(inp["dc_last"]), w.alpha)
-        oracle.project_bwd_data(bo["dU"].reshape(L, -1), inp["W"])
+        if w.mode == "layer":
+            U = timed("a1_projection", lambda: oracle.project(
+                inp["x"].reshape(L, dd), inp["W"], True)).reshape(L, 1, nd, 3, dd)
+        else:
+            U = inp["U"]
+        fwd_row = "a6_linear_forward" if w.linear else "a2_forward"
+        fo = timed(fwd_row, lambda: oracle.forward(U, inp["x"], inp["v"], inp["b"], inp["c0"],
+                                                   w.alpha))
+        if w.backward:
+            bwd_row = "a7_linear_backward" if w.linear else "a3_a4_backward"
+            bo = timed(bwd_row, lambda: oracle.backward(U, inp["x"], inp["v"], inp["b"], inp["c0"],
+                                                        fo["c"], inp["dh"], inp["dc_last"],
+                                                        w.alpha))
+            if w.mode == "layer":
+                timed("a5_projection_bwd_data",
+                      lambda: oracle.project_bwd_data(bo["dU"].reshape(L, -1), inp["W"]))
         done += 1
-        if time.perf_counter() - t0 > budget_s:
+        if time.perf_counter() - t_start > budget_s:
             break
-    secs = time.perf_counter() - t0
-    step_bytes = sum(r["bytes"] for r in row_work(w).values())
-    frac = done / B
-    return {"value": step_bytes * frac / secs / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+    frac = done * frac_unit
+    work = row_work(w)
+    rec = [n for n in times if n in RECURRENCE_ROWS]
+    rec_bytes = sum(work[n]["bytes"] for n in rec) * frac
+    rec_s = sum(times[n] for n in rec)
+    step_s = sum(times.values())
+    what = ("batch rows" if w.mode == "layer" else f"(batch row, {dd}-channel block) units")
+    return {"value": rec_bytes / rec_s / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "elem_steps_per_s": w.elem_steps * frac / secs,
-            "sample": f"{done} batch rows ({frac:.2f} passes over the {B} rows) of the same "
-                      f"training step (projection, forward, backward, dX) in double precision, "
-                      f"{secs:.1f} s; algorithmic bytes scaled by {frac:.4f}"}
+            "elem_steps_per_s": w.elem_steps * frac / rec_s,
+            "step_GB_per_s": sum(r["bytes"] for r in work.values()) * frac / step_s / 1e9,
+            "step_ms_extrapolated": step_s / frac * 1e3,
+            "row_seconds": times,
+            "sample": f"{done} {what} = {frac:.4f} of the workload, rows {sorted(times)} in "
+                      f"double precision, {step_s:.1f} s; algorithmic bytes and element-steps "
+                      f"scaled by {frac:.4f}; value = the recurrence rows' bytes over their time"}
+
+
+def cpu_baseline(w, budget_s=10.0):
+    """The oracle on every host core (OpenMP over chains and GEMM rows), with
+    the same sample single-threaded beside it."""
+    import oracle
+    every = oracle.num_threads()
+    out = cpu_baseline_run(w, budget_s, every)
+    out["single_thread"] = cpu_baseline_run(w, budget_s, 1)
+    oracle.set_num_threads(every)
+    return out
 
 
 # kernel launches of one call of each row (what its event-timed span covers)
@@ -540,8 +616,7 @@ ROW_KERNELS = {
     "a2_forward": ([r"fwd_fast<"], r"fwd_fast<"),
     "a3_a4_backward": ([r"bwd_scan<", r"bwd_fast<", r"scan_clear", r"param_reduce"],
                        r"param_reduce"),
-    "a5_projection_bwd_data": ([r"transpose16", r"gemm_lds<.*LdsCfg<128, 128, 4, 2, 4, 1>"],
-                               r"transpose16"),
+    "a5_projection_bwd_data": ([r"transpose16", r"gemm_lds<"], r"transpose16"),
 }
 
 
@@ -565,8 +640,9 @@ def _per_dispatch(run_dir, counter):
     return per
 
 
-def write_traffic(fetch_dir, write_dir, copy_bytes):
-    """profiles/traffic.json: HBM bytes per call of each row.  FETCH_SIZE and
+def write_traffic(workload, fetch_dir, write_dir, copy_bytes):
+    """profiles/traffic.json, entry ``workload``: HBM bytes per call of each
+    row at that workload (entries of other workloads are kept).  FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch) are each scaled by the factor that makes the
     calibration copy (the largest torch copy kernel of the run, which moves
     ``copy_bytes`` in and out) read and write exactly its size."""
@@ -594,42 +670,24 @@ def write_traffic(fetch_dir, write_dir, copy_bytes):
            "rows": {k: v["bytes"] for k, v in rows.items() if "bytes" in v},
            "detail": rows}
     path = os.path.join(ROOT, "profiles", "traffic.json")
+    allrec = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            allrec = json.load(f)
+    allrec = {"workloads": dict(allrec.get("workloads", {}), **{workload: rec})}
     with open(path, "w") as f:
-        json.dump(rec, f, indent=1)
+        json.dump(allrec, f, indent=1)
     print(json.dumps(rec, indent=1))
 
 
-def copy_ceiling(gib=2, reps=10):
-    """HBM bandwidth of a plain device copy (torch copy_, read + write), the
-    practical ceiling the recurrence rows are compared with (context only;
-    the roofline fractions use the published peak)."""
-    import torch
-    n = int(gib * (1 << 30)) // 4
-    src = torch.ones(n, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(2):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    secs = e0.elapsed_time(e1) / 1e3 / reps
-    del src, dst
-    torch.cuda.empty_cache()
-    return {"GB/s": 2 * n * 4 / secs / 1e9, "kind": f"torch device copy of {gib} GiB (read + write)"}
-
-
-def traffic_for(kernel_row, digest):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel sources."""
+def traffic_for(workload, kernel_row, digest):
+    """HBM bytes per call of a row from the committed counter summary, if it
+    was taken at this workload on the current kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f)
+        rec = json.load(f).get("workloads", {}).get(workload, {})
     if rec.get("source_digest") != digest:
         return None
     return rec.get("rows", {}).get(kernel_row)
@@ -640,7 +698,9 @@ def main():
     if args.write_traffic:
         if not args.copy_probe_mib:
             raise SystemExit("--write-traffic needs the --copy-probe-mib the runs used")
-        write_traffic(*args.write_traffic, copy_bytes=args.copy_probe_mib * (1 << 20))
+        from parallelizable_recurrent_units_amd.workloads import WORKLOADS
+        write_traffic(WORKLOADS[args.workload].name, *args.write_traffic,
+                      copy_bytes=args.copy_probe_mib * (1 << 20))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the "
@@ -658,6 +718,7 @@ def main():
     row_sets = row_sets_for(w, nsets, 100)
     print("[bench] timing", file=sys.stderr, flush=True)
     ms, rows = time_rows(row_sets, args.steps, args.warmup)
+    check_error_words(row_sets)
     beyond = {} if args.no_beyond else time_beyond(w, row_sets, args.steps, args.warmup)
     del row_sets
     torch.cuda.empty_cache()
@@ -668,11 +729,16 @@ def main():
     roof = dict(roofline_of(dominant, work[dominant], rows[dominant]))
     roof["kernel"] = dominant
     roof["launches_per_call"] = ROW_LAUNCHES.get(dominant)
-    roof["traffic"] = traffic_for(dominant, digest)
+    roof["traffic"] = traffic_for(w.name, dominant, digest)
     step_bytes = sum(r["bytes"] for r in work.values())
+    rec_rows = [n for n in per_row if n in RECURRENCE_ROWS]
+    rec_bytes = sum(work[n]["bytes"] for n in rec_rows)
+    rec_s = sum(rows[n] for n in rec_rows)
     line = {
         "metric": METRIC,
-        "value": step_bytes / (ms / 1e3) / 1e9,
+        "value": rec_bytes / rec_s / 1e9,
+        "value_is": "the forward + backward recurrence rows' algorithmic bytes over their "
+                    "event-timed time (" + " + ".join(rec_rows) + ")",
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -688,7 +754,11 @@ def main():
         "config": {"workload": w.name, "L": w.L, "B": w.B, "d": w.d,
                    "bidirectional": w.ndir == 2, "alpha": w.alpha,
                    "x": w.x_dtype, "W": w.w_dtype, "parallelism": "single GPU"},
-        "elem_steps_per_s": w.elem_steps / (ms / 1e3),
+        "elem_steps_per_s": w.elem_steps / rec_s,
+        "frac_of_hbm_peak": rec_bytes / rec_s / 1e9 / HBM_PEAK_GBS,
+        "gemm_frac_of_mfma_peak": {n: per_row[n]["frac"] for n in GEMM_ROWS if n in per_row},
+        "step_GB_per_s": step_bytes / (ms / 1e3) / 1e9,
+        "step_elem_steps_per_s": w.elem_steps / (ms / 1e3),
         "step_algorithmic_bytes": step_bytes,
         "rows": per_row,
         "beyond_step": beyond,
@@ -703,30 +773,11 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         line["copy_probe_bytes"] = n * 4
-    # the metric's two parts: the recurrence (forward + backward rows) in GB/s
-    # and element-steps/s, and the projection GEMMs against their roofline
-    rec_rows = [n for n in per_row if n in ("a2_forward", "a3_a4_backward",
-                                            "a6_linear_forward", "a7_linear_backward")]
-    if rec_rows:
-        rb = sum(work[n]["bytes"] for n in rec_rows)
-        rt = sum(rows[n] for n in rec_rows)
-        line["recurrence_fwd_bwd"] = {"GB/s": rb / rt / 1e9, "frac_of_hbm_peak": rb / rt / 1e9 / HBM_PEAK_GBS,
-                                      "elem_steps_per_s": w.elem_steps / rt, "rows": rec_rows}
-    # counter runs (--copy-probe-mib) skip the ceiling: its 2 GiB copies would
-    # be taken for the calibration copy
-    ceil = None if args.copy_probe_mib else copy_ceiling()
-    line["copy_ceiling"] = ceil
-    for r in per_row.values():
-        if ceil and r["unit"] == "GB/s":
-            r["frac_of_copy_ceiling"] = r["achieved"] / ceil["GB/s"]
     if not args.no_extras:
         print("[bench] other workloads", file=sys.stderr, flush=True)
-        line["other_workloads"] = extras(args.workload, max(10, args.steps // 2))
-        for rows_w in line["other_workloads"].values():
-            for r in rows_w.values():
-                if ceil and isinstance(r, dict) and r.get("unit") == "GB/s":
-                    r["frac_of_copy_ceiling"] = r["achieved"] / ceil["GB/s"]
-    if not args.no_cpu_baseline and w.mode == "layer":
+        line["other_workloads"] = extras(args.workload, max(10, args.steps // 2),
+                                         0.0 if args.no_cpu_baseline else 3.0)
+    if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

@@ -120,6 +120,14 @@ def _optf32(a):
     return _f32(a)
 
 
+def set_num_threads(n: int) -> None:
+    """Threads the whole-tensor routines use from now on (1: single-threaded)."""
+    lib = _load()
+    lib.sru_oracle_set_num_threads.restype = None
+    lib.sru_oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.sru_oracle_set_num_threads(int(n))
+
+
 def num_threads() -> int:
     """Threads the oracle's whole-tensor routines spread independent chains over."""
     return int(_load().sru_oracle_num_threads())

@@ -516,6 +516,17 @@ void sru_oracle_backward(int64_t L, int64_t B, int64_t d, int ndir, double alpha
     free(dxd);
 }
 
+/* Sets the number of threads the routines above use from now on (n >= 1);
+   the baseline timing runs them single-threaded and on every core. */
+void sru_oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n < 1 ? 1 : n);
+#else
+    (void)n;
+#endif
+}
+
 /* Number of threads the OpenMP runtime would use for the routines above. */
 int sru_oracle_num_threads(void)
 {

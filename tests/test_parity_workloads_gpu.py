@@ -7,10 +7,13 @@ the benchmark times.
   sampled rows of the weight gradient dW.
 * workload 3 (given bf16 U, L=1024 B=16 d=2048): 48 sampled chains.
 * workload 4 (training step, L=512 B=32 d=1024): every chain of 3 sampled
-  batch rows, plus size-independent properties for dv and db, and sampled
-  rows of dW (each needs the oracle's dU of every batch row for its column).
-* workload 5 (linear mode, L=16384 B=4 d=4096, chunk 256): 24 sampled chains,
-  plus size-independent properties for db.
+  batch rows; dv and db of 16 sampled channels against the oracle run on all
+  32 batch rows of each, plus size-independent properties for all of dv and
+  db; sampled rows of dW (each needs the oracle's dU of every batch row for
+  its column).
+* workload 5 (linear mode, L=16384 B=4 d=4096, chunk 256): 24 sampled chains;
+  db of 16 sampled channels against the oracle on all 4 batch rows, plus
+  size-independent properties for all of db.
 * beyond 2 GiB per tensor (L=4096 B=16 d=4096, fp32 U of 3.2 GB): the forward
   and backward on their large-tensor paths, 6 sampled chains.
 Tolerances are explained in test_parity_gpu.py.
@@ -106,6 +109,35 @@ def oracle_rows(w, inp, bs, round_x):
     return res
 
 
+def param_grad_channels(w, seed, n_random):
+    """Channels whose dv, db are compared with the oracle: both edges of the
+    first and last 64-channel tile, plus random ones."""
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 63, 64, w.d - 1], rng.integers(0, w.d, n_random)]))
+
+
+def oracle_param_grads(w, U, inp, js, linear=False):
+    """The oracle's dv, db [2, len(js)] of direction 0 for channels ``js``:
+    every batch row's chain run forward and backward (U [L, B, 3, len(js)]
+    holds those channels' gate inputs), its per-chain sums over t added over
+    b.  ``linear``: v = 0 (the linear mode has no dv)."""
+    dv = np.zeros((2, js.size))
+    db = np.zeros((2, js.size))
+    for k, j in enumerate(js):
+        vf, vr = (0.0, 0.0) if linear else (inp["v"][0, 0, j], inp["v"][0, 1, j])
+        bf, br = inp["b"][0, 0, j], inp["b"][0, 1, j]
+        for b in range(w.B):
+            uf, ur, ux = U[:, b, 0, k], U[:, b, 1, k], U[:, b, 2, k]
+            x = inp["x"][:, b, j]
+            c0 = float(inp["c0"][0, b, j])
+            _, c, _ = oracle.chain_forward(uf, ur, ux, x, vf, vr, bf, br, c0, w.alpha)
+            g = oracle.chain_backward(uf, ur, ux, x, vf, vr, bf, br, c0, c, inp["dh"][:, b, 0, j],
+                                      float(inp["dc_last"][0, b, j]), w.alpha)
+            dv[:, k] += (g["dvf"], g["dvr"])
+            db[:, k] += (g["dbf"], g["dbr"])
+    return dv, db
+
+
 def test_workload2_full():
     import torch
     w = workloads.WORKLOADS[2]
@@ -190,6 +222,27 @@ def test_workload4_sampled_rows_and_properties():
         Gs = oracle_dU_columns(w, inp, rows, round_x)
         check(f"dW ({rows.size} sampled rows, round_x={round_x})", host(g["dW"])[rows],
               oracle.project_bwd_weight(Gs, X2, round_x), tol)
+    # dv, db against the oracle: for sampled channels, every batch row's chain
+    # (the chunked backward's per-(chunk, row) partial sums and their fixed-order
+    # reduction over all 8 chunks x 32 rows).  Fed the kernel's own U, the
+    # recurrence bar applies; fed the oracle's projection from unrounded X,
+    # the bf16 bar.
+    js = param_grad_channels(w, 45, 12)
+    jt = torch.from_numpy(js).cuda()
+    Ug = host(g["U"][:, :, 0][..., jt])                  # [L, B, 3, len(js)]
+    dvo, dbo = oracle_param_grads(w, Ug, inp, js)
+    check(f"dv ({js.size} channels, all {w.B} rows, kernel's U)", host(g["dv"][0][:, jt]), dvo,
+          TIGHT)
+    check(f"db ({js.size} channels, all {w.B} rows, kernel's U)", host(g["db"][0][:, jt]), dbo,
+          TIGHT)
+    Uo = np.empty_like(Ug)
+    for k, j in enumerate(js):
+        for b in range(w.B):
+            Uo[:, b, :, k] = np.stack(oracle.chain_inputs_from_projection(
+                inp["x"], inp["W"], False, w.L, w.B, w.d, 1, 0, b, int(j)), axis=1)
+    dvo, dbo = oracle_param_grads(w, Uo, inp, js)
+    check(f"dv ({js.size} channels, fp32-X oracle)", host(g["dv"][0][:, jt]), dvo, BF16_BAR)
+    check(f"db ({js.size} channels, fp32-X oracle)", host(g["db"][0][:, jt]), dbo, BF16_BAR)
     # dv, db: exact sums of the per-step terms the kernel produced
     dU = g["dU"].double()
     c_seq = g["c_seq"].double()
@@ -244,6 +297,13 @@ def test_workload5_linear_sampled_chains():
         out["dc0"].append(host(dc0[0, b, j:j + 1]))
     for k in out:
         check(f"{k} (24 chains)", np.array(out[k]), np.array(ref[k]), TIGHT, errs)
+    # db against the oracle for sampled channels over all 4 batch rows (the
+    # fused backward's per-(chunk, chain) partials over 64 chunks, then
+    # lin_db_reduce)
+    js = param_grad_channels(w, 56, 12)
+    _, dbo = oracle_param_grads(w, U[:, :, 0][..., js], inp, js, linear=True)
+    check(f"db ({js.size} channels, all {w.B} rows)", host(db[0][:, torch.from_numpy(js).cuda()]),
+          dbo, TIGHT)
     n = w.L * w.B
     for gate, name in ((0, "f"), (1, "r")):
         dz = dU[:, :, 0, gate, :].double()
