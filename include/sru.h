@@ -303,6 +303,37 @@ sru_status sru_backward(const sru_shape *shape,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * sru_backward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight training loops, harnesses that forbid hipMalloc):
+ * the same computation, kernels and results (bit for bit) as sru_backward,
+ * with its scratch in a static device array of the library instead of a
+ * caller workspace.
+ *   The array holds SRU_BACKWARD_STATIC_SCRATCH_BYTES (16 MiB) per GPU; it
+ *   is created the first time the library's code runs on that GPU and kept
+ *   until the process ends.  Shapes whose sru_workspace_size(shape,
+ *   SRU_WS_BACKWARD, 0) exceeds it are rejected with SRU_ERR_WORKSPACE
+ *   (e.g. L = 512, B = 32, d = 1024 needs 6.3 MB and fits).
+ *   Every call on one GPU uses that GPU's one array: calls that overlap in
+ *   time on one GPU (other streams, other threads) race and give undefined
+ *   results; calls ordered on one stream are safe.  Each call clears what it
+ *   needs; nothing carries over between calls.
+ *   error_word: device pointer to a 32-bit word (4-byte aligned) or NULL.
+ *   When given, it is cleared by the call and set nonzero if a bounded wait
+ *   between chunks ran out (then the outputs are invalid), as the error word
+ *   of sru_backward's workspace is.
+ *   Nothing here calls hipMalloc or hipFree; all other arguments are those of
+ *   sru_backward.
+ */
+#define SRU_BACKWARD_STATIC_SCRATCH_BYTES (16u << 20)
+sru_status sru_backward_static(const sru_shape *shape,
+                               const void *U, sru_dtype u_dt,
+                               const void *x, sru_dtype x_dt,
+                               const float *v, const float *b, const float *c0,
+                               const float *c_seq, const float *dh, const float *dc_last,
+                               float *dU, void *dU_lp, float *dx, float *dv, float *db,
+                               float *dc0, uint32_t *error_word, void *stream);
+
+/*
  * Linear mode (v = v' = 0): f and r depend on U only, so c[t] =
  * a[t] c[t-1] + (1 - a[t]) U[t,2] is a first-order linear recurrence and is
  * evaluated as a scan over time chunks of `chunk` steps (per chunk: local scan

@@ -18,4 +18,5 @@ from ._binding import (  # noqa: F401
     SRU_WS_LINEAR_FWD,
     SruError, SruShape, load_library, sru_backward, sru_forward, sru_linear_scan, sru_project,
     sru_project_bwd_weight, sru_transpose_weight, sru_workspace_size,
-    SRU_WS_ERROR_OFFSET, workspace_error_word, check_workspace)
+    SRU_WS_ERROR_OFFSET, workspace_error_word, check_workspace,
+    SRU_BACKWARD_STATIC_SCRATCH_BYTES, sru_backward_static)

@@ -27,7 +27,8 @@ SRU_FACT_WGRAD_Q, SRU_FACT_WGRAD_O = 0, 1
 # Every symbol include/sru.h declares.
 EXPORTED = ("sru_project", "sru_project_bwd_weight", "sru_project_factored",
             "sru_project_factored_bwd_weight", "sru_attention_forward",
-            "sru_attention_workspace_size", "sru_step", "sru_forward", "sru_backward", "sru_linear_scan",
+            "sru_attention_workspace_size", "sru_step", "sru_forward", "sru_backward",
+            "sru_backward_static", "sru_linear_scan",
             "sru_transpose_weight", "sru_round_bf16", "sru_workspace_size", "sru_status_string",
             "sru_last_error")
 
@@ -110,6 +111,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sru_backward.restype = ctypes.c_int
     lib.sru_backward.argtypes = [sp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp]
+    lib.sru_backward_static.restype = ctypes.c_int
+    lib.sru_backward_static.argtypes = [sp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp,
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.sru_linear_scan.restype = ctypes.c_int
     lib.sru_linear_scan.argtypes = [sp, ctypes.c_int, i32, _vp, ctypes.c_int, _vp, ctypes.c_int,
                                     _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -287,6 +291,26 @@ def sru_backward(shape, U, x, v, b, c0, c_seq, dh, dc_last, dU, dx, dv, db, dc0,
                                        _ptr(dh), _ptr(dc_last), _ptr(dU), _ptr(dU_lp), _ptr(dx),
                                        _ptr(dv), _ptr(db), _ptr(dc0), _ptr(workspace), ws_bytes,
                                        _stream(stream)))
+
+
+# Bytes of the static scratch sru_backward_static uses on each GPU
+# (SRU_BACKWARD_STATIC_SCRATCH_BYTES in include/sru.h).
+SRU_BACKWARD_STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def sru_backward_static(shape, U, x, v, b, c0, c_seq, dh, dc_last, dU, dx, dv, db, dc0,
+                        dU_lp=None, error_word=None, stream=None):
+    """sru_backward with the library's static scratch (no workspace argument);
+    ``error_word``: an optional int32 device tensor of one element."""
+    s = _shape(shape)
+    _need_f32(v=v, b=b, c0=c0, c_seq=c_seq, dh=dh, dc_last=dc_last, dU=dU, dx=dx, dv=dv, db=db,
+              dc0=dc0)
+    if dU_lp is not None and _dtype_code(dU_lp) != SRU_BF16:
+        raise TypeError("dU_lp must be bfloat16")
+    _check(load_library().sru_backward_static(
+        ctypes.byref(s), _ptr(U), _dtype_code(U), _ptr(x), _dtype_code(x), _ptr(v), _ptr(b),
+        _ptr(c0), _ptr(c_seq), _ptr(dh), _ptr(dc_last), _ptr(dU), _ptr(dU_lp), _ptr(dx), _ptr(dv),
+        _ptr(db), _ptr(dc0), _ptr(error_word), _stream(stream)))
 
 
 def sru_linear_scan(shape, pass_: int, chunk: int, U, x, b, c0, h=None, c_seq=None,

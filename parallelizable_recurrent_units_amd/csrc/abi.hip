@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/sru.h"
 #include "internal.h"
 
@@ -616,79 +618,94 @@ sru_status sru_forward(const sru_shape *shape, const void *U, sru_dtype u_dt, co
     return launched(sru::launch_forward(a, (hipStream_t)stream), "forward recurrence");
 }
 
-sru_status sru_backward(const sru_shape *shape, const void *U, sru_dtype u_dt, const void *x,
-                        sru_dtype x_dt, const float *v, const float *b, const float *c0,
-                        const float *c_seq, const float *dh, const float *dc_last, float *dU,
-                        void *dU_lp, float *dx, float *dv, float *db, float *dc0, void *workspace,
-                        size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// The arguments of sru_backward and sru_backward_static, the workspace aside.
+struct BwdCall {
+    const sru_shape *shape;
+    const void *U;
+    sru_dtype u_dt;
+    const void *x;
+    sru_dtype x_dt;
+    const float *v, *b, *c0, *c_seq, *dh, *dc_last;
+    float *dU;
+    void *dU_lp;
+    float *dx, *dv, *db, *dc0;
+};
+
+// Validates everything but the workspace; *ws_need = the workspace bytes.
+sru_status check_backward(const BwdCall &c, Dims *dm, size_t *ws_need, const void *workspace)
 {
-    Dims dm;
-    SRU_TRY(check_shape(shape, &dm));
-    if (!valid_dtype(u_dt) || !valid_dtype(x_dt))
+    SRU_TRY(check_shape(c.shape, dm));
+    if (!valid_dtype(c.u_dt) || !valid_dtype(c.x_dt))
         return fail(SRU_ERR_INVALID_ARG, "unknown dtype");
-    SRU_TRY(need_ptr(U, "U"));
-    SRU_TRY(need_ptr(x, "x"));
-    SRU_TRY(need_ptr(v, "v"));
-    SRU_TRY(need_ptr(b, "b"));
-    SRU_TRY(opt_ptr(c0, "c0"));
-    SRU_TRY(need_ptr(c_seq, "c_seq"));
-    SRU_TRY(need_ptr(dh, "dh"));
-    SRU_TRY(opt_ptr(dc_last, "dc_last"));
-    SRU_TRY(need_ptr(dU, "dU"));
-    SRU_TRY(opt_ptr(dU_lp, "dU_lp"));
-    SRU_TRY(need_ptr(dx, "dx"));
-    SRU_TRY(opt_ptr(dv, "dv"));
-    SRU_TRY(opt_ptr(db, "db"));
-    SRU_TRY(opt_ptr(dc0, "dc0"));
-    const size_t need = backward_ws(shape, dm);
-    if (!workspace || workspace_bytes < need)
-        return fail(SRU_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need,
-                    workspace_bytes, workspace ? "" : ", NULL");
-    SRU_TRY(opt_ptr(workspace, "workspace"));
-    {
-        const size_t lbd = (size_t)(dm.LB * shape->d), hs = lbd * dm.ndir * 4;
-        const size_t cs = (size_t)dm.chains * 4, ps = (size_t)(dm.ndir * 2 * shape->d) * 4;
-        const size_t ue = (size_t)dm.u_elems;
-        const Span out[] = {{dU, ue * 4, "dU"}, {dU_lp, ue * 2, "dU_lp"}, {dx, lbd * 4, "dx"},
-                            {dv, ps, "dv"}, {db, ps, "db"}, {dc0, cs, "dc0"},
-                            {workspace, need, "workspace"}};
-        const Span in[] = {{U, ue * elem_bytes(u_dt), "U"}, {x, lbd * elem_bytes(x_dt), "x"},
-                           {v, ps, "v"}, {b, ps, "b"}, {c0, cs, "c0"}, {c_seq, hs, "c_seq"},
-                           {dh, hs, "dh"}, {dc_last, cs, "dc_last"}};
-        SRU_TRY(no_overlap(out, 7, in, 8));
-    }
-    SRU_TRY(need_device());
+    SRU_TRY(need_ptr(c.U, "U"));
+    SRU_TRY(need_ptr(c.x, "x"));
+    SRU_TRY(need_ptr(c.v, "v"));
+    SRU_TRY(need_ptr(c.b, "b"));
+    SRU_TRY(opt_ptr(c.c0, "c0"));
+    SRU_TRY(need_ptr(c.c_seq, "c_seq"));
+    SRU_TRY(need_ptr(c.dh, "dh"));
+    SRU_TRY(opt_ptr(c.dc_last, "dc_last"));
+    SRU_TRY(need_ptr(c.dU, "dU"));
+    SRU_TRY(opt_ptr(c.dU_lp, "dU_lp"));
+    SRU_TRY(need_ptr(c.dx, "dx"));
+    SRU_TRY(opt_ptr(c.dv, "dv"));
+    SRU_TRY(opt_ptr(c.db, "db"));
+    SRU_TRY(opt_ptr(c.dc0, "dc0"));
+    *ws_need = backward_ws(c.shape, *dm);
+    const size_t lbd = (size_t)(dm->LB * c.shape->d), hs = lbd * dm->ndir * 4;
+    const size_t cs = (size_t)dm->chains * 4, ps = (size_t)(dm->ndir * 2 * c.shape->d) * 4;
+    const size_t ue = (size_t)dm->u_elems;
+    const Span out[] = {{c.dU, ue * 4, "dU"},       {c.dU_lp, ue * 2, "dU_lp"},
+                        {c.dx, lbd * 4, "dx"},      {c.dv, ps, "dv"},
+                        {c.db, ps, "db"},           {c.dc0, cs, "dc0"},
+                        {workspace, *ws_need, "workspace"}};
+    const Span in[] = {{c.U, ue * elem_bytes(c.u_dt), "U"}, {c.x, lbd * elem_bytes(c.x_dt), "x"},
+                       {c.v, ps, "v"},     {c.b, ps, "b"},   {c.c0, cs, "c0"},
+                       {c.c_seq, hs, "c_seq"}, {c.dh, hs, "dh"}, {c.dc_last, cs, "dc_last"}};
+    return no_overlap(out, 7, in, 8);
+}
+
+// Launches a validated backward.  ws: backward_ws bytes of scratch whose
+// first 256 bytes are the control block; err: the call's error word (in that
+// block, or elsewhere).
+sru_status run_backward(const BwdCall &c, const Dims &dm, void *ws, uint32_t *err,
+                        hipStream_t s)
+{
+    const sru_shape *shape = c.shape;
     sru::RecArgs a{};
     a.L = shape->L;
     a.B = shape->B;
     a.d = shape->d;
     a.ndir = dm.ndir;
     a.alpha = shape->alpha;
-    a.U = U;
-    a.u_bf16 = u_dt == SRU_BF16;
-    a.x = x;
-    a.x_bf16 = x_dt == SRU_BF16;
-    a.v = v;
-    a.b = b;
-    a.c0 = c0;
-    a.c_seq_in = c_seq;
-    a.dh = dh;
-    a.dc_last = dc_last;
-    a.dU = dU;
-    a.dU_lp = (sru::bf16_bits_t *)dU_lp;
-    a.dx = dx;
-    a.dc0 = dc0;
+    a.U = c.U;
+    a.u_bf16 = c.u_dt == SRU_BF16;
+    a.x = c.x;
+    a.x_bf16 = c.x_dt == SRU_BF16;
+    a.v = c.v;
+    a.b = c.b;
+    a.c0 = c.c0;
+    a.c_seq_in = c.c_seq;
+    a.dh = c.dh;
+    a.dc_last = c.dc_last;
+    a.dU = c.dU;
+    a.dU_lp = (sru::bf16_bits_t *)c.dU_lp;
+    a.dx = c.dx;
+    a.dc0 = c.dc0;
     // the per-chain kernels' partial sums follow the control block; they
-    // clear its error word themselves (they have no look-back)
-    a.partials = (float *)workspace + sru::kCtrlWords;
-    a.err_word = (uint32_t *)workspace + sru::kErrWord;
-    hipStream_t s = (hipStream_t)stream;
+    // clear the error word themselves (they have no look-back)
+    a.partials = (float *)ws + sru::kCtrlWords;
+    a.err_word = err;
     if (sru::backward_scan_ok(a.L, a.B, a.d, a.ndir, !a.u_bf16 && !a.x_bf16))
-        return launched(sru::launch_backward_scan(a, workspace, dv, db, s), "backward scan");
+        return launched(sru::launch_backward_scan(a, ws, c.dv, c.db, s), "backward scan");
     if (sru::backward_bidi_ok(a)) {
         hipError_t e = sru::launch_backward_bidi(a, s);
-        if (e == hipSuccess && (dv || db))
-            e = sru::launch_param_reduce(a.partials, shape->B, shape->d, dm.ndir, dv, db, s);
+        if (e == hipSuccess && (c.dv || c.db))
+            e = sru::launch_param_reduce(a.partials, shape->B, shape->d, dm.ndir, c.dv, c.db, s);
         return launched(e, "backward recurrence");
     }
     // The highway gradient of x sums both directions: the last direction
@@ -699,11 +716,113 @@ sru_status sru_backward(const sru_shape *shape, const void *U, sru_dtype u_dt, c
         hipError_t e = sru::launch_backward_dir(a, s);
         if (e != hipSuccess) return launched(e, "backward recurrence");
     }
-    if (dv || db) {
-        hipError_t e = sru::launch_param_reduce(a.partials, shape->B, shape->d, dm.ndir, dv, db, s);
+    if (c.dv || c.db) {
+        hipError_t e =
+            sru::launch_param_reduce(a.partials, shape->B, shape->d, dm.ndir, c.dv, c.db, s);
         if (e != hipSuccess) return launched(e, "parameter-gradient reduction");
     }
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+sru_status sru_backward(const sru_shape *shape, const void *U, sru_dtype u_dt, const void *x,
+                        sru_dtype x_dt, const float *v, const float *b, const float *c0,
+                        const float *c_seq, const float *dh, const float *dc_last, float *dU,
+                        void *dU_lp, float *dx, float *dv, float *db, float *dc0, void *workspace,
+                        size_t workspace_bytes, void *stream)
+{
+    const BwdCall c{shape, U, u_dt, x, x_dt, v, b, c0, c_seq, dh, dc_last, dU, dU_lp, dx, dv, db,
+                    dc0};
+    Dims dm;
+    size_t need = 0;
+    SRU_TRY(check_backward(c, &dm, &need, workspace));
+    if (!workspace || workspace_bytes < need)
+        return fail(SRU_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need,
+                    workspace_bytes, workspace ? "" : ", NULL");
+    SRU_TRY(opt_ptr(workspace, "workspace"));
+    SRU_TRY(need_device());
+    return run_backward(c, dm, workspace, (uint32_t *)workspace + sru::kErrWord,
+                        (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The scratch of sru_backward_static: one array per GPU, alive until the
+// process ends, shared by every call on that GPU.  In host code `scratch`
+// names only a host-side stand-in; the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+__device__ __align__(256) unsigned char scratch[SRU_BACKWARD_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+sru_status static_scratch(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return fail(SRU_ERR_NO_DEVICE, "no current HIP device for the static scratch (%s)",
+                    e != hipSuccess ? hipGetErrorString(e) : "device index out of range");
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(SRU_ERR_LAUNCH, "static scratch address on device %d: %s", dev,
+                        hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SRU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sru_status sru_backward_static(const sru_shape *shape, const void *U, sru_dtype u_dt,
+                               const void *x, sru_dtype x_dt, const float *v, const float *b,
+                               const float *c0, const float *c_seq, const float *dh,
+                               const float *dc_last, float *dU, void *dU_lp, float *dx,
+                               float *dv, float *db, float *dc0, uint32_t *error_word,
+                               void *stream)
+{
+    const BwdCall c{shape, U, u_dt, x, x_dt, v, b, c0, c_seq, dh, dc_last, dU, dU_lp, dx, dv, db,
+                    dc0};
+    Dims dm;
+    size_t need = 0;
+    SRU_TRY(check_backward(c, &dm, &need, nullptr));
+    if (need > (size_t)SRU_BACKWARD_STATIC_SCRATCH_BYTES)
+        return fail(SRU_ERR_WORKSPACE,
+                    "this shape needs %zu bytes of scratch; the static scratch holds %zu "
+                    "(use sru_backward with a workspace)",
+                    need, (size_t)SRU_BACKWARD_STATIC_SCRATCH_BYTES);
+    if (((uintptr_t)error_word) & 3u)
+        return fail(SRU_ERR_INVALID_ARG, "error_word must be 4-byte aligned");
+    if (error_word) {
+        const Span out[] = {{error_word, 4, "error_word"}};
+        const size_t lbd = (size_t)(dm.LB * shape->d), ue = (size_t)dm.u_elems;
+        const size_t cs = (size_t)dm.chains * 4, ps = (size_t)(dm.ndir * 2 * shape->d) * 4;
+        const Span other[] = {{U, ue * elem_bytes(u_dt), "U"}, {x, lbd * elem_bytes(x_dt), "x"},
+                              {dU, ue * 4, "dU"}, {dU_lp, ue * 2, "dU_lp"}, {dx, lbd * 4, "dx"},
+                              {dv, ps, "dv"}, {db, ps, "db"}, {dc0, cs, "dc0"}};
+        SRU_TRY(no_overlap(out, 1, other, 8));
+    }
+    SRU_TRY(need_device());
+    void *ws = nullptr;
+    SRU_TRY(static_scratch(&ws));
+    uint32_t *err = error_word ? error_word : (uint32_t *)ws + sru::kErrWord;
+    return run_backward(c, dm, ws, err, (hipStream_t)stream);
 }
 
 sru_status sru_linear_scan(const sru_shape *shape, sru_pass pass, int32_t chunk, const void *U,

@@ -319,10 +319,13 @@ hipError_t launch_backward_scan(const RecArgs &r, void *ws, float *dv, float *db
     a.dc0 = r.dc0;
     a.dU_lp = r.dU_lp;
     // control block (error word, ticket), then the published adjoints, then
-    // the partial sums
+    // the partial sums.  The call's error word is r.err_word: the control
+    // block's own, or one the caller keeps elsewhere.
     uint32_t *ctrl = (uint32_t *)wsf;
-    a.lb.err = ctrl + kErrWord;
+    a.lb.err = r.err_word ? r.err_word : ctrl + kErrWord;
     a.lb.ticket = ctrl + kTicketWord;
+    if (nC > 1 && a.lb.err != ctrl + kErrWord)   // outside the region cleared below
+        hipLaunchKernelGGL(scan_clear, dim3(1), dim3(256), 0, s, a.lb.err, (int64_t)1);
     a.lb.carry = (uint64_t *)(wsf + kCtrlWords);
     a.part = wsf + kCtrlWords + 2 * nC * chains;
     const int64_t clear_words = kCtrlWords + 2 * nC * chains;

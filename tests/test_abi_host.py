@@ -20,6 +20,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 @pytest.fixture(scope="module")
 def lib():
+    # The checks below hand fake device addresses to the library and expect
+    # SRU_ERR_NO_DEVICE from calls that are otherwise valid; where a GPU is
+    # visible those calls would launch kernels on the fake addresses, so the
+    # module runs only where none is.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-only checks (fake device addresses): a GPU is visible")
     if not os.path.exists(Bd.LIB_PATH):
         from parallelizable_recurrent_units_amd import build
         build.build()
@@ -408,3 +415,35 @@ def test_error_word_reader_on_host_bytes():
     ws.zero_()
     ws[Bd.SRU_WS_ERROR_OFFSET + 4] = 7          # the ticket word is not the error word
     assert Bd.workspace_error_word(ws) == 0
+
+
+# Fake addresses 64 GiB apart: room for the large shape's tensors.
+Z = [(i + 1) << 36 for i in range(16)]
+
+
+def test_static_scratch_backward_validation(lib):
+    """sru_backward_static: the static scratch bounds the shape (checked
+    before any device use), and its error word must be 4-byte aligned and
+    apart from the outputs."""
+    def call(s, **kw):
+        a = dict(U=Z[0], x=Z[1], v=Z[2], b=Z[3], c0=None, c_seq=Z[5], dh=Z[6], dc_last=None,
+                 dU=Z[7], dU_lp=None, dx=Z[8], dv=None, db=None, dc0=None, err=None)
+        a.update(kw)
+        return lib.sru_backward_static(ctypes.byref(s), a["U"], 0, a["x"], 0, a["v"], a["b"],
+                                       a["c0"], a["c_seq"], a["dh"], a["dc_last"], a["dU"],
+                                       a["dU_lp"], a["dx"], a["dv"], a["db"], a["dc0"], a["err"],
+                                       None)
+    big = sru.SruShape(4096, 16, 4096, 0, 1.0)
+    assert sru.sru_workspace_size(big, sru.SRU_WS_BACKWARD) > Bd.SRU_BACKWARD_STATIC_SCRATCH_BYTES
+    assert call(big) == sru.SRU_ERR_WORKSPACE
+    assert b"static scratch" in lib.sru_last_error()
+    s = sru.SruShape(512, 32, 1024, 0, 1.0)      # the training step: 6.3 MB of scratch, fits
+    assert sru.sru_workspace_size(s, sru.SRU_WS_BACKWARD) <= Bd.SRU_BACKWARD_STATIC_SCRATCH_BYTES
+    assert call(s, err=Z[9] + 2) == sru.SRU_ERR_INVALID_ARG
+    assert call(s, err=Z[8]) == sru.SRU_ERR_INVALID_ARG          # on top of dx
+    assert call(s, dU=None) == sru.SRU_ERR_INVALID_ARG
+    assert call(s, err=Z[9]) in (sru.SRU_ERR_NO_DEVICE, sru.SRU_OK)
+    # the header's constant is the binding's
+    text = open(os.path.join(ROOT, "include", "sru.h")).read()
+    m = re.search(r"#define\s+SRU_BACKWARD_STATIC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == Bd.SRU_BACKWARD_STATIC_SCRATCH_BYTES
