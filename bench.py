@@ -58,6 +58,9 @@ def parse():
     p.add_argument("--workload", type=int, default=4, choices=[2, 3, 4, 5],
                    help="2, 4: training step; 3: given-U forward; 5: linear mode fwd+bwd")
     p.add_argument("--sets", type=int, default=4, help="rotating input/output sets")
+    p.add_argument("--x-copy", choices=sorted(X_ROUNDED_COPY), default="auto",
+                   help="projection of fp32 X: round X into a bf16 copy first (on), round it "
+                        "while staging (off), or by size (auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-beyond", action="store_true",
@@ -186,7 +189,7 @@ def roofline_of(name, work, seconds):
 # ---------------------------------------------------------------------------
 # device buffers for one training-step set
 # ---------------------------------------------------------------------------
-def device_set(w, seed):
+def device_set(w, seed, x_copy=False):
     import numpy as np
     import torch
     from parallelizable_recurrent_units_amd import (SRU_WS_BACKWARD, SRU_WS_BWD_WEIGHT,
@@ -215,6 +218,7 @@ def device_set(w, seed):
                ws=torch.empty(sru_workspace_size(shape, SRU_WS_BACKWARD), device="cuda",
                               dtype=torch.uint8),
                dW=torch.empty((nd * 3 * d, d), **f32))
+    dev["xb"] = torch.empty((L, B, d), device="cuda", dtype=torch.bfloat16) if x_copy else None
     nw = sru_workspace_size(shape, SRU_WS_BWD_WEIGHT)
     dev["ws_w"] = torch.empty(nw, device="cuda", dtype=torch.uint8) if nw else None
     # factorised projection (timed beyond the step): weights ~ U(-0.05, 0.05) in bf16
@@ -230,20 +234,43 @@ def device_set(w, seed):
     return shape, dev
 
 
+X_ROUNDED_COPY = {"auto": None, "on": True, "off": False}
+
+
+def rounds_x_first(w, mode):
+    """Whether the step's projection first rounds X into a bf16 copy X~
+    (sru_round_bf16) and multiplies that, rather than rounding fp32 X as it
+    stages it.  The copy halves the operand bytes the GEMM streams per k-tile
+    (the stream the projection is bound by) for one extra pass over X; it
+    pays once the GEMM is long (the L = 512, B = 32, d = 1024 step), and the
+    weight gradient then reads X~ as well."""
+    if X_ROUNDED_COPY[mode] is not None:
+        return X_ROUNDED_COPY[mode]
+    return w.x_dtype == "f32" and w.L * w.B * w.d >= (1 << 24)
+
+
 def training_step_rows(shape, t):
-    """The four row calls of one training step (C-ABI entry points).  The
-    projection reads fp32 X and rounds it to bf16 as it stages it: at these
-    shapes that is faster than rounding X into a bf16 copy first."""
+    """The four row calls of one training step (C-ABI entry points).  With
+    t["xb"] present the projection row rounds X into that bf16 copy first and
+    multiplies the copy; otherwise it reads fp32 X and rounds it to bf16 as it
+    stages it."""
     from parallelizable_recurrent_units_amd import (SRU_PROJ_BWD_DATA_WT, SRU_PROJ_FWD,
                                                     sru_backward, sru_forward, sru_project,
-                                                    sru_transpose_weight)
+                                                    sru_round_bf16, sru_transpose_weight)
 
     def bwd_data():
         sru_transpose_weight(shape, t["W"], t["Wt"])
         sru_project(shape, SRU_PROJ_BWD_DATA_WT, t["dU_lp"], t["Wt"], t["dx"], True)
 
+    def proj():
+        if t.get("xb") is not None:
+            sru_round_bf16(t["x"], t["xb"])
+            sru_project(shape, SRU_PROJ_FWD, t["xb"], t["W"], t["U"])
+        else:
+            sru_project(shape, SRU_PROJ_FWD, t["x"], t["W"], t["U"])
+
     return [
-        ("a1_projection", lambda: sru_project(shape, SRU_PROJ_FWD, t["x"], t["W"], t["U"])),
+        ("a1_projection", proj),
         ("a2_forward", lambda: sru_forward(shape, t["U"], t["x"], t["v"], t["b"], t["c0"], t["h"],
                                            t["c_seq"], t["c_last"])),
         ("a3_a4_backward", lambda: sru_backward(shape, t["U"], t["x"], t["v"], t["b"], t["c0"],
@@ -277,8 +304,9 @@ def next_rows(shape, t):
         sru_project_factored_bwd_weight(shape, di, SRU_FACT_WGRAD_O, t["dU_lp"], t["Q"],
                                         t["dWo"], SRU_BF16, False, t["ws_f"])
 
+    xs = t["xb"] if t.get("xb") is not None else t["x"]
     rows = [("f1_projection_bwd_weight",
-             lambda: sru_project_bwd_weight(shape, t["dU_lp"], t["x"], t["dW"], SRU_BF16,
+             lambda: sru_project_bwd_weight(shape, t["dU_lp"], xs, t["dW"], SRU_BF16,
                                             False, t["ws_w"])),
             ("f3_factored_forward", fact_fwd),
             ("f3_factored_backward", fact_bwd)]
@@ -389,7 +417,7 @@ def check_error_words(sets):
             check_workspace(ws, name)
 
 
-def row_sets_for(w, nsets, seed0):
+def row_sets_for(w, nsets, seed0, x_copy_mode="auto"):
     """Rotating sets of the rows of workload ``w`` (each set: list of (row, fn))."""
     import torch
     from parallelizable_recurrent_units_amd import (SRU_BWD, SRU_FWD, SRU_WS_LINEAR_BWD,
@@ -399,7 +427,7 @@ def row_sets_for(w, nsets, seed0):
     if w.mode == "layer":
         out = []
         for i in range(nsets):
-            shape, t = device_set(w, seed0 + i)
+            shape, t = device_set(w, seed0 + i, rounds_x_first(w, x_copy_mode))
             out.append(RowSet(training_step_rows(shape, t)))
             out[-1].beyond = next_rows(shape, t)
             out[-1].workspaces = [("sru_backward", t["ws"])]
@@ -582,7 +610,9 @@ def cpu_baseline(w, budget_s=10.0):
 
 # kernel launches of one call of each row (what its event-timed span covers)
 ROW_LAUNCHES = {
-    "a1_projection": ["gemm_bf16_mfma (A = fp32 X, rounded to bf16 while staged)"],
+    "a1_projection": ["round_bf16_kernel (X~ = bf16(X)) + gemm_lds (X~ x W, operands copied "
+                      "straight into LDS), or gemm_bf16_mfma (A = fp32 X, rounded to bf16 while "
+                      "staged); see config.projection_x"],
     "a2_forward": ["fwd_fast (both directions in one grid)"],
     "a3_a4_backward": ["bwd_fast (fp32 inputs, up to 128 steps; both directions in one "
                        "launch when bidirectional and L <= 64, else one per direction, the "
@@ -608,21 +638,43 @@ ROW_LAUNCHES = {
                              "gemm_bf16_mfma + split_reduce (dWo = bf16(dU)^T Q)"],
 }
 
-# kernels of each training-step row (rocprofv3 kernel names), and the one
-# kernel that runs exactly once per call of the row
-ROW_KERNELS = {
-    "a1_projection": ([r"gemm_bf16_mfma<.*>, float, false, "],
-                      r"gemm_bf16_mfma<.*>, float, false, "),
-    "a2_forward": ([r"fwd_fast<"], r"fwd_fast<"),
-    "a3_a4_backward": ([r"bwd_scan<", r"bwd_fast<", r"scan_clear", r"param_reduce"],
-                       r"param_reduce"),
-    "a5_projection_bwd_data": ([r"transpose16", r"gemm_lds<"], r"transpose16"),
-}
+# Which training-step row a dispatch belongs to, from its kernel name and,
+# for the products that several rows launch (gemm_lds), the row of the
+# dispatch before it: rows run in order a1, a2, a3/a4, a5 in every step.
+ROW_OF_KERNEL = [
+    (r"round_bf16_kernel", "a1_projection"),
+    (r"gemm_bf16_mfma<.*>, float, false, ", "a1_projection"),
+    (r"fwd_fast<|fwd_split<|fwd_generic<", "a2_forward"),
+    (r"bwd_scan<|bwd_fast<|bwd_generic<|scan_clear|param_reduce", "a3_a4_backward"),
+    (r"transpose16", "a5_projection_bwd_data"),
+]
+ROW_ONCE = {"a2_forward": r"fwd_fast<|fwd_split<|fwd_generic<"}   # one dispatch per step
+
+
+def rows_of_dispatches(names):
+    """Row of each dispatch (dict id -> row) given {id: kernel name}: a
+    kernel named in ROW_OF_KERNEL fixes the row; gemm_lds takes the row of
+    the dispatch before it; anything else (input generation, copies) none."""
+    import re
+    out, cur = {}, None
+    for did in sorted(names):
+        n = names[did]
+        row = next((r for pat, r in ROW_OF_KERNEL if re.search(pat, n)), None)
+        if row is not None:
+            cur = row
+        elif re.search(r"gemm_lds<", n) and cur in ("a1_projection", "a5_projection_bwd_data"):
+            row = cur
+        else:
+            cur = None
+        if row is not None:
+            out[did] = row
+    return out
 
 
 def _per_dispatch(run_dir, counter):
-    """{dispatch id: (kernel name, counter summed over its hardware instances)}
-    from the rocpd database(s) a rocprofv3 --pmc run wrote under ``run_dir``."""
+    """{(file, dispatch id): (kernel name, counter summed over its hardware
+    instances)} from the rocpd database(s) a rocprofv3 --pmc run wrote under
+    ``run_dir``."""
     import glob
     import sqlite3
     files = glob.glob(os.path.join(run_dir, "**", "*.db"), recursive=True)
@@ -655,13 +707,23 @@ def write_traffic(workload, fetch_dir, write_dir, copy_bytes):
         if not copies:
             raise SystemExit(f"{counter}: no calibration copy kernel under {run_dir}")
         factors[counter] = copy_bytes / (max(copies) * 1024.0)
-        for row, (pats, anchor) in ROW_KERNELS.items():
-            calls = sum(1 for n, _ in per.values() if re.search(anchor, n))
-            if not calls:
-                continue
-            kib = sum(v for n, v in per.values() if any(re.search(q, n) for q in pats))
-            r = rows.setdefault(row, {"calls": calls})
-            r[counter.lower() + "_bytes"] = kib * 1024.0 * factors[counter] / calls
+        by_file = {}
+        for (f, did), (n, v) in per.items():
+            by_file.setdefault(f, {})[did] = (n, v)
+        kib, calls = {}, {}
+        for f, disp in by_file.items():
+            owner = rows_of_dispatches({d: nv[0] for d, nv in disp.items()})
+            for did, row in owner.items():
+                n, v = disp[did]
+                kib[row] = kib.get(row, 0.0) + v
+                if re.search(ROW_ONCE["a2_forward"], n):
+                    calls["steps"] = calls.get("steps", 0) + 1
+        steps = calls.get("steps", 0)
+        if not steps:
+            raise SystemExit(f"{counter}: no forward dispatch under {run_dir}")
+        for row, k in kib.items():
+            r = rows.setdefault(row, {"calls": steps})
+            r[counter.lower() + "_bytes"] = k * 1024.0 * factors[counter] / steps
     for r in rows.values():
         if "fetch_size_bytes" in r and "write_size_bytes" in r:
             r["bytes"] = r["fetch_size_bytes"] + r["write_size_bytes"]
@@ -715,7 +777,7 @@ def main():
     w = WORKLOADS[args.workload]
     nsets = 1 if w.linear else args.sets
     print(f"[bench] workload {w.name}: building {nsets} input sets", file=sys.stderr, flush=True)
-    row_sets = row_sets_for(w, nsets, 100)
+    row_sets = row_sets_for(w, nsets, 100, args.x_copy)
     print("[bench] timing", file=sys.stderr, flush=True)
     ms, rows = time_rows(row_sets, args.steps, args.warmup)
     check_error_words(row_sets)
@@ -753,7 +815,11 @@ def main():
         "data": "synthetic (seeded Gaussian/uniform draws of the workload's shapes)",
         "config": {"workload": w.name, "L": w.L, "B": w.B, "d": w.d,
                    "bidirectional": w.ndir == 2, "alpha": w.alpha,
-                   "x": w.x_dtype, "W": w.w_dtype, "parallelism": "single GPU"},
+                   "x": w.x_dtype, "W": w.w_dtype, "parallelism": "single GPU",
+                   "projection_x": ("bf16 copy X~ = bf16(X) made in the row (sru_round_bf16)"
+                                    if w.mode == "layer" and rounds_x_first(w, args.x_copy) else
+                                    "as given (fp32 rounded to bf16 while staged)"
+                                    if w.mode == "layer" else None)},
         "elem_steps_per_s": w.elem_steps / rec_s,
         "frac_of_hbm_peak": rec_bytes / rec_s / 1e9 / HBM_PEAK_GBS,
         "gemm_frac_of_mfma_peak": {n: per_row[n]["frac"] for n in GEMM_ROWS if n in per_row},
