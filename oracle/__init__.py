@@ -60,6 +60,12 @@ def _load():
     lib.sru_oracle_sigmoid.argtypes = [ctypes.c_double]
     lib.sru_oracle_round_bf16.restype = ctypes.c_float
     lib.sru_oracle_round_bf16.argtypes = [ctypes.c_float]
+    lib.sru_oracle_attention_backward.restype = None
+    lib.sru_oracle_attention_backward.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, _dp, _dp,
+                                                  _dp, _dp, _dp, _dp, _dp]
+    lib.sru_oracle_layernorm_backward.restype = None
+    lib.sru_oracle_layernorm_backward.argtypes = [_i64, _i64, _dp, _dp, ctypes.c_double, _dp,
+                                                  _dp, _dp, _dp]
     lib.sru_oracle_project.restype = None
     lib.sru_oracle_project.argtypes = [_i64, _i64, _i64, _fp, ctypes.c_int, _fp,
                                        _ip, _i64, _ip, _i64, _dp]
@@ -379,6 +385,83 @@ def attention_project(X, Wq, Wk, Wv, Wo, L, B, alpha, mem_len=0, Kmem=None, Vmem
         R = layernorm(R, ln[0], ln[1], ln[2])
     U = matmul(_maybe_bf16(R, round_ops), Wo, b_nk=True)
     return {"Q": Q, "K": Kc, "V": Vc, "A": A.reshape(L * B, dp), "R": R, "U": U}
+
+
+def attention_backward(Q, K, V, dA, mem_len: int, causal: bool):
+    """Gradient of ``attention`` with respect to Q, K and V given dA [L, B, d']
+    (see sru_oracle_attention_backward).  Returns (dQ [L, B, d'], dK, dV
+    [mem_len + L, B, d'])."""
+    Q, pq = _f64(Q)
+    K, pk = _f64(K)
+    V, pv = _f64(V)
+    dA, pa = _f64(dA)
+    L, B, dp = Q.shape
+    assert K.shape == (mem_len + L, B, dp) and V.shape == K.shape and dA.shape == Q.shape
+    dQ = np.empty_like(Q)
+    dK = np.empty_like(K)
+    dV = np.empty_like(V)
+    _load().sru_oracle_attention_backward(L, B, dp, int(mem_len), int(bool(causal)), pq, pk, pv,
+                                          pa, dQ.ctypes.data_as(_dp), dK.ctypes.data_as(_dp),
+                                          dV.ctypes.data_as(_dp))
+    return dQ, dK, dV
+
+
+def layernorm_backward(x, gamma, eps: float, dy):
+    """Gradient of ``layernorm`` given dy: (dx, dgamma, dbeta)."""
+    x, px = _f64(x)
+    g, pg = _f64(gamma)
+    dy, pd = _f64(dy)
+    w = x.shape[-1]
+    dx = np.empty_like(x)
+    dg = np.empty(w)
+    db = np.empty(w)
+    _load().sru_oracle_layernorm_backward(x.size // w, w, px, pg, float(eps), pd,
+                                          dx.ctypes.data_as(_dp), dg.ctypes.data_as(_dp),
+                                          db.ctypes.data_as(_dp))
+    return dx, dg, db
+
+
+def attention_project_backward(X, Wq, Wk, Wv, Wo, L, B, alpha, dU, mem_len=0, Kmem=None,
+                               Vmem=None, causal=True, ln=None, round_ops=False):
+    """Gradients of ``attention_project`` (chain rule; the pages give no
+    backward) for the upstream gradient dU [L*B, n3] of U: with respect to X,
+    Wq, Wk, Wv, Wo, the residual weight alpha and, when ln, gamma and beta.
+    The previous segment's keys and values (Kmem, Vmem) are constants: no
+    gradient flows into them.  round_ops rounds every product's operands to
+    bf16 where the GPU path does (the forward's, and in the backward dU, R,
+    dO, dS', dK, dV, dQ as they enter their products), the rounding itself
+    passed through as the identity.  Returns a dict of the gradients and the
+    intermediates dR, dS, dO, dQ."""
+    f = attention_project(X, Wq, Wk, Wv, Wo, L, B, alpha, mem_len, Kmem, Vmem, causal, ln,
+                          round_ops)
+    rb = lambda a: _maybe_bf16(a, round_ops)
+    dp = Wq.shape[0]
+    Q, A, R = f["Q"], f["A"], f["R"]
+    dUt = rb(dU)
+    dWo = matmul(dUt, rb(R), a_km=True)                  # dU^T R~         [n3, dp]
+    dR = matmul(dUt, Wo)                                 # dU Wo           [LB, dp]
+    S = Q + alpha * A                                    # before the norm
+    if ln is not None:
+        dS, dgamma, dbeta = layernorm_backward(S, ln[0], ln[2], dR)
+    else:
+        dS, dgamma, dbeta = dR, None, None
+    dalpha = float(np.sum(dS * A))
+    dO = alpha * dS
+    Qt = rb(Q).reshape(L, B, dp)
+    dQa, dK, dV = attention_backward(Qt, rb(f["K"]), rb(f["V"]), rb(dO).reshape(L, B, dp),
+                                     mem_len, causal)
+    dKs = dK[mem_len:].reshape(L * B, dp)                # this segment's keys and values
+    dVs = dV[mem_len:].reshape(L * B, dp)
+    Qr = rb(Q)
+    dWk = matmul(rb(dKs), Qr, a_km=True)
+    dWv = matmul(rb(dVs), Qr, a_km=True)
+    dQ = dS + dQa.reshape(L * B, dp) + matmul(rb(dKs), Wk) + matmul(rb(dVs), Wv)
+    dQt = rb(dQ)
+    dWq = matmul(dQt, rb(X), a_km=True)
+    dX = matmul(dQt, Wq)
+    return {"dX": dX, "dWq": dWq, "dWk": dWk, "dWv": dWv, "dWo": dWo, "dalpha": dalpha,
+            "dgamma": dgamma, "dbeta": dbeta, "dR": dR, "dS": dS, "dO": dO, "dQ": dQ,
+            "dK": dKs, "dV": dVs}
 
 
 def step(x, W, v, b, c_prev, alpha, round_x: bool):

@@ -209,6 +209,130 @@ void sru_oracle_layernorm(int64_t n, int64_t w, const double *x, const double *g
 }
 
 /*
+ * Gradient of sru_oracle_attention with respect to Q, K and V, given the
+ * gradient dA of its output (chain rule; the pages give no backward).  With
+ * p the weights of query t and s the scaled scores:
+ *   dV[j] += p_j dA[t]                       (A[t] = sum_j p_j V[j])
+ *   g_j    = dA[t] . V[j],  D = sum_j p_j g_j
+ *   ds_j   = p_j (g_j - D)                   (softmax Jacobian)
+ *   dQ[t]  = sum_j ds_j K[j] / sqrt(dp),  dK[j] += ds_j Q[t] / sqrt(dp)
+ * over the keys j the query sees (masked keys take no gradient).  Layouts as
+ * in sru_oracle_attention; dQ [L, B, dp] is written, dK and dV [Lk, B, dp]
+ * are written (summed over the queries that see each key).  Sequences are
+ * independent: the loop over b runs in parallel, t and j in order.
+ */
+void sru_oracle_attention_backward(int64_t L, int64_t B, int64_t dp, int64_t Lm, int causal,
+                                   const double *Q, const double *K, const double *V,
+                                   const double *dA, double *dQ, double *dK, double *dV)
+{
+    const int64_t Lk = Lm + L;
+    const double scale = 1.0 / sqrt((double)dp);
+    for (int64_t i = 0; i < Lk * B * dp; ++i) {
+        dK[i] = 0.0;
+        dV[i] = 0.0;
+    }
+#pragma omp parallel
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)Lk);
+        double *g = (double *)malloc(sizeof(double) * (size_t)Lk);
+#pragma omp for schedule(static)
+        for (int64_t b = 0; b < B; ++b) {
+            for (int64_t t = 0; t < L; ++t) {
+                const double *q = Q + (t * B + b) * dp;
+                const double *da = dA + (t * B + b) * dp;
+                const int64_t nk = causal ? Lm + t + 1 : Lk;
+                double mx = -INFINITY;
+                for (int64_t j = 0; j < nk; ++j) {
+                    const double *k = K + (j * B + b) * dp;
+                    double s = 0.0;
+                    for (int64_t e = 0; e < dp; ++e)
+                        s += q[e] * k[e];
+                    p[j] = s * scale;
+                    if (p[j] > mx)
+                        mx = p[j];
+                }
+                double l = 0.0;
+                for (int64_t j = 0; j < nk; ++j) {
+                    p[j] = exp(p[j] - mx);
+                    l += p[j];
+                }
+                double D = 0.0;
+                for (int64_t j = 0; j < nk; ++j) {
+                    p[j] /= l;
+                    const double *v = V + (j * B + b) * dp;
+                    double gj = 0.0;
+                    for (int64_t e = 0; e < dp; ++e)
+                        gj += da[e] * v[e];
+                    g[j] = gj;
+                    D += p[j] * gj;
+                }
+                double *dq = dQ + (t * B + b) * dp;
+                for (int64_t e = 0; e < dp; ++e)
+                    dq[e] = 0.0;
+                for (int64_t j = 0; j < nk; ++j) {
+                    const double ds = p[j] * (g[j] - D) * scale;
+                    const double *k = K + (j * B + b) * dp;
+                    double *dk = dK + (j * B + b) * dp;
+                    double *dv = dV + (j * B + b) * dp;
+                    for (int64_t e = 0; e < dp; ++e) {
+                        dq[e] += ds * k[e];
+                        dk[e] += ds * q[e];
+                        dv[e] += p[j] * da[e];
+                    }
+                }
+            }
+        }
+        free(p);
+        free(g);
+    }
+}
+
+/*
+ * Gradient of sru_oracle_layernorm given dy: with xh = (x - mean) / sqrt(var
+ * + eps) per row and dxh = dy * gamma,
+ *   dx = (dxh - mean(dxh) - xh * mean(dxh * xh)) / sqrt(var + eps),
+ *   dgamma = sum over rows of dy * xh,  dbeta = sum over rows of dy.
+ * Rows in order (the parameter gradients are plain sums).
+ */
+void sru_oracle_layernorm_backward(int64_t n, int64_t w, const double *x, const double *gamma,
+                                   double eps, const double *dy, double *dx, double *dgamma,
+                                   double *dbeta)
+{
+    double *xh = (double *)malloc(sizeof(double) * (size_t)w);
+    for (int64_t e = 0; e < w; ++e) {
+        dgamma[e] = 0.0;
+        dbeta[e] = 0.0;
+    }
+    for (int64_t i = 0; i < n; ++i) {
+        const double *r = x + i * w;
+        const double *g = dy + i * w;
+        double mean = 0.0;
+        for (int64_t e = 0; e < w; ++e)
+            mean += r[e];
+        mean /= (double)w;
+        double var = 0.0;
+        for (int64_t e = 0; e < w; ++e)
+            var += (r[e] - mean) * (r[e] - mean);
+        var /= (double)w;
+        const double inv = 1.0 / sqrt(var + eps);
+        double m1 = 0.0, m2 = 0.0;
+        for (int64_t e = 0; e < w; ++e) {
+            xh[e] = (r[e] - mean) * inv;
+            const double dxh = g[e] * gamma[e];
+            m1 += dxh;
+            m2 += dxh * xh[e];
+            dgamma[e] += g[e] * xh[e];
+            dbeta[e] += g[e];
+        }
+        m1 /= (double)w;
+        m2 /= (double)w;
+        for (int64_t e = 0; e < w; ++e)
+            dx[i * w + e] = (g[e] * gamma[e] - m1 - xh[e] * m2) * inv;
+    }
+    free(xh);
+}
+
+/*
  * Projection (Eq. 1) for a cross product of selected rows and columns:
  *   out[i][k] = sum_{q<K} Atilde[rows[i]][q] * W[cols[k]][q]
  * A is [M, K] row-major, W is [N, K] row-major (row n = output feature n).

@@ -48,12 +48,27 @@ MUTANTS = [
      "const double xv = round_x ? (double)sru_oracle_round_bf16(x[q]) : (double)x[q];",
      "const double xv = (double)x[q];"),
     ("attention without the 1/sqrt(d') scale",
-     "const double scale = 1.0 / sqrt((double)dp);", "const double scale = 1.0;"),
+     "const double scale = 1.0 / sqrt((double)dp);\n#pragma omp parallel\n    {\n        double *p = (double *)malloc(sizeof(double) * (size_t)Lk);\n#pragma omp for",
+     "const double scale = 1.0;\n#pragma omp parallel\n    {\n        double *p = (double *)malloc(sizeof(double) * (size_t)Lk);\n#pragma omp for"),
     ("causal mask one key short",
-     "const int64_t nk = causal ? Lm + t + 1 : Lk;",
-     "const int64_t nk = causal ? Lm + t + (t > 0) : Lk;"),
+     "* dp;\n            const int64_t nk = causal ? Lm + t + 1 : Lk;",
+     "* dp;\n            const int64_t nk = causal ? Lm + t + (t > 0) : Lk;"),
+    ("attention backward without the 1/sqrt(d') scale",
+     "const double scale = 1.0 / sqrt((double)dp);\n    for (int64_t i = 0;",
+     "const double scale = 1.0;\n    for (int64_t i = 0;"),
+    ("attention backward with the causal mask one key short",
+     "* dp;\n                const int64_t nk = causal ? Lm + t + 1 : Lk;",
+     "* dp;\n                const int64_t nk = causal ? Lm + t + (t > 0) : Lk;"),
     ("layer norm with the unbiased variance",
-     "var /= (double)w;", "var /= (double)(w > 1 ? w - 1 : 1);"),
+     "var /= (double)w;\n        const double inv = 1.0 / sqrt(var + eps);\n        for (int64_t e = 0; e < w; ++e)\n            y[i * w + e]",
+     "var /= (double)(w > 1 ? w - 1 : 1);\n        const double inv = 1.0 / sqrt(var + eps);\n        for (int64_t e = 0; e < w; ++e)\n            y[i * w + e]"),
+    ("softmax backward without the weighted mean of the value gradients",
+     "const double ds = p[j] * (g[j] - D) * scale;", "const double ds = p[j] * g[j] * scale;"),
+    ("value gradient without the attention weight",
+     "dv[e] += p[j] * da[e];", "dv[e] += da[e];"),
+    ("layer norm backward without the mean term",
+     "dx[i * w + e] = (g[e] * gamma[e] - m1 - xh[e] * m2) * inv;",
+     "dx[i * w + e] = (g[e] * gamma[e] - xh[e] * m2) * inv;"),
 ]
 
 # (name, text in oracle/__init__.py, the planted mistake)
@@ -77,6 +92,12 @@ PY_MUTANTS = [
      "    U = matmul(_maybe_bf16(R, round_ops), Wo, b_nk=True)\n"
      "    if ln is not None:\n"
      "        U = layernorm(U, np.resize(ln[0], U.shape[1]), np.resize(ln[1], U.shape[1]), ln[2])"),
+    ("alpha's gradient taken against R instead of A",
+     "dalpha = float(np.sum(dS * A))", "dalpha = float(np.sum(dS * R))"),
+    ("no residual path from the normalised sum back to Q",
+     "dQ = dS + dQa.reshape(L * B, dp)", "dQ = dQa.reshape(L * B, dp)"),
+    ("the context rows take the key and value gradients",
+     "dKs = dK[mem_len:].reshape(L * B, dp)", "dKs = dK[:L].reshape(L * B, dp)"),
     ("layer norm of Q before the attention term is added",
      "    R = Q + alpha * A.reshape(L * B, dp)\n"
      "    if ln is not None:\n"

@@ -744,3 +744,92 @@ def test_step_closed_gate_copies_candidate():
     ucand = x.astype(np.float64) @ W[2 * d:].astype(np.float64).T
     np.testing.assert_allclose(c, ucand, rtol=1e-14, atol=1e-14)
     np.testing.assert_allclose(h, ucand, rtol=1e-14, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# SRU++ attention: backward
+# --------------------------------------------------------------------------
+
+def _central_difference(f, arr, h=1e-6):
+    """d f / d arr by central differences, element by element (arr is
+    perturbed in place and restored)."""
+    g = np.empty_like(arr, dtype=np.float64)
+    for idx in np.ndindex(arr.shape):
+        keep = arr[idx]
+        arr[idx] = keep + h
+        fp = f()
+        arr[idx] = keep - h
+        fm = f()
+        arr[idx] = keep
+        g[idx] = (fp - fm) / (2 * h)
+    return g
+
+
+@pytest.mark.parametrize("causal,ln,Lm", [(True, False, 0), (True, True, 2), (False, True, 1),
+                                          (False, False, 2)])
+def test_attention_backward_finite_differences(causal, ln, Lm):
+    """Every gradient of the attention U-producer against central differences
+    of the scalar sum(dU * U): X, Wq, Wk, Wv, Wo, alpha and (layer norm on)
+    gamma, beta.  The context rows are constants; perturbing them is not a
+    parameter of the loss."""
+    rng = np.random.default_rng(60 + Lm + 3 * causal + 7 * ln)
+    L, B, d, dp = 3, 2, 4, 3
+    P = {"X": rng.standard_normal((L * B, d)),
+         "Wq": rng.standard_normal((dp, d)) * 0.6,
+         "Wk": rng.standard_normal((dp, dp)) * 0.6,
+         "Wv": rng.standard_normal((dp, dp)) * 0.6,
+         "Wo": rng.standard_normal((3 * d, dp)) * 0.6,
+         "alpha": np.array(0.7),
+         "gamma": rng.uniform(0.5, 1.5, dp),
+         "beta": rng.uniform(-0.5, 0.5, dp)}
+    Kmem = rng.standard_normal((Lm, B, dp))
+    Vmem = rng.standard_normal((Lm, B, dp))
+    dU = rng.standard_normal((L * B, 3 * d))
+    eps = 1e-3
+
+    def loss():
+        lnp = (P["gamma"], P["beta"], eps) if ln else None
+        U = oracle.attention_project(P["X"], P["Wq"], P["Wk"], P["Wv"], P["Wo"], L, B,
+                                     float(P["alpha"]), Lm, Kmem, Vmem, causal, lnp)["U"]
+        return float(np.sum(dU * U))
+
+    g = oracle.attention_project_backward(P["X"], P["Wq"], P["Wk"], P["Wv"], P["Wo"], L, B,
+                                          float(P["alpha"]), dU, Lm, Kmem, Vmem, causal,
+                                          (P["gamma"], P["beta"], eps) if ln else None)
+    names = ["X", "Wq", "Wk", "Wv", "Wo", "alpha"] + (["gamma", "beta"] if ln else [])
+    for n in names:
+        num = _central_difference(loss, P[n])
+        got = np.asarray(g["d" + n], np.float64)
+        scale = max(1.0, float(np.max(np.abs(num))))
+        np.testing.assert_allclose(got, num, rtol=1e-6, atol=1e-7 * scale, err_msg=n)
+
+
+def test_attention_backward_single_key_closed_form():
+    """One query that sees one key: A = V, so dV = dA, and the weight is
+    constant 1, so no gradient reaches Q or K."""
+    rng = np.random.default_rng(70)
+    Q, K, V, dA = (rng.standard_normal((1, 2, 3)) for _ in range(4))
+    dQ, dK, dV = oracle.attention_backward(Q, K, V, dA, 0, True)
+    np.testing.assert_array_equal(dV, dA)
+    np.testing.assert_allclose(dQ, 0.0, atol=1e-15)
+    np.testing.assert_allclose(dK, 0.0, atol=1e-15)
+
+
+def test_layernorm_backward_closed_form():
+    """d/dx of layernorm with unit gain: the gradient sums to zero over a row
+    (shifting a row does not change its normalisation), its projection on xh
+    is sum(dy xh) eps / ((var + eps) sqrt(var + eps)) (only eps keeps the
+    scale direction alive), and dbeta, dgamma are the column sums of dy and
+    dy * xh."""
+    rng = np.random.default_rng(71)
+    x = rng.standard_normal((5, 7)) * 2 + 1
+    dy = rng.standard_normal((5, 7))
+    eps = 1e-2
+    dx, dg, db = oracle.layernorm_backward(x, np.ones(7), eps, dy)
+    var = x.var(1)
+    xh = (x - x.mean(1, keepdims=True)) / np.sqrt(var[:, None] + eps)
+    np.testing.assert_allclose(dx.sum(1), 0.0, atol=1e-12)
+    want = (dy * xh).sum(1) * eps / ((var + eps) * np.sqrt(var + eps))
+    np.testing.assert_allclose((dx * xh).sum(1), want, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(db, dy.sum(0), rtol=1e-14)
+    np.testing.assert_allclose(dg, (dy * xh).sum(0), rtol=1e-12)
