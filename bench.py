@@ -165,7 +165,22 @@ def attention_work(w):
     flops = (2 * LB * d * dp + 2 * LB * dp * 2 * dp + 4 * pairs * dp + 2 * LB * dp * n3)
     byts = (LB * d * 4 + (dp * d + 2 * dp * dp + n3 * dp) * 2 + LB * dp * 4
             + LB * 2 * dp * 2 + (Lm + L) * B * 2 * dp * 2 + LB * dp * 4 + LB * n3 * 2)
-    return {"f2_attention_forward": dict(flops=flops, bytes=byts)}
+    # backward: the forward's three attention products again (recomputed),
+    # then dR = dU Wo, dWo = dU^T R, dP = dO V^T, dQ += dS' K, dK = dS'^T Q,
+    # dV = P^T dO (visible pairs), dWkv = dKV^T Q, dQ += dKV Wkv, dWq = dQ^T X,
+    # dX = dQ Wq; bytes: X, the weights, Q, KV, R, dU (fp32) and dX read or
+    # written once, the weight gradients written once
+    seg = B * (L * (L + 1) // 2)                                # pairs within the segment
+    bflops = (4 * pairs * dp                                   # S and A recomputed
+              + 4 * LB * n3 * dp                               # dR, dWo
+              + 4 * pairs * dp + 4 * seg * dp                  # dP, dQ; dK, dV (segment keys)
+              + 8 * LB * dp * dp                               # dWkv, dQ += dKV Wkv
+              + 4 * LB * dp * d)                               # dWq, dX
+    bbytes = (LB * d * 4 + (dp * d + 2 * dp * dp + n3 * dp) * 2 + 2 * LB * dp * 4
+              + (Lm + L) * B * 2 * dp * 2 + LB * n3 * 4 + LB * d * 4
+              + (dp * d + 2 * dp * dp + n3 * dp) * 4)
+    return {"f2_attention_forward": dict(flops=flops, bytes=byts),
+            "f2_attention_backward": dict(flops=bflops, bytes=bbytes)}
 
 
 def factored_inner(w):
@@ -381,7 +396,9 @@ def attention_rows(w, shape, g):
     previous segment's keys and values ~ N(0, 1) in front; U written in
     bf16, as the given-U recurrence takes it."""
     import torch
-    from parallelizable_recurrent_units_amd import (SruAttnCfg, sru_attention_forward,
+    from parallelizable_recurrent_units_amd import (SruAttnCfg, sru_attention_backward,
+                                                    sru_attention_backward_workspace_size,
+                                                    sru_attention_forward,
                                                     sru_attention_workspace_size)
     L, B, d, nd = w.L, w.B, w.d, w.ndir
     dp, Lm = max(1, d // 4), int(ATTN_CONTEXT * L)
@@ -395,9 +412,18 @@ def attention_rows(w, shape, g):
     Q, R = torch.empty((L * B, dp), **f32), torch.empty((L * B, dp), **f32)
     U = torch.empty((L, B, nd, 3, d), device="cuda", dtype=torch.bfloat16)
     ws = torch.empty(sru_attention_workspace_size(shape, cfg), device="cuda", dtype=torch.uint8)
+    # the backward takes this forward's Q, KV and R, and dU ~ N(0, 1)
+    dU = torch.randn((L * B, nd * 3 * d), generator=g, **f32)
+    dX = torch.empty((L * B, d), **f32)
+    grads = [torch.empty(n, **f32) for n in (dp * d, 2 * dp * dp, nd * 3 * d * dp, 1, dp, dp)]
+    wsb = torch.empty(sru_attention_backward_workspace_size(shape, cfg), device="cuda",
+                      dtype=torch.uint8)
     return [("f2_attention_forward",
              lambda: sru_attention_forward(shape, cfg, X, Wq, Wkv, Wo, gamma, beta, Q, KV, R, U,
-                                           ws))]
+                                           ws)),
+            ("f2_attention_backward",
+             lambda: sru_attention_backward(shape, cfg, X, Wq, Wkv, Wo, gamma, Q, KV, R, dU, dX,
+                                            *grads, wsb))]
 
 
 class RowSet(list):
@@ -633,6 +659,12 @@ ROW_LAUNCHES = {
                              "attn_softmax", "gemm_bf16_mfma (weights x V, batched)",
                              "attn_residual (R = layernorm(Q + alpha A))",
                              "gemm_bf16_mfma (U = R Wo^T)"],
+    "f2_attention_backward": ["the forward's scores, softmax and A again (3 launches)",
+                              "gemm_bf16_mfma (dR = dU Wo)", "gemm + split_reduce (dWo)",
+                              "attn_residual_bwd + attn_part_reduce", "gemm (dP = dO V^T)",
+                              "attn_softmax_bwd", "gemm (dQ += dS' K)", "gemm TN (dK, dV)",
+                              "gemm + split_reduce (dWkv)", "gemm (dQ += dKV Wkv)",
+                              "gemm + split_reduce (dWq)", "gemm (dX = dQ Wq)"],
     "f3_factored_backward": ["gemm_bf16_mfma (dQ = bf16(dU) Wo)", "gemm_bf16_mfma (dx += dQ Wq)",
                              "gemm_bf16_mfma + split_reduce (dWq = dQ^T X)",
                              "gemm_bf16_mfma + split_reduce (dWo = bf16(dU)^T Q)"],

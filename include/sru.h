@@ -232,6 +232,44 @@ sru_status sru_attention_forward(const sru_shape *shape, const sru_attn_cfg *cfg
 size_t sru_attention_workspace_size(const sru_shape *shape, const sru_attn_cfg *cfg);
 
 /*
+ * Backward of sru_attention_forward (the chain rule through it; the paper
+ * trains the attention, its alpha and the layer norm end to end, section on
+ * SRU++): given dU, the gradient of the forward's U, writes
+ *   dX [L*B, d]           the input gradient (accumulate_dx = 1 adds it to
+ *                         dX, e.g. onto the highway dx of sru_backward, the
+ *                         layer input being shared)
+ *   dWq [d', d], dWkv [2d', d'] (Wk's rows, then Wv's), dWo [ndir*3d, d']
+ *   dalpha (one float), and when cfg->layernorm dgamma, dbeta [d']
+ * all fp32, overwritten, in device memory.  The previous segment's keys and
+ * values (KV's first mem_len rows) are treated as constants: no gradient
+ * flows into them.
+ * Inputs: the forward's X, weights, gamma (beta is not needed) and its
+ * outputs Q, KV, R, unchanged; dU [L*B, ndir*3d] fp32 or bf16 (du_dt).  The
+ * weights, attention and A are recomputed from Q and KV.  Every product
+ * rounds its operands to bf16 as it loads them (bf16 MFMA, fp32 sums); the
+ * softmax, normalisation and residual gradients are fp32.  The rounding is
+ * passed through as the identity.  dalpha, dgamma and dbeta are sums added
+ * in a fixed order (bit-reproducible run to run).
+ * cfg->d_inner <= 1024 (SRU_ERR_UNSUPPORTED above).
+ * workspace: sru_attention_backward_workspace_size(shape, cfg) bytes,
+ * 256-byte aligned; scratch.  Outputs must not overlap each other or the
+ * inputs.
+ */
+sru_status sru_attention_backward(const sru_shape *shape, const sru_attn_cfg *cfg,
+                                  const void *X, sru_dtype x_dt,
+                                  const void *Wq, const void *Wkv, const void *Wo,
+                                  const float *gamma,
+                                  const float *Q, const void *KV, const float *R,
+                                  const void *dU, sru_dtype du_dt,
+                                  float *dX, int32_t accumulate_dx,
+                                  float *dWq, float *dWkv, float *dWo,
+                                  float *dalpha, float *dgamma, float *dbeta,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of sru_attention_backward; 0 on invalid arguments. */
+size_t sru_attention_backward_workspace_size(const sru_shape *shape, const sru_attn_cfg *cfg);
+
+/*
  * One step of a unidirectional layer for decoding: the recurrence run as an
  * RNN at inference ("Parallelizing Legendre Memory Unit Training", abstract),
  * i.e. Eq. 1 and Eqs. 2-5 for a single time step with the state carried

@@ -461,7 +461,7 @@ def attention_project_backward(X, Wq, Wk, Wv, Wo, L, B, alpha, dU, mem_len=0, Km
     dX = matmul(dQt, Wq)
     return {"dX": dX, "dWq": dWq, "dWk": dWk, "dWv": dWv, "dWo": dWo, "dalpha": dalpha,
             "dgamma": dgamma, "dbeta": dbeta, "dR": dR, "dS": dS, "dO": dO, "dQ": dQ,
-            "dK": dKs, "dV": dVs}
+            "dK": dKs, "dV": dVs, "A": A}
 
 
 def step(x, W, v, b, c_prev, alpha, round_x: bool):

@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     SRU_FACT_BWD_Q, SRU_FACT_BWD_X, SRU_FACT_Q, SRU_FACT_U, SRU_FACT_WGRAD_O, SRU_FACT_WGRAD_Q,
     SRU_WS_FACTORED_WEIGHT, sru_project_factored, sru_project_factored_bwd_weight,
     SruAttnCfg, sru_attention_forward, sru_attention_workspace_size, sru_step, sru_round_bf16,
+    sru_attention_backward, sru_attention_backward_workspace_size,
     EXPORTED, LIB_PATH, SRU_BF16, SRU_BWD, SRU_ERR_INVALID_ARG, SRU_ERR_LAUNCH,
     SRU_ERR_NO_DEVICE, SRU_ERR_UNSUPPORTED, SRU_ERR_WORKSPACE, SRU_F32, SRU_FWD, SRU_OK,
     SRU_PROJ_BWD_DATA, SRU_PROJ_BWD_DATA_WT, SRU_PROJ_FWD, SRU_WS_BACKWARD, SRU_WS_BWD_WEIGHT, SRU_WS_LINEAR_BWD,

@@ -27,7 +27,8 @@ SRU_FACT_WGRAD_Q, SRU_FACT_WGRAD_O = 0, 1
 # Every symbol include/sru.h declares.
 EXPORTED = ("sru_project", "sru_project_bwd_weight", "sru_project_factored",
             "sru_project_factored_bwd_weight", "sru_attention_forward",
-            "sru_attention_workspace_size", "sru_step", "sru_forward", "sru_backward",
+            "sru_attention_workspace_size", "sru_attention_backward",
+            "sru_attention_backward_workspace_size", "sru_step", "sru_forward", "sru_backward",
             "sru_backward_static", "sru_linear_scan",
             "sru_transpose_weight", "sru_round_bf16", "sru_workspace_size", "sru_status_string",
             "sru_last_error")
@@ -100,6 +101,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                           _vp, _vp, _vp, _vp, ctypes.c_int, _vp, sz, _vp]
     lib.sru_attention_workspace_size.restype = sz
     lib.sru_attention_workspace_size.argtypes = [sp, cp]
+    lib.sru_attention_backward.restype = ctypes.c_int
+    lib.sru_attention_backward.argtypes = [sp, cp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
+                                           _vp, _vp, _vp, ctypes.c_int, _vp, i32, _vp, _vp, _vp,
+                                           _vp, _vp, _vp, _vp, sz, _vp]
+    lib.sru_attention_backward_workspace_size.restype = sz
+    lib.sru_attention_backward_workspace_size.argtypes = [sp, cp]
     lib.sru_step.restype = ctypes.c_int
     lib.sru_step.argtypes = [sp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
                              _vp]
@@ -245,6 +252,32 @@ def sru_attention_forward(shape, cfg, X, Wq, Wkv, Wo, gamma, beta, Q, KV, R, U, 
         ctypes.byref(s), ctypes.byref(cfg), _ptr(X), _dtype_code(X), _ptr(Wq), _ptr(Wkv),
         _ptr(Wo), _ptr(gamma), _ptr(beta), _ptr(Q), _ptr(KV), _ptr(R), _ptr(U), _dtype_code(U),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def sru_attention_backward_workspace_size(shape, cfg) -> int:
+    s = _shape(shape)
+    n = load_library().sru_attention_backward_workspace_size(ctypes.byref(s), ctypes.byref(cfg))
+    if n == 0:
+        raise SruError(SRU_ERR_INVALID_ARG, "SRU_ERR_INVALID_ARG",
+                       load_library().sru_last_error().decode())
+    return int(n)
+
+
+def sru_attention_backward(shape, cfg, X, Wq, Wkv, Wo, gamma, Q, KV, R, dU, dX, dWq, dWkv, dWo,
+                           dalpha, dgamma, dbeta, workspace, accumulate_dx: bool = False,
+                           stream=None):
+    s = _shape(shape)
+    for name, t in (("Wq", Wq), ("Wkv", Wkv), ("Wo", Wo), ("KV", KV)):
+        if _dtype_code(t) != SRU_BF16:
+            raise TypeError(f"{name} must be bfloat16")
+    _need_f32(gamma=gamma, Q=Q, R=R, dX=dX, dWq=dWq, dWkv=dWkv, dWo=dWo, dalpha=dalpha,
+              dgamma=dgamma, dbeta=dbeta)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().sru_attention_backward(
+        ctypes.byref(s), ctypes.byref(cfg), _ptr(X), _dtype_code(X), _ptr(Wq), _ptr(Wkv),
+        _ptr(Wo), _ptr(gamma), _ptr(Q), _ptr(KV), _ptr(R), _ptr(dU), _dtype_code(dU), _ptr(dX),
+        int(bool(accumulate_dx)), _ptr(dWq), _ptr(dWkv), _ptr(dWo), _ptr(dalpha), _ptr(dgamma),
+        _ptr(dbeta), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def sru_step(shape, x, W, v, b, c_prev, h, c_next, stream=None):

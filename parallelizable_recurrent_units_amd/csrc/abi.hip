@@ -493,6 +493,97 @@ sru_status sru_attention_forward(const sru_shape *shape, const sru_attn_cfg *cfg
     return launched(sru::launch_attention_forward(a, (hipStream_t)stream), "attention");
 }
 
+size_t sru_attention_backward_workspace_size(const sru_shape *shape, const sru_attn_cfg *cfg)
+{
+    Dims dm;
+    if (check_attn(shape, cfg, &dm) != SRU_OK) return 0;
+    ok();
+    return round256(sru::attention_backward_workspace_bytes(
+        shape->L, shape->B, shape->d, cfg->d_inner, cfg->mem_len, 3 * dm.ndir * shape->d));
+}
+
+sru_status sru_attention_backward(const sru_shape *shape, const sru_attn_cfg *cfg, const void *X,
+                                  sru_dtype x_dt, const void *Wq, const void *Wkv, const void *Wo,
+                                  const float *gamma, const float *Q, const void *KV,
+                                  const float *R, const void *dU, sru_dtype du_dt, float *dX,
+                                  int32_t accumulate_dx, float *dWq, float *dWkv, float *dWo,
+                                  float *dalpha, float *dgamma, float *dbeta, void *workspace,
+                                  size_t workspace_bytes, void *stream)
+{
+    Dims dm;
+    SRU_TRY(check_attn(shape, cfg, &dm));
+    if (!valid_dtype(x_dt) || !valid_dtype(du_dt)) return fail(SRU_ERR_INVALID_ARG, "unknown dtype");
+    if (accumulate_dx != 0 && accumulate_dx != 1)
+        return fail(SRU_ERR_INVALID_ARG, "accumulate_dx must be 0 or 1");
+    if (cfg->d_inner > sru::kAttnBwdMaxInner)
+        return fail(SRU_ERR_UNSUPPORTED, "the attention backward takes d_inner <= %lld (got %lld)",
+                    (long long)sru::kAttnBwdMaxInner, (long long)cfg->d_inner);
+    SRU_TRY(need_ptr(X, "X"));
+    SRU_TRY(need_ptr(Wq, "Wq"));
+    SRU_TRY(need_ptr(Wkv, "Wkv"));
+    SRU_TRY(need_ptr(Wo, "Wo"));
+    SRU_TRY(need_ptr(Q, "Q"));
+    SRU_TRY(need_ptr(KV, "KV"));
+    SRU_TRY(need_ptr(R, "R"));
+    SRU_TRY(need_ptr(dU, "dU"));
+    SRU_TRY(need_ptr(dX, "dX"));
+    SRU_TRY(need_ptr(dWq, "dWq"));
+    SRU_TRY(need_ptr(dWkv, "dWkv"));
+    SRU_TRY(need_ptr(dWo, "dWo"));
+    SRU_TRY(need_ptr(dalpha, "dalpha"));
+    if (cfg->layernorm) {
+        SRU_TRY(need_ptr(gamma, "gamma"));
+        SRU_TRY(need_ptr(dgamma, "dgamma"));
+        SRU_TRY(need_ptr(dbeta, "dbeta"));
+    }
+    const int64_t L = shape->L, B = shape->B, d = shape->d, dp = cfg->d_inner;
+    const int64_t Lm = cfg->mem_len, n3 = 3 * dm.ndir * d;
+    const size_t need = round256(sru::attention_backward_workspace_bytes(L, B, d, dp, Lm, n3));
+    if (!workspace || workspace_bytes < need)
+        return fail(SRU_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need,
+                    workspace_bytes, workspace ? "" : ", NULL");
+    if (((uintptr_t)workspace) & 255u)
+        return fail(SRU_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    {   // the written outputs against each other and every input
+        const size_t lbp = (size_t)(dm.LB * dp) * 4;
+        const Span out[] = {{dX, (size_t)(dm.LB * d) * 4, "dX"},
+                            {dWq, (size_t)(dp * d) * 4, "dWq"},
+                            {dWkv, (size_t)(2 * dp * dp) * 4, "dWkv"},
+                            {dWo, (size_t)(n3 * dp) * 4, "dWo"},
+                            {dalpha, 4, "dalpha"},
+                            {cfg->layernorm ? dgamma : nullptr, (size_t)dp * 4, "dgamma"},
+                            {cfg->layernorm ? dbeta : nullptr, (size_t)dp * 4, "dbeta"},
+                            {workspace, need, "workspace"}};
+        const Span in[] = {{X, (size_t)(dm.LB * d) * elem_bytes(x_dt), "X"},
+                           {Wq, (size_t)(dp * d) * 2, "Wq"},
+                           {Wkv, (size_t)(2 * dp * dp) * 2, "Wkv"},
+                           {Wo, (size_t)(n3 * dp) * 2, "Wo"},
+                           {gamma, cfg->layernorm ? (size_t)dp * 4 : 0, "gamma"},
+                           {Q, lbp, "Q"},
+                           {KV, (size_t)((Lm + L) * B * 2 * dp) * 2, "KV"},
+                           {R, lbp, "R"},
+                           {dU, (size_t)(dm.LB * n3) * elem_bytes(du_dt), "dU"}};
+        SRU_TRY(no_overlap(out, 8, in, 9));
+    }
+    SRU_TRY(need_device());
+    sru::AttnBwdArgs a;
+    a.L = L, a.B = B, a.d = d, a.dp = dp, a.Lm = Lm, a.n3 = n3;
+    a.causal = cfg->causal, a.layernorm = cfg->layernorm;
+    a.alpha = cfg->attn_alpha, a.eps = cfg->ln_eps;
+    a.X = X, a.x_bf16 = x_dt == SRU_BF16;
+    a.Wq = (const sru::bf16_bits_t *)Wq;
+    a.Wkv = (const sru::bf16_bits_t *)Wkv;
+    a.Wo = (const sru::bf16_bits_t *)Wo;
+    a.gamma = gamma;
+    a.Q = Q, a.R = R, a.KV = (const sru::bf16_bits_t *)KV;
+    a.dU = dU, a.du_bf16 = du_dt == SRU_BF16;
+    a.dX = dX, a.dx_accumulate = accumulate_dx != 0;
+    a.dWq = dWq, a.dWkv = dWkv, a.dWo = dWo, a.dalpha = dalpha;
+    a.dgamma = dgamma, a.dbeta = dbeta;
+    a.workspace = workspace;
+    return launched(sru::launch_attention_backward(a, (hipStream_t)stream), "attention backward");
+}
+
 sru_status sru_step(const sru_shape *shape, const void *x, sru_dtype x_dt, const void *W,
                     sru_dtype w_dt, const float *v, const float *b, const float *c_prev, float *h,
                     float *c_next, void *stream)

@@ -1247,6 +1247,22 @@ hipError_t launch_gemm_wgrad(const GemmArgs &g, bool f32_math, float *ws, hipStr
     return g.b_bf16 ? wgrad_launch<float, bf16_bits>(g, ws, s) : wgrad_launch<float, float>(g, ws, s);
 }
 
+namespace {
+template <typename TA, typename TB>
+hipError_t tn_launch(const GemmArgs &g, hipStream_t s)
+{
+    if (tiles_of(g, 256, 256) >= 256) return mfma_launch_cfg<CfgBig8, TA, true, TB, true>(g, s);
+    return mfma_launch_cfg<CfgSmall, TA, true, TB, true>(g, s);
+}
+}  // namespace
+
+hipError_t launch_gemm_tn(const GemmArgs &g, hipStream_t s)
+{
+    if (g.a_bf16)
+        return g.b_bf16 ? tn_launch<bf16_bits, bf16_bits>(g, s) : tn_launch<bf16_bits, float>(g, s);
+    return g.b_bf16 ? tn_launch<float, bf16_bits>(g, s) : tn_launch<float, float>(g, s);
+}
+
 hipError_t launch_gemm_bf16_out(const GemmArgs &g, hipStream_t s)
 {
     if (!g.b_bf16 || g.b_kn || g.accumulate || g.a_bf16) return hipErrorInvalidValue;

@@ -112,6 +112,10 @@ hipError_t launch_gemm_bf16_out(const GemmArgs &g, hipStream_t s);
 // fill the chip (ws then holds the partial products).
 size_t wgrad_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_wgrad(const GemmArgs &g, bool f32_math, float *ws, hipStream_t s);
+// C[M, N] (+)= A^T B with A given as [K, M] and B as [K, N] (bf16 or fp32
+// each, rounded to bf16 while staged; row strides and batches as in
+// GemmArgs), bf16 MFMA, no split of the reduction and no workspace.
+hipError_t launch_gemm_tn(const GemmArgs &g, hipStream_t s);
 // The SRU++ attention U-producer (attention.hip); layouts as in sru.h.
 struct AttnArgs {
     int64_t L, B, d, dp, Lm, n3;   // n3 = ndir * 3 * d
@@ -129,6 +133,30 @@ struct AttnArgs {
 };
 size_t attention_workspace_bytes(int64_t L, int64_t B, int64_t dp, int64_t Lm);
 hipError_t launch_attention_forward(const AttnArgs &a, hipStream_t s);
+
+// Its backward (attention.hip): the forward's Q, KV and R plus dU in; dX and
+// the parameter gradients out.  Layouts as in sru.h.
+constexpr int64_t kAttnBwdMaxInner = 1024;   // d' the row kernels hold in registers
+struct AttnBwdArgs {
+    int64_t L, B, d, dp, Lm, n3;
+    int causal, layernorm;
+    float alpha, eps;
+    const void *X;
+    bool x_bf16;
+    const bf16_bits_t *Wq, *Wkv, *Wo;
+    const float *gamma;
+    const float *Q, *R;
+    const bf16_bits_t *KV;
+    const void *dU;
+    bool du_bf16;
+    float *dX;
+    bool dx_accumulate;
+    float *dWq, *dWkv, *dWo, *dalpha, *dgamma, *dbeta;
+    void *workspace;
+};
+size_t attention_backward_workspace_bytes(int64_t L, int64_t B, int64_t d, int64_t dp,
+                                          int64_t Lm, int64_t n3);
+hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s);
 
 // One decoding step of a unidirectional layer (step.hip).
 struct StepArgs {

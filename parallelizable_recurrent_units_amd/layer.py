@@ -126,6 +126,30 @@ def attention_forward(shape, cfg, X, Wq, Wkv, Wo, gamma=None, beta=None, KV=None
     return Q, KV, R, U
 
 
+def attention_backward(shape, cfg, X, Wq, Wkv, Wo, Q, KV, R, dU, gamma=None, dX=None,
+                       accumulate_dx=False, ws=None, stream=None):
+    """Gradients of attention_forward for dU: returns a dict with dX (added
+    to the given dX when accumulate_dx), dWq, dWkv, dWo, dalpha [1] and, with
+    layer norm, dgamma and dbeta."""
+    s = B._shape(shape)
+    dev = X.device
+    dp = cfg.d_inner
+    f32 = dict(device=dev, dtype=torch.float32)
+    if dX is None:
+        dX = torch.empty((s.L * s.B, s.d), **f32)
+    out = dict(dX=dX, dWq=torch.empty((dp, s.d), **f32), dWkv=torch.empty((2 * dp, dp), **f32),
+               dWo=torch.empty((s.ndir * 3 * s.d, dp), **f32), dalpha=torch.empty(1, **f32),
+               dgamma=torch.empty(dp, **f32) if cfg.layernorm else None,
+               dbeta=torch.empty(dp, **f32) if cfg.layernorm else None)
+    if ws is None:
+        ws = torch.empty(B.sru_attention_backward_workspace_size(s, cfg), device=dev,
+                         dtype=torch.uint8)
+    B.sru_attention_backward(s, cfg, X, Wq, Wkv, Wo, gamma, Q, KV, R, dU, out["dX"], out["dWq"],
+                             out["dWkv"], out["dWo"], out["dalpha"], out["dgamma"],
+                             out["dbeta"], ws, accumulate_dx, stream)
+    return out
+
+
 def step(shape, x, W, v, b, c=None, h=None, stream=None):
     """One decoding step: (h, c_next) for input rows x [B, d] from state c
     [B, d] (zero when None).  Pass the same tensor as ``c`` each call to carry

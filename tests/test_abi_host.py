@@ -447,3 +447,38 @@ def test_static_scratch_backward_validation(lib):
     text = open(os.path.join(ROOT, "include", "sru.h")).read()
     m = re.search(r"#define\s+SRU_BACKWARD_STATIC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == Bd.SRU_BACKWARD_STATIC_SCRATCH_BYTES
+
+
+def test_attention_backward_validation(lib):
+    """sru_attention_backward: workspace size and its checks, the d' limit,
+    required pointers (gamma and the norm's gradients only with layer norm),
+    and outputs overlapping inputs, all before any device use."""
+    s = sru.SruShape(16, 2, 64, 0, 1.0)
+    cfg = Bd.SruAttnCfg(16, 8, True, True, 0.5, 1e-5)
+    need = Bd.sru_attention_backward_workspace_size(s, cfg)
+    assert need > 0 and need % 256 == 0
+
+    def call(c=cfg, ws_bytes=need, **kw):
+        a = dict(X=Z[0], Wq=Z[1], Wkv=Z[2], Wo=Z[3], gamma=Z[4], Q=Z[5], KV=Z[6], R=Z[7], dU=Z[8],
+                 dX=Z[9], dWq=Z[10], dWkv=Z[11], dWo=Z[12], dalpha=Z[13], dgamma=Z[14],
+                 dbeta=Z[15], ws=Z[15] + (1 << 20))
+        a.update(kw)
+        return lib.sru_attention_backward(
+            ctypes.byref(s), ctypes.byref(c), a["X"], 0, a["Wq"], a["Wkv"], a["Wo"], a["gamma"],
+            a["Q"], a["KV"], a["R"], a["dU"], 0, a["dX"], 0, a["dWq"], a["dWkv"], a["dWo"],
+            a["dalpha"], a["dgamma"], a["dbeta"], a["ws"], ws_bytes, None)
+    assert call() in (sru.SRU_ERR_NO_DEVICE, sru.SRU_OK)
+    assert call(ws_bytes=need - 256) == sru.SRU_ERR_WORKSPACE
+    assert call(ws=None) == sru.SRU_ERR_WORKSPACE
+    assert call(gamma=None) == sru.SRU_ERR_INVALID_ARG
+    assert call(dgamma=None) == sru.SRU_ERR_INVALID_ARG
+    assert call(dX=Z[0]) == sru.SRU_ERR_INVALID_ARG             # dX on top of X
+    assert b"overlaps" in lib.sru_last_error()
+    assert call(dWq=Z[5] + 64) == sru.SRU_ERR_INVALID_ARG       # dWq inside Q
+    no_ln = Bd.SruAttnCfg(16, 8, True, False, 0.5, 1e-5)
+    assert call(c=no_ln, gamma=None, dgamma=None, dbeta=None,
+                ws_bytes=Bd.sru_attention_backward_workspace_size(s, no_ln)) in (
+        sru.SRU_ERR_NO_DEVICE, sru.SRU_OK)
+    wide = Bd.SruAttnCfg(2048, 0, True, False, 0.5, 1e-5)
+    assert call(c=wide, ws_bytes=Bd.sru_attention_backward_workspace_size(s, wide)) == \
+        sru.SRU_ERR_UNSUPPORTED
