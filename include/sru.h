@@ -65,33 +65,42 @@ typedef enum {
     SRU_ERR_UNSUPPORTED = 2,   /* dtype combination not implemented              */
     SRU_ERR_NO_DEVICE = 3,     /* no HIP device visible                          */
     SRU_ERR_LAUNCH = 4,        /* a kernel launch failed                         */
-    SRU_ERR_WORKSPACE = 5      /* workspace NULL or smaller than required        */
+    SRU_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than required        */
+    SRU_STATUS_RANGE_ = -2147483647 - 1   /* not a status; see SRU_DTYPE_RANGE_ */
 } sru_status;
 
-typedef enum { SRU_F32 = 0, SRU_BF16 = 1 } sru_dtype;
-typedef enum { SRU_FWD = 0, SRU_BWD = 1 } sru_pass;
+/* Each enum below ends in a *_RANGE_ member that is not a valid code: it
+ * makes every int32 a representable value of the type, so that a code a C
+ * caller passes outside the listed ones is refused by the argument checks
+ * (SRU_ERR_INVALID_ARG) instead of being undefined in the library's C++. */
+typedef enum { SRU_F32 = 0, SRU_BF16 = 1, SRU_DTYPE_RANGE_ = -2147483647 - 1 } sru_dtype;
+typedef enum { SRU_FWD = 0, SRU_BWD = 1, SRU_PASS_RANGE_ = -2147483647 - 1 } sru_pass;
 typedef enum {
     SRU_PROJ_FWD = 0,        /* C (+)= A W^T  : U = X~ W^T, A = X [L*B, d]           */
     SRU_PROJ_BWD_DATA = 1,   /* C (+)= A W    : dX = dU W, A = dU [L*B, ndir*3*d]    */
-    SRU_PROJ_BWD_DATA_WT = 2 /* C (+)= A Wt^T : as BWD_DATA, with W passed transposed */
+    SRU_PROJ_BWD_DATA_WT = 2, /* C (+)= A Wt^T : as BWD_DATA, with W passed transposed */
+    SRU_PROJ_RANGE_ = -2147483647 - 1
 } sru_proj_op;
 typedef enum {
     SRU_WS_BACKWARD = 1,    /* sru_backward                      */
     SRU_WS_LINEAR_FWD = 2,  /* sru_linear_scan(SRU_FWD, chunk)   */
     SRU_WS_LINEAR_BWD = 3,  /* sru_linear_scan(SRU_BWD, chunk)   */
     SRU_WS_BWD_WEIGHT = 4,  /* sru_project_bwd_weight            */
-    SRU_WS_FACTORED_WEIGHT = 5  /* sru_project_factored_bwd_weight, either
+    SRU_WS_FACTORED_WEIGHT = 5, /* sru_project_factored_bwd_weight, either
                                    gradient; `chunk` carries the inner dimension d' */
+    SRU_WS_RANGE_ = -2147483647 - 1
 } sru_ws_op;
 typedef enum {
     SRU_FACT_Q = 0,      /* Q  [L*B, d']       (+)= X~  . Wq^T   Wq [d', d]        */
     SRU_FACT_U = 1,      /* U  [L*B, ndir*3d]  (+)= Q~  . Wo^T   Wo [ndir*3d, d']  */
     SRU_FACT_BWD_Q = 2,  /* dQ [L*B, d']       (+)= dU~ . Wo                       */
-    SRU_FACT_BWD_X = 3   /* dX [L*B, d]        (+)= dQ~ . Wq                       */
+    SRU_FACT_BWD_X = 3,  /* dX [L*B, d]        (+)= dQ~ . Wq                       */
+    SRU_FACT_RANGE_ = -2147483647 - 1
 } sru_fact_op;
 typedef enum {
     SRU_FACT_WGRAD_Q = 0,   /* dWq [d', d]      (+)= dQ~^T . X~ */
-    SRU_FACT_WGRAD_O = 1    /* dWo [ndir*3d, d'] (+)= dU~^T . Q~ */
+    SRU_FACT_WGRAD_O = 1,   /* dWo [ndir*3d, d'] (+)= dU~^T . Q~ */
+    SRU_FACT_WGRAD_RANGE_ = -2147483647 - 1
 } sru_fact_wgrad_op;
 
 typedef struct {
