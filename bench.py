@@ -85,7 +85,7 @@ def source_digest():
 # ---------------------------------------------------------------------------
 # algorithmic work of each row (every tensor counted once at its dtype)
 # ---------------------------------------------------------------------------
-def row_work(w):
+def row_work(w, x_copy=False):
     L, B, d, nd = w.L, w.B, w.d, w.ndir
     LB = L * B
     xs = 2 if w.x_dtype == "bf16" else 4
@@ -93,8 +93,10 @@ def row_work(w):
     n3 = nd * 3 * d
     rows = {}
     if w.mode == "layer":
+        if x_copy:   # X~ = bf16(X) made first (its own row), the GEMM reads X~
+            rows["a1_round_x"] = dict(bytes=LB * d * (xs + 2))
         rows["a1_projection"] = dict(flops=2 * LB * n3 * d,
-                                     bytes=LB * d * xs + n3 * d * 2 + LB * n3 * 4)
+                                     bytes=LB * d * (2 if x_copy else xs) + n3 * d * 2 + LB * n3 * 4)
         # bf16(dU) x bf16 W, plus the highway dx read and dX written
         rows["a5_projection_bwd_data"] = dict(flops=2 * LB * d * n3,
                                               bytes=LB * n3 * 2 + n3 * d * 2 + 2 * LB * d * 4)
@@ -115,7 +117,7 @@ GEMM_ROWS = ("a1_projection", "a5_projection_bwd_data")
 RECURRENCE_ROWS = ("a2_forward", "a3_a4_backward", "a6_linear_forward", "a7_linear_backward")
 
 
-def next_row_work(w):
+def next_row_work(w, x_copy=False):
     """Rows timed beside the step, not part of it: the weight gradient of
     the projection, dW = bf16(dU)^T X~ (dU's bf16 copy and X read once, dW
     written once)."""
@@ -134,7 +136,8 @@ def next_row_work(w):
                  + LB * di * 4 + LB * d * xs + di * d * 4       # dWq = dQ^T X
                  + LB * n3 * 2 + LB * di * 4 + n3 * di * 4)     # dWo = bf16(dU)^T Q
     rows = {"f1_projection_bwd_weight": dict(flops=2 * LB * n3 * d,
-                                             bytes=LB * n3 * 2 + LB * d * xs + n3 * d * 4),
+                                             bytes=LB * n3 * 2 + LB * d * (2 if x_copy else xs)
+                                             + n3 * d * 4),
             "f3_factored_forward": dict(flops=fwd_flops, bytes=fwd_bytes),
             "f3_factored_backward": dict(flops=bwd_flops, bytes=bwd_bytes)}
     if nd == 1:   # decoding steps (unidirectional layers only)
@@ -265,10 +268,10 @@ def rounds_x_first(w, mode):
 
 
 def training_step_rows(shape, t):
-    """The four row calls of one training step (C-ABI entry points).  With
-    t["xb"] present the projection row rounds X into that bf16 copy first and
-    multiplies the copy; otherwise it reads fp32 X and rounds it to bf16 as it
-    stages it."""
+    """The row calls of one training step (C-ABI entry points).  With
+    t["xb"] present a row of its own rounds X into that bf16 copy and the
+    projection multiplies the copy; otherwise the projection reads fp32 X and
+    rounds it to bf16 as it stages it."""
     from parallelizable_recurrent_units_amd import (SRU_PROJ_BWD_DATA_WT, SRU_PROJ_FWD,
                                                     sru_backward, sru_forward, sru_project,
                                                     sru_round_bf16, sru_transpose_weight)
@@ -277,15 +280,11 @@ def training_step_rows(shape, t):
         sru_transpose_weight(shape, t["W"], t["Wt"])
         sru_project(shape, SRU_PROJ_BWD_DATA_WT, t["dU_lp"], t["Wt"], t["dx"], True)
 
-    def proj():
-        if t.get("xb") is not None:
-            sru_round_bf16(t["x"], t["xb"])
-            sru_project(shape, SRU_PROJ_FWD, t["xb"], t["W"], t["U"])
-        else:
-            sru_project(shape, SRU_PROJ_FWD, t["x"], t["W"], t["U"])
-
-    return [
-        ("a1_projection", proj),
+    xb = t.get("xb")
+    first = [("a1_round_x", lambda: sru_round_bf16(t["x"], xb))] if xb is not None else []
+    return first + [
+        ("a1_projection", lambda: sru_project(shape, SRU_PROJ_FWD, t["x"] if xb is None else xb,
+                                              t["W"], t["U"])),
         ("a2_forward", lambda: sru_forward(shape, t["U"], t["x"], t["v"], t["b"], t["c0"], t["h"],
                                            t["c_seq"], t["c_last"])),
         ("a3_a4_backward", lambda: sru_backward(shape, t["U"], t["x"], t["v"], t["b"], t["c0"],
@@ -509,9 +508,9 @@ def measure(w, nsets, steps, warmup, seed0):
     sets = row_sets_for(w, nsets, seed0)
     ms, rows = time_rows(sets, steps, warmup)
     check_error_words(sets)
-    work = row_work(w)
+    work = row_work(w, w.mode == "layer" and rounds_x_first(w, "auto"))
     per_row = {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
-    beyond = time_beyond(w, sets, steps, warmup)
+    beyond = time_beyond(w, sets, steps, warmup, w.mode == "layer" and rounds_x_first(w, "auto"))
     if beyond:
         per_row["beyond_step"] = beyond
     del sets
@@ -519,14 +518,14 @@ def measure(w, nsets, steps, warmup, seed0):
     return ms, per_row
 
 
-def time_beyond(w, sets, steps, warmup):
+def time_beyond(w, sets, steps, warmup, x_copy=False):
     """{row: measurement} of the rows beyond the step (after the step has run
     on every set, so their inputs hold a step's results)."""
     beyond = [s.beyond for s in sets if getattr(s, "beyond", ())]
     if not beyond:
         return {}
     _, rows = time_rows(beyond, steps, warmup)
-    work = next_row_work(w)
+    work = next_row_work(w, x_copy)
     out = {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
     for n, r in out.items():
         if n.startswith("f4_decode_step_B"):
@@ -636,9 +635,10 @@ def cpu_baseline(w, budget_s=10.0):
 
 # kernel launches of one call of each row (what its event-timed span covers)
 ROW_LAUNCHES = {
-    "a1_projection": ["round_bf16_kernel (X~ = bf16(X)) + gemm_lds (X~ x W, operands copied "
-                      "straight into LDS), or gemm_bf16_mfma (A = fp32 X, rounded to bf16 while "
-                      "staged); see config.projection_x"],
+    "a1_round_x": ["round_bf16_kernel (X~ = bf16(X))"],
+    "a1_projection": ["gemm_lds (X~ x W, operands copied straight into LDS) after a1_round_x, "
+                      "or gemm_bf16_mfma (A = fp32 X, rounded to bf16 while staged); see "
+                      "config.projection_x"],
     "a2_forward": ["fwd_fast (both directions in one grid)"],
     "a3_a4_backward": ["bwd_fast (fp32 inputs, up to 128 steps; both directions in one "
                        "launch when bidirectional and L <= 64, else one per direction, the "
@@ -674,7 +674,7 @@ ROW_LAUNCHES = {
 # for the products that several rows launch (gemm_lds), the row of the
 # dispatch before it: rows run in order a1, a2, a3/a4, a5 in every step.
 ROW_OF_KERNEL = [
-    (r"round_bf16_kernel", "a1_projection"),
+    (r"round_bf16_kernel", "a1_round_x"),
     (r"gemm_bf16_mfma<.*>, float, false, ", "a1_projection"),
     (r"fwd_fast<|fwd_split<|fwd_generic<", "a2_forward"),
     (r"bwd_scan<|bwd_fast<|bwd_generic<|scan_clear|param_reduce", "a3_a4_backward"),
@@ -686,20 +686,27 @@ ROW_ONCE = {"a2_forward": r"fwd_fast<|fwd_split<|fwd_generic<"}   # one dispatch
 def rows_of_dispatches(names):
     """Row of each dispatch (dict id -> row) given {id: kernel name}: a
     kernel named in ROW_OF_KERNEL fixes the row; gemm_lds takes the row of
-    the dispatch before it; anything else (input generation, copies) none."""
+    the dispatch before it; anything else (input generation, copies, the rows
+    timed beyond the step) none.  Projection kernels count only when the
+    forward recurrence comes next, since the same product kernels also serve
+    rows beyond the step."""
     import re
-    out, cur = {}, None
+    out, cur, pending = {}, None, []
     for did in sorted(names):
         n = names[did]
         row = next((r for pat, r in ROW_OF_KERNEL if re.search(pat, n)), None)
-        if row is not None:
-            cur = row
-        elif re.search(r"gemm_lds<", n) and cur in ("a1_projection", "a5_projection_bwd_data"):
-            row = cur
+        if row is None and re.search(r"gemm_lds<", n) and cur in (
+                "a1_round_x", "a1_projection", "a5_projection_bwd_data"):
+            row = "a1_projection" if cur == "a1_round_x" else cur
+        if row in ("a1_round_x", "a1_projection"):
+            pending.append((did, row))
         else:
-            cur = None
-        if row is not None:
-            out[did] = row
+            if row == "a2_forward":
+                out.update(dict(pending))
+            pending = []
+            if row is not None:
+                out[did] = row
+        cur = row
     return out
 
 
@@ -813,10 +820,12 @@ def main():
     print("[bench] timing", file=sys.stderr, flush=True)
     ms, rows = time_rows(row_sets, args.steps, args.warmup)
     check_error_words(row_sets)
-    beyond = {} if args.no_beyond else time_beyond(w, row_sets, args.steps, args.warmup)
+    beyond = {} if args.no_beyond else time_beyond(
+        w, row_sets, args.steps, args.warmup, w.mode == "layer" and rounds_x_first(w, args.x_copy))
     del row_sets
     torch.cuda.empty_cache()
-    work = row_work(w)
+    x_copy = w.mode == "layer" and rounds_x_first(w, args.x_copy)
+    work = row_work(w, x_copy)
     per_row = {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
     dominant = max(rows, key=lambda n: rows[n])
     digest = source_digest()
@@ -824,6 +833,12 @@ def main():
     roof["kernel"] = dominant
     roof["launches_per_call"] = ROW_LAUNCHES.get(dominant)
     roof["traffic"] = traffic_for(w.name, dominant, digest)
+    gemm_roof = None
+    if "a1_projection" in rows and dominant != "a1_projection":
+        gemm_roof = dict(roofline_of("a1_projection", work["a1_projection"], rows["a1_projection"]))
+        gemm_roof["kernel"] = "a1_projection"
+        gemm_roof["launches_per_call"] = ROW_LAUNCHES.get("a1_projection")
+        gemm_roof["traffic"] = traffic_for(w.name, "a1_projection", digest)
     step_bytes = sum(r["bytes"] for r in work.values())
     rec_rows = [n for n in per_row if n in RECURRENCE_ROWS]
     rec_bytes = sum(work[n]["bytes"] for n in rec_rows)
@@ -861,6 +876,7 @@ def main():
         "rows": per_row,
         "beyond_step": beyond,
         "roofline": roof,
+        "roofline_projection_gemm": gemm_roof,
         "source_digest": digest,
     }
     if args.copy_probe_mib:
