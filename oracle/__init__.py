@@ -76,10 +76,12 @@ def _load():
     lib.sru_oracle_project_bwd_weight.restype = None
     lib.sru_oracle_project_bwd_weight.argtypes = [_i64, _i64, _i64, _dp, _fp, ctypes.c_int, _dp]
     lib.sru_oracle_chain_forward.restype = None
-    lib.sru_oracle_chain_forward.argtypes = [_i64, ctypes.c_int, d, _dp, _dp, _dp, _dp,
+    lib.sru_oracle_chain_forward.argtypes = [_i64, ctypes.c_int, ctypes.c_int, d,
+                                             _dp, _dp, _dp, _dp,
                                              d, d, d, d, d, _dp, _dp, _dp]
     lib.sru_oracle_chain_backward.restype = None
-    lib.sru_oracle_chain_backward.argtypes = [_i64, ctypes.c_int, d, _dp, _dp, _dp, _dp,
+    lib.sru_oracle_chain_backward.argtypes = [_i64, ctypes.c_int, ctypes.c_int, d,
+                                              _dp, _dp, _dp, _dp,
                                               d, d, d, d, d, _dp, _dp, d,
                                               _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
     lib.sru_oracle_forward.restype = None
@@ -239,8 +241,11 @@ def project_bwd_weight(G, X, round_x: bool) -> np.ndarray:
     return out
 
 
-def chain_forward(uf, ur, ux, x, vf, vr, bf, br, c0, alpha, direction=0):
-    """One chain (Eqs. 2-5).  Returns (h[L], c[L], c_last)."""
+def chain_forward(uf, ur, ux, x, vf, vr, bf, br, c0, alpha, direction=0, linear=False):
+    """One chain (Eqs. 2-5).  Returns (h[L], c[L], c_last).
+
+    linear=True: the linear mode, whose gates do not see the state (vf, vr
+    ignored; the v*c terms are not formed)."""
     uf, p1 = _f64(uf)
     ur, p2 = _f64(ur)
     ux, p3 = _f64(ux)
@@ -249,15 +254,19 @@ def chain_forward(uf, ur, ux, x, vf, vr, bf, br, c0, alpha, direction=0):
     h = np.empty(L)
     c = np.empty(L)
     cl = ctypes.c_double()
-    _load().sru_oracle_chain_forward(L, int(direction), float(alpha), p1, p2, p3, p4,
+    _load().sru_oracle_chain_forward(L, int(direction), int(bool(linear)), float(alpha),
+                                     p1, p2, p3, p4,
                                      float(vf), float(vr), float(bf), float(br), float(c0),
                                      h.ctypes.data_as(_dp), c.ctypes.data_as(_dp),
                                      ctypes.byref(cl))
     return h, c, cl.value
 
 
-def chain_backward(uf, ur, ux, x, vf, vr, bf, br, c0, c, dh, dc_last, alpha, direction=0):
-    """Chain rule through one chain.  Returns a dict of per-step and scalar grads."""
+def chain_backward(uf, ur, ux, x, vf, vr, bf, br, c0, c, dh, dc_last, alpha, direction=0,
+                   linear=False):
+    """Chain rule through one chain.  Returns a dict of per-step and scalar grads.
+
+    linear=True as for chain_forward: the state adjoint has no gate terms."""
     uf, p1 = _f64(uf)
     ur, p2 = _f64(ur)
     ux, p3 = _f64(ux)
@@ -268,7 +277,7 @@ def chain_backward(uf, ur, ux, x, vf, vr, bf, br, c0, c, dh, dc_last, alpha, dir
     outs = {k: np.empty(L) for k in ("duf", "dur", "dux", "dx_hw")}
     sc = {k: ctypes.c_double() for k in ("dvf", "dvr", "dbf", "dbr", "dc0")}
     _load().sru_oracle_chain_backward(
-        L, int(direction), float(alpha), p1, p2, p3, p4,
+        L, int(direction), int(bool(linear)), float(alpha), p1, p2, p3, p4,
         float(vf), float(vr), float(bf), float(br), float(c0), pc, pd, float(dc_last),
         *(outs[k].ctypes.data_as(_dp) for k in ("duf", "dur", "dux", "dx_hw")),
         *(ctypes.byref(sc[k]) for k in ("dvf", "dvr", "dbf", "dbr", "dc0")))
@@ -280,12 +289,13 @@ def chain_backward(uf, ur, ux, x, vf, vr, bf, br, c0, c, dh, dc_last, alpha, dir
 def forward(U, x, v, b, c0, alpha):
     """Whole-tensor forward.  U [L,B,ndir,3,d] -> h, c [L,B,ndir,d], c_last [ndir,B,d].
 
-    U may be fp32 values (given U) or the oracle's own double projection."""
+    U may be fp32 values (given U) or the oracle's own double projection.
+    v None: the linear mode (gates that do not see the state)."""
     U, pu = _f64(U)
     L, B, ndir, three, d = U.shape
     assert three == 3
     x, px = _f32(x)
-    v, pv = _f32(v)
+    v, pv = _optf32(v)
     b, pb = _f32(b)
     c0, pc0 = _optf32(c0)
     h = np.empty((L, B, ndir, d))
@@ -298,11 +308,13 @@ def forward(U, x, v, b, c0, alpha):
 
 
 def backward(U, x, v, b, c0, c, dh, dc_last, alpha):
-    """Whole-tensor backward given the oracle's own forward states ``c``."""
+    """Whole-tensor backward given the oracle's own forward states ``c``.
+
+    v None: the linear mode, as for forward."""
     U, pu = _f64(U)
     L, B, ndir, _, d = U.shape
     x, px = _f32(x)
-    v, pv = _f32(v)
+    v, pv = _optf32(v)
     b, pb = _f32(b)
     c0, pc0 = _optf32(c0)
     c, pc = _f64(c)

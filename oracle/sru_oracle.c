@@ -39,8 +39,11 @@
  *     pages print none);
  *   - the linear mode ("Parallelizing Legendre Memory Unit Training",
  *     abstract: linear recurrences can be trained in parallel) is the same
- *     recurrence with v = v' = 0.  The oracle evaluates it sequentially; it
- *     never chunks.
+ *     recurrence with v = v' = 0.  These are structural zeros: the gates do
+ *     not see the state, so no v * c term is formed at all (with a NaN state,
+ *     0 * NaN would be NaN although the linear cell's gates do not depend on
+ *     it).  For finite values this is the v = 0 evaluation exactly.  The
+ *     oracle evaluates it sequentially; it never chunks.
  *
  * All arithmetic is in double.  Inputs arrive as float (fp32, or bf16 values
  * widened exactly to fp32) and are widened once.
@@ -425,9 +428,11 @@ void sru_oracle_project_bwd_weight(int64_t M, int64_t N, int64_t K,
  * index t = 0..L-1.  dir = 0 walks t = 0..L-1, dir = 1 walks t = L-1..0.
  *   uf, ur, ux : the three slots of U for this channel (Eqs. 2, 3, 4)
  *   x          : the layer input for this channel (highway term, Eq. 5)
+ * linear = 1: the linear mode (the gates do not see the state; vf, vr are
+ * then ignored).
  * Outputs h[t], c[t] (the state after step t) and the final state.
  */
-void sru_oracle_chain_forward(int64_t L, int dir, double alpha,
+void sru_oracle_chain_forward(int64_t L, int dir, int linear, double alpha,
                               const double *uf, const double *ur,
                               const double *ux, const double *x,
                               double vf, double vr, double bf, double br,
@@ -437,8 +442,9 @@ void sru_oracle_chain_forward(int64_t L, int dir, double alpha,
     for (int64_t s = 0; s < L; ++s) {
         int64_t t = dir ? (L - 1 - s) : s;
         double prev = state;
-        double f = oracle_sigmoid(uf[t] + vf * prev + bf);          /* Eq. 2 */
-        double r = oracle_sigmoid(ur[t] + vr * prev + br);          /* Eq. 3 */
+        double seen = linear ? 0.0 : prev;    /* the state the gates see */
+        double f = oracle_sigmoid(uf[t] + vf * seen + bf);          /* Eq. 2 */
+        double r = oracle_sigmoid(ur[t] + vr * seen + br);          /* Eq. 3 */
         state = f * prev + (1.0 - f) * ux[t];                       /* Eq. 4 */
         h[t] = r * state + (1.0 - r) * alpha * x[t];                /* Eq. 5 */
         c[t] = state;
@@ -451,9 +457,10 @@ void sru_oracle_chain_forward(int64_t L, int dir, double alpha,
  * order of the direction's walk).  c[] is the forward state sequence, dh[]
  * the gradient of h, dc_last the gradient of the final state.  Outputs the
  * gradients of uf, ur, ux, of x through the highway term only, the chain's
- * contributions to dv, dv', db, db' and the gradient of c0.
+ * contributions to dv, dv', db, db' and the gradient of c0.  linear as for
+ * the forward: the state adjoint then has no terms through the gates.
  */
-void sru_oracle_chain_backward(int64_t L, int dir, double alpha,
+void sru_oracle_chain_backward(int64_t L, int dir, int linear, double alpha,
                                const double *uf, const double *ur,
                                const double *ux, const double *x,
                                double vf, double vr, double bf, double br,
@@ -472,8 +479,9 @@ void sru_oracle_chain_backward(int64_t L, int dir, double alpha,
             prev = c0;
         else
             prev = c[dir ? (t + 1) : (t - 1)];
-        double f = oracle_sigmoid(uf[t] + vf * prev + bf);
-        double r = oracle_sigmoid(ur[t] + vr * prev + br);
+        double seen = linear ? 0.0 : prev;
+        double f = oracle_sigmoid(uf[t] + vf * seen + bf);
+        double r = oracle_sigmoid(ur[t] + vr * seen + br);
         double ct = c[t];
         /* h = r*c + (1-r)*alpha*x */
         double dc = gc + dh[t] * r;
@@ -492,7 +500,7 @@ void sru_oracle_chain_backward(int64_t L, int dir, double alpha,
         sbf += dzf;
         sbr += dzr;
         /* prev reaches the loss through c (via f*prev), f and r */
-        gc = dc * f + dzf * vf + dzr * vr;
+        gc = linear ? dc * f : dc * f + dzf * vf + dzr * vr;
     }
     *dvf = svf; *dvr = svr; *dbf = sbf; *dbr = sbr;
     *dc0 = gc;
@@ -504,7 +512,8 @@ void sru_oracle_chain_backward(int64_t L, int dir, double alpha,
  *                               given fp32/bf16 values widened, or the
  *                               oracle's own projection)
  *   x      [L, B, d]            shared by both directions
- *   v, b   [ndir, 2, d]         row 0 = f gate, row 1 = r gate
+ *   v, b   [ndir, 2, d]         row 0 = f gate, row 1 = r gate; v NULL is
+ *                               the linear mode (gates without the state)
  *   c0     [ndir, B, d]         NULL means zeros
  *   h, c   [L, B, ndir, d]
  *   c_last [ndir, B, d]
@@ -544,8 +553,9 @@ void sru_oracle_forward(int64_t L, int64_t B, int64_t d, int ndir, double alpha,
             int64_t dl = ch / (B * d), b = (ch / d) % B, j = ch % d;
             gather_chain(L, B, d, ndir, dl, b, j, U, x, uf, ur, ux, xx);
             double cl;
-            sru_oracle_chain_forward(L, (int)dl, alpha, uf, ur, ux, xx,
-                                     v[(dl * 2 + 0) * d + j], v[(dl * 2 + 1) * d + j],
+            sru_oracle_chain_forward(L, (int)dl, v == NULL, alpha, uf, ur, ux, xx,
+                                     v ? v[(dl * 2 + 0) * d + j] : 0.0f,
+                                     v ? v[(dl * 2 + 1) * d + j] : 0.0f,
                                      bias[(dl * 2 + 0) * d + j], bias[(dl * 2 + 1) * d + j],
                                      c0 ? (double)c0[(dl * B + b) * d + j] : 0.0,
                                      hh, cc, &cl);
@@ -593,8 +603,9 @@ void sru_oracle_backward(int64_t L, int64_t B, int64_t d, int ndir, double alpha
                 gh[t] = dh[o];
             }
             double dvf, dvr, dbf, dbr, g0;
-            sru_oracle_chain_backward(L, (int)dl, alpha, uf, ur, ux, xx,
-                                      v[(dl * 2 + 0) * d + j], v[(dl * 2 + 1) * d + j],
+            sru_oracle_chain_backward(L, (int)dl, v == NULL, alpha, uf, ur, ux, xx,
+                                      v ? v[(dl * 2 + 0) * d + j] : 0.0f,
+                                      v ? v[(dl * 2 + 1) * d + j] : 0.0f,
                                       bias[(dl * 2 + 0) * d + j], bias[(dl * 2 + 1) * d + j],
                                       c0 ? (double)c0[(dl * B + b) * d + j] : 0.0,
                                       cc, gh,

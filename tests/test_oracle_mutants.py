@@ -28,14 +28,21 @@ MUTANTS = [
     ("bf16 ties away from zero",
      "(lower == 0x8000u && (upper & 1u))", "(lower == 0x8000u)"),
     ("Eq. 2 with the reset gate's v",
-     "double f = oracle_sigmoid(uf[t] + vf * prev + bf);          /* Eq. 2 */",
-     "double f = oracle_sigmoid(uf[t] + vr * prev + bf);          /* Eq. 2 */"),
+     "double f = oracle_sigmoid(uf[t] + vf * seen + bf);          /* Eq. 2 */",
+     "double f = oracle_sigmoid(uf[t] + vr * seen + bf);          /* Eq. 2 */"),
     ("Eq. 4 with f and 1 - f swapped",
      "state = f * prev + (1.0 - f) * ux[t];", "state = (1.0 - f) * prev + f * ux[t];"),
     ("Eq. 5 without alpha",
      "h[t] = r * state + (1.0 - r) * alpha * x[t];", "h[t] = r * state + (1.0 - r) * x[t];"),
     ("state adjoint without the reset-gate term",
-     "gc = dc * f + dzf * vf + dzr * vr;", "gc = dc * f + dzf * vf;"),
+     "gc = linear ? dc * f : dc * f + dzf * vf + dzr * vr;",
+     "gc = linear ? dc * f : dc * f + dzf * vf;"),
+    ("linear-mode gates that see the state in the backward",
+     "double seen = linear ? 0.0 : prev;\n        double f = oracle_sigmoid(uf[t] + vf * seen + bf);\n",
+     "double seen = prev;\n        double f = oracle_sigmoid(uf[t] + vf * seen + bf);\n"),
+    ("linear-mode state adjoint with the gate terms",
+     "gc = linear ? dc * f : dc * f + dzf * vf + dzr * vr;",
+     "gc = dc * f + dzf * vf + dzr * vr;"),
     ("highway gradient without alpha",
      "dx_hw[t] = dh[t] * (1.0 - r) * alpha;", "dx_hw[t] = dh[t] * (1.0 - r);"),
     ("candidate gradient with f for 1 - f",

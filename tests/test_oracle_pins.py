@@ -289,6 +289,55 @@ def test_linear_mode_time_varying_gate_sum_form():
     assert np.max(np.abs(h - (r * ref + (1 - r) * alpha * x))) < 1e-13
 
 
+def test_linear_mode_is_the_v0_recurrence_on_finite_input():
+    """The linear mode (v None: gates that do not see the state) equals the
+    recurrence at v = 0 value for value on finite input, forward and backward."""
+    rng = np.random.default_rng(9)
+    L, B, d, nd, al = 7, 2, 3, 2, 0.8
+    U, x, v, b, c0 = rand_problem(rng, L, B, d, nd)
+    z = np.zeros_like(v)
+    dh = rng.standard_normal((L, B, nd, d)).astype(np.float32)
+    dcl = rng.standard_normal((nd, B, d)).astype(np.float32)
+    f0 = oracle.forward(U, x, z, b, c0, al)
+    f1 = oracle.forward(U, x, None, b, c0, al)
+    for k in f0:
+        assert np.array_equal(f0[k], f1[k]), k
+    g0 = oracle.backward(U, x, z, b, c0, f0["c"], dh, dcl, al)
+    g1 = oracle.backward(U, x, None, b, c0, f1["c"], dh, dcl, al)
+    for k in g0:
+        assert np.array_equal(g0[k], g1[k]), k
+
+
+@pytest.mark.parametrize("direction", [0, 1])
+def test_linear_mode_gradients_that_do_not_read_the_state(direction):
+    """In the linear mode the state adjoint obeys gc[t-1] = f[t] (gc[t] +
+    r[t] dh[t]): it, the candidate's gradient dc (1 - f), the highway dx and
+    dc0 never read the state.  A NaN initial state (so every state is NaN)
+    must leave them exactly as with c0 = 0, while the gate gradients, which
+    read the state, turn NaN.  Evaluating v = 0 as a multiplied zero would
+    spoil them all through 0 * NaN."""
+    rng = np.random.default_rng(10 + direction)
+    L, al = 9, 1.1
+    uf, ur, ux, x, dh = (rng.standard_normal(L) for _ in range(5))
+    bf, br, dcl = 0.2, -0.1, 0.7
+    h, c, cl = oracle.chain_forward(uf, ur, ux, x, 0.0, 0.0, bf, br, np.nan, al, direction,
+                                    linear=True)
+    assert np.isnan(c).all() and np.isnan(h).all() and np.isnan(cl)
+    g = oracle.chain_backward(uf, ur, ux, x, 0.0, 0.0, bf, br, np.nan, c, dh, dcl, al,
+                              direction, linear=True)
+    _, c_ok, _ = oracle.chain_forward(uf, ur, ux, x, 0.0, 0.0, bf, br, 0.0, al, direction,
+                                      linear=True)
+    g_ok = oracle.chain_backward(uf, ur, ux, x, 0.0, 0.0, bf, br, 0.0, c_ok, dh, dcl, al,
+                                 direction, linear=True)
+    for k in ("dux", "dx_hw", "dc0"):
+        assert np.array_equal(g[k], g_ok[k]) and np.isfinite(g_ok[k]).all(), k
+    assert np.isnan(g["duf"]).all() and np.isnan(g["dur"]).all()
+    # the general cell at v = 0 carries the NaN state into every gradient
+    gv = oracle.chain_backward(uf, ur, ux, x, 0.0, 0.0, bf, br, np.nan, c, dh, dcl, al,
+                               direction)
+    assert np.isnan(gv["dux"]).any()
+
+
 # --------------------------------------------------------------------------
 # brute force, L <= 4
 # --------------------------------------------------------------------------
