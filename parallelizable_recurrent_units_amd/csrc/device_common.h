@@ -46,17 +46,24 @@ template <> __device__ __forceinline__ float load_as_f32<bf16_bits>(const bf16_b
 //
 // gate_scaled takes y = -z log2(e) (callers fold -log2(e) into their
 // parameters once).  y is capped at 64 so that 2^y g stays finite: for very
-// negative z, g = 2^-64 and gc = 1.  A NaN pre-activation takes the cap too
-// (the gate saturates closed) instead of propagating.
+// negative z, g = 2^-64 and gc = 1.  The cap is the IEEE 754-2019 minimum
+// (one v_minimum3_f32), which returns NaN for a NaN operand, so a NaN
+// pre-activation gives a NaN gate, as sigma(NaN) does, rather than a closed
+// one (fminf would return the cap).
 struct Gate {
     float g, gc;
 };
 
 constexpr float kNegLog2e = -1.4426950408889634f;
 
+__device__ __forceinline__ float cap_exponent(float y)
+{
+    return __builtin_elementwise_minimum(y, 64.0f);
+}
+
 __device__ __forceinline__ Gate gate_scaled(float y)
 {
-    const float e = __builtin_amdgcn_exp2f(fminf(y, 64.0f));
+    const float e = __builtin_amdgcn_exp2f(cap_exponent(y));
     const float g = __builtin_amdgcn_rcpf(1.0f + e);
     return {g, e * g};
 }
@@ -70,7 +77,7 @@ __device__ __forceinline__ Gate gate(float z) { return gate_scaled(z * kNegLog2e
 // y is that of gate_scaled; e q stays finite for |q| < 2^64.
 __device__ __forceinline__ float gate_blend(float y, float p, float q)
 {
-    const float e = __builtin_amdgcn_exp2f(fminf(y, 64.0f));
+    const float e = __builtin_amdgcn_exp2f(cap_exponent(y));
     const float g = __builtin_amdgcn_rcpf(1.0f + e);
     return g * fmaf(e, q, p);
 }
