@@ -223,10 +223,16 @@ sru_status sru_project_factored_bwd_weight(const sru_shape *shape, int64_t d_inn
  * Wv's), Wo [ndir*3d, d']: bf16 only.  "~" marks operands rounded to bf16
  * (nearest even) as the bf16 MFMA products load them; the attention weights
  * are rounded to bf16 before they multiply V.  The softmax and the
- * residual / normalisation are fp32.
+ * residual / normalisation are fp32.  For d' in {64, 128, 256, 512} the
+ * scores never leave the chip: the weights are then exp(s - m) for a running
+ * maximum m that is raised in steps (so each lies in [0, 2^8]), rounded to
+ * bf16, and A is their product with V divided by the sum of the same rounded
+ * weights; other d' normalise the weights before rounding them.
  * gamma, beta: required when cfg->layernorm, else ignored (may be NULL).
  * workspace: sru_attention_workspace_size(shape, cfg) bytes, 256-byte
- *   aligned: the scores [B, L, Lm + L] (fp32), the weights (bf16) and A.
+ *   aligned: for d' in {64, 128, 256, 512} a transposed copy of V (bf16, the
+ *   keys padded to a multiple of 32); otherwise the scores [B, L, Lm + L]
+ *   (fp32), the weights (bf16) and A.
  * Outputs must not overlap each other or the inputs.
  */
 sru_status sru_attention_forward(const sru_shape *shape, const sru_attn_cfg *cfg,

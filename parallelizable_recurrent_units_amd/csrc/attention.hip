@@ -192,6 +192,530 @@ hipError_t launch_residual(const AttnArgs &a, const float *O, hipStream_t s)
     return hipGetLastError();
 }
 
+// ---- fused forward: scores, online softmax, weights x values, residual, norm ----
+//
+// For d' in {64, 128, 256, 512} the forward's attention core runs in one
+// kernel that keeps the scores and weights on chip.  A workgroup of four waves
+// owns 64 queries of one sequence b and walks the visible keys in tiles of 32.
+// Wave w holds queries 32 (w % 2) .. + 31 and channel half h = w / 2 of the
+// d' channels; per tile it
+//   forms its half of S^T = K Q~^T over its channels (v_mfma_f32_32x32x16_bf16,
+//     keys as rows, queries as columns, so a lane's accumulators belong to one
+//     query), and adds the other half from its partner wave through LDS,
+//   runs the online softmax per query (the running maximum is raised, and the
+//     sums and accumulators rescaled, only when a tile's maximum exceeds it by
+//     more than 2^8: the unnormalised weights stay <= 2^8),
+//   accumulates its channel half of O^T += V^T P^T (the weights rounded to
+//     bf16 as the operand; the normaliser sums the same rounded weights),
+// and it ends with A = O / sum, R = Q + alpha A and the layer normalisation
+// (the row sums exchanged between the two halves), all in registers.  R is
+// the only output.  Both waves of a pair form the same scores and weights
+// from the same operands, bit for bit.
+//
+// K tiles come straight from the [Lk, B, 2d'] rows; V is first transposed
+// once per call into V^T tiles [B, Lk / 32, d', 32] (each tile one contiguous
+// block, keys padded with zeros to a multiple of 32), so that both go from
+// memory into LDS by global_load_lds_dwordx4 in whole 1 KB pieces, without
+// registers.  Two LDS stages: the next tile is copied while the current one
+// is used, and the tile after next is touched into L2.
+//
+// Within a 16-key step of the weights x values product, lane half hi of the
+// B operand takes keys 8 hi .. 8 hi + 7.  The S^T accumulator of lane half hi
+// holds rows 8 i + 4 hi + j (i, j = 0..3), so the A operand row r of the score
+// product reads K row 16 (i / 2) + 8 hi + 4 (i % 2) + j (r = 8 i + 4 hi + j):
+// accumulator values 8 s .. 8 s + 7 of a lane are then exactly keys
+// 16 s + 8 hi .. + 7, the B operand of step s.
+constexpr int kFusedKT = 32;      // keys per tile
+constexpr int kFusedBQ = 64;      // queries per workgroup
+constexpr float kFusedLazy = 8.0f;
+
+typedef __bf16 fbf16x8 __attribute__((ext_vector_type(8)));
+typedef float ff32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t fu32x4 __attribute__((ext_vector_type(4)));
+
+int64_t fused_keys_padded(int64_t Lk) { return (Lk + kFusedKT - 1) / kFusedKT * kFusedKT; }
+
+// The fused kernel takes d' in {64, 128, 256, 512}, with the per-lane copy
+// offsets of a tile (32 key rows of [Lk, B, 2d'] bf16) and the key counts
+// inside 31 bits.
+bool fused_forward_ok(int64_t L, int64_t B, int64_t dp, int64_t Lm)
+{
+    if (dp != 64 && dp != 128 && dp != 256 && dp != 512) return false;
+    const int64_t Lkp = fused_keys_padded(Lm + L), lim = (int64_t)1 << 31;
+    return kFusedKT * B * 4 * dp < lim && Lkp < lim;
+}
+
+template <int DP> struct FusedLay {
+    static constexpr int DPH = DP / 2;                  // channels per wave
+    static constexpr int KROW = 2 * DP;                 // bytes of one key row of K
+    // d' = 512: a K row is one 1 KB request; the rows sit 16 bytes apart
+    // beyond their length, so that the 16 rows a quarter-wave reads fall on 16
+    // different bank groups and every fragment of a lane is its first one plus
+    // a constant (no per-fragment address arithmetic).  Other d': rows packed,
+    // the pieces swizzled by fk_swz.
+    static constexpr bool PADK = DP == 512;
+    static constexpr int KPITCH = PADK ? KROW + 16 : KROW;
+    static constexpr int K_BYTES = kFusedKT * KPITCH;   // the tile's K rows
+    static constexpr int V_BYTES = DP * 2 * kFusedKT;   // the tile's V^T block
+    static constexpr int SB = K_BYTES + V_BYTES;        // one stage
+    static constexpr int QK = kFusedKT * KROW / 1024;   // 1 KB requests for K
+    static constexpr int REQ = QK + V_BYTES / 1024;
+    static constexpr int IPW = REQ / 4;                 // requests per wave
+    static constexpr int XB = 4 * 4096;                 // partial scores, 4 KB per wave
+    static_assert(IPW * 4 == REQ && QK == 2 * IPW, "K requests on waves 0, 1");
+};
+
+// Position keys of the 16-byte pieces (XOR on the piece index).  K rows: the
+// 16 rows a quarter-wave reads at once (16 u .. 16 u + 15 in some order) land
+// on 16 different 16-byte bank groups.  V^T rows (64 bytes, four to a bank
+// line): the 16 consecutive rows of a quarter-wave likewise.
+template <int DP> __device__ __forceinline__ int fk_swz(int row)
+{
+    if constexpr (DP == 64) return (row >> 1) & 7;   // 128-byte rows, two to a bank line
+    return row & 15;
+}
+__device__ __forceinline__ int fv_swz(int row) { return (row >> 2) & 3; }
+
+// V^T tiles [B, Lkp / 32, dp, 32] from the V half of KV [Lk, B, 2 dp], zeros
+// for keys past Lk.  64 keys x 64 channels per block through LDS.
+__global__ __launch_bounds__(256) void attn_v_transpose(const bf16_bits *__restrict__ KV,
+                                                        bf16_bits *__restrict__ Vt, int64_t Lk,
+                                                        int64_t Lkp, int64_t B, int64_t dp)
+{
+    __shared__ bf16_bits tile[64][64 + 2];
+    const int64_t k0 = (int64_t)blockIdx.x * 64, e0 = (int64_t)blockIdx.y * 64, b = blockIdx.z;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int idx = tid + 256 * i, kk = idx >> 3, ec = (idx & 7) * 8;
+        const int64_t k = k0 + kk;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (k < Lk) v = *(const uint4 *)(KV + (k * B + b) * 2 * dp + dp + e0 + ec);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            tile[kk][ec + 2 * j] = (bf16_bits)(w[j] & 0xffffu);
+            tile[kk][ec + 2 * j + 1] = (bf16_bits)(w[j] >> 16);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int idx = tid + 256 * i, ee = idx >> 3, kc = (idx & 7) * 8;
+        const int64_t k = k0 + kc;
+        if (k >= Lkp) continue;
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            w[j] = (uint32_t)tile[kc + 2 * j][ee] | ((uint32_t)tile[kc + 2 * j + 1][ee] << 16);
+        bf16_bits *dst = Vt + ((b * (Lkp / kFusedKT) + k / kFusedKT) * dp + e0 + ee) * kFusedKT +
+                         k % kFusedKT;
+        *(uint4 *)dst = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+struct FusedArgs {
+    int64_t L, B, Lm, Lk, Lkp;
+    int causal, layernorm;
+    float alpha, eps;
+    const float *Q;
+    const bf16_bits *KV, *Vt;
+    const float *gamma, *beta;
+    float *R;
+};
+
+template <int DP>
+__global__ __launch_bounds__(256, 1) void attn_fwd_fused(FusedArgs a)
+{
+    typedef FusedLay<DP> Lay;
+    constexpr int SB = Lay::SB, IPW = Lay::IPW, DPH = Lay::DPH;
+    constexpr int NKS = DPH / 16, NOB = DPH / 32;       // score k-steps, O blocks per wave
+    // two stages, the partial scores, then 1 KB that the L2 prefetches land in
+    __shared__ __attribute__((aligned(16))) char smem[2 * SB + Lay::XB + 1024];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar registers
+    const int qg = wave & 1, h = wave >> 1, r32 = lane & 31, hi = lane >> 5;
+    const int64_t L = a.L, B = a.B, Lk = a.Lk, Lkp = a.Lkp;
+
+    // workgroup -> (sequence, query block); consecutive workgroups go to
+    // different XCDs, so a sequence's blocks are gathered on one XCD (whose
+    // L2 then serves its keys and values to all of them)
+    const int64_t nqb = (L + kFusedBQ - 1) / kFusedBQ, nwg = nqb * B;
+    int64_t id = blockIdx.x;
+    if (nwg % 8 == 0) id = (id % 8) * (nwg / 8) + id / 8;
+    const int64_t b = id / nqb, qb = id % nqb;
+    const int64_t t0w = qb * kFusedBQ + 32 * qg, t = t0w + r32;
+    const bool tv = t < L;
+    auto keys_of = [&](int64_t tq) -> int64_t {   // keys query tq sees
+        return a.causal ? (a.Lm + tq + 1 < Lk ? a.Lm + tq + 1 : Lk) : Lk;
+    };
+    const int64_t tl = (qb + 1) * kFusedBQ < L ? (qb + 1) * kFusedBQ - 1 : L - 1;
+    const int ntiles = (int)((keys_of(tl) + kFusedKT - 1) / kFusedKT);
+    const int nk_wave = t0w < L ? (int)keys_of(t0w + 31 < L ? t0w + 31 : L - 1) : 0;
+    const int nk_q = (int)keys_of(t);
+
+    // Q~ fragments (B operand of S^T): query r32, channels DPH h + 16 ks + 8 hi .. + 7
+    fbf16x8 qf[NKS];
+    const float *qrow = a.Q + (t * B + b) * DP + DPH * h;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        fu32x4 u = {0u, 0u, 0u, 0u};
+        if (tv) {
+            const float4 x0 = *(const float4 *)(qrow + 16 * ks + 8 * hi);
+            const float4 x1 = *(const float4 *)(qrow + 16 * ks + 8 * hi + 4);
+            u[0] = pack_bf16x2(x0.x, x0.y);
+            u[1] = pack_bf16x2(x0.z, x0.w);
+            u[2] = pack_bf16x2(x1.x, x1.y);
+            u[3] = pack_bf16x2(x1.z, x1.w);
+        }
+        qf[ks] = __builtin_bit_cast(fbf16x8, u);
+    }
+
+    // The tile's copies: waves 0, 1 copy K rows, waves 2, 3 the V^T block.
+    // Every request is a per-lane 32-bit byte offset from a wave-uniform base
+    // (the tile's first K row of sequence b, or the tile's V^T block).
+    const bool kwave = wave < 2;
+    // V^T request q: rows 16 (q - QK) + lane / 4; the piece swizzle of such a
+    // row is (lane / 16) % 4, so one offset serves every request
+    const uint32_t voff_v = (uint32_t)((lane >> 2) * 64 + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
+    // K request q (packed rows): rows q RPQ + lane / CPR
+    constexpr int CPR = DP / 8, RPQ = 1024 / Lay::KROW;    // pieces per row, rows per request
+    uint32_t koff[Lay::PADK ? 1 : IPW];
+    int krow_of[Lay::PADK ? 1 : IPW];
+#pragma unroll
+    for (int i = 0; i < (Lay::PADK ? 1 : IPW); ++i) {
+        const int row = (wave * IPW + i) * RPQ + lane / CPR;
+        const int c = (lane % CPR) ^ fk_swz<DP>(row);
+        krow_of[i] = row;
+        koff[i] = (uint32_t)(row * B * 4 * DP + 16 * c);
+    }
+    const char *kbase = (const char *)(a.KV + b * 2 * DP);
+    const char *vbase = (const char *)(a.Vt + b * (Lkp / kFusedKT) * DP * kFusedKT);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    char *xbuf = smem + 2 * SB;                          // partial scores [wave][16][64 lanes]
+    // L2 prefetch of a later tile: the workgroups of a sequence walk its keys
+    // in step, so without it every tile's first touch of a line is a miss that
+    // all of them wait for.  Each lane copies 16 bytes of one 128-byte line
+    // (every line of the tile's K rows and V^T block) into a 1 KB LDS area
+    // nobody reads; PF requests per wave, always issued (past the last item the
+    // last line again), so that the waits can count them.
+    constexpr int PF_ITEMS = DP, PF = (PF_ITEMS + 255) / 256;
+    auto prefetch = [&](int kt) {
+        kt = kt < ntiles ? kt : ntiles - 1;
+        const uint32_t dummy = __builtin_amdgcn_readfirstlane(lds0 + 2 * SB + Lay::XB);
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            int j = tid + 256 * i;
+            j = j < PF_ITEMS ? j : PF_ITEMS - 1;
+            const void *src;
+            if (j < DP / 2) {
+                constexpr int LPR = DP / 64;   // 128-byte lines per key row
+                int64_t key = (int64_t)kt * kFusedKT + j / LPR;
+                key = key < Lk ? key : Lk - 1;
+                src = a.KV + (key * B + b) * 2 * DP + (j % LPR) * 64;
+            } else {
+                src = vbase + (int64_t)kt * Lay::V_BYTES + (j - DP / 2) * 128;
+            }
+            dma16(src, dummy);
+        }
+    };
+    auto issue = [&](int kt, int st) {
+        const uint32_t ldss = lds0 + st * SB;
+        if (kwave) {
+            const char *base = kbase + (int64_t)kt * kFusedKT * B * 4 * DP;
+            // rows past the last key (the last tile) repeat it; they are masked
+            const int last = (int)(Lk - 1 - (int64_t)kt * kFusedKT);
+            if constexpr (Lay::PADK) {   // request q = K row q
+                const uint32_t rstride = (uint32_t)(B * 4 * DP);   // bytes between key rows
+#pragma unroll
+                for (int i = 0; i < IPW; ++i) {
+                    int q = wave * IPW + i;
+                    q = q < last ? q : last;
+                    dma16s(base, 16 * lane + (uint32_t)q * rstride,
+                           __builtin_amdgcn_readfirstlane(ldss + (wave * IPW + i) * Lay::KPITCH));
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < IPW; ++i) {
+                    const int over = krow_of[i] > last ? krow_of[i] - last : 0;
+                    dma16s(base, koff[i] - (uint32_t)(over * B * 4 * DP),
+                           __builtin_amdgcn_readfirstlane(ldss + (wave * IPW + i) * 1024));
+                }
+            }
+        } else {
+            const char *base = vbase + (int64_t)kt * Lay::V_BYTES;
+#pragma unroll
+            for (int i = 0; i < IPW; ++i) {
+                const int q = wave * IPW + i - Lay::QK;
+                dma16s(base, voff_v + (uint32_t)q * 1024u,
+                       __builtin_amdgcn_readfirstlane(ldss + Lay::K_BYTES + q * 1024));
+            }
+        }
+    };
+
+    ff32x16 o[NOB];
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[ob][e] = 0.0f;
+    float mrun = -INFINITY, lsum = 0.0f;
+    const float csc = kLog2e / sqrtf((float)DP);
+
+    // the K row this lane reads for the score product (see above), and the
+    // byte offsets of its fragment pieces
+    const int ri = r32 >> 3, rhi = (r32 >> 2) & 1, rj = r32 & 3;
+    const int krow = 16 * (ri >> 1) + 8 * rhi + 4 * (ri & 1) + rj;
+    const int c0 = 2 * (DPH / 16) * h + hi;              // first piece of this wave's channels
+    const int fk = fk_swz<DP>(krow);
+    // byte offset of K piece c0 + 2 ks of row krow: kof + 32 ks when padded
+    const int kof = Lay::PADK ? krow * Lay::KPITCH + 16 * c0 : krow * Lay::KPITCH;
+    auto kpiece = [&](int ks) -> int {
+        return Lay::PADK ? kof + 32 * ks : kof + (((c0 + 2 * ks) ^ fk) << 4);
+    };
+    // V^T row DPH h + 32 ob + r32, keys 16 s + 8 hi ..: vo[s] + 2048 ob
+    // ((DPH h + 32 ob) is a multiple of 4, so the row's swizzle is r32's)
+    const int fv = fv_swz(r32);
+    const int vo0 = Lay::K_BYTES + (DPH * h + r32) * 64 + ((hi ^ fv) << 4);
+    const int vo1 = Lay::K_BYTES + (DPH * h + r32) * 64 + (((2 + hi) ^ fv) << 4);
+    // the wave's fewest visible keys (its first query): tiles below it need no mask
+    const int nk_min = t0w < L ? (int)keys_of(t0w) : 0;
+
+    // One tile: wait for its copies, request the next, the score half, the
+    // exchange with the partner wave, scaled and masked scores in v[].
+    // Returns false when no query of the wave sees the tile.
+    float v[16];
+    bool full = false;   // the tile is visible to every query of the wave: no mask
+    auto scores = [&](int kt) -> bool {
+        const int st = kt & 1;
+        // this wave's copies of tile kt are done once at most the PF
+        // prefetch requests issued after them are in flight
+        if (kt == 0)
+            wait_vmcnt<0>();
+        else
+            wait_vmcnt<PF>();
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+        if (kt + 1 < ntiles) {
+            issue(kt + 1, st ^ 1);
+            prefetch(kt + 3);
+        }
+        const bool active = kt * kFusedKT < nk_wave;     // the same in both waves of the pair
+        ff32x16 sacc;
+        if (active) {
+            const char *kst = smem + st * SB;
+            // two accumulation chains (even and odd k-steps), added at the end
+            ff32x16 s1;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sacc[e] = s1[e] = 0.0f;
+            fbf16x8 kf[4];
+#pragma unroll
+            for (int j = 0; j < 4 && j < NKS; ++j) kf[j] = *(const fbf16x8 *)(kst + kpiece(j));
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const fbf16x8 cur = kf[ks & 3];
+                if (ks + 4 < NKS) kf[ks & 3] = *(const fbf16x8 *)(kst + kpiece(ks + 4));
+                if (ks & 1)
+                    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], s1, 0, 0, 0);
+                else
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], sacc, 0, 0, 0);
+            }
+            sacc += s1;
+            // this half to the partner: [wave][4 pieces][64 lanes][4 floats]
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                *(float4 *)(xbuf + ((wave * 4 + q4) * 64 + lane) * 16) =
+                    make_float4(sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]);
+        }
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+        if (!active) return false;
+        const int pw = wave ^ 2;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 x = *(const float4 *)(xbuf + ((pw * 4 + q4) * 64 + lane) * 16);
+            sacc[4 * q4] += x.x;
+            sacc[4 * q4 + 1] += x.y;
+            sacc[4 * q4 + 2] += x.z;
+            sacc[4 * q4 + 3] += x.w;
+        }
+        // accumulator value 4 i + j: key kt*32 + 16 (i / 2) + 8 hi + 4 (i % 2) + j
+        full = (kt + 1) * kFusedKT <= nk_min;
+        if (full) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) v[e] = sacc[e] * csc;
+        } else {
+            const int kb = kt * kFusedKT + 8 * hi;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int key = kb + 16 * (e >> 3) + (e & 7);
+                v[e] = key < nk_q ? sacc[e] * csc : -INFINITY;
+            }
+        }
+        return true;
+    };
+    auto tile_max = [&]() -> float {
+        float mt = v[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mt = fmaxf(mt, v[e]);
+        return fmaxf(mt, __shfl_xor(mt, 32, 64));
+    };
+    // weights (rounded to bf16) and O^T += V^T P^T for this wave's channels
+    auto accumulate = [&](int st) {
+        const char *vst = smem + st * SB;
+        fu32x4 pu[2];
+        float ps = 0.0f;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x0 = v[8 * s2 + 2 * i], x1 = v[8 * s2 + 2 * i + 1];
+                float p0 = __builtin_amdgcn_exp2f(x0 - mrun), p1 = __builtin_amdgcn_exp2f(x1 - mrun);
+                if (!full) {   // masked scores are -inf; mrun may be too
+                    p0 = x0 > -INFINITY ? p0 : 0.0f;
+                    p1 = x1 > -INFINITY ? p1 : 0.0f;
+                }
+                pu[s2][i] = pack_bf16x2(p0, p1);
+                ps += __uint_as_float(pu[s2][i] << 16) + __uint_as_float(pu[s2][i] & 0xffff0000u);
+            }
+        lsum += ps;
+        const fbf16x8 pf0 = __builtin_bit_cast(fbf16x8, pu[0]);
+        const fbf16x8 pf1 = __builtin_bit_cast(fbf16x8, pu[1]);
+        // V^T piece of row DPH h + 32 ob + r32 holding keys 16 s + 8 hi ..
+        fbf16x8 vf[4];
+        // step n = s NOB + ob: consecutive MFMAs update different blocks
+        auto vread = [&](int n) {
+            const int ob = n % NOB, s2 = n / NOB;
+            return *(const fbf16x8 *)(vst + (s2 ? vo1 : vo0) + ob * 32 * 64);
+        };
+#pragma unroll
+        for (int j = 0; j < 4 && j < 2 * NOB; ++j) vf[j] = vread(j);
+#pragma unroll
+        for (int n = 0; n < 2 * NOB; ++n) {
+            const fbf16x8 cur = vf[n & 3];
+            if (n + 4 < 2 * NOB) vf[n & 3] = vread(n + 4);
+            o[n % NOB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, n < NOB ? pf0 : pf1, o[n % NOB],
+                                                                0, 0, 0);
+        }
+    };
+
+    prefetch(1);
+    prefetch(2);
+    issue(0, 0);
+    // tile 0 holds key 0, which every query sees: its maximum starts mrun
+    if (scores(0)) {
+        mrun = tile_max();
+        accumulate(0);
+    }
+    int kt = 1;
+    while (kt < ntiles) {
+        // the common case: the running maximum stays within 2^8 of each
+        // tile's maximum, and O is never rescaled
+        bool raise = false;
+        for (; kt < ntiles; ++kt) {
+            if (!scores(kt)) continue;
+            const float mt = tile_max();
+            if (__any(mt > mrun + kFusedLazy)) {
+                raise = true;
+                break;
+            }
+            accumulate(kt & 1);
+        }
+        if (!raise) break;
+        // a tile raised some query's maximum: rescale, then finish the tile
+        const float mt = tile_max();
+        const float mnew = mt > mrun + kFusedLazy ? mt : mrun;
+        const float f = __builtin_amdgcn_exp2f(mrun - mnew);
+        lsum *= f;
+#pragma unroll
+        for (int ob = 0; ob < NOB; ++ob) o[ob] *= f;
+        mrun = mnew;
+        accumulate(kt & 1);
+        ++kt;
+    }
+    wait_vmcnt<0>();   // no copy may land in LDS after the workgroup ends
+
+    // A = O / sum, R = Q + alpha A, layer norm.  Lane holds query r32 and
+    // channels DPH h + 32 ob + 8 i + 4 hi + j (value 4 i + j of block ob).
+    float l = lsum + __shfl_xor(lsum, 32, 64);
+    const float inv = 1.0f / l;
+    float sum = 0.0f;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float4 qv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (tv) qv = *(const float4 *)(qrow + 32 * ob + 8 * i + 4 * hi);
+            o[ob][4 * i] = fmaf(a.alpha, o[ob][4 * i] * inv, qv.x);
+            o[ob][4 * i + 1] = fmaf(a.alpha, o[ob][4 * i + 1] * inv, qv.y);
+            o[ob][4 * i + 2] = fmaf(a.alpha, o[ob][4 * i + 2] * inv, qv.z);
+            o[ob][4 * i + 3] = fmaf(a.alpha, o[ob][4 * i + 3] * inv, qv.w);
+            sum += (o[ob][4 * i] + o[ob][4 * i + 1]) + (o[ob][4 * i + 2] + o[ob][4 * i + 3]);
+        }
+    if (a.layernorm) {
+        // the row's sums: this lane pair's half, then the partner wave's half
+        float *xs = (float *)xbuf;                       // [wave][32 queries]
+        auto row_total = [&](float part) -> float {
+            part += __shfl_xor(part, 32, 64);
+            __builtin_amdgcn_s_barrier();                // the last reads of xs are done
+            if (hi == 0) xs[wave * 32 + r32] = part;
+            wait_lgkm0();
+            __builtin_amdgcn_s_barrier();
+            const float other = xs[(wave ^ 2) * 32 + r32];
+            return h == 0 ? part + other : other + part;
+        };
+        const float mean = row_total(sum) / (float)DP;
+        float sq = 0.0f;
+#pragma unroll
+        for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sq += (o[ob][e] - mean) * (o[ob][e] - mean);
+        const float rs = 1.0f / sqrtf(row_total(sq) / (float)DP + a.eps);
+#pragma unroll
+        for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e0 = DPH * h + 32 * ob + 8 * i + 4 * hi;
+                const float4 gm = *(const float4 *)(a.gamma + e0);
+                const float4 bt = *(const float4 *)(a.beta + e0);
+                o[ob][4 * i] = fmaf(gm.x * (o[ob][4 * i] - mean), rs, bt.x);
+                o[ob][4 * i + 1] = fmaf(gm.y * (o[ob][4 * i + 1] - mean), rs, bt.y);
+                o[ob][4 * i + 2] = fmaf(gm.z * (o[ob][4 * i + 2] - mean), rs, bt.z);
+                o[ob][4 * i + 3] = fmaf(gm.w * (o[ob][4 * i + 3] - mean), rs, bt.w);
+            }
+    }
+    if (tv) {
+        float *rrow = a.R + (t * B + b) * DP + DPH * h;
+#pragma unroll
+        for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *(float4 *)(rrow + 32 * ob + 8 * i + 4 * hi) =
+                    make_float4(o[ob][4 * i], o[ob][4 * i + 1], o[ob][4 * i + 2], o[ob][4 * i + 3]);
+    }
+}
+
+hipError_t launch_fused(const AttnArgs &a, bf16_bits *Vt, hipStream_t s)
+{
+    const int64_t Lk = a.Lm + a.L, Lkp = fused_keys_padded(Lk);
+    hipLaunchKernelGGL(attn_v_transpose, dim3((unsigned)((Lkp + 63) / 64), (unsigned)(a.dp / 64),
+                                              (unsigned)a.B),
+                       dim3(256), 0, s, (const bf16_bits *)a.KV, Vt, Lk, Lkp, a.B, a.dp);
+    FusedArgs f;
+    f.L = a.L, f.B = a.B, f.Lm = a.Lm, f.Lk = Lk, f.Lkp = Lkp;
+    f.causal = a.causal, f.layernorm = a.layernorm;
+    f.alpha = a.alpha, f.eps = a.eps;
+    f.Q = a.Q, f.KV = (const bf16_bits *)a.KV, f.Vt = Vt;
+    f.gamma = a.gamma, f.beta = a.beta, f.R = a.R;
+    const dim3 grid((unsigned)(((a.L + kFusedBQ - 1) / kFusedBQ) * a.B)), block(256);
+    switch (a.dp) {
+    case 64: hipLaunchKernelGGL(attn_fwd_fused<64>, grid, block, 0, s, f); break;
+    case 128: hipLaunchKernelGGL(attn_fwd_fused<128>, grid, block, 0, s, f); break;
+    case 256: hipLaunchKernelGGL(attn_fwd_fused<256>, grid, block, 0, s, f); break;
+    default: hipLaunchKernelGGL(attn_fwd_fused<512>, grid, block, 0, s, f); break;
+    }
+    return hipGetLastError();
+}
+
 // ---- backward -----------------------------------------------------------
 
 constexpr int kResRowsPerWave = 16;   // rows of attn_residual_bwd per wave (64 per block)
@@ -620,6 +1144,8 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
 
 size_t attention_workspace_bytes(int64_t L, int64_t B, int64_t dp, int64_t Lm)
 {
+    if (fused_forward_ok(L, B, dp, Lm))   // V^T only
+        return (size_t)B * (size_t)dp * (size_t)fused_keys_padded(Lm + L) * 2;
     return ws_layout(L, B, dp, Lm).total;
 }
 
@@ -649,8 +1175,12 @@ hipError_t launch_attention_forward(const AttnArgs &a, hipStream_t s)
         g.C = (float *)(KV + Lm * B * 2 * dp), g.accumulate = false;
         if ((e = launch_gemm_bf16_out(g, s)) != hipSuccess) return e;
     }
-    if ((e = attend(L, B, dp, Lm, a.causal, a.Q, KV, S, P, O, s)) != hipSuccess) return e;
-    if ((e = launch_residual(a, O, s)) != hipSuccess) return e;
+    if (fused_forward_ok(L, B, dp, Lm)) {
+        if ((e = launch_fused(a, (bf16_bits *)ws, s)) != hipSuccess) return e;
+    } else {
+        if ((e = attend(L, B, dp, Lm, a.causal, a.Q, KV, S, P, O, s)) != hipSuccess) return e;
+        if ((e = launch_residual(a, O, s)) != hipSuccess) return e;
+    }
     {   // U [L*B, ndir*3d] = R~ Wo^T, fp32 or rounded to bf16
         GemmArgs g;
         g.M = LB, g.N = a.n3, g.K = dp;

@@ -82,4 +82,47 @@ __device__ __forceinline__ float gate_blend(float y, float p, float q)
     return g * fmaf(e, q, p);
 }
 
+// ---- memory-to-LDS copies (global_load_lds_dwordx4) ----------------------
+
+// Wait until at most N_ of this wave's vector memory requests are in flight
+// (the copies below count as such requests until their data is in LDS).
+template <int N_> __device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N_ >= 0 && N_ < 64, "vmcnt is 6 bits");
+    // vmcnt[3:0] | expcnt[6:4] = 7 | lgkmcnt[11:8] = 15 | vmcnt[5:4] at [15:14]
+    __builtin_amdgcn_s_waitcnt((N_ & 15) | (7 << 4) | (15 << 8) | ((N_ >> 4) << 14));
+}
+
+// Wait for every LDS access of this wave.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// 16 bytes per lane from gptr into LDS at lds_base + 16 * lane (lds_base is
+// wave-uniform; M0 carries it).  The instruction has no register result; the
+// caller accounts for its completion with wait_vmcnt.
+__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_base), "v"(gptr)
+                 : "memory");
+}
+
+// The same with the address split into a wave-uniform base (SGPR pair) and a
+// per-lane unsigned 32-bit byte offset: no 64-bit address arithmetic per lane.
+// The base must be wave-uniform; it is read from the first lane so that it
+// can live in scalar registers.
+__device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, uint32_t lds_base)
+{
+    // (readfirstlane returns int: each half goes through uint32_t, so the low
+    // half is zero-extended, never sign-extended into the high half)
+    const uint64_t p = (uint64_t)(uintptr_t)sbase;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    const uint64_t u = ((uint64_t)hi << 32) | (uint64_t)lo;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"((const void *)(uintptr_t)u)
+                 : "memory");
+}
+
 }  // namespace sru

@@ -592,28 +592,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(
 // once.  (fp32 A is not taken: converted as its fragments
 // are read, by every wave that reads them, it is slower than the register-
 // staged kernel, which converts each element once.)
-template <int N_> __device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N_ >= 0 && N_ < 64, "vmcnt is 6 bits");
-    // vmcnt[3:0] | expcnt[6:4] = 7 | lgkmcnt[11:8] = 15 | vmcnt[5:4] at [15:14]
-    __builtin_amdgcn_s_waitcnt((N_ & 15) | (7 << 4) | (15 << 8) | ((N_ >> 4) << 14));
-}
-
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
-
 // position key of a 128-byte LDS row (see above)
 __device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & 7; }
-
-// 16 bytes per lane from gptr into LDS at lds_base + 16 * lane (lds_base is
-// wave-uniform; M0 carries it).  The instruction has no register result; the
-// caller accounts for its completion with wait_vmcnt.
-__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_base)
-{
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :
-                 : "s"(lds_base), "v"(gptr)
-                 : "memory");
-}
 
 template <int BM_, int BN_, int NS_, int WGM_, int WGN_, int MINB_>
 struct LdsCfg {

@@ -96,8 +96,22 @@ CASES = [(8, 3, 64, 1, 16, 0, True, False, 0.5),
          (1, 2, 64, 1, 16, 5, True, True, 1.0),
          (5, 2, 64, 1, 16, 0, False, False, 1.0)]
 
+# d' in {64, 128, 256, 512} takes the fused kernel (scores, softmax, weights x
+# values, residual and norm in one pass over key tiles of 32): query blocks
+# of 64 with ragged ends, context rows not a multiple of 32, both masks,
+# layer norm on and off, workgroup counts that are and are not multiples of
+# 8 (the XCD grouping), one query over one key
+FUSED_CASES = [(100, 3, 256, 1, 64, 37, True, True, 0.8),
+               (130, 4, 512, 1, 128, 70, True, False, 1.0),
+               (70, 8, 512, 2, 128, 0, False, True, 0.5),
+               (200, 2, 1024, 1, 256, 100, True, True, 1.0),
+               (129, 2, 2048, 1, 512, 64, True, True, 1.0),
+               (64, 16, 1024, 1, 512, 31, False, True, 0.7),
+               (1, 1, 256, 1, 64, 0, True, True, 1.0),
+               (33, 2, 512, 1, 128, 5, True, False, 2.0)]
 
-@pytest.mark.parametrize("L,B,d,nd,dp,Lm,causal,ln,alpha", CASES)
+
+@pytest.mark.parametrize("L,B,d,nd,dp,Lm,causal,ln,alpha", CASES + FUSED_CASES)
 def test_attention_forward(L, B, d, nd, dp, Lm, causal, ln, alpha):
     inp = workloads.attention_inputs(L, B, d, nd, dp, Lm, seed=1000 + L + dp)
     print(f"case L={L} B={B} d={d} nd={nd} d'={dp} Lm={Lm} causal={causal} ln={ln}", flush=True)
