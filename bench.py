@@ -171,7 +171,7 @@ def attention_work(w):
     # backward: the forward's three attention products again (recomputed),
     # then dR = dU Wo, dWo = dU^T R, dP = dO V^T, dQ += dS' K, dK = dS'^T Q,
     # dV = P^T dO (visible pairs), dWkv = dKV^T Q, dQ += dKV Wkv, dWq = dQ^T X,
-    # dX = dQ Wq; bytes: X, the weights, Q, KV, R, dU (fp32) and dX read or
+    # dX = dQ Wq; bytes: X, the weights, Q, KV, R, dU (bf16) and dX read or
     # written once, the weight gradients written once
     seg = B * (L * (L + 1) // 2)                                # pairs within the segment
     bflops = (4 * pairs * dp                                   # S and A recomputed
@@ -180,7 +180,7 @@ def attention_work(w):
               + 8 * LB * dp * dp                               # dWkv, dQ += dKV Wkv
               + 4 * LB * dp * d)                               # dWq, dX
     bbytes = (LB * d * 4 + (dp * d + 2 * dp * dp + n3 * dp) * 2 + 2 * LB * dp * 4
-              + (Lm + L) * B * 2 * dp * 2 + LB * n3 * 4 + LB * d * 4
+              + (Lm + L) * B * 2 * dp * 2 + LB * n3 * 2 + LB * d * 4
               + (dp * d + 2 * dp * dp + n3 * dp) * 4)
     return {"f2_attention_forward": dict(flops=flops, bytes=byts),
             "f2_attention_backward": dict(flops=bflops, bytes=bbytes)}
@@ -411,8 +411,10 @@ def attention_rows(w, shape, g):
     Q, R = torch.empty((L * B, dp), **f32), torch.empty((L * B, dp), **f32)
     U = torch.empty((L, B, nd, 3, d), device="cuda", dtype=torch.bfloat16)
     ws = torch.empty(sru_attention_workspace_size(shape, cfg), device="cuda", dtype=torch.uint8)
-    # the backward takes this forward's Q, KV and R, and dU ~ N(0, 1)
-    dU = torch.randn((L * B, nd * 3 * d), generator=g, **f32)
+    # the backward takes this forward's Q, KV and R, and dU ~ N(0, 1) in bf16:
+    # the copy the recurrence's backward writes for the products (the kernels
+    # round an fp32 dU to bf16 as they load it, so the result is the same)
+    dU = torch.randn((L * B, nd * 3 * d), generator=g, **f32).to(torch.bfloat16)
     dX = torch.empty((L * B, d), **f32)
     grads = [torch.empty(n, **f32) for n in (dp * d, 2 * dp * dp, nd * 3 * d * dp, 1, dp, dp)]
     wsb = torch.empty(sru_attention_backward_workspace_size(shape, cfg), device="cuda",
@@ -655,12 +657,13 @@ ROW_LAUNCHES = {
     "f4_decode_step_B1": [f"step_cell x {DECODE_STEPS} (one call per step, state in place, "
                           "replayed from a HIP graph)"],
     "f2_attention_forward": ["gemm_bf16_mfma (Q = X Wq^T)", "gemm_bf16_mfma ([K|V] = Q Wkv^T, "
-                             "bf16 out)", "gemm_bf16_mfma (scores, one batch per sequence)",
-                             "attn_softmax", "gemm_bf16_mfma (weights x V, batched)",
-                             "attn_residual (R = layernorm(Q + alpha A))",
+                             "bf16 out)", "attn_v_transpose (V^T tiles)",
+                             "attn_fwd_fused (scores, online softmax, weights x V, "
+                             "R = layernorm(Q + alpha A))",
                              "gemm_bf16_mfma (U = R Wo^T)"],
     "f2_attention_backward": ["the forward's scores, softmax and A again (3 launches)",
-                              "gemm_bf16_mfma (dR = dU Wo)", "gemm + split_reduce (dWo)",
+                              "transpose16 (Wo^T) + gemm_lds (dR = dU Wo, bf16 dU)",
+                              "gemm + split_reduce (dWo)",
                               "attn_residual_bwd + attn_part_reduce", "gemm (dP = dO V^T)",
                               "attn_softmax_bwd", "gemm (dQ += dS' K)", "gemm TN (dK, dV)",
                               "gemm + split_reduce (dWkv)", "gemm (dQ += dKV Wkv)",

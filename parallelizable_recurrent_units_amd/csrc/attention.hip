@@ -718,7 +718,7 @@ hipError_t launch_fused(const AttnArgs &a, bf16_bits *Vt, hipStream_t s)
 
 // ---- backward -----------------------------------------------------------
 
-constexpr int kResRowsPerWave = 16;   // rows of attn_residual_bwd per wave (64 per block)
+constexpr int kResRowsPerWave = 4;    // rows of attn_residual_bwd per wave (16 per block)
 
 // The residual and normalisation backward, one wave per row, kResRowsPerWave
 // rows per wave.  From dR (the gradient of R) it recomputes S = Q + alpha O
@@ -823,24 +823,47 @@ __global__ __launch_bounds__(256) void attn_residual_bwd(
     }
 }
 
-// dgamma, dbeta (when ln) and dalpha: the blocks' partial rows added in block
-// order (bit-reproducible run to run).
-__global__ __launch_bounds__(256) void attn_part_reduce(const float *__restrict__ part,
-                                                        int64_t nblk, int64_t dp,
-                                                        float *__restrict__ dgamma,
-                                                        float *__restrict__ dbeta,
-                                                        float *__restrict__ dalpha)
+// dgamma, dbeta (when ln) and dalpha: the blocks' partial rows added in a
+// fixed order (bit-reproducible run to run).  A block of 16 waves owns 64
+// consecutive entries: wave w adds the partial rows of residue w (mod 16) in
+// increasing order, eight loads in flight, then the 16 sums are added in
+// wave order.
+constexpr int kPartWaves = 16;
+
+__global__ __launch_bounds__(64 * kPartWaves) void attn_part_reduce(const float *__restrict__ part,
+                                                                    int64_t nblk, int64_t dp,
+                                                                    float *__restrict__ dgamma,
+                                                                    float *__restrict__ dbeta,
+                                                                    float *__restrict__ dalpha)
 {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= 2 * dp + 1) return;
+    constexpr int U = 8;
+    __shared__ float red[kPartWaves][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t n = 2 * dp + 1, e = (int64_t)blockIdx.x * 64 + lane;
     float acc = 0.0f;
-    for (int64_t b = 0; b < nblk; ++b) acc += part[b * (2 * dp + 1) + e];
+    if (e < n) {
+        int64_t b = wv;
+        for (; b + (U - 1) * kPartWaves < nblk; b += U * kPartWaves) {
+            float v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = part[(b + u * kPartWaves) * n + e];
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc += v[u];
+        }
+        for (; b < nblk; b += kPartWaves) acc += part[b * n + e];
+    }
+    red[wv][lane] = acc;
+    __syncthreads();
+    if (wv != 0 || e >= n) return;
+    float t = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < kPartWaves; ++w) t += red[w][lane];
     if (e < dp) {
-        if (dgamma) dgamma[e] = acc;
+        if (dgamma) dgamma[e] = t;
     } else if (e < 2 * dp) {
-        if (dbeta) dbeta[e - dp] = acc;
+        if (dbeta) dbeta[e - dp] = t;
     } else {
-        *dalpha = acc;
+        *dalpha = t;
     }
 }
 
@@ -905,6 +928,71 @@ __global__ __launch_bounds__(256) void attn_softmax_bwd(const float *__restrict_
     }
 }
 
+// The same for rows whose length is a multiple of 4 (Lk <= 256 NV): each lane
+// holds four consecutive keys per group of 256, S and dP are read with 16-byte
+// loads up front, the weights are exponentiated once, and dS' leaves as
+// 8-byte stores.
+template <int NV>
+__global__ __launch_bounds__(256) void attn_softmax_bwd_v4(const float *__restrict__ S,
+                                                           const float *__restrict__ dP,
+                                                           const float *__restrict__ D,
+                                                           bf16_bits *__restrict__ dSp, int64_t rows,
+                                                           int64_t L, int64_t B, int64_t Lk,
+                                                           int64_t Lm, int causal, float scale)
+{
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const int64_t b = row / L, t = row % L;
+    const int64_t nk = causal ? (Lm + t + 1 < Lk ? Lm + t + 1 : Lk) : Lk;
+    const float4 *s4 = (const float4 *)(S + row * Lk), *g4 = (const float4 *)(dP + row * Lk);
+    const float c = scale * kLog2e;
+    const float d = D[t * B + b];
+    float sv[NV][4], gv[NV][4];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int64_t j = 4 * (lane + 64 * i);
+        float4 x = make_float4(0.0f, 0.0f, 0.0f, 0.0f), y = x;
+        if (j < Lk) {
+            x = s4[lane + 64 * i];
+            y = g4[lane + 64 * i];
+        }
+        sv[i][0] = x.x, sv[i][1] = x.y, sv[i][2] = x.z, sv[i][3] = x.w;
+        gv[i][0] = y.x, gv[i][1] = y.y, gv[i][2] = y.z, gv[i][3] = y.w;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t j = 4 * (lane + 64 * i) + e;
+            sv[i][e] = j < nk ? sv[i][e] * c : -INFINITY;
+            mx = fmaxf(mx, sv[i][e]);
+        }
+    mx = wave_max(mx);
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t j = 4 * (lane + 64 * i) + e;
+            sv[i][e] = j < nk ? __builtin_amdgcn_exp2f(sv[i][e] - mx) : 0.0f;
+            sum += sv[i][e];
+        }
+    const float inv = 1.0f / wave_sum(sum);
+    bf16_bits *o = dSp + row * Lk;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int64_t j = 4 * (lane + 64 * i);
+        if (j >= Lk) continue;
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            r[e] = j + e < nk ? sv[i][e] * inv * (gv[i][e] - d) * scale : 0.0f;
+        *(uint2 *)(o + j) = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
+    }
+}
+
 struct WsLayout {
     size_t s_off, p_off, o_off, total;   // bytes
 };
@@ -951,7 +1039,7 @@ hipError_t attend(int64_t L, int64_t B, int64_t dp, int64_t Lm, int causal, cons
 // Workspace of the backward (bytes, each region 256-byte aligned).
 struct BwdLayout {
     size_t s_off, p_off, dp_off, dsp_off, o_off, dr_off, dq_off, do_off, dkv_off, d_off,
-        part_off, wg_off, total;
+        part_off, wg_off, wot_off, total;
     int64_t nblk;
 };
 
@@ -978,6 +1066,7 @@ BwdLayout bwd_layout(int64_t L, int64_t B, int64_t d, int64_t dp, int64_t Lm, in
     w.dkv_off = take(LB * 2 * dp * 4);
     w.d_off = take(LB * 4);
     w.part_off = take((size_t)w.nblk * (size_t)(2 * dp + 1) * 4);
+    w.wot_off = take((size_t)n3 * (size_t)dp * 2);                 // Wo^T, for a bf16 dU
     size_t wg = wgrad_workspace_bytes(n3, dp, (int64_t)LB);
     const size_t w2 = wgrad_workspace_bytes(2 * dp, dp, (int64_t)LB);
     const size_t w3 = wgrad_workspace_bytes(dp, d, (int64_t)LB);
@@ -1018,11 +1107,20 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
     hipError_t e;
     // the forward's weights and A, recomputed from Q and KV
     if ((e = attend(L, B, dp, Lm, a.causal, a.Q, KV, S, P, O, s)) != hipSuccess) return e;
-    {   // dR [LB, d'] = dU Wo (Wo [n3, d'] read as [K, N])
+    {   // dR [LB, d'] = dU Wo: with a bf16 dU, Wo^T [d', n3] is formed first so
+        // that both operands are bf16 rows along the reduction (the kernel that
+        // copies them straight into LDS); with an fp32 dU, Wo is read as [K, N]
         GemmArgs g;
         g.M = LB, g.N = dp, g.K = n3;
         g.A = a.dU, g.a_bf16 = a.du_bf16;
-        g.Bm = a.Wo, g.b_bf16 = true, g.b_kn = true;
+        g.b_bf16 = true;
+        if (a.du_bf16) {
+            bf16_bits *WoT = (bf16_bits *)(ws + w.wot_off);
+            if ((e = launch_transpose(n3, dp, a.Wo, WoT, true, s)) != hipSuccess) return e;
+            g.Bm = WoT, g.b_kn = false;
+        } else {
+            g.Bm = a.Wo, g.b_kn = true;
+        }
         g.C = dR, g.accumulate = false;
         if ((e = launch_gemm(g, s)) != hipSuccess) return e;
     }
@@ -1048,9 +1146,10 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
         else
             SRU_RES_BWD(16);
 #undef SRU_RES_BWD
-        hipLaunchKernelGGL(attn_part_reduce, dim3((unsigned)((2 * dp + 1 + 255) / 256)), dim3(256),
-                           0, s, part, w.nblk, dp, a.layernorm ? a.dgamma : nullptr,
-                           a.layernorm ? a.dbeta : nullptr, a.dalpha);
+        hipLaunchKernelGGL(attn_part_reduce, dim3((unsigned)((2 * dp + 1 + 63) / 64)),
+                           dim3(64 * kPartWaves), 0, s, part, w.nblk, dp,
+                           a.layernorm ? a.dgamma : nullptr, a.layernorm ? a.dbeta : nullptr,
+                           a.dalpha);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     {   // dP_b [L, Lk] = dO~_b V~_b^T
@@ -1069,7 +1168,17 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
 #define SRU_SM_BWD(NR)                                                                           \
     hipLaunchKernelGGL((attn_softmax_bwd<NR>), grid, block, 0, s, S, dP, D, dSp, rows, L, B, Lk, \
                        Lm, a.causal, scale)
-        if (Lk <= 256)
+#define SRU_SM_BWD4(NV)                                                                          \
+    hipLaunchKernelGGL((attn_softmax_bwd_v4<NV>), grid, block, 0, s, S, dP, D, dSp, rows, L, B,  \
+                       Lk, Lm, a.causal, scale)
+        if (Lk % 4 == 0 && Lk <= 2048) {
+            if (Lk <= 512)
+                SRU_SM_BWD4(2);
+            else if (Lk <= 1024)
+                SRU_SM_BWD4(4);
+            else
+                SRU_SM_BWD4(8);
+        } else if (Lk <= 256)
             SRU_SM_BWD(4);
         else if (Lk <= 512)
             SRU_SM_BWD(8);
@@ -1079,6 +1188,7 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
             SRU_SM_BWD(32);
         else
             SRU_SM_BWD(0);
+#undef SRU_SM_BWD4
 #undef SRU_SM_BWD
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }

@@ -119,3 +119,37 @@ def test_attention_backward_accumulates_dx_and_repeats_bit_for_bit():
     assert torch.equal(b["dX"], dX0 + dX0)
     for k in ("dWq", "dWkv", "dWo", "dalpha", "dgamma", "dbeta"):
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("L,B,d,nd,dp,Lm", [(64, 4, 64, 1, 32, 16), (33, 3, 100, 2, 25, 7),
+                                            (100, 2, 256, 1, 64, 40)])
+def test_attention_backward_bf16_du_matches_fp32_du(L, B, d, nd, dp, Lm):
+    """A bf16 dU (the copy the recurrence's backward writes) gives the
+    gradients of the fp32 dU it was rounded from: every product rounds dU to
+    bf16 as it loads it, so only the products' accumulation order differs
+    (the bf16 dU takes W_o^T and the kernel that copies operands straight into
+    LDS when n3 is a multiple of 64).  Within 1e-4 normwise."""
+    import torch
+    shape = SruShape(L, B, d, nd == 2, 1.0)
+    cfg = SruAttnCfg(dp, Lm, True, True, 0.8, 1e-5)
+    inp = workloads.attention_inputs(L, B, d, nd, dp, Lm, seed=2200 + L)
+    KV = torch.empty((Lm + L, B, 2 * dp), device="cuda", dtype=torch.bfloat16)
+    KV[:Lm] = torch.cat([dev(inp["Kmem"], inp["Kmem_bits"]), dev(inp["Vmem"], inp["Vmem_bits"])],
+                        dim=2)
+    g = dict(gamma=dev(inp["gamma"]), beta=dev(inp["beta"]))
+    X, Wq = dev(inp["X"]), dev(inp["Wq"], inp["Wq_bits"])
+    Wkv, Wo = dev(inp["Wkv"], inp["Wkv_bits"]), dev(inp["Wo"], inp["Wo_bits"])
+    Q, KV, R, _ = layer.attention_forward(shape, cfg, X, Wq, Wkv, Wo, KV=KV, **g)
+    dU = np.random.default_rng(2300 + L).standard_normal((L * B, nd * 3 * d)).astype(np.float32)
+    print(f"case L={L} B={B} d={d} nd={nd} d'={dp} Lm={Lm}", flush=True)
+    a = layer.attention_backward(shape, cfg, X, Wq, Wkv, Wo, Q, KV, R, dev(dU),
+                                 gamma=g["gamma"])
+    b = layer.attention_backward(shape, cfg, X, Wq, Wkv, Wo, Q, KV, R,
+                                 dev(dU).to(torch.bfloat16), gamma=g["gamma"])
+    torch.cuda.synchronize()
+    for k in ("dX", "dWq", "dWkv", "dWo", "dgamma", "dbeta"):
+        check(k, host(b[k]), host(a[k]), 1e-4)
+    # dalpha is one sum whose terms cancel: compared relative to its size plus one
+    da, db_ = float(host(a["dalpha"])[0]), float(host(b["dalpha"])[0])
+    print(f"  dalpha: {da:.6g} vs {db_:.6g}", flush=True)
+    assert abs(db_ - da) <= 1e-3 * (abs(da) + 1.0)
