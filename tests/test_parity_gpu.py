@@ -519,10 +519,12 @@ def test_bwd_data_bf16_dU_transposed_weight(L, B, d, nd):
           1e-6)
 
 
-@pytest.mark.parametrize("n", [1, 3, 4, 5, 1000003])
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 4096, 12289, 1000003, 40000003])
 def test_round_bf16_exact(n):
     """sru_round_bf16 bit for bit against the oracle's rounding (ties, both
-    parities of the kept bit, infinities, tiny and huge values, NaN)."""
+    parities of the kept bit, infinities, tiny and huge values, NaN).  The
+    sizes cover one whole block step (4096), a ragged last step, and more
+    elements than one pass of the capped grid (8192 blocks of 4096)."""
     import torch
     rng = np.random.default_rng(n)
     x = (rng.standard_normal(n) * 10.0 ** rng.integers(-30, 30, n)).astype(np.float32)
