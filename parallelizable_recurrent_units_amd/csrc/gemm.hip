@@ -638,7 +638,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
     __shared__ __attribute__((aligned(16))) char smem[NS * SB];
 
     const int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb, ldc = p.ldc;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
     const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
     A += (int64_t)blockIdx.y * p.sa;
     B += (int64_t)blockIdx.y * p.sb;
@@ -649,38 +650,41 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
     const int64_t m0 = tm * BM, n0 = tn * BN;
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;    // low half of a flat LDS address
 
-    // this lane's source of each of the wave's requests, at k = 0.  Request q
-    // fills 1 KB of the stage: 1024 / AROW rows of A (q < QA) or 8 rows of B.
-    // Lane l takes piece l % (pieces per row) of row l / (pieces per row); in
-    // a row the piece at position s holds k-chunk s ^ lds_swz(row).
-    // Rows past M or N repeat the last row (loaded, never stored).
-    const char *src[IPW];
+    // Request q fills 1 KB of the stage: 8 rows of A (q < QA) or of B, each
+    // row's 128 bytes as eight 16-byte pieces; lane l takes piece l % 8 of row
+    // l / 8, and in a row the piece at position s holds k-chunk s ^ lds_swz(row).
+    // A wave's requests are all rows of A or all rows of B, so the wave keeps
+    // one uniform base (its first row, at k = 0; a scalar register pair) and a
+    // 32-bit byte offset per lane and request.  Rows past M or N repeat the
+    // last row (loaded, never stored).
+    static_assert(sizeof(TA) == 2 && AROW == 128, "bf16 A");
+    static_assert(St::QA % IPW == 0, "a wave's requests stay within one operand");
+    const char *wbase;
+    uint32_t voff[IPW];
+    {
+        const int q0 = wave * IPW;
+        const bool isA = q0 < St::QA;
+        const int64_t r0 = isA ? q0 * 8 : (q0 - St::QA) * 8;   // the wave's first row in the tile
+        const int64_t last = isA ? M - 1 - m0 : N - 1 - n0;     // last valid row in the tile
+        const int64_t ld = isA ? lda : ldb;
+        const int64_t rb = r0 < last ? r0 : last;
+        wbase = (const char *)((isA ? A + m0 * ld : B + n0 * ld) + rb * ld);
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-        const int q = wave * IPW + i;
-        if (q < St::QA) {
-            const int row = q * (1024 / AROW) + lane / APR;
+        for (int i = 0; i < IPW; ++i) {
+            const int row = (int)r0 + i * 8 + lane / APR;
             const int c = (lane % APR) ^ lds_swz(row);
-            const int64_t m = m0 + row < M ? m0 + row : M - 1;
-            src[i] = (const char *)(A + m * lda) + 16 * c;
-        } else {
-            const int row = (q - St::QA) * 8 + lane / 8;
-            const int c = (lane % 8) ^ lds_swz(row);
-            const int64_t n = n0 + row < N ? n0 + row : N - 1;
-            src[i] = (const char *)(B + n * ldb) + 16 * c;
+            const int64_t rr = row < last ? row : last;
+            voff[i] = (uint32_t)((rr - rb) * ld * 2 + 16 * c);
         }
     }
     const int64_t KT = K / 64;
     // requests of k-tile kt into stage st; past the last k-tile the last one
     // is requested again, so every iteration waits on the same count
     auto issue = [&](int64_t kt, int st) {
-        const int64_t k0 = (kt < KT ? kt : KT - 1) * 64;
+        const char *kb = wbase + (kt < KT ? kt : KT - 1) * 128;
 #pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const int q = wave * IPW + i;
-            const int64_t off = k0 * (q < St::QA ? (int64_t)sizeof(TA) : 2);
-            dma16(src[i] + off, __builtin_amdgcn_readfirstlane(lds0 + st * SB + q * 1024));
-        }
+        for (int i = 0; i < IPW; ++i)
+            dma16s(kb, voff[i], lds0 + st * SB + (wave * IPW + i) * 1024);
     };
 
     f32x16 acc[TI][TJ];
@@ -693,7 +697,6 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
 
     const int r32 = lane & 31, hi = lane >> 5;
     // fragment of 8 k-values (16 ks + 8 hi ..) of A row `row` / B row `row`
-    static_assert(sizeof(TA) == 2, "bf16 A");
     auto afrag = [&](int st, int row, int ks) -> bf16x8 {
         const int c = 2 * ks + hi;
         return *(const bf16x8 *)(smem + st * SB + row * AROW + ((c ^ lds_swz(row)) << 4));
@@ -710,7 +713,6 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
         wait_vmcnt<(NS - 2) * IPW>();                    // this wave's share of k-tile kt
         wait_lgkm0();                                    // and its reads of the last stage
         __builtin_amdgcn_s_barrier();
-        issue(kt + NS - 1, (int)((kt + NS - 1) % NS));   // into the stage read last time
         bf16x8 a[2][TI], b[2][TJ];
         auto rd = [&](int buf, int ks) {
 #pragma unroll
@@ -718,7 +720,10 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
 #pragma unroll
             for (int j = 0; j < TJ; ++j) b[buf][j] = bfrag(st, wn * WN + j * 32 + r32, ks);
         };
+        // the first fragments are read while the copies are issued
         rd(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(kt + NS - 1, (int)((kt + NS - 1) % NS));   // into the stage read last time
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int cur = ks & 1;
@@ -787,14 +792,16 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
 }
 
 // The bf16 x bf16^T products that gemm_lds takes: whole 64-deep k-tiles,
-// 16-byte aligned operand rows and batch offsets.
+// 16-byte aligned operand rows and batch offsets, and row strides below 2^24
+// elements (a wave's 64 rows then span less than 2^31 bytes: 32-bit lane
+// offsets).
 bool lds_path_ok(const GemmArgs &g)
 {
     if (!g.a_bf16 || !g.b_bf16 || g.b_kn || g.K % 64 != 0 || g.K < 64) return false;
     const int64_t lda = g.lda ? g.lda : g.K, ldb = g.ldb ? g.ldb : g.K;
     auto al16 = [](const void *q) { return ((uintptr_t)q & 15u) == 0; };
     return lda % 8 == 0 && ldb % 8 == 0 && g.sa % 8 == 0 && g.sb % 8 == 0 && al16(g.A) &&
-           al16(g.Bm);
+           al16(g.Bm) && lda < (int64_t(1) << 24) && ldb < (int64_t(1) << 24);
 }
 
 template <class Cfg, typename TA>
