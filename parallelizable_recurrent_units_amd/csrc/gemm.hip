@@ -614,15 +614,16 @@ template <class Cfg, typename TA> struct LdsStage {
     static constexpr int Q = BYTES / 1024;
     static constexpr int IPW = Q / Cfg::NW;              // requests per wave per stage
     static_assert(IPW * Cfg::NW == Q, "whole 1 KB requests per wave");
-    static_assert(Cfg::NW * 32 * Cfg::EPI_LD * 4 <= Cfg::NS * BYTES, "epilogue staging fits");
+    static_assert(Cfg::NW * 16 * Cfg::EPI_LD * 4 <= Cfg::NS * BYTES, "epilogue staging fits");
 };
 
-// 256 x 256 tiles, 8 waves, two stages: long reductions on grids that fill
-// the chip.  128 x 128 tiles, 8 waves, four stages (one block per CU): long
-// reductions on smaller grids, where an operand streamed from HBM needs
-// requests several k-tiles ahead.  128 x 128 tiles, 4 waves, two stages (two
-// blocks per CU): short reductions.
-typedef LdsCfg<256, 256, 2, 2, 4, 1> LdsBig;
+// 256 x 256 tiles, 16 waves of 64 x 64, two stages: long reductions on grids
+// that fill the chip (four waves per SIMD hide more of the barrier and LDS
+// latency than two).  128 x 128 tiles, 8 waves, four stages (one block per
+// CU): long reductions on smaller grids, where an operand streamed from HBM
+// needs requests several k-tiles ahead.  128 x 128 tiles, 4 waves, two stages
+// (two blocks per CU): short reductions.
+typedef LdsCfg<256, 256, 2, 4, 4, 1> LdsBig;
 typedef LdsCfg<128, 128, 4, 2, 4, 1> LdsDeep;
 typedef LdsCfg<128, 128, 2, 2, 2, 2> LdsSmall;
 
@@ -749,43 +750,49 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
 
-    // epilogue through LDS, one 32-row band per wave at a time (the 32x32
-    // accumulator holds column lane & 31, rows 8 (r / 4) + 4 (lane / 32) + r % 4)
+    // epilogue through LDS, one 16-row half of a 32-row band per wave at a
+    // time (the 32x32 accumulator holds column lane & 31, rows
+    // 8 (r / 4) + 4 (lane / 32) + r % 4: values r = 8 h .. 8 h + 7 are the
+    // rows of half h)
     constexpr int EPI_LD = Cfg::EPI_LD, C4 = WN / 4;
-    float *stage = (float *)smem + wave * (32 * EPI_LD);
+    float *stage = (float *)smem + wave * (16 * EPI_LD);
     const int64_t nw = n0 + wn * WN;
     const bool vec = N % 4 == 0 && ldc % 4 == 0 && p.sc % 4 == 0 && ((uintptr_t)C & 15u) == 0;
     const bool accumulate = p.accumulate;
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                stage[(8 * (r / 4) + 4 * hi + (r % 4)) * EPI_LD + j * 32 + r32] = acc[i][j][r];
-        const int64_t mw = m0 + wm * WM + i * 32;
+            for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                for (int r = 8 * h; r < 8 * h + 8; ++r)
+                    stage[(8 * (r / 4 - 2 * h) + 4 * hi + (r % 4)) * EPI_LD + j * 32 + r32] =
+                        acc[i][j][r];
+            const int64_t mw = m0 + wm * WM + i * 32 + 16 * h;
 #pragma unroll 4
-        for (int it = 0; it < 32 * C4 / 64; ++it) {
-            const int idx = it * 64 + lane;
-            const int row = idx / C4, c4 = idx % C4;
-            const int64_t m = mw + row, n = nw + c4 * 4;
-            if (m >= M) continue;
-            const float4 v = *(const float4 *)(stage + row * EPI_LD + c4 * 4);
-            float *q = C + m * ldc + n;
-            if (vec) {
-                if (n < N) {
-                    float4 o = v;
-                    if (accumulate) {
-                        const float4 c = *(const float4 *)q;
-                        o.x += c.x; o.y += c.y; o.z += c.z; o.w += c.w;
+            for (int it = 0; it < 16 * C4 / 64; ++it) {
+                const int idx = it * 64 + lane;
+                const int row = idx / C4, c4 = idx % C4;
+                const int64_t m = mw + row, n = nw + c4 * 4;
+                const float4 v = *(const float4 *)(stage + row * EPI_LD + c4 * 4);
+                if (m >= M) continue;
+                float *q = C + m * ldc + n;
+                if (vec) {
+                    if (n < N) {
+                        float4 o = v;
+                        if (accumulate) {
+                            const float4 c = *(const float4 *)q;
+                            o.x += c.x; o.y += c.y; o.z += c.z; o.w += c.w;
+                        }
+                        *(float4 *)q = o;
                     }
-                    *(float4 *)q = o;
-                }
-            } else {
-                const float vv[4] = {v.x, v.y, v.z, v.w};
+                } else {
+                    const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (n + e < N) q[e] = accumulate ? q[e] + vv[e] : vv[e];
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) q[e] = accumulate ? q[e] + vv[e] : vv[e];
+                }
             }
         }
     }
