@@ -231,8 +231,9 @@ sru_status sru_project_factored_bwd_weight(const sru_shape *shape, int64_t d_inn
  * gamma, beta: required when cfg->layernorm, else ignored (may be NULL).
  * workspace: sru_attention_workspace_size(shape, cfg) bytes, 256-byte
  *   aligned: for d' in {64, 128, 256, 512} a transposed copy of V (bf16, the
- *   keys padded to a multiple of 32); otherwise the scores [B, L, Lm + L]
- *   (fp32), the weights (bf16) and A.
+ *   keys padded to a multiple of 32) and R~ (R rounded to bf16, the operand
+ *   of the U product); otherwise the scores [B, L, Lm + L] (fp32), the
+ *   weights (bf16) and A.
  * Outputs must not overlap each other or the inputs.
  */
 sru_status sru_attention_forward(const sru_shape *shape, const sru_attn_cfg *cfg,

@@ -322,6 +322,7 @@ struct FusedArgs {
     const bf16_bits *KV, *Vt;
     const float *gamma, *beta;
     float *R;
+    bf16_bits *Rb;         // R rounded to bf16 (the U product's operand), or null
 };
 
 template <int DP>
@@ -691,10 +692,20 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_fused(FusedArgs a)
             for (int i = 0; i < 4; ++i)
                 *(float4 *)(rrow + 32 * ob + 8 * i + 4 * hi) =
                     make_float4(o[ob][4 * i], o[ob][4 * i + 1], o[ob][4 * i + 2], o[ob][4 * i + 3]);
+        if (a.Rb) {
+            bf16_bits *brow = a.Rb + (t * B + b) * DP + DPH * h;
+#pragma unroll
+            for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *(uint2 *)(brow + 32 * ob + 8 * i + 4 * hi) =
+                        make_uint2(pack_bf16x2(o[ob][4 * i], o[ob][4 * i + 1]),
+                                   pack_bf16x2(o[ob][4 * i + 2], o[ob][4 * i + 3]));
+        }
     }
 }
 
-hipError_t launch_fused(const AttnArgs &a, bf16_bits *Vt, hipStream_t s)
+hipError_t launch_fused(const AttnArgs &a, bf16_bits *Vt, bf16_bits *Rb, hipStream_t s)
 {
     const int64_t Lk = a.Lm + a.L, Lkp = fused_keys_padded(Lk);
     hipLaunchKernelGGL(attn_v_transpose, dim3((unsigned)((Lkp + 63) / 64), (unsigned)(a.dp / 64),
@@ -705,7 +716,7 @@ hipError_t launch_fused(const AttnArgs &a, bf16_bits *Vt, hipStream_t s)
     f.causal = a.causal, f.layernorm = a.layernorm;
     f.alpha = a.alpha, f.eps = a.eps;
     f.Q = a.Q, f.KV = (const bf16_bits *)a.KV, f.Vt = Vt;
-    f.gamma = a.gamma, f.beta = a.beta, f.R = a.R;
+    f.gamma = a.gamma, f.beta = a.beta, f.R = a.R, f.Rb = Rb;
     const dim3 grid((unsigned)(((a.L + kFusedBQ - 1) / kFusedBQ) * a.B)), block(256);
     switch (a.dp) {
     case 64: hipLaunchKernelGGL(attn_fwd_fused<64>, grid, block, 0, s, f); break;
@@ -1252,10 +1263,18 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
     return launch_gemm(g, s);
 }
 
+// Fused shapes: the V^T copy, then R rounded to bf16 (the U product's
+// operand, copied straight into LDS by the bf16 x bf16^T kernel).
+size_t fused_vt_bytes(int64_t L, int64_t B, int64_t dp, int64_t Lm)
+{
+    const size_t n = (size_t)B * (size_t)dp * (size_t)fused_keys_padded(Lm + L) * 2;
+    return (n + 255) & ~(size_t)255;
+}
+
 size_t attention_workspace_bytes(int64_t L, int64_t B, int64_t dp, int64_t Lm)
 {
-    if (fused_forward_ok(L, B, dp, Lm))   // V^T only
-        return (size_t)B * (size_t)dp * (size_t)fused_keys_padded(Lm + L) * 2;
+    if (fused_forward_ok(L, B, dp, Lm))
+        return fused_vt_bytes(L, B, dp, Lm) + (size_t)L * (size_t)B * (size_t)dp * 2;
     return ws_layout(L, B, dp, Lm).total;
 }
 
@@ -1285,16 +1304,19 @@ hipError_t launch_attention_forward(const AttnArgs &a, hipStream_t s)
         g.C = (float *)(KV + Lm * B * 2 * dp), g.accumulate = false;
         if ((e = launch_gemm_bf16_out(g, s)) != hipSuccess) return e;
     }
-    if (fused_forward_ok(L, B, dp, Lm)) {
-        if ((e = launch_fused(a, (bf16_bits *)ws, s)) != hipSuccess) return e;
+    const bool fused = fused_forward_ok(L, B, dp, Lm);
+    bf16_bits *Rb = fused ? (bf16_bits *)(ws + fused_vt_bytes(L, B, dp, Lm)) : nullptr;
+    if (fused) {
+        if ((e = launch_fused(a, (bf16_bits *)ws, Rb, s)) != hipSuccess) return e;
     } else {
         if ((e = attend(L, B, dp, Lm, a.causal, a.Q, KV, S, P, O, s)) != hipSuccess) return e;
         if ((e = launch_residual(a, O, s)) != hipSuccess) return e;
     }
-    {   // U [L*B, ndir*3d] = R~ Wo^T, fp32 or rounded to bf16
+    {   // U [L*B, ndir*3d] = R~ Wo^T, fp32 or rounded to bf16; R~ is the fused
+        // kernel's bf16 copy of R, or R rounded as the product loads it
         GemmArgs g;
         g.M = LB, g.N = a.n3, g.K = dp;
-        g.A = a.R, g.a_bf16 = false;
+        g.A = fused ? (const void *)Rb : (const void *)a.R, g.a_bf16 = fused;
         g.Bm = a.Wo, g.b_bf16 = true, g.b_kn = false;
         g.C = (float *)a.U, g.accumulate = false;
         if ((e = a.u_bf16 ? launch_gemm_bf16_out(g, s) : launch_gemm(g, s)) != hipSuccess)

@@ -627,10 +627,10 @@ typedef LdsCfg<256, 256, 2, 4, 4, 1> LdsBig;
 typedef LdsCfg<128, 128, 4, 2, 4, 1> LdsDeep;
 typedef LdsCfg<128, 128, 2, 2, 2, 2> LdsSmall;
 
-template <class Cfg, typename TA>
+template <class Cfg, typename TA, typename TC>
 __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *__restrict__ A,
                                                                const bf16_bits *__restrict__ B,
-                                                               float *__restrict__ C)
+                                                               TC *__restrict__ C)
 {
     typedef LdsStage<Cfg, TA> St;
     constexpr int BM = Cfg::BM, BN = Cfg::BN, NS = Cfg::NS, IPW = St::IPW;
@@ -757,7 +757,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
     constexpr int EPI_LD = Cfg::EPI_LD, C4 = WN / 4;
     float *stage = (float *)smem + wave * (16 * EPI_LD);
     const int64_t nw = n0 + wn * WN;
-    const bool vec = N % 4 == 0 && ldc % 4 == 0 && p.sc % 4 == 0 && ((uintptr_t)C & 15u) == 0;
+    const bool vec = N % 4 == 0 && ldc % 4 == 0 && p.sc % 4 == 0 &&
+                     ((uintptr_t)C & (4 * sizeof(TC) - 1)) == 0;
     const bool accumulate = p.accumulate;
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
@@ -777,8 +778,17 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
                 const int64_t m = mw + row, n = nw + c4 * 4;
                 const float4 v = *(const float4 *)(stage + row * EPI_LD + c4 * 4);
                 if (m >= M) continue;
-                float *q = C + m * ldc + n;
-                if (vec) {
+                TC *q = C + m * ldc + n;
+                if constexpr (std::is_same<TC, bf16_bits>::value) {   // rounded, never accumulated
+                    if (vec) {
+                        if (n < N) *(u32x2 *)q = u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+                    } else {
+                        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < N) q[e] = f32_to_bf16(vv[e]);
+                    }
+                } else if (vec) {
                     if (n < N) {
                         float4 o = v;
                         if (accumulate) {
@@ -811,7 +821,7 @@ bool lds_path_ok(const GemmArgs &g)
            al16(g.Bm) && lda < (int64_t(1) << 24) && ldb < (int64_t(1) << 24);
 }
 
-template <class Cfg, typename TA>
+template <class Cfg, typename TA, typename TC>
 hipError_t lds_launch_cfg(const GemmArgs &g, hipStream_t s)
 {
     MM p;
@@ -828,27 +838,31 @@ hipError_t lds_launch_cfg(const GemmArgs &g, hipStream_t s)
     p.gm = 8;
     p.accumulate = g.accumulate;
     const int64_t tiles = ((g.M + Cfg::BM - 1) / Cfg::BM) * ((g.N + Cfg::BN - 1) / Cfg::BN);
-    hipLaunchKernelGGL((gemm_lds<Cfg, TA>),
+    hipLaunchKernelGGL((gemm_lds<Cfg, TA, TC>),
                        dim3((unsigned)tiles, (unsigned)(g.batch > 0 ? g.batch : 1)),
-                       dim3(Cfg::NT), 0, s, p, (const TA *)g.A, (const bf16_bits *)g.Bm, g.C);
+                       dim3(Cfg::NT), 0, s, p, (const TA *)g.A, (const bf16_bits *)g.Bm, (TC *)g.C);
     return hipGetLastError();
 }
 
-template <typename TA>
+#ifndef SRU_LDS_BIG_MIN_K
+#define SRU_LDS_BIG_MIN_K 512
+#endif
+
+template <typename TA, typename TC>
 hipError_t lds_launch_t(const GemmArgs &g, hipStream_t s)
 {
     // the large tiles once they give every CU one and the reduction is long
-    // enough to amortise their prologue and epilogue; deep small tiles for
+    // enough to amortise their prologue and epilogue (from K = 512: the SRU++
+    // output projection at K = d' = 512, L*B = 16384, 3d = 6144 runs about
+    // 30 us faster on them than on the small tiles); deep small tiles for
     // other long reductions; two small blocks per CU for short ones
     const int64_t big = ((g.M + 255) / 256) * ((g.N + 255) / 256) * (g.batch > 0 ? g.batch : 1);
-    if (g.K >= 1024) {
-        if (big >= 256) return lds_launch_cfg<LdsBig, TA>(g, s);
-        return lds_launch_cfg<LdsDeep, TA>(g, s);
-    }
-    return lds_launch_cfg<LdsSmall, TA>(g, s);
+    if (g.K >= SRU_LDS_BIG_MIN_K && big >= 256) return lds_launch_cfg<LdsBig, TA, TC>(g, s);
+    if (g.K >= 1024) return lds_launch_cfg<LdsDeep, TA, TC>(g, s);
+    return lds_launch_cfg<LdsSmall, TA, TC>(g, s);
 }
 
-hipError_t lds_launch(const GemmArgs &g, hipStream_t s) { return lds_launch_t<bf16_bits>(g, s); }
+hipError_t lds_launch(const GemmArgs &g, hipStream_t s) { return lds_launch_t<bf16_bits, float>(g, s); }
 
 // dst[i] = bf16(src[i]) (nearest even), four elements per lane and step.
 __global__ __launch_bounds__(256) void round_bf16_kernel(int64_t n, const float *__restrict__ src,
@@ -1259,7 +1273,11 @@ hipError_t launch_gemm_tn(const GemmArgs &g, hipStream_t s)
 
 hipError_t launch_gemm_bf16_out(const GemmArgs &g, hipStream_t s)
 {
-    if (!g.b_bf16 || g.b_kn || g.accumulate || g.a_bf16) return hipErrorInvalidValue;
+    if (!g.b_bf16 || g.b_kn || g.accumulate) return hipErrorInvalidValue;
+    if (g.a_bf16) {
+        if (lds_path_ok(g)) return lds_launch_t<bf16_bits, bf16_bits>(g, s);
+        return mfma_launch<bf16_bits, false, bf16_bits>(g, s);
+    }
     return mfma_launch<float, false, bf16_bits>(g, s);
 }
 

@@ -102,8 +102,10 @@ struct GemmArgs {
 
 // bf16 B: bf16 MFMA (A rounded to bf16 as it is loaded); fp32 B: fp32 FMA.
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
-// As launch_gemm for fp32 A, bf16 B given as [N, K], no accumulation, with
-// C written as bf16 (rounded to nearest even); C points to bf16 storage.
+// As launch_gemm for fp32 or bf16 A, bf16 B given as [N, K], no
+// accumulation, with C written as bf16 (rounded to nearest even); C points to
+// bf16 storage.  For bf16 A the product takes the same kernel as launch_gemm
+// would for the same operands, so the bf16 C is the fp32 C rounded.
 hipError_t launch_gemm_bf16_out(const GemmArgs &g, hipStream_t s);
 // C[M, N] (+)= A^T B with A given as [K, M] and B as [K, N] (each bf16 or
 // fp32): the weight gradient dW = dU^T Xt.  f32_math: fp32 FMA throughout;
