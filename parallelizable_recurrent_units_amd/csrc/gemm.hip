@@ -604,26 +604,33 @@ struct LdsCfg {
 };
 
 // Stage layout for an A of element type TA: BM rows of 64 A elements (128 or
-// 256 bytes), then BN rows of 64 bf16 of B (128 bytes); 1 KB requests.
+// 256 bytes), then BN rows of 64 bf16 of B (128 bytes); 1 KB requests.  The
+// first half of the waves copies A (IPWA requests each), the second half B
+// (IPWB each).
 template <class Cfg, typename TA> struct LdsStage {
     static constexpr int AROW = 64 * (int)sizeof(TA);   // bytes of one A row
     static constexpr int APR = AROW / 16;                // 16-byte pieces per A row
     static constexpr int A_BYTES = Cfg::BM * AROW;
     static constexpr int BYTES = A_BYTES + Cfg::BN * 128;
     static constexpr int QA = A_BYTES / 1024;            // requests for A
-    static constexpr int Q = BYTES / 1024;
-    static constexpr int IPW = Q / Cfg::NW;              // requests per wave per stage
-    static_assert(IPW * Cfg::NW == Q, "whole 1 KB requests per wave");
+    static constexpr int QB = Cfg::BN * 128 / 1024;      // requests for B
+    static constexpr int HW = Cfg::NW / 2;               // waves per operand
+    static constexpr int IPWA = QA / HW, IPWB = QB / HW; // requests per wave per stage
+    static constexpr int IPW = IPWA > IPWB ? IPWA : IPWB;
+    static_assert(IPWA * HW == QA && IPWB * HW == QB, "whole 1 KB requests per wave");
     static_assert(Cfg::NW * 16 * Cfg::EPI_LD * 4 <= Cfg::NS * BYTES, "epilogue staging fits");
 };
 
 // 256 x 256 tiles, 16 waves of 64 x 64, two stages: long reductions on grids
 // that fill the chip (four waves per SIMD hide more of the barrier and LDS
-// latency than two).  128 x 128 tiles, 8 waves, four stages (one block per
-// CU): long reductions on smaller grids, where an operand streamed from HBM
-// needs requests several k-tiles ahead.  128 x 128 tiles, 4 waves, two stages
-// (two blocks per CU): short reductions.
+// latency than two).  256 x 128 tiles, 8 waves of 64 x 64, three stages: long
+// reductions where the large tiles would leave CUs idle but these fill them
+// (N = 512).  128 x 128 tiles, 8 waves, four stages (one block per CU): long
+// reductions on smaller grids, where an operand streamed from HBM needs
+// requests several k-tiles ahead.  128 x 128 tiles, 4 waves, two stages (two
+// blocks per CU): short reductions.
 typedef LdsCfg<256, 256, 2, 4, 4, 1> LdsBig;
+typedef LdsCfg<256, 128, 3, 4, 2, 1> LdsMid;
 typedef LdsCfg<128, 128, 4, 2, 4, 1> LdsDeep;
 typedef LdsCfg<128, 128, 2, 2, 2, 2> LdsSmall;
 
@@ -659,12 +666,12 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
     // 32-bit byte offset per lane and request.  Rows past M or N repeat the
     // last row (loaded, never stored).
     static_assert(sizeof(TA) == 2 && AROW == 128, "bf16 A");
-    static_assert(St::QA % IPW == 0, "a wave's requests stay within one operand");
+    constexpr int IPWA = St::IPWA, IPWB = St::IPWB;
+    const bool isA = wave < St::HW;                      // uniform
+    const int q0 = isA ? wave * IPWA : St::QA + (wave - St::HW) * IPWB;   // first request
     const char *wbase;
     uint32_t voff[IPW];
     {
-        const int q0 = wave * IPW;
-        const bool isA = q0 < St::QA;
         const int64_t r0 = isA ? q0 * 8 : (q0 - St::QA) * 8;   // the wave's first row in the tile
         const int64_t last = isA ? M - 1 - m0 : N - 1 - n0;     // last valid row in the tile
         const int64_t ld = isA ? lda : ldb;
@@ -683,9 +690,15 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
     // is requested again, so every iteration waits on the same count
     auto issue = [&](int64_t kt, int st) {
         const char *kb = wbase + (kt < KT ? kt : KT - 1) * 128;
+        if (isA) {
 #pragma unroll
-        for (int i = 0; i < IPW; ++i)
-            dma16s(kb, voff[i], lds0 + st * SB + (wave * IPW + i) * 1024);
+            for (int i = 0; i < IPWA; ++i)
+                dma16s(kb, voff[i], lds0 + st * SB + (q0 + i) * 1024);
+        } else {
+#pragma unroll
+            for (int i = 0; i < IPWB; ++i)
+                dma16s(kb, voff[i], lds0 + st * SB + (q0 + i) * 1024);
+        }
     };
 
     f32x16 acc[TI][TJ];
@@ -711,7 +724,10 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
     for (int st = 0; st < NS - 1; ++st) issue(st, st);
     for (int64_t kt = 0; kt < KT; ++kt) {
         const int st = (int)(kt % NS);
-        wait_vmcnt<(NS - 2) * IPW>();                    // this wave's share of k-tile kt
+        if (isA)                                         // this wave's share of k-tile kt
+            wait_vmcnt<(NS - 2) * IPWA>();
+        else
+            wait_vmcnt<(NS - 2) * IPWB>();
         wait_lgkm0();                                    // and its reads of the last stage
         __builtin_amdgcn_s_barrier();
         bf16x8 a[2][TI], b[2][TJ];
@@ -856,8 +872,11 @@ hipError_t lds_launch_t(const GemmArgs &g, hipStream_t s)
     // output projection at K = d' = 512, L*B = 16384, 3d = 6144 runs about
     // 30 us faster on them than on the small tiles); deep small tiles for
     // other long reductions; two small blocks per CU for short ones
-    const int64_t big = ((g.M + 255) / 256) * ((g.N + 255) / 256) * (g.batch > 0 ? g.batch : 1);
+    const int64_t nb = g.batch > 0 ? g.batch : 1;
+    const int64_t big = ((g.M + 255) / 256) * ((g.N + 255) / 256) * nb;
+    const int64_t mid = ((g.M + 255) / 256) * ((g.N + 127) / 128) * nb;
     if (g.K >= SRU_LDS_BIG_MIN_K && big >= 256) return lds_launch_cfg<LdsBig, TA, TC>(g, s);
+    if (g.K >= 1024 && mid >= 256 && mid % 256 == 0) return lds_launch_cfg<LdsMid, TA, TC>(g, s);
     if (g.K >= 1024) return lds_launch_cfg<LdsDeep, TA, TC>(g, s);
     return lds_launch_cfg<LdsSmall, TA, TC>(g, s);
 }

@@ -42,7 +42,7 @@ def dev(a, bits=None):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def run(L, B, d, nd, dp, Lm, causal, ln, alpha, inp, X=None, kv_mem=None):
+def run(L, B, d, nd, dp, Lm, causal, ln, alpha, inp, X=None, kv_mem=None, u_dtype=None):
     """GPU call; the KV buffer's first Lm rows hold the previous segment."""
     import torch
     shape = SruShape(L, B, d, nd == 2, 1.0)
@@ -52,6 +52,8 @@ def run(L, B, d, nd, dp, Lm, causal, ln, alpha, inp, X=None, kv_mem=None):
         KV[:Lm] = kv_mem if kv_mem is not None else torch.cat(
             [dev(inp["Kmem"], inp["Kmem_bits"]), dev(inp["Vmem"], inp["Vmem_bits"])], dim=2)
     g = dict(gamma=dev(inp["gamma"]), beta=dev(inp["beta"])) if ln else {}
+    if u_dtype is not None:
+        g["u_dtype"] = u_dtype
     Q, KV, R, U = layer.attention_forward(
         shape, cfg, dev(inp["X"]) if X is None else X, dev(inp["Wq"], inp["Wq_bits"]),
         dev(inp["Wkv"], inp["Wkv_bits"]), dev(inp["Wo"], inp["Wo_bits"]), KV=KV, **g)
@@ -185,13 +187,19 @@ def test_attention_two_segments_carry_context():
 def test_attention_workload_sampled_sequences():
     """The shape whose U the given-U workload consumes: L=1024, B=16, d=2048,
     d' = d/4 = 512, causal, the previous 1024-step segment as context.  Two
-    whole sequences (every row of Q, K, V, R, U) against the oracle."""
+    whole sequences (every row of Q, K, V, R, U) against the oracle; the bf16
+    U that the given-U recurrence takes (the same product with a rounding
+    epilogue) is the fp32 U rounded, bit for bit, over every row."""
     import torch
     L, B, d, dp, Lm = 1024, 16, 2048, 512, 1024
     inp = workloads.attention_inputs(L, B, d, 1, dp, Lm, seed=1401)
     print("workload attention L=1024 B=16 d=2048 d'=512 Lm=1024", flush=True)
     Q, KV, R, U = run(L, B, d, 1, dp, Lm, True, True, 1.0, inp)
+    Ub = run(L, B, d, 1, dp, Lm, True, True, 1.0, inp, u_dtype=torch.bfloat16)[3]
     torch.cuda.synchronize()
+    assert Ub.dtype == torch.bfloat16
+    assert torch.equal(Ub.view(torch.int16), U.to(torch.bfloat16).view(torch.int16))
+    del Ub
     X3 = inp["X"].reshape(L, B, d)
     for b in (0, B - 1):
         print(f" sequence {b}", flush=True)

@@ -484,12 +484,14 @@ def test_projection_bwd_weight_is_deterministic():
 
 # bf16 dU times the transposed bf16 weights: the products whose operands go
 # straight to LDS (whole 64-deep k-tiles), at ragged M and N, one k-tile up to
-# long reductions, with accumulation; the last two cases take the 256 x 256
-# tiles, ragged in M and in both M and N (sampled rows, the last ragged tile
-# included).
+# long reductions, with accumulation; (100, 164, 1024) and (100, 140, 1088)
+# take the 256 x 256 tiles, ragged in M and in both M and N, and the last two
+# the 256 x 128 three-stage tiles (N = 512, and N = 448 with M ragged)
+# (sampled rows, the last ragged tile included).
 @pytest.mark.parametrize("L,B,d,nd", [(3, 5, 64, 1), (7, 19, 128, 2), (64, 4, 256, 2),
                                       (33, 3, 64, 1), (1, 1, 64, 1), (40, 50, 512, 2),
-                                      (100, 164, 1024, 1), (100, 140, 1088, 1)])
+                                      (100, 164, 1024, 1), (100, 140, 1088, 1),
+                                      (128, 128, 512, 1), (92, 177, 448, 1)])
 def test_bwd_data_bf16_dU_transposed_weight(L, B, d, nd):
     import torch
     rng = np.random.default_rng(6000 + d + L)
