@@ -824,6 +824,215 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
     }
 }
 
+// ---- both operands K-major: C (+)= A^T B with A [K, M], B [K, N] ----------
+// The weight gradient's layout (the reduction index L*B is the slow one).  A
+// k-tile of each operand is 64 rows of 256 columns (512 bytes); the copies
+// move it memory -> LDS in 1 KB requests of two rows, and the MFMA operands
+// (8 consecutive k of one column per lane) are read back with
+// ds_read_b64_tr_b16: within a group of 16 lanes, lane i receives the i-th
+// 16-bit element of each of the four 8-byte pieces that lanes 4j + i / 4
+// address (j = 0..3), so when lanes 4j .. 4j + 3 address row k0 + j, columns
+// c .. c + 15, lane i gets column c + i at k0 .. k0 + 3, and two such reads
+// give the 8 k of the 32x32x16 operand.
+//
+// The 16-byte pieces of a row (P = 0..31, columns 8P .. 8P + 7) are stored
+// at position tr_pos(P, row): writing P = 4a + 2b + c, position
+// c + 2 (a mod 4) + 8 b + 16 (a / 4), XOR 2 (row mod 4).  A read of 16
+// columns touches pieces 4a + 2b + {0, 1} of four consecutive rows: the XOR
+// spreads the four rows over four bank groups and b puts the two 16-column
+// halves of a 32-column block eight positions apart, so each half-wave's 256
+// bytes fall on distinct banks.
+__device__ __forceinline__ int tr_pos(int P, int row)
+{
+    const int c = P & 1, b = (P >> 1) & 1, a = P >> 2;
+    return (c + 2 * (a & 3) + 8 * b + 16 * (a >> 2)) ^ (2 * (row & 3));
+}
+__device__ __forceinline__ int tr_piece(int pos, int row)   // the inverse of tr_pos
+{
+    const int q = pos ^ (2 * (row & 3));
+    return 4 * (((q >> 1) & 3) + 4 * (q >> 4)) + 2 * ((q >> 3) & 1) + (q & 1);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// 256 x 256 tiles, 16 waves of 64 x 64, two stages.  With several splits
+// block s of a tile covers k in [s ksplit, (s + 1) ksplit) and writes its
+// partial product to C + s M ldc (summed in order by split_reduce).
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds_t(MM p, const bf16_bits *__restrict__ A,
+                                                                 const bf16_bits *__restrict__ B,
+                                                                 float *__restrict__ C)
+{
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, NW = Cfg::NW, NS = Cfg::NS;
+    constexpr int WM = Cfg::WM, WN = Cfg::WN, TI = Cfg::TI, TJ = Cfg::TJ;
+    static_assert(BM == 256 && BN == 256 && NS == 2, "256-column rows, two stages");
+    constexpr int ROWB = 512, SA = 64 * ROWB, SB = 2 * SA, HW = NW / 2, IPW = (SA / 1024) / HW;
+    static_assert(IPW * HW * 1024 == SA, "whole requests per wave");
+    __shared__ __attribute__((aligned(16))) char smem[NS * SB];
+
+    const int64_t M = p.M, N = p.N, lda = p.lda, ldb = p.ldb, ldc = p.ldc;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
+    const int64_t TM = (M + BM - 1) / BM, TN = (N + BN - 1) / BN;
+    const int64_t split = (int64_t)blockIdx.x / (TM * TN);
+    const int64_t kb = split * p.ksplit;
+    const int64_t K = (p.K - kb) < p.ksplit ? (p.K - kb) : p.ksplit;
+    C += split * M * ldc;
+    int64_t tm, tn;
+    tile_of((int64_t)blockIdx.x % (TM * TN), TM, TN, p.gm, &tm, &tn);
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+    // copies: waves 0 .. HW - 1 take A's requests, the others B's; request q
+    // fills rows 2q, 2q + 1 of the operand's k-tile, lane l position l % 32
+    // of row 2q + l / 32.  Columns past M or N repeat the last whole piece
+    // (loaded, never stored).
+    const bool isA = wave < HW;
+    const int q0 = (isA ? wave : wave - HW) * IPW;
+    const int64_t ld = isA ? lda : ldb, c0 = isA ? m0 : n0, cols = isA ? M : N;
+    const char *wbase = (const char *)((isA ? A : B) + (kb + 2 * q0) * ld);
+    uint32_t voff[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int row = 2 * (q0 + i) + lane / 32;
+        int64_t col = c0 + 8 * tr_piece(lane % 32, row);
+        if (col > cols - 8) col = cols - 8;
+        voff[i] = (uint32_t)(((int64_t)(2 * i + lane / 32) * ld + col) * 2);
+    }
+    const uint32_t qbase = lds0 + (isA ? 0 : SA) + q0 * 1024;
+    const int64_t KT = K / 64, kstep = 64 * ld * 2;
+    auto issue = [&](int64_t kt, int st) {
+        const char *b = wbase + (kt < KT ? kt : KT - 1) * kstep;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) dma16s(b, voff[i], qbase + st * SB + i * 1024);
+    };
+
+    f32x16 acc[TI][TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // operand of columns c .. c + 31 (c a multiple of 32) at k-step ks: lane
+    // l gets column c + l % 32, k = 16 ks + 8 (l / 32) + 0..7
+    const int g = lane >> 4, pl = lane & 15;
+    auto frag = [&](int st, int region, int c, int ks) -> bf16x8 {
+        const int col = c + 16 * (g & 1) + 4 * (pl & 3);
+        const int P = col >> 3, h8 = (col >> 2) & 1;
+        const int r0 = 16 * ks + 8 * (g >> 1) + (pl >> 2), r1 = r0 + 4;
+        typedef __attribute__((address_space(3))) i16x4 *lds_p;
+        const char *base = smem + st * SB + region + h8 * 8;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_p)(base + r0 * ROWB + tr_pos(P, r0) * 16));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_p)(base + r1 * ROWB + tr_pos(P, r1) * 16));
+        const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, v);
+    };
+
+    issue(0, 0);
+    for (int64_t kt = 0; kt < KT; ++kt) {
+        const int st = (int)(kt & 1);
+        wait_vmcnt<0>();
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+        bf16x8 a[2][TI], b[2][TJ];
+        auto rd = [&](int buf, int ks) {
+#pragma unroll
+            for (int i = 0; i < TI; ++i) a[buf][i] = frag(st, 0, wm * WM + 32 * i, ks);
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) b[buf][j] = frag(st, SA, wn * WN + 32 * j, ks);
+        };
+        rd(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(kt + 1, st ^ 1);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int cur = ks & 1;
+            if (ks < 3) rd(cur ^ 1, ks + 1);
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j],
+                                                                        acc[i][j], 0, 0, 0);
+            if (ks < 3) {   // the fragment reads spread among the MFMAs
+                constexpr int NF = 2 * (TI + TJ), MF = TI * TJ;
+#pragma unroll
+                for (int t = 0; t < NF; ++t) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, MF / NF > 0 ? MF / NF : 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    wait_vmcnt<0>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+
+    // epilogue as gemm_lds's (16-row halves of each 32-row band through LDS)
+    constexpr int EPI_LD = Cfg::EPI_LD, C4 = WN / 4;
+    static_assert(NW * 16 * EPI_LD * 4 <= NS * SB, "epilogue staging fits");
+    float *stage = (float *)smem + wave * (16 * EPI_LD);
+    const int64_t nw = n0 + wn * WN;
+    const bool vec = N % 4 == 0 && ldc % 4 == 0 && ((uintptr_t)C & 15u) == 0;
+    const bool accumulate = p.accumulate;
+    const int r32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                for (int r = 8 * h; r < 8 * h + 8; ++r)
+                    stage[(8 * (r / 4 - 2 * h) + 4 * hi + (r % 4)) * EPI_LD + j * 32 + r32] =
+                        acc[i][j][r];
+            const int64_t mw = m0 + wm * WM + i * 32 + 16 * h;
+#pragma unroll 4
+            for (int it = 0; it < 16 * C4 / 64; ++it) {
+                const int idx = it * 64 + lane;
+                const int row = idx / C4, c4 = idx % C4;
+                const int64_t m = mw + row, n = nw + c4 * 4;
+                const float4 v = *(const float4 *)(stage + row * EPI_LD + c4 * 4);
+                if (m >= M) continue;
+                float *q = C + m * ldc + n;
+                if (vec) {
+                    if (n < N) {
+                        float4 o = v;
+                        if (accumulate) {
+                            const float4 c = *(const float4 *)q;
+                            o.x += c.x; o.y += c.y; o.z += c.z; o.w += c.w;
+                        }
+                        *(float4 *)q = o;
+                    }
+                } else {
+                    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) q[e] = accumulate ? q[e] + vv[e] : vv[e];
+                }
+            }
+        }
+    }
+}
+
+// The weight-gradient products (A as [K, M], B as [K, N]) gemm_lds_t takes:
+// bf16 operands, whole 64-deep k-tiles per split, 16-byte aligned rows and
+// columns in whole 16-byte pieces (M, N multiples of 8), no batches, row
+// strides below 2^24 elements.
+bool lds_t_ok(const GemmArgs &g)
+{
+    if (!g.a_bf16 || !g.b_bf16 || g.K % 64 != 0 || g.batch > 1) return false;
+    const int64_t lda = g.lda ? g.lda : g.M, ldb = g.ldb ? g.ldb : g.N;
+    auto al16 = [](const void *q) { return ((uintptr_t)q & 15u) == 0; };
+    return g.M % 8 == 0 && g.N % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0 && al16(g.A) &&
+           al16(g.Bm) && lda < (int64_t(1) << 24) && ldb < (int64_t(1) << 24);
+}
+
 // The bf16 x bf16^T products that gemm_lds takes: whole 64-deep k-tiles,
 // 16-byte aligned operand rows and batch offsets, and row strides below 2^24
 // elements (a wave's 64 rows then span less than 2^31 bytes: 32-bit lane
@@ -1181,14 +1390,47 @@ WgradPlan wgrad_plan(int64_t M, int64_t N, int64_t K)
     return best;
 }
 
+// The weight gradient on the K-major LDS-copy kernel (256 x 256 tiles);
+// splits as mfma_launch_cfg's.
+hipError_t lds_t_launch(const GemmArgs &g, hipStream_t s, int64_t splits, int64_t ksplit,
+                        float *ws)
+{
+    MM p;
+    p.M = g.M;
+    p.N = g.N;
+    p.K = g.K;
+    p.lda = g.lda ? g.lda : g.M;
+    p.ldb = g.ldb ? g.ldb : g.N;
+    p.ldc = g.ldc ? g.ldc : g.N;
+    p.sa = p.sb = p.sc = 0;
+    p.gm = 8;
+    p.ksplit = splits > 1 ? ksplit : g.K;
+    p.accumulate = splits > 1 ? false : g.accumulate;
+    float *C = g.C;
+    if (splits > 1) {
+        C = ws;
+        p.ldc = g.N;
+    }
+    const int64_t tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256) * (splits > 1 ? splits : 1);
+    hipLaunchKernelGGL((gemm_lds_t<LdsBig>), dim3((unsigned)tiles), dim3(LdsBig::NT), 0, s, p,
+                       (const bf16_bits *)g.A, (const bf16_bits *)g.Bm, C);
+    return hipGetLastError();
+}
+
 template <class Cfg, typename TA, typename TB>
 hipError_t wgrad_launch_cfg(const GemmArgs &g, int64_t sp, float *ws, hipStream_t s)
 {
-    if (sp <= 1) return mfma_launch_cfg<Cfg, TA, true, TB, true>(g, s);
+    // bf16 operands on the 256 x 256 plan: the LDS-copy kernel
+    constexpr bool lds_t = std::is_same<TA, bf16_bits>::value &&
+                           std::is_same<TB, bf16_bits>::value && Cfg::BM == 256 && Cfg::BN == 256;
+    const bool use_t = lds_t && lds_t_ok(g);
+    if (sp <= 1) return use_t ? lds_t_launch(g, s, 1, 0, nullptr)
+                              : mfma_launch_cfg<Cfg, TA, true, TB, true>(g, s);
     const int64_t kt = g.K / Cfg::BK;
     const int64_t ksplit = ((kt + sp - 1) / sp) * Cfg::BK;
     const int64_t used = (g.K + ksplit - 1) / ksplit;      // splits with work
-    hipError_t e = mfma_launch_cfg<Cfg, TA, true, TB, true>(g, s, used, ksplit, ws);
+    hipError_t e = use_t ? lds_t_launch(g, s, used, ksplit, ws)
+                         : mfma_launch_cfg<Cfg, TA, true, TB, true>(g, s, used, ksplit, ws);
     if (e != hipSuccess) return e;
     const int64_t n = g.M * g.N;
     hipLaunchKernelGGL(split_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ws, n,

@@ -440,11 +440,17 @@ def test_projection_bwd_weight(L, B, d, nd):
 
 
 # 256 x 256 tiles: split 16 ways (ragged M = 1800 and N = 300, K = 8192), and
-# unsplit (M = 7800, N = 1300, K = 2048).  Sampled rows of dW (the first and
-# last ragged tiles included) against the oracle on the bf16 operands, with
-# and without accumulation; the split sums are deterministic.
-@pytest.mark.parametrize("L,B,d,nd", [(128, 64, 300, 2), (64, 32, 1300, 2)])
-def test_projection_bwd_weight_large_tiles(L, B, d, nd):
+# unsplit (M = 7800, N = 1300, K = 2048).  With bf16 X and M, N multiples of 8
+# the product copies both K-major operands into LDS and reads them back
+# transposed: split 16 ways (M = 1536, N = 512, K = 8192), 3 ways with ragged
+# tiles (M = 3288, N = 1096, K = 2048) and unsplit (M = 6144, N = 2048,
+# K = 1024).  Sampled rows of dW (the first and last ragged tiles included)
+# against the oracle on the bf16 operands, with and without accumulation;
+# the split sums are deterministic.
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+@pytest.mark.parametrize("L,B,d,nd", [(128, 64, 300, 2), (64, 32, 1300, 2), (128, 64, 512, 1),
+                                      (64, 32, 1096, 1), (32, 32, 2048, 1)])
+def test_projection_bwd_weight_large_tiles(L, B, d, nd, xdt):
     import torch
     rng = np.random.default_rng(5500 + d)
     M, n3 = L * B, nd * 3 * d
@@ -452,15 +458,19 @@ def test_projection_bwd_weight_large_tiles(L, B, d, nd):
     X = rng.standard_normal((L, B, d)).astype(np.float32)
     Gb_bits, Gb = workloads.to_bf16(rng.standard_normal((L, B, nd, 3, d)).astype(np.float32))
     Gbd = torch.from_numpy(Gb_bits.view(np.int16)).cuda().view(torch.bfloat16)
-    Xd = torch.from_numpy(X).cuda()
-    print(f"case K={M} M={n3} N={d}", flush=True)
+    if xdt == "bf16":
+        Xb_bits, _ = workloads.to_bf16(X)
+        Xd = torch.from_numpy(Xb_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        Xd = torch.from_numpy(X).cuda()
+    print(f"case K={M} M={n3} N={d} X {xdt}", flush=True)
     rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(n3 - 40, n3),
                                      rng.integers(0, n3, 24)]))
     G2 = Gb.reshape(M, n3)
     want = oracle.matmul(np.ascontiguousarray(G2[:, rows]), oracle.round_bf16(X.reshape(M, d)),
                          a_km=True)
     dW = layer.project_bwd_weight(shape, Gbd, Xd)
-    check("dW (bf16 dU, f32 X; sampled rows)", host(dW)[rows], want, GEMM_ACC)
+    check(f"dW (bf16 dU, {xdt} X; sampled rows)", host(dW)[rows], want, GEMM_ACC)
     C0 = rng.standard_normal((n3, d)).astype(np.float32)
     dW2 = torch.from_numpy(C0.copy()).cuda()
     layer.project_bwd_weight(shape, Gbd, Xd, dW2, accumulate=True)
