@@ -638,9 +638,9 @@ def cpu_baseline(w, budget_s=10.0):
 # kernel launches of one call of each row (what its event-timed span covers)
 ROW_LAUNCHES = {
     "a1_round_x": ["round_bf16_kernel (X~ = bf16(X))"],
-    "a1_projection": ["gemm_lds (X~ x W, operands copied straight into LDS) after a1_round_x, "
-                      "or gemm_bf16_mfma (A = fp32 X, rounded to bf16 while staged); see "
-                      "config.projection_x"],
+    "a1_projection": ["gemm_lds (X~ x W, operands copied straight into LDS; 256x256 tiles of "
+                      "16 waves) after a1_round_x, or gemm_bf16_mfma (A = fp32 X, rounded to "
+                      "bf16 while staged); see config.projection_x"],
     "a2_forward": ["fwd_fast (both directions in one grid)"],
     "a3_a4_backward": ["bwd_fast (fp32 inputs, up to 128 steps; both directions in one "
                        "launch when bidirectional and L <= 64, else one per direction, the "
@@ -650,8 +650,9 @@ ROW_LAUNCHES = {
                                "gemm_lds (bf16 dU copy x bf16 W, operands copied straight into LDS)"],
     "a6_linear_forward": ["scan_clear", "lin_fwd_fused"],
     "a7_linear_backward": ["scan_clear", "lin_bwd_fused", "lin_db_reduce"],
-    "f1_projection_bwd_weight": ["gemm_bf16_mfma (A = bf16 dU copy and B = fp32 X, both read "
-                                 "along L*B; the reduction split over blocks)",
+    "f1_projection_bwd_weight": ["gemm_lds_t (A = bf16 dU copy and B = bf16 X~, both read "
+                                 "along L*B, copied straight into LDS and read back transposed) "
+                                 "or gemm_bf16_mfma (fp32 X); the reduction split over blocks",
                                  "split_reduce (partial sums added in split order)"],
     "f3_factored_forward": ["gemm_bf16_mfma (Q = X Wq^T)", "gemm_bf16_mfma (U = Q Wo^T)"],
     "f4_decode_step_B1": [f"step_cell x {DECODE_STEPS} (one call per step, state in place, "
@@ -659,10 +660,11 @@ ROW_LAUNCHES = {
     "f2_attention_forward": ["gemm_bf16_mfma (Q = X Wq^T)", "gemm_bf16_mfma ([K|V] = Q Wkv^T, "
                              "bf16 out)", "attn_v_transpose (V^T tiles)",
                              "attn_fwd_fused (scores, online softmax, weights x V, "
-                             "R = layernorm(Q + alpha A))",
-                             "gemm_bf16_mfma (U = R Wo^T)"],
+                             "R = layernorm(Q + alpha A) and its bf16 copy R~)",
+                             "gemm_lds (U = R~ Wo^T, operands copied straight into LDS)"],
     "f2_attention_backward": ["the forward's scores, softmax and A again (3 launches)",
-                              "transpose16 (Wo^T) + gemm_lds (dR = dU Wo, bf16 dU)",
+                              "transpose16 (Wo^T) + gemm_lds (dR = dU Wo, bf16 dU; 256x128 "
+                              "tiles in three stages)",
                               "gemm + split_reduce (dWo)",
                               "attn_residual_bwd + attn_part_reduce", "gemm (dP = dO V^T)",
                               "attn_softmax_bwd", "gemm (dQ += dS' K)", "gemm TN (dK, dV)",
