@@ -1024,14 +1024,17 @@ WsLayout ws_layout(int64_t L, int64_t B, int64_t dp, int64_t Lm)
 // t*B + b), P = the masked softmax of S / sqrt(d') in bf16, and O_b = P_b V_b
 // into O's rows t*B + b.
 hipError_t attend(int64_t L, int64_t B, int64_t dp, int64_t Lm, int causal, const float *Q,
-                  const bf16_bits *KV, float *S, bf16_bits *P, float *O, hipStream_t s)
+                  const bf16_bits *KV, float *S, bf16_bits *P, float *O, hipStream_t s,
+                  const bf16_bits *Qb = nullptr)
 {
     const int64_t Lk = Lm + L;
     hipError_t e;
-    {
+    {   // with Qb (Q rounded to bf16, the values the product would round Q to)
+        // both operands are bf16 rows along d' and go straight into LDS
         GemmArgs g;
         g.M = L, g.N = Lk, g.K = dp;
-        g.A = Q, g.a_bf16 = false, g.lda = B * dp, g.sa = dp;
+        g.A = Qb ? (const void *)Qb : (const void *)Q, g.a_bf16 = Qb != nullptr;
+        g.lda = B * dp, g.sa = dp;
         g.Bm = KV, g.b_bf16 = true, g.b_kn = false, g.ldb = B * 2 * dp, g.sb = 2 * dp;
         g.C = S, g.ldc = Lk, g.sc = L * Lk, g.accumulate = false;
         g.batch = B;
@@ -1050,7 +1053,7 @@ hipError_t attend(int64_t L, int64_t B, int64_t dp, int64_t Lm, int causal, cons
 // Workspace of the backward (bytes, each region 256-byte aligned).
 struct BwdLayout {
     size_t s_off, p_off, dp_off, dsp_off, o_off, dr_off, dq_off, do_off, dkv_off, d_off,
-        part_off, wg_off, wot_off, total;
+        part_off, wg_off, wot_off, qb_off, rb_off, dob_off, total;
     int64_t nblk;
 };
 
@@ -1078,6 +1081,12 @@ BwdLayout bwd_layout(int64_t L, int64_t B, int64_t d, int64_t dp, int64_t Lm, in
     w.d_off = take(LB * 4);
     w.part_off = take((size_t)w.nblk * (size_t)(2 * dp + 1) * 4);
     w.wot_off = take((size_t)n3 * (size_t)dp * 2);                 // Wo^T, for a bf16 dU
+    // Q, R and dO rounded to bf16: the values the products would round them
+    // to as they load them, made once so that both operands of those products
+    // are bf16 (copied straight into LDS)
+    w.qb_off = take(LB * dp * 2);
+    w.rb_off = take(LB * dp * 2);
+    w.dob_off = take(LB * dp * 2);
     size_t wg = wgrad_workspace_bytes(n3, dp, (int64_t)LB);
     const size_t w2 = wgrad_workspace_bytes(2 * dp, dp, (int64_t)LB);
     const size_t w3 = wgrad_workspace_bytes(dp, d, (int64_t)LB);
@@ -1114,10 +1123,15 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
     float *D = (float *)(ws + w.d_off);
     float *part = (float *)(ws + w.part_off);
     float *wg = (float *)(ws + w.wg_off);
+    bf16_bits *Qb = (bf16_bits *)(ws + w.qb_off);
+    bf16_bits *Rb = (bf16_bits *)(ws + w.rb_off);
+    bf16_bits *dOb = (bf16_bits *)(ws + w.dob_off);
     const bf16_bits *KV = a.KV;
     hipError_t e;
+    if ((e = launch_round_bf16(LB * dp, a.Q, Qb, s)) != hipSuccess) return e;
+    if ((e = launch_round_bf16(LB * dp, a.R, Rb, s)) != hipSuccess) return e;
     // the forward's weights and A, recomputed from Q and KV
-    if ((e = attend(L, B, dp, Lm, a.causal, a.Q, KV, S, P, O, s)) != hipSuccess) return e;
+    if ((e = attend(L, B, dp, Lm, a.causal, a.Q, KV, S, P, O, s, Qb)) != hipSuccess) return e;
     {   // dR [LB, d'] = dU Wo: with a bf16 dU, Wo^T [d', n3] is formed first so
         // that both operands are bf16 rows along the reduction (the kernel that
         // copies them straight into LDS); with an fp32 dU, Wo is read as [K, N]
@@ -1139,7 +1153,7 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
         GemmArgs g;
         g.M = n3, g.N = dp, g.K = LB;
         g.A = a.dU, g.a_bf16 = a.du_bf16;
-        g.Bm = a.R, g.b_bf16 = false;
+        g.Bm = Rb, g.b_bf16 = true;
         g.C = a.dWo, g.accumulate = false;
         if ((e = launch_gemm_wgrad(g, false, wg, s)) != hipSuccess) return e;
     }
@@ -1162,11 +1176,12 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
                            a.layernorm ? a.dgamma : nullptr, a.layernorm ? a.dbeta : nullptr,
                            a.dalpha);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_round_bf16(LB * dp, dO, dOb, s)) != hipSuccess) return e;
     }
     {   // dP_b [L, Lk] = dO~_b V~_b^T
         GemmArgs g;
         g.M = L, g.N = Lk, g.K = dp;
-        g.A = dO, g.a_bf16 = false, g.lda = B * dp, g.sa = dp;
+        g.A = dOb, g.a_bf16 = true, g.lda = B * dp, g.sa = dp;
         g.Bm = KV + dp, g.b_bf16 = true, g.b_kn = false, g.ldb = B * 2 * dp, g.sb = 2 * dp;
         g.C = dP, g.ldc = Lk, g.sc = L * Lk, g.accumulate = false;
         g.batch = B;
@@ -1216,7 +1231,7 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
         GemmArgs g;
         g.M = L, g.N = dp, g.K = L;
         g.A = dSp + Lm, g.a_bf16 = true, g.lda = Lk, g.sa = L * Lk;
-        g.Bm = a.Q, g.b_bf16 = false, g.ldb = B * dp, g.sb = dp;
+        g.Bm = Qb, g.b_bf16 = true, g.ldb = B * dp, g.sb = dp;
         g.C = dKV, g.ldc = B * 2 * dp, g.sc = 2 * dp, g.accumulate = false;
         g.batch = B;
         if ((e = launch_gemm_tn(g, s)) != hipSuccess) return e;
@@ -1225,7 +1240,7 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
         GemmArgs g;
         g.M = L, g.N = dp, g.K = L;
         g.A = P + Lm, g.a_bf16 = true, g.lda = Lk, g.sa = L * Lk;
-        g.Bm = dO, g.b_bf16 = false, g.ldb = B * dp, g.sb = dp;
+        g.Bm = dOb, g.b_bf16 = true, g.ldb = B * dp, g.sb = dp;
         g.C = dKV + dp, g.ldc = B * 2 * dp, g.sc = 2 * dp, g.accumulate = false;
         g.batch = B;
         if ((e = launch_gemm_tn(g, s)) != hipSuccess) return e;
@@ -1234,7 +1249,7 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
         GemmArgs g;
         g.M = 2 * dp, g.N = dp, g.K = LB;
         g.A = dKV, g.a_bf16 = false;
-        g.Bm = a.Q, g.b_bf16 = false;
+        g.Bm = Qb, g.b_bf16 = true;
         g.C = a.dWkv, g.accumulate = false;
         if ((e = launch_gemm_wgrad(g, false, wg, s)) != hipSuccess) return e;
     }
