@@ -625,13 +625,13 @@ template <class Cfg, typename TA> struct LdsStage {
 // that fill the chip (four waves per SIMD hide more of the barrier and LDS
 // latency than two).  256 x 128 tiles, 8 waves of 64 x 64, three stages: long
 // reductions where the large tiles would leave CUs idle but these fill them
-// (N = 512).  128 x 128 tiles, 8 waves, four stages (one block per CU): long
-// reductions on smaller grids, where an operand streamed from HBM needs
-// requests several k-tiles ahead.  128 x 128 tiles, 4 waves, two stages (two
+// (N = 512).  128 x 128 tiles, 16 waves of 32 x 32, four stages (one block
+// per CU): long reductions on smaller grids, where an operand streamed from
+// HBM needs requests several k-tiles ahead.  128 x 128 tiles, 4 waves, two stages (two
 // blocks per CU): short reductions.
 typedef LdsCfg<256, 256, 2, 4, 4, 1> LdsBig;
 typedef LdsCfg<256, 128, 3, 4, 2, 1> LdsMid;
-typedef LdsCfg<128, 128, 4, 2, 4, 1> LdsDeep;
+typedef LdsCfg<128, 128, 4, 4, 4, 1> LdsDeep;
 typedef LdsCfg<128, 128, 2, 2, 2, 2> LdsSmall;
 
 template <class Cfg, typename TA, typename TC>
