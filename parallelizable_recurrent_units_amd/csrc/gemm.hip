@@ -277,6 +277,17 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t TM, int64_t TN, int
     *tn = in / gsz;
 }
 
+// Row tiles per group of the tile order.  When the tiles of one XCD's share
+// (T / 8) are whole rows of column tiles, one group is that share, so each
+// row block of A is read by one XCD only (the projection on fp32 X at L*B =
+// 8192, 3d = 3072: 4 row tiles of 16); otherwise groups of 8 row tiles.
+inline int64_t group_rows(int64_t M, int64_t N, int64_t bm, int64_t bn)
+{
+    const int64_t TM = (M + bm - 1) / bm, TN = (N + bn - 1) / bn, T8 = TM * TN / 8;
+    if (T8 >= TN && T8 % TN == 0 && T8 / TN <= 8) return T8 / TN;
+    return 8;
+}
+
 // Shape, strides and options of one launch (passed by value).
 struct MM {
     int64_t M, N, K;
@@ -1060,7 +1071,7 @@ hipError_t lds_launch_cfg(const GemmArgs &g, hipStream_t s)
     p.sb = g.sb;
     p.sc = g.sc;
     p.ksplit = g.K;
-    p.gm = 8;
+    p.gm = (int)group_rows(g.M, g.N, Cfg::BM, Cfg::BN);
     p.accumulate = g.accumulate;
     const int64_t tiles = ((g.M + Cfg::BM - 1) / Cfg::BM) * ((g.N + Cfg::BN - 1) / Cfg::BN);
     hipLaunchKernelGGL((gemm_lds<Cfg, TA, TC>),
@@ -1272,7 +1283,7 @@ hipError_t mfma_launch_cfg(const GemmArgs &g, hipStream_t s, int64_t splits = 1,
     p.sa = g.sa;
     p.sb = g.sb;
     p.sc = g.sc;
-    p.gm = 8;
+    p.gm = (int)group_rows(g.M, g.N, Cfg::BM, Cfg::BN);
     p.ksplit = splits > 1 ? ksplit : g.K;
     p.accumulate = splits > 1 ? false : g.accumulate;
     const int64_t batch = g.batch > 0 ? g.batch : 1;
