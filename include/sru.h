@@ -158,7 +158,11 @@ sru_status sru_project(const sru_shape *shape, sru_proj_op op,
  * math_dt = SRU_F32: fp32 arithmetic throughout (bf16 inputs widened).
  * accumulate = 0 overwrites dW, 1 adds to it.
  * workspace: sru_workspace_size(shape, SRU_WS_BWD_WEIGHT, 0) bytes of device
- *   memory, 256-byte aligned (may be NULL when that size is 0); scratch.
+ *   memory, 256-byte aligned (may be NULL when that size is 0); scratch: the
+ *   split partial sums, then room for X rounded to bf16, which a bf16 dU with
+ *   an fp32 X is multiplied with when the workspace has that room (the same
+ *   values the product would round X to; a smaller workspace that still
+ *   holds the partial sums is accepted and takes the product without it).
  */
 sru_status sru_project_bwd_weight(const sru_shape *shape,
                                   const void *dU, sru_dtype du_dt,

@@ -159,9 +159,16 @@ sru_status no_overlap(const Span *out, int nout, const Span *in, int nin)
     return SRU_OK;
 }
 
+// Workspace a product needs (the weight gradient's partial sums) ...
 size_t product_ws(Layout lay, int64_t M, int64_t N, int64_t K)
 {
     return lay == Layout::TN ? round256(sru::wgrad_workspace_bytes(M, N, K)) : 0;
+}
+// ... and what the workspace queries report: room for a bf16 copy of an
+// fp32 B as well, which the weight gradient uses when it is given that much
+size_t product_ws_query(Layout lay, int64_t M, int64_t N, int64_t K)
+{
+    return product_ws(lay, M, N, K) + (lay == Layout::TN ? sru::wgrad_b_copy_bytes(M, N, K) : 0);
 }
 
 // Validates and launches one product.  bf16 math: MFMA on operands rounded
@@ -213,8 +220,11 @@ sru_status run_product(Layout lay, int64_t M, int64_t N, int64_t K, const void *
     g.b_kn = lay != Layout::NT;
     g.C = C;
     g.accumulate = accumulate != 0;
-    if (lay == Layout::TN)
-        return launched(sru::launch_gemm_wgrad(g, f32_math, (float *)workspace, stream), what);
+    if (lay == Layout::TN) {
+        const bool b_copy = workspace && workspace_bytes >= product_ws_query(lay, M, N, K);
+        return launched(sru::launch_gemm_wgrad(g, f32_math, (float *)workspace, stream, b_copy),
+                        what);
+    }
     return launched(sru::launch_gemm(g, stream), what);
 }
 
@@ -256,15 +266,15 @@ size_t sru_workspace_size(const sru_shape *shape, sru_ws_op op, int32_t chunk)
                                                     chunk, op == SRU_WS_LINEAR_BWD));
     case SRU_WS_BWD_WEIGHT:
         ok();
-        return round256(sru::wgrad_workspace_bytes(3 * dm.ndir * shape->d, shape->d, dm.LB));
+        return product_ws_query(Layout::TN, 3 * dm.ndir * shape->d, shape->d, dm.LB);
     case SRU_WS_FACTORED_WEIGHT: {
         const int64_t di = chunk;   // the inner dimension d'
         if (di < 1) {
             fail(SRU_ERR_INVALID_ARG, "the inner dimension must be >= 1 (got %d)", (int)chunk);
             return 0;
         }
-        const size_t a = product_ws(Layout::TN, di, shape->d, dm.LB);
-        const size_t b = product_ws(Layout::TN, 3 * dm.ndir * shape->d, di, dm.LB);
+        const size_t a = product_ws_query(Layout::TN, di, shape->d, dm.LB);
+        const size_t b = product_ws_query(Layout::TN, 3 * dm.ndir * shape->d, di, dm.LB);
         ok();
         return a > b ? a : b;
     }

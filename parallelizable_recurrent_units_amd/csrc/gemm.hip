@@ -1512,8 +1512,29 @@ size_t wgrad_workspace_bytes(int64_t M, int64_t N, int64_t K)
     return sp <= 1 ? 0 : (size_t)(sp * M * N) * sizeof(float);
 }
 
-hipError_t launch_gemm_wgrad(const GemmArgs &g, bool f32_math, float *ws, hipStream_t s)
+size_t wgrad_b_copy_bytes(int64_t M, int64_t N, int64_t K)
 {
+    const WgradPlan pl = wgrad_plan(M, N, K);
+    if (!pl.big || M % 8 != 0 || N % 8 != 0 || K % 64 != 0) return 0;
+    return ((size_t)K * (size_t)N * 2 + 255) & ~(size_t)255;
+}
+
+hipError_t launch_gemm_wgrad(const GemmArgs &g, bool f32_math, float *ws, hipStream_t s,
+                             bool b_copy)
+{
+    // bf16 A, fp32 B: B rounded into the workspace (after the partial sums)
+    // gives the bf16 operands the K-major LDS-copy kernel takes, with the
+    // values the product would round B to as it loads it
+    if (b_copy && !f32_math && g.a_bf16 && !g.b_bf16 && ws && g.batch <= 1 &&
+        (g.ldb == 0 || g.ldb == g.N) && wgrad_b_copy_bytes(g.M, g.N, g.K) > 0) {
+        const size_t part = (wgrad_workspace_bytes(g.M, g.N, g.K) + 255) & ~(size_t)255;
+        bf16_bits *Bb = (bf16_bits *)((char *)ws + part);
+        hipError_t e = launch_round_bf16(g.K * g.N, (const float *)g.Bm, Bb, s);
+        if (e != hipSuccess) return e;
+        GemmArgs g2 = g;
+        g2.Bm = Bb, g2.b_bf16 = true, g2.ldb = g.N;
+        return wgrad_launch<bf16_bits, bf16_bits>(g2, ws, s);
+    }
     if (f32_math) {
         if (g.a_bf16)
             return g.b_bf16 ? f32_launch<bf16_bits, true, bf16_bits, true>(g, s)

@@ -113,7 +113,13 @@ hipError_t launch_gemm_bf16_out(const GemmArgs &g, hipStream_t s);
 // reduction over K split across blocks when the output alone would not
 // fill the chip (ws then holds the partial products).
 size_t wgrad_workspace_bytes(int64_t M, int64_t N, int64_t K);
-hipError_t launch_gemm_wgrad(const GemmArgs &g, bool f32_math, float *ws, hipStream_t s);
+// Bytes after the partial sums that hold a bf16 copy of an fp32 B when
+// launch_gemm_wgrad is given b_copy (0 where the copy would not be used: the
+// product then keeps the register-staged kernel).  With b_copy the
+// workspace must hold wgrad_workspace_bytes rounded up to 256, then these.
+size_t wgrad_b_copy_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_wgrad(const GemmArgs &g, bool f32_math, float *ws, hipStream_t s,
+                             bool b_copy = false);
 // C[M, N] (+)= A^T B with A given as [K, M] and B as [K, N] (bf16 or fp32
 // each, rounded to bf16 while staged; row strides and batches as in
 // GemmArgs), bf16 MFMA, no split of the reduction and no workspace.

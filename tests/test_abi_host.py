@@ -68,7 +68,8 @@ def test_workspace_sizes(lib, L, B, d, bi):
         assert sru.sru_workspace_size(s, sru.SRU_WS_LINEAR_FWD, chunk) == round256((3 * nC * B * d + 64) * 4)
         assert sru.sru_workspace_size(s, sru.SRU_WS_LINEAR_BWD, chunk) == round256((5 * nC * B * d + 64) * 4)
     # weight gradient: the split-reduction workspace of [ndir*3d, d] = dU^T X
-    assert sru.sru_workspace_size(s, sru.SRU_WS_BWD_WEIGHT) == wgrad_ws(3 * nd * d, d, L * B)
+    # and room for a bf16 copy of an fp32 X
+    assert sru.sru_workspace_size(s, sru.SRU_WS_BWD_WEIGHT) == wgrad_query(3 * nd * d, d, L * B)
     assert lib.sru_workspace_size(ctypes.byref(s), sru.SRU_WS_LINEAR_FWD, 0) == 0
     assert b"chunk" in lib.sru_last_error()
     assert lib.sru_workspace_size(ctypes.byref(s), 9, 1) == 0
@@ -165,7 +166,7 @@ def wgrad(lib, s, ws_bytes, **kw):
 def test_bwd_weight_validation(lib):
     s = sru.SruShape(128, 16, 128, 0, 1.0)
     need = sru.sru_workspace_size(s, sru.SRU_WS_BWD_WEIGHT)
-    assert need > 0
+    assert need > 0 and need == wgrad_ws(384, 128, 2048)   # no copy on this plan
     assert wgrad(lib, s, need, dU=None) == sru.SRU_ERR_INVALID_ARG
     assert wgrad(lib, s, need, X=Q[1] + 2) == sru.SRU_ERR_INVALID_ARG
     assert wgrad(lib, s, need, du_dt=3) == sru.SRU_ERR_INVALID_ARG
@@ -182,27 +183,52 @@ def test_bwd_weight_validation(lib):
     # fp32 arithmetic needs no workspace
     if __import__("torch").cuda.device_count() == 0:
         assert wgrad(lib, s, 0, math=0, ws=None) == sru.SRU_ERR_NO_DEVICE
+    # the reported size adds room for a bf16 copy of an fp32 X (L = 512,
+    # B = 32, d = 1024: 256 x 256 plan in 5 splits); a workspace that holds
+    # only the partial sums is still accepted
+    s4 = sru.SruShape(512, 32, 1024, 0, 1.0)
+    part, full = wgrad_ws(3072, 1024, 16384), sru.sru_workspace_size(s4, sru.SRU_WS_BWD_WEIGHT)
+    assert full == part + 16384 * 1024 * 2 and part > 0
+    assert wgrad(lib, s4, part - 1) == sru.SRU_ERR_WORKSPACE
+    if __import__("torch").cuda.device_count() == 0:
+        assert wgrad(lib, s4, part) == sru.SRU_ERR_NO_DEVICE
+        assert wgrad(lib, s4, full) == sru.SRU_ERR_NO_DEVICE
     # no split: no workspace at all
     s1 = sru.SruShape(3, 5, 64, 0, 1.0)
     assert sru.sru_workspace_size(s1, sru.SRU_WS_BWD_WEIGHT) == 0
     assert lib.sru_last_error() == b""
 
 
-def wgrad_ws(M, N, K):
-    """Split-reduction workspace of one weight-gradient product: partial
-    products [splits, M, N] when the reduction over L*B is split (128 x 128
+def wgrad_plan(M, N, K):
+    """(splits, 256 x 256 tiles) of one weight-gradient product: 128 x 128
     output tiles in 512 block slots or 256 x 256 in 256, 64-deep k-tiles,
-    >= 8 k-tiles per split, cost in k-tile rounds plus M*N/1e6 per split)."""
+    >= 8 k-tiles per split, cost in k-tile rounds plus M*N/1e6 per split."""
     kt = K // 64
-    sp, best = 1, None
+    sp, big, best = 1, False, None
     if K % 64 == 0 and kt >= 16:
         for t, slots in ((128, 512), (256, 256)):
             tiles = -(-M // t) * -(-N // t)
             for n in range(1, min(kt // 8, 64) + 1):
                 cost = -(-tiles * n // slots) * -(-kt // n) + (M * N * 1e-6 * n if n > 1 else 0)
                 if best is None or cost < best:
-                    sp, best = n, cost
+                    sp, big, best = n, t == 256, cost
+    return sp, big
+
+
+def wgrad_ws(M, N, K):
+    """Split-reduction workspace of one weight-gradient product: partial
+    products [splits, M, N] when the reduction over L*B is split."""
+    sp, _ = wgrad_plan(M, N, K)
     return 0 if sp == 1 else round256(sp * M * N * 4)
+
+
+def wgrad_query(M, N, K):
+    """What the workspace queries report for it: the partial products, then
+    room for a bf16 copy of an fp32 [K, N] operand where the product would
+    take the K-major LDS-copy kernel (256 x 256 plan, M and N multiples of 8)."""
+    _, big = wgrad_plan(M, N, K)
+    copy = round256(K * N * 2) if big and M % 8 == 0 and N % 8 == 0 and K % 64 == 0 else 0
+    return wgrad_ws(M, N, K) + copy
 
 
 @pytest.mark.parametrize("L,B,d,bi,di", [(128, 16, 128, 0, 32), (64, 128, 512, 1, 128),
@@ -210,7 +236,7 @@ def wgrad_ws(M, N, K):
 def test_factored_workspace_size(lib, L, B, d, bi, di):
     s = sru.SruShape(L, B, d, bi, 1.0)
     n3 = 3 * (2 if bi else 1) * d
-    want = max(wgrad_ws(di, d, L * B), wgrad_ws(n3, di, L * B))
+    want = max(wgrad_query(di, d, L * B), wgrad_query(n3, di, L * B))
     assert sru.sru_workspace_size(s, sru.SRU_WS_FACTORED_WEIGHT, di) == want
     assert lib.sru_workspace_size(ctypes.byref(s), sru.SRU_WS_FACTORED_WEIGHT, 0) == 0
     assert b"inner" in lib.sru_last_error()

@@ -478,6 +478,14 @@ def test_projection_bwd_weight_large_tiles(L, B, d, nd, xdt):
     dW3 = layer.project_bwd_weight(shape, Gbd, Xd)
     torch.cuda.synchronize()
     assert torch.equal(dW.view(torch.int32), dW3.view(torch.int32))
+    if xdt == "f32" and d % 8 == 0 and n3 % 8 == 0:
+        # fp32 X is rounded into the workspace and takes the same kernel as a
+        # bf16 X of the same values: the same bits
+        Xb_bits, _ = workloads.to_bf16(X)
+        Xbd = torch.from_numpy(Xb_bits.view(np.int16)).cuda().view(torch.bfloat16)
+        dWb = layer.project_bwd_weight(shape, Gbd, Xbd)
+        torch.cuda.synchronize()
+        assert torch.equal(dW.view(torch.int32), dWb.view(torch.int32))
 
 
 def test_projection_bwd_weight_is_deterministic():
