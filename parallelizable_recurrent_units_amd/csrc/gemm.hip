@@ -603,6 +603,57 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_bf16_mfma(
 // once.  (fp32 A is not taken: converted as its fragments
 // are read, by every wave that reads them, it is slower than the register-
 // staged kernel, which converts each element once.)
+// ---- K-major operands in LDS: transposing reads ---------------------------
+// An operand stored K-major (rows along k, columns along M or N) keeps that
+// layout in LDS: a k-tile is 64 rows of the tile's 128 or 256 columns, copied
+// memory -> LDS in 1 KB requests of whole rows.  The MFMA operand (8
+// consecutive k of one column per lane) is read back with ds_read_b64_tr_b16:
+// within a group of 16 lanes, lane i receives the i-th 16-bit element of each
+// of the four 8-byte pieces that lanes 4j + i / 4 address (j = 0..3), so when
+// lanes 4j .. 4j + 3 address row k0 + j, columns c .. c + 15, lane i gets
+// column c + i at k0 .. k0 + 3, and two such reads give the 8 k of the
+// 32x32x16 operand.
+//
+// The 16-byte pieces of a row (P = 0..31, columns 8P .. 8P + 7; 0..15 for
+// 128 columns) are stored at position tr_pos(P, row): writing P = 4a + 2b +
+// c, position c + 2 (a mod 4) + 8 b + 16 (a / 4), XOR 2 (row mod 4).  A read
+// of 16 columns touches pieces 4a + 2b + {0, 1} of four consecutive rows: the
+// XOR spreads the four rows over four bank groups and b puts the two
+// 16-column halves of a 32-column block eight positions apart, so each
+// half-wave's 256 bytes fall on distinct banks (rows are 512 or 256 bytes,
+// whole bank lines).
+__device__ __forceinline__ int tr_pos(int P, int row)
+{
+    const int c = P & 1, b = (P >> 1) & 1, a = P >> 2;
+    return (c + 2 * (a & 3) + 8 * b + 16 * (a >> 2)) ^ (2 * (row & 3));
+}
+__device__ __forceinline__ int tr_piece(int pos, int row)   // the inverse of tr_pos
+{
+    const int q = pos ^ (2 * (row & 3));
+    return 4 * (((q >> 1) & 3) + 4 * (q >> 4)) + 2 * ((q >> 3) & 1) + (q & 1);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// The 32x32x16 operand of columns c .. c + 31 (c a multiple of 32) at k-step
+// ks from a K-major tile at `base` (rows of ROWB bytes): lane l gets column
+// c + l % 32, k = 16 ks + 8 (l / 32) + 0..7.
+template <int ROWB>
+__device__ __forceinline__ bf16x8 tr_frag(const char *base, int c, int ks, int lane)
+{
+    const int g = lane >> 4, pl = lane & 15;
+    const int col = c + 16 * (g & 1) + 4 * (pl & 3);
+    const int P = col >> 3, h8 = (col >> 2) & 1;
+    const int r0 = 16 * ks + 8 * (g >> 1) + (pl >> 2), r1 = r0 + 4;
+    typedef __attribute__((address_space(3))) i16x4 *lds_p;
+    const char *b = base + h8 * 8;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_p)(b + r0 * ROWB + tr_pos(P, r0) * 16));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_p)(b + r1 * ROWB + tr_pos(P, r1) * 16));
+    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
 // position key of a 128-byte LDS row (see above)
 __device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & 7; }
 
@@ -615,13 +666,16 @@ struct LdsCfg {
 };
 
 // Stage layout for an A of element type TA: BM rows of 64 A elements (128 or
-// 256 bytes), then BN rows of 64 bf16 of B (128 bytes); 1 KB requests.  The
-// first half of the waves copies A (IPWA requests each), the second half B
-// (IPWB each).
-template <class Cfg, typename TA> struct LdsStage {
+// 256 bytes), then B: BN rows of 64 bf16 (128 bytes), or with BKN (B stored
+// K-major, [K, N]) 64 k-rows of BN bf16 in the transposed-read layout of
+// tr_pos; 1 KB requests.  The first half of the waves copies A (IPWA
+// requests each), the second half B (IPWB each).
+template <class Cfg, typename TA, bool BKN = false> struct LdsStage {
     static constexpr int AROW = 64 * (int)sizeof(TA);   // bytes of one A row
     static constexpr int APR = AROW / 16;                // 16-byte pieces per A row
     static constexpr int A_BYTES = Cfg::BM * AROW;
+    static constexpr int BROW = BKN ? 2 * Cfg::BN : 128; // bytes of one B row in LDS
+    static constexpr int BRQ = 1024 / BROW;              // B rows per request
     static constexpr int BYTES = A_BYTES + Cfg::BN * 128;
     static constexpr int QA = A_BYTES / 1024;            // requests for A
     static constexpr int QB = Cfg::BN * 128 / 1024;      // requests for B
@@ -630,6 +684,7 @@ template <class Cfg, typename TA> struct LdsStage {
     static constexpr int IPW = IPWA > IPWB ? IPWA : IPWB;
     static_assert(IPWA * HW == QA && IPWB * HW == QB, "whole 1 KB requests per wave");
     static_assert(Cfg::NW * 16 * Cfg::EPI_LD * 4 <= Cfg::NS * BYTES, "epilogue staging fits");
+    static_assert(!BKN || Cfg::BN == 128 || Cfg::BN == 256, "K-major B: 128 or 256 columns");
 };
 
 // 256 x 256 tiles, 16 waves of 64 x 64, two stages: long reductions on grids
@@ -645,12 +700,12 @@ typedef LdsCfg<256, 128, 3, 4, 2, 1> LdsMid;
 typedef LdsCfg<128, 128, 4, 4, 4, 1> LdsDeep;
 typedef LdsCfg<128, 128, 2, 2, 2, 2> LdsSmall;
 
-template <class Cfg, typename TA, typename TC>
+template <class Cfg, typename TA, typename TC, bool BKN = false>
 __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *__restrict__ A,
                                                                const bf16_bits *__restrict__ B,
                                                                TC *__restrict__ C)
 {
-    typedef LdsStage<Cfg, TA> St;
+    typedef LdsStage<Cfg, TA, BKN> St;
     constexpr int BM = Cfg::BM, BN = Cfg::BN, NS = Cfg::NS, IPW = St::IPW;
     constexpr int WM = Cfg::WM, WN = Cfg::WN, TI = Cfg::TI, TJ = Cfg::TJ;
     constexpr int SB = St::BYTES, AROW = St::AROW, APR = St::APR;
@@ -672,17 +727,31 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
     // Request q fills 1 KB of the stage: 8 rows of A (q < QA) or of B, each
     // row's 128 bytes as eight 16-byte pieces; lane l takes piece l % 8 of row
     // l / 8, and in a row the piece at position s holds k-chunk s ^ lds_swz(row).
+    // With BKN a B request is BRQ k-rows of BN columns instead: lane l takes
+    // position l % (BN / 8) of k-row l / (BN / 8), which holds the piece
+    // tr_piece(position, row).
     // A wave's requests are all rows of A or all rows of B, so the wave keeps
     // one uniform base (its first row, at k = 0; a scalar register pair) and a
-    // 32-bit byte offset per lane and request.  Rows past M or N repeat the
-    // last row (loaded, never stored).
+    // 32-bit byte offset per lane and request.  Rows past M or N (columns past
+    // N for BKN) repeat the last row (piece): loaded, never stored.
     static_assert(sizeof(TA) == 2 && AROW == 128, "bf16 A");
     constexpr int IPWA = St::IPWA, IPWB = St::IPWB;
     const bool isA = wave < St::HW;                      // uniform
     const int q0 = isA ? wave * IPWA : St::QA + (wave - St::HW) * IPWB;   // first request
     const char *wbase;
     uint32_t voff[IPW];
-    {
+    if (BKN && !isA) {
+        constexpr int BPR = Cfg::BN / 8;                 // pieces per k-row
+        const int64_t r0 = (int64_t)(q0 - St::QA) * St::BRQ;   // the wave's first k-row
+        wbase = (const char *)(B + r0 * ldb);
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int rr = i * St::BRQ + lane / BPR;     // k-row from the wave's first
+            int64_t col = n0 + 8 * tr_piece(lane % BPR, (int)r0 + rr);
+            if (col > N - 8) col = N - 8;
+            voff[i] = (uint32_t)(((int64_t)rr * ldb + col) * 2);
+        }
+    } else {
         const int64_t r0 = isA ? q0 * 8 : (q0 - St::QA) * 8;   // the wave's first row in the tile
         const int64_t last = isA ? M - 1 - m0 : N - 1 - n0;     // last valid row in the tile
         const int64_t ld = isA ? lda : ldb;
@@ -697,10 +766,11 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
         }
     }
     const int64_t KT = K / 64;
+    const int64_t kstep = (BKN && !isA) ? 64 * ldb * 2 : 128;   // bytes per k-tile
     // requests of k-tile kt into stage st; past the last k-tile the last one
     // is requested again, so every iteration waits on the same count
     auto issue = [&](int64_t kt, int st) {
-        const char *kb = wbase + (kt < KT ? kt : KT - 1) * 128;
+        const char *kb = wbase + (kt < KT ? kt : KT - 1) * kstep;
         if (isA) {
 #pragma unroll
             for (int i = 0; i < IPWA; ++i)
@@ -726,7 +796,11 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
         const int c = 2 * ks + hi;
         return *(const bf16x8 *)(smem + st * SB + row * AROW + ((c ^ lds_swz(row)) << 4));
     };
+    // B: rows of [N, K] (row = the column of C), or with BKN the 32 columns
+    // from row - row % 32 of the K-major tile
     auto bfrag = [&](int st, int row, int ks) -> bf16x8 {
+        if constexpr (BKN)
+            return tr_frag<St::BROW>(smem + st * SB + St::A_BYTES, row - r32, ks, lane);
         const int c = 2 * ks + hi;
         return *(const bf16x8 *)(smem + st * SB + St::A_BYTES + row * 128 + ((c ^ lds_swz(row)) << 4));
     };
@@ -836,37 +910,9 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
 }
 
 // ---- both operands K-major: C (+)= A^T B with A [K, M], B [K, N] ----------
-// The weight gradient's layout (the reduction index L*B is the slow one).  A
-// k-tile of each operand is 64 rows of 256 columns (512 bytes); the copies
-// move it memory -> LDS in 1 KB requests of two rows, and the MFMA operands
-// (8 consecutive k of one column per lane) are read back with
-// ds_read_b64_tr_b16: within a group of 16 lanes, lane i receives the i-th
-// 16-bit element of each of the four 8-byte pieces that lanes 4j + i / 4
-// address (j = 0..3), so when lanes 4j .. 4j + 3 address row k0 + j, columns
-// c .. c + 15, lane i gets column c + i at k0 .. k0 + 3, and two such reads
-// give the 8 k of the 32x32x16 operand.
-//
-// The 16-byte pieces of a row (P = 0..31, columns 8P .. 8P + 7) are stored
-// at position tr_pos(P, row): writing P = 4a + 2b + c, position
-// c + 2 (a mod 4) + 8 b + 16 (a / 4), XOR 2 (row mod 4).  A read of 16
-// columns touches pieces 4a + 2b + {0, 1} of four consecutive rows: the XOR
-// spreads the four rows over four bank groups and b puts the two 16-column
-// halves of a 32-column block eight positions apart, so each half-wave's 256
-// bytes fall on distinct banks.
-__device__ __forceinline__ int tr_pos(int P, int row)
-{
-    const int c = P & 1, b = (P >> 1) & 1, a = P >> 2;
-    return (c + 2 * (a & 3) + 8 * b + 16 * (a >> 2)) ^ (2 * (row & 3));
-}
-__device__ __forceinline__ int tr_piece(int pos, int row)   // the inverse of tr_pos
-{
-    const int q = pos ^ (2 * (row & 3));
-    return 4 * (((q >> 1) & 3) + 4 * (q >> 4)) + 2 * ((q >> 3) & 1) + (q & 1);
-}
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-
+// The weight gradient's layout (the reduction index L*B is the slow one): a
+// k-tile of each operand is 64 rows of 256 columns, copied and read back as
+// described at tr_pos.
 // 256 x 256 tiles, 16 waves of 64 x 64, two stages.  With several splits
 // block s of a tile covers k in [s ksplit, (s + 1) ksplit) and writes its
 // partial product to C + s M ldc (summed in order by split_reduce).
@@ -928,19 +974,8 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds_t(MM p, const bf1
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // operand of columns c .. c + 31 (c a multiple of 32) at k-step ks: lane
-    // l gets column c + l % 32, k = 16 ks + 8 (l / 32) + 0..7
-    const int g = lane >> 4, pl = lane & 15;
     auto frag = [&](int st, int region, int c, int ks) -> bf16x8 {
-        const int col = c + 16 * (g & 1) + 4 * (pl & 3);
-        const int P = col >> 3, h8 = (col >> 2) & 1;
-        const int r0 = 16 * ks + 8 * (g >> 1) + (pl >> 2), r1 = r0 + 4;
-        typedef __attribute__((address_space(3))) i16x4 *lds_p;
-        const char *base = smem + st * SB + region + h8 * 8;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_p)(base + r0 * ROWB + tr_pos(P, r0) * 16));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_p)(base + r1 * ROWB + tr_pos(P, r1) * 16));
-        const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        return __builtin_bit_cast(bf16x8, v);
+        return tr_frag<ROWB>(smem + st * SB + region, c, ks, lane);
     };
 
     issue(0, 0);
@@ -1057,7 +1092,7 @@ bool lds_path_ok(const GemmArgs &g)
            al16(g.Bm) && lda < (int64_t(1) << 24) && ldb < (int64_t(1) << 24);
 }
 
-template <class Cfg, typename TA, typename TC>
+template <class Cfg, typename TA, typename TC, bool BKN = false>
 hipError_t lds_launch_cfg(const GemmArgs &g, hipStream_t s)
 {
     MM p;
@@ -1065,7 +1100,7 @@ hipError_t lds_launch_cfg(const GemmArgs &g, hipStream_t s)
     p.N = g.N;
     p.K = g.K;
     p.lda = g.lda ? g.lda : g.K;
-    p.ldb = g.ldb ? g.ldb : g.K;
+    p.ldb = g.ldb ? g.ldb : (BKN ? g.N : g.K);
     p.ldc = g.ldc ? g.ldc : g.N;
     p.sa = g.sa;
     p.sb = g.sb;
@@ -1074,7 +1109,7 @@ hipError_t lds_launch_cfg(const GemmArgs &g, hipStream_t s)
     p.gm = (int)group_rows(g.M, g.N, Cfg::BM, Cfg::BN);
     p.accumulate = g.accumulate;
     const int64_t tiles = ((g.M + Cfg::BM - 1) / Cfg::BM) * ((g.N + Cfg::BN - 1) / Cfg::BN);
-    hipLaunchKernelGGL((gemm_lds<Cfg, TA, TC>),
+    hipLaunchKernelGGL((gemm_lds<Cfg, TA, TC, BKN>),
                        dim3((unsigned)tiles, (unsigned)(g.batch > 0 ? g.batch : 1)),
                        dim3(Cfg::NT), 0, s, p, (const TA *)g.A, (const bf16_bits *)g.Bm, (TC *)g.C);
     return hipGetLastError();
@@ -1084,7 +1119,7 @@ hipError_t lds_launch_cfg(const GemmArgs &g, hipStream_t s)
 #define SRU_LDS_BIG_MIN_K 512
 #endif
 
-template <typename TA, typename TC>
+template <typename TA, typename TC, bool BKN = false>
 hipError_t lds_launch_t(const GemmArgs &g, hipStream_t s)
 {
     // the large tiles once they give every CU one and the reduction is long
@@ -1095,13 +1130,31 @@ hipError_t lds_launch_t(const GemmArgs &g, hipStream_t s)
     const int64_t nb = g.batch > 0 ? g.batch : 1;
     const int64_t big = ((g.M + 255) / 256) * ((g.N + 255) / 256) * nb;
     const int64_t mid = ((g.M + 255) / 256) * ((g.N + 127) / 128) * nb;
-    if (g.K >= SRU_LDS_BIG_MIN_K && big >= 256) return lds_launch_cfg<LdsBig, TA, TC>(g, s);
-    if (g.K >= 1024 && mid >= 256 && mid % 256 == 0) return lds_launch_cfg<LdsMid, TA, TC>(g, s);
-    if (g.K >= 1024) return lds_launch_cfg<LdsDeep, TA, TC>(g, s);
-    return lds_launch_cfg<LdsSmall, TA, TC>(g, s);
+    if (g.K >= SRU_LDS_BIG_MIN_K && big >= 256) return lds_launch_cfg<LdsBig, TA, TC, BKN>(g, s);
+    if (g.K >= 1024 && mid >= 256 && mid % 256 == 0)
+        return lds_launch_cfg<LdsMid, TA, TC, BKN>(g, s);
+    if (g.K >= 1024) return lds_launch_cfg<LdsDeep, TA, TC, BKN>(g, s);
+    return lds_launch_cfg<LdsSmall, TA, TC, BKN>(g, s);
 }
 
 hipError_t lds_launch(const GemmArgs &g, hipStream_t s) { return lds_launch_t<bf16_bits, float>(g, s); }
+
+// bf16 A (K-contiguous) times a bf16 B given as [K, N]: whole 64-deep
+// k-tiles, 16-byte aligned rows and batch offsets, N a multiple of 8 (whole
+// 16-byte pieces of a k-row), row strides below 2^24 elements.
+#ifndef SRU_LDS_KN
+#define SRU_LDS_KN 1
+#endif
+bool lds_kn_path_ok(const GemmArgs &g)
+{
+    if (!SRU_LDS_KN || !g.a_bf16 || !g.b_bf16 || !g.b_kn || g.K % 64 != 0 || g.K < 64 ||
+        g.N % 8 != 0)
+        return false;
+    const int64_t lda = g.lda ? g.lda : g.K, ldb = g.ldb ? g.ldb : g.N;
+    auto al16 = [](const void *q) { return ((uintptr_t)q & 15u) == 0; };
+    return lda % 8 == 0 && ldb % 8 == 0 && g.sa % 8 == 0 && g.sb % 8 == 0 && al16(g.A) &&
+           al16(g.Bm) && lda < (int64_t(1) << 24) && ldb < (int64_t(1) << 24);
+}
 
 // dst[i] = bf16(src[i]) (nearest even), four elements per lane and step.
 __global__ __launch_bounds__(256) void round_bf16_kernel(int64_t n, const float *__restrict__ src,
@@ -1578,6 +1631,7 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t s)
 {
     if (g.b_bf16) {
         if (lds_path_ok(g)) return lds_launch(g, s);
+        if (lds_kn_path_ok(g)) return lds_launch_t<bf16_bits, float, true>(g, s);
         if (g.a_bf16)
             return g.b_kn ? mfma_launch<bf16_bits, true>(g, s) : mfma_launch<bf16_bits, false>(g, s);
         return g.b_kn ? mfma_launch<float, true>(g, s) : mfma_launch<float, false>(g, s);

@@ -537,6 +537,15 @@ def test_bwd_data_bf16_dU_transposed_weight(L, B, d, nd):
     dX1 = layer.project_bwd_data(shape, Gd, Wd, Wt=Wt)
     check("dX == accumulated - C0", host(dX1).reshape(M, d), host(dX).reshape(M, d) - C0.reshape(M, d),
           1e-6)
+    # W untransposed ([K, N], read back by transposing LDS reads when d is a
+    # multiple of 8): the same bf16 operands in the same k order, so the
+    # same bits as the transposed weights
+    dX2 = layer.project_bwd_data(shape, Gd, Wd)
+    torch.cuda.synchronize()
+    if d % 8 == 0:
+        assert torch.equal(dX2.view(torch.int32), dX1.view(torch.int32))
+    else:
+        check("dX (W untransposed)", host(dX2).reshape(M, d), host(dX1).reshape(M, d), 1e-6)
 
 
 @pytest.mark.parametrize("n", [1, 3, 4, 5, 4096, 12289, 1000003, 40000003])
