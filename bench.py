@@ -232,7 +232,6 @@ def device_set(w, seed, x_copy=False):
                dU_lp=torch.empty((L, B, nd, 3, d), device="cuda", dtype=torch.bfloat16),
                dv=torch.empty((nd, 2, d), **f32), db=torch.empty((nd, 2, d), **f32),
                dc0=torch.empty((nd, B, d), **f32),
-               Wt=torch.empty((d, nd * 3 * d), device="cuda", dtype=dev["W"].dtype),
                ws=torch.empty(sru_workspace_size(shape, SRU_WS_BACKWARD), device="cuda",
                               dtype=torch.uint8),
                dW=torch.empty((nd * 3 * d, d), **f32))
@@ -272,13 +271,14 @@ def training_step_rows(shape, t):
     t["xb"] present a row of its own rounds X into that bf16 copy and the
     projection multiplies the copy; otherwise the projection reads fp32 X and
     rounds it to bf16 as it stages it."""
-    from parallelizable_recurrent_units_amd import (SRU_PROJ_BWD_DATA_WT, SRU_PROJ_FWD,
+    from parallelizable_recurrent_units_amd import (SRU_PROJ_BWD_DATA, SRU_PROJ_FWD,
                                                     sru_backward, sru_forward, sru_project,
-                                                    sru_round_bf16, sru_transpose_weight)
+                                                    sru_round_bf16)
 
     def bwd_data():
-        sru_transpose_weight(shape, t["W"], t["Wt"])
-        sru_project(shape, SRU_PROJ_BWD_DATA_WT, t["dU_lp"], t["Wt"], t["dx"], True)
+        # W as stored ([ndir 3d, d], K-major for this product): the kernel reads
+        # it back transposed from LDS, so no W^T pass is needed
+        sru_project(shape, SRU_PROJ_BWD_DATA, t["dU_lp"], t["W"], t["dx"], True)
 
     xb = t.get("xb")
     first = [("a1_round_x", lambda: sru_round_bf16(t["x"], xb))] if xb is not None else []
@@ -646,8 +646,9 @@ ROW_LAUNCHES = {
                        "launch when bidirectional and L <= 64, else one per direction, the "
                        "last one first) or scan_clear + bwd_scan per direction",
                        "param_reduce (dv, db)"],
-    "a5_projection_bwd_data": ["transpose16 (W -> W^T)",
-                               "gemm_lds (bf16 dU copy x bf16 W, operands copied straight into LDS)"],
+    "a5_projection_bwd_data": ["gemm_lds (bf16 dU copy x bf16 W as stored, K-major: both "
+                               "operands copied straight into LDS, W read back by transposing "
+                               "LDS reads)"],
     "a6_linear_forward": ["scan_clear", "lin_fwd_fused"],
     "a7_linear_backward": ["scan_clear", "lin_bwd_fused", "lin_db_reduce"],
     "f1_projection_bwd_weight": ["gemm_lds_t (A = bf16 dU copy and B = bf16 X~, both read "
@@ -676,14 +677,15 @@ ROW_LAUNCHES = {
 }
 
 # Which training-step row a dispatch belongs to, from its kernel name and,
-# for the products that several rows launch (gemm_lds), the row of the
-# dispatch before it: rows run in order a1, a2, a3/a4, a5 in every step.
+# for the products that several rows launch (gemm_lds), the dispatch before
+# it: rows run in order a1, a2, a3/a4, a5 in every step, so a gemm_lds after
+# the X rounding is the projection, and one after the backward (or after a
+# W^T transpose that follows the backward) the backward-data product.
 ROW_OF_KERNEL = [
     (r"round_bf16_kernel", "a1_round_x"),
     (r"gemm_bf16_mfma<.*>, float, false, ", "a1_projection"),
     (r"fwd_fast<|fwd_split<|fwd_generic<", "a2_forward"),
     (r"bwd_scan<|bwd_fast<|bwd_generic<|scan_clear|param_reduce", "a3_a4_backward"),
-    (r"transpose16", "a5_projection_bwd_data"),
 ]
 ROW_ONCE = {"a2_forward": r"fwd_fast<|fwd_split<|fwd_generic<"}   # one dispatch per step
 
@@ -696,13 +698,19 @@ def rows_of_dispatches(names):
     forward recurrence comes next, since the same product kernels also serve
     rows beyond the step."""
     import re
-    out, cur, pending = {}, None, []
+    out, cur, pending, a5_transpose = {}, None, [], False
     for did in sorted(names):
         n = names[did]
         row = next((r for pat, r in ROW_OF_KERNEL if re.search(pat, n)), None)
-        if row is None and re.search(r"gemm_lds<", n) and cur in (
-                "a1_round_x", "a1_projection", "a5_projection_bwd_data"):
-            row = "a1_projection" if cur == "a1_round_x" else cur
+        transpose = re.search(r"transpose16", n) is not None
+        if row is None and transpose and cur == "a3_a4_backward":
+            row = "a5_projection_bwd_data"               # W^T for the backward-data product
+        elif row is None and re.search(r"gemm_lds<", n):
+            if cur == "a1_round_x":
+                row = "a1_projection"
+            elif cur == "a3_a4_backward" or a5_transpose:
+                row = "a5_projection_bwd_data"
+        a5_transpose = transpose and row == "a5_projection_bwd_data"
         if row in ("a1_round_x", "a1_projection"):
             pending.append((did, row))
         else:

@@ -10,19 +10,24 @@
 // product when W has been transposed once by sru_transpose_weight) or as
 // [K, N] (C = A B, transposed while it is staged into LDS).
 //
-// Block tiles: a grid of waves, each wave a tile of 32 x 32 MFMA blocks; the
-// k-tile is staged global -> registers -> LDS (double-buffered in LDS) while
-// the previous one is multiplied.  Large problems use 256 x 256 blocks of 8
-// waves (one block per CU, two waves per SIMD), small ones 128 x 128 blocks
-// of 4 waves (two blocks per CU) to keep every CU busy.  C is fp32, or bf16
-// for the products whose consumers take bf16.
+// Block tiles of the register-staged kernel (gemm_bf16_mfma): a grid of
+// waves, each wave a tile of 32 x 32 MFMA blocks; the k-tile is staged
+// global -> registers -> LDS (double-buffered in LDS) while the previous one
+// is multiplied.  Large problems use 256 x 256 blocks of 8 waves (one block
+// per CU, two waves per SIMD), small ones 128 x 128 blocks of 4 waves (two
+// blocks per CU) to keep every CU busy.  C is fp32, or bf16 for the products
+// whose consumers take bf16.
 //
-// When both operands are bf16 and K-contiguous, gemm_lds copies the k-tiles
-// from memory straight into LDS (no registers, no LDS write instructions).
+// When both operands are bf16, gemm_lds copies the k-tiles from memory
+// straight into LDS (no registers, no LDS write instructions): A as [M, K]
+// rows, B as [N, K] rows or as [K, N] k-rows (read back by transposing LDS
+// reads, ds_read_b64_tr_b16).
 //
 // The weight gradient dW = dU^T X~ reads both operands K-major (the
 // reduction index L*B is the slow one) and may split that reduction across
 // blocks; split_reduce then adds the partial products in a fixed order.
+// With bf16 operands (an fp32 X is rounded into the workspace first)
+// gemm_lds_t copies both into LDS and reads both back transposed.
 //
 // fp32 path (W in fp32): LDS-tiled FMA kernel, fp32 products and sums.
 #include <type_traits>

@@ -758,16 +758,16 @@ tail:
 
 // dv[dl, g, j] = sum_b partials[dl, b, g, j]; db[dl, g, j] likewise with rows
 // 2, 3.  A block of 16 waves owns 64 consecutive j of one (dl, g): wave w sums
-// the b of residue w (mod 16), eight loads in flight at a time, then the 16
-// partial sums are added in wave order.  The summation order depends only on
-// B, so results are identical run to run.
+// the b of residue w (mod 16) in increasing order, sixteen (then eight) loads
+// in flight at a time, then the 16 partial sums are added in wave order.  The
+// summation order depends only on B, so results are identical run to run.
 constexpr int kReduceWaves = 16;
 
 __global__ __launch_bounds__(64 * kReduceWaves) void param_reduce(const float *__restrict__ part,
                                                                  int64_t B, int64_t d, float *dv,
                                                                  float *db)
 {
-    constexpr int NWv = kReduceWaves, U = 8;
+    constexpr int NWv = kReduceWaves;
     __shared__ float red[NWv][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t jblocks = (d + 63) / 64;
@@ -779,13 +779,19 @@ __global__ __launch_bounds__(64 * kReduceWaves) void param_reduce(const float *_
         const float *p = part + ((int64_t)dl * B * 4 + g) * d + j;
         const int64_t stride = 4 * d;                   // next b
         int64_t bb = wv;
-        for (; bb + (U - 1) * NWv < B; bb += U * NWv) {
-            float v[U];
+        // U rows of this wave's residue per batch of loads, added in order
+        auto batch = [&](auto u_const) {
+            constexpr int U = decltype(u_const)::value;
+            for (; bb + (U - 1) * NWv < B; bb += U * NWv) {
+                float v[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = p[(bb + u * NWv) * stride];
+                for (int u = 0; u < U; ++u) v[u] = p[(bb + u * NWv) * stride];
 #pragma unroll
-            for (int u = 0; u < U; ++u) s += v[u];
-        }
+                for (int u = 0; u < U; ++u) s += v[u];
+            }
+        };
+        batch(std::integral_constant<int, 16>());
+        batch(std::integral_constant<int, 8>());
         for (; bb < B; bb += NWv) s += p[bb * stride];
     }
     red[wv][lane] = s;

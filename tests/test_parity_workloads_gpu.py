@@ -49,8 +49,7 @@ def training_step(w, t):
     h, c_seq, c_last = layer.forward(shape, U, t["x"], t["v"], t["b"], t["c0"], keep_c_seq=True)
     dU, dx, dv, db, dc0, dU_lp = layer.backward(shape, U, t["x"], t["v"], t["b"], t["c0"], c_seq,
                                                 t["dh"], t["dc_last"], bf16_copy=True)
-    Wt = layer.transpose_weight(shape, t["W"])
-    layer.project_bwd_data(shape, dU_lp, t["W"], dx, accumulate=True, Wt=Wt)
+    layer.project_bwd_data(shape, dU_lp, t["W"], dx, accumulate=True)   # W as stored
     dW = layer.project_bwd_weight(shape, dU_lp, t["x"])
     return dict(U=U, h=h, c_seq=c_seq, c_last=c_last, dU=dU, dX=dx, dv=dv, db=db, dc0=dc0,
                 dW=dW)
