@@ -125,7 +125,7 @@ def next_row_work(w, x_copy=False):
         return attention_work(w) if not w.linear else {}
     L, B, d, nd = w.L, w.B, w.d, w.ndir
     LB, n3 = L * B, nd * 3 * d
-    xs = 2 if w.x_dtype == "bf16" else 4
+    xs = 2 if (w.x_dtype == "bf16" or x_copy) else 4   # X~ when the step made it
     di = factored_inner(w)
     fwd_flops = 2 * LB * d * di + 2 * LB * di * n3
     fwd_bytes = (LB * d * xs + di * d * 2 + LB * di * 4          # Q = X Wq^T
@@ -136,8 +136,7 @@ def next_row_work(w, x_copy=False):
                  + LB * di * 4 + LB * d * xs + di * d * 4       # dWq = dQ^T X
                  + LB * n3 * 2 + LB * di * 4 + n3 * di * 4)     # dWo = bf16(dU)^T Q
     rows = {"f1_projection_bwd_weight": dict(flops=2 * LB * n3 * d,
-                                             bytes=LB * n3 * 2 + LB * d * (2 if x_copy else xs)
-                                             + n3 * d * 4),
+                                             bytes=LB * n3 * 2 + LB * d * xs + n3 * d * 4),
             "f3_factored_forward": dict(flops=fwd_flops, bytes=fwd_bytes),
             "f3_factored_backward": dict(flops=bwd_flops, bytes=bwd_bytes)}
     if nd == 1:   # decoding steps (unidirectional layers only)
@@ -298,27 +297,29 @@ def training_step_rows(shape, t):
 def next_rows(shape, t):
     """The rows beyond the step, run on a step's buffers (dU_lp as the step
     left it): the weight gradient, and the factorised projection's forward
-    (writing U) and backward (adding to dx)."""
+    (writing U) and backward (adding to dx).  Where the step made the bf16
+    copy X~, the products that read X read X~ (the values they would round X
+    to as they load it)."""
     from parallelizable_recurrent_units_amd import (SRU_BF16, SRU_FACT_BWD_Q, SRU_FACT_BWD_X,
                                                     SRU_FACT_Q, SRU_FACT_U, SRU_FACT_WGRAD_O,
                                                     SRU_FACT_WGRAD_Q, sru_project_bwd_weight,
                                                     sru_project_factored,
                                                     sru_project_factored_bwd_weight)
     di = t["Q"].shape[1]
+    xs = t["xb"] if t.get("xb") is not None else t["x"]
 
     def fact_fwd():
-        sru_project_factored(shape, di, SRU_FACT_Q, t["x"], t["Wq"], t["Q"])
+        sru_project_factored(shape, di, SRU_FACT_Q, xs, t["Wq"], t["Q"])
         sru_project_factored(shape, di, SRU_FACT_U, t["Q"], t["Wo"], t["U"])
 
     def fact_bwd():
         sru_project_factored(shape, di, SRU_FACT_BWD_Q, t["dU_lp"], t["Wo"], t["dQ"])
         sru_project_factored(shape, di, SRU_FACT_BWD_X, t["dQ"], t["Wq"], t["dx"], True)
-        sru_project_factored_bwd_weight(shape, di, SRU_FACT_WGRAD_Q, t["dQ"], t["x"], t["dWq"],
+        sru_project_factored_bwd_weight(shape, di, SRU_FACT_WGRAD_Q, t["dQ"], xs, t["dWq"],
                                         SRU_BF16, False, t["ws_f"])
         sru_project_factored_bwd_weight(shape, di, SRU_FACT_WGRAD_O, t["dU_lp"], t["Q"],
                                         t["dWo"], SRU_BF16, False, t["ws_f"])
 
-    xs = t["xb"] if t.get("xb") is not None else t["x"]
     rows = [("f1_projection_bwd_weight",
              lambda: sru_project_bwd_weight(shape, t["dU_lp"], xs, t["dW"], SRU_BF16,
                                             False, t["ws_w"])),

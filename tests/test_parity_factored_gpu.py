@@ -104,6 +104,13 @@ def test_factored_products(L, B, d, nd, di):
               oracle.matmul(r(G), r(Y), a_km=True), GEMM_ACC)
         check(f"wgrad {which} vs exact oracle", host(dW), oracle.matmul(G, Y, a_km=True),
               BF16_BAR)
+        # Y already in bf16 (e.g. the layer's X~ copy): the values it is rounded to
+        # as loaded, so the same bits
+        Yb_bits, Yb = workloads.to_bf16(Y)
+        dWb = torch.empty(wshape, **f32)
+        sru_project_factored_bwd_weight(shape, di, which, dev(G), dev(Yb, Yb_bits), dWb, SRU_BF16,
+                                        False, ws)
+        assert torch.equal(dWb, dW), f"wgrad {which}: bf16 Y differs from fp32 Y rounded"
         sru_project_factored_bwd_weight(shape, di, which, dev(G), dev(Y), dW, SRU_F32)
         check(f"wgrad {which} (fp32)", host(dW), oracle.matmul(G, Y, a_km=True), TIGHT)
 
