@@ -671,7 +671,8 @@ ROW_LAUNCHES = {
                               "attn_residual_bwd + attn_part_reduce", "gemm (dP = dO V^T)",
                               "attn_softmax_bwd", "gemm (dQ += dS' K)", "gemm TN (dK, dV)",
                               "gemm + split_reduce (dWkv)", "gemm (dQ += dKV Wkv)",
-                              "gemm + split_reduce (dWq)", "gemm (dX = dQ Wq)"],
+                              "gemm + split_reduce (dWq)", "round_bf16 (dQ~)",
+                              "gemm (dX = dQ~ Wq)"],
     "f3_factored_backward": ["gemm_bf16_mfma (dQ = bf16(dU) Wo)", "gemm_bf16_mfma (dx += dQ Wq)",
                              "gemm_bf16_mfma + split_reduce (dWq = dQ^T X)",
                              "gemm_bf16_mfma + split_reduce (dWo = bf16(dU)^T Q)"],

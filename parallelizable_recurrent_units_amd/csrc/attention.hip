@@ -1077,7 +1077,7 @@ BwdLayout bwd_layout(int64_t L, int64_t B, int64_t d, int64_t dp, int64_t Lm, in
     w.dr_off = take(LB * dp * 4);
     w.dq_off = take(LB * dp * 4);
     w.do_off = take(LB * dp * 4);
-    w.dkv_off = take(LB * 2 * dp * 4);
+    w.dkv_off = take(LB * 2 * dp * 2);   // [dK | dV], bf16
     w.d_off = take(LB * 4);
     w.part_off = take((size_t)w.nblk * (size_t)(2 * dp + 1) * 4);
     w.wot_off = take((size_t)n3 * (size_t)dp * 2);                 // Wo^T, for a bf16 dU
@@ -1119,7 +1119,9 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
     float *dR = (float *)(ws + w.dr_off);
     float *dQ = (float *)(ws + w.dq_off);
     float *dO = (float *)(ws + w.do_off);
-    float *dKV = (float *)(ws + w.dkv_off);
+    // [dK | dV] written rounded to bf16: the values the two products that read
+    // it would round it to as they load it
+    bf16_bits *dKVb = (bf16_bits *)(ws + w.dkv_off);
     float *D = (float *)(ws + w.d_off);
     float *part = (float *)(ws + w.part_off);
     float *wg = (float *)(ws + w.wg_off);
@@ -1232,23 +1234,23 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
         g.M = L, g.N = dp, g.K = L;
         g.A = dSp + Lm, g.a_bf16 = true, g.lda = Lk, g.sa = L * Lk;
         g.Bm = Qb, g.b_bf16 = true, g.ldb = B * dp, g.sb = dp;
-        g.C = dKV, g.ldc = B * 2 * dp, g.sc = 2 * dp, g.accumulate = false;
+        g.C = (float *)dKVb, g.ldc = B * 2 * dp, g.sc = 2 * dp, g.accumulate = false;
         g.batch = B;
-        if ((e = launch_gemm_tn(g, s)) != hipSuccess) return e;
+        if ((e = launch_gemm_tn_bf16_out(g, s)) != hipSuccess) return e;
     }
     {   // and values: dV_b [L, d'] = P_b[:, Lm:]^T dO~_b, into dKV[:, d':]
         GemmArgs g;
         g.M = L, g.N = dp, g.K = L;
         g.A = P + Lm, g.a_bf16 = true, g.lda = Lk, g.sa = L * Lk;
         g.Bm = dOb, g.b_bf16 = true, g.ldb = B * dp, g.sb = dp;
-        g.C = dKV + dp, g.ldc = B * 2 * dp, g.sc = 2 * dp, g.accumulate = false;
+        g.C = (float *)(dKVb + dp), g.ldc = B * 2 * dp, g.sc = 2 * dp, g.accumulate = false;
         g.batch = B;
-        if ((e = launch_gemm_tn(g, s)) != hipSuccess) return e;
+        if ((e = launch_gemm_tn_bf16_out(g, s)) != hipSuccess) return e;
     }
     {   // dWkv [2d', d'] = [dK | dV]^T Q~
         GemmArgs g;
         g.M = 2 * dp, g.N = dp, g.K = LB;
-        g.A = dKV, g.a_bf16 = false;
+        g.A = dKVb, g.a_bf16 = true;
         g.Bm = Qb, g.b_bf16 = true;
         g.C = a.dWkv, g.accumulate = false;
         if ((e = launch_gemm_wgrad(g, false, wg, s)) != hipSuccess) return e;
@@ -1256,7 +1258,7 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
     {   // dQ += [dK | dV] Wkv (Wkv [2d', d'] read as [K, N])
         GemmArgs g;
         g.M = LB, g.N = dp, g.K = 2 * dp;
-        g.A = dKV, g.a_bf16 = false;
+        g.A = dKVb, g.a_bf16 = true;
         g.Bm = a.Wkv, g.b_bf16 = true, g.b_kn = true;
         g.C = dQ, g.accumulate = true;
         if ((e = launch_gemm(g, s)) != hipSuccess) return e;
@@ -1269,10 +1271,14 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
         g.C = a.dWq, g.accumulate = false;
         if ((e = launch_gemm_wgrad(g, false, wg, s)) != hipSuccess) return e;
     }
-    // dX (+)= dQ Wq (Wq [d', d] read as [K, N])
+    // dX (+)= dQ~ Wq (Wq [d', d] read as [K, N]), dQ rounded to bf16 once into
+    // Q~'s space (the products that read Q~ have run) so that both operands
+    // go straight into LDS
+    bf16_bits *dQb = Qb;
+    if ((e = launch_round_bf16(LB * dp, dQ, dQb, s)) != hipSuccess) return e;
     GemmArgs g;
     g.M = LB, g.N = d, g.K = dp;
-    g.A = dQ, g.a_bf16 = false;
+    g.A = dQb, g.a_bf16 = true;
     g.Bm = a.Wq, g.b_bf16 = true, g.b_kn = true;
     g.C = a.dX, g.accumulate = a.dx_accumulate;
     return launch_gemm(g, s);

@@ -1607,11 +1607,12 @@ hipError_t launch_gemm_wgrad(const GemmArgs &g, bool f32_math, float *ws, hipStr
 }
 
 namespace {
-template <typename TA, typename TB>
+template <typename TA, typename TB, typename TC = float>
 hipError_t tn_launch(const GemmArgs &g, hipStream_t s)
 {
-    if (tiles_of(g, 256, 256) >= 256) return mfma_launch_cfg<CfgBig8, TA, true, TB, true>(g, s);
-    return mfma_launch_cfg<CfgSmall, TA, true, TB, true>(g, s);
+    if (tiles_of(g, 256, 256) >= 256)
+        return mfma_launch_cfg<CfgBig8, TA, true, TB, true, TC>(g, s);
+    return mfma_launch_cfg<CfgSmall, TA, true, TB, true, TC>(g, s);
 }
 }  // namespace
 
@@ -1620,6 +1621,12 @@ hipError_t launch_gemm_tn(const GemmArgs &g, hipStream_t s)
     if (g.a_bf16)
         return g.b_bf16 ? tn_launch<bf16_bits, bf16_bits>(g, s) : tn_launch<bf16_bits, float>(g, s);
     return g.b_bf16 ? tn_launch<float, bf16_bits>(g, s) : tn_launch<float, float>(g, s);
+}
+
+hipError_t launch_gemm_tn_bf16_out(const GemmArgs &g, hipStream_t s)
+{
+    if (!g.a_bf16 || !g.b_bf16 || g.accumulate) return hipErrorInvalidValue;
+    return tn_launch<bf16_bits, bf16_bits, bf16_bits>(g, s);
 }
 
 hipError_t launch_gemm_bf16_out(const GemmArgs &g, hipStream_t s)

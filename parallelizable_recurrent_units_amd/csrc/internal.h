@@ -124,6 +124,11 @@ hipError_t launch_gemm_wgrad(const GemmArgs &g, bool f32_math, float *ws, hipStr
 // each, rounded to bf16 while staged; row strides and batches as in
 // GemmArgs), bf16 MFMA, no split of the reduction and no workspace.
 hipError_t launch_gemm_tn(const GemmArgs &g, hipStream_t s);
+// As launch_gemm_tn for bf16 A and B, no accumulation, with C written as bf16
+// (rounded to nearest even; C points to bf16 storage, row stride ldc): the
+// same kernel and products as launch_gemm_tn, so the bf16 C is its fp32 C
+// rounded.
+hipError_t launch_gemm_tn_bf16_out(const GemmArgs &g, hipStream_t s);
 // The SRU++ attention U-producer (attention.hip); layouts as in sru.h.
 struct AttnArgs {
     int64_t L, B, d, dp, Lm, n3;   // n3 = ndir * 3 * d
