@@ -669,7 +669,7 @@ ROW_LAUNCHES = {
                               "tiles in three stages)",
                               "gemm + split_reduce (dWo)",
                               "attn_residual_bwd + attn_part_reduce", "gemm (dP = dO V^T)",
-                              "attn_softmax_bwd", "gemm (dQ += dS' K)", "gemm TN (dK, dV)",
+                              "attn_softmax_bwd", "gemm (dQ += dS' K)", "gemm TN (dK, dV, bf16 out)",
                               "gemm + split_reduce (dWkv)", "gemm (dQ += dKV Wkv)",
                               "gemm + split_reduce (dWq)", "round_bf16 (dQ~)",
                               "gemm (dX = dQ~ Wq)"],
