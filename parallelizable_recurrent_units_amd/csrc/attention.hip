@@ -520,6 +520,14 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_fused(FusedArgs a)
                 else
                     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], sacc, 0, 0, 0);
             }
+            // keep four K reads in flight ahead of the MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int ks = 0; ks + 4 < NKS; ++ks) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             sacc += s1;
             // this half to the partner: [wave][4 pieces][64 lanes][4 floats]
 #pragma unroll
@@ -597,6 +605,14 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_fused(FusedArgs a)
             o[n % NOB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, n < NOB ? pf0 : pf1, o[n % NOB],
                                                                 0, 0, 0);
         }
+        // keep four V reads in flight ahead of the MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int n = 0; n + 4 < 2 * NOB; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     };
 
     prefetch(1);
