@@ -671,7 +671,7 @@ ROW_LAUNCHES = {
                               "attn_residual_bwd + attn_part_reduce", "gemm (dP = dO V^T)",
                               "attn_softmax_bwd", "gemm (dQ += dS' K)", "gemm TN (dK, dV, bf16 out)",
                               "gemm + split_reduce (dWkv)", "gemm (dQ += dKV Wkv)",
-                              "gemm + split_reduce (dWq)", "round_bf16 (dQ~)",
+                              "round_bf16 (dQ~)", "gemm + split_reduce (dWq = dQ~^T X)",
                               "gemm (dX = dQ~ Wq)"],
     "f3_factored_backward": ["gemm_bf16_mfma (dQ = bf16(dU) Wo)", "gemm_bf16_mfma (dx += dQ Wq)",
                              "gemm_bf16_mfma + split_reduce (dWq = dQ^T X)",

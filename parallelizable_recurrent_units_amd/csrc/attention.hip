@@ -1279,19 +1279,20 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
         g.C = dQ, g.accumulate = true;
         if ((e = launch_gemm(g, s)) != hipSuccess) return e;
     }
-    {   // dWq [d', d] = dQ^T X~
+    // dQ is final: rounded to bf16 once, into Q~'s space (the products that
+    // read Q~ have run), for its two products below
+    bf16_bits *dQb = Qb;
+    if ((e = launch_round_bf16(LB * dp, dQ, dQb, s)) != hipSuccess) return e;
+    {   // dWq [d', d] = dQ~^T X~
         GemmArgs g;
         g.M = dp, g.N = d, g.K = LB;
-        g.A = dQ, g.a_bf16 = false;
+        g.A = dQb, g.a_bf16 = true;
         g.Bm = a.X, g.b_bf16 = a.x_bf16;
         g.C = a.dWq, g.accumulate = false;
         if ((e = launch_gemm_wgrad(g, false, wg, s)) != hipSuccess) return e;
     }
-    // dX (+)= dQ~ Wq (Wq [d', d] read as [K, N]), dQ rounded to bf16 once into
-    // Q~'s space (the products that read Q~ have run) so that both operands
-    // go straight into LDS
-    bf16_bits *dQb = Qb;
-    if ((e = launch_round_bf16(LB * dp, dQ, dQb, s)) != hipSuccess) return e;
+    // dX (+)= dQ~ Wq (Wq [d', d] read as [K, N]): both operands go straight
+    // into LDS
     GemmArgs g;
     g.M = LB, g.N = d, g.K = dp;
     g.A = dQb, g.a_bf16 = true;
