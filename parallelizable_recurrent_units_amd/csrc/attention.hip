@@ -1054,6 +1054,7 @@ hipError_t attend(int64_t L, int64_t B, int64_t dp, int64_t Lm, int causal, cons
         g.Bm = KV, g.b_bf16 = true, g.b_kn = false, g.ldb = B * 2 * dp, g.sb = 2 * dp;
         g.C = S, g.ldc = Lk, g.sc = L * Lk, g.accumulate = false;
         g.batch = B;
+        g.causal_skip = causal ? Lm : -1;   // the softmax reads no masked score
         if ((e = launch_gemm(g, s)) != hipSuccess) return e;
     }
     if ((e = launch_softmax(L, B, dp, Lm, causal, S, P, s)) != hipSuccess) return e;
@@ -1063,6 +1064,7 @@ hipError_t attend(int64_t L, int64_t B, int64_t dp, int64_t Lm, int causal, cons
     g.Bm = KV + dp, g.b_bf16 = true, g.b_kn = true, g.ldb = B * 2 * dp, g.sb = 2 * dp;
     g.C = O, g.ldc = B * dp, g.sc = dp, g.accumulate = false;
     g.batch = B;
+    g.causal_klim = causal ? Lm : -1;       // masked weights are zeros
     return launch_gemm(g, s);
 }
 
@@ -1203,6 +1205,7 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
         g.Bm = KV + dp, g.b_bf16 = true, g.b_kn = false, g.ldb = B * 2 * dp, g.sb = 2 * dp;
         g.C = dP, g.ldc = Lk, g.sc = L * Lk, g.accumulate = false;
         g.batch = B;
+        g.causal_skip = a.causal ? Lm : -1;   // the softmax backward reads none masked
         if ((e = launch_gemm(g, s)) != hipSuccess) return e;
     }
     {   // dS' = p (dP - D) / sqrt(d') in bf16
@@ -1243,6 +1246,7 @@ hipError_t launch_attention_backward(const AttnBwdArgs &a, hipStream_t s)
         g.Bm = KV, g.b_bf16 = true, g.b_kn = true, g.ldb = B * 2 * dp, g.sb = 2 * dp;
         g.C = dQ, g.ldc = B * dp, g.sc = dp, g.accumulate = true;
         g.batch = B;
+        g.causal_klim = a.causal ? Lm : -1;   // dS' is zero at masked keys
         if ((e = launch_gemm(g, s)) != hipSuccess) return e;
     }
     {   // this segment's keys: dK_b [L, d'] = dS'_b[:, Lm:]^T Q~_b, into dKV[:, :d']

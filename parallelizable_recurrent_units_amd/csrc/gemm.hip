@@ -301,6 +301,11 @@ struct MM {
     int64_t ksplit;          // k-range per split (>= K: no split)
     int gm;                  // row tiles per group of the tile order
     bool accumulate;
+    // causal products (gemm_lds only; -1: off), row m seeing columns
+    // n <= c + m: cskip = c skips tiles with no such column, whose C is never
+    // read; klim = c ends each row tile's reduction after k = c + its last
+    // row, the rest of its A row being zeros
+    int64_t cskip = -1, klim = -1;
 };
 
 // C[M, N] (+)= A . B, where A is given as [M, K] (AKM = false) or [K, M]
@@ -727,6 +732,7 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
     int64_t tm, tn;
     tile_of((int64_t)blockIdx.x, TM, TN, p.gm, &tm, &tn);
     const int64_t m0 = tm * BM, n0 = tn * BN;
+    if (p.cskip >= 0 && n0 >= p.cskip + m0 + BM) return;   // the whole block: uniform
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;    // low half of a flat LDS address
 
     // Request q fills 1 KB of the stage: 8 rows of A (q < QA) or of B, each
@@ -770,7 +776,11 @@ __global__ __launch_bounds__(Cfg::NT, Cfg::MINB) void gemm_lds(MM p, const TA *_
             voff[i] = (uint32_t)((rr - rb) * ld * 2 + 16 * c);
         }
     }
-    const int64_t KT = K / 64;
+    int64_t KT = K / 64;
+    if (p.klim >= 0) {   // k-tiles up to the last one holding k = klim + the tile's last row
+        const int64_t kt_end = (p.klim + m0 + BM - 1) / 64 + 1;
+        KT = kt_end < KT ? kt_end : KT;
+    }
     const int64_t kstep = (BKN && !isA) ? 64 * ldb * 2 : 128;   // bytes per k-tile
     // requests of k-tile kt into stage st; past the last k-tile the last one
     // is requested again, so every iteration waits on the same count
@@ -1113,6 +1123,8 @@ hipError_t lds_launch_cfg(const GemmArgs &g, hipStream_t s)
     p.ksplit = g.K;
     p.gm = (int)group_rows(g.M, g.N, Cfg::BM, Cfg::BN);
     p.accumulate = g.accumulate;
+    p.cskip = g.causal_skip;
+    p.klim = g.causal_klim;
     const int64_t tiles = ((g.M + Cfg::BM - 1) / Cfg::BM) * ((g.N + Cfg::BN - 1) / Cfg::BN);
     hipLaunchKernelGGL((gemm_lds<Cfg, TA, TC, BKN>),
                        dim3((unsigned)tiles, (unsigned)(g.batch > 0 ? g.batch : 1)),

@@ -98,6 +98,12 @@ struct GemmArgs {
     bool accumulate;
     int64_t lda = 0, ldb = 0, ldc = 0;
     int64_t batch = 1, sa = 0, sb = 0, sc = 0;
+    // Causal products, where row m of C sees columns n <= c + m (-1: off).
+    // causal_skip = c: tiles with no such column may be left unwritten (their
+    // C is never read).  causal_klim = c: A's row m holds zeros past
+    // k = c + m, so a row tile's reduction may stop there.  Hints: only the
+    // kernels that copy bf16 operands straight into LDS use them.
+    int64_t causal_skip = -1, causal_klim = -1;
 };
 
 // bf16 B: bf16 MFMA (A rounded to bf16 as it is loaded); fp32 B: fp32 FMA.
