@@ -369,9 +369,21 @@ def time_rows(row_sets, steps, warmup):
             fn()
     torch.cuda.synchronize()
     names = [n for n, _ in row_sets[0]]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if len(names) == 1:
+        # a step of one row: its launches back to back between the two events
+        # (events between the steps would add a marker's drain to every launch)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            for _, fn in row_sets[i % nsets]:
+                fn()
+        end.record()
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(end)
+        return total_ms / steps, {names[0]: total_ms / 1e3 / steps}
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
            for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(steps):
