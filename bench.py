@@ -358,15 +358,22 @@ def decode_rows(shape, t):
     return out
 
 
-def time_rows(row_sets, steps, warmup):
-    """Run ``steps`` passes (rotating sets), HIP events between the rows.
+def time_rows(row_sets, steps, warmup, min_warm_s=0.0):
+    """Run ``steps`` passes (rotating sets), HIP events between the rows,
+    after ``warmup`` untimed passes (continued until ``min_warm_s`` seconds
+    have gone by, so a GPU that sat idle reaches its working clock first).
 
     Returns (ms per step, {row: mean seconds})."""
     import torch
     nsets = len(row_sets)
-    for i in range(warmup):
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t0 < min_warm_s:
         for _, fn in row_sets[i % nsets]:
             fn()
+        i += 1
+        if i >= warmup:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     names = [n for n, _ in row_sets[0]]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -517,11 +524,16 @@ def row_sets_for(w, nsets, seed0, x_copy_mode="auto"):
     return [rs]
 
 
+# untimed warm-up of each workload timed beside the headline one: it follows the
+# input generation (and, for the headline, the CPU baselines' idle GPU)
+EXTRA_WARM_S = 0.2
+
+
 def measure(w, nsets, steps, warmup, seed0):
     """(ms per step, {row: measurement}) for workload ``w``."""
     import torch
     sets = row_sets_for(w, nsets, seed0)
-    ms, rows = time_rows(sets, steps, warmup)
+    ms, rows = time_rows(sets, steps, warmup, EXTRA_WARM_S)
     check_error_words(sets)
     work = row_work(w, w.mode == "layer" and rounds_x_first(w, "auto"))
     per_row = {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
@@ -539,7 +551,7 @@ def time_beyond(w, sets, steps, warmup, x_copy=False):
     beyond = [s.beyond for s in sets if getattr(s, "beyond", ())]
     if not beyond:
         return {}
-    _, rows = time_rows(beyond, steps, warmup)
+    _, rows = time_rows(beyond, steps, warmup, EXTRA_WARM_S)
     work = next_row_work(w, x_copy)
     out = {n: dict(us=rows[n] * 1e6, **roofline_of(n, work[n], rows[n])) for n in rows}
     for n, r in out.items():
@@ -554,15 +566,14 @@ def extras(main_id, steps, cpu_s=0.0):
     """Rows at the other workload sizes, each workload timed on its own."""
     from parallelizable_recurrent_units_amd.workloads import WORKLOADS
     out = {}
-    for wid in (2, 3, 4, 5):
-        if wid == main_id:
-            continue
-        w = WORKLOADS[wid]
+    others = [(wid, WORKLOADS[wid]) for wid in (2, 3, 4, 5) if wid != main_id]
+    for wid, w in others:                 # every GPU measurement before the CPU ones
         linear = w.linear
         ms, per_row = measure(w, 1 if linear else 4, max(3, steps // 5) if linear else steps,
                               2 if linear else 3, 40 + 10 * wid)
         out[w.name] = dict(per_row, ms_per_step=ms)
-        if cpu_s > 0:
+    if cpu_s > 0:
+        for _, w in others:
             print(f"[bench] CPU oracle baseline, {w.name}", file=sys.stderr, flush=True)
             out[w.name]["cpu_baseline"] = cpu_baseline(w, cpu_s)
     return out
