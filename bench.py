@@ -524,8 +524,9 @@ def row_sets_for(w, nsets, seed0, x_copy_mode="auto"):
     return [rs]
 
 
-# untimed warm-up of each workload timed beside the headline one: it follows the
-# input generation (and, for the headline, the CPU baselines' idle GPU)
+# the untimed warm-up of every timed set of rows lasts at least this long (and
+# at least the requested number of steps): a GPU that has idled, or has only
+# generated inputs, runs below its working clock for the first milliseconds
 EXTRA_WARM_S = 0.2
 
 
@@ -856,7 +857,7 @@ def main():
     print(f"[bench] workload {w.name}: building {nsets} input sets", file=sys.stderr, flush=True)
     row_sets = row_sets_for(w, nsets, 100, args.x_copy)
     print("[bench] timing", file=sys.stderr, flush=True)
-    ms, rows = time_rows(row_sets, args.steps, args.warmup)
+    ms, rows = time_rows(row_sets, args.steps, args.warmup, EXTRA_WARM_S)
     check_error_words(row_sets)
     beyond = {} if args.no_beyond else time_beyond(
         w, row_sets, args.steps, args.warmup, w.mode == "layer" and rounds_x_first(w, args.x_copy))
@@ -890,6 +891,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_min_s": EXTRA_WARM_S,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
